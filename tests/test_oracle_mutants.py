@@ -1,0 +1,74 @@
+"""Planted mistakes in the oracle (CPU only): each mutant is a copy of oracle.c with one
+plausible error (a wrong sign, a transposed index, an off-by-one bound, swapped dims).  The
+pins must reject every mutant, which shows they are sharp enough to trust the oracle."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "pad_sign": ("int64_t iy = e * stride - pad + r;\n            if (iy < 0 || iy >= H) continue;",
+                 "int64_t iy = e * stride + pad + r;\n            if (iy < 0 || iy >= H) continue;"),
+    "r_s_transposed": ("int64_t r = (col / S) % R;\n        int64_t s = col % S;\n        double v",
+                       "int64_t r = col % R;\n        int64_t s = (col / R) % S;\n        double v"),
+    "row_bound_off_by_one": ("if (iy < 0 || iy >= H) continue;\n            for",
+                             "if (iy < 0 || iy >= H - 1) continue;\n            for"),
+    "stride_dropped_x": ("int64_t ix = f * stride - pad + s;\n                if (ix < 0 || ix >= W) continue;\n                double prod = v",
+                         "int64_t ix = f - pad + s;\n                if (ix < 0 || ix >= W) continue;\n                double prod = v"),
+    "stretch_h_w_swapped": ("off[j] = (uint32_t)(((int64_t)c * H + r) * W + s);",
+                            "off[j] = (uint32_t)(((int64_t)c * W + r) * H + s);"),
+    "value_sign": ("double v = (double)value[j];", "double v = -(double)value[j];"),
+    "output_transposed": ("yp[e * F + f] += prod;", "yp[f * E + e] += prod;"),
+}
+
+
+def _pins_pass():
+    """A compact run of the pins: torch float64 conv2d on non-square strided/padded shapes,
+    and the stretched-offset gather."""
+    for seed, (N, C, H, W, M, R, S, st, p) in enumerate([(2, 3, 9, 7, 4, 3, 2, 2, 1),
+                                                          (1, 2, 8, 11, 3, 2, 4, 1, 2),
+                                                          (1, 2, 12, 12, 2, 3, 3, 1, 1)]):
+        d = workloads.make_custom(N, C, H, W, M, R, S, st, p, 0.7, 900 + seed)
+        r = oracle.reference(d["x"], d["w"], d["mask"], st, p)
+        t = torch.nn.functional.conv2d(torch.from_numpy(d["x"]).double(),
+                                       torch.from_numpy(d["w_masked"]).double(), stride=st, padding=p).numpy()
+        if t.shape != r["y64"].shape or not np.all(np.abs(t - r["y64"]) <= 1e-12 * r["mag"] + 1e-300):
+            return False
+    C, R, S, H, W = 3, 2, 3, 5, 7
+    off = oracle.stretch(np.arange(C * R * S, dtype=np.int32), C, R, S, H, W).reshape(C, R, S)
+    x = np.arange(C * H * W, dtype=np.float32).reshape(C, H, W)
+    for c in range(C):
+        for r_ in range(R):
+            for s in range(S):
+                if x.reshape(-1)[off[c, r_, s]] != x[c, r_, s]:
+                    return False
+    return True
+
+
+def test_unmutated_oracle_passes_compact_pins():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_rejected(name, tmp_path):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-o", str(so_path), str(c_path), "-lm"])
+    saved = oracle._lib
+    try:
+        oracle._lib = oracle._bind(str(so_path))
+        assert not _pins_pass(), f"mutant {name} survived the pins"
+    finally:
+        oracle._lib = saved
