@@ -1,0 +1,165 @@
+/*
+ * sparseconv.h -- C ABI of the MI355X (gfx950) sparse direct convolution library.
+ *
+ * What it computes.  Direct convolution of dense NCHW fp32 feature maps with an
+ * unstructured-sparse filter bank, without lowering (no im2col) and without a dense
+ * fallback.  For an image n, output channel m and output position (e, f):
+ *
+ *     Y[n,m,e,f] = sum over stored non-zeros (c, r, s, v) of row m of  v * X[n, c, iy, ix]
+ *                  with iy = e*stride - pad + r, ix = f*stride - pad + s,
+ *                  terms with (iy, ix) outside [0,H) x [0,W) omitted,
+ *     E = (H + 2*pad - R) / stride + 1,  F = (W + 2*pad - S) / stride + 1.
+ *
+ * This is the multi-channel convolution of Tuteja et al., "Theoretical and Empirical
+ * Analysis of Sparse Convolution", Sec. 3 Eq. (1)-(3) (sum clipped to the image, sparse
+ * form over the non-zeros N(oc,h,w), output size Eq. (2)), read with a stride in both
+ * axes.  There is no bias and no activation.  The filter bank is the M x (C*R*S) matrix
+ * of "Escoin: Efficient Sparse Convolutional Neural Network Inference on GPUs" (lowering
+ * section), column index col = c*R*S + r*S + s, stored row by row in CSR form
+ * (value / colidx / rowptr, CSR section of the same page).  Packing turns every column
+ * index into the input offset of the layout function f(c,r,s) = (c*H + r)*W + s of the
+ * UNPADDED input ("weight stretching", same page) and keeps each row's entries contiguous
+ * as {offset, value} pairs, so that one load returns everything a non-zero needs (the
+ * packed-weight idea of Tuteja et al., Sec. 5.3).
+ *
+ * Conventions.
+ *  - Plain C: fixed-width integers, pointers and sizes.  No exception crosses this ABI.
+ *  - "host" pointers are read only during the call and never retained.
+ *  - "device" pointers are HIP device allocations on the current device.
+ *  - Every entry point returns sc_status; sparseconv_last_error() describes the last
+ *    failure of the calling thread.
+ *  - All argument checks happen before any device work: on error nothing is written.
+ */
+#ifndef SPARSECONV_H
+#define SPARSECONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sc_handle sc_handle; /* opaque packed filter bank, immutable after pack */
+
+typedef enum {
+  SC_OK = 0,
+  SC_EINVAL = 1,       /* null pointer, malformed CSR, overlapping buffers, bad flag */
+  SC_ESHAPE = 2,       /* a dimension is <= 0, E or F <= 0, or forward dims differ from the handle */
+  SC_ENOMEM = 3,       /* host or device allocation failed */
+  SC_EDEVICE = 4,      /* a HIP runtime call or kernel launch failed (incl. no device) */
+  SC_EUNSUPPORTED = 5  /* size outside the documented limits below */
+} sc_status;
+
+typedef enum {
+  SC_WEIGHTS_DENSE = 0, /* values: M*C*R*S fp32, (m,c,r,s) row-major; optional mask */
+  SC_WEIGHTS_CSR = 1    /* values/colidx: nnz entries; rowptr: M+1 entries */
+} sc_weights_format;
+
+/* Pack flags. */
+#define SC_PACK_HOST_ONLY 1u /* build the packed form on the host only: query and export
+                                work, forward returns SC_EINVAL.  Needs no GPU. */
+
+typedef struct {
+  int32_t format;          /* sc_weights_format */
+  const float* values;     /* host.  DENSE: M*C*R*S values.  CSR: nnz values (row order) */
+  const int32_t* colidx;   /* host.  CSR only: nnz column indices, 0 <= col < C*R*S,
+                              no duplicate within a row (any order within a row) */
+  const int32_t* rowptr;   /* host.  CSR only: M+1 entries, rowptr[0] = 0, non-decreasing,
+                              rowptr[M] = nnz */
+  const uint8_t* mask;     /* host.  DENSE only, optional M*C*R*S bytes: a position is a
+                              stored non-zero iff mask != 0 (explicit zero values kept).
+                              NULL: a position is stored iff its value != 0.0f
+                              (so -0.0 is dropped and NaN kept). */
+} sc_weights;
+
+typedef struct {
+  int32_t M, C, R, S, H, W, stride, pad, E, F;
+  int64_t nnz;
+  int64_t packed_bytes;  /* (2*nnz + M + 1) * 4: canonical {offset, value} entries + rowptr,
+                            the CSR size of "Escoin", CSR section */
+  int64_t device_bytes;  /* bytes this handle holds on the device (kernel stream + tables) */
+  int32_t tile_pixels;   /* launch plan: extended output positions per workgroup */
+  int32_t rows_per_wave; /* launch plan: output-channel slots per wavefront */
+  int32_t row_groups;    /* launch plan: workgroups sharing one tile (output-channel groups) */
+  int32_t chunk_channels;/* launch plan: input channels staged in LDS at a time */
+  int32_t lds_bytes;     /* launch plan: dynamic LDS per workgroup */
+  int32_t max_wave_nnz;  /* largest non-zero count given to one wavefront */
+  int32_t reserved[4];
+} sc_info;
+
+/*
+ * Pack a filter bank for one layer geometry (once per layer; weights then stay resident).
+ *   w          host description of the weights (see sc_weights).
+ *   M,C,R,S    output channels, input channels, filter rows, filter columns (all >= 1).
+ *   H,W        unpadded input height and width the layer will be applied to (>= 1).
+ *   stride>=1, pad>=0; E and F from the formula above must be >= 1.
+ *   flags      0 or SC_PACK_HOST_ONLY.
+ *   out        receives the new handle (set to NULL on failure).
+ * Steps: validate -> CSR (columns sorted within each row, values moved with them) ->
+ * stretched offsets -> wavefront schedule balanced by non-zero count -> upload.
+ * Limits (SC_EUNSUPPORTED): C*H*W < 2^32 (offsets are u32), M*C*R*S < 2^31,
+ * nnz < 2^31.  Errors: SC_EINVAL (null w/out/arrays, malformed CSR, unknown format/flag),
+ * SC_ESHAPE, SC_ENOMEM, SC_EDEVICE.
+ * The handle owns its device buffers (hipMalloc on the device current at pack time).
+ */
+sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, int32_t S,
+                          int32_t H, int32_t W, int32_t stride, int32_t pad, uint32_t flags,
+                          sc_handle** out);
+
+/*
+ * Forward pass: output = conv(input, packed filters), overwriting the whole output.
+ *   h         handle from sparseconv_pack (device-resident, not SC_PACK_HOST_ONLY).
+ *   input     device, N*C*H*W fp32, NCHW contiguous, 4-byte aligned.
+ *   output    device, N*M*E*F fp32, NCHW contiguous; must not overlap input.
+ *   N >= 0 (0 is a no-op); C,H,W,M,R,S,stride,pad must equal the handle's.
+ *   hip_stream  hipStream_t to launch on (NULL: the default stream).
+ * Asynchronous: returns after the launch; nothing is synchronised.  The handle is never
+ * written, so forwards on several streams may run at once.  Limits (SC_EUNSUPPORTED):
+ * N*C*H*W < 2^31 and N*M*E*F < 2^31 elements.  Errors: SC_EINVAL (null handle or
+ * pointers, host-only handle, overlap), SC_ESHAPE (dims differ from the handle),
+ * SC_EDEVICE (launch failure).
+ */
+sc_status sparseconv_forward(const sc_handle* h, const float* input, float* output, int32_t N,
+                             int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                             int32_t stride, int32_t pad, void* hip_stream);
+
+/* Fill *info with the handle's geometry, sizes and launch plan.  SC_EINVAL on NULL. */
+sc_status sparseconv_query(const sc_handle* h, sc_info* info);
+
+/*
+ * Copy out the canonical packed form (host buffers owned by the caller):
+ *   rowptr  M+1 entries; offsets, values  nnz entries each.
+ * Canonical order: rows m ascending; within a row, columns c*R*S + r*S + s ascending.
+ * offsets[j] = c*H*W + r*W + s of entry j; values[j] its fp32 weight, bit for bit.
+ * Any of the three pointers may be NULL to skip it.  SC_EINVAL on a NULL handle.
+ */
+sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t* offsets,
+                                   float* values);
+
+/* Free the handle and its device buffers.  NULL is a no-op.  Must not race a forward
+ * still running on the device that reads this handle (synchronise the stream first). */
+void sparseconv_destroy(sc_handle* h);
+
+/* Message of the calling thread's last failure ("" if none).  Valid until that thread's
+ * next call into the library. */
+const char* sparseconv_last_error(void);
+
+/*
+ * Dense direct convolution with the same tiling and staging, over every filter tap
+ * including zeros: the on-GPU baseline the sparse path is measured against (dense
+ * counterpart of Tuteja et al., Sec. 4 Eq. (5)/(6)).  Same conventions as forward:
+ *   w_dense  device, M*C*R*S fp32 (m,c,r,s) row-major.
+ *   input    device, N*C*H*W;  output device, N*M*E*F (overwritten, must not overlap).
+ * Errors: SC_EINVAL (null pointers, overlap), SC_ESHAPE, SC_EUNSUPPORTED (limits as
+ * forward), SC_EDEVICE.
+ */
+sc_status sparseconv_dense_forward(const float* w_dense, const float* input, float* output,
+                                   int32_t N, int32_t C, int32_t H, int32_t W, int32_t M,
+                                   int32_t R, int32_t S, int32_t stride, int32_t pad,
+                                   void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSECONV_H */

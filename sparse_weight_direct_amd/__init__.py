@@ -1,0 +1,219 @@
+"""Python binding of libsparseconv.so (the C ABI in include/sparseconv.h).
+
+Argument marshalling only: every step of packing and of the forward pass runs in the
+native library (host C++ for packing, gfx950 HIP kernels for the convolution).  PyTorch is
+used for device memory and streams.  There is no fallback: if the library is missing the
+import fails, and the forward pass needs a ROCm device.
+
+The functions keep the C names:
+    sparseconv_pack, sparseconv_forward, sparseconv_query, sparseconv_export_packed,
+    sparseconv_destroy, sparseconv_last_error, sparseconv_dense_forward
+plus ``Handle`` (owns a packed filter bank and destroys it when collected).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparseconv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                      " (or python sparse_weight_direct_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SC_OK, SC_EINVAL, SC_ESHAPE, SC_ENOMEM, SC_EDEVICE, SC_EUNSUPPORTED = range(6)
+SC_WEIGHTS_DENSE, SC_WEIGHTS_CSR = 0, 1
+SC_PACK_HOST_ONLY = 1
+_STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: "SC_EDEVICE",
+                 5: "SC_EUNSUPPORTED"}
+
+EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_query", "sparseconv_export_packed",
+            "sparseconv_destroy", "sparseconv_last_error", "sparseconv_dense_forward")
+
+
+class sc_weights(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("values", ctypes.c_void_p), ("colidx", ctypes.c_void_p),
+                ("rowptr", ctypes.c_void_p), ("mask", ctypes.c_void_p)]
+
+
+class sc_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("M", "C", "R", "S", "H", "W", "stride", "pad", "E", "F")] + \
+               [("nnz", ctypes.c_int64), ("packed_bytes", ctypes.c_int64), ("device_bytes", ctypes.c_int64)] + \
+               [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
+                                               "lds_bytes", "max_wave_nnz")] + \
+               [("reserved", ctypes.c_int32 * 4)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_vp, _i32, _u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32
+_lib.sparseconv_pack.restype = _i32
+_lib.sparseconv_pack.argtypes = [ctypes.POINTER(sc_weights)] + [_i32] * 8 + [_u32, ctypes.POINTER(_vp)]
+_lib.sparseconv_forward.restype = _i32
+_lib.sparseconv_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
+_lib.sparseconv_query.restype = _i32
+_lib.sparseconv_query.argtypes = [_vp, ctypes.POINTER(sc_info)]
+_lib.sparseconv_export_packed.restype = _i32
+_lib.sparseconv_export_packed.argtypes = [_vp, _vp, _vp, _vp]
+_lib.sparseconv_destroy.restype = None
+_lib.sparseconv_destroy.argtypes = [_vp]
+_lib.sparseconv_last_error.restype = ctypes.c_char_p
+_lib.sparseconv_last_error.argtypes = []
+_lib.sparseconv_dense_forward.restype = _i32
+_lib.sparseconv_dense_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
+
+
+class SparseConvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS_NAMES.get(status, status)}: {sparseconv_last_error()}")
+
+
+def _check(status: int, where: str):
+    if status != SC_OK:
+        raise SparseConvError(status, where)
+
+
+def _np_ptr(a, dtype):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(a, dtype=dtype)
+    return arr, arr.ctypes.data_as(_vp)
+
+
+def _dev_ptr(t):
+    """Device pointer of a contiguous fp32 torch tensor (or a raw int address)."""
+    if isinstance(t, int):
+        return t
+    import torch
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+        raise ValueError("expected a contiguous float32 tensor on the GPU")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def sparseconv_last_error() -> str:
+    return _lib.sparseconv_last_error().decode()
+
+
+def sparseconv_pack(M, C, R, S, H, W, stride, pad, *, values=None, mask=None, colidx=None, rowptr=None,
+                    fmt=None, flags=0) -> int:
+    """Pack weights; returns the raw handle address.  Dense: ``values`` (M*C*R*S fp32) and an
+    optional ``mask`` (u8).  CSR: ``values``, ``colidx``, ``rowptr``."""
+    if fmt is None:
+        fmt = SC_WEIGHTS_CSR if rowptr is not None else SC_WEIGHTS_DENSE
+    v, vp = _np_ptr(values, np.float32)
+    m, mp = _np_ptr(mask, np.uint8)
+    ci, cp = _np_ptr(colidx, np.int32)
+    rp, rpp = _np_ptr(rowptr, np.int32)
+    w = sc_weights(fmt, vp, cp, rpp, mp)
+    out = _vp()
+    st = _lib.sparseconv_pack(ctypes.byref(w), M, C, R, S, H, W, stride, pad, flags, ctypes.byref(out))
+    del v, m, ci, rp
+    _check(st, "sparseconv_pack")
+    return out.value
+
+
+def sparseconv_forward(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
+    _check(_lib.sparseconv_forward(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad,
+                                   _stream_ptr(stream)), "sparseconv_forward")
+
+
+def sparseconv_query(handle: int) -> dict:
+    info = sc_info()
+    _check(_lib.sparseconv_query(handle, ctypes.byref(info)), "sparseconv_query")
+    return info.as_dict()
+
+
+def sparseconv_export_packed(handle: int):
+    """Canonical (rowptr, offsets, values) as numpy arrays."""
+    info = sparseconv_query(handle)
+    rowptr = np.zeros(info["M"] + 1, np.int32)
+    off = np.zeros(info["nnz"], np.uint32)
+    val = np.zeros(info["nnz"], np.float32)
+    _check(_lib.sparseconv_export_packed(handle, rowptr.ctypes.data_as(_vp), off.ctypes.data_as(_vp),
+                                         val.ctypes.data_as(_vp)), "sparseconv_export_packed")
+    return rowptr, off, val
+
+
+def sparseconv_destroy(handle) -> None:
+    _lib.sparseconv_destroy(handle)
+
+
+def sparseconv_dense_forward(w_dense, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
+    _check(_lib.sparseconv_dense_forward(_dev_ptr(w_dense), _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S,
+                                         stride, pad, _stream_ptr(stream)), "sparseconv_dense_forward")
+
+
+def out_size(n_in: int, pad: int, k: int, stride: int) -> int:
+    return (n_in + 2 * pad - k) // stride + 1
+
+
+class Handle:
+    """A packed filter bank for one layer geometry; destroyed with the object."""
+
+    def __init__(self, M, C, R, S, H, W, stride, pad, *, values=None, mask=None, colidx=None,
+                 rowptr=None, flags=0):
+        self.geom = dict(M=M, C=C, R=R, S=S, H=H, W=W, stride=stride, pad=pad)
+        self.E, self.F = out_size(H, pad, R, stride), out_size(W, pad, S, stride)
+        self.ptr = sparseconv_pack(M, C, R, S, H, W, stride, pad, values=values, mask=mask,
+                                   colidx=colidx, rowptr=rowptr, flags=flags)
+
+    @classmethod
+    def from_dense(cls, w: np.ndarray, H: int, W: int, stride: int, pad: int, mask=None, flags=0):
+        M, C, R, S = w.shape
+        return cls(M, C, R, S, H, W, stride, pad, values=w, mask=mask, flags=flags)
+
+    def info(self) -> dict:
+        return sparseconv_query(self.ptr)
+
+    def export(self):
+        return sparseconv_export_packed(self.ptr)
+
+    def forward(self, x, out=None, stream=None):
+        """x: (N, C, H, W) float32 CUDA tensor; returns out (N, M, E, F)."""
+        import torch
+        g = self.geom
+        N = x.shape[0]
+        if out is None:
+            out = torch.empty((N, g["M"], self.E, self.F), dtype=torch.float32, device=x.device)
+        sparseconv_forward(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
+                           g["stride"], g["pad"], stream)
+        return out
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            sparseconv_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dense_forward(w_dense, x, stride, pad, out=None, stream=None):
+    """Dense direct convolution baseline on the GPU (every tap, zeros included)."""
+    import torch
+    M, C, R, S = w_dense.shape
+    N, _, H, W = x.shape
+    E, F = out_size(H, pad, R, stride), out_size(W, pad, S, stride)
+    if out is None:
+        out = torch.empty((N, M, E, F), dtype=torch.float32, device=x.device)
+    sparseconv_dense_forward(w_dense, x, out, N, C, H, W, M, R, S, stride, pad, stream)
+    return out

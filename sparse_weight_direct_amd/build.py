@@ -1,0 +1,36 @@
+"""Build the gfx950 shared library (libsparseconv.so) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libsparseconv.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "pack.cpp", "api.cpp")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed FP32 instructions are disabled for all device code: hipcc would otherwise form
+# v_pk_fma_f32 from scalar float code by itself.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source into libsparseconv.so (always recompiles)."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,406 @@
+// C ABI of the sparse direct convolution library (declared in include/sparseconv.h).
+//
+// sparseconv_pack: validate -> CSR rows ("Escoin", CSR section; columns sorted within a row,
+// values moved with them) -> stretched u32 input offsets c*H*W + r*W + s ("Escoin", weight
+// stretching) kept as the canonical host copy -> wavefront schedule (pack.cpp) -> kernel
+// stream of {LDS-encoded offset, value} per (workgroup group, wavefront, channel chunk,
+// slot) -> one device allocation.  sparseconv_forward validates against the handle and
+// launches asynchronously on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/sparseconv.h"
+#include "plan.h"
+
+namespace {
+
+constexpr uint64_t kMagic = 0x53434f4e56484e44ull;  // live handle
+constexpr uint64_t kDead = 0x444541444841444eull;   // destroyed handle
+
+thread_local std::string g_err;
+
+sc_status fail(sc_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool fail_alloc_hook() {
+  const char* e = std::getenv("SPARSECONV_TEST_FAIL_ALLOC");
+  return e && e[0] == '1';
+}
+
+}  // namespace
+
+struct sc_handle {
+  uint64_t magic;
+  sc::Geom g;
+  sc::Plan p;
+  int64_t nnz;
+  std::vector<int32_t> rowptr;   // canonical CSR row pointers
+  std::vector<uint32_t> off;     // canonical stretched offsets
+  std::vector<float> val;        // canonical values
+  int32_t max_wave_nnz;
+  int device;
+  bool host_only;
+  void* dmem;
+  size_t dbytes;
+  const uint32_t* d_ent;
+  const int32_t* d_seg;
+  const int32_t* d_slot;
+};
+
+namespace {
+
+bool valid_handle(const sc_handle* h) { return h && h->magic == kMagic; }
+
+// CSR rows from the caller's weights, columns ascending within each row.
+sc_status build_csr(const sc_weights* w, int M, long long crs, std::vector<int32_t>& rowptr,
+                    std::vector<int32_t>& col, std::vector<float>& val) {
+  rowptr.assign(M + 1, 0);
+  if (w->format == SC_WEIGHTS_DENSE) {
+    if (!w->values) return fail(SC_EINVAL, "dense weights: values is NULL");
+    if (w->colidx || w->rowptr) return fail(SC_EINVAL, "dense weights: colidx/rowptr must be NULL");
+    long long nnz = 0;
+    for (int m = 0; m < M; m++) {
+      const float* wr = w->values + (long long)m * crs;
+      const uint8_t* mr = w->mask ? w->mask + (long long)m * crs : nullptr;
+      for (long long c = 0; c < crs; c++) nnz += mr ? (mr[c] != 0) : (wr[c] != 0.0f);
+      if (nnz >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "more than 2^31-1 non-zeros");
+      rowptr[m + 1] = (int32_t)nnz;
+    }
+    col.resize(nnz);
+    val.resize(nnz);
+    long long j = 0;
+    for (int m = 0; m < M; m++) {
+      const float* wr = w->values + (long long)m * crs;
+      const uint8_t* mr = w->mask ? w->mask + (long long)m * crs : nullptr;
+      for (long long c = 0; c < crs; c++) {
+        const bool keep = mr ? (mr[c] != 0) : (wr[c] != 0.0f);
+        if (keep) {
+          col[j] = (int32_t)c;
+          val[j] = wr[c];
+          j++;
+        }
+      }
+    }
+    return SC_OK;
+  }
+  if (w->format != SC_WEIGHTS_CSR) return fail(SC_EINVAL, "unknown weights format");
+  if (!w->rowptr) return fail(SC_EINVAL, "CSR weights: rowptr is NULL");
+  if (w->mask) return fail(SC_EINVAL, "CSR weights: mask must be NULL");
+  if (w->rowptr[0] != 0) return fail(SC_EINVAL, "CSR weights: rowptr[0] != 0");
+  for (int m = 0; m < M; m++)
+    if (w->rowptr[m + 1] < w->rowptr[m]) return fail(SC_EINVAL, "CSR weights: rowptr decreases at row " + std::to_string(m));
+  const long long nnz = w->rowptr[M];
+  if (nnz > 0 && (!w->colidx || !w->values)) return fail(SC_EINVAL, "CSR weights: colidx/values is NULL");
+  col.resize(nnz);
+  val.resize(nnz);
+  std::vector<long long> idx;
+  for (int m = 0; m < M; m++) {
+    const int b = w->rowptr[m], e = w->rowptr[m + 1];
+    idx.resize(e - b);
+    for (int j = b; j < e; j++) {
+      if (w->colidx[j] < 0 || w->colidx[j] >= crs)
+        return fail(SC_EINVAL, "CSR weights: colidx out of range at entry " + std::to_string(j));
+      idx[j - b] = j;
+    }
+    std::stable_sort(idx.begin(), idx.end(), [&](long long a, long long c) { return w->colidx[a] < w->colidx[c]; });
+    for (int j = b; j < e; j++) {
+      col[j] = w->colidx[idx[j - b]];
+      val[j] = w->values[idx[j - b]];
+      if (j > b && col[j] == col[j - 1])
+        return fail(SC_EINVAL, "CSR weights: duplicate column " + std::to_string(col[j]) + " in row " + std::to_string(m));
+    }
+    rowptr[m + 1] = e;
+  }
+  return SC_OK;
+}
+
+// Deal rows to (group, wavefront, slot), largest first onto the least-loaded wavefront with
+// a free slot (weights nnz + 1 so empty rows are spread too).  Returns slot_row.
+std::vector<int32_t> schedule_rows(const sc::Geom& g, const sc::Plan& p, const std::vector<int32_t>& rowptr,
+                                   int32_t* max_wave_nnz) {
+  const int M = g.M;
+  const int waves = p.G * sc::kWaves;
+  std::vector<int> order(M);
+  std::iota(order.begin(), order.end(), 0);
+  auto nnz_of = [&](int m) { return rowptr[m + 1] - rowptr[m]; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return nnz_of(a) > nnz_of(b); });
+  std::vector<long long> load(waves, 0), nz(waves, 0);
+  std::vector<int> cnt(waves, 0);
+  std::vector<int32_t> slot_row((size_t)waves * p.OCW, -1);
+  for (int m : order) {
+    int best = -1;
+    for (int w = 0; w < waves; w++)
+      if (cnt[w] < p.OCW && (best < 0 || load[w] < load[best])) best = w;
+    slot_row[(size_t)best * p.OCW + cnt[best]] = m;
+    cnt[best]++;
+    load[best] += nnz_of(m) + 1;
+    nz[best] += nnz_of(m);
+  }
+  *max_wave_nnz = (int32_t)*std::max_element(nz.begin(), nz.end());
+  return slot_row;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparseconv_last_error(void) { return g_err.c_str(); }
+
+sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, int32_t S,
+                          int32_t H, int32_t W, int32_t stride, int32_t pad, uint32_t flags,
+                          sc_handle** out) {
+  g_err.clear();
+  if (!out) return fail(SC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!w) return fail(SC_EINVAL, "weights descriptor is NULL");
+  if (flags & ~SC_PACK_HOST_ONLY) return fail(SC_EINVAL, "unknown pack flag");
+  sc::Geom g;
+  if (!sc::make_geom(M, C, R, S, H, W, stride, pad, &g))
+    return fail(SC_ESHAPE, "invalid layer geometry (dims >= 1, stride >= 1, pad >= 0, output >= 1x1)");
+  const long long crs = (long long)C * R * S;
+  if ((long long)M * crs >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "M*C*R*S >= 2^31");
+  if ((long long)C * H * W >= (1LL << 32)) return fail(SC_EUNSUPPORTED, "C*H*W >= 2^32: offsets do not fit u32");
+  if (fail_alloc_hook()) return fail(SC_ENOMEM, "allocation failure (injected by SPARSECONV_TEST_FAIL_ALLOC)");
+  sc_handle* h = nullptr;
+  try {
+    std::vector<int32_t> rowptr, col;
+    std::vector<float> val;
+    sc_status s = build_csr(w, M, crs, rowptr, col, val);
+    if (s != SC_OK) return s;
+    const long long nnz = (long long)col.size();
+    sc::Plan p = sc::choose_plan(g, rowptr);
+    if (p.K == 0) return fail(SC_EUNSUPPORTED, "input rows too wide for the LDS tile");
+
+    h = new sc_handle();
+    h->magic = kMagic;
+    h->g = g;
+    h->p = p;
+    h->nnz = nnz;
+    h->host_only = (flags & SC_PACK_HOST_ONLY) != 0;
+    h->dmem = nullptr;
+    h->dbytes = 0;
+    h->off.resize(nnz);
+    for (long long j = 0; j < nnz; j++) {
+      const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
+      h->off[j] = (uint32_t)(((long long)c * H + r) * W + sx);
+    }
+    h->val = val;
+    h->rowptr = rowptr;
+
+    // Kernel stream, ordered (group, wavefront, chunk, slot) so that a wavefront's
+    // non-zeros for one chunk are contiguous.
+    std::vector<int32_t> slot_row = schedule_rows(g, p, rowptr, &h->max_wave_nnz);
+    const int waves = p.G * sc::kWaves;
+    const size_t nslots = (size_t)waves * p.OCW;
+    std::vector<uint32_t> ent(2 * (size_t)nnz);
+    std::vector<int32_t> seg(2 * nslots * p.nch, 0);
+    // per row: first entry of each chunk
+    std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
+    for (int m = 0; m < M; m++) {
+      int j = rowptr[m];
+      for (int k = 0; k <= p.nch; k++) {
+        while (j < rowptr[m + 1] && col[j] / (R * S) < k * p.Cc) j++;
+        chunk_start[(size_t)m * (p.nch + 1) + k] = j;
+      }
+      chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
+    }
+    size_t pos = 0;
+    for (int wv = 0; wv < waves; wv++)
+      for (int k = 0; k < p.nch; k++)
+        for (int o = 0; o < p.OCW; o++) {
+          const size_t slot = (size_t)wv * p.OCW + o;
+          const int m = slot_row[slot];
+          const size_t sidx = 2 * (slot * p.nch + k);
+          seg[sidx] = (int32_t)pos;
+          if (m >= 0) {
+            const int b = chunk_start[(size_t)m * (p.nch + 1) + k];
+            const int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
+            for (int j = b; j < e; j++) {
+              const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
+              const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PH +
+                                              (r / stride) * g.Pp + sx / stride);
+              uint32_t vbits;
+              std::memcpy(&vbits, &val[j], 4);
+              ent[2 * pos] = enc;
+              ent[2 * pos + 1] = vbits;
+              pos++;
+            }
+          }
+          seg[sidx + 1] = (int32_t)pos;
+        }
+
+    if (!h->host_only) {
+      if (hipGetDevice(&h->device) != hipSuccess) {
+        sparseconv_destroy(h);
+        return fail(SC_EDEVICE, "no HIP device available");
+      }
+      auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+      const size_t b_ent = al(std::max<size_t>(ent.size() * 4, 8));
+      const size_t b_seg = al(seg.size() * 4);
+      const size_t b_slot = al(slot_row.size() * 4);
+      h->dbytes = b_ent + b_seg + b_slot;
+      if (hipMalloc(&h->dmem, h->dbytes) != hipSuccess) {
+        h->dmem = nullptr;
+        sparseconv_destroy(h);
+        return fail(SC_ENOMEM, "hipMalloc of the packed filter bank failed");
+      }
+      char* base = static_cast<char*>(h->dmem);
+      h->d_ent = reinterpret_cast<const uint32_t*>(base);
+      h->d_seg = reinterpret_cast<const int32_t*>(base + b_ent);
+      h->d_slot = reinterpret_cast<const int32_t*>(base + b_ent + b_seg);
+      hipError_t e1 = hipMemcpy(base, ent.data(), ent.size() * 4, hipMemcpyHostToDevice);
+      hipError_t e2 = hipMemcpy(base + b_ent, seg.data(), seg.size() * 4, hipMemcpyHostToDevice);
+      hipError_t e3 = hipMemcpy(base + b_ent + b_seg, slot_row.data(), slot_row.size() * 4, hipMemcpyHostToDevice);
+      if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+        sparseconv_destroy(h);
+        return fail(SC_EDEVICE, "upload of the packed filter bank failed");
+      }
+    }
+    *out = h;
+    return SC_OK;
+  } catch (const std::bad_alloc&) {
+    if (h) sparseconv_destroy(h);
+    return fail(SC_ENOMEM, "host allocation failed");
+  } catch (...) {
+    if (h) sparseconv_destroy(h);
+    return fail(SC_EINVAL, "unexpected error while packing");
+  }
+}
+
+sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!info) return fail(SC_EINVAL, "info is NULL");
+  std::memset(info, 0, sizeof(*info));
+  info->M = h->g.M; info->C = h->g.C; info->R = h->g.R; info->S = h->g.S;
+  info->H = h->g.H; info->W = h->g.W; info->stride = h->g.st; info->pad = h->g.pad;
+  info->E = h->g.E; info->F = h->g.F;
+  info->nnz = h->nnz;
+  info->packed_bytes = (2 * h->nnz + h->g.M + 1) * 4;
+  info->device_bytes = (int64_t)h->dbytes;
+  info->tile_pixels = 64 * h->p.K;
+  info->rows_per_wave = h->p.OCW;
+  info->row_groups = h->p.G;
+  info->chunk_channels = h->p.Cc;
+  info->lds_bytes = h->p.lds_bytes;
+  info->max_wave_nnz = h->max_wave_nnz;
+  return SC_OK;
+}
+
+sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t* offsets, float* values) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (rowptr) std::memcpy(rowptr, h->rowptr.data(), h->rowptr.size() * 4);
+  if (offsets && h->nnz) std::memcpy(offsets, h->off.data(), h->off.size() * 4);
+  if (values && h->nnz) std::memcpy(values, h->val.data(), h->val.size() * 4);
+  return SC_OK;
+}
+
+void sparseconv_destroy(sc_handle* h) {
+  if (!h || h->magic != kMagic) return;
+  if (h->dmem) (void)hipFree(h->dmem);
+  h->magic = kDead;
+  delete h;
+}
+
+}  // extern "C"
+
+namespace {
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+sc_status check_io(const sc::Geom& g, const float* in, const float* outp, int N) {
+  const long long nin = (long long)N * g.C * g.H * g.W;
+  const long long nout = (long long)N * g.M * g.E * g.F;
+  if (nin >= (1LL << 31) || nout >= (1LL << 31))
+    return fail(SC_EUNSUPPORTED, "N*C*H*W or N*M*E*F >= 2^31 elements");
+  if ((long long)N * g.HYp * g.Pp >= (1LL << 31) - (1LL << 12))
+    return fail(SC_EUNSUPPORTED, "padded batch extent >= 2^31");
+  if (!in || !outp) return fail(SC_EINVAL, "input or output is NULL");
+  if (ranges_overlap(in, nin * 4, outp, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
+  return SC_OK;
+}
+
+sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float* outp, int N) {
+  sc::KArgs a{};
+  a.x = in; a.y = outp;
+  a.N = N; a.C = g.C; a.H = g.H; a.W = g.W; a.M = g.M; a.E = g.E; a.F = g.F;
+  a.R = g.R; a.S = g.S; a.st = g.st; a.pad = g.pad;
+  a.Pp = g.Pp; a.HYp = g.HYp; a.img_ext = g.HYp * g.Pp;
+  a.NRmax = p.NRmax; a.PH = p.PH; a.CHS = p.CHS; a.Cc = p.Cc; a.nch = p.nch; a.G = p.G;
+  a.lds_floats = p.lds_floats;
+  a.ext_total = (long long)N * a.img_ext;
+  return a;
+}
+
+int num_blocks(const sc::Plan& p, long long ext_total) {
+  const long long tiles = (ext_total + 64LL * p.K - 1) / (64LL * p.K);
+  return (int)(tiles * p.G);
+}
+
+}  // namespace
+
+extern "C" {
+
+sc_status sparseconv_forward(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C,
+                             int32_t H, int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride,
+                             int32_t pad, void* hip_stream) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (h->host_only) return fail(SC_EINVAL, "handle was packed with SC_PACK_HOST_ONLY");
+  const sc::Geom& g = h->g;
+  if (N < 0) return fail(SC_ESHAPE, "N < 0");
+  if (C != g.C || H != g.H || W != g.W || M != g.M || R != g.R || S != g.S || stride != g.st || pad != g.pad)
+    return fail(SC_ESHAPE, "forward dims differ from the packed handle");
+  if (N == 0) return SC_OK;
+  sc_status s = check_io(g, input, output, N);
+  if (s != SC_OK) return s;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+  sc::KArgs a = make_args(g, h->p, input, output, N);
+  a.ent = h->d_ent;
+  a.seg = h->d_seg;
+  a.slot_row = h->d_slot;
+  const int e = sc::launch_sparse(h->p, a, hip_stream, num_blocks(h->p, a.ext_total));
+  if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
+  return SC_OK;
+}
+
+sc_status sparseconv_dense_forward(const float* w_dense, const float* input, float* output, int32_t N,
+                                   int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                                   int32_t stride, int32_t pad, void* hip_stream) {
+  g_err.clear();
+  sc::Geom g;
+  if (N < 0 || !sc::make_geom(M, C, R, S, H, W, stride, pad, &g)) return fail(SC_ESHAPE, "invalid layer geometry");
+  if (!w_dense) return fail(SC_EINVAL, "dense weights are NULL");
+  if (N == 0) return SC_OK;
+  sc_status s = check_io(g, input, output, N);
+  if (s != SC_OK) return s;
+  const long long nw = (long long)M * C * R * S;
+  if (ranges_overlap(w_dense, nw * 4, output, (long long)N * M * g.E * g.F * 4))
+    return fail(SC_EINVAL, "weights and output overlap");
+  sc::Plan p = sc::choose_plan(g, {});
+  if (p.K == 0) return fail(SC_EUNSUPPORTED, "input rows too wide for the LDS tile");
+  sc::KArgs a = make_args(g, p, input, output, N);
+  a.wd = w_dense;
+  const int e = sc::launch_dense(p, a, hip_stream, num_blocks(p, a.ext_total));
+  if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
+  return SC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and compare with
+the oracle element by element (|gpu - oracle| <= 1e-5 * sum|w*x|, exact zero where that
+sum is zero)."""
+import numpy as np
+import torch
+
+import oracle
+import sparse_weight_direct_amd as sc
+
+REL_TOL = 1e-5
+
+
+def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None):
+    N, C, H, W = x.shape
+    M, _, R, S = w.shape
+    if handle is None:
+        handle = sc.Handle(M, C, R, S, H, W, stride, pad, values=w, mask=mask)
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out = torch.full((N, M, handle.E, handle.F), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
+    handle.forward(xd, out, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), handle
+
+
+def gpu_dense(x, w_masked, stride, pad):
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    wd = torch.from_numpy(np.ascontiguousarray(w_masked)).cuda()
+    N, C, H, W = x.shape
+    M, _, R, S = w_masked.shape
+    E, F = sc.out_size(H, pad, R, stride), sc.out_size(W, pad, S, stride)
+    out = torch.full((N, M, E, F), float("nan"), dtype=torch.float32, device="cuda")
+    sc.dense_forward(wd, xd, stride, pad, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_parity(y_gpu, y64, mag, what=""):
+    assert y_gpu.shape == y64.shape, (y_gpu.shape, y64.shape)
+    assert np.isfinite(y_gpu).all(), f"{what}: {int((~np.isfinite(y_gpu)).sum())} outputs not written / not finite"
+    ok = oracle.within_tolerance(y_gpu, y64, mag, REL_TOL)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} outside tolerance; first at {i}: gpu={y_gpu[i]!r} "
+                             f"oracle={y64[i]!r} mag={mag[i]!r}")

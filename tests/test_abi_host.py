@@ -1,0 +1,174 @@
+"""The C-ABI library on the host (CPU only, no GPU calls): symbols, packing, validation.
+
+Packing with SC_PACK_HOST_ONLY runs the whole host part of the packer (CSR, stretched
+offsets, schedule, kernel encoding) without a device, so the canonical packed form can be
+checked bit-exactly against the oracle's independent CSR builder and stretch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_weight_direct_amd as sc
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sparseconv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparseconv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) == 7
+    lib = ctypes.CDLL(sc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(sc.EXPORTED) == names
+    for n in names:
+        assert callable(getattr(sc, n))
+
+
+def _pack_host(d, L, **kw):
+    return sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                     flags=sc.SC_PACK_HOST_ONLY, **kw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "late", "imb95", "first11", "pw1x1"])
+def test_canonical_export_bit_exact_vs_oracle(name):
+    d = workloads.make(name, n_override=1)
+    L = d["layer"]
+    h = _pack_host(d, L)
+    rowptr, off, val = h.export()
+    o_rowptr, o_col, o_val = oracle.csr_from_dense(d["w"], d["mask"])
+    o_off = oracle.stretch(o_col, L.C, L.R, L.S, L.H, L.W)
+    np.testing.assert_array_equal(rowptr, o_rowptr)
+    np.testing.assert_array_equal(off, o_off)
+    np.testing.assert_array_equal(val.view(np.uint32), o_val.view(np.uint32))
+    info = h.info()
+    nnz = int(d["mask"].sum())
+    assert info["nnz"] == nnz
+    assert info["packed_bytes"] == (2 * nnz + L.M + 1) * 4
+    assert (info["E"], info["F"]) == (L.E, L.F)
+
+
+def test_dense_mask_and_csr_inputs_give_identical_handles():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h1 = _pack_host(d, L)
+    rowptr, col, val = oracle.csr_from_dense(d["w"], d["mask"])
+    # shuffle columns within rows: the packer must sort them, moving values along
+    rng = np.random.default_rng(0)
+    col_s, val_s = col.copy(), val.copy()
+    for m in range(L.M):
+        b, e = rowptr[m], rowptr[m + 1]
+        perm = rng.permutation(e - b) + b
+        col_s[b:e], val_s[b:e] = col[perm], val[perm]
+    h2 = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=val_s, colidx=col_s, rowptr=rowptr,
+                   flags=sc.SC_PACK_HOST_ONLY)
+    for a, b in zip(h1.export(), h2.export()):
+        np.testing.assert_array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+    assert h1.info() == h2.info()
+
+
+def test_no_mask_storage_rule_and_explicit_zeros():
+    w = np.array([0.0, 1.5, -0.0, np.nan, 2.0, 0.0, 0.0, 3.0], np.float32).reshape(2, 1, 2, 2)
+    h = sc.Handle.from_dense(w, 3, 3, 1, 0, flags=sc.SC_PACK_HOST_ONLY)
+    rowptr, off, val = h.export()
+    assert rowptr.tolist() == [0, 2, 4]
+    # columns 1, 3 | 0, 3 -> (r, s) = (0,1), (1,1) | (0,0), (1,1) with W = 3
+    assert off.tolist() == [1, 4, 0, 4]
+    assert val[0] == 1.5 and np.isnan(val[1]) and val[2] == 2.0 and val[3] == 3.0
+    mask = np.array([0, 1, 1, 0, 1, 0, 0, 0], np.uint8).reshape(2, 1, 2, 2)
+    h = sc.Handle.from_dense(w, 3, 3, 1, 0, mask=mask, flags=sc.SC_PACK_HOST_ONLY)
+    rowptr, off, val = h.export()
+    assert rowptr.tolist() == [0, 2, 3]
+    assert np.signbit(val[1]) and val[1] == 0.0
+
+
+def _status(fn):
+    try:
+        fn()
+    except sc.SparseConvError as e:
+        return e.status, str(e)
+    return sc.SC_OK, ""
+
+
+@pytest.mark.parametrize("bad,expect", [
+    ("rowptr_decreasing", sc.SC_EINVAL), ("rowptr0_nonzero", sc.SC_EINVAL), ("col_out_of_range", sc.SC_EINVAL),
+    ("col_negative", sc.SC_EINVAL), ("duplicate", sc.SC_EINVAL),
+])
+def test_invalid_csr_rejected(bad, expect):
+    M, C, R, S = 2, 2, 3, 3
+    rowptr = np.array([0, 2, 4], np.int32)
+    col = np.array([0, 5, 3, 17], np.int32)
+    val = np.ones(4, np.float32)
+    if bad == "rowptr_decreasing":
+        rowptr = np.array([0, 3, 2], np.int32)
+    elif bad == "rowptr0_nonzero":
+        rowptr = np.array([1, 2, 4], np.int32)
+    elif bad == "col_out_of_range":
+        col[3] = C * R * S
+    elif bad == "col_negative":
+        col[0] = -1
+    elif bad == "duplicate":
+        col[1] = 0
+    st, msg = _status(lambda: sc.sparseconv_pack(M, C, R, S, 5, 5, 1, 1, values=val, colidx=col, rowptr=rowptr,
+                                                 flags=sc.SC_PACK_HOST_ONLY))
+    assert st == expect and "CSR" in msg
+
+
+def test_shape_and_limit_errors():
+    w = np.ones((2, 1, 3, 3), np.float32)
+    st, _ = _status(lambda: sc.sparseconv_pack(0, 1, 3, 3, 5, 5, 1, 1, values=w, flags=sc.SC_PACK_HOST_ONLY))
+    assert st == sc.SC_ESHAPE
+    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 2, 2, 1, 0, values=w, flags=sc.SC_PACK_HOST_ONLY))
+    assert st == sc.SC_ESHAPE  # output would be empty
+    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 0, 1, values=w, flags=sc.SC_PACK_HOST_ONLY))
+    assert st == sc.SC_ESHAPE  # stride 0
+    big = np.ones((1, 1, 1, 1), np.float32)
+    st, msg = _status(lambda: sc.sparseconv_pack(1, 1, 1, 1, 65536, 65536, 1, 0, values=big,
+                                                 flags=sc.SC_PACK_HOST_ONLY))
+    assert st == sc.SC_EUNSUPPORTED and "2^32" in msg
+    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 1, 1, values=w, flags=8))
+    assert st == sc.SC_EINVAL
+
+
+def test_forward_validation_without_device():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = _pack_host(d, L)
+    st, msg = _status(lambda: sc.sparseconv_forward(h.ptr, 1 << 20, 1 << 24, 1, L.C, L.H, L.W, L.M, L.R, L.S,
+                                                    L.stride, L.pad, stream=0))
+    assert st == sc.SC_EINVAL and "HOST_ONLY" in msg
+    st, _ = _status(lambda: sc.sparseconv_forward(0, 1 << 20, 1 << 24, 1, L.C, L.H, L.W, L.M, L.R, L.S,
+                                                  L.stride, L.pad, stream=0))
+    assert st == sc.SC_EINVAL
+    assert sc.sparseconv_last_error() != ""
+    sc.sparseconv_destroy(None)  # no-op
+
+
+def test_injected_allocation_failure(monkeypatch):
+    d = workloads.make("tiny")
+    L = d["layer"]
+    monkeypatch.setenv("SPARSECONV_TEST_FAIL_ALLOC", "1")
+    st, msg = _status(lambda: _pack_host(d, L))
+    assert st == sc.SC_ENOMEM and "injected" in msg
+
+
+@pytest.mark.parametrize("name", ["imb80", "imb95", "imb99"])
+def test_schedule_balances_wavefronts_by_nnz(name):
+    d = workloads.make(name, n_override=1)
+    L = d["layer"]
+    info = _pack_host(d, L).info()
+    nnz = int(d["mask"].sum())
+    waves = info["row_groups"] * 8
+    rows = d["mask"].reshape(L.M, -1).sum(1)
+    # largest-first greedy: the heaviest wavefront exceeds the mean by less than one row
+    assert info["max_wave_nnz"] <= nnz / waves + rows.max()
+    assert info["max_wave_nnz"] <= 1.15 * nnz / waves

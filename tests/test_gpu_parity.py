@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bar: |gpu - oracle| <= 1e-5 * sum|w*x| per output element (fp32 accumulation in any order
+stays well inside it; see the tolerance derivation in the design notes), exact +0 where
+no term contributes, and bit-exact results for the closed forms (one non-zero per output:
+the GPU's fma(w, x, 0) and the oracle's rounded double product are the same fp32 value)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_weight_direct_amd as sc
+import workloads
+from gpu_util import assert_parity, gpu_dense, gpu_sparse
+
+pytestmark = pytest.mark.gpu
+
+FULL_LAYERS = ["tiny", "mid", "late", "first11", "pw1x1"]
+
+
+@pytest.mark.parametrize("name", FULL_LAYERS)
+def test_layer_full_parity(name):
+    d = workloads.make(name)
+    L = d["layer"]
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert_parity(y, r["y64"], r["mag"], name)
+    # packed offsets exported by the device handle are the canonical ones, bit for bit
+    rowptr, off, val = h.export()
+    np.testing.assert_array_equal(rowptr, r["rowptr"])
+    np.testing.assert_array_equal(off, r["offsets"])
+    np.testing.assert_array_equal(val.view(np.uint32), r["values"].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["imb80", "imb90", "imb95", "imb99"])
+def test_imbalance_sweep_sampled_planes(name):
+    """Full-size 112x112 batch-8 layers in the benchmark's launch configuration; the oracle
+    recomputes a sample of (n, m) planes one by one: the heaviest and lightest channels,
+    empty channels and random ones, in the first and last image."""
+    d = workloads.make(name)
+    L = d["layer"]
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert np.isfinite(y).all()
+    rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+    rows = np.diff(rowptr)
+    rng = np.random.default_rng(L.seed)
+    ms = {int(rows.argmax()), int(rows.argmin())} | set(int(m) for m in rng.choice(L.M, 6, replace=False))
+    ms |= set(int(m) for m in np.flatnonzero(rows == 0)[:2])
+    planes = sorted({n * L.M + m for n in (0, L.N - 1, int(rng.integers(L.N))) for m in ms})
+    y64, mag = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, L.M, L.R, L.S, L.stride, L.pad, planes)
+    got = np.stack([y[p // L.M, p % L.M] for p in planes])
+    assert_parity(got, y64, mag, name)
+    # empty channels are exact +0
+    for m in np.flatnonzero(rows == 0):
+        assert np.all(y[:, m] == 0) and not np.signbit(y[:, m]).any()
+
+
+def _tiny_cases(count, seed0):
+    rng = np.random.default_rng(seed0)
+    keeps = [0.9, 0.5, 0.1, 0.0, 1.0]
+    out = []
+    for i in range(count):
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        stride, pad = int(rng.integers(1, 5)), int(rng.integers(0, 3))
+        H = int(rng.integers(max(1, R - 2 * pad), 40))
+        W = int(rng.integers(max(1, S - 2 * pad), 40))
+        out.append(dict(N=int(rng.integers(1, 4)), C=int(rng.integers(1, 40)), H=H, W=W,
+                        M=int(rng.integers(1, 70)), R=R, S=S, stride=stride, pad=pad, keep=keeps[i % 5],
+                        seed=5000 + i))
+    return out
+
+
+@pytest.mark.parametrize("c", _tiny_cases(40, 3), ids=lambda c: "N{N}C{C}H{H}W{W}M{M}R{R}S{S}st{stride}p{pad}k{keep}".format(**c))
+def test_random_shapes(c):
+    d = workloads.make_custom(c["N"], c["C"], c["H"], c["W"], c["M"], c["R"], c["S"], c["stride"], c["pad"],
+                              c["keep"], c["seed"])
+    r = oracle.reference(d["x"], d["w"], d["mask"], c["stride"], c["pad"])
+    y, _ = gpu_sparse(d["x"], d["w"], d["mask"], c["stride"], c["pad"])
+    assert_parity(y, r["y64"], r["mag"], str(c))
+
+
+@pytest.mark.parametrize("plan", ["K=1,OCW=1", "K=2,OCW=4", "K=8,OCW=16", "K=4,OCW=2,CC=3"])
+def test_every_plan_shape(plan, monkeypatch):
+    """The same layer through several launch plans (positions per lane, slots per wave,
+    channel chunk), including chunking that leaves a ragged last chunk."""
+    monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make_custom(3, 20, 23, 37, 50, 3, 3, 1, 1, 0.15, 77)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    assert_parity(y, r["y64"], r["mag"], plan)
+
+
+@pytest.mark.parametrize("R,S,stride,pad,H,W", [(3, 3, 1, 1, 30, 41), (11, 11, 4, 0, 67, 59), (5, 3, 2, 2, 17, 23),
+                                                (1, 1, 1, 0, 7, 7)])
+def test_single_nonzero_bit_exact(R, S, stride, pad, H, W):
+    rng = np.random.default_rng(R * 31 + W)
+    N, C, M = 2, 5, 6
+    x = rng.uniform(-1, 1, (N, C, H, W)).astype(np.float32)
+    w = np.zeros((M, C, R, S), np.float32)
+    w[2, 4, R - 1, 0] = np.float32(0.8125)
+    w[5, 0, 0, S - 1] = np.float32(-1.3)
+    r = oracle.reference(x, w, None, stride, pad)
+    y, _ = gpu_sparse(x, w, None, stride, pad)
+    np.testing.assert_array_equal(y.view(np.uint32), r["y"].view(np.uint32))
+
+
+def test_delta_kernel_identity_bit_exact():
+    d = workloads.make_custom(2, 24, 31, 29, 24, 3, 3, 1, 1, 0.0, 8)
+    w = np.zeros((24, 24, 3, 3), np.float32)
+    for m in range(24):
+        w[m, m, 1, 1] = 1.0
+    y, _ = gpu_sparse(d["x"], w, None, 1, 1)
+    np.testing.assert_array_equal(y.view(np.uint32), d["x"].view(np.uint32))
+
+
+def test_all_zero_weights_and_empty_rows():
+    d = workloads.make_custom(2, 8, 12, 12, 40, 3, 3, 1, 1, 0.2, 21)
+    mask = d["mask"].copy()
+    mask[::3] = 0
+    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    assert np.all(y[:, ::3] == 0) and not np.signbit(y[:, ::3]).any()
+    y0, _ = gpu_sparse(d["x"], d["w"], np.zeros_like(mask), 1, 1)
+    assert np.all(y0 == 0) and not np.signbit(y0).any()
+
+
+def test_skewed_rows_one_dense_channel():
+    """One fully dense output channel among nearly empty ones (worst case for balance)."""
+    d = workloads.make_custom(2, 64, 20, 20, 32, 3, 3, 1, 1, 0.02, 31)
+    mask = d["mask"].copy()
+    mask[7] = 1
+    r = oracle.reference(d["x"], d["w"], mask, 1, 1)
+    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    assert_parity(y, r["y64"], r["mag"], "skewed")
+
+
+def test_csr_input_path_and_determinism():
+    d = workloads.make("mid")
+    L = d["layer"]
+    rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=value, colidx=colidx, rowptr=rowptr)
+    y1, _ = gpu_sparse(d["x"], d["w"], None, L.stride, L.pad, handle=h)
+    y2, _ = gpu_sparse(d["x"], d["w"], None, L.stride, L.pad, handle=h)
+    np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert_parity(y1, r["y64"], r["mag"], "csr")
+
+
+def test_batch_sizes_share_one_handle():
+    """N is a forward-time argument: one handle, several batch sizes, incl. N = 0."""
+    d = workloads.make("late")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    for n in (1, 3, 32):
+        x = d["x"][:n]
+        r = oracle.reference(x, d["w"], d["mask"], L.stride, L.pad)
+        y, _ = gpu_sparse(x, d["w"], d["mask"], L.stride, L.pad, handle=h)
+        assert_parity(y, r["y64"], r["mag"], f"late N={n}")
+    xd = torch.zeros((0, L.C, L.H, L.W), device="cuda")
+    out = torch.zeros((0, L.M, L.E, L.F), device="cuda")
+    h.forward(xd, out)
+
+
+def test_forward_rejects_mismatched_dims_and_overlap():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    x = torch.zeros((1, L.C, L.H, L.W), device="cuda")
+    y = torch.zeros((1, L.M, L.E, L.F), device="cuda")
+    with pytest.raises(sc.SparseConvError) as e:
+        sc.sparseconv_forward(h.ptr, x, y, 1, L.C, L.H + 1, L.W, L.M, L.R, L.S, L.stride, L.pad)
+    assert e.value.status == sc.SC_ESHAPE
+    big = torch.zeros(L.M * L.E * L.F + L.C * L.H * L.W, device="cuda")
+    with pytest.raises(sc.SparseConvError) as e:
+        sc.sparseconv_forward(h.ptr, big.data_ptr(), big.data_ptr() + 64, 1, L.C, L.H, L.W, L.M, L.R, L.S,
+                              L.stride, L.pad)
+    assert e.value.status == sc.SC_EINVAL
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "first11"])
+def test_dense_baseline_parity(name):
+    d = workloads.make(name, n_override=2)
+    L = d["layer"]
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    y = gpu_dense(d["x"], d["w_masked"], L.stride, L.pad)
+    assert_parity(y, r["y64"], r["mag"], "dense " + name)
+
+
+def test_side_stream():
+    d = workloads.make("mid")
+    L = d["layer"]
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, stream=s)
+    assert_parity(y, r["y64"], r["mag"], "stream")
