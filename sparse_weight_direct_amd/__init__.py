@@ -17,6 +17,11 @@ import os
 
 import numpy as np
 
+# torch first: it ships its own HIP runtime under the same soname (libamdhip64.so.7) as the
+# system one this library links; loading torch first makes both use torch's runtime, so
+# device pointers and streams from torch are valid here.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsparseconv.so")
 
