@@ -153,10 +153,10 @@ def main():
 
     extra = {}
     if not args.no_dense:
-        wd = torch.from_numpy(d["w_masked"]).to(dev)
+        hd = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w_masked"], flags=sc.SC_PACK_ALL_TAPS)
 
         def dense_step(i):
-            sc.dense_forward(wd, xs[i], st, pad, out=ys[i], stream=stream)
+            hd.forward(xs[i], ys[i], stream=stream)
 
         dsteps = max(10, args.steps // 10)
         log(f"[bench] dense direct baseline: warmup 2, timed {dsteps}")

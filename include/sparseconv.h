@@ -58,6 +58,10 @@ typedef enum {
 /* Pack flags. */
 #define SC_PACK_HOST_ONLY 1u /* build the packed form on the host only: query and export
                                 work, forward returns SC_EINVAL.  Needs no GPU. */
+#define SC_PACK_ALL_TAPS 2u  /* DENSE weights only: store every filter position, zeros
+                                included (mask ignored).  A forward on such a handle is the
+                                dense direct convolution with the same kernel: the on-GPU
+                                baseline, counterpart of Tuteja et al., Sec. 4 Eq. (5)/(6). */
 
 typedef struct {
   int32_t format;          /* sc_weights_format */
@@ -84,7 +88,9 @@ typedef struct {
   int32_t chunk_channels;/* launch plan: input channels staged in LDS at a time */
   int32_t lds_bytes;     /* launch plan: dynamic LDS per workgroup */
   int32_t max_wave_nnz;  /* largest non-zero count given to one wavefront */
-  int32_t reserved[4];
+  int32_t waves_per_group;  /* launch plan: wavefronts per workgroup */
+  int32_t pipeline_depth;   /* launch plan: LDS chunk buffers (depth-1 chunks in flight) */
+  int32_t reserved[2];
 } sc_info;
 
 /*
@@ -93,7 +99,7 @@ typedef struct {
  *   M,C,R,S    output channels, input channels, filter rows, filter columns (all >= 1).
  *   H,W        unpadded input height and width the layer will be applied to (>= 1).
  *   stride>=1, pad>=0; E and F from the formula above must be >= 1.
- *   flags      0 or SC_PACK_HOST_ONLY.
+ *   flags      0, or SC_PACK_HOST_ONLY and/or SC_PACK_ALL_TAPS.
  *   out        receives the new handle (set to NULL on failure).
  * Steps: validate -> CSR (columns sorted within each row, values moved with them) ->
  * stretched offsets -> wavefront schedule balanced by non-zero count -> upload.
@@ -143,20 +149,6 @@ void sparseconv_destroy(sc_handle* h);
 /* Message of the calling thread's last failure ("" if none).  Valid until that thread's
  * next call into the library. */
 const char* sparseconv_last_error(void);
-
-/*
- * Dense direct convolution with the same tiling and staging, over every filter tap
- * including zeros: the on-GPU baseline the sparse path is measured against (dense
- * counterpart of Tuteja et al., Sec. 4 Eq. (5)/(6)).  Same conventions as forward:
- *   w_dense  device, M*C*R*S fp32 (m,c,r,s) row-major.
- *   input    device, N*C*H*W;  output device, N*M*E*F (overwritten, must not overlap).
- * Errors: SC_EINVAL (null pointers, overlap), SC_ESHAPE, SC_EUNSUPPORTED (limits as
- * forward), SC_EDEVICE.
- */
-sc_status sparseconv_dense_forward(const float* w_dense, const float* input, float* output,
-                                   int32_t N, int32_t C, int32_t H, int32_t W, int32_t M,
-                                   int32_t R, int32_t S, int32_t stride, int32_t pad,
-                                   void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -7,8 +7,9 @@ import fails, and the forward pass needs a ROCm device.
 
 The functions keep the C names:
     sparseconv_pack, sparseconv_forward, sparseconv_query, sparseconv_export_packed,
-    sparseconv_destroy, sparseconv_last_error, sparseconv_dense_forward
-plus ``Handle`` (owns a packed filter bank and destroys it when collected).
+    sparseconv_destroy, sparseconv_last_error
+plus ``Handle`` (owns a packed filter bank and destroys it when collected).  The dense
+direct baseline is a Handle packed with SC_PACK_ALL_TAPS (every filter tap stored).
 """
 from __future__ import annotations
 
@@ -34,11 +35,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 SC_OK, SC_EINVAL, SC_ESHAPE, SC_ENOMEM, SC_EDEVICE, SC_EUNSUPPORTED = range(6)
 SC_WEIGHTS_DENSE, SC_WEIGHTS_CSR = 0, 1
 SC_PACK_HOST_ONLY = 1
+SC_PACK_ALL_TAPS = 2
 _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: "SC_EDEVICE",
                  5: "SC_EUNSUPPORTED"}
 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_query", "sparseconv_export_packed",
-            "sparseconv_destroy", "sparseconv_last_error", "sparseconv_dense_forward")
+            "sparseconv_destroy", "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -50,8 +52,9 @@ class sc_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("M", "C", "R", "S", "H", "W", "stride", "pad", "E", "F")] + \
                [("nnz", ctypes.c_int64), ("packed_bytes", ctypes.c_int64), ("device_bytes", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
-                                               "lds_bytes", "max_wave_nnz")] + \
-               [("reserved", ctypes.c_int32 * 4)]
+                                               "lds_bytes", "max_wave_nnz", "waves_per_group",
+                                               "pipeline_depth")] + \
+               [("reserved", ctypes.c_int32 * 2)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
@@ -70,8 +73,6 @@ _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
 _lib.sparseconv_last_error.argtypes = []
-_lib.sparseconv_dense_forward.restype = _i32
-_lib.sparseconv_dense_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
 
 
 class SparseConvError(RuntimeError):
@@ -159,11 +160,6 @@ def sparseconv_destroy(handle) -> None:
     _lib.sparseconv_destroy(handle)
 
 
-def sparseconv_dense_forward(w_dense, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
-    _check(_lib.sparseconv_dense_forward(_dev_ptr(w_dense), _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S,
-                                         stride, pad, _stream_ptr(stream)), "sparseconv_dense_forward")
-
-
 def out_size(n_in: int, pad: int, k: int, stride: int) -> int:
     return (n_in + 2 * pad - k) // stride + 1
 
@@ -210,15 +206,3 @@ class Handle:
             self.close()
         except Exception:
             pass
-
-
-def dense_forward(w_dense, x, stride, pad, out=None, stream=None):
-    """Dense direct convolution baseline on the GPU (every tap, zeros included)."""
-    import torch
-    M, C, R, S = w_dense.shape
-    N, _, H, W = x.shape
-    E, F = out_size(H, pad, R, stride), out_size(W, pad, S, stride)
-    if out is None:
-        out = torch.empty((N, M, E, F), dtype=torch.float32, device=x.device)
-    sparseconv_dense_forward(w_dense, x, out, N, C, H, W, M, R, S, stride, pad, stream)
-    return out

@@ -62,9 +62,10 @@ namespace {
 bool valid_handle(const sc_handle* h) { return h && h->magic == kMagic; }
 
 // CSR rows from the caller's weights, columns ascending within each row.
-sc_status build_csr(const sc_weights* w, int M, long long crs, std::vector<int32_t>& rowptr,
+sc_status build_csr(const sc_weights* w, int M, long long crs, bool all_taps, std::vector<int32_t>& rowptr,
                     std::vector<int32_t>& col, std::vector<float>& val) {
   rowptr.assign(M + 1, 0);
+  if (all_taps && w->format != SC_WEIGHTS_DENSE) return fail(SC_EINVAL, "SC_PACK_ALL_TAPS needs dense weights");
   if (w->format == SC_WEIGHTS_DENSE) {
     if (!w->values) return fail(SC_EINVAL, "dense weights: values is NULL");
     if (w->colidx || w->rowptr) return fail(SC_EINVAL, "dense weights: colidx/rowptr must be NULL");
@@ -72,7 +73,7 @@ sc_status build_csr(const sc_weights* w, int M, long long crs, std::vector<int32
     for (int m = 0; m < M; m++) {
       const float* wr = w->values + (long long)m * crs;
       const uint8_t* mr = w->mask ? w->mask + (long long)m * crs : nullptr;
-      for (long long c = 0; c < crs; c++) nnz += mr ? (mr[c] != 0) : (wr[c] != 0.0f);
+      for (long long c = 0; c < crs; c++) nnz += all_taps ? 1 : mr ? (mr[c] != 0) : (wr[c] != 0.0f);
       if (nnz >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "more than 2^31-1 non-zeros");
       rowptr[m + 1] = (int32_t)nnz;
     }
@@ -83,7 +84,7 @@ sc_status build_csr(const sc_weights* w, int M, long long crs, std::vector<int32
       const float* wr = w->values + (long long)m * crs;
       const uint8_t* mr = w->mask ? w->mask + (long long)m * crs : nullptr;
       for (long long c = 0; c < crs; c++) {
-        const bool keep = mr ? (mr[c] != 0) : (wr[c] != 0.0f);
+        const bool keep = all_taps || (mr ? (mr[c] != 0) : (wr[c] != 0.0f));
         if (keep) {
           col[j] = (int32_t)c;
           val[j] = wr[c];
@@ -124,32 +125,6 @@ sc_status build_csr(const sc_weights* w, int M, long long crs, std::vector<int32
   return SC_OK;
 }
 
-// Deal rows to (group, wavefront, slot), largest first onto the least-loaded wavefront with
-// a free slot (weights nnz + 1 so empty rows are spread too).  Returns slot_row.
-std::vector<int32_t> schedule_rows(const sc::Geom& g, const sc::Plan& p, const std::vector<int32_t>& rowptr,
-                                   int32_t* max_wave_nnz) {
-  const int M = g.M;
-  const int waves = p.G * sc::kWaves;
-  std::vector<int> order(M);
-  std::iota(order.begin(), order.end(), 0);
-  auto nnz_of = [&](int m) { return rowptr[m + 1] - rowptr[m]; };
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return nnz_of(a) > nnz_of(b); });
-  std::vector<long long> load(waves, 0), nz(waves, 0);
-  std::vector<int> cnt(waves, 0);
-  std::vector<int32_t> slot_row((size_t)waves * p.OCW, -1);
-  for (int m : order) {
-    int best = -1;
-    for (int w = 0; w < waves; w++)
-      if (cnt[w] < p.OCW && (best < 0 || load[w] < load[best])) best = w;
-    slot_row[(size_t)best * p.OCW + cnt[best]] = m;
-    cnt[best]++;
-    load[best] += nnz_of(m) + 1;
-    nz[best] += nnz_of(m);
-  }
-  *max_wave_nnz = (int32_t)*std::max_element(nz.begin(), nz.end());
-  return slot_row;
-}
-
 }  // namespace
 
 extern "C" {
@@ -163,7 +138,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
   if (!out) return fail(SC_EINVAL, "out is NULL");
   *out = nullptr;
   if (!w) return fail(SC_EINVAL, "weights descriptor is NULL");
-  if (flags & ~SC_PACK_HOST_ONLY) return fail(SC_EINVAL, "unknown pack flag");
+  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS)) return fail(SC_EINVAL, "unknown pack flag");
   sc::Geom g;
   if (!sc::make_geom(M, C, R, S, H, W, stride, pad, &g))
     return fail(SC_ESHAPE, "invalid layer geometry (dims >= 1, stride >= 1, pad >= 0, output >= 1x1)");
@@ -175,11 +150,13 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
   try {
     std::vector<int32_t> rowptr, col;
     std::vector<float> val;
-    sc_status s = build_csr(w, M, crs, rowptr, col, val);
+    sc_status s = build_csr(w, M, crs, (flags & SC_PACK_ALL_TAPS) != 0, rowptr, col, val);
     if (s != SC_OK) return s;
     const long long nnz = (long long)col.size();
-    sc::Plan p = sc::choose_plan(g, rowptr);
-    if (p.K == 0) return fail(SC_EUNSUPPORTED, "input rows too wide for the LDS tile");
+    std::vector<int32_t> slot_row;
+    int32_t max_wave_nnz = 0;
+    sc::Plan p = sc::choose_plan(g, rowptr, col, &slot_row, &max_wave_nnz);
+    if (p.K == 0) return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
     h->magic = kMagic;
@@ -187,6 +164,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->p = p;
     h->nnz = nnz;
     h->host_only = (flags & SC_PACK_HOST_ONLY) != 0;
+    h->max_wave_nnz = max_wave_nnz;
     h->dmem = nullptr;
     h->dbytes = 0;
     h->off.resize(nnz);
@@ -197,14 +175,12 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->val = val;
     h->rowptr = rowptr;
 
-    // Kernel stream, ordered (group, wavefront, chunk, slot) so that a wavefront's
-    // non-zeros for one chunk are contiguous.
-    std::vector<int32_t> slot_row = schedule_rows(g, p, rowptr, &h->max_wave_nnz);
-    const int waves = p.G * sc::kWaves;
-    const size_t nslots = (size_t)waves * p.OCW;
-    std::vector<uint32_t> ent(2 * (size_t)nnz);
-    std::vector<int32_t> seg(2 * nslots * p.nch, 0);
-    // per row: first entry of each chunk
+    // Kernel stream: per (group, wavefront), one block per chunk holding header entries
+    // {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
+    // non-zeros {enc, value} in slot order, each slot's run padded to an even count with
+    // {0, +0.0f} entries; bstart[(group*NW + wave)*(nch+1) + k] is the first entry of
+    // block k (and bstart[.. + nch] the end of the last one).
+    const int waves = p.G * p.NW;
     std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
     for (int m = 0; m < M; m++) {
       int j = rowptr[m];
@@ -214,14 +190,23 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       }
       chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
     }
+    const int hdr_n = sc::block_header(p.OCW);
+    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + p.OCW);
+    if (n_ent >= (size_t)1 << 31) {
+      sparseconv_destroy(h);
+      return fail(SC_EUNSUPPORTED, "kernel stream too large");
+    }
+    std::vector<uint32_t> ent(2 * std::max<size_t>(n_ent, 1), 0);
+    std::vector<int32_t> bstart((size_t)waves * (p.nch + 1));
     size_t pos = 0;
-    for (int wv = 0; wv < waves; wv++)
-      for (int k = 0; k < p.nch; k++)
+    for (int wv = 0; wv < waves; wv++) {
+      for (int k = 0; k < p.nch; k++) {
+        bstart[(size_t)wv * (p.nch + 1) + k] = (int32_t)pos;
+        const size_t hdr = pos;
+        pos += hdr_n;
         for (int o = 0; o < p.OCW; o++) {
-          const size_t slot = (size_t)wv * p.OCW + o;
-          const int m = slot_row[slot];
-          const size_t sidx = 2 * (slot * p.nch + k);
-          seg[sidx] = (int32_t)pos;
+          const int m = slot_row[(size_t)wv * p.OCW + o];
+          int cnt = 0;
           if (m >= 0) {
             const int b = chunk_start[(size_t)m * (p.nch + 1) + k];
             const int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
@@ -235,9 +220,19 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
               ent[2 * pos + 1] = vbits;
               pos++;
             }
+            cnt = e - b;
+            if (cnt & 1) {  // zero-weight pad entry (offset 0 is a valid LDS word)
+              ent[2 * pos] = 0;
+              ent[2 * pos + 1] = 0;
+              pos++;
+              cnt++;
+            }
           }
-          seg[sidx + 1] = (int32_t)pos;
+          ent[2 * (hdr + o)] = (uint32_t)cnt;
         }
+      }
+      bstart[(size_t)wv * (p.nch + 1) + p.nch] = (int32_t)pos;
+    }
 
     if (!h->host_only) {
       if (hipGetDevice(&h->device) != hipSuccess) {
@@ -245,8 +240,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_EDEVICE, "no HIP device available");
       }
       auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-      const size_t b_ent = al(std::max<size_t>(ent.size() * 4, 8));
-      const size_t b_seg = al(seg.size() * 4);
+      const size_t b_ent = al(ent.size() * 4);
+      const size_t b_seg = al(bstart.size() * 4);
       const size_t b_slot = al(slot_row.size() * 4);
       h->dbytes = b_ent + b_seg + b_slot;
       if (hipMalloc(&h->dmem, h->dbytes) != hipSuccess) {
@@ -259,7 +254,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       h->d_seg = reinterpret_cast<const int32_t*>(base + b_ent);
       h->d_slot = reinterpret_cast<const int32_t*>(base + b_ent + b_seg);
       hipError_t e1 = hipMemcpy(base, ent.data(), ent.size() * 4, hipMemcpyHostToDevice);
-      hipError_t e2 = hipMemcpy(base + b_ent, seg.data(), seg.size() * 4, hipMemcpyHostToDevice);
+      hipError_t e2 = hipMemcpy(base + b_ent, bstart.data(), bstart.size() * 4, hipMemcpyHostToDevice);
       hipError_t e3 = hipMemcpy(base + b_ent + b_seg, slot_row.data(), slot_row.size() * 4, hipMemcpyHostToDevice);
       if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
         sparseconv_destroy(h);
@@ -289,6 +284,8 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->packed_bytes = (2 * h->nnz + h->g.M + 1) * 4;
   info->device_bytes = (int64_t)h->dbytes;
   info->tile_pixels = 64 * h->p.K;
+  info->waves_per_group = h->p.NW;
+  info->pipeline_depth = 2;
   info->rows_per_wave = h->p.OCW;
   info->row_groups = h->p.G;
   info->chunk_channels = h->p.Cc;
@@ -323,8 +320,10 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
-sc_status check_io(const sc::Geom& g, const float* in, const float* outp, int N) {
+sc_status check_io(const sc::Geom& g, const sc::Plan& p, const float* in, const float* outp, int N) {
   const long long nin = (long long)N * g.C * g.H * g.W;
+  if ((long long)p.span_images * g.C * g.H * g.W * 4 >= (1LL << 31) - (1LL << 20))
+    return fail(SC_EUNSUPPORTED, "C*H*W too large for 32-bit staging offsets");
   const long long nout = (long long)N * g.M * g.E * g.F;
   if (nin >= (1LL << 31) || nout >= (1LL << 31))
     return fail(SC_EUNSUPPORTED, "N*C*H*W or N*M*E*F >= 2^31 elements");
@@ -341,15 +340,16 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.N = N; a.C = g.C; a.H = g.H; a.W = g.W; a.M = g.M; a.E = g.E; a.F = g.F;
   a.R = g.R; a.S = g.S; a.st = g.st; a.pad = g.pad;
   a.Pp = g.Pp; a.HYp = g.HYp; a.img_ext = g.HYp * g.Pp;
-  a.NRmax = p.NRmax; a.PH = p.PH; a.CHS = p.CHS; a.Cc = p.Cc; a.nch = p.nch; a.G = p.G;
-  a.lds_floats = p.lds_floats;
+  a.NRmax = p.NRmax; a.PH = p.PH; a.CHS = p.CHS; a.nblk = p.nblk; a.Cc = p.Cc; a.nch = p.nch; a.G = p.G;
+  a.rt = p.rt;
+  a.QE = p.QE;
+  a.nin = p.nin;
+  a.slot_words = p.slot_words;
+  a.HW = g.H * g.W;
+  a.x_words = (long long)N * g.C * g.H * g.W;
   a.ext_total = (long long)N * a.img_ext;
+  a.ntiles = (int)((a.ext_total + 64LL * p.K - 1) / (64LL * p.K));
   return a;
-}
-
-int num_blocks(const sc::Plan& p, long long ext_total) {
-  const long long tiles = (ext_total + 64LL * p.K - 1) / (64LL * p.K);
-  return (int)(tiles * p.G);
 }
 
 }  // namespace
@@ -367,7 +367,7 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   if (C != g.C || H != g.H || W != g.W || M != g.M || R != g.R || S != g.S || stride != g.st || pad != g.pad)
     return fail(SC_ESHAPE, "forward dims differ from the packed handle");
   if (N == 0) return SC_OK;
-  sc_status s = check_io(g, input, output, N);
+  sc_status s = check_io(g, h->p, input, output, N);
   if (s != SC_OK) return s;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
@@ -376,29 +376,10 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   a.ent = h->d_ent;
   a.seg = h->d_seg;
   a.slot_row = h->d_slot;
-  const int e = sc::launch_sparse(h->p, a, hip_stream, num_blocks(h->p, a.ext_total));
-  if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
-  return SC_OK;
-}
-
-sc_status sparseconv_dense_forward(const float* w_dense, const float* input, float* output, int32_t N,
-                                   int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
-                                   int32_t stride, int32_t pad, void* hip_stream) {
-  g_err.clear();
-  sc::Geom g;
-  if (N < 0 || !sc::make_geom(M, C, R, S, H, W, stride, pad, &g)) return fail(SC_ESHAPE, "invalid layer geometry");
-  if (!w_dense) return fail(SC_EINVAL, "dense weights are NULL");
-  if (N == 0) return SC_OK;
-  sc_status s = check_io(g, input, output, N);
-  if (s != SC_OK) return s;
-  const long long nw = (long long)M * C * R * S;
-  if (ranges_overlap(w_dense, nw * 4, output, (long long)N * M * g.E * g.F * 4))
-    return fail(SC_EINVAL, "weights and output overlap");
-  sc::Plan p = sc::choose_plan(g, {});
-  if (p.K == 0) return fail(SC_EUNSUPPORTED, "input rows too wide for the LDS tile");
-  sc::KArgs a = make_args(g, p, input, output, N);
-  a.wd = w_dense;
-  const int e = sc::launch_dense(p, a, hip_stream, num_blocks(p, a.ext_total));
+  int gerr = 0;
+  const int nb = sc::grid_size(h->p, (long long)a.ntiles * h->p.G, &gerr);
+  if (gerr) return fail(SC_EDEVICE, std::string("occupancy query failed: ") + hipGetErrorString((hipError_t)gerr));
+  const int e = sc::launch_sparse(h->p, a, hip_stream, nb);
   if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
   return SC_OK;
 }

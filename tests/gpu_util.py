@@ -23,15 +23,11 @@ def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None):
 
 
 def gpu_dense(x, w_masked, stride, pad):
-    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    wd = torch.from_numpy(np.ascontiguousarray(w_masked)).cuda()
+    """Dense direct baseline: the same kernel on a handle storing every filter tap."""
     N, C, H, W = x.shape
-    M, _, R, S = w_masked.shape
-    E, F = sc.out_size(H, pad, R, stride), sc.out_size(W, pad, S, stride)
-    out = torch.full((N, M, E, F), float("nan"), dtype=torch.float32, device="cuda")
-    sc.dense_forward(wd, xd, stride, pad, out=out)
-    torch.cuda.synchronize()
-    return out.cpu().numpy()
+    h = sc.Handle.from_dense(np.ascontiguousarray(w_masked), H, W, stride, pad, flags=sc.SC_PACK_ALL_TAPS)
+    y, _ = gpu_sparse(x, w_masked, None, stride, pad, handle=h)
+    return y
 
 
 def assert_parity(y_gpu, y64, mag, what=""):

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 7
+    assert len(names) == 6
     lib = ctypes.CDLL(sc.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -151,6 +151,23 @@ def test_forward_validation_without_device():
     assert st == sc.SC_EINVAL
     assert sc.sparseconv_last_error() != ""
     sc.sparseconv_destroy(None)  # no-op
+
+
+def test_all_taps_flag_stores_every_position():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w_masked"],
+                  flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ALL_TAPS)
+    rowptr, off, val = h.export()
+    crs = L.C * L.R * L.S
+    assert rowptr.tolist() == [m * crs for m in range(L.M + 1)]
+    np.testing.assert_array_equal(val, d["w_masked"].reshape(-1))
+    o_off = oracle.stretch(np.tile(np.arange(crs, dtype=np.int32), L.M), L.C, L.R, L.S, L.H, L.W)
+    np.testing.assert_array_equal(off, o_off)
+    rp, col, v = oracle.csr_from_dense(d["w"], d["mask"])
+    st, _ = _status(lambda: sc.sparseconv_pack(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=v, colidx=col,
+                                               rowptr=rp, flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ALL_TAPS))
+    assert st == sc.SC_EINVAL
 
 
 def test_injected_allocation_failure(monkeypatch):

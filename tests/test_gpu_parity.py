@@ -79,12 +79,26 @@ def test_random_shapes(c):
     assert_parity(y, r["y64"], r["mag"], str(c))
 
 
-@pytest.mark.parametrize("plan", ["K=1,OCW=1", "K=2,OCW=4", "K=8,OCW=16", "K=4,OCW=2,CC=3"])
+@pytest.mark.parametrize("plan", ["K=1,OCW=1", "K=2,OCW=4", "K=8,OCW=8", "K=4,OCW=2,CC=3", "K=4,OCW=8,NW=16,D=2",
+                                  "K=2,OCW=4,NW=16,D=3", "K=1,OCW=16,D=4,CC=1", "K=8,OCW=8,NW=16,D=4",
+                                  "K=4,OCW=16,NW=16,D=3"])
 def test_every_plan_shape(plan, monkeypatch):
     """The same layer through several launch plans (positions per lane, slots per wave,
-    channel chunk), including chunking that leaves a ragged last chunk."""
+    wavefronts per workgroup, pipeline depth, channel chunk), including chunking that
+    leaves a ragged last chunk."""
     monkeypatch.setenv("SPARSECONV_PLAN", plan)
     d = workloads.make_custom(3, 20, 23, 37, 50, 3, 3, 1, 1, 0.15, 77)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    assert_parity(y, r["y64"], r["mag"], plan)
+
+
+@pytest.mark.parametrize("plan", ["K=1,OCW=4,D=4", "K=1,OCW=4,D=2", "K=2,OCW=2,NW=16,D=3"])
+def test_persistent_runs_of_many_units(plan, monkeypatch):
+    """More work units than resident workgroups: each persistent workgroup walks a run of
+    several tiles, with the staging pipeline crossing tile boundaries."""
+    monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make_custom(6, 5, 60, 60, 20, 3, 3, 1, 1, 0.3, 91)
     r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
     y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
     assert_parity(y, r["y64"], r["mag"], plan)
