@@ -17,7 +17,6 @@ direct baseline on the same GPU, and the CPU oracle timed on this host as a base
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -28,30 +27,22 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "sparse_direct_fwd_imb95_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "sparse_weight_direct_amd", "csrc", f)
-                  for f in ("kernels.hip", "plan.h", "pack.cpp", "api.cpp")]
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_digest() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(layer: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
     missing, for another workload, or taken on different kernel sources."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    from sparse_weight_direct_amd.rocprof_summary import kernel_digest
+    path = os.path.join(PROFILE_DIR, f"sparse_direct_fwd_{layer}_traffic.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         m = re.match(r"^(\w+):\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
@@ -73,7 +64,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense direct baseline")
     ap.add_argument("--miopen", action="store_true", help="also time torch conv2d (MIOpen) as context")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-mb", type=int, default=1024,
+                    help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -174,6 +167,20 @@ def main():
         mms, _ = run(miopen_step, max(10, args.steps // 10), 3)
         extra["torch_conv2d_miopen_ms"] = round(mms, 5)
 
+    if args.copy_mb > 0:
+        nb = args.copy_mb << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+
+        def copy_step(i):
+            dst.copy_(src)
+
+        cms, _ = run(copy_step, 10, 2)
+        extra["copy_reference"] = {"bytes_per_copy": nb, "ms": round(cms, 5),
+                                   "gbs_read_plus_write": round(2 * nb / (cms * 1e-3) / 1e9, 1)}
+        log(f"[bench] copy of {args.copy_mb} MiB: {cms * 1e3:.1f} us -> {2 * nb / (cms * 1e-3) / 1e9:.0f} GB/s (read+write)")
+        del src, dst
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -183,14 +190,17 @@ def main():
         oracle.conv_csr(d["x"][:1], rowptr, colidx, value, M, R, S, st, pad)
         t1 = time.perf_counter() - t
         n_img = max(1, min(N, int(args.cpu_seconds / max(t1, 1e-3))))
-        log(f"[bench] CPU oracle: 1 image {t1:.2f} s; timing {n_img} image(s) on {threads} threads")
+        # a batch that finishes quickly is repeated until about cpu_seconds have passed
+        reps = 1 if n_img < N else max(1, min(1000, int(args.cpu_seconds / max(t1 * N, 1e-3))))
+        log(f"[bench] CPU oracle: 1 image {t1:.3f} s; timing {reps} x {n_img} image(s) on {threads} threads")
         t = time.perf_counter()
-        oracle.conv_csr(d["x"][:n_img], rowptr, colidx, value, M, R, S, st, pad)
+        for _ in range(reps):
+            oracle.conv_csr(d["x"][:n_img], rowptr, colidx, value, M, R, S, st, pad)
         tc = time.perf_counter() - t
-        cpu = {"value": roofline.effective_flops(nnz, n_img, E, F) / tc / 1e12, "unit": "TFLOP/s",
+        cpu = {"value": roofline.effective_flops(nnz, n_img, E, F) * reps / tc / 1e12, "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"list-form oracle (fp64 accumulate) over {n_img} of {N} images, all {M} output channels, "
-                         f"{tc:.1f} s"}
+               "sample": f"list-form oracle (fp64 accumulate), {reps} run(s) over {n_img} of {N} images, "
+                         f"all {M} output channels, {tc:.1f} s"}
 
     traffic = stored_traffic(layer)
     out = {
