@@ -90,7 +90,10 @@ typedef struct {
   int32_t max_wave_nnz;  /* largest non-zero count given to one wavefront */
   int32_t waves_per_group;  /* launch plan: wavefronts per workgroup */
   int32_t pipeline_depth;   /* launch plan: LDS chunk buffers (depth-1 chunks in flight) */
-  int32_t reserved[2];
+  int32_t step_balance_permille; /* 1000 * (sum over chunks of the busiest wavefront's
+                                    non-zero entries) / (sum of the means): the cost of
+                                    synchronising the wavefronts once per chunk (>= 1000) */
+  int32_t reserved;
 } sc_info;
 
 /*

@@ -53,8 +53,8 @@ class sc_info(ctypes.Structure):
                [("nnz", ctypes.c_int64), ("packed_bytes", ctypes.c_int64), ("device_bytes", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
-                                               "pipeline_depth")] + \
-               [("reserved", ctypes.c_int32 * 2)]
+                                               "pipeline_depth", "step_balance_permille")] + \
+               [("reserved", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}

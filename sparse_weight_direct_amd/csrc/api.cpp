@@ -212,7 +212,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
             const int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
             for (int j = b; j < e; j++) {
               const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
-              const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PH +
+              const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
                                               (r / stride) * g.Pp + sx / stride);
               uint32_t vbits;
               std::memcpy(&vbits, &val[j], 4);
@@ -285,7 +285,8 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->device_bytes = (int64_t)h->dbytes;
   info->tile_pixels = 64 * h->p.K;
   info->waves_per_group = h->p.NW;
-  info->pipeline_depth = 2;
+  info->pipeline_depth = h->p.D;
+  info->step_balance_permille = h->p.step_permille;
   info->rows_per_wave = h->p.OCW;
   info->row_groups = h->p.G;
   info->chunk_channels = h->p.Cc;
@@ -340,9 +341,11 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.N = N; a.C = g.C; a.H = g.H; a.W = g.W; a.M = g.M; a.E = g.E; a.F = g.F;
   a.R = g.R; a.S = g.S; a.st = g.st; a.pad = g.pad;
   a.Pp = g.Pp; a.HYp = g.HYp; a.img_ext = g.HYp * g.Pp;
-  a.NRmax = p.NRmax; a.PH = p.PH; a.CHS = p.CHS; a.nblk = p.nblk; a.Cc = p.Cc; a.nch = p.nch; a.G = p.G;
-  a.rt = p.rt;
-  a.QE = p.QE;
+  a.PL = p.PL; a.CHS = p.CHS; a.nblk = p.nblk; a.Cc = p.Cc; a.nch = p.nch; a.G = p.G;
+  a.xoff = g.xoff; a.cshift = g.cshift;
+  a.wide16 = (g.wide && (reinterpret_cast<uintptr_t>(in) & 15) == 0) ? 1 : 0;
+  a.nsb = a.wide16 ? p.nblk / 4 : p.nblk;
+  a.D = p.D; a.QE = p.QE; a.QR = a.wide16 ? p.QR : p.QR1; a.QB = p.QE + a.QR; a.issue_late = p.issue_late;
   a.nin = p.nin;
   a.slot_words = p.slot_words;
   a.HW = g.H * g.W;

@@ -9,13 +9,15 @@
 //
 // Per workgroup (NW wavefronts), the units are walked as a stream of steps
 // (unit, chunk of Cc input channels):
-//   staging  - each step's input rows (stride-phase planes, zero padding included) are
-//              copied HBM -> LDS by direct buffer loads into LDS (gfx950 LDS DMA) into
-//              one of two ring slots while the other is consumed.  A wavefront owns
-//              fixed 64-word blocks of the staged channel layout; a block's per-lane
-//              source offsets are computed once per step and serve every channel of the
-//              chunk (only a scalar offset of c*H*W words changes), and padding words
-//              get an out-of-range offset, which the load turns into 0;
+//   staging  - each step's input (the exact range of every stride-phase plane the tile
+//              reads, zero padding included) is copied HBM -> LDS by direct buffer loads
+//              into LDS (gfx950 LDS DMA) into a ring of D slots, D-1 steps ahead of the
+//              one being computed.  The (64-word block, channel) loads of a step are split
+//              evenly over the wavefronts in block-major order; a block's per-lane source
+//              offsets serve every channel (only a scalar offset of c*H*W words changes),
+//              and padding words get an out-of-range offset, which the load turns into 0.
+//              Every wavefront issues the same number of loads per step (padding with
+//              repeats of an identical load), so a counted vmcnt wait finds its step;
 //   compute  - each wavefront walks the non-zeros of its output-channel slots for the
 //              step.  Its block of {enc, value} non-zeros is staged into the same ring slot
 //              by the same loads; the wavefront reads it 64 entries at a time (one per
@@ -25,7 +27,7 @@
 //              slots of channels without non-zeros store exact zeros.
 // One barrier per step: before it, each wavefront waits (vmcnt) until its own loads of the
 // step have landed; after it, the slot consumed in the previous step is refilled with the
-// next step while this one is computed (two ring slots).
+// step D-1 ahead while this one is computed.
 //
 // Prior art kept from the pages: the input tile plus halo staged once per block and reused
 // by every output channel, the packed per-non-zero word, and per-thread register
@@ -71,6 +73,20 @@ __device__ __forceinline__ void lds_dma_dword(v4i rsrc, const float* lds, uint32
       : "memory", "m0");
 }
 
+// The same with 16 bytes per lane (gfx950): lane i writes the 4 dwords at byte voff + soff
+// to LDS byte address lds + 16*i; the source must be 16-byte aligned.
+__device__ __forceinline__ void lds_dma_dwordx4(v4i rsrc, const float* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lds);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc), "s"(so)
+      : "memory", "m0");
+}
+
 // Workgroups are handed to the 8 XCDs round-robin; renumber them so that consecutive
 // logical ids (hence adjacent runs of tiles, which share halo rows) sit on one XCD's L2.
 __device__ __forceinline__ int xcd_logical(int b, int nb) {
@@ -79,69 +95,117 @@ __device__ __forceinline__ int xcd_logical(int b, int nb) {
   return xcd < rmd ? xcd * (q + 1) + k : rmd * (q + 1) + (xcd - rmd) * q + k;
 }
 
-// Wait until this wavefront's staging loads have landed, then barrier.  The empty asm keeps
-// the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0); expcnt, lgkmcnt untouched
+// s_waitcnt vmcnt(N) for a wave-uniform N in [0, 63] (gfx9 encoding: vmcnt bits [3:0] and
+// [15:14]; expcnt and lgkmcnt left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void waitvm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+#define SC_VM4(b) case b: waitvm<b>(); break; case b + 1: waitvm<b + 1>(); break; \
+                  case b + 2: waitvm<b + 2>(); break; case b + 3: waitvm<b + 3>(); break;
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    SC_VM4(0) SC_VM4(4) SC_VM4(8) SC_VM4(12) SC_VM4(16) SC_VM4(20) SC_VM4(24) SC_VM4(28)
+    SC_VM4(32) SC_VM4(36) SC_VM4(40) SC_VM4(44) SC_VM4(48) SC_VM4(52) SC_VM4(56) SC_VM4(60)
+    default: waitvm<0>(); break;
+  }
+}
+#undef SC_VM4
+
+// Wait until at most `later` of this wavefront's loads are outstanding (the loads of the
+// steps issued after the one about to be computed), then barrier.  The empty asm keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void step_barrier(int later) {
+  wait_vmcnt(later);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Row table of a tile, per wavefront: entry py*NRmax + j holds the word offset of the
-// input row behind phase row j of phase row-plane py, relative to channel 0 of the tile's
-// first image n0 (returned): (n-n0)*C*H*W + y*W, or -1 for padding rows and rows past the
-// last image.
-__device__ __forceinline__ int tile_rows(const KArgs& a, int tile, int K, int lane, int* rowtab) {
-  const int t0 = tile * (64 * K) / a.Pp;
-  const int n0 = t0 / a.HYp;
-  for (int i = lane; i < a.st * a.NRmax; i += 64) {
-    const int py = i / a.NRmax;
-    const int j = i - py * a.NRmax;
-    const int Tr = t0 + j;
-    const int n = Tr / a.HYp;
-    const int y = (Tr - n * a.HYp) * a.st + py - a.pad;
-    rowtab[i] = (n < a.N && y >= 0 && y < a.H) ? ((n - n0) * a.C * a.H + y) * a.W : -1;
-  }
-  return n0;
-}
-
-// Source byte offset of the lane's word in block blk of the staged channel layout
-// (channel term excluded), or out of range for padding, missing rows and the slack at the
-// end of a channel.
-__device__ __forceinline__ uint32_t block_voff(const KArgs& a, int blk, int lane, const int* rowtab) {
+// Source byte offset of the lane's word in block blk of the staged channel layout of the
+// tile starting at extended index I0 (channel term excluded), relative to channel 0 of the
+// tile's first image n0; out of range for padding, positions past the last image and the
+// slack at the end of a channel.  (Wide layout with 16-byte loads: block_voff16 below.)
+__device__ __forceinline__ uint32_t block_voff(const KArgs& a, int I0, int n0, int blk, int lane) {
   const int w = 64 * blk + lane;
-  const int ph = w / a.PH;
+  const int ph = w / a.PL;
   uint32_t off = kOutOfRange;
   if (ph < a.st * a.st) {
-    const int rem = w - ph * a.PH;
-    const int j = rem / a.Pp;
-    const int xq = rem - j * a.Pp;
+    const int J = I0 + (w - ph * a.PL);
+    const int n = J / a.img_ext;
+    const int rem = J - n * a.img_ext;
+    const int t = rem / a.Pp;
     const int py = ph / a.st;
-    const int xg = xq * a.st + (ph - py * a.st) - a.pad;
-    if (xg >= 0 && xg < a.W) {
-      const int r = rowtab[py * a.NRmax + j];
-      if (r >= 0) off = 4u * (uint32_t)(r + xg);
-    }
+    const int y = t * a.st + py - a.pad;
+    const int x = (rem - t * a.Pp) * a.st + (ph - py * a.st) - a.xoff;
+    if (n < a.N && y >= 0 && y < a.H && x >= 0 && x < a.W)
+      off = 4u * (uint32_t)(((n - n0) * a.C * a.H + y) * a.W + x);
   }
   return off;
 }
 
-// Start the asynchronous copy of channels [c0, c0 + ncl) of a tile into the input part of a
-// ring slot: the wavefront's blocks blk = wave, wave + NW, ... of every channel.
-template <int NW>
-__device__ __forceinline__ void stage_rows(const KArgs& a, v4i rsrc, int c0, int ncl, float* slot, int wave,
-                                           int lane, const int* rowtab) {
-  for (int blk = wave; blk < a.nblk; blk += NW) {
-    const uint32_t voff = block_voff(a, blk, lane, rowtab);
-    uint32_t soff = 4u * (uint32_t)(c0 * a.HW);
-    const float* dst = slot + 64 * blk;
-    for (int cl = 0; cl < ncl; cl++) {
-      lds_dma_dword(rsrc, dst, voff, soff);
-      dst += a.CHS;
-      soff += 4u * (uint32_t)a.HW;
-    }
+// Wide layout (stride 1): source byte offset of the lane's 4 words in block sb of 256 words;
+// the 4 words are one aligned group of 4 input words or 4 zeros.
+__device__ __forceinline__ uint32_t block_voff16(const KArgs& a, int I0, int n0, int sb, int lane) {
+  const int w = 256 * sb + 4 * lane;
+  uint32_t off = kOutOfRange;
+  if (w < a.PL) {
+    const int J = I0 + w;
+    const int n = J / a.img_ext;
+    const int rem = J - n * a.img_ext;
+    const int t = rem / a.Pp;
+    const int y = t - a.pad;
+    const int x = rem - t * a.Pp - a.xoff;
+    if (n < a.N && y >= 0 && y < a.H && x >= 0 && x < a.W)
+      off = 4u * (uint32_t)(((n - n0) * a.C * a.H + y) * a.W + x);
   }
+  return off;
+}
+
+// Issue one step's loads into a ring slot: the wavefront's block of non-zeros (QE 16-byte
+// loads of 128 entries, contiguous per wavefront), then its share [p0, p1) of the step's
+// (block, channel) loads in block-major order (blocks of 256 words with 16-byte loads, or
+// of 64 words), then repeats of its first non-zero load up to QB loads in all.  Channels
+// at or past C (last chunk) are not loaded.
+template <int T>
+__device__ __forceinline__ void stage_step(const KArgs& a, const uint2* __restrict__ ent, int b0, int b1,
+                                           v4i rsrc, int I0, int n0, int c0, int p0, int p1, float* slot,
+                                           int wave, int lane) {
+  const v4i ersrc = make_rsrc(ent + b0, (uint32_t)(b1 - b0) * 8u);
+  float* edst = slot + a.nin + wave * (256 * a.QE);
+  for (int q = 0; q < a.QE; q++) lds_dma_dwordx4(ersrc, edst + 256 * q, 16u * (64 * q + lane), 0u);
+  const int ncl = __builtin_amdgcn_readfirstlane(min(a.Cc, a.C - c0));
+  int issued = a.QE;
+  const int bw = a.wide16 ? 256 : 64;
+  int blk = p0 / a.Cc;
+  int cl = p0 - blk * a.Cc;
+  int p = p0;
+  while (p < p1) {
+    const uint32_t voff = a.wide16 ? block_voff16(a, I0, n0, blk, lane) : block_voff(a, I0, n0, blk, lane);
+    const int cend = min(a.Cc, cl + (p1 - p));  // channels of this block in the share
+    const int cstop = min(cend, ncl);
+    const float* dst = slot + blk * bw + cl * a.CHS;
+    uint32_t soff = 4u * (uint32_t)((c0 + cl) * a.HW);
+    if (a.wide16) {
+      for (int c = cl; c < cstop; c++) {
+        lds_dma_dwordx4(rsrc, dst, voff, soff);
+        dst += a.CHS;
+        soff += 4u * (uint32_t)a.HW;
+      }
+    } else {
+      for (int c = cl; c < cstop; c++) {
+        lds_dma_dword(rsrc, dst, voff, soff);
+        dst += a.CHS;
+        soff += 4u * (uint32_t)a.HW;
+      }
+    }
+    issued += cstop - cl;
+    p += cend - cl;
+    cl = 0;
+    blk++;
+  }
+  if (a.D > 2)
+    for (; issued < a.QB; issued++) lds_dma_dwordx4(ersrc, edst, 16u * lane, 0u);
 }
 
 // Output word offset (without the channel term) of each of the lane's K positions, or -1.
@@ -156,8 +220,8 @@ __device__ __forceinline__ void output_bases(const KArgs& a, int I0, int lane, i
       const int n = Ii / a.img_ext;
       const int rem = Ii - n * a.img_ext;
       const int e = rem / a.Pp;
-      const int f = rem - e * a.Pp;
-      if (e < a.E && f < a.F) ob[b] = (n * a.M * a.E + e) * a.F + f;
+      const int f = rem - e * a.Pp - a.cshift;
+      if (e < a.E && f >= 0 && f < a.F) ob[b] = (n * a.M * a.E + e) * a.F + f;
     }
   }
 }
@@ -208,56 +272,56 @@ __device__ __forceinline__ void run_pairs(float (&acc)[K], const float* lane_lds
   }
 }
 
-// Stage the wavefront's block of non-zeros (stream entries [b0, b1)) into its share of a
-// ring slot: QE loads of 64 words (32 entries) each; words past the block's end load as 0.
-// Entry e of the block lands at word nin + T*(e/32) + 64*wave + 2*(e%32) of the slot.
-template <int T>
-__device__ __forceinline__ void stage_block(const KArgs& a, const uint2* __restrict__ ent, int b0, int b1,
-                                            float* slot, int wave, int lane) {
-  const v4i rsrc = make_rsrc(ent + b0, (uint32_t)(b1 - b0) * 8u);
-  for (int q = 0; q < a.QE; q++) lds_dma_dword(rsrc, slot + a.nin + T * q + 64 * wave, 4u * (64 * q + lane), 0u);
-}
-
 // One step: the wavefront's slots and their non-zeros of this chunk, read from the block
 // staged in the ring slot: header entries {count of slot o, 0} (OCW of them, rounded up to
 // an even number), then the slots' non-zeros {enc, value} in slot order, each slot's run
 // padded to an even length with zero-weight entries so that it is walked in pairs that
-// never straddle a group of 64 (lane i holds entry i of the group).
-template <int K, int OCW, int NW>
-__device__ __forceinline__ void sparse_step(const KArgs& a, float (&acc)[OCW][K], const float* lane_lds,
-                                            const float* slot, int wave, int lane) {
-  constexpr int T = NW * 64;
-  constexpr int HDR = (OCW + 1) & ~1;
-  const uint32_t* eb = reinterpret_cast<const uint32_t*>(slot + a.nin) + 64 * wave;
-  const int emax = 32 * a.QE - 1;
-  auto group = [&](int base) -> uint2 {
-    const int e = min(base + lane, emax);
-    return *reinterpret_cast<const uint2*>(eb + T * (e >> 5) + 2 * (e & 31));
-  };
-  const uint2 head = group(0);
-  uint2 cur = head;
-  int r = HDR;   // next entry's lane within the current group
-  int base = 0;  // entry index of the current group's lane 0
+// never straddle a group of 64 (lane i holds entry i of the group).  The walk is split in
+// slot ranges [O0, O1) so that the caller can issue staging loads between them; after(o)
+// runs once slot o's run is done.
+struct Walk {
+  const uint32_t* eb;  // the wavefront's entries in the ring slot
+  uint2 head;          // entries 0..63 (the header in lanes 0..OCW-1)
+  uint2 cur;           // the current group of 64 entries
+  int r;               // next entry's lane within the current group
+  int base;            // entry index of the current group's lane 0
+};
+
+template <int NW>
+__device__ __forceinline__ uint2 walk_group(const KArgs& a, const Walk& w, int base, int lane) {
+  const int e = min(base + lane, 128 * a.QE - 1);
+  return *reinterpret_cast<const uint2*>(w.eb + 2 * e);
+}
+
+template <int OCW, int NW>
+__device__ __forceinline__ Walk walk_begin(const KArgs& a, const float* slot, int wave, int lane) {
+  Walk w;
+  w.eb = reinterpret_cast<const uint32_t*>(slot + a.nin) + wave * (256 * a.QE);
+  w.head = walk_group<NW>(a, w, 0, lane);
+  w.cur = w.head;
+  w.r = (OCW + 1) & ~1;
+  w.base = 0;
+  return w;
+}
+
+template <int K, int OCW, int NW, int O0, int O1, typename After>
+__device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)[OCW][K], const float* lane_lds,
+                                           int lane, After&& after) {
 #pragma unroll
-  for (int o = 0; o < OCW; o++) {
-    int n = __builtin_amdgcn_readlane((int)head.x, o);  // even
-    if (n == 0) continue;
-    if (r + n <= 64) {  // the run lies in the current group
-      run_pairs<K>(acc[o], lane_lds, cur, r, n >> 1);
-      r += n;
-      continue;
-    }
-    do {
-      if (r == 64) {
-        base += 64;
-        cur = group(base);
-        r = 0;
+  for (int o = O0; o < O1; o++) {
+    int n = __builtin_amdgcn_readlane((int)w.head.x, o);  // even
+    while (n > 0) {
+      if (w.r == 64) {
+        w.base += 64;
+        w.cur = walk_group<NW>(a, w, w.base, lane);
+        w.r = 0;
       }
-      const int take = min(n, 64 - r);
-      run_pairs<K>(acc[o], lane_lds, cur, r, take >> 1);
-      r += take;
+      const int take = min(n, 64 - w.r);
+      run_pairs<K>(acc[o], lane_lds, w.cur, w.r, take >> 1);
+      w.r += take;
       n -= take;
-    } while (n > 0);
+    }
+    after(o);
   }
 }
 
@@ -272,8 +336,7 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   extern __shared__ float lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int* rowtab = reinterpret_cast<int*>(lds + 2 * a.slot_words) + wave * a.rt;
-  int* bst = reinterpret_cast<int*>(lds + 2 * a.slot_words) + NW * a.rt;
+  int* bst = reinterpret_cast<int*>(lds + a.D * a.slot_words);
 
   const int b = xcd_logical(blockIdx.x, gridDim.x);
   const long long units = (long long)a.ntiles * a.G;
@@ -285,22 +348,27 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   for (int i = threadIdx.x; i < a.G * NW * (a.nch + 1); i += T) bst[i] = bstart[i];
   __syncthreads();
 
+  // this wavefront's share of a step's (block, channel) loads
+  const int P = a.nsb * a.Cc;
+  const int p0 = __builtin_amdgcn_readfirstlane((int)((long long)P * wave / NW));
+  const int p1 = __builtin_amdgcn_readfirstlane((int)((long long)P * (wave + 1) / NW));
+
   // issue side: the next step to stage (unit = tile * G + g, chunk is_k, ring slot is_buf)
   int is_tile = u0 / a.G, is_g = u0 - (u0 / a.G) * a.G, is_k = 0, is_buf = 0, is_new_tile = 1;
+  int is_I0 = 0, is_n0 = 0;
   v4i rsrc = make_rsrc(x, 0u);
   auto issue = [&]() {
     if (is_new_tile) {
-      const int n0 = tile_rows(a, is_tile, K, lane, rowtab);
-      const long long first = (long long)n0 * a.C * a.HW;
+      is_I0 = is_tile * (64 * K);
+      is_n0 = is_I0 / a.img_ext;
+      const long long first = (long long)is_n0 * a.C * a.HW;
       rsrc = make_rsrc(x + first, (uint32_t)min((a.x_words - first) * 4, 0x7ffffff0LL));
       is_new_tile = 0;
     }
     const int* bw = bst + (is_g * NW + wave) * (a.nch + 1) + is_k;
-    float* slot = lds + is_buf * a.slot_words;
-    stage_block<T>(a, ent, bw[0], bw[1], slot, wave, lane);
-    const int c0 = is_k * a.Cc;
-    stage_rows<NW>(a, rsrc, c0, min(a.Cc, a.C - c0), slot, wave, lane, rowtab);
-    is_buf ^= 1;
+    stage_step<T>(a, ent, bw[0], bw[1], rsrc, is_I0, is_n0, is_k * a.Cc, p0, p1, lds + is_buf * a.slot_words,
+                  wave, lane);
+    if (++is_buf == a.D) is_buf = 0;
     if (++is_k == a.nch) {
       is_k = 0;
       if (++is_g == a.G) {
@@ -310,7 +378,7 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
       }
     }
   };
-  issue();
+  for (int s = 0; s < a.D - 1 && s < S; s++) issue();
 
   float acc[OCW][K];
 #pragma unroll
@@ -319,17 +387,23 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
     for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
 
   int tile = u0 / a.G, g = u0 - (u0 / a.G) * a.G, ck = 0, cbuf = 0;
-  int I0 = tile * (64 * K);
-  int lane_pos = I0 - (I0 / a.Pp) * a.Pp + lane;
+  int drained = 0;  // a unit's stores were issued since the last wait: wait for everything
   for (int s = 0; s < S; s++) {
-    step_barrier();  // step s landed; every wavefront is done with the other slot
-    if (s + 1 < S) issue();
+    // loads issued after step s's: those of steps s+1 .. min(s+D-2, S-1)
+    const int later = drained ? 0 : a.QB * min(a.D - 2, S - 1 - s);
+    step_barrier(later);  // step s landed; every wavefront is done with step s-1's slot
+    drained = 0;
+    const bool more = s + a.D - 1 < S;
+    if (more && !a.issue_late) issue();
     const float* slot = lds + cbuf * a.slot_words;
-    sparse_step<K, OCW, NW>(a, acc, slot + lane_pos, slot, wave, lane);
-    cbuf ^= 1;
-    if (++ck == a.nch) {
+    Walk w = walk_begin<OCW, NW>(a, slot, wave, lane);
+    walk_slots<K, OCW, NW, 0, OCW>(a, w, acc, slot + lane, lane, [](int) {});
+    // issued late, the loads of step s+D-1 overlap the wait at the next barrier; their
+    // slot held step s-1, which every wavefront finished before this step's barrier
+    if (more && a.issue_late) issue();
+    if (ck + 1 == a.nch) {
       int ob[K];
-      output_bases<K>(a, I0, lane, ob);
+      output_bases<K>(a, tile * (64 * K), lane, ob);
       const int plane = a.E * a.F;
 #pragma unroll
       for (int o = 0; o < OCW; o++) {
@@ -342,12 +416,14 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
 #pragma unroll
         for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
       }
+      drained = 1;
+    }
+    if (++cbuf == a.D) cbuf = 0;
+    if (++ck == a.nch) {
       ck = 0;
       if (++g == a.G) {
         g = 0;
         tile++;
-        I0 = tile * (64 * K);
-        lane_pos = I0 - (I0 / a.Pp) * a.Pp + lane;
       }
     }
   }

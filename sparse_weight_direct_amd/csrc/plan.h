@@ -6,20 +6,28 @@
 //    position (yp, xp) lands in phase (yp % st, xp % st) at phase coordinates
 //    (yp / st, xp / st).  A phase plane has HYp = ceil((H+2p)/st) rows of Pp = ceil((W+2p)/st)
 //    words.  For stride 1 this is just the zero-padded image.
+//  * Wide layout (stride 1, W % 4 == 0, pad <= 2): input column x sits at phase column x + 4
+//    and Pp = W + 4, so every aligned group of 4 words is 4 input words or 4 zeros and can be
+//    copied with 16-byte loads; output column f then sits at extended column f + 4 - pad.
+//    In general input column x sits at phase column (x + xoff) / st (xoff = pad, or 4 in the
+//    wide layout) and output column f at extended column f + cshift (cshift = xoff - pad).
 //  * Output (e, f) of image n reads, for tap (r, s), phase (r % st, s % st) at
 //    (e + r/st, f + s/st): with stride folded into the phases every tap is a unit-stride
 //    shift, so a run of consecutive "extended" output indices I = n*HYp*Pp + e*Pp + f maps
 //    to consecutive LDS words for every tap.  Positions with e >= E or f >= F are junk
 //    (computed, never stored).
-//  * A workgroup owns 64*K consecutive extended indices (K per lane, 64 apart) and stages
-//    the phase rows they touch, NRmax rows per phase, for Cc channels at a time:
-//        LDS word = c_l*CHS + (py*st + px)*PH + row*Pp + col,  PH = NRmax*Pp,
-//    with the channel stride CHS = st*st*PH rounded up to a multiple of 64 words, so that
+//  * A workgroup owns a tile of 64*K consecutive extended indices [I0, I0 + 64K) (K per
+//    lane, 64 apart).  For every phase plane it stages exactly the range the tile's taps
+//    read, PL = 64K + (Rr-1)*Pp + (S-1)/st consecutive phase-plane words starting at I0
+//    (rows of the next image and padding included as zeros), for Cc channels at a time:
+//        LDS word = c_l*CHS + (py*st + px)*PL + (J - I0)   for phase-plane index J,
+//    with the channel stride CHS = st*st*PL rounded up to a multiple of 64 words, so that
 //    every channel is nblk = CHS/64 blocks of 64 words and a block's source offsets are
 //    the same for every channel (they differ by a multiple of H*W).
 //  * Each stored non-zero (c, r, s, v) is re-encoded at pack time as
-//        enc = (c % Cc)*CHS + ((r % st)*st + (s % st))*PH + (r / st)*Pp + (s / st)
-//    so the inner loop is: one address add, K LDS reads 64 words apart, K FMAs.
+//        enc = (c % Cc)*CHS + ((r % st)*st + (s % st))*PL + (r / st)*Pp + (s / st)
+//    so lane l, position b reads LDS word enc + l + 64*b: one address add, K LDS reads 64
+//    words apart and K FMAs per non-zero.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -33,6 +41,9 @@ struct Geom {
   int E, F;        // output extent
   int Pp, HYp;     // phase plane row pitch and rows per image
   int Rr;          // distinct r / st values = (R-1)/st + 1
+  int wide;        // 1: wide layout (16-byte staging loads possible)
+  int xoff;        // padded-column offset of input column 0 (pad, or 4 in the wide layout)
+  int cshift;      // extended column of output column 0 (xoff - pad)
 };
 
 struct Plan {
@@ -42,17 +53,24 @@ struct Plan {
   int G;           // output-channel groups (work units per tile)
   int Cc;          // channels staged per chunk
   int nch;         // number of chunks = ceil(C / Cc)
-  int NRmax;       // phase rows staged per phase plane
-  int PH;          // words per phase plane = NRmax * Pp
-  int CHS;         // words per staged channel = st*st*PH rounded up to a multiple of 64
-  int nblk;        // 64-word blocks per staged channel = CHS / 64
-  int rt;          // row-table entries per wavefront (>= st*NRmax, multiple of 64)
-  int QE;          // loads of 64 words per wavefront per step carrying its block of
-                   // non-zeros (32 entries each)
-  int nin;         // words of a ring slot holding input rows (Cc*CHS + read slack)
-  int slot_words;  // words of one ring slot = nin + QE*64*NW
-  int lds_bytes;   // two ring slots + per-wavefront row tables + block-start table
-  int span_images; // most images one tile's staged rows can touch
+  int PL;          // staged words per phase plane = 64K + (Rr-1)*Pp + (S-1)/st
+  int CHS;         // words per staged channel = st*st*PL rounded up to a multiple of 64
+  int nblk;        // 64-word blocks per staged channel = CHS / 64 (CHS a multiple of 256
+                   // in the wide layout: nblk/4 blocks of 256 words)
+  int D;           // LDS ring slots: D-1 chunks in flight
+  int QE;          // 16-byte loads per wavefront per step carrying its block of non-zeros
+                   // (128 entries each)
+  int QR;          // loads per wavefront per step carrying input rows: ceil(nblk*Cc/NW)
+                   // 4-byte loads, or ceil(nblk/4*Cc/NW) 16-byte loads in the wide layout
+  int QR1;         // the 4-byte count, used in the wide layout when the input pointer is not
+                   // 16-byte aligned
+  int QB;          // loads per wavefront per step, QE + QR (padded with repeats)
+  int nin;         // words of a ring slot holding input rows = Cc*CHS
+  int slot_words;  // words of one ring slot = nin + QE*256*NW
+  int lds_bytes;   // D ring slots + block-start table
+  int span_images; // most images one tile's staged range can touch
+  int step_permille;  // 1000 * sum over chunks of the busiest wavefront's entries / mean
+  int issue_late;     // 1: staging loads are issued after a step's walk, 0: before it
 };
 
 // Kernel arguments (by value).
@@ -64,7 +82,12 @@ struct KArgs {
   const int* slot_row;    // sparse: [group][wave][slot] -> output channel or -1
   int N, C, H, W, M, E, F, R, S, st, pad;
   int Pp, HYp, img_ext;   // img_ext = HYp * Pp
-  int NRmax, PH, CHS, nblk, Cc, nch, G, rt, QE, nin, slot_words;
+  int xoff, cshift;       // see Geom
+  int wide16;             // 1: stage rows with 16-byte loads (wide layout, aligned input)
+  int nsb;                // staging blocks per channel: nblk/4 of 256 words (wide16) or nblk
+  int PL, CHS, nblk, Cc, nch, G, D, QE, QR, QB, nin, slot_words;
+  int issue_late;         // 1: a step's staging loads are issued after the walk of the step
+                          // D-1 before it (D >= 3), 0: at the start of that step
   int HW;                 // H * W
   int ntiles;             // tiles of 64*K extended positions
   long long x_words;      // N * C * H * W
@@ -76,7 +99,7 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
 // slots (slot_row) and sizes each wavefront's per-chunk block of non-zeros.
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                  std::vector<int32_t>* slot_row, int32_t* max_wave_nnz);
-int plan_nrmax(const Geom& g, int K);
+int plan_pl(const Geom& g, int K);
 
 // Header entries at the start of a wavefront's per-chunk block of non-zeros.
 int block_header(int OCW);

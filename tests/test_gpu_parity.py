@@ -93,6 +93,38 @@ def test_every_plan_shape(plan, monkeypatch):
     assert_parity(y, r["y64"], r["mag"], plan)
 
 
+@pytest.mark.parametrize("plan", ["K=8,OCW=8", "K=4,OCW=2,CC=3,D=3", "K=2,OCW=4,NW=8,D=4", "K=1,OCW=16,CC=1",
+                                  "NARROW,K=4,OCW=8"])
+@pytest.mark.parametrize("pad", [0, 1, 2])
+def test_wide_layout_plans(plan, pad, monkeypatch):
+    """Stride 1 with W % 4 == 0 and pad <= 2 uses the wide layout (input column x at phase
+    column x + 4, 16-byte staging loads); NARROW forces the padded layout for the same layer."""
+    monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make_custom(3, 20, 23, 36, 50, 3, 3, 1, pad, 0.15, 78 + pad)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, pad)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, pad)
+    assert_parity(y, r["y64"], r["mag"], f"{plan} pad {pad}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_misaligned_input_pointer(name):
+    """An input that is 4-byte but not 16-byte aligned: the wide layout is then staged with
+    4-byte loads (same LDS layout); the output is also written through an offset view."""
+    d = workloads.make(name)
+    L = d["layer"]
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    xs = torch.empty(d["x"].size + 1, dtype=torch.float32, device="cuda")
+    x = xs[1:].view(d["x"].shape)
+    x.copy_(torch.from_numpy(d["x"]))
+    assert x.data_ptr() % 16 != 0
+    ys = torch.full((r["y64"].size + 3,), float("nan"), dtype=torch.float32, device="cuda")
+    y = ys[3:].view(r["y64"].shape)
+    h.forward(x, y)
+    torch.cuda.synchronize()
+    assert_parity(y.cpu().numpy(), r["y64"], r["mag"], "misaligned " + name)
+
+
 @pytest.mark.parametrize("plan", ["K=1,OCW=4,D=4", "K=1,OCW=4,D=2", "K=2,OCW=2,NW=16,D=3"])
 def test_persistent_runs_of_many_units(plan, monkeypatch):
     """More work units than resident workgroups: each persistent workgroup walks a run of
