@@ -175,12 +175,12 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->val = val;
     h->rowptr = rowptr;
 
-    // Kernel stream: per (group, wavefront), one block per chunk holding header entries
+    // Kernel stream: per (group, consumer wavefront), one block per chunk holding header entries
     // {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
     // non-zeros {enc, value} in slot order, each slot's run padded to an even count with
-    // {0, +0.0f} entries; bstart[(group*NW + wave)*(nch+1) + k] is the first entry of
+    // {0, +0.0f} entries; bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of
     // block k (and bstart[.. + nch] the end of the last one).
-    const int waves = p.G * p.NW;
+    const int waves = p.G * (p.NW - 1);  // consumer wavefronts
     std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
     for (int m = 0; m < M; m++) {
       int j = rowptr[m];
@@ -284,7 +284,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->packed_bytes = (2 * h->nnz + h->g.M + 1) * 4;
   info->device_bytes = (int64_t)h->dbytes;
   info->tile_pixels = 64 * h->p.K;
-  info->waves_per_group = h->p.NW;
+  info->waves_per_group = h->p.NW - 1;
   info->pipeline_depth = h->p.D;
   info->step_balance_permille = h->p.step_permille;
   info->rows_per_wave = h->p.OCW;
@@ -345,7 +345,7 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.xoff = g.xoff; a.cshift = g.cshift;
   a.wide16 = (g.wide && (reinterpret_cast<uintptr_t>(in) & 15) == 0) ? 1 : 0;
   a.nsb = a.wide16 ? p.nblk / 4 : p.nblk;
-  a.D = p.D; a.QE = p.QE; a.QR = a.wide16 ? p.QR : p.QR1; a.QB = p.QE + a.QR; a.issue_late = p.issue_late;
+  a.D = p.D; a.QE = p.QE;
   a.nin = p.nin;
   a.slot_words = p.slot_words;
   a.HW = g.H * g.W;

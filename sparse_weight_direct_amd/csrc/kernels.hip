@@ -5,29 +5,32 @@
 // work unit is one tile for one group of output channels.  The grid is persistent: every
 // CU runs the workgroups its LDS and registers allow, and each workgroup owns one
 // contiguous run of units (runs differ by at most one unit), so neighbouring tiles, whose
-// staged rows overlap, are handled by the same workgroup one after the other.
+// staged ranges overlap, are handled by the same workgroup one after the other.
 //
-// Per workgroup (NW wavefronts), the units are walked as a stream of steps
-// (unit, chunk of Cc input channels):
-//   staging  - each step's input (the exact range of every stride-phase plane the tile
-//              reads, zero padding included) is copied HBM -> LDS by direct buffer loads
-//              into LDS (gfx950 LDS DMA) into a ring of D slots, D-1 steps ahead of the
-//              one being computed.  The (64-word block, channel) loads of a step are split
-//              evenly over the wavefronts in block-major order; a block's per-lane source
-//              offsets serve every channel (only a scalar offset of c*H*W words changes),
-//              and padding words get an out-of-range offset, which the load turns into 0.
-//              Every wavefront issues the same number of loads per step (padding with
-//              repeats of an identical load), so a counted vmcnt wait finds its step;
-//   compute  - each wavefront walks the non-zeros of its output-channel slots for the
-//              step.  Its block of {enc, value} non-zeros is staged into the same ring slot
-//              by the same loads; the wavefront reads it 64 entries at a time (one per
-//              lane) and broadcasts each entry with v_readlane.  Per non-zero each lane
-//              does one address add, K LDS reads 64 words apart and K fp32 FMAs;
-//   store    - after a unit's last chunk, coalesced NCHW stores of the valid positions;
-//              slots of channels without non-zeros store exact zeros.
-// One barrier per step: before it, each wavefront waits (vmcnt) until its own loads of the
-// step have landed; after it, the slot consumed in the previous step is refilled with the
-// step D-1 ahead while this one is computed.
+// Per workgroup the units are walked as a stream of steps (unit, chunk of Cc input
+// channels) through a ring of D LDS slots, by two roles that synchronise only through
+// counters in LDS (no workgroup barrier inside the stream):
+//   producer - one wavefront copies each step's input (the exact range of every
+//              stride-phase plane the tile reads, zero padding included) HBM -> LDS with
+//              direct buffer loads into LDS (gfx950 LDS DMA), into the slot of the step D
+//              before it once every consumer has released that slot (done counter), and
+//              publishes the step (ready counter) once its loads have landed.  A block's
+//              per-lane source offsets serve every channel (only a scalar offset of c*H*W
+//              words changes); padding words get an out-of-range offset, which the load
+//              turns into 0;
+//   consumers - the other wavefronts each own OCW output-channel slots.  A consumer copies
+//              its own block of {enc, value} non-zeros for a step into its private part of
+//              the step's slot (D-1 steps ahead, counted vmcnt waits), waits for the step's
+//              ready counter, and walks its slots: the block is read 64 entries at a time
+//              (one per lane) and each entry is broadcast with v_readlane.  Per non-zero
+//              each lane does one address add, K LDS reads 64 words apart and K fp32 FMAs.
+//              It then releases the slot (done counter);
+//   store    - after a unit's last chunk, each consumer stores its valid positions with
+//              coalesced NCHW stores; slots of channels without non-zeros store exact zeros.
+// A consumer ahead of the others is held back only when it needs a step whose slot an
+// earlier step still occupies, so per-step imbalance between wavefronts averages out over
+// the ring.  Every wait on a counter is bounded (kSpinLimit sleeps), so a wavefront can
+// never wait forever.
 //
 // Prior art kept from the pages: the input tile plus halo staged once per block and reused
 // by every output channel, the packed per-non-zero word, and per-thread register
@@ -112,13 +115,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 #undef SC_VM4
 
-// Wait until at most `later` of this wavefront's loads are outstanding (the loads of the
-// steps issued after the one about to be computed), then barrier.  The empty asm keeps the
-// compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void step_barrier(int later) {
-  wait_vmcnt(later);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
+// Bounded wait until the LDS counter *p reaches target (every lane reads the same word).
+constexpr int kSpinLimit = 1 << 22;  // sleeps of about 64 cycles: far beyond any real wait
+__device__ __forceinline__ void lds_wait_ge(const uint32_t* p, uint32_t target) {
+  for (int i = 0; i < kSpinLimit; i++) {
+    if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
   asm volatile("" ::: "memory");
 }
 
@@ -162,50 +165,46 @@ __device__ __forceinline__ uint32_t block_voff16(const KArgs& a, int I0, int n0,
   return off;
 }
 
-// Issue one step's loads into a ring slot: the wavefront's block of non-zeros (QE 16-byte
-// loads of 128 entries, contiguous per wavefront), then its share [p0, p1) of the step's
-// (block, channel) loads in block-major order (blocks of 256 words with 16-byte loads, or
-// of 64 words), then repeats of its first non-zero load up to QB loads in all.  Channels
-// at or past C (last chunk) are not loaded.
-template <int T>
-__device__ __forceinline__ void stage_step(const KArgs& a, const uint2* __restrict__ ent, int b0, int b1,
-                                           v4i rsrc, int I0, int n0, int c0, int p0, int p1, float* slot,
-                                           int wave, int lane) {
-  const v4i ersrc = make_rsrc(ent + b0, (uint32_t)(b1 - b0) * 8u);
-  float* edst = slot + a.nin + wave * (256 * a.QE);
-  for (int q = 0; q < a.QE; q++) lds_dma_dwordx4(ersrc, edst + 256 * q, 16u * (64 * q + lane), 0u);
-  const int ncl = __builtin_amdgcn_readfirstlane(min(a.Cc, a.C - c0));
-  int issued = a.QE;
+// Producer: issue the input loads of one step (channels [c0, c0 + ncl) of a tile) into a
+// ring slot, block by block (blocks of 256 words with 16-byte loads, or of 64 words).
+// Returns the number of loads issued.  voff0..voff3 hold the first blocks' offsets for the
+// tile; further blocks are computed on the fly.
+__device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int n0, int c0, int ncl,
+                                          const uint32_t (&voffc)[4], float* slot, int lane) {
   const int bw = a.wide16 ? 256 : 64;
-  int blk = p0 / a.Cc;
-  int cl = p0 - blk * a.Cc;
-  int p = p0;
-  while (p < p1) {
-    const uint32_t voff = a.wide16 ? block_voff16(a, I0, n0, blk, lane) : block_voff(a, I0, n0, blk, lane);
-    const int cend = min(a.Cc, cl + (p1 - p));  // channels of this block in the share
-    const int cstop = min(cend, ncl);
-    const float* dst = slot + blk * bw + cl * a.CHS;
-    uint32_t soff = 4u * (uint32_t)((c0 + cl) * a.HW);
+  for (int blk = 0; blk < a.nsb; blk++) {
+    // explicit selects keep the cached offsets in registers (no indexed private array)
+    const uint32_t voff = blk == 0 ? voffc[0]
+                          : blk == 1 ? voffc[1]
+                          : blk == 2 ? voffc[2]
+                          : blk == 3 ? voffc[3]
+                          : (a.wide16 ? block_voff16(a, I0, n0, blk, lane) : block_voff(a, I0, n0, blk, lane));
+    const float* dst = slot + blk * bw;
+    uint32_t soff = 4u * (uint32_t)(c0 * a.HW);
     if (a.wide16) {
-      for (int c = cl; c < cstop; c++) {
+      for (int c = 0; c < ncl; c++) {
         lds_dma_dwordx4(rsrc, dst, voff, soff);
         dst += a.CHS;
         soff += 4u * (uint32_t)a.HW;
       }
     } else {
-      for (int c = cl; c < cstop; c++) {
+      for (int c = 0; c < ncl; c++) {
         lds_dma_dword(rsrc, dst, voff, soff);
         dst += a.CHS;
         soff += 4u * (uint32_t)a.HW;
       }
     }
-    issued += cstop - cl;
-    p += cend - cl;
-    cl = 0;
-    blk++;
   }
-  if (a.D > 2)
-    for (; issued < a.QB; issued++) lds_dma_dwordx4(ersrc, edst, 16u * lane, 0u);
+  return a.nsb * ncl;
+}
+
+// Consumer: copy its block of non-zeros (stream entries [b0, b1), an even count) into its
+// private part of a ring slot: QE 16-byte loads of 128 entries; entries past the block's
+// end load as 0.
+__device__ __forceinline__ void stage_entries(const KArgs& a, const uint2* __restrict__ ent, int b0, int b1,
+                                              float* edst, int lane) {
+  const v4i ersrc = make_rsrc(ent + b0, (uint32_t)(b1 - b0) * 8u);
+  for (int q = 0; q < a.QE; q++) lds_dma_dwordx4(ersrc, edst + 256 * q, 16u * (64 * q + lane), 0u);
 }
 
 // Output word offset (without the channel term) of each of the lane's K positions, or -1.
@@ -325,89 +324,118 @@ __device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)
   }
 }
 
-// Pointers are separate restrict-qualified arguments so the compiler knows the streams
-// are read-only.
-template <int K, int OCW, int NW>
-__global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
-    const KArgs a, const float* __restrict__ x, float* __restrict__ y,
-    const uint2* __restrict__ ent, const int* __restrict__ bstart,
-    const int* __restrict__ slot_row) {
-  constexpr int T = NW * 64;
-  extern __shared__ float lds[];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int* bst = reinterpret_cast<int*>(lds + a.D * a.slot_words);
-
-  const int b = xcd_logical(blockIdx.x, gridDim.x);
-  const long long units = (long long)a.ntiles * a.G;
-  const int u0 = (int)(units * b / gridDim.x);
-  const int u1 = (int)(units * (b + 1) / gridDim.x);
-  const int S = (u1 - u0) * a.nch;
-  if (S == 0) return;
-
-  for (int i = threadIdx.x; i < a.G * NW * (a.nch + 1); i += T) bst[i] = bstart[i];
-  __syncthreads();
-
-  // this wavefront's share of a step's (block, channel) loads
-  const int P = a.nsb * a.Cc;
-  const int p0 = __builtin_amdgcn_readfirstlane((int)((long long)P * wave / NW));
-  const int p1 = __builtin_amdgcn_readfirstlane((int)((long long)P * (wave + 1) / NW));
-
-  // issue side: the next step to stage (unit = tile * G + g, chunk is_k, ring slot is_buf)
-  int is_tile = u0 / a.G, is_g = u0 - (u0 / a.G) * a.G, is_k = 0, is_buf = 0, is_new_tile = 1;
-  int is_I0 = 0, is_n0 = 0;
-  v4i rsrc = make_rsrc(x, 0u);
-  auto issue = [&]() {
-    if (is_new_tile) {
-      is_I0 = is_tile * (64 * K);
-      is_n0 = is_I0 / a.img_ext;
-      const long long first = (long long)is_n0 * a.C * a.HW;
-      rsrc = make_rsrc(x + first, (uint32_t)min((a.x_words - first) * 4, 0x7ffffff0LL));
-      is_new_tile = 0;
-    }
-    const int* bw = bst + (is_g * NW + wave) * (a.nch + 1) + is_k;
-    stage_step<T>(a, ent, bw[0], bw[1], rsrc, is_I0, is_n0, is_k * a.Cc, p0, p1, lds + is_buf * a.slot_words,
-                  wave, lane);
-    if (++is_buf == a.D) is_buf = 0;
-    if (++is_k == a.nch) {
-      is_k = 0;
-      if (++is_g == a.G) {
-        is_g = 0;
-        is_tile++;
-        is_new_tile = 1;
+// Step iterator over a workgroup's run of units: unit = tile * G + g, then chunk k.
+struct StepIt {
+  int tile, g, k;
+  __device__ __forceinline__ void next(const KArgs& a) {
+    if (++k == a.nch) {
+      k = 0;
+      if (++g == a.G) {
+        g = 0;
+        tile++;
       }
     }
-  };
-  for (int s = 0; s < a.D - 1 && s < S; s++) issue();
+  }
+};
 
+template <int K, int NW>
+__device__ __forceinline__ void producer(const KArgs& a, const float* __restrict__ x, StepIt it, int S,
+                                         uint32_t* ready, uint32_t* done, float* lds, int lane) {
+  constexpr int NC = NW - 1;
+  int cur_tile = -1, I0 = 0, n0 = 0;
+  v4i rsrc = make_rsrc(x, 0u);
+  uint32_t voffc[4] = {kOutOfRange, kOutOfRange, kOutOfRange, kOutOfRange};
+  int pending = -1;  // the step whose loads were issued but not yet published
+  for (int t = 0; t < S; t++) {
+    const int buf = t % a.D;
+    // the slot held step t - D: wait until every consumer has released it
+    if (t >= a.D) lds_wait_ge(&done[buf], (uint32_t)(NC * (t / a.D)));
+    if (it.tile != cur_tile) {
+      cur_tile = it.tile;
+      I0 = cur_tile * (64 * K);
+      n0 = I0 / a.img_ext;
+      const long long first = (long long)n0 * a.C * a.HW;
+      rsrc = make_rsrc(x + first, (uint32_t)min((a.x_words - first) * 4, 0x7ffffff0LL));
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        voffc[i] = a.wide16 ? block_voff16(a, I0, n0, i, lane) : block_voff(a, I0, n0, i, lane);
+    }
+    const int c0 = it.k * a.Cc;
+    const int ncl = __builtin_amdgcn_readfirstlane(min(a.Cc, a.C - c0));
+    const int n = stage_rows(a, rsrc, I0, n0, c0, ncl, voffc, lds + buf * a.slot_words, lane);
+    if (pending >= 0) {
+      // step t-1 landed once at most this step's n loads are outstanding
+      wait_vmcnt(n <= 63 ? n : 0);
+      __hip_atomic_store(&ready[pending % a.D], (uint32_t)(pending / a.D + 1), __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (n > 63) {  // everything landed: publish this step too
+        __hip_atomic_store(&ready[buf], (uint32_t)(t / a.D + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        pending = -1;
+      } else {
+        pending = t;
+      }
+    } else {
+      pending = t;
+    }
+    it.next(a);
+  }
+  if (pending >= 0) {
+    wait_vmcnt(0);
+    __hip_atomic_store(&ready[pending % a.D], (uint32_t)(pending / a.D + 1), __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+template <int K, int OCW, int NW>
+__device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, const uint2* __restrict__ ent,
+                                         const int* bst, const int* __restrict__ slot_row, StepIt it, int S,
+                                         const uint32_t* ready, uint32_t* done, float* lds, int c, int lane) {
+  constexpr int NC = NW - 1;
+  const int ew = 256 * a.QE;  // words of a consumer's private part of a slot
+  // entries of steps 0 .. D-1 ahead of time
+  StepIt is = it;
+  for (int t = 0; t < a.D && t < S; t++) {
+    const int* bw = bst + (is.g * NC + c) * (a.nch + 1) + is.k;
+    stage_entries(a, ent, bw[0], bw[1], lds + t * a.slot_words + a.nin + c * ew, lane);
+    is.next(a);
+  }
   float acc[OCW][K];
 #pragma unroll
   for (int o = 0; o < OCW; o++)
 #pragma unroll
     for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
-
-  int tile = u0 / a.G, g = u0 - (u0 / a.G) * a.G, ck = 0, cbuf = 0;
-  int drained = 0;  // a unit's stores were issued since the last wait: wait for everything
+  int drained = 0;  // stores were issued since the last wait: wait for everything
   for (int s = 0; s < S; s++) {
-    // loads issued after step s's: those of steps s+1 .. min(s+D-2, S-1)
-    const int later = drained ? 0 : a.QB * min(a.D - 2, S - 1 - s);
-    step_barrier(later);  // step s landed; every wavefront is done with step s-1's slot
+    const int buf = s % a.D;
+    // own entries of step s landed: later entry loads outstanding are those of steps
+    // s+1 .. min(s+D-1, S-1)
+    wait_vmcnt(drained ? 0 : a.QE * min(a.D - 1, S - 1 - s));
     drained = 0;
-    const bool more = s + a.D - 1 < S;
-    if (more && !a.issue_late) issue();
-    const float* slot = lds + cbuf * a.slot_words;
-    Walk w = walk_begin<OCW, NW>(a, slot, wave, lane);
+    lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
+    const float* slot = lds + buf * a.slot_words;
+    Walk w = walk_begin<OCW, NW>(a, slot, c, lane);
     walk_slots<K, OCW, NW, 0, OCW>(a, w, acc, slot + lane, lane, [](int) {});
-    // issued late, the loads of step s+D-1 overlap the wait at the next barrier; their
-    // slot held step s-1, which every wavefront finished before this step's barrier
-    if (more && a.issue_late) issue();
-    if (ck + 1 == a.nch) {
+    // release the slot's input part (the walk's LDS reads are complete before the add);
+    // one lane adds, so the counter advances by one per consumer
+    uint32_t before = 0;
+    if (lane == 0) before = __hip_atomic_fetch_add(&done[buf], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // wave priority from this consumer's finishing rank on the step: the issue arbiter
+    // favours older waves, so without this the highest-index consumers lag behind and
+    // hold up the refill of their slots
+    const int rank = __builtin_amdgcn_readfirstlane((int)(before - (uint32_t)(NC * (s / a.D))));
+    if (rank >= NC - 4)
+      __builtin_amdgcn_s_setprio(2);
+    else if (2 * rank >= NC)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+    if (it.k + 1 == a.nch) {
       int ob[K];
-      output_bases<K>(a, tile * (64 * K), lane, ob);
+      output_bases<K>(a, it.tile * (64 * K), lane, ob);
       const int plane = a.E * a.F;
 #pragma unroll
       for (int o = 0; o < OCW; o++) {
-        const int row = slot_row[(g * NW + wave) * OCW + o];
+        const int row = slot_row[(it.g * NC + c) * OCW + o];
         if (row >= 0) {
 #pragma unroll
           for (int q = 0; q < K; q++)
@@ -418,29 +446,62 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
       }
       drained = 1;
     }
-    if (++cbuf == a.D) cbuf = 0;
-    if (++ck == a.nch) {
-      ck = 0;
-      if (++g == a.G) {
-        g = 0;
-        tile++;
-      }
+    // the private part of this slot is free again: entries of step s + D
+    if (s + a.D < S) {
+      const int* bw = bst + (is.g * NC + c) * (a.nch + 1) + is.k;
+      stage_entries(a, ent, bw[0], bw[1], lds + buf * a.slot_words + a.nin + c * ew, lane);
+      is.next(a);
     }
+    it.next(a);
   }
+}
+
+// Pointers are separate restrict-qualified arguments so the compiler knows the streams
+// are read-only.
+template <int K, int OCW, int NW>
+__global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
+    const KArgs a, const float* __restrict__ x, float* __restrict__ y,
+    const uint2* __restrict__ ent, const int* __restrict__ bstart,
+    const int* __restrict__ slot_row) {
+  constexpr int T = NW * 64;
+  constexpr int NC = NW - 1;
+  extern __shared__ float lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* ready = reinterpret_cast<uint32_t*>(lds + a.D * a.slot_words);
+  uint32_t* done = ready + kMaxDepth;
+  int* bst = reinterpret_cast<int*>(done + kMaxDepth);
+
+  const int b = xcd_logical(blockIdx.x, gridDim.x);
+  const long long units = (long long)a.ntiles * a.G;
+  const int u0 = (int)(units * b / gridDim.x);
+  const int u1 = (int)(units * (b + 1) / gridDim.x);
+  const int S = (u1 - u0) * a.nch;
+  if (S == 0) return;
+
+  if (threadIdx.x < 2 * kMaxDepth) ready[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < a.G * NC * (a.nch + 1); i += T) bst[i] = bstart[i];
+  __syncthreads();
+
+  StepIt it{u0 / a.G, u0 - (u0 / a.G) * a.G, 0};
+  if (wave == NC) __builtin_amdgcn_s_setprio(3);  // the producer must never starve
+  if (wave == NC)
+    producer<K, NW>(a, x, it, S, ready, done, lds, lane);
+  else
+    consumer<K, OCW, NW>(a, y, ent, bst, slot_row, it, S, ready, done, lds, wave, lane);
 }
 
 using SparseFn = void (*)(KArgs, const float*, float*, const uint2*, const int*, const int*);
 
 #define SC_FOR_EACH_KO(X, NW) \
-  X(1, 1, NW) X(1, 2, NW) X(1, 4, NW) X(1, 8, NW) X(1, 16, NW) \
-  X(2, 1, NW) X(2, 2, NW) X(2, 4, NW) X(2, 8, NW) X(2, 16, NW) \
-  X(4, 1, NW) X(4, 2, NW) X(4, 4, NW) X(4, 8, NW) X(4, 16, NW) \
-  X(8, 1, NW) X(8, 2, NW) X(8, 4, NW) X(8, 8, NW) \
-  X(16, 1, NW) X(16, 2, NW) X(16, 4, NW)
+  X(1, 1, NW) X(2, 1, NW) X(4, 1, NW) X(6, 1, NW) X(7, 1, NW) X(8, 1, NW) X(12, 1, NW) X(16, 1, NW) \
+  X(1, 2, NW) X(2, 2, NW) X(4, 2, NW) X(6, 2, NW) X(7, 2, NW) X(8, 2, NW) X(12, 2, NW) X(16, 2, NW) \
+  X(1, 3, NW) X(2, 3, NW) X(4, 3, NW) X(6, 3, NW) X(7, 3, NW) X(8, 3, NW) X(12, 3, NW) X(16, 3, NW) \
+  X(1, 5, NW) X(2, 5, NW) X(4, 5, NW) X(6, 5, NW) X(7, 5, NW) X(8, 5, NW) X(12, 5, NW) \
+  X(1, 9, NW) X(2, 9, NW) X(4, 9, NW) X(6, 9, NW) X(7, 9, NW)
 
 static SparseFn pick_sparse(const Plan& p) {
 #define SC_CASE(KK, OO, WW) if (p.K == KK && p.OCW == OO && p.NW == WW) return sparse_direct_fwd<KK, OO, WW>;
-  SC_FOR_EACH_KO(SC_CASE, 8)
   SC_FOR_EACH_KO(SC_CASE, 16)
 #undef SC_CASE
   return nullptr;

@@ -45,8 +45,8 @@ static int env_int(const char* s, const char* key, int dflt) {
   return std::atoi(p + 1);
 }
 
-// Deal rows to (group, wavefront, slot).  The kernel synchronises the wavefronts of a
-// workgroup once per chunk, so a step lasts as long as its busiest wavefront: each row is
+// Deal rows to (group, consumer wavefront, slot).  A workgroup's consumers share each
+// chunk's ring slot, so a step is released only when its busiest consumer is done: each row is
 // described by its per-chunk entry counts (padded to even, as stored) and rows are dealt
 // largest first to the wavefront with a free slot that least increases the sum over chunks
 // of the busiest wavefront's count (ties: the smaller total, then the lower index).  With
@@ -54,7 +54,7 @@ static int env_int(const char* s, const char* key, int dflt) {
 // with room.  Empty rows weigh 1 so that they are spread too.
 static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const std::vector<int32_t>& rowptr,
                                           const std::vector<int32_t>& col, int32_t* max_wave_nnz) {
-  const int M = g.M, NW = p.NW, OCW = p.OCW, G = p.G, nch = p.nch, RS = g.R * g.S;
+  const int M = g.M, NC = p.NW - 1, OCW = p.OCW, G = p.G, nch = p.nch, RS = g.R * g.S;
   std::vector<int32_t> vec((size_t)M * nch, 0);
   std::vector<long long> tot(M, 1);
   for (int m = 0; m < M; m++) {
@@ -75,16 +75,16 @@ static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const st
     for (int m : order) {
       int best = -1;
       for (int q = 0; q < G; q++)
-        if ((int)grp[q].size() < NW * OCW && (best < 0 || gl[q] < gl[best])) best = q;
+        if ((int)grp[q].size() < NC * OCW && (best < 0 || gl[q] < gl[best])) best = q;
       grp[best].push_back(m);  // stays in largest-first order
       gl[best] += tot[m];
     }
   }
-  std::vector<int32_t> slot_row((size_t)G * NW * OCW, -1);
+  std::vector<int32_t> slot_row((size_t)G * NC * OCW, -1);
   long long mwn = 0;
-  std::vector<long long> load((size_t)NW * nch), wt(NW);
+  std::vector<long long> load((size_t)NC * nch), wt(NC);
   std::vector<long long> gmax(nch);
-  std::vector<int> cnt(NW);
+  std::vector<int> cnt(NC);
   for (int q = 0; q < G; q++) {
     std::fill(load.begin(), load.end(), 0);
     std::fill(wt.begin(), wt.end(), 0);
@@ -94,7 +94,7 @@ static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const st
       const int32_t* v = &vec[(size_t)m * nch];
       int best = -1;
       long long bcost = 0;
-      for (int w = 0; w < NW; w++) {
+      for (int w = 0; w < NC; w++) {
         if (cnt[w] >= OCW) continue;
         long long cost = 0;
         for (int k = 0; k < nch; k++) cost += std::max(gmax[k], load[(size_t)w * nch + k] + v[k]);
@@ -109,13 +109,13 @@ static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const st
         gmax[k] = std::max(gmax[k], l);
       }
       wt[best] += tot[m];
-      slot_row[((size_t)q * NW + best) * OCW + cnt[best]] = m;
+      slot_row[((size_t)q * NC + best) * OCW + cnt[best]] = m;
       cnt[best]++;
     }
-    for (int w = 0; w < NW; w++) {
+    for (int w = 0; w < NC; w++) {
       long long nz = 0;
       for (int o = 0; o < OCW; o++) {
-        const int m = slot_row[((size_t)q * NW + w) * OCW + o];
+        const int m = slot_row[((size_t)q * NC + w) * OCW + o];
         if (m >= 0) nz += rowptr[m + 1] - rowptr[m];
       }
       mwn = std::max(mwn, nz);
@@ -127,13 +127,12 @@ static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const st
 
 int block_header(int OCW) { return (OCW + 1) & ~1; }
 
-// Input layout for K positions per lane with D ring slots whose non-zero part takes
-// QE loads per wavefront: the largest chunk that fits the LDS beside the block-start table
-// and keeps QE + QR loads per wavefront per step within what the counted wait can express
-// (vmcnt <= 63 covers the D-2 later steps in flight).  Chunks are then evened out:
-// nch = ceil(C / Cc_max) chunks of about C / nch channels.
-static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, Plan* p) {
-  const int T = 64 * p->NW;
+// Input layout for K positions per lane with D ring slots whose non-zero part takes QE
+// loads per consumer: the largest chunk that fits the LDS beside the counters and the
+// block-start table.  Chunks are then evened out: nch = ceil(C / Cc_max) chunks of about
+// C / nch channels.
+static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds_max, Plan* p) {
+  const int NC = p->NW - 1;
   p->K = K;
   p->D = D;
   p->QE = QE;
@@ -143,28 +142,21 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, Plan* p
   if (chs > (1 << 24)) return false;
   p->CHS = (int)chs;
   p->nblk = p->CHS / 64;
-  const int qmax = D > 2 ? 63 / (D - 2) : 63;
   int nch = 1;
   for (int it = 0; it < 16; it++) {  // the block-start table grows with the chunk count
-    const long long table = 4LL * p->G * p->NW * (nch + 1);
-    const long long room = (kLdsMax - table) / (4LL * D) - (long long)QE * 4 * T;  // row words per slot
+    const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth;
+    const long long room = (lds_max - fixed) / (4LL * D) - (long long)QE * 256 * NC;  // row words per slot
     if (room < p->CHS) return false;
     int cc = (int)std::min<long long>(g.C, room / p->CHS);
     if (cc_cap > 0) cc = std::min(cc, cc_cap);
-    // the 4-byte count bounds both (it is used when the wide layout meets a misaligned input)
-    while (cc > 0 && QE + (p->nblk * cc + p->NW - 1) / p->NW > qmax) cc--;
-    if (cc < 1) return false;
     const int n2 = (g.C + cc - 1) / cc;
     if (n2 <= nch) break;
     nch = n2;
   }
   p->Cc = (g.C + nch - 1) / nch;
   p->nch = (g.C + p->Cc - 1) / p->Cc;  // every chunk non-empty
-  p->QR1 = (p->nblk * p->Cc + p->NW - 1) / p->NW;
-  p->QR = g.wide ? (p->nblk / 4 * p->Cc + p->NW - 1) / p->NW : p->QR1;
-  p->QB = p->QE + p->QR;
   p->nin = p->Cc * p->CHS;
-  p->slot_words = p->nin + QE * 4 * T;
+  p->slot_words = p->nin + QE * 256 * NC;
   return true;
 }
 
@@ -180,7 +172,7 @@ static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& r
   std::vector<long long> kmax((size_t)p.G * p.nch, 0), ksum((size_t)p.G * p.nch, 0);
   int best = 0;
   for (size_t wv = 0; wv < slot_row.size() / p.OCW; wv++) {
-    const size_t q = wv / p.NW;
+    const size_t q = wv / (p.NW - 1);
     std::fill(tot.begin(), tot.end(), 0);
     for (int o = 0; o < p.OCW; o++) {
       const int m = slot_row[wv * p.OCW + o];
@@ -201,57 +193,75 @@ static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& r
       mx += kmax[i];
       sm += ksum[i];
     }
-    *step_permille = sm > 0 ? (int32_t)(1000.0 * (double)mx * p.NW / (double)sm + 0.5) : 1000;
+    *step_permille = sm > 0 ? (int32_t)(1000.0 * (double)mx * (p.NW - 1) / (double)sm + 0.5) : 1000;
   }
   return best;
 }
 
-// Launch plan.  K (positions per lane) trades staging overhead (the filter's reach past
-// the tile) against the number of work units; OCW (channel slots per wavefront) is the
-// smallest power of two that lets one workgroup hold all output channels, capped at 8,
-// and G work units share a tile when M needs more slots.  D ring slots (2 by default: one
-// chunk in flight while one is computed) share the CU's LDS; large chunks mean few steps
-// and few per-step synchronisations.  QE is the smallest number of 128-entry loads that holds every
-// wavefront's block of non-zeros for one chunk.
-// SPARSECONV_PLAN="K=..,OCW=..,NW=..,D=..,CC=.." overrides the choice (tuning only).
+// Launch plan.  A workgroup has NW = 16 wavefronts: NC = 15 consumers with OCW output-
+// channel slots each and one producer.  OCW is the smallest instantiated count (1, 2, 3, 5,
+// 9) that lets one workgroup hold all output channels, else 9 with G groups of channels per
+// tile.  K (positions per lane) trades staging overhead (the filter's reach past the
+// tile) against the number of work units: the largest instantiated K with OCW*K <= 64
+// accumulators, capped by the image size.  D ring slots (3 by default: a consumer may run
+// a step ahead of the slowest) share the CU's LDS with the counters and the block-start
+// table; large chunks mean few steps.  QE is the smallest number of 128-entry loads that
+// holds every consumer's block of non-zeros for one chunk.
+// SPARSECONV_PLAN="K=..,OCW=..,D=..,CC=..,LDSKB=..,NARROW" overrides the choice (tuning only).
+static bool instantiated(int K, int OCW) {
+  static const int kk[] = {1, 2, 4, 6, 7, 8, 12, 16};
+  static const int oo[] = {1, 2, 3, 5, 9};
+  bool okk = false, oko = false;
+  for (int v : kk) okk = okk || v == K;
+  for (int v : oo) oko = oko || v == OCW;
+  return okk && oko && K * OCW <= 64;
+}
+
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                  std::vector<int32_t>* slot_row, int32_t* max_wave_nnz) {
+  static const int kOcw[] = {1, 2, 3, 5, 9};
+  static const int kKs[] = {16, 12, 8, 7, 6, 4, 2, 1};
   Plan p{};
+  p.NW = 16;
+  const int NC = p.NW - 1;
   const long long img_ext = (long long)g.HYp * g.Pp;
-  int K = img_ext >= 4096 ? 8 : img_ext >= 1024 ? 4 : img_ext >= 256 ? 2 : 1;
-  int NW = 16;
-  int OCW = 1;
-  while (OCW < 8 && OCW * NW < g.M) OCW *= 2;
+  const int kmax = img_ext >= 4096 ? 8 : img_ext >= 1024 ? 4 : img_ext >= 256 ? 2 : 1;
+  int OCW = 9;
+  for (int o : kOcw)
+    if (NC * o >= g.M) {
+      OCW = o;
+      break;
+    }
   const char* env = std::getenv("SPARSECONV_PLAN");
-  K = env_int(env, "K", K);
-  NW = env_int(env, "NW", NW);
   OCW = env_int(env, "OCW", OCW);
-  int D = env_int(env, "D", 2);
-  const int issue_late = env_int(env, "LATE", 0);
+  const int kenv = env_int(env, "K", 0);
+  int D = env_int(env, "D", 3);
   const int cc_cap = env_int(env, "CC", 0);
-  if (K != 1 && K != 2 && K != 4 && K != 8 && K != 16) K = 4;
-  if (OCW != 1 && OCW != 2 && OCW != 4 && OCW != 8 && OCW != 16) OCW = 8;
-  if (NW != 8 && NW != 16) NW = 16;
-  if (D < 2 || D > 4) D = 2;
-  while (OCW * K > 64 && K > 1) K /= 2;
-  p.NW = NW;
-  for (int ocw = OCW; ocw >= 1; ocw /= 2) {
-    p.issue_late = issue_late != 0 ? 1 : 0;
-    p.OCW = ocw;
-    p.G = (g.M + NW * ocw - 1) / (NW * ocw);
-    for (int k = K; k >= 1; k /= 2) {
+  const int lds_max = std::min(kLdsMax, 1024 * env_int(env, "LDSKB", kLdsMax / 1024));
+  if (D < 2 || D > kMaxDepth) D = 3;
+  bool oko = false;
+  for (int o : kOcw) oko = oko || o == OCW;
+  if (!oko) OCW = 9;
+  // fewer slots per consumer (more groups) when the blocks of non-zeros do not fit
+  for (int oi = 4; oi >= 0; oi--) {
+    if (kOcw[oi] > OCW) continue;
+    p.OCW = kOcw[oi];
+    p.G = (g.M + NC * p.OCW - 1) / (NC * p.OCW);
+    for (int k : kKs) {
+      if (!instantiated(k, p.OCW)) continue;
+      if (kenv > 0 ? k > kenv : k > kmax) continue;
       bool ok = false;
       int32_t mwn = 0;
       std::vector<int32_t> sr;
-      for (int qe = 1; qe <= 63 && !ok; qe++) {
-        if (!fill_layout(g, k, D, qe, cc_cap, &p)) break;
+      for (int qe = 1; qe <= 64 && !ok; qe++) {
+        if (!fill_layout(g, k, D, qe, cc_cap, lds_max, &p)) break;
         sr = schedule_rows(g, p, rowptr, col, &mwn);
         if (max_block(g, p, rowptr, col, sr, &p.step_permille) <= 128 * qe) ok = true;
       }
       if (!ok) continue;
-      const int table = p.G * NW * (p.nch + 1);
-      p.lds_bytes = 4 * p.D * p.slot_words + 4 * table;
-      if (p.lds_bytes > kLdsMax) continue;
+      const int table = p.G * NC * (p.nch + 1);
+      p.lds_bytes = 4 * p.D * p.slot_words + 8 * kMaxDepth + 4 * table;
+      if (p.lds_bytes > lds_max) continue;
       p.span_images = (int)((p.PL + img_ext - 2) / img_ext + 1);
       if (slot_row) *slot_row = sr;
       if (max_wave_nnz) *max_wave_nnz = mwn;

@@ -35,6 +35,7 @@
 namespace sc {
 
 constexpr int kLdsMax = 160 * 1024;     // LDS per CU
+constexpr int kMaxDepth = 4;            // most LDS ring slots (ready/done counter pairs)
 
 struct Geom {
   int M, C, R, S, H, W, st, pad;
@@ -49,7 +50,7 @@ struct Geom {
 struct Plan {
   int K;           // extended output positions per lane (64 apart)
   int OCW;         // output-channel slots per wavefront
-  int NW;          // wavefronts per workgroup (8 or 16)
+  int NW;          // wavefronts per workgroup: NW-1 consumers (OCW slots each) + 1 producer
   int G;           // output-channel groups (work units per tile)
   int Cc;          // channels staged per chunk
   int nch;         // number of chunks = ceil(C / Cc)
@@ -58,19 +59,13 @@ struct Plan {
   int nblk;        // 64-word blocks per staged channel = CHS / 64 (CHS a multiple of 256
                    // in the wide layout: nblk/4 blocks of 256 words)
   int D;           // LDS ring slots: D-1 chunks in flight
-  int QE;          // 16-byte loads per wavefront per step carrying its block of non-zeros
+  int QE;          // 16-byte loads per consumer per step carrying its block of non-zeros
                    // (128 entries each)
-  int QR;          // loads per wavefront per step carrying input rows: ceil(nblk*Cc/NW)
-                   // 4-byte loads, or ceil(nblk/4*Cc/NW) 16-byte loads in the wide layout
-  int QR1;         // the 4-byte count, used in the wide layout when the input pointer is not
-                   // 16-byte aligned
-  int QB;          // loads per wavefront per step, QE + QR (padded with repeats)
   int nin;         // words of a ring slot holding input rows = Cc*CHS
-  int slot_words;  // words of one ring slot = nin + QE*256*NW
-  int lds_bytes;   // D ring slots + block-start table
+  int slot_words;  // words of one ring slot = nin + QE*256*(NW-1)
+  int lds_bytes;   // D ring slots + ready/done counters + block-start table
   int span_images; // most images one tile's staged range can touch
   int step_permille;  // 1000 * sum over chunks of the busiest wavefront's entries / mean
-  int issue_late;     // 1: staging loads are issued after a step's walk, 0: before it
 };
 
 // Kernel arguments (by value).
@@ -78,16 +73,14 @@ struct KArgs {
   const float* x;
   float* y;
   const uint32_t* ent;    // sparse: pairs {enc, value bits}
-  const int32_t* seg;     // sparse: [(group*NW + wave)*(nch+1) + k] -> first entry of block k
-  const int* slot_row;    // sparse: [group][wave][slot] -> output channel or -1
+  const int32_t* seg;     // sparse: [(group*NC + consumer)*(nch+1) + k] -> first entry of block k
+  const int* slot_row;    // sparse: [group][consumer][slot] -> output channel or -1
   int N, C, H, W, M, E, F, R, S, st, pad;
   int Pp, HYp, img_ext;   // img_ext = HYp * Pp
   int xoff, cshift;       // see Geom
   int wide16;             // 1: stage rows with 16-byte loads (wide layout, aligned input)
   int nsb;                // staging blocks per channel: nblk/4 of 256 words (wide16) or nblk
-  int PL, CHS, nblk, Cc, nch, G, D, QE, QR, QB, nin, slot_words;
-  int issue_late;         // 1: a step's staging loads are issued after the walk of the step
-                          // D-1 before it (D >= 3), 0: at the start of that step
+  int PL, CHS, nblk, Cc, nch, G, D, QE, nin, slot_words;
   int HW;                 // H * W
   int ntiles;             // tiles of 64*K extended positions
   long long x_words;      // N * C * H * W
