@@ -88,12 +88,16 @@ typedef struct {
   int32_t chunk_channels;/* launch plan: input channels staged in LDS at a time */
   int32_t lds_bytes;     /* launch plan: dynamic LDS per workgroup */
   int32_t max_wave_nnz;  /* largest non-zero count given to one wavefront */
-  int32_t waves_per_group;  /* launch plan: wavefronts per workgroup */
-  int32_t pipeline_depth;   /* launch plan: LDS chunk buffers (depth-1 chunks in flight) */
+  int32_t waves_per_group;  /* launch plan: computing wavefronts per workgroup (one more
+                               wavefront copies the input into LDS) */
+  int32_t pipeline_depth;   /* launch plan: LDS ring slots (up to depth-1 chunks staged
+                               ahead of the one being computed) */
   int32_t step_balance_permille; /* 1000 * (sum over chunks of the busiest wavefront's
                                     non-zero entries) / (sum of the means): the cost of
                                     synchronising the wavefronts once per chunk (>= 1000) */
-  int32_t reserved;
+  int32_t split_pieces;  /* rows longer than a wavefront's fair share are split into pieces
+                            held by different wavefronts and summed in a fixed order at the
+                            end of a work unit: the number of pieces beyond the first */
 } sc_info;
 
 /*

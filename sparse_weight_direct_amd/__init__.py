@@ -53,11 +53,11 @@ class sc_info(ctypes.Structure):
                [("nnz", ctypes.c_int64), ("packed_bytes", ctypes.c_int64), ("device_bytes", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
-                                               "pipeline_depth", "step_balance_permille")] + \
-               [("reserved", ctypes.c_int32)]
+                                               "pipeline_depth", "step_balance_permille",
+                                               "split_pieces")]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _vp, _i32, _u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32

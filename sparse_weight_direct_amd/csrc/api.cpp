@@ -48,6 +48,7 @@ struct sc_handle {
   std::vector<uint32_t> off;     // canonical stretched offsets
   std::vector<float> val;        // canonical values
   int32_t max_wave_nnz;
+  int32_t split_pieces;
   int device;
   bool host_only;
   void* dmem;
@@ -55,6 +56,7 @@ struct sc_handle {
   const uint32_t* d_ent;
   const int32_t* d_seg;
   const int32_t* d_slot;
+  const int32_t* d_comb;
 };
 
 namespace {
@@ -153,9 +155,9 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     sc_status s = build_csr(w, M, crs, (flags & SC_PACK_ALL_TAPS) != 0, rowptr, col, val);
     if (s != SC_OK) return s;
     const long long nnz = (long long)col.size();
-    std::vector<int32_t> slot_row;
-    int32_t max_wave_nnz = 0;
-    sc::Plan p = sc::choose_plan(g, rowptr, col, &slot_row, &max_wave_nnz);
+    sc::Sched sched;
+    sc::Plan p = sc::choose_plan(g, rowptr, col, &sched);
+    const int32_t max_wave_nnz = sched.max_wave_nnz;
     if (p.K == 0) return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
@@ -165,6 +167,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->nnz = nnz;
     h->host_only = (flags & SC_PACK_HOST_ONLY) != 0;
     h->max_wave_nnz = max_wave_nnz;
+    h->split_pieces = sched.split_pieces;
     h->dmem = nullptr;
     h->dbytes = 0;
     h->off.resize(nnz);
@@ -205,11 +208,13 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         const size_t hdr = pos;
         pos += hdr_n;
         for (int o = 0; o < p.OCW; o++) {
-          const int m = slot_row[(size_t)wv * p.OCW + o];
+          const size_t sl = (size_t)wv * p.OCW + o;
+          const int m = sched.src_row[sl];
           int cnt = 0;
-          if (m >= 0) {
-            const int b = chunk_start[(size_t)m * (p.nch + 1) + k];
-            const int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
+          if (m >= 0) {  // this slot's piece of row m: part of the row's entries of chunk k
+            int b = chunk_start[(size_t)m * (p.nch + 1) + k];
+            int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
+            sc::piece_range(b, e, sched.piece[sl], sched.npieces[sl], &b, &e);
             for (int j = b; j < e; j++) {
               const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
               const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
@@ -242,8 +247,9 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
       const size_t b_ent = al(ent.size() * 4);
       const size_t b_seg = al(bstart.size() * 4);
-      const size_t b_slot = al(slot_row.size() * 4);
-      h->dbytes = b_ent + b_seg + b_slot;
+      const size_t b_slot = al(sched.slot_row.size() * 4);
+      const size_t b_comb = al(sched.slot_comb.size() * 4);
+      h->dbytes = b_ent + b_seg + b_slot + b_comb;
       if (hipMalloc(&h->dmem, h->dbytes) != hipSuccess) {
         h->dmem = nullptr;
         sparseconv_destroy(h);
@@ -253,10 +259,14 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       h->d_ent = reinterpret_cast<const uint32_t*>(base);
       h->d_seg = reinterpret_cast<const int32_t*>(base + b_ent);
       h->d_slot = reinterpret_cast<const int32_t*>(base + b_ent + b_seg);
+      h->d_comb = reinterpret_cast<const int32_t*>(base + b_ent + b_seg + b_slot);
       hipError_t e1 = hipMemcpy(base, ent.data(), ent.size() * 4, hipMemcpyHostToDevice);
       hipError_t e2 = hipMemcpy(base + b_ent, bstart.data(), bstart.size() * 4, hipMemcpyHostToDevice);
-      hipError_t e3 = hipMemcpy(base + b_ent + b_seg, slot_row.data(), slot_row.size() * 4, hipMemcpyHostToDevice);
-      if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+      hipError_t e3 = hipMemcpy(base + b_ent + b_seg, sched.slot_row.data(), sched.slot_row.size() * 4,
+                                hipMemcpyHostToDevice);
+      hipError_t e4 = hipMemcpy(base + b_ent + b_seg + b_slot, sched.slot_comb.data(), sched.slot_comb.size() * 4,
+                                hipMemcpyHostToDevice);
+      if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess) {
         sparseconv_destroy(h);
         return fail(SC_EDEVICE, "upload of the packed filter bank failed");
       }
@@ -287,6 +297,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->waves_per_group = h->p.NW - 1;
   info->pipeline_depth = h->p.D;
   info->step_balance_permille = h->p.step_permille;
+  info->split_pieces = h->split_pieces;
   info->rows_per_wave = h->p.OCW;
   info->row_groups = h->p.G;
   info->chunk_channels = h->p.Cc;
@@ -345,7 +356,7 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.xoff = g.xoff; a.cshift = g.cshift;
   a.wide16 = (g.wide && (reinterpret_cast<uintptr_t>(in) & 15) == 0) ? 1 : 0;
   a.nsb = a.wide16 ? p.nblk / 4 : p.nblk;
-  a.D = p.D; a.QE = p.QE;
+  a.D = p.D; a.QE = p.QE; a.nbuf = p.nbuf;
   a.nin = p.nin;
   a.slot_words = p.slot_words;
   a.HW = g.H * g.W;
@@ -379,6 +390,7 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   a.ent = h->d_ent;
   a.seg = h->d_seg;
   a.slot_row = h->d_slot;
+  a.slot_comb = h->d_comb;
   int gerr = 0;
   const int nb = sc::grid_size(h->p, (long long)a.ntiles * h->p.G, &gerr);
   if (gerr) return fail(SC_EDEVICE, std::string("occupancy query failed: ") + hipGetErrorString((hipError_t)gerr));

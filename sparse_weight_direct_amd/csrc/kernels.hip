@@ -27,6 +27,9 @@
 //              It then releases the slot (done counter);
 //   store    - after a unit's last chunk, each consumer stores its valid positions with
 //              coalesced NCHW stores; slots of channels without non-zeros store exact zeros.
+//              A row split over several consumers (pieces) is summed first: later pieces
+//              leave partial sums in LDS buffers, the owner (piece 0) adds them in piece
+//              order, so the result does not depend on timing.
 // A consumer ahead of the others is held back only when it needs a step whose slot an
 // earlier step still occupies, so per-step imbalance between wavefronts averages out over
 // the ring.  Every wait on a counter is bounded (kSpinLimit sleeps), so a wavefront can
@@ -388,8 +391,10 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
 
 template <int K, int OCW, int NW>
 __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, const uint2* __restrict__ ent,
-                                         const int* bst, const int* __restrict__ slot_row, StepIt it, int S,
-                                         const uint32_t* ready, uint32_t* done, float* lds, int c, int lane) {
+                                         const int* bst, const int* __restrict__ slot_row,
+                                         const int* __restrict__ slot_comb, StepIt it, int S, const uint32_t* ready,
+                                         uint32_t* done, uint32_t* pfull, uint32_t* pcons, float* pbuf, float* lds,
+                                         int c, int lane) {
   constexpr int NC = NW - 1;
   const int ew = 256 * a.QE;  // words of a consumer's private part of a slot
   // entries of steps 0 .. D-1 ahead of time
@@ -404,7 +409,8 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
   for (int o = 0; o < OCW; o++)
 #pragma unroll
     for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
-  int drained = 0;  // stores were issued since the last wait: wait for everything
+  int drained = 0;     // stores were issued since the last wait: wait for everything
+  int units_done = 0;  // units finished by this workgroup (generation of the partial buffers)
   for (int s = 0; s < S; s++) {
     const int buf = s % a.D;
     // own entries of step s landed: later entry loads outstanding are those of steps
@@ -430,13 +436,43 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
     else
       __builtin_amdgcn_s_setprio(0);
     if (it.k + 1 == a.nch) {
+      const int* rows = slot_row + (it.g * NC + c) * OCW;
+      const int* comb = slot_comb + (it.g * NC + c) * OCW;
+      // later pieces of split rows leave their partial sums in LDS buffers (after the
+      // previous unit's owner has read the buffer) ...
+#pragma unroll
+      for (int o = 0; o < OCW; o++) {
+        const int v = rows[o];
+        if (v <= -2) {
+          const int b = -2 - v;
+          lds_wait_ge(&pcons[b], (uint32_t)units_done);
+          float* pb = pbuf + b * (64 * K) + lane;
+#pragma unroll
+          for (int q = 0; q < K; q++) pb[64 * q] = acc[o][q];
+          if (lane == 0)
+            __hip_atomic_store(&pfull[b], (uint32_t)(units_done + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+          for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
+        }
+      }
+      // ... and the owner of each row adds them in piece order, then stores
       int ob[K];
       output_bases<K>(a, it.tile * (64 * K), lane, ob);
       const int plane = a.E * a.F;
 #pragma unroll
       for (int o = 0; o < OCW; o++) {
-        const int row = slot_row[(it.g * NC + c) * OCW + o];
+        const int row = rows[o];
         if (row >= 0) {
+          const int cm = comb[o];
+          for (int i = 0; i < (cm & 255); i++) {
+            const int b = (cm >> 8) + i;
+            lds_wait_ge(&pfull[b], (uint32_t)(units_done + 1));
+            const float* pb = pbuf + b * (64 * K) + lane;
+#pragma unroll
+            for (int q = 0; q < K; q++) acc[o][q] += pb[64 * q];
+            if (lane == 0)
+              __hip_atomic_store(&pcons[b], (uint32_t)(units_done + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
 #pragma unroll
           for (int q = 0; q < K; q++)
             if (ob[q] >= 0) __builtin_nontemporal_store(acc[o][q], y + ob[q] + row * plane);
@@ -445,6 +481,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
         for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
       }
       drained = 1;
+      units_done++;
     }
     // the private part of this slot is free again: entries of step s + D
     if (s + a.D < S) {
@@ -462,7 +499,7 @@ template <int K, int OCW, int NW>
 __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
     const KArgs a, const float* __restrict__ x, float* __restrict__ y,
     const uint2* __restrict__ ent, const int* __restrict__ bstart,
-    const int* __restrict__ slot_row) {
+    const int* __restrict__ slot_row, const int* __restrict__ slot_comb) {
   constexpr int T = NW * 64;
   constexpr int NC = NW - 1;
   extern __shared__ float lds[];
@@ -471,6 +508,9 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   uint32_t* ready = reinterpret_cast<uint32_t*>(lds + a.D * a.slot_words);
   uint32_t* done = ready + kMaxDepth;
   int* bst = reinterpret_cast<int*>(done + kMaxDepth);
+  uint32_t* pfull = reinterpret_cast<uint32_t*>(bst + a.G * NC * (a.nch + 1));  // split rows
+  uint32_t* pcons = pfull + a.nbuf;
+  float* pbuf = reinterpret_cast<float*>(pcons + a.nbuf);
 
   const int b = xcd_logical(blockIdx.x, gridDim.x);
   const long long units = (long long)a.ntiles * a.G;
@@ -480,6 +520,7 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   if (S == 0) return;
 
   if (threadIdx.x < 2 * kMaxDepth) ready[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < 2 * a.nbuf; i += T) pfull[i] = 0u;
   for (int i = threadIdx.x; i < a.G * NC * (a.nch + 1); i += T) bst[i] = bstart[i];
   __syncthreads();
 
@@ -488,10 +529,11 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   if (wave == NC)
     producer<K, NW>(a, x, it, S, ready, done, lds, lane);
   else
-    consumer<K, OCW, NW>(a, y, ent, bst, slot_row, it, S, ready, done, lds, wave, lane);
+    consumer<K, OCW, NW>(a, y, ent, bst, slot_row, slot_comb, it, S, ready, done, pfull, pcons, pbuf, lds, wave,
+                         lane);
 }
 
-using SparseFn = void (*)(KArgs, const float*, float*, const uint2*, const int*, const int*);
+using SparseFn = void (*)(KArgs, const float*, float*, const uint2*, const int*, const int*, const int*);
 
 #define SC_FOR_EACH_KO(X, NW) \
   X(1, 1, NW) X(2, 1, NW) X(4, 1, NW) X(6, 1, NW) X(7, 1, NW) X(8, 1, NW) X(12, 1, NW) X(16, 1, NW) \
@@ -538,7 +580,7 @@ int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks) {
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), p.lds_bytes);
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(fn, dim3(nblocks), dim3(p.NW * 64), p.lds_bytes, reinterpret_cast<hipStream_t>(stream), a,
-                     a.x, a.y, reinterpret_cast<const uint2*>(a.ent), a.seg, a.slot_row);
+                     a.x, a.y, reinterpret_cast<const uint2*>(a.ent), a.seg, a.slot_row, a.slot_comb);
   return (int)hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 // wavefront slots largest-first so that, chunk by chunk, every wavefront of a workgroup
 // carries about the same number of non-zeros whatever the per-channel density.
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <numeric>
@@ -46,61 +47,115 @@ static int env_int(const char* s, const char* key, int dflt) {
 }
 
 // Deal rows to (group, consumer wavefront, slot).  A workgroup's consumers share each
-// chunk's ring slot, so a step is released only when its busiest consumer is done: each row is
-// described by its per-chunk entry counts (padded to even, as stored) and rows are dealt
-// largest first to the wavefront with a free slot that least increases the sum over chunks
-// of the busiest wavefront's count (ties: the smaller total, then the lower index).  With
-// several groups, rows are first dealt to groups largest-first onto the least-loaded group
-// with room.  Empty rows weigh 1 so that they are spread too.
-static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const std::vector<int32_t>& rowptr,
-                                          const std::vector<int32_t>& col, int32_t* max_wave_nnz) {
+// chunk's ring slot, so a step is released only when its busiest consumer is done: each
+// item (a row, or a piece of a split row) is described by its per-chunk entry counts
+// (padded to even, as stored), and items are dealt largest first to the consumer with a
+// free slot that least increases the sum over chunks of the busiest consumer's count
+// (ties: the smaller total, then the lower index), preferring consumers that hold no other
+// piece of the same row.  A row whose entries exceed a consumer's fair share of the group
+// is split into pieces of at most half that share (at most one per consumer, and as many
+// as the free slots allow).  Rows are first dealt, with all their pieces, to groups
+// largest-first onto the least-loaded group with room.  Empty rows weigh 1 so that they
+// are spread too.
+static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32_t>& rowptr,
+                           const std::vector<int32_t>& col) {
   const int M = g.M, NC = p.NW - 1, OCW = p.OCW, G = p.G, nch = p.nch, RS = g.R * g.S;
-  std::vector<int32_t> vec((size_t)M * nch, 0);
+  std::vector<int32_t> raw((size_t)M * nch, 0);
   std::vector<long long> tot(M, 1);
+  long long total = 0;
   for (int m = 0; m < M; m++) {
-    int32_t* v = &vec[(size_t)m * nch];
+    int32_t* v = &raw[(size_t)m * nch];
     for (int j = rowptr[m]; j < rowptr[m + 1]; j++) v[(col[j] / RS) / p.Cc]++;
-    for (int k = 0; k < nch; k++) {
-      v[k] = (v[k] + 1) & ~1;
-      tot[m] += v[k];
-    }
+    for (int k = 0; k < nch; k++) tot[m] += (v[k] + 1) & ~1;
+    total += tot[m];
   }
+  // pieces per row
+  const double fair = (double)total / ((double)G * NC);
+  std::vector<int> P(M, 1);
+  long long pieces = M;
+  for (int m = 0; m < M; m++)
+    if (rowptr[m + 1] > rowptr[m] && (double)tot[m] > fair) {
+      P[m] = std::min<long long>(NC, (long long)std::ceil(2.0 * (double)tot[m] / fair));
+      pieces += P[m] - 1;
+    }
+  const long long slots = (long long)G * NC * OCW;
+  while (pieces > slots) {  // not enough slots: take pieces from the most split rows
+    int big = 0;
+    for (int m = 1; m < M; m++)
+      if (P[m] > P[big]) big = m;
+    if (P[big] <= 1) break;
+    P[big]--;
+    pieces--;
+  }
+  // items: (row, piece) with padded per-chunk counts
+  struct Item { int m, p; long long tot; };
+  std::vector<Item> items;
+  std::vector<int32_t> ivec;
+  for (int m = 0; m < M; m++)
+    for (int q = 0; q < P[m]; q++) {
+      long long t = 1;
+      for (int k = 0; k < nch; k++) {
+        int pb, pe;
+        piece_range(0, raw[(size_t)m * nch + k], q, P[m], &pb, &pe);
+        const int n = ((pe - pb) + 1) & ~1;
+        ivec.push_back(n);
+        t += n;
+      }
+      items.push_back({m, q, t});
+    }
+  std::vector<int> first_item(M);
+  for (int i = (int)items.size() - 1; i >= 0; i--) first_item[items[i].m] = i;
+  // rows (with their pieces) -> groups
   std::vector<int> order(M);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return tot[a] > tot[b]; });
-  // rows -> groups
-  std::vector<std::vector<int>> grp(G);
+  std::vector<std::vector<int>> grp(G);  // item indices per group
   {
     std::vector<long long> gl(G, 0);
+    std::vector<int> used(G, 0);
     for (int m : order) {
       int best = -1;
       for (int q = 0; q < G; q++)
-        if ((int)grp[q].size() < NC * OCW && (best < 0 || gl[q] < gl[best])) best = q;
-      grp[best].push_back(m);  // stays in largest-first order
+        if (used[q] + P[m] <= NC * OCW && (best < 0 || gl[q] < gl[best])) best = q;
+      if (best < 0) best = 0;  // cannot happen: pieces never exceed the slots
+      for (int q = 0; q < P[m]; q++) grp[best].push_back(first_item[m] + q);
       gl[best] += tot[m];
+      used[best] += P[m];
     }
   }
-  std::vector<int32_t> slot_row((size_t)G * NC * OCW, -1);
-  long long mwn = 0;
+  Sched sc;
+  sc.slot_row.assign((size_t)G * NC * OCW, -1);
+  sc.slot_comb.assign((size_t)G * NC * OCW, 0);
+  sc.src_row.assign((size_t)G * NC * OCW, -1);
+  sc.piece.assign((size_t)G * NC * OCW, 0);
+  sc.npieces.assign((size_t)G * NC * OCW, 1);
   std::vector<long long> load((size_t)NC * nch), wt(NC);
   std::vector<long long> gmax(nch);
   std::vector<int> cnt(NC);
+  std::vector<int> holder((size_t)NC * M, 0);  // consumer w holds a piece of row m
   for (int q = 0; q < G; q++) {
     std::fill(load.begin(), load.end(), 0);
     std::fill(wt.begin(), wt.end(), 0);
     std::fill(gmax.begin(), gmax.end(), 0);
     std::fill(cnt.begin(), cnt.end(), 0);
-    for (int m : grp[q]) {
-      const int32_t* v = &vec[(size_t)m * nch];
+    std::vector<int> its = grp[q];
+    std::stable_sort(its.begin(), its.end(), [&](int a, int b) { return items[a].tot > items[b].tot; });
+    for (int i : its) {
+      const Item& it = items[i];
+      const int32_t* v = &ivec[(size_t)i * nch];
       int best = -1;
       long long bcost = 0;
+      bool bfree = false;
       for (int w = 0; w < NC; w++) {
         if (cnt[w] >= OCW) continue;
+        const bool fr = !holder[(size_t)w * M + it.m];
         long long cost = 0;
         for (int k = 0; k < nch; k++) cost += std::max(gmax[k], load[(size_t)w * nch + k] + v[k]);
-        if (best < 0 || cost < bcost || (cost == bcost && wt[w] < wt[best])) {
+        if (best < 0 || (fr && !bfree) ||
+            (fr == bfree && (cost < bcost || (cost == bcost && wt[w] < wt[best])))) {
           best = w;
           bcost = cost;
+          bfree = fr;
         }
       }
       for (int k = 0; k < nch; k++) {
@@ -108,28 +163,60 @@ static std::vector<int32_t> schedule_rows(const Geom& g, const Plan& p, const st
         l += v[k];
         gmax[k] = std::max(gmax[k], l);
       }
-      wt[best] += tot[m];
-      slot_row[((size_t)q * NC + best) * OCW + cnt[best]] = m;
+      wt[best] += it.tot;
+      holder[(size_t)best * M + it.m] = 1;
+      const size_t sl = ((size_t)q * NC + best) * OCW + cnt[best];
+      sc.src_row[sl] = it.m;
+      sc.piece[sl] = it.p;
+      sc.npieces[sl] = P[it.m];
       cnt[best]++;
     }
+    std::fill(holder.begin(), holder.end(), 0);
+    // kernel tables: piece 0 owns the row; later pieces get partial buffers in order
+    int nb = 0;
+    std::vector<int> first_buf(M, -1);
+    for (int w = 0; w < NC; w++)
+      for (int o = 0; o < OCW; o++) {
+        const size_t sl = ((size_t)q * NC + w) * OCW + o;
+        const int m = sc.src_row[sl];
+        if (m >= 0 && P[m] > 1 && first_buf[m] < 0) {
+          first_buf[m] = nb;
+          nb += P[m] - 1;
+        }
+      }
+    sc.nbuf = std::max(sc.nbuf, nb);
     for (int w = 0; w < NC; w++) {
       long long nz = 0;
       for (int o = 0; o < OCW; o++) {
-        const int m = slot_row[((size_t)q * NC + w) * OCW + o];
-        if (m >= 0) nz += rowptr[m + 1] - rowptr[m];
+        const size_t sl = ((size_t)q * NC + w) * OCW + o;
+        const int m = sc.src_row[sl];
+        if (m < 0) continue;
+        if (P[m] == 1) {
+          sc.slot_row[sl] = m;
+        } else if (sc.piece[sl] == 0) {
+          sc.slot_row[sl] = m;
+          sc.slot_comb[sl] = (first_buf[m] << 8) | (P[m] - 1);
+        } else {
+          sc.slot_row[sl] = -2 - (first_buf[m] + sc.piece[sl] - 1);
+        }
+        for (int k = 0; k < nch; k++) {
+          int pb, pe;
+          piece_range(0, raw[(size_t)m * nch + k], sc.piece[sl], P[m], &pb, &pe);
+          nz += pe - pb;
+        }
       }
-      mwn = std::max(mwn, nz);
+      sc.max_wave_nnz = std::max<int32_t>(sc.max_wave_nnz, (int32_t)nz);
     }
   }
-  *max_wave_nnz = (int32_t)mwn;
-  return slot_row;
+  sc.split_pieces = (int32_t)(pieces - M);
+  return sc;
 }
 
 int block_header(int OCW) { return (OCW + 1) & ~1; }
 
 // Input layout for K positions per lane with D ring slots whose non-zero part takes QE
-// loads per consumer: the largest chunk that fits the LDS beside the counters and the
-// block-start table.  Chunks are then evened out: nch = ceil(C / Cc_max) chunks of about
+// loads per consumer: the largest chunk that fits the LDS beside the counters, the
+// block-start table and the partial-sum buffers of split rows.  Chunks are then evened out: nch = ceil(C / Cc_max) chunks of about
 // C / nch channels.
 static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds_max, Plan* p) {
   const int NC = p->NW - 1;
@@ -144,7 +231,7 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds
   p->nblk = p->CHS / 64;
   int nch = 1;
   for (int it = 0; it < 16; it++) {  // the block-start table grows with the chunk count
-    const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth;
+    const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth + 8LL * p->nbuf + 256LL * p->nbuf * K;
     const long long room = (lds_max - fixed) / (4LL * D) - (long long)QE * 256 * NC;  // row words per slot
     if (room < p->CHS) return false;
     int cc = (int)std::min<long long>(g.C, room / p->CHS);
@@ -165,21 +252,25 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds
 // Also returns (step_permille) the cost of the per-chunk synchronisation: 1000 * the sum
 // over groups and chunks of the busiest wavefront's entries over the sum of the means.
 static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& rowptr,
-                     const std::vector<int32_t>& col, const std::vector<int32_t>& slot_row,
-                     int32_t* step_permille = nullptr) {
+                     const std::vector<int32_t>& col, const Sched& sc, int32_t* step_permille = nullptr) {
   const int RS = g.R * g.S;
   std::vector<int> cnt(p.nch), tot(p.nch);
   std::vector<long long> kmax((size_t)p.G * p.nch, 0), ksum((size_t)p.G * p.nch, 0);
   int best = 0;
-  for (size_t wv = 0; wv < slot_row.size() / p.OCW; wv++) {
+  for (size_t wv = 0; wv < sc.src_row.size() / p.OCW; wv++) {
     const size_t q = wv / (p.NW - 1);
     std::fill(tot.begin(), tot.end(), 0);
     for (int o = 0; o < p.OCW; o++) {
-      const int m = slot_row[wv * p.OCW + o];
+      const size_t sl = wv * p.OCW + o;
+      const int m = sc.src_row[sl];
       if (m < 0) continue;
       std::fill(cnt.begin(), cnt.end(), 0);
       for (int j = rowptr[m]; j < rowptr[m + 1]; j++) cnt[(col[j] / RS) / p.Cc]++;
-      for (int k = 0; k < p.nch; k++) tot[k] += (cnt[k] + 1) & ~1;
+      for (int k = 0; k < p.nch; k++) {
+        int pb, pe;
+        piece_range(0, cnt[k], sc.piece[sl], sc.npieces[sl], &pb, &pe);
+        tot[k] += ((pe - pb) + 1) & ~1;
+      }
     }
     for (int k = 0; k < p.nch; k++) {
       best = std::max(best, block_header(p.OCW) + tot[k]);
@@ -218,7 +309,7 @@ static bool instantiated(int K, int OCW) {
 }
 
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 std::vector<int32_t>* slot_row, int32_t* max_wave_nnz) {
+                 Sched* sched) {
   static const int kOcw[] = {1, 2, 3, 5, 9};
   static const int kKs[] = {16, 12, 8, 7, 6, 4, 2, 1};
   Plan p{};
@@ -226,9 +317,18 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
   const int NC = p.NW - 1;
   const long long img_ext = (long long)g.HYp * g.Pp;
   const int kmax = img_ext >= 4096 ? 8 : img_ext >= 1024 ? 4 : img_ext >= 256 ? 2 : 1;
+  // slots for every row plus the extra pieces of rows longer than a consumer's fair share
+  long long extra = 0;
+  {
+    const double fair = std::max(1.0, (double)rowptr[g.M] / NC);
+    for (int m = 0; m < g.M; m++) {
+      const int n = rowptr[m + 1] - rowptr[m];
+      if (n > fair) extra += std::min<long long>(NC, (long long)std::ceil(2.0 * n / fair)) - 1;
+    }
+  }
   int OCW = 9;
   for (int o : kOcw)
-    if (NC * o >= g.M) {
+    if (NC * o >= g.M + extra) {
       OCW = o;
       break;
     }
@@ -251,20 +351,29 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
       if (!instantiated(k, p.OCW)) continue;
       if (kenv > 0 ? k > kenv : k > kmax) continue;
       bool ok = false;
-      int32_t mwn = 0;
-      std::vector<int32_t> sr;
+      Sched sc;
       for (int qe = 1; qe <= 64 && !ok; qe++) {
-        if (!fill_layout(g, k, D, qe, cc_cap, lds_max, &p)) break;
-        sr = schedule_rows(g, p, rowptr, col, &mwn);
-        if (max_block(g, p, rowptr, col, sr, &p.step_permille) <= 128 * qe) ok = true;
+        bool fits = true;
+        p.nbuf = 0;
+        for (int attempt = 0; attempt < 2; attempt++) {  // the partial buffers take LDS too
+          if (!fill_layout(g, k, D, qe, cc_cap, lds_max, &p)) {
+            fits = false;
+            break;
+          }
+          sc = schedule_rows(g, p, rowptr, col);
+          if (sc.nbuf <= p.nbuf) break;
+          p.nbuf = sc.nbuf;
+        }
+        if (!fits) break;
+        if (max_block(g, p, rowptr, col, sc, &p.step_permille) <= 128 * qe) ok = true;
       }
       if (!ok) continue;
+      p.nbuf = sc.nbuf;
       const int table = p.G * NC * (p.nch + 1);
-      p.lds_bytes = 4 * p.D * p.slot_words + 8 * kMaxDepth + 4 * table;
+      p.lds_bytes = 4 * p.D * p.slot_words + 8 * kMaxDepth + 4 * table + 8 * p.nbuf + 4 * p.nbuf * 64 * k;
       if (p.lds_bytes > lds_max) continue;
       p.span_images = (int)((p.PL + img_ext - 2) / img_ext + 1);
-      if (slot_row) *slot_row = sr;
-      if (max_wave_nnz) *max_wave_nnz = mwn;
+      if (sched) *sched = std::move(sc);
       return p;
     }
   }

@@ -66,7 +66,33 @@ struct Plan {
   int lds_bytes;   // D ring slots + ready/done counters + block-start table
   int span_images; // most images one tile's staged range can touch
   int step_permille;  // 1000 * sum over chunks of the busiest wavefront's entries / mean
+  int nbuf;        // LDS partial-sum buffers per workgroup (pieces of split rows)
 };
+
+// Row schedule.  A row longer than a consumer's fair share of a group's non-zeros is split
+// into pieces held by different consumers of its group: in every chunk, piece p of P takes
+// a contiguous part of the row's entries of that chunk (piece_range).  Piece 0's slot
+// owns the row: after the unit's last chunk it adds the other pieces' partial sums, which
+// they leave in LDS buffers, in piece order, and stores.
+struct Sched {
+  std::vector<int32_t> slot_row;   // kernel table per (group, consumer, slot): >= 0 output
+                                   // channel (whole row or piece 0), -1 empty, <= -2: a
+                                   // later piece writing partial buffer -2 - value
+  std::vector<int32_t> slot_comb;  // kernel table: for piece 0 of a split row,
+                                   // (first partial buffer << 8) | (pieces - 1); else 0
+  std::vector<int32_t> src_row;    // row whose piece a slot holds, -1 empty
+  std::vector<int32_t> piece;      // piece index of the slot
+  std::vector<int32_t> npieces;    // pieces of that row
+  int nbuf = 0;                    // partial buffers a group needs
+  int32_t max_wave_nnz = 0;        // largest non-zero count of one consumer
+  int32_t split_pieces = 0;        // pieces beyond the first, over all rows
+};
+
+// Entries [pb, pe) of piece p of P of a chunk's entry range [b, e).
+inline void piece_range(int b, int e, int p, int P, int* pb, int* pe) {
+  *pb = b + (int)((long long)(e - b) * p / P);
+  *pe = b + (int)((long long)(e - b) * (p + 1) / P);
+}
 
 // Kernel arguments (by value).
 struct KArgs {
@@ -74,13 +100,15 @@ struct KArgs {
   float* y;
   const uint32_t* ent;    // sparse: pairs {enc, value bits}
   const int32_t* seg;     // sparse: [(group*NC + consumer)*(nch+1) + k] -> first entry of block k
-  const int* slot_row;    // sparse: [group][consumer][slot] -> output channel or -1
+  const int* slot_row;    // sparse: [group][consumer][slot] -> Sched::slot_row
+  const int* slot_comb;   // sparse: [group][consumer][slot] -> Sched::slot_comb
   int N, C, H, W, M, E, F, R, S, st, pad;
   int Pp, HYp, img_ext;   // img_ext = HYp * Pp
   int xoff, cshift;       // see Geom
   int wide16;             // 1: stage rows with 16-byte loads (wide layout, aligned input)
   int nsb;                // staging blocks per channel: nblk/4 of 256 words (wide16) or nblk
   int PL, CHS, nblk, Cc, nch, G, D, QE, nin, slot_words;
+  int nbuf;               // partial-sum buffers (split rows)
   int HW;                 // H * W
   int ntiles;             // tiles of 64*K extended positions
   long long x_words;      // N * C * H * W
@@ -91,7 +119,7 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
 // Launch plan for the CSR filter matrix (rowptr, col): also schedules rows onto wavefront
 // slots (slot_row) and sizes each wavefront's per-chunk block of non-zeros.
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 std::vector<int32_t>* slot_row, int32_t* max_wave_nnz);
+                 Sched* sched);
 int plan_pl(const Geom& g, int K);
 
 // Header entries at the start of a wavefront's per-chunk block of non-zeros.

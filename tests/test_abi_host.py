@@ -191,3 +191,30 @@ def test_schedule_balances_wavefronts_by_nnz(name):
     assert info["max_wave_nnz"] <= nnz / waves + rows.max()
     assert info["max_wave_nnz"] <= 1.15 * nnz / waves
     assert 1000 <= info["step_balance_permille"] <= {"imb80": 1100, "imb95": 1150, "imb99": 1250}[name]
+
+
+@pytest.mark.parametrize("dense_rows", [1, 3])
+def test_long_rows_are_split_across_wavefronts(dense_rows):
+    """Rows longer than a wavefront's fair share are split into pieces on different
+    wavefronts: the heaviest wavefront stays near the mean instead of carrying a whole dense
+    row, and the canonical export is unchanged."""
+    d = workloads.make_custom(1, 32, 20, 20, 40, 3, 3, 1, 1, 0.05, 5)
+    mask = d["mask"].copy()
+    mask[7:7 + dense_rows] = 1
+    h = sc.Handle(40, 32, 3, 3, 20, 20, 1, 1, values=d["w"], mask=mask, flags=sc.SC_PACK_HOST_ONLY)
+    info = h.info()
+    nnz = int(mask.sum())
+    waves = info["row_groups"] * info["waves_per_group"]
+    assert info["split_pieces"] > 0
+    assert info["max_wave_nnz"] < 32 * 9  # no wavefront holds a whole dense row
+    assert info["max_wave_nnz"] <= 1.5 * nnz / waves
+    rowptr, off, val = h.export()
+    r = oracle.reference(d["x"][:1], d["w"], mask, 1, 1)
+    assert np.array_equal(rowptr, r["rowptr"]) and np.array_equal(off, r["offsets"])
+    assert np.array_equal(val.view(np.uint32), r["values"].view(np.uint32))
+
+
+def test_no_split_for_balanced_layers():
+    for name in ("imb80", "imb95", "tiny", "late"):
+        d = workloads.make(name, n_override=1)
+        assert _pack_host(d, d["layer"]).info()["split_pieces"] == 0, name

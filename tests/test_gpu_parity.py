@@ -179,6 +179,34 @@ def test_skewed_rows_one_dense_channel():
     assert_parity(y, r["y64"], r["mag"], "skewed")
 
 
+@pytest.mark.parametrize("plan", ["", "K=1,OCW=3,D=4", "K=2,OCW=2,D=2"])
+def test_split_rows_many_units(plan, monkeypatch):
+    """Dense channels split over several wavefronts, with many work units per workgroup, so
+    the partial-sum buffers are reused from unit to unit; run twice to check that the fixed
+    combine order makes the result identical."""
+    if plan:
+        monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make_custom(6, 24, 40, 40, 36, 3, 3, 1, 1, 0.03, 41)
+    mask = d["mask"].copy()
+    mask[3] = 1
+    mask[20] = 1
+    r = oracle.reference(d["x"], d["w"], mask, 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    assert h.info()["split_pieces"] > 0
+    assert_parity(y, r["y64"], r["mag"], "split " + plan)
+    y2, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1, handle=h)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_fewer_channels_than_wavefronts():
+    """M = 4 output channels on 15 computing wavefronts: every channel is split."""
+    d = workloads.make_custom(2, 16, 30, 30, 4, 3, 3, 1, 1, 0.5, 42)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    assert h.info()["split_pieces"] > 0
+    assert_parity(y, r["y64"], r["mag"], "M=4")
+
+
 def test_csr_input_path_and_determinism():
     d = workloads.make("mid")
     L = d["layer"]
