@@ -190,13 +190,16 @@ def main():
         oracle.conv_csr(d["x"][:1], rowptr, colidx, value, M, R, S, st, pad)
         t1 = time.perf_counter() - t
         n_img = max(1, min(N, int(args.cpu_seconds / max(t1, 1e-3))))
+        log(f"[bench] CPU oracle: 1 image {t1:.3f} s; timing {n_img} image(s) per run on {threads} threads")
         # a batch that finishes quickly is repeated until about cpu_seconds have passed
-        reps = 1 if n_img < N else max(1, min(1000, int(args.cpu_seconds / max(t1 * N, 1e-3))))
-        log(f"[bench] CPU oracle: 1 image {t1:.3f} s; timing {reps} x {n_img} image(s) on {threads} threads")
+        reps = 0
         t = time.perf_counter()
-        for _ in range(reps):
+        while True:
             oracle.conv_csr(d["x"][:n_img], rowptr, colidx, value, M, R, S, st, pad)
-        tc = time.perf_counter() - t
+            reps += 1
+            tc = time.perf_counter() - t
+            if tc >= args.cpu_seconds or reps >= 10000:
+                break
         cpu = {"value": roofline.effective_flops(nnz, n_img, E, F) * reps / tc / 1e12, "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
                "sample": f"list-form oracle (fp64 accumulate), {reps} run(s) over {n_img} of {N} images, "
