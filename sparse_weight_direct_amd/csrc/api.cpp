@@ -180,9 +180,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
 
     // Kernel stream: per (group, consumer wavefront), one block per chunk holding header entries
     // {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
-    // non-zeros {enc, value} in slot order, each slot's run padded to an even count with
-    // {0, +0.0f} entries; bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of
-    // block k (and bstart[.. + nch] the end of the last one).
+    // non-zeros {enc, value} in slot order; bstart[(group*NC + consumer)*(nch+1) + k] is the
+    // first entry of block k (and bstart[.. + nch] the end of the last one).
     const int waves = p.G * (p.NW - 1);  // consumer wavefronts
     std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
     for (int m = 0; m < M; m++) {
@@ -194,7 +193,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
     }
     const int hdr_n = sc::block_header(p.OCW);
-    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + p.OCW);
+    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * hdr_n;
     if (n_ent >= (size_t)1 << 31) {
       sparseconv_destroy(h);
       return fail(SC_EUNSUPPORTED, "kernel stream too large");
@@ -226,12 +225,6 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
               pos++;
             }
             cnt = e - b;
-            if (cnt & 1) {  // zero-weight pad entry (offset 0 is a valid LDS word)
-              ent[2 * pos] = 0;
-              ent[2 * pos + 1] = 0;
-              pos++;
-              cnt++;
-            }
           }
           ent[2 * (hdr + o)] = (uint32_t)cnt;
         }

@@ -261,10 +261,11 @@ __device__ __forceinline__ void pair(float (&acc)[K], const float* lane_lds, con
   for (int b = 0; b < K; b++) acc[b] = fmaf(w1, v1[b], acc[b]);
 }
 
+// n consecutive non-zeros starting at lane l of a group: pairs, then a single one if n is odd.
 template <int K>
-__device__ __forceinline__ void run_pairs(float (&acc)[K], const float* lane_lds, const uint2 grp, int l, int np) {
-  const int lend = l + 2 * np;
-  if (np & 1) {
+__device__ __forceinline__ void run_entries(float (&acc)[K], const float* lane_lds, const uint2 grp, int l, int n) {
+  const int lend = l + (n & ~1);
+  if (n & 2) {
     pair<K>(acc, lane_lds, grp, l);
     l += 2;
   }
@@ -272,13 +273,16 @@ __device__ __forceinline__ void run_pairs(float (&acc)[K], const float* lane_lds
     pair<K>(acc, lane_lds, grp, l);
     pair<K>(acc, lane_lds, grp, l + 2);
   }
+  if (n & 1)
+    fma_entry<K>(acc, lane_lds, (uint32_t)__builtin_amdgcn_readlane((int)grp.x, lend),
+                 __int_as_float(__builtin_amdgcn_readlane((int)grp.y, lend)));
 }
 
 // One step: the wavefront's slots and their non-zeros of this chunk, read from the block
 // staged in the ring slot: header entries {count of slot o, 0} (OCW of them, rounded up to
-// an even number), then the slots' non-zeros {enc, value} in slot order, each slot's run
-// padded to an even length with zero-weight entries so that it is walked in pairs that
-// never straddle a group of 64 (lane i holds entry i of the group).  The walk is split in
+// an even number), then the slots' non-zeros {enc, value} in slot order, walked in pairs
+// (and a single last one for an odd run) that never straddle a group of 64 (lane i holds
+// entry i of the group).  The walk is split in
 // slot ranges [O0, O1) so that the caller can issue staging loads between them; after(o)
 // runs once slot o's run is done.
 struct Walk {
@@ -311,7 +315,7 @@ __device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)
                                            int lane, After&& after) {
 #pragma unroll
   for (int o = O0; o < O1; o++) {
-    int n = __builtin_amdgcn_readlane((int)w.head.x, o);  // even
+    int n = __builtin_amdgcn_readlane((int)w.head.x, o);
     while (n > 0) {
       if (w.r == 64) {
         w.base += 64;
@@ -319,7 +323,7 @@ __device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)
         w.r = 0;
       }
       const int take = min(n, 64 - w.r);
-      run_pairs<K>(acc[o], lane_lds, w.cur, w.r, take >> 1);
+      run_entries<K>(acc[o], lane_lds, w.cur, w.r, take);
       w.r += take;
       n -= take;
     }
@@ -351,8 +355,19 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
   int pending = -1;  // the step whose loads were issued but not yet published
   for (int t = 0; t < S; t++) {
     const int buf = t % a.D;
-    // the slot held step t - D: wait until every consumer has released it
-    if (t >= a.D) lds_wait_ge(&done[buf], (uint32_t)(NC * (t / a.D)));
+    // the slot held step t - D: wait until every consumer has released it.  If that wait
+    // would block, publish the pending step as soon as it has landed instead of after the
+    // next issue, so that consumers ahead of the slowest one can start on it.
+    if (t >= a.D) {
+      const uint32_t target = (uint32_t)(NC * (t / a.D));
+      if (pending >= 0 && __hip_atomic_load(&done[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        wait_vmcnt(0);
+        __hip_atomic_store(&ready[pending % a.D], (uint32_t)(pending / a.D + 1), __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        pending = -1;
+      }
+      lds_wait_ge(&done[buf], target);
+    }
     if (it.tile != cur_tile) {
       cur_tile = it.tile;
       I0 = cur_tile * (64 * K);

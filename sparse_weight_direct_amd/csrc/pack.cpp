@@ -49,7 +49,7 @@ static int env_int(const char* s, const char* key, int dflt) {
 // Deal rows to (group, consumer wavefront, slot).  A workgroup's consumers share each
 // chunk's ring slot, so a step is released only when its busiest consumer is done: each
 // item (a row, or a piece of a split row) is described by its per-chunk entry counts
-// (padded to even, as stored), and items are dealt largest first to the consumer with a
+// (as stored), and items are dealt largest first to the consumer with a
 // free slot that least increases the sum over chunks of the busiest consumer's count
 // (ties: the smaller total, then the lower index), preferring consumers that hold no other
 // piece of the same row.  A row whose entries exceed a consumer's fair share of the group
@@ -66,7 +66,7 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
   for (int m = 0; m < M; m++) {
     int32_t* v = &raw[(size_t)m * nch];
     for (int j = rowptr[m]; j < rowptr[m + 1]; j++) v[(col[j] / RS) / p.Cc]++;
-    for (int k = 0; k < nch; k++) tot[m] += (v[k] + 1) & ~1;
+    for (int k = 0; k < nch; k++) tot[m] += v[k];
     total += tot[m];
   }
   // pieces per row
@@ -97,7 +97,7 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
       for (int k = 0; k < nch; k++) {
         int pb, pe;
         piece_range(0, raw[(size_t)m * nch + k], q, P[m], &pb, &pe);
-        const int n = ((pe - pb) + 1) & ~1;
+        const int n = pe - pb;
         ivec.push_back(n);
         t += n;
       }
@@ -248,7 +248,7 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds
 }
 
 // Largest block one wavefront gets for one chunk: header entries (OCW rounded up to even)
-// plus each slot's non-zeros of the chunk rounded up to even.
+// plus each slot's non-zeros of the chunk.
 // Also returns (step_permille) the cost of the per-chunk synchronisation: 1000 * the sum
 // over groups and chunks of the busiest wavefront's entries over the sum of the means.
 static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& rowptr,
@@ -269,7 +269,7 @@ static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& r
       for (int k = 0; k < p.nch; k++) {
         int pb, pe;
         piece_range(0, cnt[k], sc.piece[sl], sc.npieces[sl], &pb, &pe);
-        tot[k] += ((pe - pb) + 1) & ~1;
+        tot[k] += pe - pb;
       }
     }
     for (int k = 0; k < p.nch; k++) {
