@@ -180,8 +180,10 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
 
     // Kernel stream: per (group, consumer wavefront), one block per chunk holding header entries
     // {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
-    // non-zeros {enc, value} in slot order; bstart[(group*NC + consumer)*(nch+1) + k] is the
-    // first entry of block k (and bstart[.. + nch] the end of the last one).
+    // non-zeros {enc, value} in slot order; each block starts at a multiple of 64 entries
+    // (the kernel loads whole groups of 64), with zero entries in the gaps.
+    // bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of block k and
+    // bstart[.. + nch] the end of the last one.
     const int waves = p.G * (p.NW - 1);  // consumer wavefronts
     std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
     for (int m = 0; m < M; m++) {
@@ -193,7 +195,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
     }
     const int hdr_n = sc::block_header(p.OCW);
-    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * hdr_n;
+    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + 63) + 64;
     if (n_ent >= (size_t)1 << 31) {
       sparseconv_destroy(h);
       return fail(SC_EUNSUPPORTED, "kernel stream too large");
@@ -203,6 +205,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     size_t pos = 0;
     for (int wv = 0; wv < waves; wv++) {
       for (int k = 0; k < p.nch; k++) {
+        pos = (pos + 63) & ~(size_t)63;
         bstart[(size_t)wv * (p.nch + 1) + k] = (int32_t)pos;
         const size_t hdr = pos;
         pos += hdr_n;
@@ -349,8 +352,7 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.xoff = g.xoff; a.cshift = g.cshift;
   a.wide16 = (g.wide && (reinterpret_cast<uintptr_t>(in) & 15) == 0) ? 1 : 0;
   a.nsb = a.wide16 ? p.nblk / 4 : p.nblk;
-  a.D = p.D; a.QE = p.QE; a.nbuf = p.nbuf;
-  a.nin = p.nin;
+  a.D = p.D; a.nbuf = p.nbuf;
   a.slot_words = p.slot_words;
   a.HW = g.H * g.W;
   a.x_words = (long long)N * g.C * g.H * g.W;

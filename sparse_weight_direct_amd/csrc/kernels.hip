@@ -169,11 +169,14 @@ __device__ __forceinline__ uint32_t block_voff16(const KArgs& a, int I0, int n0,
 }
 
 // Producer: issue the input loads of one step (channels [c0, c0 + ncl) of a tile) into a
-// ring slot, block by block (blocks of 256 words with 16-byte loads, or of 64 words).
-// Returns the number of loads issued.  voff0..voff3 hold the first blocks' offsets for the
-// tile; further blocks are computed on the fly.
+// ring slot, block by block (blocks of 256 words with 16-byte loads, or of 64 words), and
+// call first_done(ncl) once the first block's ncl loads are issued.  Returns the number of
+// loads issued.  voff0..voff3 hold the first blocks' offsets for the tile; further blocks
+// are computed on the fly.
+template <typename FirstDone>
 __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int n0, int c0, int ncl,
-                                          const uint32_t (&voffc)[4], float* slot, int lane) {
+                                          const uint32_t (&voffc)[4], float* slot, int lane,
+                                          FirstDone&& first_done) {
   const int bw = a.wide16 ? 256 : 64;
   for (int blk = 0; blk < a.nsb; blk++) {
     // explicit selects keep the cached offsets in registers (no indexed private array)
@@ -197,17 +200,9 @@ __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int 
         soff += 4u * (uint32_t)a.HW;
       }
     }
+    if (blk == 0) first_done(ncl);
   }
   return a.nsb * ncl;
-}
-
-// Consumer: copy its block of non-zeros (stream entries [b0, b1), an even count) into its
-// private part of a ring slot: QE 16-byte loads of 128 entries; entries past the block's
-// end load as 0.
-__device__ __forceinline__ void stage_entries(const KArgs& a, const uint2* __restrict__ ent, int b0, int b1,
-                                              float* edst, int lane) {
-  const v4i ersrc = make_rsrc(ent + b0, (uint32_t)(b1 - b0) * 8u);
-  for (int q = 0; q < a.QE; q++) lds_dma_dwordx4(ersrc, edst + 256 * q, 16u * (64 * q + lane), 0u);
 }
 
 // Output word offset (without the channel term) of each of the lane's K positions, or -1.
@@ -278,48 +273,28 @@ __device__ __forceinline__ void run_entries(float (&acc)[K], const float* lane_l
                  __int_as_float(__builtin_amdgcn_readlane((int)grp.y, lend)));
 }
 
-// One step: the wavefront's slots and their non-zeros of this chunk, read from the block
-// staged in the ring slot: header entries {count of slot o, 0} (OCW of them, rounded up to
-// an even number), then the slots' non-zeros {enc, value} in slot order, walked in pairs
-// (and a single last one for an odd run) that never straddle a group of 64 (lane i holds
-// entry i of the group).  The walk is split in
-// slot ranges [O0, O1) so that the caller can issue staging loads between them; after(o)
-// runs once slot o's run is done.
+// One step: the wavefront's slots and their non-zeros of this chunk, from its block of the
+// stream: header entries {count of slot o, 0} (OCW of them, rounded up to an even number),
+// then the slots' non-zeros {enc, value} in slot order, walked in pairs (and a single last
+// one for an odd run) that never straddle a group of 64 (lane i holds entry i of the
+// group).  Blocks start at multiples of 64 entries, so a block is a whole number of groups;
+// the groups arrive in registers from the caller (next_group), which loads them one group
+// ahead straight from the stream in global memory.
 struct Walk {
-  const uint32_t* eb;  // the wavefront's entries in the ring slot
-  uint2 head;          // entries 0..63 (the header in lanes 0..OCW-1)
-  uint2 cur;           // the current group of 64 entries
-  int r;               // next entry's lane within the current group
-  int base;            // entry index of the current group's lane 0
+  uint2 head;  // the block's first group (the header in lanes 0..OCW-1)
+  uint2 cur;   // the current group of 64 entries
+  int r;       // next entry's lane within the current group
 };
 
-template <int NW>
-__device__ __forceinline__ uint2 walk_group(const KArgs& a, const Walk& w, int base, int lane) {
-  const int e = min(base + lane, 128 * a.QE - 1);
-  return *reinterpret_cast<const uint2*>(w.eb + 2 * e);
-}
-
-template <int OCW, int NW>
-__device__ __forceinline__ Walk walk_begin(const KArgs& a, const float* slot, int wave, int lane) {
-  Walk w;
-  w.eb = reinterpret_cast<const uint32_t*>(slot + a.nin) + wave * (256 * a.QE);
-  w.head = walk_group<NW>(a, w, 0, lane);
-  w.cur = w.head;
-  w.r = (OCW + 1) & ~1;
-  w.base = 0;
-  return w;
-}
-
-template <int K, int OCW, int NW, int O0, int O1, typename After>
-__device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)[OCW][K], const float* lane_lds,
-                                           int lane, After&& after) {
+template <int K, int OCW, typename NextGroup>
+__device__ __forceinline__ void walk_slots(Walk& w, float (&acc)[OCW][K], const float* lane_lds,
+                                           NextGroup&& next_group) {
 #pragma unroll
-  for (int o = O0; o < O1; o++) {
+  for (int o = 0; o < OCW; o++) {
     int n = __builtin_amdgcn_readlane((int)w.head.x, o);
     while (n > 0) {
       if (w.r == 64) {
-        w.base += 64;
-        w.cur = walk_group<NW>(a, w, w.base, lane);
+        w.cur = next_group();
         w.r = 0;
       }
       const int take = min(n, 64 - w.r);
@@ -327,7 +302,6 @@ __device__ __forceinline__ void walk_slots(const KArgs& a, Walk& w, float (&acc)
       w.r += take;
       n -= take;
     }
-    after(o);
   }
 }
 
@@ -380,21 +354,17 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
     }
     const int c0 = it.k * a.Cc;
     const int ncl = __builtin_amdgcn_readfirstlane(min(a.Cc, a.C - c0));
-    const int n = stage_rows(a, rsrc, I0, n0, c0, ncl, voffc, lds + buf * a.slot_words, lane);
-    if (pending >= 0) {
-      // step t-1 landed once at most this step's n loads are outstanding
-      wait_vmcnt(n <= 63 ? n : 0);
-      __hip_atomic_store(&ready[pending % a.D], (uint32_t)(pending / a.D + 1), __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (n > 63) {  // everything landed: publish this step too
-        __hip_atomic_store(&ready[buf], (uint32_t)(t / a.D + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        pending = -1;
-      } else {
-        pending = t;
+    // the previous step is published as soon as it has landed, which is once at most the
+    // first block of this step is outstanding (the loads complete in order): the copy engine
+    // keeps working on this step meanwhile
+    stage_rows(a, rsrc, I0, n0, c0, ncl, voffc, lds + buf * a.slot_words, lane, [&](int issued) {
+      if (pending >= 0) {
+        wait_vmcnt(issued <= 63 ? issued : 0);
+        __hip_atomic_store(&ready[pending % a.D], (uint32_t)(pending / a.D + 1), __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-    } else {
-      pending = t;
-    }
+    });
+    pending = t;
     it.next(a);
   }
   if (pending >= 0) {
@@ -411,31 +381,50 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
                                          uint32_t* done, uint32_t* pfull, uint32_t* pcons, float* pbuf, float* lds,
                                          int c, int lane) {
   constexpr int NC = NW - 1;
-  const int ew = 256 * a.QE;  // words of a consumer's private part of a slot
-  // entries of steps 0 .. D-1 ahead of time
-  StepIt is = it;
-  for (int t = 0; t < a.D && t < S; t++) {
-    const int* bw = bst + (is.g * NC + c) * (a.nch + 1) + is.k;
-    stage_entries(a, ent, bw[0], bw[1], lds + t * a.slot_words + a.nin + c * ew, lane);
-    is.next(a);
-  }
+  // The consumer's groups of 64 entries, in walk order (every group of a step's block, then
+  // the next step's): cur is walked while nxt, the following group, is in flight.  Only one
+  // load is outstanding at a time, apart from the output stores after a unit.
+  StepIt pf = it;  // step of the group in nxt
+  int pg = 0;      // its index within that step's block
+  int pstep = 0;   // its step number in this workgroup's stream
+  auto block = [&](const StepIt& p) -> const int* { return bst + (p.g * NC + c) * (a.nch + 1) + p.k; };
+  auto load_group = [&]() -> uint2 { return pstep < S ? ent[block(pf)[0] + 64 * pg + lane] : make_uint2(0u, 0u); };
+  auto advance = [&]() {
+    const int* bw = block(pf);
+    if (64 * (pg + 1) < bw[1] - bw[0]) {
+      pg++;
+    } else {
+      pg = 0;
+      pf.next(a);
+      pstep++;
+    }
+  };
+  uint2 nxt = load_group();  // group 0 of step 0
+  auto next_group = [&]() -> uint2 {
+    wait_vmcnt(0);
+    const uint2 g = nxt;
+    advance();
+    nxt = load_group();
+    return g;
+  };
+  uint2 first = next_group();  // step 0's first group; nxt holds the one after it
   float acc[OCW][K];
 #pragma unroll
   for (int o = 0; o < OCW; o++)
 #pragma unroll
     for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
-  int drained = 0;     // stores were issued since the last wait: wait for everything
   int units_done = 0;  // units finished by this workgroup (generation of the partial buffers)
   for (int s = 0; s < S; s++) {
     const int buf = s % a.D;
-    // own entries of step s landed: later entry loads outstanding are those of steps
-    // s+1 .. min(s+D-1, S-1)
-    wait_vmcnt(drained ? 0 : a.QE * min(a.D - 1, S - 1 - s));
-    drained = 0;
     lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
     const float* slot = lds + buf * a.slot_words;
-    Walk w = walk_begin<OCW, NW>(a, slot, c, lane);
-    walk_slots<K, OCW, NW, 0, OCW>(a, w, acc, slot + lane, lane, [](int) {});
+    Walk w;
+    w.head = first;
+    w.cur = first;
+    w.r = (OCW + 1) & ~1;
+    walk_slots<K, OCW>(w, acc, slot + lane, next_group);
+    // every group of this step's block has been walked: nxt is the next step's first group
+    if (s + 1 < S) first = next_group();
     // release the slot's input part (the walk's LDS reads are complete before the add);
     // one lane adds, so the counter advances by one per consumer
     uint32_t before = 0;
@@ -488,21 +477,16 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
             if (lane == 0)
               __hip_atomic_store(&pcons[b], (uint32_t)(units_done + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
+          // ordinary (write-back) stores: the partial 64-byte segments at output-row and tile
+          // boundaries are merged in L2 instead of being written to HBM separately
 #pragma unroll
           for (int q = 0; q < K; q++)
-            if (ob[q] >= 0) __builtin_nontemporal_store(acc[o][q], y + ob[q] + row * plane);
+            if (ob[q] >= 0) y[ob[q] + row * plane] = acc[o][q];
         }
 #pragma unroll
         for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
       }
-      drained = 1;
       units_done++;
-    }
-    // the private part of this slot is free again: entries of step s + D
-    if (s + a.D < S) {
-      const int* bw = bst + (is.g * NC + c) * (a.nch + 1) + is.k;
-      stage_entries(a, ent, bw[0], bw[1], lds + buf * a.slot_words + a.nin + c * ew, lane);
-      is.next(a);
     }
     it.next(a);
   }

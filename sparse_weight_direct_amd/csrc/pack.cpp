@@ -214,15 +214,13 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
 
 int block_header(int OCW) { return (OCW + 1) & ~1; }
 
-// Input layout for K positions per lane with D ring slots whose non-zero part takes QE
-// loads per consumer: the largest chunk that fits the LDS beside the counters, the
-// block-start table and the partial-sum buffers of split rows.  Chunks are then evened out: nch = ceil(C / Cc_max) chunks of about
-// C / nch channels.
-static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds_max, Plan* p) {
+// Input layout for K positions per lane with D ring slots: the largest chunk that fits the
+// LDS beside the counters, the block-start table and the partial-sum buffers of split rows.
+// Chunks are then evened out: nch = ceil(C / Cc_max) chunks of about C / nch channels.
+static bool fill_layout(const Geom& g, int K, int D, int cc_cap, int lds_max, Plan* p) {
   const int NC = p->NW - 1;
   p->K = K;
   p->D = D;
-  p->QE = QE;
   p->PL = plan_pl(g, K);
   const int align = g.wide ? 256 : 64;
   const long long chs = ((long long)g.st * g.st * p->PL + align - 1) / align * align;
@@ -232,7 +230,7 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds
   int nch = 1;
   for (int it = 0; it < 16; it++) {  // the block-start table grows with the chunk count
     const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth + 8LL * p->nbuf + 256LL * p->nbuf * K;
-    const long long room = (lds_max - fixed) / (4LL * D) - (long long)QE * 256 * NC;  // row words per slot
+    const long long room = (lds_max - fixed) / (4LL * D);  // input words per slot
     if (room < p->CHS) return false;
     int cc = (int)std::min<long long>(g.C, room / p->CHS);
     if (cc_cap > 0) cc = std::min(cc, cc_cap);
@@ -242,8 +240,7 @@ static bool fill_layout(const Geom& g, int K, int D, int QE, int cc_cap, int lds
   }
   p->Cc = (g.C + nch - 1) / nch;
   p->nch = (g.C + p->Cc - 1) / p->Cc;  // every chunk non-empty
-  p->nin = p->Cc * p->CHS;
-  p->slot_words = p->nin + QE * 256 * NC;
+  p->slot_words = p->Cc * p->CHS;
   return true;
 }
 
@@ -296,8 +293,7 @@ static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& r
 // tile) against the number of work units: the largest instantiated K with OCW*K <= 64
 // accumulators, capped by the image size.  D ring slots (3 by default: a consumer may run
 // a step ahead of the slowest) share the CU's LDS with the counters and the block-start
-// table; large chunks mean few steps.  QE is the smallest number of 128-entry loads that
-// holds every consumer's block of non-zeros for one chunk.
+// table; large chunks mean few steps.
 // SPARSECONV_PLAN="K=..,OCW=..,D=..,CC=..,LDSKB=..,NARROW" overrides the choice (tuning only).
 static bool instantiated(int K, int OCW) {
   static const int kk[] = {1, 2, 4, 6, 7, 8, 12, 16};
@@ -342,7 +338,7 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
   bool oko = false;
   for (int o : kOcw) oko = oko || o == OCW;
   if (!oko) OCW = 9;
-  // fewer slots per consumer (more groups) when the blocks of non-zeros do not fit
+  // fewer slots per consumer (more groups) when nothing fits
   for (int oi = 4; oi >= 0; oi--) {
     if (kOcw[oi] > OCW) continue;
     p.OCW = kOcw[oi];
@@ -350,24 +346,20 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
     for (int k : kKs) {
       if (!instantiated(k, p.OCW)) continue;
       if (kenv > 0 ? k > kenv : k > kmax) continue;
-      bool ok = false;
+      bool fits = true;
       Sched sc;
-      for (int qe = 1; qe <= 64 && !ok; qe++) {
-        bool fits = true;
-        p.nbuf = 0;
-        for (int attempt = 0; attempt < 2; attempt++) {  // the partial buffers take LDS too
-          if (!fill_layout(g, k, D, qe, cc_cap, lds_max, &p)) {
-            fits = false;
-            break;
-          }
-          sc = schedule_rows(g, p, rowptr, col);
-          if (sc.nbuf <= p.nbuf) break;
-          p.nbuf = sc.nbuf;
+      p.nbuf = 0;
+      for (int attempt = 0; attempt < 2; attempt++) {  // the partial buffers take LDS too
+        if (!fill_layout(g, k, D, cc_cap, lds_max, &p)) {
+          fits = false;
+          break;
         }
-        if (!fits) break;
-        if (max_block(g, p, rowptr, col, sc, &p.step_permille) <= 128 * qe) ok = true;
+        sc = schedule_rows(g, p, rowptr, col);
+        if (sc.nbuf <= p.nbuf) break;
+        p.nbuf = sc.nbuf;
       }
-      if (!ok) continue;
+      if (!fits) continue;
+      max_block(g, p, rowptr, col, sc, &p.step_permille);
       p.nbuf = sc.nbuf;
       const int table = p.G * NC * (p.nch + 1);
       p.lds_bytes = 4 * p.D * p.slot_words + 8 * kMaxDepth + 4 * table + 8 * p.nbuf + 4 * p.nbuf * 64 * k;

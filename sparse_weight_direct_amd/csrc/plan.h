@@ -59,10 +59,7 @@ struct Plan {
   int nblk;        // 64-word blocks per staged channel = CHS / 64 (CHS a multiple of 256
                    // in the wide layout: nblk/4 blocks of 256 words)
   int D;           // LDS ring slots: D-1 chunks in flight
-  int QE;          // 16-byte loads per consumer per step carrying its block of non-zeros
-                   // (128 entries each)
-  int nin;         // words of a ring slot holding input rows = Cc*CHS
-  int slot_words;  // words of one ring slot = nin + QE*256*(NW-1)
+  int slot_words;  // words of one ring slot (the chunk's input rows) = Cc*CHS
   int lds_bytes;   // D ring slots + ready/done counters + block-start table
   int span_images; // most images one tile's staged range can touch
   int step_permille;  // 1000 * sum over chunks of the busiest wavefront's entries / mean
@@ -107,7 +104,7 @@ struct KArgs {
   int xoff, cshift;       // see Geom
   int wide16;             // 1: stage rows with 16-byte loads (wide layout, aligned input)
   int nsb;                // staging blocks per channel: nblk/4 of 256 words (wide16) or nblk
-  int PL, CHS, nblk, Cc, nch, G, D, QE, nin, slot_words;
+  int PL, CHS, nblk, Cc, nch, G, D, slot_words;
   int nbuf;               // partial-sum buffers (split rows)
   int HW;                 // H * W
   int ntiles;             // tiles of 64*K extended positions
