@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense direct baseline")
     ap.add_argument("--miopen", action="store_true", help="also time torch conv2d (MIOpen) as context")
+    ap.add_argument("--chain", default=None,
+                    help="also time a layer stack from workloads.CHAINS, eager launches vs one graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
@@ -166,6 +168,23 @@ def main():
 
         mms, _ = run(miopen_step, max(10, args.steps // 10), 3)
         extra["torch_conv2d_miopen_ms"] = round(mms, 5)
+
+    if args.chain:
+        from sparse_weight_direct_amd.chain import LayerChain
+        layers = workloads.make_chain(args.chain)
+        chain = LayerChain([sc.Handle(values=cd["w"], mask=cd["mask"], **cd["geom"]) for cd in layers],
+                           N=layers[0]["x"].shape[0], device=dev)
+        chain.x.copy_(torch.from_numpy(layers[0]["x"]))
+        eager_ms, _ = run(lambda i: chain.run(), args.steps, args.warmup)
+        chain.capture()
+        graph_ms, _ = run(lambda i: chain.replay(), args.steps, args.warmup)
+        cflops = sum(roofline.effective_flops(int(cd["mask"].sum()), cd["x"].shape[0] if j == 0 else chain.N,
+                                              chain.handles[j].E, chain.handles[j].F)
+                     for j, cd in enumerate(layers))
+        extra["chain"] = {"name": args.chain, "layers": len(layers), "eager_us": round(eager_ms * 1e3, 2),
+                          "graph_us": round(graph_ms * 1e3, 2),
+                          "graph_tflops": round(cflops / (graph_ms * 1e-3) / 1e12, 3)}
+        log(f"[bench] chain {args.chain}: eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3:.1f} us per stack")
 
     if args.copy_mb > 0:
         nb = args.copy_mb << 20

@@ -413,7 +413,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
   for (int o = 0; o < OCW; o++)
 #pragma unroll
     for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
-  int units_done = 0;  // units finished by this workgroup (generation of the partial buffers)
+  int units_done = 0;  // units finished by this workgroup
   for (int s = 0; s < S; s++) {
     const int buf = s % a.D;
     lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
@@ -440,6 +440,9 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
     else
       __builtin_amdgcn_s_setprio(0);
     if (it.k + 1 == a.nch) {
+      // generation of this group's partial buffers: the group's units this workgroup has
+      // finished (units cycle through the G groups, so every G-th unit is this group's)
+      const int gen = units_done / a.G;
       const int* rows = slot_row + (it.g * NC + c) * OCW;
       const int* comb = slot_comb + (it.g * NC + c) * OCW;
       // later pieces of split rows leave their partial sums in LDS buffers (after the
@@ -449,12 +452,12 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
         const int v = rows[o];
         if (v <= -2) {
           const int b = -2 - v;
-          lds_wait_ge(&pcons[b], (uint32_t)units_done);
+          lds_wait_ge(&pcons[b], (uint32_t)gen);
           float* pb = pbuf + b * (64 * K) + lane;
 #pragma unroll
           for (int q = 0; q < K; q++) pb[64 * q] = acc[o][q];
           if (lane == 0)
-            __hip_atomic_store(&pfull[b], (uint32_t)(units_done + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(&pfull[b], (uint32_t)(gen + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
           for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
         }
@@ -470,12 +473,12 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
           const int cm = comb[o];
           for (int i = 0; i < (cm & 255); i++) {
             const int b = (cm >> 8) + i;
-            lds_wait_ge(&pfull[b], (uint32_t)(units_done + 1));
+            lds_wait_ge(&pfull[b], (uint32_t)(gen + 1));
             const float* pb = pbuf + b * (64 * K) + lane;
 #pragma unroll
             for (int q = 0; q < K; q++) acc[o][q] += pb[64 * q];
             if (lane == 0)
-              __hip_atomic_store(&pcons[b], (uint32_t)(units_done + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              __hip_atomic_store(&pcons[b], (uint32_t)(gen + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
           // ordinary (write-back) stores: the partial 64-byte segments at output-row and tile
           // boundaries are merged in L2 instead of being written to HBM separately

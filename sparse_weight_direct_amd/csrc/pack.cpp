@@ -133,6 +133,9 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
   std::vector<long long> gmax(nch);
   std::vector<int> cnt(NC);
   std::vector<int> holder((size_t)NC * M, 0);  // consumer w holds a piece of row m
+  // partial-sum buffers are numbered across all groups: a buffer belongs to one group, so it
+  // is used once in every unit of that group (the kernel counts its uses per group)
+  int nb = 0;
   for (int q = 0; q < G; q++) {
     std::fill(load.begin(), load.end(), 0);
     std::fill(wt.begin(), wt.end(), 0);
@@ -173,7 +176,6 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
     }
     std::fill(holder.begin(), holder.end(), 0);
     // kernel tables: piece 0 owns the row; later pieces get partial buffers in order
-    int nb = 0;
     std::vector<int> first_buf(M, -1);
     for (int w = 0; w < NC; w++)
       for (int o = 0; o < OCW; o++) {
@@ -184,7 +186,7 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
           nb += P[m] - 1;
         }
       }
-    sc.nbuf = std::max(sc.nbuf, nb);
+    sc.nbuf = nb;
     for (int w = 0; w < NC; w++) {
       long long nz = 0;
       for (int o = 0; o < OCW; o++) {

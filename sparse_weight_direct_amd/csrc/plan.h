@@ -80,7 +80,7 @@ struct Sched {
   std::vector<int32_t> src_row;    // row whose piece a slot holds, -1 empty
   std::vector<int32_t> piece;      // piece index of the slot
   std::vector<int32_t> npieces;    // pieces of that row
-  int nbuf = 0;                    // partial buffers a group needs
+  int nbuf = 0;                    // partial buffers of all groups (each used by one group)
   int32_t max_wave_nnz = 0;        // largest non-zero count of one consumer
   int32_t split_pieces = 0;        // pieces beyond the first, over all rows
 };

@@ -218,3 +218,11 @@ def test_no_split_for_balanced_layers():
     for name in ("imb80", "imb95", "tiny", "late"):
         d = workloads.make(name, n_override=1)
         assert _pack_host(d, d["layer"]).info()["split_pieces"] == 0, name
+
+
+def test_chain_rejects_mismatched_shapes():
+    from sparse_weight_direct_amd.chain import LayerChain
+    a = sc.Handle(8, 4, 3, 3, 10, 10, 1, 1, values=np.ones((8, 4, 3, 3), np.float32), flags=sc.SC_PACK_HOST_ONLY)
+    b = sc.Handle(8, 6, 3, 3, 10, 10, 1, 1, values=np.ones((8, 6, 3, 3), np.float32), flags=sc.SC_PACK_HOST_ONLY)
+    with pytest.raises(ValueError):
+        LayerChain([a, b], N=1)

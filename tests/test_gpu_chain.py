@@ -1,0 +1,58 @@
+"""Layer stacks (chain.LayerChain): each layer's output against the oracle applied to that
+layer's actual input, and graph replays against the eager run.
+
+A stack runs the same kernels in the same order whether launched eagerly or replayed from
+a captured graph, and the kernel's summation order is fixed by the schedule, so every
+replay must equal the eager output bit for bit.  Replays are interleaved with other eager
+GPU work and checked one by one (a graph that recorded state-dependent nodes would drift
+on later replays)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_weight_direct_amd as sc
+import workloads
+from gpu_util import assert_parity
+from sparse_weight_direct_amd.chain import LayerChain
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain(name):
+    layers = workloads.make_chain(name)
+    handles = [sc.Handle(values=d["w"], mask=d["mask"], **d["geom"]) for d in layers]
+    ch = LayerChain(handles, N=layers[0]["x"].shape[0])
+    ch.x.copy_(torch.from_numpy(layers[0]["x"]))
+    return layers, ch
+
+
+@pytest.mark.parametrize("name", list(workloads.CHAINS))
+def test_chain_each_layer_matches_oracle(name):
+    layers, ch = _chain(name)
+    ch.run()
+    torch.cuda.synchronize()
+    src = layers[0]["x"]
+    for i, (d, out) in enumerate(zip(layers, ch.outs)):
+        g = d["geom"]
+        ref = oracle.reference(src, d["w"], d["mask"], g["stride"], g["pad"])
+        y = out.cpu().numpy()
+        assert_parity(y, ref["y64"], ref["mag"], f"{name} layer {i}")
+        src = y  # the next layer's oracle input is this layer's GPU output
+
+
+@pytest.mark.parametrize("name", list(workloads.CHAINS))
+def test_chain_graph_replays_equal_eager(name):
+    _, ch = _chain(name)
+    eager = ch.run().clone()
+    torch.cuda.synchronize()
+    ch.capture()
+    other = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        for o in ch.outs:
+            o.fill_(float("nan"))
+        _ = (other * 2.0).sum()  # unrelated eager work between replays
+        ch.replay()
+        torch.cuda.synchronize()
+        got = ch.outs[-1]
+        assert torch.equal(got, eager), f"replay {rep}: {int((got != eager).sum())} outputs differ"

@@ -198,6 +198,31 @@ def test_split_rows_many_units(plan, monkeypatch):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+@pytest.mark.parametrize("name,plan", [("mid", "K=1,OCW=1"), ("pw1x1", "K=1,OCW=2"), ("tiny", "K=1,OCW=1,D=2")])
+def test_split_rows_in_some_groups_finish_promptly(name, plan, monkeypatch):
+    """Several groups of output channels per tile, where only some groups split rows: a
+    group's partial-sum buffers are used only in that group's units, so the waits on them
+    must follow that group's units alone.  (Counted over all units they wait for a use that
+    never comes, until the bounded spin gives up about 0.1 s later.)"""
+    monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make(name)
+    L = d["layer"]
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    info = h.info()
+    assert info["row_groups"] > 1 and info["split_pieces"] > 0
+    assert_parity(y, r["y64"], r["mag"], f"{name} {plan}")
+    xd = torch.from_numpy(d["x"]).cuda()
+    out = torch.empty((L.N, L.M, L.E, L.F), dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h.forward(xd, out)
+    e0.record()
+    h.forward(xd, out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) < 20.0, f"forward took {e0.elapsed_time(e1):.1f} ms"
+
+
 def test_fewer_channels_than_wavefronts():
     """M = 4 output channels on 15 computing wavefronts: every channel is split."""
     d = workloads.make_custom(2, 16, 30, 30, 4, 3, 3, 1, 1, 0.5, 42)

@@ -27,7 +27,7 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Layer", "LAYERS", "BENCH_LAYER", "make", "make_custom", "layer_seed"]
+__all__ = ["Layer", "LAYERS", "BENCH_LAYER", "CHAINS", "make", "make_custom", "make_chain", "layer_seed"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -148,3 +148,31 @@ def make(name: str, n_override: int | None = None):
                     L.x_dist, L.w_dist, L.mask_kind, n_override)
     d["layer"] = L
     return d
+
+
+# Layer stacks for the chaining measurement: the same shape repeated, each layer with its own
+# weights (layer family 9 + the stack's index in CHAINS, sweep point = position in the
+# stack); layer i+1 takes layer i's output, so C = M and the 3x3, stride-1, pad-1 layers
+# keep H x W.
+CHAINS = {
+    "tiny4": dict(depth=4, N=1, C=16, H=16, W=16, R=3, S=3, stride=1, pad=1, keep=0.10,
+                  w_dist="u11", mask_kind="bernoulli"),
+    "mid4": dict(depth=4, N=1, C=64, H=56, W=56, R=3, S=3, stride=1, pad=1, keep=0.05,
+                 w_dist="n0.05", mask_kind="exact"),
+}
+
+
+def make_chain(name: str):
+    """Draw a layer stack: the first layer's activations and every layer's (w, mask).
+    Returns a list of per-layer dicts (as make_custom, with ``geom``); only the first holds
+    a meaningful ``x``."""
+    c = CHAINS[name]
+    out = []
+    for j in range(c["depth"]):
+        d = make_custom(c["N"], c["C"], c["H"], c["W"], c["C"], c["R"], c["S"], c["stride"], c["pad"],
+                        c["keep"], layer_seed(9 + list(CHAINS).index(name), j), "u11", c["w_dist"],
+                        c["mask_kind"], n_override=c["N"] if j == 0 else 1)
+        d["geom"] = dict(M=c["C"], C=c["C"], R=c["R"], S=c["S"], H=c["H"], W=c["W"],
+                         stride=c["stride"], pad=c["pad"])
+        out.append(d)
+    return out
