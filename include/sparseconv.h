@@ -98,6 +98,12 @@ typedef struct {
   int32_t split_pieces;  /* rows longer than a wavefront's fair share are split into pieces
                             held by different wavefronts and summed in a fixed order at the
                             end of a work unit: the number of pieces beyond the first */
+  int32_t plan_variants; /* launch plans the handle holds.  The fields above describe the
+                            default one (most positions per workgroup); the others have fewer
+                            positions per workgroup or fewer rows per wavefront, i.e. more
+                            work units, and the forward pass takes the one estimated fastest
+                            for its N (small batches and small images use more, smaller
+                            units so that every CU has work) */
 } sc_info;
 
 /*

@@ -54,7 +54,7 @@ class sc_info(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
                                                "pipeline_depth", "step_balance_permille",
-                                               "split_pieces")]
+                                               "split_pieces", "plan_variants")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -39,24 +39,36 @@ bool fail_alloc_hook() {
 
 }  // namespace
 
-struct sc_handle {
-  uint64_t magic;
-  sc::Geom g;
+// One launch plan of a handle with its own kernel stream and tables on the device.  A handle
+// holds the default plan (variant 0, the most positions per lane that fit) and a few plans
+// with fewer positions per lane or fewer rows per wavefront, which make more work units: the
+// forward pass picks the one a cost model rates fastest for its batch size.
+struct Variant {
   sc::Plan p;
-  int64_t nnz;
-  std::vector<int32_t> rowptr;   // canonical CSR row pointers
-  std::vector<uint32_t> off;     // canonical stretched offsets
-  std::vector<float> val;        // canonical values
+  sc::Sched sched;
   int32_t max_wave_nnz;
   int32_t split_pieces;
-  int device;
-  bool host_only;
-  void* dmem;
-  size_t dbytes;
+  int cus, per_cu;  // device CUs and workgroups of this plan's kernel per CU
+  std::vector<uint32_t> ent;
+  std::vector<int32_t> bstart;
   const uint32_t* d_ent;
   const int32_t* d_seg;
   const int32_t* d_slot;
   const int32_t* d_comb;
+};
+
+struct sc_handle {
+  uint64_t magic;
+  sc::Geom g;
+  int64_t nnz;
+  std::vector<int32_t> rowptr;   // canonical CSR row pointers
+  std::vector<uint32_t> off;     // canonical stretched offsets
+  std::vector<float> val;        // canonical values
+  std::vector<Variant> var;
+  int device;
+  bool host_only;
+  void* dmem;
+  size_t dbytes;
 };
 
 namespace {
@@ -155,19 +167,32 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     sc_status s = build_csr(w, M, crs, (flags & SC_PACK_ALL_TAPS) != 0, rowptr, col, val);
     if (s != SC_OK) return s;
     const long long nnz = (long long)col.size();
-    sc::Sched sched;
-    sc::Plan p = sc::choose_plan(g, rowptr, col, &sched);
-    const int32_t max_wave_nnz = sched.max_wave_nnz;
-    if (p.K == 0) return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
+    // plan variants: the default, then caps on positions per lane and rows per wavefront
+    // (none when SPARSECONV_PLAN forces a plan)
+    std::vector<Variant> vars;
+    {
+      static const int caps[][2] = {{0, 0}, {4, 0}, {2, 0}, {1, 0}, {2, 2}, {2, 1}, {1, 1}};
+      const bool forced = std::getenv("SPARSECONV_PLAN") != nullptr;
+      for (const auto& cap : caps) {
+        Variant v;
+        v.p = sc::choose_plan(g, rowptr, col, &v.sched, cap[0], cap[1]);
+        if (v.p.K == 0) {
+          if (vars.empty()) break;
+          continue;
+        }
+        bool dup = false;
+        for (const Variant& u : vars) dup = dup || (u.p.K == v.p.K && u.p.OCW == v.p.OCW);
+        if (!dup) vars.push_back(std::move(v));
+        if (forced) break;
+      }
+    }
+    if (vars.empty()) return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
     h->magic = kMagic;
     h->g = g;
-    h->p = p;
     h->nnz = nnz;
     h->host_only = (flags & SC_PACK_HOST_ONLY) != 0;
-    h->max_wave_nnz = max_wave_nnz;
-    h->split_pieces = sched.split_pieces;
     h->dmem = nullptr;
     h->dbytes = 0;
     h->off.resize(nnz);
@@ -178,62 +203,73 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->val = val;
     h->rowptr = rowptr;
 
-    // Kernel stream: per (group, consumer wavefront), one block per chunk holding header entries
-    // {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
-    // non-zeros {enc, value} in slot order; each block starts at a multiple of 64 entries
-    // (the kernel loads whole groups of 64), with zero entries in the gaps.
-    // bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of block k and
-    // bstart[.. + nch] the end of the last one.
-    const int waves = p.G * (p.NW - 1);  // consumer wavefronts
-    std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
-    for (int m = 0; m < M; m++) {
-      int j = rowptr[m];
-      for (int k = 0; k <= p.nch; k++) {
-        while (j < rowptr[m + 1] && col[j] / (R * S) < k * p.Cc) j++;
-        chunk_start[(size_t)m * (p.nch + 1) + k] = j;
-      }
-      chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
-    }
-    const int hdr_n = sc::block_header(p.OCW);
-    const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + 63) + 64;
-    if (n_ent >= (size_t)1 << 31) {
-      sparseconv_destroy(h);
-      return fail(SC_EUNSUPPORTED, "kernel stream too large");
-    }
-    std::vector<uint32_t> ent(2 * std::max<size_t>(n_ent, 1), 0);
-    std::vector<int32_t> bstart((size_t)waves * (p.nch + 1));
-    size_t pos = 0;
-    for (int wv = 0; wv < waves; wv++) {
-      for (int k = 0; k < p.nch; k++) {
-        pos = (pos + 63) & ~(size_t)63;
-        bstart[(size_t)wv * (p.nch + 1) + k] = (int32_t)pos;
-        const size_t hdr = pos;
-        pos += hdr_n;
-        for (int o = 0; o < p.OCW; o++) {
-          const size_t sl = (size_t)wv * p.OCW + o;
-          const int m = sched.src_row[sl];
-          int cnt = 0;
-          if (m >= 0) {  // this slot's piece of row m: part of the row's entries of chunk k
-            int b = chunk_start[(size_t)m * (p.nch + 1) + k];
-            int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
-            sc::piece_range(b, e, sched.piece[sl], sched.npieces[sl], &b, &e);
-            for (int j = b; j < e; j++) {
-              const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
-              const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
-                                              (r / stride) * g.Pp + sx / stride);
-              uint32_t vbits;
-              std::memcpy(&vbits, &val[j], 4);
-              ent[2 * pos] = enc;
-              ent[2 * pos + 1] = vbits;
-              pos++;
-            }
-            cnt = e - b;
-          }
-          ent[2 * (hdr + o)] = (uint32_t)cnt;
+    for (Variant& v : vars) {
+      const sc::Plan& p = v.p;
+      const sc::Sched& sched = v.sched;
+      v.max_wave_nnz = sched.max_wave_nnz;
+      v.split_pieces = sched.split_pieces;
+      // Kernel stream: per (group, consumer wavefront), one block per chunk holding header
+      // entries {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
+      // non-zeros {enc, value} in slot order; each block starts at a multiple of 64 entries
+      // (the kernel loads whole groups of 64), with zero entries in the gaps.
+      // bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of block k and
+      // bstart[.. + nch] the end of the last one.
+      const int waves = p.G * (p.NW - 1);  // consumer wavefronts
+      std::vector<int32_t> chunk_start((size_t)M * (p.nch + 1));
+      for (int m = 0; m < M; m++) {
+        int j = rowptr[m];
+        for (int k = 0; k <= p.nch; k++) {
+          while (j < rowptr[m + 1] && col[j] / (R * S) < k * p.Cc) j++;
+          chunk_start[(size_t)m * (p.nch + 1) + k] = j;
         }
+        chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
       }
-      bstart[(size_t)wv * (p.nch + 1) + p.nch] = (int32_t)pos;
+      const int hdr_n = sc::block_header(p.OCW);
+      const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + 63) + 64;
+      if (n_ent >= (size_t)1 << 31) {
+        sparseconv_destroy(h);
+        return fail(SC_EUNSUPPORTED, "kernel stream too large");
+      }
+      std::vector<uint32_t>& ent = v.ent;
+      std::vector<int32_t>& bstart = v.bstart;
+      ent.assign(2 * std::max<size_t>(n_ent, 1), 0);
+      bstart.assign((size_t)waves * (p.nch + 1), 0);
+      size_t pos = 0;
+      for (int wv = 0; wv < waves; wv++) {
+        for (int k = 0; k < p.nch; k++) {
+          pos = (pos + 63) & ~(size_t)63;
+          bstart[(size_t)wv * (p.nch + 1) + k] = (int32_t)pos;
+          const size_t hdr = pos;
+          pos += hdr_n;
+          for (int o = 0; o < p.OCW; o++) {
+            const size_t sl = (size_t)wv * p.OCW + o;
+            const int m = sched.src_row[sl];
+            int cnt = 0;
+            if (m >= 0) {  // this slot's piece of row m: part of the row's entries of chunk k
+              int b = chunk_start[(size_t)m * (p.nch + 1) + k];
+              int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
+              sc::piece_range(b, e, sched.piece[sl], sched.npieces[sl], &b, &e);
+              for (int j = b; j < e; j++) {
+                const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
+                const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
+                                                (r / stride) * g.Pp + sx / stride);
+                uint32_t vbits;
+                std::memcpy(&vbits, &val[j], 4);
+                ent[2 * pos] = enc;
+                ent[2 * pos + 1] = vbits;
+                pos++;
+              }
+              cnt = e - b;
+            }
+            ent[2 * (hdr + o)] = (uint32_t)cnt;
+          }
+        }
+        bstart[(size_t)wv * (p.nch + 1) + p.nch] = (int32_t)pos;
+      }
+      v.cus = 256;
+      v.per_cu = 1;
     }
+    h->var = std::move(vars);
 
     if (!h->host_only) {
       if (hipGetDevice(&h->device) != hipSuccess) {
@@ -241,31 +277,41 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_EDEVICE, "no HIP device available");
       }
       auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-      const size_t b_ent = al(ent.size() * 4);
-      const size_t b_seg = al(bstart.size() * 4);
-      const size_t b_slot = al(sched.slot_row.size() * 4);
-      const size_t b_comb = al(sched.slot_comb.size() * 4);
-      h->dbytes = b_ent + b_seg + b_slot + b_comb;
+      size_t total = 0;
+      for (const Variant& v : h->var)
+        total += al(v.ent.size() * 4) + al(v.bstart.size() * 4) + al(v.sched.slot_row.size() * 4) +
+                 al(v.sched.slot_comb.size() * 4);
+      h->dbytes = total;
       if (hipMalloc(&h->dmem, h->dbytes) != hipSuccess) {
         h->dmem = nullptr;
         sparseconv_destroy(h);
         return fail(SC_ENOMEM, "hipMalloc of the packed filter bank failed");
       }
       char* base = static_cast<char*>(h->dmem);
-      h->d_ent = reinterpret_cast<const uint32_t*>(base);
-      h->d_seg = reinterpret_cast<const int32_t*>(base + b_ent);
-      h->d_slot = reinterpret_cast<const int32_t*>(base + b_ent + b_seg);
-      h->d_comb = reinterpret_cast<const int32_t*>(base + b_ent + b_seg + b_slot);
-      hipError_t e1 = hipMemcpy(base, ent.data(), ent.size() * 4, hipMemcpyHostToDevice);
-      hipError_t e2 = hipMemcpy(base + b_ent, bstart.data(), bstart.size() * 4, hipMemcpyHostToDevice);
-      hipError_t e3 = hipMemcpy(base + b_ent + b_seg, sched.slot_row.data(), sched.slot_row.size() * 4,
-                                hipMemcpyHostToDevice);
-      hipError_t e4 = hipMemcpy(base + b_ent + b_seg + b_slot, sched.slot_comb.data(), sched.slot_comb.size() * 4,
-                                hipMemcpyHostToDevice);
-      if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess) {
-        sparseconv_destroy(h);
-        return fail(SC_EDEVICE, "upload of the packed filter bank failed");
+      for (Variant& v : h->var) {
+        const size_t b_ent = al(v.ent.size() * 4), b_seg = al(v.bstart.size() * 4);
+        const size_t b_slot = al(v.sched.slot_row.size() * 4), b_comb = al(v.sched.slot_comb.size() * 4);
+        v.d_ent = reinterpret_cast<const uint32_t*>(base);
+        v.d_seg = reinterpret_cast<const int32_t*>(base + b_ent);
+        v.d_slot = reinterpret_cast<const int32_t*>(base + b_ent + b_seg);
+        v.d_comb = reinterpret_cast<const int32_t*>(base + b_ent + b_seg + b_slot);
+        hipError_t e1 = hipMemcpy(base, v.ent.data(), v.ent.size() * 4, hipMemcpyHostToDevice);
+        hipError_t e2 = hipMemcpy(base + b_ent, v.bstart.data(), v.bstart.size() * 4, hipMemcpyHostToDevice);
+        hipError_t e3 = hipMemcpy(base + b_ent + b_seg, v.sched.slot_row.data(), v.sched.slot_row.size() * 4,
+                                  hipMemcpyHostToDevice);
+        hipError_t e4 = hipMemcpy(base + b_ent + b_seg + b_slot, v.sched.slot_comb.data(),
+                                  v.sched.slot_comb.size() * 4, hipMemcpyHostToDevice);
+        const int eo = sc::occupancy(v.p, &v.cus, &v.per_cu);
+        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess || eo != (int)hipSuccess) {
+          sparseconv_destroy(h);
+          return fail(SC_EDEVICE, "upload of the packed filter bank failed");
+        }
+        base += b_ent + b_seg + b_slot + b_comb;
       }
+    }
+    for (Variant& v : h->var) {  // the host copies are not needed any more
+      std::vector<uint32_t>().swap(v.ent);
+      std::vector<int32_t>().swap(v.bstart);
     }
     *out = h;
     return SC_OK;
@@ -289,16 +335,18 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->nnz = h->nnz;
   info->packed_bytes = (2 * h->nnz + h->g.M + 1) * 4;
   info->device_bytes = (int64_t)h->dbytes;
-  info->tile_pixels = 64 * h->p.K;
-  info->waves_per_group = h->p.NW - 1;
-  info->pipeline_depth = h->p.D;
-  info->step_balance_permille = h->p.step_permille;
-  info->split_pieces = h->split_pieces;
-  info->rows_per_wave = h->p.OCW;
-  info->row_groups = h->p.G;
-  info->chunk_channels = h->p.Cc;
-  info->lds_bytes = h->p.lds_bytes;
-  info->max_wave_nnz = h->max_wave_nnz;
+  const Variant& v = h->var[0];  // the default plan
+  info->tile_pixels = 64 * v.p.K;
+  info->waves_per_group = v.p.NW - 1;
+  info->pipeline_depth = v.p.D;
+  info->step_balance_permille = v.p.step_permille;
+  info->split_pieces = v.split_pieces;
+  info->rows_per_wave = v.p.OCW;
+  info->row_groups = v.p.G;
+  info->chunk_channels = v.p.Cc;
+  info->lds_bytes = v.p.lds_bytes;
+  info->max_wave_nnz = v.max_wave_nnz;
+  info->plan_variants = (int32_t)h->var.size();
   return SC_OK;
 }
 
@@ -361,6 +409,34 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   return a;
 }
 
+// Estimated cycles of a forward over N images with plan variant v: the busiest CU's units
+// times a unit's cost, the larger of its input copy (LDS DMA at ~15 B/cycle with 16-byte
+// loads, ~3.7 with 4-byte ones) and its walk (~2.3 cycles per non-zero and 64-position block
+// of LDS reads), plus a fixed cost per chunk step and per launch.  Only used to rank the
+// handle's variants.
+double estimate_cycles(const sc::Geom& g, const Variant& v, int N, long long nnz) {
+  const sc::Plan& p = v.p;
+  const long long ext = (long long)N * g.HYp * g.Pp;
+  const long long units = (ext + 64LL * p.K - 1) / (64LL * p.K) * p.G;
+  const long long per_cu = (units + v.cus - 1) / v.cus;
+  const double stage = (double)g.C * p.CHS * 4.0 / (g.wide ? 15.0 : 3.7);
+  const double walk = (double)nnz / p.G * p.K * (p.K >= 2 ? 2.3 : 3.0);
+  return 6000.0 + (double)per_cu * (1500.0 * p.nch + std::max(stage, walk));
+}
+
+size_t pick_variant(const sc_handle* h, int N) {
+  size_t best = 0;
+  double bc = 0;
+  for (size_t i = 0; i < h->var.size(); i++) {
+    const double c = estimate_cycles(h->g, h->var[i], N, h->nnz);
+    if (i == 0 || c < bc) {
+      best = i;
+      bc = c;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,20 +452,21 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   if (C != g.C || H != g.H || W != g.W || M != g.M || R != g.R || S != g.S || stride != g.st || pad != g.pad)
     return fail(SC_ESHAPE, "forward dims differ from the packed handle");
   if (N == 0) return SC_OK;
-  sc_status s = check_io(g, h->p, input, output, N);
+  const Variant& v = h->var[pick_variant(h, N)];
+  sc_status s = check_io(g, v.p, input, output, N);
   if (s != SC_OK) return s;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
-  sc::KArgs a = make_args(g, h->p, input, output, N);
-  a.ent = h->d_ent;
-  a.seg = h->d_seg;
-  a.slot_row = h->d_slot;
-  a.slot_comb = h->d_comb;
-  int gerr = 0;
-  const int nb = sc::grid_size(h->p, (long long)a.ntiles * h->p.G, &gerr);
-  if (gerr) return fail(SC_EDEVICE, std::string("occupancy query failed: ") + hipGetErrorString((hipError_t)gerr));
-  const int e = sc::launch_sparse(h->p, a, hip_stream, nb);
+  sc::KArgs a = make_args(g, v.p, input, output, N);
+  a.ent = v.d_ent;
+  a.seg = v.d_seg;
+  a.slot_row = v.d_slot;
+  a.slot_comb = v.d_comb;
+  const long long units = (long long)a.ntiles * v.p.G;
+  const long long slots = (long long)v.cus * v.per_cu;
+  const int nb = (int)(units < slots ? units : slots);
+  const int e = sc::launch_sparse(v.p, a, hip_stream, nb);
   if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
   return SC_OK;
 }

@@ -556,24 +556,18 @@ static hipError_t allow_lds(const void* fn, int bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-int grid_size(const Plan& p, long long units, int* err) {
-  *err = 0;
+int occupancy(const Plan& p, int* cus, int* per_cu) {
+  *cus = 0;
+  *per_cu = 0;
   const void* fn = reinterpret_cast<const void*>(pick_sparse(p));
-  if (!fn) {
-    *err = (int)hipErrorInvalidDeviceFunction;
-    return 0;
-  }
-  int dev = 0, cus = 0, per_cu = 0;
+  if (!fn) return (int)hipErrorInvalidDeviceFunction;
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) e = allow_lds(fn, p.lds_bytes);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, p.NW * 64, p.lds_bytes);
-  if (e != hipSuccess) {
-    *err = (int)e;
-    return 0;
-  }
-  const long long slots = (long long)cus * (per_cu > 0 ? per_cu : 1);
-  return (int)(units < slots ? units : slots);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, p.NW * 64, p.lds_bytes);
+  if (*per_cu < 1) *per_cu = 1;
+  return (int)e;
 }
 
 int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks) {

@@ -87,10 +87,38 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
     P[big]--;
     pieces--;
   }
-  // items: (row, piece) with padded per-chunk counts
+  // rows (with all their pieces) -> groups, largest first onto the least-loaded group with
+  // room.  A row whose pieces fit no group (the free slots are spread over groups) gets as
+  // many pieces as the roomiest group has slots left; the total never exceeds the slots, so
+  // one piece always fits.
+  std::vector<int> order(M);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return tot[a] > tot[b]; });
+  std::vector<int> row_group(M, 0);
+  {
+    std::vector<long long> gl(G, 0);
+    std::vector<int> used(G, 0);
+    for (int m : order) {
+      int best = -1;
+      for (int q = 0; q < G; q++)
+        if (used[q] + P[m] <= NC * OCW && (best < 0 || gl[q] < gl[best])) best = q;
+      if (best < 0) {
+        for (int q = 0; q < G; q++)
+          if (best < 0 || used[q] < used[best]) best = q;
+        const int fit = std::max(1, NC * OCW - used[best]);
+        pieces -= P[m] - fit;
+        P[m] = fit;
+      }
+      row_group[m] = best;
+      gl[best] += tot[m];
+      used[best] += P[m];
+    }
+  }
+  // items: (row, piece) with their per-chunk counts
   struct Item { int m, p; long long tot; };
   std::vector<Item> items;
   std::vector<int32_t> ivec;
+  std::vector<std::vector<int>> grp(G);  // item indices per group
   for (int m = 0; m < M; m++)
     for (int q = 0; q < P[m]; q++) {
       long long t = 1;
@@ -101,28 +129,9 @@ static Sched schedule_rows(const Geom& g, const Plan& p, const std::vector<int32
         ivec.push_back(n);
         t += n;
       }
+      grp[row_group[m]].push_back((int)items.size());
       items.push_back({m, q, t});
     }
-  std::vector<int> first_item(M);
-  for (int i = (int)items.size() - 1; i >= 0; i--) first_item[items[i].m] = i;
-  // rows (with their pieces) -> groups
-  std::vector<int> order(M);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return tot[a] > tot[b]; });
-  std::vector<std::vector<int>> grp(G);  // item indices per group
-  {
-    std::vector<long long> gl(G, 0);
-    std::vector<int> used(G, 0);
-    for (int m : order) {
-      int best = -1;
-      for (int q = 0; q < G; q++)
-        if (used[q] + P[m] <= NC * OCW && (best < 0 || gl[q] < gl[best])) best = q;
-      if (best < 0) best = 0;  // cannot happen: pieces never exceed the slots
-      for (int q = 0; q < P[m]; q++) grp[best].push_back(first_item[m] + q);
-      gl[best] += tot[m];
-      used[best] += P[m];
-    }
-  }
   Sched sc;
   sc.slot_row.assign((size_t)G * NC * OCW, -1);
   sc.slot_comb.assign((size_t)G * NC * OCW, 0);
@@ -307,7 +316,7 @@ static bool instantiated(int K, int OCW) {
 }
 
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched) {
+                 Sched* sched, int k_cap, int ocw_cap) {
   static const int kOcw[] = {1, 2, 3, 5, 9};
   static const int kKs[] = {16, 12, 8, 7, 6, 4, 2, 1};
   Plan p{};
@@ -340,6 +349,12 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
   bool oko = false;
   for (int o : kOcw) oko = oko || o == OCW;
   if (!oko) OCW = 9;
+  if (ocw_cap > 0 && OCW > ocw_cap) {  // the largest instantiated count within the cap
+    int best = kOcw[0];
+    for (int o : kOcw)
+      if (o <= ocw_cap) best = o;
+    OCW = best;
+  }
   // fewer slots per consumer (more groups) when nothing fits
   for (int oi = 4; oi >= 0; oi--) {
     if (kOcw[oi] > OCW) continue;
@@ -347,7 +362,7 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
     p.G = (g.M + NC * p.OCW - 1) / (NC * p.OCW);
     for (int k : kKs) {
       if (!instantiated(k, p.OCW)) continue;
-      if (kenv > 0 ? k > kenv : k > kmax) continue;
+      if (k > (kenv > 0 ? kenv : k_cap > 0 ? std::min(kmax, k_cap) : kmax)) continue;
       bool fits = true;
       Sched sc;
       p.nbuf = 0;

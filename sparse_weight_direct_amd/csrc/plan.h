@@ -116,15 +116,17 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
 // Launch plan for the CSR filter matrix (rowptr, col): also schedules rows onto wavefront
 // slots (slot_row) and sizes each wavefront's per-chunk block of non-zeros.
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched);
+                 Sched* sched, int k_cap = 0, int ocw_cap = 0);
 int plan_pl(const Geom& g, int K);
 
 // Header entries at the start of a wavefront's per-chunk block of non-zeros.
 int block_header(int OCW);
 
-// Workgroups to launch for `units` work units: every CU busy, each workgroup a contiguous
-// run of units (kernels.hip; uses the occupancy of the chosen kernel).
-int grid_size(const Plan& p, long long units, int* err);
+// CUs of the current device and workgroups of the plan's kernel that fit on one CU; also
+// raises the kernel's dynamic LDS limit to the plan's size (kernels.hip).  Returns a
+// hipError_t.  The persistent grid is min(units, cus * per_cu) workgroups, each taking a
+// contiguous run of units.
+int occupancy(const Plan& p, int* cus, int* per_cu);
 
 // Launchers (kernels.hip).  Return a hipError_t value as int.
 int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks);

@@ -10,6 +10,12 @@ import sparse_weight_direct_amd as sc
 REL_TOL = 1e-5
 
 
+# Every wait inside the kernel is bounded (about 0.1 s of spinning before it gives up), so a
+# synchronisation mistake can leave results right and only make the forward slow.  Each
+# forward here is therefore also timed: none of the test layers takes a millisecond.
+MAX_FORWARD_MS = 100.0
+
+
 def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None):
     N, C, H, W = x.shape
     M, _, R, S = w.shape
@@ -17,8 +23,15 @@ def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None):
         handle = sc.Handle(M, C, R, S, H, W, stride, pad, values=w, mask=mask)
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     out = torch.full((N, M, handle.E, handle.F), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    handle.forward(xd, out, stream=stream)  # the first launch of a kernel also loads it
+    e0.record(s)
     handle.forward(xd, out, stream=stream)
+    e1.record(s)
     torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert ms < MAX_FORWARD_MS, f"forward took {ms:.1f} ms: a bounded wait in the kernel timed out"
     return out.cpu().numpy(), handle
 
 
