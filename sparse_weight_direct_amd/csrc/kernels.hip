@@ -150,6 +150,58 @@ __device__ __forceinline__ uint32_t block_voff(const KArgs& a, int I0, int n0, i
   return off;
 }
 
+// The same offsets for consecutive blocks blk, blk+1, ... without divisions: the lane's
+// position (phase ph, word j of the phase plane, image n, row t, column x of the extended
+// plane) advances by 64 words per block.  A step that leaves the phase plane, and images
+// smaller than two blocks, fall back to the divisions.  (Producer only: narrow layout with
+// more blocks than it caches.)
+struct VoffIter {
+  int w, ph, j, n, t, x;
+  int q64, r64;  // 64 = q64 * Pp + r64
+  __device__ __forceinline__ void full(const KArgs& a, int I0) {
+    ph = w / a.PL;
+    j = w - ph * a.PL;
+    const int J = I0 + j;
+    n = J / a.img_ext;
+    const int rem = J - n * a.img_ext;
+    t = rem / a.Pp;
+    x = rem - t * a.Pp;
+  }
+  __device__ __forceinline__ void init(const KArgs& a, int I0, int blk, int lane) {
+    w = 64 * blk + lane;
+    q64 = 64 / a.Pp;
+    r64 = 64 - q64 * a.Pp;
+    full(a, I0);
+  }
+  __device__ __forceinline__ void next(const KArgs& a, int I0) {
+    w += 64;
+    j += 64;
+    if (j >= a.PL || a.img_ext < 128) {
+      full(a, I0);
+      return;
+    }
+    x += r64;
+    t += q64;
+    if (x >= a.Pp) {
+      x -= a.Pp;
+      t++;
+    }
+    if (t >= a.HYp) {  // q64 + 1 < HYp here, so at most one image boundary is crossed
+      t -= a.HYp;
+      n++;
+    }
+  }
+  __device__ __forceinline__ uint32_t off(const KArgs& a, int n0) const {
+    if (ph >= a.st * a.st) return kOutOfRange;
+    const int py = ph / a.st;
+    const int y = t * a.st + py - a.pad;
+    const int xx = x * a.st + (ph - py * a.st) - a.xoff;
+    if (n < a.N && y >= 0 && y < a.H && xx >= 0 && xx < a.W)
+      return 4u * (uint32_t)(((n - n0) * a.C * a.H + y) * a.W + xx);
+    return kOutOfRange;
+  }
+};
+
 // Wide layout (stride 1): source byte offset of the lane's 4 words in block sb of 256 words;
 // the 4 words are one aligned group of 4 input words or 4 zeros.
 __device__ __forceinline__ uint32_t block_voff16(const KArgs& a, int I0, int n0, int sb, int lane) {
@@ -178,13 +230,19 @@ __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int 
                                           const uint32_t (&voffc)[4], float* slot, int lane,
                                           FirstDone&& first_done) {
   const int bw = a.wide16 ? 256 : 64;
+  VoffIter vi;
+  if (!a.wide16 && a.nsb > 4) vi.init(a, I0, 4, lane);
   for (int blk = 0; blk < a.nsb; blk++) {
     // explicit selects keep the cached offsets in registers (no indexed private array)
-    const uint32_t voff = blk == 0 ? voffc[0]
-                          : blk == 1 ? voffc[1]
-                          : blk == 2 ? voffc[2]
-                          : blk == 3 ? voffc[3]
-                          : (a.wide16 ? block_voff16(a, I0, n0, blk, lane) : block_voff(a, I0, n0, blk, lane));
+    uint32_t voff;
+    if (blk < 4) {
+      voff = blk == 0 ? voffc[0] : blk == 1 ? voffc[1] : blk == 2 ? voffc[2] : voffc[3];
+    } else if (a.wide16) {
+      voff = block_voff16(a, I0, n0, blk, lane);
+    } else {
+      if (blk > 4) vi.next(a, I0);
+      voff = vi.off(a, n0);
+    }
     const float* dst = slot + blk * bw;
     uint32_t soff = 4u * (uint32_t)(c0 * a.HW);
     if (a.wide16) {
