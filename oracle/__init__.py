@@ -57,6 +57,18 @@ def _bind(path: str):
     lib.oracle_conv_csr.argtypes = [_i32] * 9 + [_p] * 6 + [_i32]
     lib.oracle_conv_csr_planes.restype = None
     lib.oracle_conv_csr_planes.argtypes = [_i32] * 9 + [_p] * 4 + [_i64, _p, _p, _p, _i32]
+    lib.oracle_fp16_bits.restype = ctypes.c_uint16
+    lib.oracle_fp16_bits.argtypes = [ctypes.c_float]
+    lib.oracle_fp16_value.restype = ctypes.c_double
+    lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_pack_word.restype = ctypes.c_uint32
+    lib.oracle_pack_word.argtypes = [ctypes.c_float, _i32, _i32, _i32]
+    lib.oracle_unpack_word.restype = None
+    lib.oracle_unpack_word.argtypes = [ctypes.c_uint32, _p, _p, _p, _p]
+    lib.oracle_words_from_csr.restype = None
+    lib.oracle_words_from_csr.argtypes = [_i32, _i32, _i64, _p, _p, _p]
+    lib.oracle_csr_from_words.restype = None
+    lib.oracle_csr_from_words.argtypes = [_i32, _i32, _i64, _p, _p, _p]
     lib.oracle_max_threads.restype = _i32
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -182,6 +194,67 @@ def reference(x: np.ndarray, w: np.ndarray, mask: np.ndarray | None, stride: int
     y64, mag = conv_csr(x, rowptr, colidx, value, M, R, S, stride, pad, nthreads)
     return {"y": to_fp32(y64), "y64": y64, "mag": mag, "rowptr": rowptr, "colidx": colidx,
             "offsets": stretch(colidx, C, R, S, H, W), "values": value}
+
+
+def fp16_bits(v: float) -> int:
+    """IEEE binary16 bits of an fp32 value, round to nearest even (the packed word's weight)."""
+    return int(_load().oracle_fp16_bits(float(np.float32(v))))
+
+
+def fp16_value(h: int) -> float:
+    """Value of binary16 bits, exactly."""
+    return float(_load().oracle_fp16_value(int(h)))
+
+
+def pack_word(v: float, ic: int, px: int, py: int) -> int:
+    """[T] Sec. 5.3 / Fig. 4 packed word: fp16 weight << 16 | ic << 8 | px << 4 | py."""
+    if not (0 <= ic < 256 and 0 <= px < 16 and 0 <= py < 16):
+        raise ValueError("packed word fields out of range (ic < 256, px, py < 16)")
+    return int(_load().oracle_pack_word(float(np.float32(v)), ic, px, py))
+
+
+def unpack_word(wd: int):
+    """(value as double, ic, px, py) of a packed word."""
+    v = ctypes.c_double()
+    ic, px, py = _i32(), _i32(), _i32()
+    _load().oracle_unpack_word(int(wd), ctypes.byref(v), ctypes.byref(ic), ctypes.byref(px), ctypes.byref(py))
+    return v.value, ic.value, px.value, py.value
+
+
+def words_from_csr(colidx, value, C: int, R: int, S: int) -> np.ndarray:
+    """Packed words of the CSR non-zeros in CSR order.  The word holds C <= 256 input
+    channels and R, S <= 16 ([T] Fig. 4 field widths)."""
+    if C > 256 or R > 16 or S > 16:
+        raise ValueError("the packed word holds C <= 256 and R, S <= 16")
+    colidx, value = _c(colidx, np.int32), _c(value, np.float32)
+    words = np.zeros(colidx.size, np.uint32)
+    _load().oracle_words_from_csr(R, S, colidx.size, _ptr(colidx), _ptr(value), _ptr(words))
+    return words
+
+
+def csr_from_words(words, R: int, S: int):
+    """(colidx, value) the packed words describe; values are the fp16 weights in fp32."""
+    words = _c(words, np.uint32)
+    colidx = np.zeros(words.size, np.int32)
+    value = np.zeros(words.size, np.float32)
+    _load().oracle_csr_from_words(R, S, words.size, _ptr(words), _ptr(colidx), _ptr(value))
+    return colidx, value
+
+
+def reference_fp16(x: np.ndarray, w: np.ndarray, mask: np.ndarray | None, stride: int, pad: int,
+                   nthreads: int = 0):
+    """Oracle result for the packed-word form of a layer ([T] Sec. 5.3): the CSR non-zeros
+    are encoded as packed words, decoded again, and the list-form convolution runs on the
+    decoded (fp16-rounded) weights with double accumulation.  Same dict as ``reference``
+    plus ``words``; ``values`` are the fp16-rounded weights."""
+    M, C, R, S = w.shape
+    H, W = x.shape[2], x.shape[3]
+    rowptr, colidx, value = csr_from_dense(w, mask)
+    words = words_from_csr(colidx, value, C, R, S)
+    colidx16, value16 = csr_from_words(words, R, S)
+    y64, mag = conv_csr(x, rowptr, colidx16, value16, M, R, S, stride, pad, nthreads)
+    return {"y": to_fp32(y64), "y64": y64, "mag": mag, "rowptr": rowptr, "colidx": colidx16,
+            "offsets": stretch(colidx16, C, R, S, H, W), "values": value16, "words": words}
 
 
 def within_tolerance(y_gpu: np.ndarray, y_ref64: np.ndarray, mag: np.ndarray, rel: float = 1e-5):

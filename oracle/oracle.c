@@ -17,6 +17,10 @@
  *      f(c,r,s) = (c*H + r)*W + s ("weight stretching"), and the sequential direct
  *      sparse convolution (its Algorithm 2: image n, output channel m, non-zero j,
  *      then the 2-D output plane).
+ *  [T] Sec. 5.3 and Fig. 4 (the packed weight word): one u32 per non-zero holding the fp16
+ *      weight in bits 31-16, the input channel in bits 15-8, the kernel column offset px in
+ *      bits 7-4 and the kernel row offset py in bits 3-0; the weight is widened to fp32
+ *      before use and all accumulation stays in fp32 (here: double).
  *
  * Readings taken where the pages are silent (each also listed in the design notes):
  *  - stride enters as iy = e*stride - pad + r, ix = f*stride - pad + s (cross-correlation,
@@ -26,6 +30,9 @@
  *    kept); without a mask, every w != 0.0f (so -0.0 is dropped and NaN kept).
  *  - accumulation in double precision; the caller rounds the result once to fp32.
  *  - MAG[n,m,e,f] = sum of |w * x| over the same terms, the scale of the error bound.
+ *  - fp32 -> fp16 of the packed word: IEEE 754 binary16, round to nearest with ties to
+ *    even (the pages name no rounding); magnitudes at or above 65520 become infinity, NaN
+ *    stays NaN.  px is the filter column s, py the filter row r.
  */
 #include <math.h>
 #include <stdint.h>
@@ -196,6 +203,83 @@ void oracle_conv_csr_planes(int32_t N, int32_t C, int32_t H, int32_t W, int32_t 
     for (int64_t q = 0; q < nsel; q++)
         conv_plane_csr(planes_sel[q] / M, planes_sel[q] % M, C, H, W, R, S, stride, pad, E, F,
                        x, rowptr, colidx, value, y + q * E * F, mag + q * E * F);
+}
+
+/*
+ * IEEE 754 binary16 bits of the fp32 value v, rounded to nearest, ties to even.  Written
+ * from the format's definition: a finite half is (-1)^sign * n * 2^(e-10) with an 11-bit
+ * significand n in [1024, 2048) for normal exponents e in [-14, 15], and n * 2^-24 with
+ * n < 1024 below 2^-14 (subnormals).  The magnitude is divided by its quantum (exact, both
+ * are powers of two times fp32 values in a double), rounded with rint (ties to even in the
+ * default rounding mode) and re-assembled; a carry into the next binade is handled by the
+ * re-assembly, and a result past 65504 is infinity.
+ */
+uint16_t oracle_fp16_bits(float v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs((double)v);
+    if (isinf(v) || a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexp(1.0, -14)) {                 /* subnormal quantum 2^-24 */
+        double n = rint(a / ldexp(1.0, -24)); /* 0 .. 1024 (1024 is the smallest normal) */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int k;
+    (void)frexp(a, &k);                        /* a = f * 2^k, f in [0.5, 1): exponent e = k-1 */
+    int e = k - 1;
+    double n = rint(a / ldexp(1.0, e - 10));   /* 1024 .. 2048 */
+    if (n == 2048.0) { n = 1024.0; e += 1; }
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+/* Value of the binary16 bits h, as a double (exact). */
+double oracle_fp16_value(uint16_t h) {
+    double sgn = (h & 0x8000u) ? -1.0 : 1.0;
+    int ex = (h >> 10) & 31;
+    int mant = h & 1023;
+    if (ex == 31) return mant ? NAN : sgn * INFINITY;
+    if (ex == 0) return sgn * ldexp((double)mant, -24);
+    return sgn * ldexp((double)(1024 + mant), ex - 25);
+}
+
+/* [T] Sec. 5.3 / Fig. 4: the packed word of one non-zero. ic < 256, px, py < 16. */
+uint32_t oracle_pack_word(float v, int32_t ic, int32_t px, int32_t py) {
+    return ((uint32_t)oracle_fp16_bits(v) << 16) | ((uint32_t)ic << 8) | ((uint32_t)px << 4) |
+           (uint32_t)py;
+}
+
+/* Fields of a packed word: the fp16 weight widened to double, ic, px, py. */
+void oracle_unpack_word(uint32_t wd, double* v, int32_t* ic, int32_t* px, int32_t* py) {
+    *v = oracle_fp16_value((uint16_t)(wd >> 16));
+    *ic = (int32_t)((wd >> 8) & 255u);
+    *px = (int32_t)((wd >> 4) & 15u);
+    *py = (int32_t)(wd & 15u);
+}
+
+/* Packed words of every CSR non-zero, in CSR order: column c*R*S + r*S + s gives ic = c,
+ * px = s (kernel column), py = r (kernel row). */
+void oracle_words_from_csr(int32_t R, int32_t S, int64_t nnz, const int32_t* colidx,
+                           const float* value, uint32_t* words) {
+    for (int64_t j = 0; j < nnz; j++) {
+        int32_t col = colidx[j];
+        int32_t c = col / (R * S);
+        int32_t r = (col / S) % R;
+        int32_t s = col % S;
+        words[j] = oracle_pack_word(value[j], c, s, r);
+    }
+}
+
+/* The CSR non-zeros a list of packed words describes: column c*R*S + r*S + s from
+ * (ic, py, px) and the fp16 weight widened to fp32 (exact). */
+void oracle_csr_from_words(int32_t R, int32_t S, int64_t nnz, const uint32_t* words,
+                           int32_t* colidx, float* value) {
+    for (int64_t j = 0; j < nnz; j++) {
+        double v;
+        int32_t ic, px, py;
+        oracle_unpack_word(words[j], &v, &ic, &px, &py);
+        colidx[j] = (ic * R + py) * S + px;
+        value[j] = (float)v;
+    }
 }
 
 int32_t oracle_max_threads(void) {

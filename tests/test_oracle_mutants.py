@@ -26,12 +26,44 @@ MUTANTS = {
                             "off[j] = (uint32_t)(((int64_t)c * W + r) * H + s);"),
     "value_sign": ("double v = (double)value[j];", "double v = -(double)value[j];"),
     "output_transposed": ("yp[e * F + f] += prod;", "yp[f * E + e] += prod;"),
+    # packed-word form ([T] Sec. 5.3 / Fig. 4)
+    "fp16_truncates": ("double n = rint(a / ldexp(1.0, e - 10));", "double n = floor(a / ldexp(1.0, e - 10));"),
+    "fp16_ties_away": ("double n = rint(a / ldexp(1.0, e - 10));", "double n = round(a / ldexp(1.0, e - 10));"),
+    "fp16_subnormal_quantum": ("double n = rint(a / ldexp(1.0, -24));", "double n = rint(a / ldexp(1.0, -23));"),
+    "fp16_exponent_bias": ("(uint16_t)((e + 15) << 10)", "(uint16_t)((e + 14) << 10)"),
+    "word_px_py_swapped": ("words[j] = oracle_pack_word(value[j], c, s, r);",
+                           "words[j] = oracle_pack_word(value[j], c, r, s);"),
+    "word_ic_shift": ("((uint32_t)ic << 8)", "((uint32_t)ic << 9)"),
+    "word_decode_col_order": ("colidx[j] = (ic * R + py) * S + px;", "colidx[j] = (ic * S + px) * R + py;"),
 }
+
+
+def _word_pins_pass():
+    """Compact packed-word pins: binary16 values from the format's definition (with ties),
+    numpy's float16 cast, a literal word, and the packed-word oracle against the
+    definitional form on numpy-rounded weights (R != S)."""
+    for v, bits in [(1.0, 0x3C00), (65504.0, 0x7BFF), (2.0 ** -24, 0x0001), (1.0 + 3 * 2.0 ** -11, 0x3C02),
+                    (1.0 + 2.0 ** -11, 0x3C00),
+                    (2047.5, 0x6800), (3 * 2.0 ** -25, 0x0002)]:
+        if oracle.fp16_bits(v) != bits:
+            return False
+    rng = np.random.default_rng(3)
+    vals = (rng.standard_normal(2000) * np.exp2(rng.integers(-26, 15, 2000))).astype(np.float32)
+    if any(oracle.fp16_bits(float(v)) != int(np.float16(v).view(np.uint16)) for v in vals):
+        return False
+    if oracle.pack_word(1.0, 0xAB, 0xC, 0xD) != 0x3C00ABCD:
+        return False
+    d = workloads.make_custom(1, 3, 7, 9, 3, 2, 3, 1, 1, 0.6, 77)
+    r16 = oracle.reference_fp16(d["x"], d["w"], d["mask"], 1, 1)
+    y, mag = oracle.conv_def(d["x"], d["w"].astype(np.float16).astype(np.float32), d["mask"], 1, 1)
+    return bool(np.all(np.abs(r16["y64"] - y) <= 1e-12 * mag + 1e-300))
 
 
 def _pins_pass():
     """A compact run of the pins: torch float64 conv2d on non-square strided/padded shapes,
-    and the stretched-offset gather."""
+    the stretched-offset gather, and the packed-word pins."""
+    if not _word_pins_pass():
+        return False
     for seed, (N, C, H, W, M, R, S, st, p) in enumerate([(2, 3, 9, 7, 4, 3, 2, 2, 1),
                                                           (1, 2, 8, 11, 3, 2, 4, 1, 2),
                                                           (1, 2, 12, 12, 2, 3, 3, 1, 1)]):
