@@ -36,7 +36,8 @@ def log(msg):
 
 def stored_traffic(layer: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
-    missing, for another workload, or taken on different kernel sources."""
+    missing, for another workload, or taken on different kernel sources.  ``layer`` is the
+    workload tag (the layer name, with "_fp16word" for the packed-word form)."""
     from sparse_weight_direct_amd.rocprof_summary import kernel_digest
     path = os.path.join(PROFILE_DIR, f"sparse_direct_fwd_{layer}_traffic.txt")
     if not os.path.exists(path):
@@ -66,6 +67,8 @@ def main():
     ap.add_argument("--miopen", action="store_true", help="also time torch conv2d (MIOpen) as context")
     ap.add_argument("--chain", default=None,
                     help="also time a layer stack from workloads.CHAINS, eager launches vs one graph replay")
+    ap.add_argument("--fp16-word", action="store_true",
+                    help="pack the weights as 32-bit words with an fp16 value (SC_PACK_FP16_WORD)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
@@ -89,11 +92,13 @@ def main():
     N, C, H, W, M, R, S, st, pad, E, F = L.N, L.C, L.H, L.W, L.M, L.R, L.S, L.stride, L.pad, L.E, L.F
     log(f"[bench] layer {layer}: N={N} C={C} {H}x{W} M={M} {R}x{S} s{st} p{pad} -> {E}x{F}")
     dev = torch.device("cuda:0")
-    h = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w"], mask=d["mask"])
+    h = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_FP16_WORD if args.fp16_word else 0)
     info = h.info()
     nnz = info["nnz"]
+    tag = layer + ("_fp16word" if args.fp16_word else "")
     flops = roofline.effective_flops(nnz, N, E, F)
-    alg_bytes = roofline.algorithmic_bytes(N, C, H, W, M, E, F, nnz)
+    alg_bytes = roofline.algorithmic_bytes(N, C, H, W, M, E, F, nnz, info["entry_bytes"])
     set_bytes = 4 * (N * C * H * W + N * M * E * F)
     nsets = max(1, math.ceil(args.rotate_mb * (1 << 20) / set_bytes))
     x0 = torch.from_numpy(d["x"]).to(dev)
@@ -132,11 +137,20 @@ def main():
     flop_roof = min(roofline.HBM_PEAK_GBS * 1e9 * ai, roofline.FP32_VECTOR_PEAK_TFLOPS * 1e12) / 1e12
     log(f"[bench] sparse {ms * 1e3:.2f} us/step (SEM {sem * 1e3:.2f}), {tflops:.2f} TFLOP/s, {achieved_gbs:.0f} GB/s")
 
+    def oracle_csr():
+        """The oracle's CSR of the layer; for the packed-word form, the non-zeros decoded
+        from the oracle's own words (fp16-rounded weights)."""
+        import oracle
+        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+        if args.fp16_word:
+            colidx, value = oracle.csr_from_words(oracle.words_from_csr(colidx, value, C, R, S), R, S)
+        return rowptr, colidx, value
+
     # correctness of the timed buffers: sampled planes against the oracle
     parity = None
     try:
         import oracle
-        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+        rowptr, colidx, value = oracle_csr()
         rng = np.random.default_rng(0)
         planes = sorted(set(int(p) for p in rng.choice(N * M, min(8, N * M), replace=False)))
         y64, mag = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, M, R, S, st, pad, planes)
@@ -203,7 +217,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+        rowptr, colidx, value = oracle_csr()
         threads = oracle.max_threads()
         t = time.perf_counter()
         oracle.conv_csr(d["x"][:1], rowptr, colidx, value, M, R, S, st, pad)
@@ -224,7 +238,7 @@ def main():
                "sample": f"list-form oracle (fp64 accumulate), {reps} run(s) over {n_img} of {N} images, "
                          f"all {M} output channels, {tc:.1f} s"}
 
-    traffic = stored_traffic(layer)
+    traffic = stored_traffic(tag)
     out = {
         "metric": "sparse conv effective TFLOP/s (2*nnz*N*E*F/s) and % of HBM roofline",
         "value": round(tflops, 4),
@@ -240,7 +254,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{layer}: N={N} C={C} H=W={H} M={M} {R}x{S} stride {st} pad {pad}, "
                                f"per-channel density Beta(0.5,b) mean sparsity {round(100 * L.sparsity)}%, "
-                               f"realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)",
+                               f"realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)"
+                               + (", weights as 32-bit words with fp16 values" if args.fp16_word else ""),
                    "N": N, "C": C, "H": H, "W": W, "M": M, "R": R, "S": S, "stride": st, "pad": pad, "nnz": nnz},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved_gbs / roofline.HBM_PEAK_GBS, 4), "traffic": traffic},
@@ -250,7 +265,7 @@ def main():
         "flop_roofline_frac": round(tflops / flop_roof, 4),
         "parity_on_timed_buffers": parity,
         "plan": {k: info[k] for k in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels", "lds_bytes",
-                                      "max_wave_nnz")},
+                                      "max_wave_nnz", "entry_bytes")},
         "rotated_sets": nsets,
     }
     out.update(extra)

@@ -62,6 +62,17 @@ typedef enum {
                                 included (mask ignored).  A forward on such a handle is the
                                 dense direct convolution with the same kernel: the on-GPU
                                 baseline, counterpart of Tuteja et al., Sec. 4 Eq. (5)/(6). */
+#define SC_PACK_FP16_WORD 4u /* store each non-zero in the 32-bit packed word of Tuteja et al.,
+                                Sec. 5.3 and Fig. 4: the weight rounded to fp16 (to nearest,
+                                ties to even) in bits 31-16, the input channel in bits 15-8,
+                                the filter column s (px) in bits 7-4 and the filter row r (py)
+                                in bits 3-0 (sparseconv_export_words returns them).  The kernel
+                                stream then takes 4 bytes per non-zero instead of 8; the fp16
+                                weight is widened to fp32 and accumulated in fp32, so the
+                                result is the convolution with the fp16-rounded weights.
+                                Limits: C <= 256, R <= 16, S <= 16 (SC_EUNSUPPORTED); a finite
+                                weight of magnitude >= 65520 (which rounds to infinity) is
+                                SC_EINVAL. */
 
 typedef struct {
   int32_t format;          /* sc_weights_format */
@@ -80,7 +91,8 @@ typedef struct {
   int32_t M, C, R, S, H, W, stride, pad, E, F;
   int64_t nnz;
   int64_t packed_bytes;  /* (2*nnz + M + 1) * 4: canonical {offset, value} entries + rowptr,
-                            the CSR size of "Escoin", CSR section */
+                            the CSR size of "Escoin", CSR section; (nnz + M + 1) * 4 with
+                            SC_PACK_FP16_WORD (one 32-bit word per non-zero + rowptr) */
   int64_t device_bytes;  /* bytes this handle holds on the device (kernel stream + tables) */
   int32_t tile_pixels;   /* launch plan: extended output positions per workgroup */
   int32_t rows_per_wave; /* launch plan: output-channel slots per wavefront */
@@ -104,6 +116,8 @@ typedef struct {
                             work units, and the forward pass takes the one estimated fastest
                             for its N (small batches and small images use more, smaller
                             units so that every CU has work) */
+  int32_t entry_bytes;   /* bytes per non-zero in the kernel stream: 8 ({LDS offset, fp32
+                            weight}), or 4 ({LDS offset, fp16 weight}) with SC_PACK_FP16_WORD */
 } sc_info;
 
 /*
@@ -112,7 +126,7 @@ typedef struct {
  *   M,C,R,S    output channels, input channels, filter rows, filter columns (all >= 1).
  *   H,W        unpadded input height and width the layer will be applied to (>= 1).
  *   stride>=1, pad>=0; E and F from the formula above must be >= 1.
- *   flags      0, or SC_PACK_HOST_ONLY and/or SC_PACK_ALL_TAPS.
+ *   flags      0, or any of SC_PACK_HOST_ONLY, SC_PACK_ALL_TAPS, SC_PACK_FP16_WORD.
  *   out        receives the new handle (set to NULL on failure).
  * Steps: validate -> CSR (columns sorted within each row, values moved with them) ->
  * stretched offsets -> wavefront schedule balanced by non-zero count -> upload.
@@ -149,11 +163,21 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info);
  * Copy out the canonical packed form (host buffers owned by the caller):
  *   rowptr  M+1 entries; offsets, values  nnz entries each.
  * Canonical order: rows m ascending; within a row, columns c*R*S + r*S + s ascending.
- * offsets[j] = c*H*W + r*W + s of entry j; values[j] its fp32 weight, bit for bit.
+ * offsets[j] = c*H*W + r*W + s of entry j; values[j] its fp32 weight, bit for bit (with
+ * SC_PACK_FP16_WORD: the fp16-rounded weight the kernel uses, widened to fp32 exactly).
  * Any of the three pointers may be NULL to skip it.  SC_EINVAL on a NULL handle.
  */
 sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t* offsets,
                                    float* values);
+
+/*
+ * Copy out the 32-bit packed words of a handle packed with SC_PACK_FP16_WORD (Tuteja et
+ * al., Sec. 5.3 and Fig. 4), in the canonical order above (host buffers owned by the
+ * caller): rowptr  M+1 entries (the per-output-channel start/end array of that section);
+ * words  nnz entries, words[j] = fp16(v) << 16 | c << 8 | s << 4 | r.  Either pointer may
+ * be NULL.  SC_EINVAL on a NULL handle or one packed without SC_PACK_FP16_WORD.
+ */
+sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t* words);
 
 /* Free the handle and its device buffers.  NULL is a no-op.  Must not race a forward
  * still running on the device that reads this handle (synchronise the stream first). */

@@ -7,7 +7,7 @@ import fails, and the forward pass needs a ROCm device.
 
 The functions keep the C names:
     sparseconv_pack, sparseconv_forward, sparseconv_query, sparseconv_export_packed,
-    sparseconv_destroy, sparseconv_last_error
+    sparseconv_export_words, sparseconv_destroy, sparseconv_last_error
 plus ``Handle`` (owns a packed filter bank and destroys it when collected).  The dense
 direct baseline is a Handle packed with SC_PACK_ALL_TAPS (every filter tap stored).
 """
@@ -36,11 +36,12 @@ SC_OK, SC_EINVAL, SC_ESHAPE, SC_ENOMEM, SC_EDEVICE, SC_EUNSUPPORTED = range(6)
 SC_WEIGHTS_DENSE, SC_WEIGHTS_CSR = 0, 1
 SC_PACK_HOST_ONLY = 1
 SC_PACK_ALL_TAPS = 2
+SC_PACK_FP16_WORD = 4
 _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: "SC_EDEVICE",
                  5: "SC_EUNSUPPORTED"}
 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_query", "sparseconv_export_packed",
-            "sparseconv_destroy", "sparseconv_last_error")
+            "sparseconv_export_words", "sparseconv_destroy", "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -54,7 +55,7 @@ class sc_info(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
                                                "pipeline_depth", "step_balance_permille",
-                                               "split_pieces", "plan_variants")]
+                                               "split_pieces", "plan_variants", "entry_bytes")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -69,6 +70,8 @@ _lib.sparseconv_query.restype = _i32
 _lib.sparseconv_query.argtypes = [_vp, ctypes.POINTER(sc_info)]
 _lib.sparseconv_export_packed.restype = _i32
 _lib.sparseconv_export_packed.argtypes = [_vp, _vp, _vp, _vp]
+_lib.sparseconv_export_words.restype = _i32
+_lib.sparseconv_export_words.argtypes = [_vp, _vp, _vp]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -156,6 +159,16 @@ def sparseconv_export_packed(handle: int):
     return rowptr, off, val
 
 
+def sparseconv_export_words(handle: int):
+    """(rowptr, words): the 32-bit packed words of an SC_PACK_FP16_WORD handle."""
+    info = sparseconv_query(handle)
+    rowptr = np.zeros(info["M"] + 1, np.int32)
+    words = np.zeros(info["nnz"], np.uint32)
+    _check(_lib.sparseconv_export_words(handle, rowptr.ctypes.data_as(_vp), words.ctypes.data_as(_vp)),
+           "sparseconv_export_words")
+    return rowptr, words
+
+
 def sparseconv_destroy(handle) -> None:
     _lib.sparseconv_destroy(handle)
 
@@ -184,6 +197,9 @@ class Handle:
 
     def export(self):
         return sparseconv_export_packed(self.ptr)
+
+    def export_words(self):
+        return sparseconv_export_words(self.ptr)
 
     def forward(self, x, out=None, stream=None):
         """x: (N, C, H, W) float32 CUDA tensor; returns out (N, M, E, F)."""

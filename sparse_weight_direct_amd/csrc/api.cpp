@@ -2,13 +2,16 @@
 //
 // sparseconv_pack: validate -> CSR rows ("Escoin", CSR section; columns sorted within a row,
 // values moved with them) -> stretched u32 input offsets c*H*W + r*W + s ("Escoin", weight
-// stretching) kept as the canonical host copy -> wavefront schedule (pack.cpp) -> kernel
-// stream of {LDS-encoded offset, value} per (workgroup group, wavefront, channel chunk,
-// slot) -> one device allocation.  sparseconv_forward validates against the handle and
+// stretching) kept as the canonical host copy -> (with SC_PACK_FP16_WORD) the 32-bit packed
+// words of Tuteja et al., Sec. 5.3 / Fig. 4 and fp16-rounded values -> wavefront schedule
+// (pack.cpp) -> kernel stream of {LDS-encoded offset, value} (8 bytes) or {LDS-encoded
+// offset, fp16 value} (4 bytes) per (workgroup group, wavefront, channel chunk, slot) ->
+// one device allocation.  sparseconv_forward validates against the handle and
 // launches asynchronously on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -61,9 +64,11 @@ struct sc_handle {
   uint64_t magic;
   sc::Geom g;
   int64_t nnz;
+  bool h16;                      // packed with SC_PACK_FP16_WORD
   std::vector<int32_t> rowptr;   // canonical CSR row pointers
   std::vector<uint32_t> off;     // canonical stretched offsets
-  std::vector<float> val;        // canonical values
+  std::vector<float> val;        // canonical values (fp16-rounded when h16)
+  std::vector<uint32_t> words;   // h16: the 32-bit packed words, canonical order
   std::vector<Variant> var;
   int device;
   bool host_only;
@@ -74,6 +79,46 @@ struct sc_handle {
 namespace {
 
 bool valid_handle(const sc_handle* h) { return h && h->magic == kMagic; }
+
+// IEEE 754 binary16 bits of an fp32 value, rounded to nearest with ties to even, by integer
+// operations on the fp32 encoding: rebias the exponent (normal halves) or shift the full
+// significand to the 2^-24 grid (subnormal halves), then round the dropped bits.  Values at
+// or above 65520 in magnitude become infinity; NaN stays a quiet NaN.
+uint16_t half_bits(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax > 0x7f800000u) return (uint16_t)(sign | 0x7e00u | ((ax >> 13) & 0x3ffu));
+  if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);  // >= 65520 (and infinity)
+  auto rne = [](uint32_t v, int sh) {
+    const uint32_t q = v >> sh, rem = v & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+  };
+  if (ax >= 0x38800000u)  // >= 2^-14: normal half; a carry into the exponent is correct
+    return (uint16_t)(sign | rne(ax - 0x38000000u, 13));
+  if (ax <= 0x33000000u) return (uint16_t)sign;  // <= 2^-25: rounds to zero (2^-25 is a tie)
+  const uint32_t e = ax >> 23, m = (ax & 0x7fffffu) | 0x800000u;
+  return (uint16_t)(sign | rne(m, (int)(126 - e)));  // value / 2^-24 = m * 2^(e - 126)
+}
+
+float half_value(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t ex = (h >> 10) & 31u, man = h & 1023u;
+  uint32_t x;
+  if (ex == 31) {
+    x = sign | 0x7f800000u | (man << 13);
+  } else if (ex != 0) {
+    x = sign | ((ex + 112u) << 23) | (man << 13);
+  } else {
+    float v = std::ldexp((float)man, -24);  // exact
+    std::memcpy(&x, &v, 4);
+    x |= sign;
+  }
+  float f;
+  std::memcpy(&f, &x, 4);
+  return f;
+}
 
 // CSR rows from the caller's weights, columns ascending within each row.
 sc_status build_csr(const sc_weights* w, int M, long long crs, bool all_taps, std::vector<int32_t>& rowptr,
@@ -152,13 +197,16 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
   if (!out) return fail(SC_EINVAL, "out is NULL");
   *out = nullptr;
   if (!w) return fail(SC_EINVAL, "weights descriptor is NULL");
-  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS)) return fail(SC_EINVAL, "unknown pack flag");
+  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS | SC_PACK_FP16_WORD)) return fail(SC_EINVAL, "unknown pack flag");
+  const bool h16 = (flags & SC_PACK_FP16_WORD) != 0;
   sc::Geom g;
   if (!sc::make_geom(M, C, R, S, H, W, stride, pad, &g))
     return fail(SC_ESHAPE, "invalid layer geometry (dims >= 1, stride >= 1, pad >= 0, output >= 1x1)");
   const long long crs = (long long)C * R * S;
   if ((long long)M * crs >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "M*C*R*S >= 2^31");
   if ((long long)C * H * W >= (1LL << 32)) return fail(SC_EUNSUPPORTED, "C*H*W >= 2^32: offsets do not fit u32");
+  if (h16 && (C > 256 || R > 16 || S > 16))
+    return fail(SC_EUNSUPPORTED, "SC_PACK_FP16_WORD: the 32-bit word holds C <= 256 and R, S <= 16");
   if (fail_alloc_hook()) return fail(SC_ENOMEM, "allocation failure (injected by SPARSECONV_TEST_FAIL_ALLOC)");
   sc_handle* h = nullptr;
   try {
@@ -167,6 +215,18 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     sc_status s = build_csr(w, M, crs, (flags & SC_PACK_ALL_TAPS) != 0, rowptr, col, val);
     if (s != SC_OK) return s;
     const long long nnz = (long long)col.size();
+    std::vector<uint32_t> words;
+    if (h16) {  // the packed word of each non-zero; the kernel uses the rounded weight
+      words.resize(nnz);
+      for (long long j = 0; j < nnz; j++) {
+        const uint16_t hb = half_bits(val[j]);
+        if ((hb & 0x7fffu) == 0x7c00u && !std::isinf(val[j]))
+          return fail(SC_EINVAL, "SC_PACK_FP16_WORD: weight " + std::to_string(val[j]) + " overflows fp16");
+        const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
+        words[j] = ((uint32_t)hb << 16) | ((uint32_t)c << 8) | ((uint32_t)sx << 4) | (uint32_t)r;
+        val[j] = half_value(hb);
+      }
+    }
     // plan variants: the default, then caps on positions per lane and rows per wavefront
     // (none when SPARSECONV_PLAN forces a plan)
     std::vector<Variant> vars;
@@ -192,6 +252,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->magic = kMagic;
     h->g = g;
     h->nnz = nnz;
+    h->h16 = h16;
+    h->words = std::move(words);
     h->host_only = (flags & SC_PACK_HOST_ONLY) != 0;
     h->dmem = nullptr;
     h->dbytes = 0;
@@ -204,6 +266,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     h->rowptr = rowptr;
 
     for (Variant& v : vars) {
+      v.p.h16 = h16 ? 1 : 0;
       const sc::Plan& p = v.p;
       const sc::Sched& sched = v.sched;
       v.max_wave_nnz = sched.max_wave_nnz;
@@ -211,7 +274,10 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       // Kernel stream: per (group, consumer wavefront), one block per chunk holding header
       // entries {count of slot o, 0} (OCW of them, rounded up to even) followed by the slots'
       // non-zeros {enc, value} in slot order; each block starts at a multiple of 64 entries
-      // (the kernel loads whole groups of 64), with zero entries in the gaps.
+      // (the kernel loads whole groups of 64), with zero entries in the gaps.  In the 4-byte
+      // form an entry is one word: a header holds the count, a non-zero (enc << 16) | fp16
+      // bits of its weight.
+      const int ew = h16 ? 1 : 2;  // words per entry
       // bstart[(group*NC + consumer)*(nch+1) + k] is the first entry of block k and
       // bstart[.. + nch] the end of the last one.
       const int waves = p.G * (p.NW - 1);  // consumer wavefronts
@@ -232,7 +298,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       }
       std::vector<uint32_t>& ent = v.ent;
       std::vector<int32_t>& bstart = v.bstart;
-      ent.assign(2 * std::max<size_t>(n_ent, 1), 0);
+      ent.assign(ew * std::max<size_t>(n_ent, 1), 0);
       bstart.assign((size_t)waves * (p.nch + 1), 0);
       size_t pos = 0;
       for (int wv = 0; wv < waves; wv++) {
@@ -253,15 +319,23 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
                 const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
                 const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
                                                 (r / stride) * g.Pp + sx / stride);
-                uint32_t vbits;
-                std::memcpy(&vbits, &val[j], 4);
-                ent[2 * pos] = enc;
-                ent[2 * pos + 1] = vbits;
+                if (h16) {
+                  if (enc > 0xffffu) {
+                    sparseconv_destroy(h);
+                    return fail(SC_EUNSUPPORTED, "SC_PACK_FP16_WORD: LDS offset does not fit 16 bits");
+                  }
+                  ent[pos] = (enc << 16) | (h->words[j] >> 16);
+                } else {
+                  uint32_t vbits;
+                  std::memcpy(&vbits, &val[j], 4);
+                  ent[2 * pos] = enc;
+                  ent[2 * pos + 1] = vbits;
+                }
                 pos++;
               }
               cnt = e - b;
             }
-            ent[2 * (hdr + o)] = (uint32_t)cnt;
+            ent[ew * (hdr + o)] = (uint32_t)cnt;
           }
         }
         bstart[(size_t)wv * (p.nch + 1) + p.nch] = (int32_t)pos;
@@ -333,7 +407,8 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->H = h->g.H; info->W = h->g.W; info->stride = h->g.st; info->pad = h->g.pad;
   info->E = h->g.E; info->F = h->g.F;
   info->nnz = h->nnz;
-  info->packed_bytes = (2 * h->nnz + h->g.M + 1) * 4;
+  info->packed_bytes = ((h->h16 ? 1 : 2) * h->nnz + h->g.M + 1) * 4;
+  info->entry_bytes = h->h16 ? 4 : 8;
   info->device_bytes = (int64_t)h->dbytes;
   const Variant& v = h->var[0];  // the default plan
   info->tile_pixels = 64 * v.p.K;
@@ -356,6 +431,15 @@ sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t
   if (rowptr) std::memcpy(rowptr, h->rowptr.data(), h->rowptr.size() * 4);
   if (offsets && h->nnz) std::memcpy(offsets, h->off.data(), h->off.size() * 4);
   if (values && h->nnz) std::memcpy(values, h->val.data(), h->val.size() * 4);
+  return SC_OK;
+}
+
+sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t* words) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!h->h16) return fail(SC_EINVAL, "handle was not packed with SC_PACK_FP16_WORD");
+  if (rowptr) std::memcpy(rowptr, h->rowptr.data(), h->rowptr.size() * 4);
+  if (words && h->nnz) std::memcpy(words, h->words.data(), h->words.size() * 4);
   return SC_OK;
 }
 

@@ -18,13 +18,15 @@
 //              per-lane source offsets serve every channel (only a scalar offset of c*H*W
 //              words changes); padding words get an out-of-range offset, which the load
 //              turns into 0;
-//   consumers - the other wavefronts each own OCW output-channel slots.  A consumer copies
-//              its own block of {enc, value} non-zeros for a step into its private part of
-//              the step's slot (D-1 steps ahead, counted vmcnt waits), waits for the step's
-//              ready counter, and walks its slots: the block is read 64 entries at a time
-//              (one per lane) and each entry is broadcast with v_readlane.  Per non-zero
-//              each lane does one address add, K LDS reads 64 words apart and K fp32 FMAs.
-//              It then releases the slot (done counter);
+//   consumers - the other wavefronts each own OCW output-channel slots.  A consumer waits
+//              for the step's ready counter and walks its slots over its own block of
+//              non-zeros for the step, which it loads from global memory 64 entries at a
+//              time (one per lane, one group ahead of the walk) and broadcasts entry by
+//              entry with v_readlane.  Per non-zero each lane does one address add, K LDS
+//              reads 64 words apart and K fp32 FMAs.  It then releases the slot (done
+//              counter).  An entry is 8 bytes {LDS offset, fp32 weight}, or 4 bytes
+//              {LDS offset, fp16 weight} for filter banks packed in the 32-bit word form
+//              (the fp16 weight is widened to fp32 before the FMAs);
 //   store    - after a unit's last chunk, each consumer stores its valid positions with
 //              coalesced NCHW stores; slots of channels without non-zeros store exact zeros.
 //              A row split over several consumers (pieces) is summed first: later pieces
@@ -281,6 +283,30 @@ __device__ __forceinline__ void output_bases(const KArgs& a, int I0, int lane, i
   }
 }
 
+// Entry formats of the kernel stream.  A group of 64 entries is held one per lane; header
+// entries hold a slot's count in their first (or only) word.
+struct EntF32 {  // 8 bytes: {LDS word offset, fp32 weight bits}
+  using T = uint2;
+  static __device__ __forceinline__ T zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ int count(T g, int o) { return __builtin_amdgcn_readlane((int)g.x, o); }
+  static __device__ __forceinline__ void get(T g, int l, uint32_t& off, float& w) {
+    off = (uint32_t)__builtin_amdgcn_readlane((int)g.x, l);
+    w = __int_as_float(__builtin_amdgcn_readlane((int)g.y, l));
+  }
+};
+// 4 bytes: fp16 weight bits in bits 15..0, LDS word offset in bits 31..16 (one v_readlane
+// per entry; the conversion reads the low half directly)
+struct EntH16 {
+  using T = uint32_t;
+  static __device__ __forceinline__ T zero() { return 0u; }
+  static __device__ __forceinline__ int count(T g, int o) { return __builtin_amdgcn_readlane((int)g, o); }
+  static __device__ __forceinline__ void get(T g, int l, uint32_t& off, float& w) {
+    const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)g, l);
+    off = e >> 16;
+    w = (float)__builtin_bit_cast(_Float16, (unsigned short)(e & 0xffffu));
+  }
+};
+
 // One non-zero: K FMAs of the wave-uniform weight into the lane's K positions.
 template <int K>
 __device__ __forceinline__ void fma_entry(float (&acc)[K], const float* lane_lds, uint32_t off, float w) {
@@ -294,12 +320,12 @@ __device__ __forceinline__ void fma_entry(float (&acc)[K], const float* lane_lds
 // access in the loop).  The empty asm after the reads keeps the scheduler from
 // interleaving each read with its FMAs (under register pressure it otherwise waits on
 // every read); a pair keeps 2*K LDS reads in flight.
-template <int K>
-__device__ __forceinline__ void pair(float (&acc)[K], const float* lane_lds, const uint2 grp, int l) {
-  const uint32_t o0 = (uint32_t)__builtin_amdgcn_readlane((int)grp.x, l);
-  const uint32_t o1 = (uint32_t)__builtin_amdgcn_readlane((int)grp.x, l + 1);
-  const float w0 = __int_as_float(__builtin_amdgcn_readlane((int)grp.y, l));
-  const float w1 = __int_as_float(__builtin_amdgcn_readlane((int)grp.y, l + 1));
+template <int K, typename EF>
+__device__ __forceinline__ void pair(float (&acc)[K], const float* lane_lds, const typename EF::T grp, int l) {
+  uint32_t o0, o1;
+  float w0, w1;
+  EF::get(grp, l, o0, w0);
+  EF::get(grp, l + 1, o1, w1);
   const float* p0 = lane_lds + o0;
   const float* p1 = lane_lds + o1;
   float v0[K], v1[K];
@@ -315,48 +341,53 @@ __device__ __forceinline__ void pair(float (&acc)[K], const float* lane_lds, con
 }
 
 // n consecutive non-zeros starting at lane l of a group: pairs, then a single one if n is odd.
-template <int K>
-__device__ __forceinline__ void run_entries(float (&acc)[K], const float* lane_lds, const uint2 grp, int l, int n) {
+template <int K, typename EF>
+__device__ __forceinline__ void run_entries(float (&acc)[K], const float* lane_lds, const typename EF::T grp, int l,
+                                            int n) {
   const int lend = l + (n & ~1);
   if (n & 2) {
-    pair<K>(acc, lane_lds, grp, l);
+    pair<K, EF>(acc, lane_lds, grp, l);
     l += 2;
   }
   for (; l < lend; l += 4) {
-    pair<K>(acc, lane_lds, grp, l);
-    pair<K>(acc, lane_lds, grp, l + 2);
+    pair<K, EF>(acc, lane_lds, grp, l);
+    pair<K, EF>(acc, lane_lds, grp, l + 2);
   }
-  if (n & 1)
-    fma_entry<K>(acc, lane_lds, (uint32_t)__builtin_amdgcn_readlane((int)grp.x, lend),
-                 __int_as_float(__builtin_amdgcn_readlane((int)grp.y, lend)));
+  if (n & 1) {
+    uint32_t o;
+    float w;
+    EF::get(grp, lend, o, w);
+    fma_entry<K>(acc, lane_lds, o, w);
+  }
 }
 
 // One step: the wavefront's slots and their non-zeros of this chunk, from its block of the
-// stream: header entries {count of slot o, 0} (OCW of them, rounded up to an even number),
-// then the slots' non-zeros {enc, value} in slot order, walked in pairs (and a single last
+// stream: header entries holding the count of slot o (OCW of them, rounded up to an even
+// number), then the slots' non-zeros in slot order, walked in pairs (and a single last
 // one for an odd run) that never straddle a group of 64 (lane i holds entry i of the
 // group).  Blocks start at multiples of 64 entries, so a block is a whole number of groups;
 // the groups arrive in registers from the caller (next_group), which loads them one group
 // ahead straight from the stream in global memory.
+template <typename EF>
 struct Walk {
-  uint2 head;  // the block's first group (the header in lanes 0..OCW-1)
-  uint2 cur;   // the current group of 64 entries
-  int r;       // next entry's lane within the current group
+  typename EF::T head;  // the block's first group (the header in lanes 0..OCW-1)
+  typename EF::T cur;   // the current group of 64 entries
+  int r;                // next entry's lane within the current group
 };
 
-template <int K, int OCW, typename NextGroup>
-__device__ __forceinline__ void walk_slots(Walk& w, float (&acc)[OCW][K], const float* lane_lds,
+template <int K, int OCW, typename EF, typename NextGroup>
+__device__ __forceinline__ void walk_slots(Walk<EF>& w, float (&acc)[OCW][K], const float* lane_lds,
                                            NextGroup&& next_group) {
 #pragma unroll
   for (int o = 0; o < OCW; o++) {
-    int n = __builtin_amdgcn_readlane((int)w.head.x, o);
+    int n = EF::count(w.head, o);
     while (n > 0) {
       if (w.r == 64) {
         w.cur = next_group();
         w.r = 0;
       }
       const int take = min(n, 64 - w.r);
-      run_entries<K>(acc[o], lane_lds, w.cur, w.r, take);
+      run_entries<K, EF>(acc[o], lane_lds, w.cur, w.r, take);
       w.r += take;
       n -= take;
     }
@@ -432,8 +463,8 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
   }
 }
 
-template <int K, int OCW, int NW>
-__device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, const uint2* __restrict__ ent,
+template <int K, int OCW, int NW, typename EF>
+__device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, const typename EF::T* __restrict__ ent,
                                          const int* bst, const int* __restrict__ slot_row,
                                          const int* __restrict__ slot_comb, StepIt it, int S, const uint32_t* ready,
                                          uint32_t* done, uint32_t* pfull, uint32_t* pcons, float* pbuf, float* lds,
@@ -446,7 +477,8 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
   int pg = 0;      // its index within that step's block
   int pstep = 0;   // its step number in this workgroup's stream
   auto block = [&](const StepIt& p) -> const int* { return bst + (p.g * NC + c) * (a.nch + 1) + p.k; };
-  auto load_group = [&]() -> uint2 { return pstep < S ? ent[block(pf)[0] + 64 * pg + lane] : make_uint2(0u, 0u); };
+  using ET = typename EF::T;
+  auto load_group = [&]() -> ET { return pstep < S ? ent[block(pf)[0] + 64 * pg + lane] : EF::zero(); };
   auto advance = [&]() {
     const int* bw = block(pf);
     if (64 * (pg + 1) < bw[1] - bw[0]) {
@@ -457,15 +489,15 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
       pstep++;
     }
   };
-  uint2 nxt = load_group();  // group 0 of step 0
-  auto next_group = [&]() -> uint2 {
+  ET nxt = load_group();  // group 0 of step 0
+  auto next_group = [&]() -> ET {
     wait_vmcnt(0);
-    const uint2 g = nxt;
+    const ET g = nxt;
     advance();
     nxt = load_group();
     return g;
   };
-  uint2 first = next_group();  // step 0's first group; nxt holds the one after it
+  ET first = next_group();  // step 0's first group; nxt holds the one after it
   float acc[OCW][K];
 #pragma unroll
   for (int o = 0; o < OCW; o++)
@@ -476,11 +508,11 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
     const int buf = s % a.D;
     lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
     const float* slot = lds + buf * a.slot_words;
-    Walk w;
+    Walk<EF> w;
     w.head = first;
     w.cur = first;
     w.r = (OCW + 1) & ~1;
-    walk_slots<K, OCW>(w, acc, slot + lane, next_group);
+    walk_slots<K, OCW, EF>(w, acc, slot + lane, next_group);
     // every group of this step's block has been walked: nxt is the next step's first group
     if (s + 1 < S) first = next_group();
     // release the slot's input part (the walk's LDS reads are complete before the add);
@@ -555,10 +587,10 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
 
 // Pointers are separate restrict-qualified arguments so the compiler knows the streams
 // are read-only.
-template <int K, int OCW, int NW>
+template <int K, int OCW, int NW, typename EF>
 __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
     const KArgs a, const float* __restrict__ x, float* __restrict__ y,
-    const uint2* __restrict__ ent, const int* __restrict__ bstart,
+    const typename EF::T* __restrict__ ent, const int* __restrict__ bstart,
     const int* __restrict__ slot_row, const int* __restrict__ slot_comb) {
   constexpr int T = NW * 64;
   constexpr int NC = NW - 1;
@@ -589,11 +621,12 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   if (wave == NC)
     producer<K, NW>(a, x, it, S, ready, done, lds, lane);
   else
-    consumer<K, OCW, NW>(a, y, ent, bst, slot_row, slot_comb, it, S, ready, done, pfull, pcons, pbuf, lds, wave,
+    consumer<K, OCW, NW, EF>(a, y, ent, bst, slot_row, slot_comb, it, S, ready, done, pfull, pcons, pbuf, lds, wave,
                          lane);
 }
 
-using SparseFn = void (*)(KArgs, const float*, float*, const uint2*, const int*, const int*, const int*);
+template <typename EF>
+using SparseFn = void (*)(KArgs, const float*, float*, const typename EF::T*, const int*, const int*, const int*);
 
 #define SC_FOR_EACH_KO(X, NW) \
   X(1, 1, NW) X(2, 1, NW) X(4, 1, NW) X(6, 1, NW) X(7, 1, NW) X(8, 1, NW) X(12, 1, NW) X(16, 1, NW) \
@@ -602,11 +635,17 @@ using SparseFn = void (*)(KArgs, const float*, float*, const uint2*, const int*,
   X(1, 5, NW) X(2, 5, NW) X(4, 5, NW) X(6, 5, NW) X(7, 5, NW) X(8, 5, NW) X(12, 5, NW) \
   X(1, 9, NW) X(2, 9, NW) X(4, 9, NW) X(6, 9, NW) X(7, 9, NW)
 
-static SparseFn pick_sparse(const Plan& p) {
-#define SC_CASE(KK, OO, WW) if (p.K == KK && p.OCW == OO && p.NW == WW) return sparse_direct_fwd<KK, OO, WW>;
+template <typename EF>
+static SparseFn<EF> pick_sparse(const Plan& p) {
+#define SC_CASE(KK, OO, WW) if (p.K == KK && p.OCW == OO && p.NW == WW) return sparse_direct_fwd<KK, OO, WW, EF>;
   SC_FOR_EACH_KO(SC_CASE, 16)
 #undef SC_CASE
   return nullptr;
+}
+
+static const void* kernel_of(const Plan& p) {
+  return p.h16 ? reinterpret_cast<const void*>(pick_sparse<EntH16>(p))
+               : reinterpret_cast<const void*>(pick_sparse<EntF32>(p));
 }
 
 static hipError_t allow_lds(const void* fn, int bytes) {
@@ -617,7 +656,7 @@ static hipError_t allow_lds(const void* fn, int bytes) {
 int occupancy(const Plan& p, int* cus, int* per_cu) {
   *cus = 0;
   *per_cu = 0;
-  const void* fn = reinterpret_cast<const void*>(pick_sparse(p));
+  const void* fn = kernel_of(p);
   if (!fn) return (int)hipErrorInvalidDeviceFunction;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -628,14 +667,19 @@ int occupancy(const Plan& p, int* cus, int* per_cu) {
   return (int)e;
 }
 
-int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks) {
-  SparseFn fn = pick_sparse(p);
+template <typename EF>
+static int launch_as(const Plan& p, const KArgs& a, void* stream, int nblocks) {
+  SparseFn<EF> fn = pick_sparse<EF>(p);
   if (!fn) return (int)hipErrorInvalidDeviceFunction;
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), p.lds_bytes);
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(fn, dim3(nblocks), dim3(p.NW * 64), p.lds_bytes, reinterpret_cast<hipStream_t>(stream), a,
-                     a.x, a.y, reinterpret_cast<const uint2*>(a.ent), a.seg, a.slot_row, a.slot_comb);
+                     a.x, a.y, reinterpret_cast<const typename EF::T*>(a.ent), a.seg, a.slot_row, a.slot_comb);
   return (int)hipGetLastError();
+}
+
+int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks) {
+  return p.h16 ? launch_as<EntH16>(p, a, stream, nblocks) : launch_as<EntF32>(p, a, stream, nblocks);
 }
 
 }  // namespace sc

@@ -27,7 +27,8 @@
 //  * Each stored non-zero (c, r, s, v) is re-encoded at pack time as
 //        enc = (c % Cc)*CHS + ((r % st)*st + (s % st))*PL + (r / st)*Pp + (s / st)
 //    so lane l, position b reads LDS word enc + l + 64*b: one address add, K LDS reads 64
-//    words apart and K FMAs per non-zero.
+//    words apart and K FMAs per non-zero.  enc < slot_words < 2^16, so it also fits the
+//    16-bit field of the 4-byte entry form.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -64,6 +65,8 @@ struct Plan {
   int span_images; // most images one tile's staged range can touch
   int step_permille;  // 1000 * sum over chunks of the busiest wavefront's entries / mean
   int nbuf;        // LDS partial-sum buffers per workgroup (pieces of split rows)
+  int h16;         // entry format: 0 {LDS offset, fp32 weight} (8 bytes), 1 fp16 weight in
+                   // bits 15..0 and the LDS offset in bits 31..16 (4 bytes)
 };
 
 // Row schedule.  A row longer than a consumer's fair share of a group's non-zeros is split
@@ -95,7 +98,7 @@ inline void piece_range(int b, int e, int p, int P, int* pb, int* pe) {
 struct KArgs {
   const float* x;
   float* y;
-  const uint32_t* ent;    // sparse: pairs {enc, value bits}
+  const uint32_t* ent;    // sparse: entries {enc, value bits}, or one word each (Plan::h16)
   const int32_t* seg;     // sparse: [(group*NC + consumer)*(nch+1) + k] -> first entry of block k
   const int* slot_row;    // sparse: [group][consumer][slot] -> Sched::slot_row
   const int* slot_comb;   // sparse: [group][consumer][slot] -> Sched::slot_comb

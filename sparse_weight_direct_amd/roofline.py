@@ -45,9 +45,10 @@ def effective_flops(nnz: int, N: int, E: int, F: int) -> float:
     return 2.0 * nnz * N * E * F
 
 
-def algorithmic_bytes(N, C, H, W, M, E, F, nnz) -> int:
-    """Input once + output once + packed filter bank ((2*nnz + M + 1) * 4) once."""
-    return 4 * N * C * H * W + 4 * N * M * E * F + 4 * (2 * nnz + M + 1)
+def algorithmic_bytes(N, C, H, W, M, E, F, nnz, entry_bytes=8) -> int:
+    """Input once + output once + packed filter bank once: (2*nnz + M + 1) * 4 bytes for
+    {offset, fp32 value} entries, (nnz + M + 1) * 4 for 32-bit packed words (entry_bytes 4)."""
+    return 4 * N * C * H * W + 4 * N * M * E * F + entry_bytes * nnz + 4 * (M + 1)
 
 
 def dense_flops(N, C, M, E, F, R, S) -> float:
