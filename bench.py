@@ -69,6 +69,8 @@ def main():
                     help="also time a layer stack from workloads.CHAINS, eager launches vs one graph replay")
     ap.add_argument("--fp16-word", action="store_true",
                     help="pack the weights as 32-bit words with an fp16 value (SC_PACK_FP16_WORD)")
+    ap.add_argument("--escoin", action="store_true",
+                    help="time the second mapping (SC_PACK_ESCOIN_MAP: pad_in + one output channel per workgroup)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
@@ -93,10 +95,12 @@ def main():
     log(f"[bench] layer {layer}: N={N} C={C} {H}x{W} M={M} {R}x{S} s{st} p{pad} -> {E}x{F}")
     dev = torch.device("cuda:0")
     h = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w"], mask=d["mask"],
-                  flags=sc.SC_PACK_FP16_WORD if args.fp16_word else 0)
+                  flags=(sc.SC_PACK_FP16_WORD if args.fp16_word else 0) | (sc.SC_PACK_ESCOIN_MAP if args.escoin else 0))
     info = h.info()
     nnz = info["nnz"]
-    tag = layer + ("_fp16word" if args.fp16_word else "")
+    tag = layer + ("_fp16word" if args.fp16_word else "") + ("_escoin" if args.escoin else "")
+    ws_bytes = h.workspace_size(N)
+    ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=dev) if ws_bytes else None
     flops = roofline.effective_flops(nnz, N, E, F)
     alg_bytes = roofline.algorithmic_bytes(N, C, H, W, M, E, F, nnz, info["entry_bytes"])
     set_bytes = 4 * (N * C * H * W + N * M * E * F)
@@ -127,7 +131,7 @@ def main():
         return mean, sem
 
     def sparse_step(i):
-        h.forward(xs[i], ys[i], stream=stream)
+        h.forward(xs[i], ys[i], stream=stream, workspace=ws)
 
     log(f"[bench] sparse: warmup {args.warmup}, timed {args.steps}")
     ms, sem = run(sparse_step, args.steps, args.warmup)
@@ -255,7 +259,8 @@ def main():
         "config": {"workload": f"{layer}: N={N} C={C} H=W={H} M={M} {R}x{S} stride {st} pad {pad}, "
                                f"per-channel density Beta(0.5,b) mean sparsity {round(100 * L.sparsity)}%, "
                                f"realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)"
-                               + (", weights as 32-bit words with fp16 values" if args.fp16_word else ""),
+                               + (", weights as 32-bit words with fp16 values" if args.fp16_word else "")
+                               + (", Escoin mapping (pad_in + one output channel per workgroup)" if args.escoin else ""),
                    "N": N, "C": C, "H": H, "W": W, "M": M, "R": R, "S": S, "stride": st, "pad": pad, "nnz": nnz},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved_gbs / roofline.HBM_PEAK_GBS, 4), "traffic": traffic},
@@ -265,7 +270,7 @@ def main():
         "flop_roofline_frac": round(tflops / flop_roof, 4),
         "parity_on_timed_buffers": parity,
         "plan": {k: info[k] for k in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels", "lds_bytes",
-                                      "max_wave_nnz", "entry_bytes")},
+                                      "max_wave_nnz", "entry_bytes", "mapping")},
         "rotated_sets": nsets,
     }
     out.update(extra)

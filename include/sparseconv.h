@@ -73,6 +73,19 @@ typedef enum {
                                 Limits: C <= 256, R <= 16, S <= 16 (SC_EUNSUPPORTED); a finite
                                 weight of magnitude >= 65520 (which rounds to infinity) is
                                 SC_EINVAL. */
+#define SC_PACK_ESCOIN_MAP 8u /* second mapping, for comparison: the dataflow of "Escoin:
+                                Efficient Sparse Convolutional Neural Network Inference on
+                                GPUs" (dataflow and data-placement sections).  A pad_in
+                                kernel writes the zero-padded input to a caller-provided
+                                workspace; then one workgroup per output channel (and tile of
+                                output positions and image) keeps its CSR row, stretched
+                                against the padded pitch ((c*(H+2pad) + r)*(W+2pad) + s), in
+                                LDS and reads the padded input through the caches, one output
+                                position per thread at a time.  Same result bar as the default
+                                mapping.  Such a handle runs only through
+                                sparseconv_forward_workspace.  Not combinable with
+                                SC_PACK_FP16_WORD (SC_EINVAL).  Limit: C*(H+2pad)*(W+2pad) <
+                                2^30 (SC_EUNSUPPORTED). */
 
 typedef struct {
   int32_t format;          /* sc_weights_format */
@@ -118,6 +131,9 @@ typedef struct {
                             units so that every CU has work) */
   int32_t entry_bytes;   /* bytes per non-zero in the kernel stream: 8 ({LDS offset, fp32
                             weight}), or 4 ({LDS offset, fp16 weight}) with SC_PACK_FP16_WORD */
+  int32_t mapping;       /* 0: LDS-tile kernel (the plan fields above); 1: SC_PACK_ESCOIN_MAP
+                            (tile_pixels = output positions per workgroup, lds_bytes = its
+                            row buffer, max_wave_nnz = the longest row) */
 } sc_info;
 
 /*
@@ -126,7 +142,8 @@ typedef struct {
  *   M,C,R,S    output channels, input channels, filter rows, filter columns (all >= 1).
  *   H,W        unpadded input height and width the layer will be applied to (>= 1).
  *   stride>=1, pad>=0; E and F from the formula above must be >= 1.
- *   flags      0, or any of SC_PACK_HOST_ONLY, SC_PACK_ALL_TAPS, SC_PACK_FP16_WORD.
+ *   flags      0, or any of SC_PACK_HOST_ONLY, SC_PACK_ALL_TAPS, SC_PACK_FP16_WORD,
+ *              SC_PACK_ESCOIN_MAP (see each flag for the combinations it rejects).
  *   out        receives the new handle (set to NULL on failure).
  * Steps: validate -> CSR (columns sorted within each row, values moved with them) ->
  * stretched offsets -> wavefront schedule balanced by non-zero count -> upload.
@@ -149,12 +166,35 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
  * Asynchronous: returns after the launch; nothing is synchronised.  The handle is never
  * written, so forwards on several streams may run at once.  Limits (SC_EUNSUPPORTED):
  * N*C*H*W < 2^31 and N*M*E*F < 2^31 elements.  Errors: SC_EINVAL (null handle or
- * pointers, host-only handle, overlap), SC_ESHAPE (dims differ from the handle),
- * SC_EDEVICE (launch failure).
+ * pointers, host-only handle, overlap, a handle packed with SC_PACK_ESCOIN_MAP), SC_ESHAPE
+ * (dims differ from the handle), SC_EDEVICE (launch failure).
  */
 sc_status sparseconv_forward(const sc_handle* h, const float* input, float* output, int32_t N,
                              int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
                              int32_t stride, int32_t pad, void* hip_stream);
+
+/*
+ * Device workspace a forward of N images needs, in bytes (*bytes; 0 if none).  Handles
+ * packed with SC_PACK_ESCOIN_MAP need N*C*(H+2pad)*(W+2pad)*4 bytes (rounded up to 256) for
+ * the padded input; all others need none.  SC_EINVAL on a NULL handle or bytes, SC_ESHAPE
+ * for N < 0.
+ */
+sc_status sparseconv_workspace_size(const sc_handle* h, int32_t N, int64_t* bytes);
+
+/*
+ * Forward pass with a caller-owned device workspace (the same contract as sparseconv_forward
+ * otherwise).  workspace: device, at least sparseconv_workspace_size(h, N) bytes, 4-byte
+ * aligned, overlapping neither input nor output (it may be NULL when that size is 0);
+ * its contents are scratch, overwritten by the call, and two calls that share a workspace
+ * must not run at the same time.  Required for SC_PACK_ESCOIN_MAP handles; for others the
+ * workspace is not touched.  Errors as sparseconv_forward, plus SC_EINVAL for a missing,
+ * small, misaligned or overlapping workspace.  Limits (SC_EUNSUPPORTED) as
+ * sparseconv_forward, plus N*C*ceil((H+2pad)*(W+2pad)/256) and N*M*ceil(E*F/1024) below 2^31.
+ */
+sc_status sparseconv_forward_workspace(const sc_handle* h, const float* input, float* output,
+                                       int32_t N, int32_t C, int32_t H, int32_t W, int32_t M,
+                                       int32_t R, int32_t S, int32_t stride, int32_t pad,
+                                       void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 /* Fill *info with the handle's geometry, sizes and launch plan.  SC_EINVAL on NULL. */
 sc_status sparseconv_query(const sc_handle* h, sc_info* info);

@@ -6,7 +6,8 @@ used for device memory and streams.  There is no fallback: if the library is mis
 import fails, and the forward pass needs a ROCm device.
 
 The functions keep the C names:
-    sparseconv_pack, sparseconv_forward, sparseconv_query, sparseconv_export_packed,
+    sparseconv_pack, sparseconv_forward, sparseconv_forward_workspace,
+    sparseconv_workspace_size, sparseconv_query, sparseconv_export_packed,
     sparseconv_export_words, sparseconv_destroy, sparseconv_last_error
 plus ``Handle`` (owns a packed filter bank and destroys it when collected).  The dense
 direct baseline is a Handle packed with SC_PACK_ALL_TAPS (every filter tap stored).
@@ -37,11 +38,13 @@ SC_WEIGHTS_DENSE, SC_WEIGHTS_CSR = 0, 1
 SC_PACK_HOST_ONLY = 1
 SC_PACK_ALL_TAPS = 2
 SC_PACK_FP16_WORD = 4
+SC_PACK_ESCOIN_MAP = 8
 _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: "SC_EDEVICE",
                  5: "SC_EUNSUPPORTED"}
 
-EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_query", "sparseconv_export_packed",
-            "sparseconv_export_words", "sparseconv_destroy", "sparseconv_last_error")
+EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
+            "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words", "sparseconv_destroy",
+            "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -55,7 +58,7 @@ class sc_info(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
                                                "pipeline_depth", "step_balance_permille",
-                                               "split_pieces", "plan_variants", "entry_bytes")]
+                                               "split_pieces", "plan_variants", "entry_bytes", "mapping")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -66,6 +69,10 @@ _lib.sparseconv_pack.restype = _i32
 _lib.sparseconv_pack.argtypes = [ctypes.POINTER(sc_weights)] + [_i32] * 8 + [_u32, ctypes.POINTER(_vp)]
 _lib.sparseconv_forward.restype = _i32
 _lib.sparseconv_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
+_lib.sparseconv_forward_workspace.restype = _i32
+_lib.sparseconv_forward_workspace.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp, ctypes.c_int64, _vp]
+_lib.sparseconv_workspace_size.restype = _i32
+_lib.sparseconv_workspace_size.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_int64)]
 _lib.sparseconv_query.restype = _i32
 _lib.sparseconv_query.argtypes = [_vp, ctypes.POINTER(sc_info)]
 _lib.sparseconv_export_packed.restype = _i32
@@ -142,6 +149,28 @@ def sparseconv_forward(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, stre
                                    _stream_ptr(stream)), "sparseconv_forward")
 
 
+def sparseconv_forward_workspace(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, workspace, workspace_bytes,
+                                 stream=None) -> None:
+    """``workspace``: a device tensor (any dtype, contiguous), a raw address, or None."""
+    if workspace is None:
+        wp = None
+    elif isinstance(workspace, int):
+        wp = workspace
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the GPU")
+        wp = workspace.data_ptr()
+    _check(_lib.sparseconv_forward_workspace(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad, wp,
+                                             int(workspace_bytes), _stream_ptr(stream)),
+           "sparseconv_forward_workspace")
+
+
+def sparseconv_workspace_size(handle: int, N: int) -> int:
+    b = ctypes.c_int64()
+    _check(_lib.sparseconv_workspace_size(handle, N, ctypes.byref(b)), "sparseconv_workspace_size")
+    return b.value
+
+
 def sparseconv_query(handle: int) -> dict:
     info = sc_info()
     _check(_lib.sparseconv_query(handle, ctypes.byref(info)), "sparseconv_query")
@@ -201,15 +230,25 @@ class Handle:
     def export_words(self):
         return sparseconv_export_words(self.ptr)
 
-    def forward(self, x, out=None, stream=None):
-        """x: (N, C, H, W) float32 CUDA tensor; returns out (N, M, E, F)."""
+    def workspace_size(self, N: int) -> int:
+        return sparseconv_workspace_size(self.ptr, N)
+
+    def forward(self, x, out=None, stream=None, workspace=None):
+        """x: (N, C, H, W) float32 CUDA tensor; returns out (N, M, E, F).  With ``workspace``
+        (a device tensor of at least workspace_size(N) bytes) the workspace entry point is
+        used; handles packed with SC_PACK_ESCOIN_MAP need one."""
         import torch
         g = self.geom
         N = x.shape[0]
         if out is None:
             out = torch.empty((N, g["M"], self.E, self.F), dtype=torch.float32, device=x.device)
-        sparseconv_forward(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
-                           g["stride"], g["pad"], stream)
+        if workspace is None:
+            sparseconv_forward(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
+                               g["stride"], g["pad"], stream)
+        else:
+            sparseconv_forward_workspace(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
+                                         g["stride"], g["pad"], workspace,
+                                         workspace.numel() * workspace.element_size(), stream)
         return out
 
     def close(self):

@@ -69,7 +69,11 @@ struct sc_handle {
   std::vector<uint32_t> off;     // canonical stretched offsets
   std::vector<float> val;        // canonical values (fp16-rounded when h16)
   std::vector<uint32_t> words;   // h16: the 32-bit packed words, canonical order
-  std::vector<Variant> var;
+  std::vector<Variant> var;      // LDS-tile mapping: launch plans (empty for escoin)
+  bool escoin;                   // packed with SC_PACK_ESCOIN_MAP
+  sc::EscoinArgs esc;            // escoin: geometry part of the kernel arguments
+  const uint32_t* d_esc_ent;     // escoin: {padded-pitch offset, value bits} per non-zero
+  const int32_t* d_esc_rowptr;   // escoin: M + 1 row pointers
   int device;
   bool host_only;
   void* dmem;
@@ -197,14 +201,19 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
   if (!out) return fail(SC_EINVAL, "out is NULL");
   *out = nullptr;
   if (!w) return fail(SC_EINVAL, "weights descriptor is NULL");
-  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS | SC_PACK_FP16_WORD)) return fail(SC_EINVAL, "unknown pack flag");
+  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS | SC_PACK_FP16_WORD | SC_PACK_ESCOIN_MAP))
+    return fail(SC_EINVAL, "unknown pack flag");
   const bool h16 = (flags & SC_PACK_FP16_WORD) != 0;
+  const bool escoin = (flags & SC_PACK_ESCOIN_MAP) != 0;
+  if (h16 && escoin) return fail(SC_EINVAL, "SC_PACK_FP16_WORD and SC_PACK_ESCOIN_MAP cannot be combined");
   sc::Geom g;
   if (!sc::make_geom(M, C, R, S, H, W, stride, pad, &g))
     return fail(SC_ESHAPE, "invalid layer geometry (dims >= 1, stride >= 1, pad >= 0, output >= 1x1)");
   const long long crs = (long long)C * R * S;
   if ((long long)M * crs >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "M*C*R*S >= 2^31");
   if ((long long)C * H * W >= (1LL << 32)) return fail(SC_EUNSUPPORTED, "C*H*W >= 2^32: offsets do not fit u32");
+  if (escoin && (long long)C * (H + 2LL * pad) * (W + 2LL * pad) >= (1LL << 30))
+    return fail(SC_EUNSUPPORTED, "SC_PACK_ESCOIN_MAP: C*(H+2pad)*(W+2pad) >= 2^30 (32-bit byte offsets)");
   if (h16 && (C > 256 || R > 16 || S > 16))
     return fail(SC_EUNSUPPORTED, "SC_PACK_FP16_WORD: the 32-bit word holds C <= 256 and R, S <= 16");
   if (fail_alloc_hook()) return fail(SC_ENOMEM, "allocation failure (injected by SPARSECONV_TEST_FAIL_ALLOC)");
@@ -230,7 +239,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     // plan variants: the default, then caps on positions per lane and rows per wavefront
     // (none when SPARSECONV_PLAN forces a plan)
     std::vector<Variant> vars;
-    {
+    if (!escoin) {
       static const int caps[][2] = {{0, 0}, {4, 0}, {2, 0}, {1, 0}, {2, 2}, {2, 1}, {1, 1}};
       const bool forced = std::getenv("SPARSECONV_PLAN") != nullptr;
       for (const auto& cap : caps) {
@@ -246,7 +255,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         if (forced) break;
       }
     }
-    if (vars.empty()) return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
+    if (vars.empty() && !escoin)
+      return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
     h->magic = kMagic;
@@ -344,6 +354,29 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       v.per_cu = 1;
     }
     h->var = std::move(vars);
+    h->escoin = escoin;
+    h->d_esc_ent = nullptr;
+    h->d_esc_rowptr = nullptr;
+    std::vector<uint32_t> esc_ent;
+    if (escoin) {
+      // "Escoin" weight stretching against the padded input: (c*Hp + r)*Wp + s
+      sc::EscoinArgs& e = h->esc;
+      e = sc::EscoinArgs{};
+      e.C = C; e.H = H; e.W = W; e.M = M; e.E = g.E; e.F = g.F; e.st = stride; e.pad = pad;
+      e.Hp = H + 2 * pad;
+      e.Wp = W + 2 * pad;
+      e.img_words = C * e.Hp * e.Wp;
+      e.tiles = (g.E * g.F + 256 * sc::kEscoinP - 1) / (256 * sc::kEscoinP);
+      int longest = 1;
+      for (int m = 0; m < M; m++) longest = std::max(longest, rowptr[m + 1] - rowptr[m]);
+      e.chunk = std::min(longest, sc::kEscoinChunk);
+      esc_ent.assign(2 * std::max<long long>(nnz, 1), 0);
+      for (long long j = 0; j < nnz; j++) {
+        const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
+        esc_ent[2 * j] = (uint32_t)((c * e.Hp + r) * e.Wp + sx);
+        std::memcpy(&esc_ent[2 * j + 1], &val[j], 4);
+      }
+    }
 
     if (!h->host_only) {
       if (hipGetDevice(&h->device) != hipSuccess) {
@@ -351,7 +384,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_EDEVICE, "no HIP device available");
       }
       auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-      size_t total = 0;
+      size_t total = al(esc_ent.size() * 4) + (escoin ? al(rowptr.size() * 4) : 0);
       for (const Variant& v : h->var)
         total += al(v.ent.size() * 4) + al(v.bstart.size() * 4) + al(v.sched.slot_row.size() * 4) +
                  al(v.sched.slot_comb.size() * 4);
@@ -362,6 +395,18 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_ENOMEM, "hipMalloc of the packed filter bank failed");
       }
       char* base = static_cast<char*>(h->dmem);
+      if (escoin) {
+        h->d_esc_ent = reinterpret_cast<const uint32_t*>(base);
+        h->d_esc_rowptr = reinterpret_cast<const int32_t*>(base + al(esc_ent.size() * 4));
+        hipError_t e1 = hipMemcpy(base, esc_ent.data(), esc_ent.size() * 4, hipMemcpyHostToDevice);
+        hipError_t e2 = hipMemcpy(base + al(esc_ent.size() * 4), rowptr.data(), rowptr.size() * 4,
+                                  hipMemcpyHostToDevice);
+        if (e1 != hipSuccess || e2 != hipSuccess) {
+          sparseconv_destroy(h);
+          return fail(SC_EDEVICE, "upload of the packed filter bank failed");
+        }
+        base += al(esc_ent.size() * 4) + al(rowptr.size() * 4);
+      }
       for (Variant& v : h->var) {
         const size_t b_ent = al(v.ent.size() * 4), b_seg = al(v.bstart.size() * 4);
         const size_t b_slot = al(v.sched.slot_row.size() * 4), b_comb = al(v.sched.slot_comb.size() * 4);
@@ -408,8 +453,21 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->E = h->g.E; info->F = h->g.F;
   info->nnz = h->nnz;
   info->packed_bytes = ((h->h16 ? 1 : 2) * h->nnz + h->g.M + 1) * 4;
-  info->entry_bytes = h->h16 ? 4 : 8;
   info->device_bytes = (int64_t)h->dbytes;
+  info->entry_bytes = h->h16 ? 4 : 8;
+  info->mapping = h->escoin ? 1 : 0;
+  if (h->escoin) {
+    info->tile_pixels = 256 * sc::kEscoinP;
+    info->rows_per_wave = 1;
+    info->row_groups = 1;
+    info->chunk_channels = h->g.C;
+    info->lds_bytes = h->esc.chunk * 8;
+    info->waves_per_group = 4;
+    int64_t longest = 0;
+    for (int m = 0; m < h->g.M; m++) longest = std::max<int64_t>(longest, h->rowptr[m + 1] - h->rowptr[m]);
+    info->max_wave_nnz = (int32_t)longest;
+    return SC_OK;
+  }
   const Variant& v = h->var[0];  // the default plan
   info->tile_pixels = 64 * v.p.K;
   info->waves_per_group = v.p.NW - 1;
@@ -521,14 +579,15 @@ size_t pick_variant(const sc_handle* h, int N) {
   return best;
 }
 
-}  // namespace
+// Bytes of the padded input the "Escoin" mapping writes for N images (0 for other handles).
+long long workspace_bytes(const sc_handle* h, int N) {
+  if (!h->escoin || N <= 0) return 0;
+  return ((long long)N * h->esc.img_words * 4 + 255) & ~255LL;
+}
 
-extern "C" {
-
-sc_status sparseconv_forward(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C,
-                             int32_t H, int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride,
-                             int32_t pad, void* hip_stream) {
-  g_err.clear();
+sc_status forward_impl(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C, int32_t H,
+                       int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride, int32_t pad, void* workspace,
+                       int64_t ws_bytes, bool with_ws, void* hip_stream) {
   if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
   if (h->host_only) return fail(SC_EINVAL, "handle was packed with SC_PACK_HOST_ONLY");
   const sc::Geom& g = h->g;
@@ -536,10 +595,38 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   if (C != g.C || H != g.H || W != g.W || M != g.M || R != g.R || S != g.S || stride != g.st || pad != g.pad)
     return fail(SC_ESHAPE, "forward dims differ from the packed handle");
   if (N == 0) return SC_OK;
+  int dev = -1;
+  if (h->escoin) {
+    if (!with_ws)
+      return fail(SC_EINVAL, "handle was packed with SC_PACK_ESCOIN_MAP: it needs a workspace (sparseconv_forward_workspace)");
+    const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
+    if (nin >= (1LL << 31) || nout >= (1LL << 31))
+      return fail(SC_EUNSUPPORTED, "N*C*H*W or N*M*E*F >= 2^31 elements");
+    const long long runs = (h->esc.Hp * (long long)h->esc.Wp + 255) / 256;
+    if ((long long)N * g.C * runs >= (1LL << 31) || (long long)N * g.M * h->esc.tiles >= (1LL << 31))
+      return fail(SC_EUNSUPPORTED, "too many workgroups for one launch");
+    if (!input || !output) return fail(SC_EINVAL, "input or output is NULL");
+    const long long need = workspace_bytes(h, N);
+    if (!workspace || ws_bytes < need)
+      return fail(SC_EINVAL, "workspace is NULL or smaller than sparseconv_workspace_size (" + std::to_string(need) +
+                                 " bytes)");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3) != 0) return fail(SC_EINVAL, "workspace is not 4-byte aligned");
+    if (ranges_overlap(input, nin * 4, output, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
+    if (ranges_overlap(workspace, need, input, nin * 4) || ranges_overlap(workspace, need, output, nout * 4))
+      return fail(SC_EINVAL, "workspace overlaps input or output");
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+      return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+    sc::EscoinArgs a = h->esc;
+    a.N = N;
+    const int e = sc::launch_escoin(a, input, static_cast<float*>(workspace), output, h->d_esc_ent, h->d_esc_rowptr,
+                                    hip_stream);
+    if (e != (int)hipSuccess)
+      return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
+    return SC_OK;
+  }
   const Variant& v = h->var[pick_variant(h, N)];
   sc_status s = check_io(g, v.p, input, output, N);
   if (s != SC_OK) return s;
-  int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
   sc::KArgs a = make_args(g, v.p, input, output, N);
@@ -553,6 +640,35 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
   const int e = sc::launch_sparse(v.p, a, hip_stream, nb);
   if (e != (int)hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
   return SC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sc_status sparseconv_forward(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C,
+                             int32_t H, int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride,
+                             int32_t pad, void* hip_stream) {
+  g_err.clear();
+  return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, nullptr, 0, false, hip_stream);
+}
+
+sc_status sparseconv_workspace_size(const sc_handle* h, int32_t N, int64_t* bytes) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!bytes) return fail(SC_EINVAL, "bytes is NULL");
+  if (N < 0) return fail(SC_ESHAPE, "N < 0");
+  *bytes = workspace_bytes(h, N);
+  return SC_OK;
+}
+
+sc_status sparseconv_forward_workspace(const sc_handle* h, const float* input, float* output, int32_t N,
+                                       int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                                       int32_t stride, int32_t pad, void* workspace, int64_t workspace_bytes,
+                                       void* hip_stream) {
+  g_err.clear();
+  return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, workspace, workspace_bytes, true,
+                      hip_stream);
 }
 
 }  // extern "C"

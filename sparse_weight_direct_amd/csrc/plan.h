@@ -134,4 +134,22 @@ int occupancy(const Plan& p, int* cus, int* per_cu);
 // Launchers (kernels.hip).  Return a hipError_t value as int.
 int launch_sparse(const Plan& p, const KArgs& a, void* stream, int nblocks);
 
+// Second mapping ("Escoin" dataflow, escoin.hip): a pad_in kernel writes the zero-padded
+// input (planes of Hp x Wp words) to a workspace, then one workgroup per (output channel,
+// tile of 256*kEscoinP output positions, image) keeps its CSR row in LDS and reads the
+// padded input through the caches.  Entries are {(c*Hp + r)*Wp + s, fp32 value bits}.
+constexpr int kEscoinP = 4;      // output positions per thread (256 apart)
+constexpr int kEscoinChunk = 4096;  // most row entries held in LDS at once
+
+struct EscoinArgs {
+  int N, C, H, W, M, E, F, st, pad;
+  int Hp, Wp;        // padded plane: H + 2 pad, W + 2 pad
+  int img_words;     // C * Hp * Wp
+  int tiles;         // ceil(E*F / (256 * kEscoinP))
+  int chunk;         // row entries per LDS pass: min(longest row, kEscoinChunk), >= 1
+};
+
+int launch_escoin(const EscoinArgs& a, const float* x, float* xp, float* y, const uint32_t* ent,
+                  const int32_t* rowptr, void* stream);
+
 }  // namespace sc

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 7
+    assert len(names) == 9
     lib = ctypes.CDLL(sc.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -135,7 +135,7 @@ def test_shape_and_limit_errors():
     st, msg = _status(lambda: sc.sparseconv_pack(1, 1, 1, 1, 65536, 65536, 1, 0, values=big,
                                                  flags=sc.SC_PACK_HOST_ONLY))
     assert st == sc.SC_EUNSUPPORTED and "2^32" in msg
-    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 1, 1, values=w, flags=8))
+    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 1, 1, values=w, flags=16))
     assert st == sc.SC_EINVAL
 
 
@@ -226,3 +226,32 @@ def test_chain_rejects_mismatched_shapes():
     b = sc.Handle(8, 6, 3, 3, 10, 10, 1, 1, values=np.ones((8, 6, 3, 3), np.float32), flags=sc.SC_PACK_HOST_ONLY)
     with pytest.raises(ValueError):
         LayerChain([a, b], N=1)
+
+
+def test_escoin_mapping_handle_on_host():
+    """SC_PACK_ESCOIN_MAP: same canonical export, its own info and workspace size, and the
+    combinations the header rejects."""
+    d = workloads.make("mid", n_override=1)
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ESCOIN_MAP)
+    rowptr, off, val = h.export()
+    o_rowptr, o_col, o_val = oracle.csr_from_dense(d["w"], d["mask"])
+    np.testing.assert_array_equal(rowptr, o_rowptr)
+    np.testing.assert_array_equal(off, oracle.stretch(o_col, L.C, L.R, L.S, L.H, L.W))
+    np.testing.assert_array_equal(val.view(np.uint32), o_val.view(np.uint32))
+    info = h.info()
+    assert info["mapping"] == 1 and info["max_wave_nnz"] == int(np.diff(o_rowptr).max())
+    for n in (0, 1, 3):
+        want = n * L.C * (L.H + 2 * L.pad) * (L.W + 2 * L.pad) * 4
+        assert h.workspace_size(n) == (want + 255) // 256 * 256
+    assert _pack_host(d, L).workspace_size(5) == 0 and _pack_host(d, L).info()["mapping"] == 0
+    st, msg = _status(lambda: sc.sparseconv_pack(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"],
+                                                 mask=d["mask"], flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ESCOIN_MAP
+                                                 | sc.SC_PACK_FP16_WORD))
+    assert st == sc.SC_EINVAL and "ESCOIN" in msg
+    st, _ = _status(lambda: h.workspace_size(-1))
+    assert st == sc.SC_ESHAPE
+    st, msg = _status(lambda: sc.sparseconv_forward_workspace(h.ptr, 1 << 20, 1 << 24, 1, L.C, L.H, L.W, L.M, L.R,
+                                                              L.S, L.stride, L.pad, 1 << 28, 1 << 24, stream=0))
+    assert st == sc.SC_EINVAL and "HOST_ONLY" in msg
