@@ -11,8 +11,8 @@
 //            from LDS (one broadcast read per wavefront), the inputs come from the padded
 //            buffer through the caches (consecutive lanes read consecutive words for
 //            stride 1), and each lane does P FMAs.  Workgroups of all output channels of one
-//            spatial tile are launched next to each other, so they share the tile's input in
-//            the L2 cache.
+//            spatial tile run next to each other on one XCD, so they share the tile's input in
+//            that XCD's L2 cache.
 //
 // Unlike the LDS-tile kernel (kernels.hip), nothing here stages the input: every non-zero
 // re-reads its input words through L1/L2.  The two are kept side by side to measure that
@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include "plan.h"
+#include "xcd.h"
 
 namespace sc {
 
@@ -54,8 +55,9 @@ __global__ __launch_bounds__(256) void sconv(const EscoinArgs a, const float* __
                                              const int* __restrict__ rowptr) {
   extern __shared__ uint2 wrow[];
   const int t = threadIdx.x;
-  // block -> (output channel m fastest, then spatial tile, then image)
-  const int b = blockIdx.x;
+  // block -> (output channel m fastest, then spatial tile, then image); consecutive ids on
+  // one XCD, so that the workgroups of a tile's output channels share that XCD's L2
+  const int b = xcd_logical(blockIdx.x, gridDim.x);
   const int m = b % a.M;
   const int rest = b / a.M;
   const int tile = rest % a.tiles;

@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include "plan.h"
+#include "xcd.h"
 
 namespace sc {
 
@@ -93,14 +94,6 @@ __device__ __forceinline__ void lds_dma_dwordx4(v4i rsrc, const float* lds, uint
       :
       : "s"(m0), "v"(voff), "s"(rsrc), "s"(so)
       : "memory", "m0");
-}
-
-// Workgroups are handed to the 8 XCDs round-robin; renumber them so that consecutive
-// logical ids (hence adjacent runs of tiles, which share halo rows) sit on one XCD's L2.
-__device__ __forceinline__ int xcd_logical(int b, int nb) {
-  const int q = nb >> 3, rmd = nb & 7;
-  const int xcd = b & 7, k = b >> 3;
-  return xcd < rmd ? xcd * (q + 1) + k : rmd * (q + 1) + (xcd - rmd) * q + k;
 }
 
 // s_waitcnt vmcnt(N) for a wave-uniform N in [0, 63] (gfx9 encoding: vmcnt bits [3:0] and
@@ -604,6 +597,7 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   uint32_t* pcons = pfull + a.nbuf;
   float* pbuf = reinterpret_cast<float*>(pcons + a.nbuf);
 
+  // adjacent runs of tiles, which share halo rows, on one XCD's L2
   const int b = xcd_logical(blockIdx.x, gridDim.x);
   const long long units = (long long)a.ntiles * a.G;
   const int u0 = (int)(units * b / gridDim.x);

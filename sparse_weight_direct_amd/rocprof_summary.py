@@ -26,7 +26,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_weight_direct_amd", "csrc", f)
-                  for f in ("kernels.hip", "plan.h", "pack.cpp", "api.cpp")]
+                  for f in ("kernels.hip", "xcd.h", "plan.h", "pack.cpp", "api.cpp")]
 COPY_KERNELS = ("__amd_rocclr_copyBuffer", "copy", "Copy")
 
 
