@@ -147,12 +147,14 @@ __device__ __forceinline__ uint32_t block_voff(const KArgs& a, int I0, int n0, i
 
 // The same offsets for consecutive blocks blk, blk+1, ... without divisions: the lane's
 // position (phase ph, word j of the phase plane, image n, row t, column x of the extended
-// plane) advances by 64 words per block.  A step that leaves the phase plane, and images
-// smaller than two blocks, fall back to the divisions.  (Producer only: narrow layout with
-// more blocks than it caches.)
+// plane) advances by 64 words per block.  When PL is a multiple of 64 (stride > 1), a step
+// into the next phase plane lands on word j = lane again, whose position is kept from
+// init; otherwise that step, and images smaller than two blocks, fall back to the
+// divisions.  (Producer only: narrow layout with more blocks than it caches.)
 struct VoffIter {
   int w, ph, j, n, t, x;
-  int q64, r64;  // 64 = q64 * Pp + r64
+  int n_s, t_s, x_s;  // position of word j = lane of a phase plane
+  int q64, r64;       // 64 = q64 * Pp + r64
   __device__ __forceinline__ void full(const KArgs& a, int I0) {
     ph = w / a.PL;
     j = w - ph * a.PL;
@@ -166,13 +168,30 @@ struct VoffIter {
     w = 64 * blk + lane;
     q64 = 64 / a.Pp;
     r64 = 64 - q64 * a.Pp;
+    const int J = I0 + lane;
+    n_s = J / a.img_ext;
+    const int rem = J - n_s * a.img_ext;
+    t_s = rem / a.Pp;
+    x_s = rem - t_s * a.Pp;
     full(a, I0);
   }
   __device__ __forceinline__ void next(const KArgs& a, int I0) {
     w += 64;
     j += 64;
-    if (j >= a.PL || a.img_ext < 128) {
+    if (a.img_ext < 128) {
       full(a, I0);
+      return;
+    }
+    if (j >= a.PL) {
+      if ((a.PL & 63) == 0) {  // next phase plane, word j = lane
+        ph++;
+        j -= a.PL;
+        n = n_s;
+        t = t_s;
+        x = x_s;
+      } else {
+        full(a, I0);
+      }
       return;
     }
     x += r64;
@@ -194,6 +213,80 @@ struct VoffIter {
     if (n < a.N && y >= 0 && y < a.H && xx >= 0 && xx < a.W)
       return 4u * (uint32_t)(((n - n0) * a.C * a.H + y) * a.W + xx);
     return kOutOfRange;
+  }
+};
+
+// Floor division by a positive divisor for a numerator of either sign.
+__device__ __forceinline__ int floor_div(int n, int d) { return n >= 0 ? n / d : -((d - 1 - n) / d); }
+
+// Narrow layout with stride > 1 (PL a multiple of 64, images of at least 128 words): the
+// lane's source offsets for every block of a channel in order, with additions and compares
+// only (integer multiplies and divisions are quarter rate and the producer is a single
+// wavefront).  Each phase plane (py, px) starts at word j = lane, whose image n, phase row t
+// and phase column x are found once per tile; the source word of (n, t, x) in phase
+// (py, px) is (n - n0)*C*H*W + (t*st + py - pad)*W + x*st + px - xoff, a linear function that
+// is stepped with the position.  A word is in range when n < N and t, x fall inside the
+// phase's rows and columns of the image.
+struct PlaneIter {
+  int n, t, x, src;      // current position and its source word offset
+  int ns, ts, xs, srcs;  // position of word j = lane in phase (0, 0)
+  int bi, py, px;        // block within the phase plane, phase
+  int tlo, thi, xlo, xhi;
+  __device__ __forceinline__ void bounds(const KArgs& a) {
+    tlo = max(0, floor_div(a.pad - py + a.st - 1, a.st));
+    thi = floor_div(a.H - 1 + a.pad - py, a.st);
+    xlo = max(0, floor_div(a.xoff - px + a.st - 1, a.st));
+    xhi = floor_div(a.W - 1 + a.xoff - px, a.st);
+  }
+  __device__ __forceinline__ void init(const KArgs& a, int I0, int n0, int lane) {
+    const int J = I0 + lane;
+    ns = J / a.img_ext;
+    const int rem = J - ns * a.img_ext;
+    ts = rem / a.Pp;
+    xs = rem - ts * a.Pp;
+    srcs = ((ns - n0) * a.C * a.H + ts * a.st - a.pad) * a.W + xs * a.st - a.xoff;
+    bi = 0;
+    py = 0;
+    px = 0;
+    n = ns;
+    t = ts;
+    x = xs;
+    src = srcs;
+    bounds(a);
+  }
+  __device__ __forceinline__ uint32_t off(const KArgs& a) const {
+    const bool in = n < a.N && t >= tlo && t <= thi && x >= xlo && x <= xhi;
+    return in ? 4u * (uint32_t)src : kOutOfRange;
+  }
+  // dT, dX: 64 = dT * Pp + dX; s1, s2, s3: source steps of 64 words, of a column wrap and of
+  // an image wrap
+  __device__ __forceinline__ void next(const KArgs& a, int nbp, int dT, int dX, int s1, int s2, int s3) {
+    if (++bi == nbp) {  // next phase plane
+      bi = 0;
+      if (++px == a.st) {
+        px = 0;
+        py++;
+      }
+      n = ns;
+      t = ts;
+      x = xs;
+      src = srcs + py * a.W + px;
+      bounds(a);
+      return;
+    }
+    x += dX;
+    t += dT;
+    src += s1;
+    if (x >= a.Pp) {
+      x -= a.Pp;
+      t++;
+      src += s2;
+    }
+    if (t >= a.HYp) {  // at most one image boundary per block (images of >= 128 words)
+      t -= a.HYp;
+      n++;
+      src += s3;
+    }
   }
 };
 
@@ -225,12 +318,24 @@ __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int 
                                           const uint32_t (&voffc)[4], float* slot, int lane,
                                           FirstDone&& first_done) {
   const int bw = a.wide16 ? 256 : 64;
+  // narrow layout, stride > 1: additions-only stepping through the phase planes
+  const bool planes = !a.wide16 && a.st > 1 && (a.PL & 63) == 0 && a.img_ext >= 128;
+  const int nbp = a.PL >> 6;
+  const int dT = 64 / a.Pp, dX = 64 - dT * a.Pp;
+  const int s1 = dT * a.st * a.W + dX * a.st;
+  const int s2 = a.st * a.W - a.Pp * a.st;
+  const int s3 = a.C * a.H * a.W - a.HYp * a.st * a.W;
+  PlaneIter pi;
+  if (planes) pi.init(a, I0, n0, lane);
   VoffIter vi;
-  if (!a.wide16 && a.nsb > 4) vi.init(a, I0, 4, lane);
+  if (!planes && !a.wide16 && a.nsb > 4) vi.init(a, I0, 4, lane);
   for (int blk = 0; blk < a.nsb; blk++) {
     // explicit selects keep the cached offsets in registers (no indexed private array)
     uint32_t voff;
-    if (blk < 4) {
+    if (planes) {
+      if (blk > 0) pi.next(a, nbp, dT, dX, s1, s2, s3);
+      voff = pi.off(a);
+    } else if (blk < 4) {
       voff = blk == 0 ? voffc[0] : blk == 1 ? voffc[1] : blk == 2 ? voffc[2] : voffc[3];
     } else if (a.wide16) {
       voff = block_voff16(a, I0, n0, blk, lane);

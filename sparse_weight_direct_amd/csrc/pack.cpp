@@ -233,6 +233,9 @@ static bool fill_layout(const Geom& g, int K, int D, int cc_cap, int lds_max, Pl
   p->K = K;
   p->D = D;
   p->PL = plan_pl(g, K);
+  // stride > 1: phase planes start on 64-word blocks, so that no staging block straddles two
+  // planes and the producer can step its offsets from plane to plane without divisions
+  if (g.st > 1) p->PL = (p->PL + 63) / 64 * 64;
   const int align = g.wide ? 256 : 64;
   const long long chs = ((long long)g.st * g.st * p->PL + align - 1) / align * align;
   if (chs > (1 << 24)) return false;

@@ -19,7 +19,9 @@
 //  * A workgroup owns a tile of 64*K consecutive extended indices [I0, I0 + 64K) (K per
 //    lane, 64 apart).  For every phase plane it stages exactly the range the tile's taps
 //    read, PL = 64K + (Rr-1)*Pp + (S-1)/st consecutive phase-plane words starting at I0
-//    (rows of the next image and padding included as zeros), for Cc channels at a time:
+//    (rows of the next image and padding included as zeros; for stride > 1 PL is rounded up
+//    to a multiple of 64, so every 64-word block lies in one phase plane), for Cc channels
+//    at a time:
 //        LDS word = c_l*CHS + (py*st + px)*PL + (J - I0)   for phase-plane index J,
 //    with the channel stride CHS = st*st*PL rounded up to a multiple of 64 words, so that
 //    every channel is nblk = CHS/64 blocks of 64 words and a block's source offsets are
@@ -55,7 +57,8 @@ struct Plan {
   int G;           // output-channel groups (work units per tile)
   int Cc;          // channels staged per chunk
   int nch;         // number of chunks = ceil(C / Cc)
-  int PL;          // staged words per phase plane = 64K + (Rr-1)*Pp + (S-1)/st
+  int PL;          // staged words per phase plane >= 64K + (Rr-1)*Pp + (S-1)/st (a multiple
+                   // of 64 for stride > 1)
   int CHS;         // words per staged channel = st*st*PL rounded up to a multiple of 64
   int nblk;        // 64-word blocks per staged channel = CHS / 64 (CHS a multiple of 256
                    // in the wide layout: nblk/4 blocks of 256 words)
