@@ -254,6 +254,16 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         if (!dup) vars.push_back(std::move(v));
         if (forced) break;
       }
+      // two ring slots where that makes all input channels one chunk: a unit is then a
+      // single step (no per-chunk synchronisation), and one slot is staged while the other
+      // is walked
+      const size_t nv = forced ? 0 : vars.size();
+      for (size_t i = 0; i < nv; i++) {
+        if (vars[i].p.nch <= 1 || vars[i].p.D == 2) continue;
+        Variant v;
+        v.p = sc::choose_plan(g, rowptr, col, &v.sched, vars[i].p.K, vars[i].p.OCW, 2);
+        if (v.p.K == vars[i].p.K && v.p.OCW == vars[i].p.OCW && v.p.nch == 1) vars.push_back(std::move(v));
+      }
     }
     if (vars.empty() && !escoin)
       return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");

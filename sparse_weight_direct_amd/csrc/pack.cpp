@@ -319,7 +319,7 @@ static bool instantiated(int K, int OCW) {
 }
 
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched, int k_cap, int ocw_cap) {
+                 Sched* sched, int k_cap, int ocw_cap, int d) {
   static const int kOcw[] = {1, 2, 3, 5, 9};
   static const int kKs[] = {16, 12, 8, 7, 6, 4, 2, 1};
   Plan p{};
@@ -345,7 +345,7 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
   const char* env = std::getenv("SPARSECONV_PLAN");
   OCW = env_int(env, "OCW", OCW);
   const int kenv = env_int(env, "K", 0);
-  int D = env_int(env, "D", 3);
+  int D = env_int(env, "D", d > 0 ? d : 3);
   const int cc_cap = env_int(env, "CC", 0);
   const int lds_max = std::min(kLdsMax, 1024 * env_int(env, "LDSKB", kLdsMax / 1024));
   if (D < 2 || D > kMaxDepth) D = 3;

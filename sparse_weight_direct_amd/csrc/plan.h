@@ -121,8 +121,9 @@ struct KArgs {
 bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* g);
 // Launch plan for the CSR filter matrix (rowptr, col): also schedules rows onto wavefront
 // slots (slot_row) and sizes each wavefront's per-chunk block of non-zeros.
+// k_cap / ocw_cap > 0 cap K and OCW; d > 0 sets the ring depth (default 3).
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched, int k_cap = 0, int ocw_cap = 0);
+                 Sched* sched, int k_cap = 0, int ocw_cap = 0, int d = 0);
 int plan_pl(const Geom& g, int K);
 
 // Header entries at the start of a wavefront's per-chunk block of non-zeros.
