@@ -6,7 +6,9 @@ the whole stack instead of one host launch per layer.  Layer i+1 reads layer i's
 The forward passes themselves are the library's (sparseconv_forward through Handle); this
 module only allocates the intermediate buffers and drives torch's graph capture, whose
 stream the forward launches go to.  sparseconv_forward allocates nothing and records no
-memset, so it can be captured.
+memset, so it can be captured.  Handles that need a workspace (the Escoin mapping) share
+one, allocated here once for the largest of them; the layers run one after another on
+one stream, so the shared workspace is never used by two at once.
 """
 from __future__ import annotations
 
@@ -26,13 +28,15 @@ class LayerChain:
         g0 = handles[0].geom
         self.x = torch.empty((N, g0["C"], g0["H"], g0["W"]), dtype=torch.float32, device=device)
         self.outs = [torch.empty((N, h.geom["M"], h.E, h.F), dtype=torch.float32, device=device) for h in handles]
+        ws = max(h.workspace_size(N) for h in handles)
+        self.ws = torch.empty((ws + 3) // 4, dtype=torch.float32, device=device) if ws else None
         self.graph = None
 
     def run(self, stream=None):
         """All layers on the current (or given) stream, from self.x into self.outs."""
         src = self.x
         for h, out in zip(self.handles, self.outs):
-            h.forward(src, out, stream=stream)
+            h.forward(src, out, stream=stream, workspace=self.ws if h.workspace_size(self.N) else None)
             src = out
         return self.outs[-1]
 

@@ -19,9 +19,11 @@ from sparse_weight_direct_amd.chain import LayerChain
 pytestmark = pytest.mark.gpu
 
 
-def _chain(name):
+def _chain(name, flags=(0,)):
+    """The stack with layer i packed with flags[i % len(flags)]."""
     layers = workloads.make_chain(name)
-    handles = [sc.Handle(values=d["w"], mask=d["mask"], **d["geom"]) for d in layers]
+    handles = [sc.Handle(values=d["w"], mask=d["mask"], flags=flags[i % len(flags)], **d["geom"])
+               for i, d in enumerate(layers)]
     ch = LayerChain(handles, N=layers[0]["x"].shape[0])
     ch.x.copy_(torch.from_numpy(layers[0]["x"]))
     return layers, ch
@@ -56,3 +58,28 @@ def test_chain_graph_replays_equal_eager(name):
         torch.cuda.synchronize()
         got = ch.outs[-1]
         assert torch.equal(got, eager), f"replay {rep}: {int((got != eager).sum())} outputs differ"
+
+
+def test_mixed_chain_fp16_word_and_escoin_layers():
+    """A stack mixing the default handle, a packed-word handle and an Escoin-mapping handle
+    (which needs the chain's workspace): each layer against the oracle of its own form, and
+    graph replays equal to the eager run."""
+    layers, ch = _chain("tiny4", flags=(0, sc.SC_PACK_FP16_WORD, sc.SC_PACK_ESCOIN_MAP))
+    assert ch.ws is not None
+    eager = ch.run().clone()
+    torch.cuda.synchronize()
+    src = layers[0]["x"]
+    for i, (d, out) in enumerate(zip(layers, ch.outs)):
+        g = d["geom"]
+        ref_fn = oracle.reference_fp16 if i % 3 == 1 else oracle.reference
+        ref = ref_fn(src, d["w"], d["mask"], g["stride"], g["pad"])
+        y = out.cpu().numpy()
+        assert_parity(y, ref["y64"], ref["mag"], f"mixed layer {i}")
+        src = y
+    ch.capture()
+    for rep in range(3):
+        for o in ch.outs:
+            o.fill_(float("nan"))
+        ch.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ch.outs[-1], eager), f"replay {rep}"
