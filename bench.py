@@ -243,6 +243,13 @@ def main():
                          f"all {M} output channels, {tc:.1f} s"}
 
     traffic = stored_traffic(tag)
+    sp = round(100 * L.sparsity)
+    mask_text = {"beta_rows": f"per-channel density Beta(0.5,b) mean sparsity {sp}%",
+                 "exact": f"uniform unstructured {sp}% sparsity (exact count)",
+                 "bernoulli": f"i.i.d. Bernoulli mask, {sp}% sparsity"}.get(L.mask_kind, f"{sp}% sparsity")
+    mask_text += {"u11": ", inputs U[-1,1]", "relu_n01": ", inputs ReLU(N(0,1))"}.get(L.x_dist, "")
+    mask_text += {"u11": ", weights U[-1,1]", "n0.05": ", weights N(0,0.05)", "n0.02": ", weights N(0,0.02)"}.get(
+        L.w_dist, "")
     out = {
         "metric": "sparse conv effective TFLOP/s (2*nnz*N*E*F/s) and % of HBM roofline",
         "value": round(tflops, 4),
@@ -257,7 +264,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{layer}: N={N} C={C} H=W={H} M={M} {R}x{S} stride {st} pad {pad}, "
-                               f"per-channel density Beta(0.5,b) mean sparsity {round(100 * L.sparsity)}%, "
+                               f"{mask_text}, "
                                f"realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)"
                                + (", weights as 32-bit words with fp16 values" if args.fp16_word else "")
                                + (", Escoin mapping (pad_in + one output channel per workgroup)" if args.escoin else ""),
