@@ -102,3 +102,38 @@ def test_fp16_and_fp32_handles_agree_on_fp16_exact_weights():
     y16, _ = gpu_sparse(d["x"], w16, d["mask"], L.stride, L.pad,
                         handle=_handle16(w16, d["mask"], L.H, L.W, L.stride, L.pad))
     np.testing.assert_array_equal(y16.view(np.uint32), y32.view(np.uint32))
+
+
+def _cases(count, seed0):
+    rng = np.random.default_rng(seed0)
+    out = []
+    for i in range(count):
+        R, S = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        st, p = int(rng.integers(1, 5)), int(rng.integers(0, 3))
+        H = int(rng.integers(max(1, R - 2 * p), 48))
+        W = int(rng.integers(max(1, S - 2 * p), 48))
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 40)), H, W, int(rng.integers(1, 70)), R, S, st, p,
+                    [0.9, 0.5, 0.1, 0.0, 1.0, 0.03][i % 6], 7000 + i))
+    return out
+
+
+@pytest.mark.parametrize("c", _cases(24, 5), ids=lambda c: "N{}C{}H{}W{}M{}R{}S{}st{}p{}k{}".format(*c[:10]))
+def test_random_shapes_fp16_word(c):
+    N, C, H, W, M, R, S, st, p, keep, seed = c
+    d = workloads.make_custom(N, C, H, W, M, R, S, st, p, keep, seed)
+    r = oracle.reference_fp16(d["x"], d["w"], d["mask"], st, p)
+    h = _handle16(d["w"], d["mask"], H, W, st, p)
+    y, _ = gpu_sparse(d["x"], d["w"], d["mask"], st, p, handle=h)
+    assert_parity(y, r["y64"], r["mag"], "fp16 word random")
+
+
+def test_batch_sizes_share_one_fp16_word_handle():
+    """N is a forward-time argument, and the forward picks a plan variant per N."""
+    d = workloads.make("late")
+    L = d["layer"]
+    h = _handle16(d["w"], d["mask"], L.H, L.W, L.stride, L.pad)
+    for n in (1, 5, 32):
+        x = d["x"][:n]
+        r = oracle.reference_fp16(x, d["w"], d["mask"], L.stride, L.pad)
+        y, _ = gpu_sparse(x, d["w"], d["mask"], L.stride, L.pad, handle=h)
+        assert_parity(y, r["y64"], r["mag"], f"late fp16 word N={n}")
