@@ -126,9 +126,11 @@ typedef struct {
   int32_t plan_variants; /* launch plans the handle holds.  The fields above describe the
                             default one (most positions per workgroup); the others have fewer
                             positions per workgroup or fewer rows per wavefront, i.e. more
-                            work units, and the forward pass takes the one estimated fastest
+                            work units, or (8-byte entries only) hold four consecutive
+                            positions per lane read with 16-byte LDS reads (504 positions per
+                            workgroup), and the forward pass takes the one estimated fastest
                             for its N (small batches and small images use more, smaller
-                            units so that every CU has work) */
+                            units so that every CU has work; denser filters the quad plan) */
   int32_t entry_bytes;   /* bytes per non-zero in the kernel stream: 8 ({LDS offset, fp32
                             weight}), or 4 ({LDS offset, fp16 weight}) with SC_PACK_FP16_WORD */
   int32_t mapping;       /* 0: LDS-tile kernel (the plan fields above); 1: SC_PACK_ESCOIN_MAP

@@ -241,7 +241,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     std::vector<Variant> vars;
     if (!escoin) {
       static const int caps[][2] = {{0, 0}, {4, 0}, {2, 0}, {1, 0}, {2, 2}, {2, 1}, {1, 1}};
-      const bool forced = std::getenv("SPARSECONV_PLAN") != nullptr;
+      const char* plan_env = std::getenv("SPARSECONV_PLAN");
+      const bool forced = plan_env != nullptr && plan_env[0] != '\0';
       for (const auto& cap : caps) {
         Variant v;
         v.p = sc::choose_plan(g, rowptr, col, &v.sched, cap[0], cap[1]);
@@ -249,10 +250,18 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
           if (vars.empty()) break;
           continue;
         }
+        if (v.p.quad && h16) continue;  // quad plans take the 8-byte entries only
         bool dup = false;
-        for (const Variant& u : vars) dup = dup || (u.p.K == v.p.K && u.p.OCW == v.p.OCW);
+        for (const Variant& u : vars) dup = dup || (u.p.K == v.p.K && u.p.OCW == v.p.OCW && u.p.quad == v.p.quad);
         if (!dup) vars.push_back(std::move(v));
         if (forced) break;
+      }
+      // quad plans (8-byte entries): four consecutive positions per lane read with 16-byte
+      // LDS reads
+      if (!forced && !h16) {
+        Variant v;
+        v.p = sc::choose_plan(g, rowptr, col, &v.sched, 0, 0, 0, 1);
+        if (v.p.K != 0 && v.p.quad) vars.push_back(std::move(v));
       }
       // two ring slots where that makes all input channels one chunk: a unit is then a
       // single step (no per-chunk synchronisation), and one slot is staged while the other
@@ -261,8 +270,9 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       for (size_t i = 0; i < nv; i++) {
         if (vars[i].p.nch <= 1 || vars[i].p.D == 2) continue;
         Variant v;
-        v.p = sc::choose_plan(g, rowptr, col, &v.sched, vars[i].p.K, vars[i].p.OCW, 2);
-        if (v.p.K == vars[i].p.K && v.p.OCW == vars[i].p.OCW && v.p.nch == 1) vars.push_back(std::move(v));
+        v.p = sc::choose_plan(g, rowptr, col, &v.sched, vars[i].p.K, vars[i].p.OCW, 2, vars[i].p.quad);
+        if (v.p.K == vars[i].p.K && v.p.OCW == vars[i].p.OCW && v.p.quad == vars[i].p.quad && v.p.nch == 1)
+          vars.push_back(std::move(v));
       }
     }
     if (vars.empty() && !escoin)
@@ -311,7 +321,10 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         chunk_start[(size_t)m * (p.nch + 1) + p.nch] = rowptr[m + 1];
       }
       const int hdr_n = sc::block_header(p.OCW);
-      const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + 63) + 64;
+      // quad plans: two zero entries close every block, so that the walk, which reads one
+      // entry ahead, never reads past its block
+      const int tail = p.quad ? 2 : 0;
+      const size_t n_ent = (size_t)nnz + (size_t)waves * p.nch * (hdr_n + tail + 63) + 64;
       if (n_ent >= (size_t)1 << 31) {
         sparseconv_destroy(h);
         return fail(SC_EUNSUPPORTED, "kernel stream too large");
@@ -331,14 +344,39 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
             const size_t sl = (size_t)wv * p.OCW + o;
             const int m = sched.src_row[sl];
             int cnt = 0;
+            uint32_t ncls[4] = {0, 0, 0, 0};
             if (m >= 0) {  // this slot's piece of row m: part of the row's entries of chunk k
               int b = chunk_start[(size_t)m * (p.nch + 1) + k];
               int e = chunk_start[(size_t)m * (p.nch + 1) + k + 1];
               sc::piece_range(b, e, sched.piece[sl], sched.npieces[sl], &b, &e);
-              for (int j = b; j < e; j++) {
+              auto enc_of = [&](int j) {
                 const int c = col[j] / (R * S), r = (col[j] / S) % R, sx = col[j] % S;
-                const uint32_t enc = (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
-                                                (r / stride) * g.Pp + sx / stride);
+                return (uint32_t)((c % p.Cc) * p.CHS + ((r % stride) * stride + (sx % stride)) * p.PL +
+                                  (r / stride) * g.Pp + sx / stride);
+              };
+              if (p.quad) {
+                // class-sorted (stable): {byte offset of the aligned quad, fp32 weight}
+                for (int cls = 0; cls < 4; cls++)
+                  for (int j = b; j < e; j++) {
+                    const uint32_t enc = enc_of(j);
+                    if ((int)(enc & 3u) != cls) continue;
+                    uint32_t vbits;
+                    std::memcpy(&vbits, &val[j], 4);
+                    ent[2 * pos] = 4u * (enc & ~3u);
+                    ent[2 * pos + 1] = vbits;
+                    pos++;
+                    ncls[cls]++;
+                  }
+                if (ncls[0] > 0xffffu || ncls[1] > 0xffffu || ncls[2] > 0xffffu || ncls[3] > 0xffffu) {
+                  sparseconv_destroy(h);
+                  return fail(SC_EUNSUPPORTED, "quad plan: more than 65535 non-zeros of one class in a block");
+                }
+                ent[2 * (hdr + o)] = ncls[0] | (ncls[1] << 16);
+                ent[2 * (hdr + o) + 1] = ncls[2] | (ncls[3] << 16);
+                continue;
+              }
+              for (int j = b; j < e; j++) {
+                const uint32_t enc = enc_of(j);
                 if (h16) {
                   if (enc > 0xffffu) {
                     sparseconv_destroy(h);
@@ -357,6 +395,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
             }
             ent[ew * (hdr + o)] = (uint32_t)cnt;
           }
+          pos += tail;
         }
         bstart[(size_t)wv * (p.nch + 1) + p.nch] = (int32_t)pos;
       }
@@ -479,7 +518,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
     return SC_OK;
   }
   const Variant& v = h->var[0];  // the default plan
-  info->tile_pixels = 64 * v.p.K;
+  info->tile_pixels = v.p.tp;
   info->waves_per_group = v.p.NW - 1;
   info->pipeline_depth = v.p.D;
   info->step_balance_permille = v.p.step_permille;
@@ -557,23 +596,34 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.HW = g.H * g.W;
   a.x_words = (long long)N * g.C * g.H * g.W;
   a.ext_total = (long long)N * a.img_ext;
-  a.ntiles = (int)((a.ext_total + 64LL * p.K - 1) / (64LL * p.K));
+  a.tp = p.tp;
+  a.ring_words = p.ring_words;
+  a.ntiles = (int)((a.ext_total + p.tp - 1) / p.tp);
   return a;
 }
 
 // Estimated cycles of a forward over N images with plan variant v: the busiest CU's units
 // times a unit's cost, the larger of its input copy (LDS DMA at ~15 B/cycle with 16-byte
 // loads, ~3.7 with 4-byte ones) and its walk (~2.3 cycles per non-zero and 64-position block
-// of LDS reads), plus a fixed cost per chunk step and per launch.  Only used to rank the
-// handle's variants.
+// of LDS reads), plus a fixed cost per chunk step and per launch.  A quad plan's walk costs
+// 0.70 + 0.334 / r of a K = 7 walk per non-zero, r being the mean run of one class of one
+// slot in one chunk (a run boundary breaks its pipeline), and its steps ~3500 cycles more
+// (36 class runs per consumer per step); both fitted to imb80/95/99 on MI355X.  Only used to
+// rank the handle's variants.
 double estimate_cycles(const sc::Geom& g, const Variant& v, int N, long long nnz) {
   const sc::Plan& p = v.p;
   const long long ext = (long long)N * g.HYp * g.Pp;
-  const long long units = (ext + 64LL * p.K - 1) / (64LL * p.K) * p.G;
+  const long long units = (ext + p.tp - 1) / p.tp * p.G;
   const long long per_cu = (units + v.cus - 1) / v.cus;
   const double stage = (double)g.C * p.CHS * 4.0 / (g.wide ? 15.0 : 3.7);
-  const double walk = (double)nnz / p.G * p.K * (p.K >= 2 ? 2.3 : 3.0);
-  return 6000.0 + (double)per_cu * (1500.0 * p.nch + std::max(stage, walk));
+  double walk = (double)nnz / p.G * p.K * (p.K >= 2 ? 2.3 : 3.0);
+  double step = 1500.0;
+  if (p.quad) {
+    const double r = std::max(0.05, (double)nnz / ((double)g.M * p.nch * 4.0));
+    walk = (double)nnz / p.G * 7 * 2.3 * (0.70 + 0.334 / r);
+    step += 3500.0;
+  }
+  return 6000.0 + (double)per_cu * (step * p.nch + std::max(stage, walk));
 }
 
 size_t pick_variant(const sc_handle* h, int N) {

@@ -23,8 +23,9 @@
 //              non-zeros for the step, which it loads from global memory 64 entries at a
 //              time (one per lane, one group ahead of the walk) and broadcasts entry by
 //              entry with v_readlane.  Per non-zero each lane does one address add, K LDS
-//              reads 64 words apart and K fp32 FMAs.  It then releases the slot (done
-//              counter).  An entry is 8 bytes {LDS offset, fp32 weight}, or 4 bytes
+//              reads 64 words apart and K fp32 FMAs.  (Quad plans walk differently: four
+//              consecutive positions per lane and entries read from LDS, see the quad walk
+//              below.)  It then releases the slot (done counter).  An entry is 8 bytes {LDS offset, fp32 weight}, or 4 bytes
 //              {LDS offset, fp16 weight} for filter banks packed in the 32-bit word form
 //              (the fp16 weight is widened to fp32 before the FMAs);
 //   store    - after a unit's last chunk, each consumer stores its valid positions with
@@ -42,6 +43,8 @@
 // accumulators (Tuteja et al., Sec. 5.1-5.5); the wave-uniform weight with lanes over
 // consecutive output positions (the thread-per-output dataflow of "Escoin").
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "plan.h"
 #include "xcd.h"
@@ -364,13 +367,15 @@ __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int 
 }
 
 // Output word offset (without the channel term) of each of the lane's K positions, or -1.
-template <int K>
+// Position b of the lane is I0 + lane + 64 b, or in a quad plan I0 + 252 (b / 4) + 4 lane +
+// b % 4 (lane 63 stores nothing).
+template <int K, bool Q>
 __device__ __forceinline__ void output_bases(const KArgs& a, int I0, int lane, int (&ob)[K]) {
 #pragma unroll
   for (int b = 0; b < K; b++) {
-    const long long I = (long long)I0 + lane + 64 * b;
+    const long long I = Q ? (long long)I0 + kQuadBlock * (b >> 2) + 4 * lane + (b & 3) : (long long)I0 + lane + 64 * b;
     ob[b] = -1;
-    if (I < a.ext_total) {
+    if ((!Q || lane < 63) && I < a.ext_total) {
       const int Ii = (int)I;
       const int n = Ii / a.img_ext;
       const int rem = Ii - n * a.img_ext;
@@ -492,6 +497,99 @@ __device__ __forceinline__ void walk_slots(Walk<EF>& w, float (&acc)[OCW][K], co
   }
 }
 
+// Quad walk (quad plans).  Lane l holds positions 4l..4l+3 of two blocks 252 words apart.
+// A non-zero whose LDS offset is enc reads, per block, the aligned quad at word
+// 4l + (enc & ~3) (one 16-byte read) and needs its words j + cls (cls = enc & 3) for
+// positions j: words past 3 are words j + cls - 4 of the next lane's quad, which a DPP FMA
+// (wave_shl:1) takes from lane l + 1.  A slot's non-zeros of a chunk come sorted by class,
+// so each class is a run with a fixed FMA pattern.  Entries {byte offset of the aligned
+// quad, fp32 weight} are read by the whole wave from the consumer's entry ring in LDS (one
+// broadcast read, no v_readlane), and the walk is pipelined: the quads of the next
+// non-zero and the entry after it are read before the current non-zero's FMAs.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// the DPP FMAs of one non-zero of class C (C = 1..3): acc[4b + 4 - C + i] += w * word i of
+// the next lane's quad b.  The s_nop gives the two wait states a DPP read needs after a
+// vector write of any of its registers.
+template <int C>
+__device__ __forceinline__ void quad_dpp(float (&A)[8], const v4f q0, const v4f q1, float w) {
+  if constexpr (C == 1) {
+    asm volatile("s_nop 1\n"
+                 "v_fmac_f32_dpp %0, %2, %4 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %1, %3, %4 wave_shl:1 row_mask:0xf bank_mask:0xf"
+                 : "+v"(A[3]), "+v"(A[7])
+                 : "v"(q0.x), "v"(q1.x), "v"(w));
+  } else if constexpr (C == 2) {
+    asm volatile("s_nop 1\n"
+                 "v_fmac_f32_dpp %0, %4, %8 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %1, %5, %8 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %2, %6, %8 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %3, %7, %8 wave_shl:1 row_mask:0xf bank_mask:0xf"
+                 : "+v"(A[2]), "+v"(A[3]), "+v"(A[6]), "+v"(A[7])
+                 : "v"(q0.x), "v"(q0.y), "v"(q1.x), "v"(q1.y), "v"(w));
+  } else if constexpr (C == 3) {
+    asm volatile("s_nop 1\n"
+                 "v_fmac_f32_dpp %0, %6, %12 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %1, %7, %12 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %2, %8, %12 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %3, %9, %12 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %4, %10, %12 wave_shl:1 row_mask:0xf bank_mask:0xf\n"
+                 "v_fmac_f32_dpp %5, %11, %12 wave_shl:1 row_mask:0xf bank_mask:0xf"
+                 : "+v"(A[1]), "+v"(A[2]), "+v"(A[3]), "+v"(A[5]), "+v"(A[6]), "+v"(A[7])
+                 : "v"(q0.x), "v"(q0.y), "v"(q0.z), "v"(q1.x), "v"(q1.y), "v"(q1.z), "v"(w));
+  }
+}
+
+// The 8 FMAs of one non-zero of class C.
+template <int C>
+__device__ __forceinline__ void quad_fma(float (&A)[8], const v4f q0, const v4f q1, float w) {
+#pragma unroll
+  for (int j = 0; j + C < 4; j++) {
+    A[j] = fmaf(w, q0[j + C], A[j]);
+    A[4 + j] = fmaf(w, q1[j + C], A[4 + j]);
+  }
+  quad_dpp<C>(A, q0, q1, w);
+}
+
+// Pipeline state between runs: the quads and weight of the current non-zero (reads in
+// flight), the entry after it (read in flight) and the index of the entry after that.
+struct QuadPipe {
+  v4f q0, q1;
+  float w;
+  uint2 en;
+  int i;
+};
+
+// lb: the lane's byte address of its first quad in the slot (slot + 16 lane).
+__device__ __forceinline__ void quad_read(const char* lb, uint32_t off, v4f& q0, v4f& q1) {
+  q0 = *reinterpret_cast<const v4f*>(lb + off);
+  q1 = *reinterpret_cast<const v4f*>(lb + off + 4 * kQuadBlock);
+}
+
+// A run of n non-zeros of class C into the slot's accumulators A.  fetch(i) returns entry i
+// of the step's block (already in the ring); the two zero entries that close every block
+// keep the one-ahead reads of the block's last run inside the block.
+template <int C, typename Fetch>
+__device__ __forceinline__ void quad_run(float (&A)[8], QuadPipe& p, const char* lb, int n, Fetch&& fetch) {
+  for (; n >= 2; n -= 2) {
+    v4f b0, b1;
+    quad_read(lb, p.en.x, b0, b1);
+    const float wb = __uint_as_float(p.en.y);
+    p.en = fetch(p.i++);
+    quad_fma<C>(A, p.q0, p.q1, p.w);
+    quad_read(lb, p.en.x, p.q0, p.q1);
+    p.w = __uint_as_float(p.en.y);
+    p.en = fetch(p.i++);
+    quad_fma<C>(A, b0, b1, wb);
+  }
+  if (n) {
+    quad_fma<C>(A, p.q0, p.q1, p.w);
+    quad_read(lb, p.en.x, p.q0, p.q1);
+    p.w = __uint_as_float(p.en.y);
+    p.en = fetch(p.i++);
+  }
+}
+
 // Step iterator over a workgroup's run of units: unit = tile * G + g, then chunk k.
 struct StepIt {
   int tile, g, k;
@@ -531,7 +629,7 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
     }
     if (it.tile != cur_tile) {
       cur_tile = it.tile;
-      I0 = cur_tile * (64 * K);
+      I0 = cur_tile * a.tp;
       n0 = I0 / a.img_ext;
       const long long first = (long long)n0 * a.C * a.HW;
       rsrc = make_rsrc(x + first, (uint32_t)min((a.x_words - first) * 4, 0x7ffffff0LL));
@@ -561,7 +659,7 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
   }
 }
 
-template <int K, int OCW, int NW, typename EF>
+template <int K, int OCW, int NW, typename EF, bool Q>
 __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, const typename EF::T* __restrict__ ent,
                                          const int* bst, const int* __restrict__ slot_row,
                                          const int* __restrict__ slot_comb, StepIt it, int S, const uint32_t* ready,
@@ -606,11 +704,54 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
     const int buf = s % a.D;
     lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
     const float* slot = lds + buf * a.slot_words;
-    Walk<EF> w;
-    w.head = first;
-    w.cur = first;
-    w.r = (OCW + 1) & ~1;
-    walk_slots<K, OCW, EF>(w, acc, slot + lane, next_group);
+    if constexpr (Q) {
+      // the consumer's entry ring: entry i of the step's block sits at i & 127.  Before
+      // each run of at most 64 entries, the groups it reads are copied in (the ring half a
+      // group overwrites held group g - 2, all of whose entries were read before the run),
+      // so the run itself only reads LDS.
+      uint2* ring = reinterpret_cast<uint2*>(lds + a.ring_words) + (threadIdx.x >> 6) * 128;
+      ring[lane] = first;
+      int gi = 0;
+      auto ensure = [&](int last) {
+        while (gi < (last >> 6)) {
+          gi++;
+          ring[((gi & 1) << 6) + lane] = next_group();
+        }
+      };
+      auto fetch = [&](int i) -> uint2 { return ring[i & 127]; };
+      const char* lb = reinterpret_cast<const char*>(slot) + 16 * lane;
+      constexpr int H = (OCW + 1) & ~1;  // header entries: per slot, the four class counts
+      QuadPipe qp;
+      ensure(H + 1);
+      const uint2 e0 = fetch(H);
+      quad_read(lb, e0.x, qp.q0, qp.q1);
+      qp.w = __uint_as_float(e0.y);
+      qp.en = fetch(H + 1);
+      qp.i = H + 2;
+      auto run = [&](auto cls, float (&A)[8], int n) {
+        while (n > 0) {
+          const int t = min(n, 64);
+          ensure(qp.i + t - 1);
+          quad_run<decltype(cls)::value>(A, qp, lb, t, fetch);
+          n -= t;
+        }
+      };
+#pragma unroll
+      for (int o = 0; o < OCW; o++) {
+        const uint32_t c01 = (uint32_t)__builtin_amdgcn_readlane((int)first.x, o);
+        const uint32_t c23 = (uint32_t)__builtin_amdgcn_readlane((int)first.y, o);
+        run(std::integral_constant<int, 0>{}, acc[o], (int)(c01 & 0xffffu));
+        run(std::integral_constant<int, 1>{}, acc[o], (int)(c01 >> 16));
+        run(std::integral_constant<int, 2>{}, acc[o], (int)(c23 & 0xffffu));
+        run(std::integral_constant<int, 3>{}, acc[o], (int)(c23 >> 16));
+      }
+    } else {
+      Walk<EF> w;
+      w.head = first;
+      w.cur = first;
+      w.r = (OCW + 1) & ~1;
+      walk_slots<K, OCW, EF>(w, acc, slot + lane, next_group);
+    }
     // every group of this step's block has been walked: nxt is the next step's first group
     if (s + 1 < S) first = next_group();
     // release the slot's input part (the walk's LDS reads are complete before the add);
@@ -652,7 +793,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
       }
       // ... and the owner of each row adds them in piece order, then stores
       int ob[K];
-      output_bases<K>(a, it.tile * (64 * K), lane, ob);
+      output_bases<K, Q>(a, it.tile * a.tp, lane, ob);
       const int plane = a.E * a.F;
 #pragma unroll
       for (int o = 0; o < OCW; o++) {
@@ -685,7 +826,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
 
 // Pointers are separate restrict-qualified arguments so the compiler knows the streams
 // are read-only.
-template <int K, int OCW, int NW, typename EF>
+template <int K, int OCW, int NW, typename EF, bool Q>
 __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
     const KArgs a, const float* __restrict__ x, float* __restrict__ y,
     const typename EF::T* __restrict__ ent, const int* __restrict__ bstart,
@@ -720,8 +861,8 @@ __global__ __launch_bounds__(NW * 64, 4) void sparse_direct_fwd(
   if (wave == NC)
     producer<K, NW>(a, x, it, S, ready, done, lds, lane);
   else
-    consumer<K, OCW, NW, EF>(a, y, ent, bst, slot_row, slot_comb, it, S, ready, done, pfull, pcons, pbuf, lds, wave,
-                         lane);
+    consumer<K, OCW, NW, EF, Q>(a, y, ent, bst, slot_row, slot_comb, it, S, ready, done, pfull, pcons, pbuf, lds,
+                                wave, lane);
 }
 
 template <typename EF>
@@ -736,7 +877,17 @@ using SparseFn = void (*)(KArgs, const float*, float*, const typename EF::T*, co
 
 template <typename EF>
 static SparseFn<EF> pick_sparse(const Plan& p) {
-#define SC_CASE(KK, OO, WW) if (p.K == KK && p.OCW == OO && p.NW == WW) return sparse_direct_fwd<KK, OO, WW, EF>;
+  if (p.quad) {  // quad kernels: 8-byte entries, K = 8, 3/5/9 slots
+    if constexpr (std::is_same<EF, EntF32>::value) {
+      if (p.K == 8 && p.NW == 16) {
+        if (p.OCW == 3) return sparse_direct_fwd<8, 3, 16, EF, true>;
+        if (p.OCW == 5) return sparse_direct_fwd<8, 5, 16, EF, true>;
+        if (p.OCW == 9) return sparse_direct_fwd<8, 9, 16, EF, true>;
+      }
+    }
+    return nullptr;
+  }
+#define SC_CASE(KK, OO, WW) if (p.K == KK && p.OCW == OO && p.NW == WW) return sparse_direct_fwd<KK, OO, WW, EF, false>;
   SC_FOR_EACH_KO(SC_CASE, 16)
 #undef SC_CASE
   return nullptr;

@@ -34,8 +34,11 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
 }
 
 // Phase-plane words a tile of 64*K extended positions reads: the tile plus the reach of
-// the filter below and to the right of it.
-int plan_pl(const Geom& g, int K) { return 64 * K + (g.Rr - 1) * g.Pp + (g.S - 1) / g.st; }
+// the filter below and to the right of it.  A quad tile (504 positions) reads 508 words
+// plus the reach: lane 63's second quad, whose words only feed lane 62, ends at word 507.
+int plan_pl(const Geom& g, int K, int quad) {
+  return (quad ? kQuadTile + 4 : 64 * K) + (g.Rr - 1) * g.Pp + (g.S - 1) / g.st;
+}
 
 static int env_int(const char* s, const char* key, int dflt) {
   if (!s) return dflt;
@@ -232,7 +235,8 @@ static bool fill_layout(const Geom& g, int K, int D, int cc_cap, int lds_max, Pl
   const int NC = p->NW - 1;
   p->K = K;
   p->D = D;
-  p->PL = plan_pl(g, K);
+  p->PL = plan_pl(g, K, p->quad);
+  p->tp = p->quad ? kQuadTile : 64 * K;
   // stride > 1: phase planes start on 64-word blocks, so that no staging block straddles two
   // planes and the producer can step its offsets from plane to plane without divisions
   if (g.st > 1) p->PL = (p->PL + 63) / 64 * 64;
@@ -243,7 +247,8 @@ static bool fill_layout(const Geom& g, int K, int D, int cc_cap, int lds_max, Pl
   p->nblk = p->CHS / 64;
   int nch = 1;
   for (int it = 0; it < 16; it++) {  // the block-start table grows with the chunk count
-    const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth + 8LL * p->nbuf + 256LL * p->nbuf * K;
+    const long long fixed = 4LL * p->G * NC * (nch + 1) + 8LL * kMaxDepth + 8LL * p->nbuf + 256LL * p->nbuf * K +
+                            (p->quad ? 16LL + (long long)kQuadRingBytes * NC : 0);
     const long long room = (lds_max - fixed) / (4LL * D);  // input words per slot
     if (room < p->CHS) return false;
     int cc = (int)std::min<long long>(g.C, room / p->CHS);
@@ -309,7 +314,8 @@ static int max_block(const Geom& g, const Plan& p, const std::vector<int32_t>& r
 // a step ahead of the slowest) share the CU's LDS with the counters and the block-start
 // table; large chunks mean few steps.
 // SPARSECONV_PLAN="K=..,OCW=..,D=..,CC=..,LDSKB=..,NARROW" overrides the choice (tuning only).
-static bool instantiated(int K, int OCW) {
+static bool instantiated(int K, int OCW, int quad) {
+  if (quad) return K == 8 && (OCW == 3 || OCW == 5 || OCW == 9);
   static const int kk[] = {1, 2, 4, 6, 7, 8, 12, 16};
   static const int oo[] = {1, 2, 3, 5, 9};
   bool okk = false, oko = false;
@@ -319,12 +325,15 @@ static bool instantiated(int K, int OCW) {
 }
 
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched, int k_cap, int ocw_cap, int d) {
+                 Sched* sched, int k_cap, int ocw_cap, int d, int quad) {
   static const int kOcw[] = {1, 2, 3, 5, 9};
   static const int kKs[] = {16, 12, 8, 7, 6, 4, 2, 1};
   Plan p{};
   p.NW = 16;
   const int NC = p.NW - 1;
+  const char* env0 = std::getenv("SPARSECONV_PLAN");
+  if (env_int(env0, "QUAD", -1) >= 0) quad = env_int(env0, "QUAD", 0) ? 1 : 0;  // tuning only
+  p.quad = quad;
   const long long img_ext = (long long)g.HYp * g.Pp;
   const int kmax = img_ext >= 4096 ? 8 : img_ext >= 1024 ? 4 : img_ext >= 256 ? 2 : 1;
   // slots for every row plus the extra pieces of rows longer than a consumer's fair share
@@ -352,6 +361,7 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
   bool oko = false;
   for (int o : kOcw) oko = oko || o == OCW;
   if (!oko) OCW = 9;
+  if (quad && OCW < 3) OCW = 3;  // quad kernels exist for 3, 5 and 9 slots
   if (ocw_cap > 0 && OCW > ocw_cap) {  // the largest instantiated count within the cap
     int best = kOcw[0];
     for (int o : kOcw)
@@ -364,8 +374,8 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
     p.OCW = kOcw[oi];
     p.G = (g.M + NC * p.OCW - 1) / (NC * p.OCW);
     for (int k : kKs) {
-      if (!instantiated(k, p.OCW)) continue;
-      if (k > (kenv > 0 ? kenv : k_cap > 0 ? std::min(kmax, k_cap) : kmax)) continue;
+      if (!instantiated(k, p.OCW, quad)) continue;
+      if (!quad && k > (kenv > 0 ? kenv : k_cap > 0 ? std::min(kmax, k_cap) : kmax)) continue;
       bool fits = true;
       Sched sc;
       p.nbuf = 0;
@@ -383,6 +393,11 @@ Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::v
       p.nbuf = sc.nbuf;
       const int table = p.G * NC * (p.nch + 1);
       p.lds_bytes = 4 * p.D * p.slot_words + 8 * kMaxDepth + 4 * table + 8 * p.nbuf + 4 * p.nbuf * 64 * k;
+      p.ring_words = 0;
+      if (quad) {  // 16-byte aligned entry rings after everything else
+        p.ring_words = (p.lds_bytes / 4 + 3) & ~3;
+        p.lds_bytes = 4 * p.ring_words + kQuadRingBytes * NC;
+      }
       if (p.lds_bytes > lds_max) continue;
       p.span_images = (int)((p.PL + img_ext - 2) / img_ext + 1);
       if (sched) *sched = std::move(sc);

@@ -17,7 +17,7 @@
 //    to consecutive LDS words for every tap.  Positions with e >= E or f >= F are junk
 //    (computed, never stored).
 //  * A workgroup owns a tile of 64*K consecutive extended indices [I0, I0 + 64K) (K per
-//    lane, 64 apart).  For every phase plane it stages exactly the range the tile's taps
+//    lane, 64 apart; quad plans below: 504).  For every phase plane it stages exactly the range the tile's taps
 //    read, PL = 64K + (Rr-1)*Pp + (S-1)/st consecutive phase-plane words starting at I0
 //    (rows of the next image and padding included as zeros; for stride > 1 PL is rounded up
 //    to a multiple of 64, so every 64-word block lies in one phase plane), for Cc channels
@@ -31,6 +31,14 @@
 //    so lane l, position b reads LDS word enc + l + 64*b: one address add, K LDS reads 64
 //    words apart and K FMAs per non-zero.  enc < slot_words < 2^16, so it also fits the
 //    16-bit field of the 4-byte entry form.
+//  * Quad plans (Plan::quad): lane l holds the 4 consecutive positions 4l..4l+3 of two
+//    blocks 252 apart, so a tile is 504 positions (lane 63 computes junk that is never
+//    stored: its words only feed lane 62 through a one-lane shift).  A non-zero's words for
+//    the lane are then the aligned quad at word 4l + (enc & ~3) shifted by enc & 3 (the
+//    tap's class): two 16-byte LDS reads per non-zero, the shifted words taken from the next
+//    lane's quad by a DPP FMA.  Each slot's non-zeros of a chunk are sorted by class, the
+//    header gives the four class counts, and an entry holds the byte offset of its aligned
+//    quad.  PL = 508 + (Rr-1)*Pp + (S-1)/st covers lane 63's reads.
 #pragma once
 #include <cstdint>
 #include <vector>
@@ -70,7 +78,15 @@ struct Plan {
   int nbuf;        // LDS partial-sum buffers per workgroup (pieces of split rows)
   int h16;         // entry format: 0 {LDS offset, fp32 weight} (8 bytes), 1 fp16 weight in
                    // bits 15..0 and the LDS offset in bits 31..16 (4 bytes)
+  int quad;        // 1: quad plan (K = 8: two blocks of 4 consecutive positions per lane)
+  int tp;          // extended positions per tile: 64*K, or kQuadTile for quad plans
+  int ring_words;  // quad plans: LDS word offset of the consumers' entry rings (a multiple
+                   // of 4; each consumer has 128 entries of 8 bytes there)
 };
+
+constexpr int kQuadTile = 504;        // 63 lanes x 4 positions x 2 blocks
+constexpr int kQuadBlock = 252;       // words between a lane's two quads
+constexpr int kQuadRingBytes = 1024;  // per consumer: two groups of 64 entries
 
 // Row schedule.  A row longer than a consumer's fair share of a group's non-zeros is split
 // into pieces held by different consumers of its group: in every chunk, piece p of P takes
@@ -113,7 +129,9 @@ struct KArgs {
   int PL, CHS, nblk, Cc, nch, G, D, slot_words;
   int nbuf;               // partial-sum buffers (split rows)
   int HW;                 // H * W
-  int ntiles;             // tiles of 64*K extended positions
+  int ntiles;             // tiles of tp extended positions
+  int tp;                 // extended positions per tile (Plan::tp)
+  int ring_words;         // quad plans: LDS word offset of the entry rings (Plan::ring_words)
   long long x_words;      // N * C * H * W
   long long ext_total;    // N * img_ext
 };
@@ -122,9 +140,10 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
 // Launch plan for the CSR filter matrix (rowptr, col): also schedules rows onto wavefront
 // slots (slot_row) and sizes each wavefront's per-chunk block of non-zeros.
 // k_cap / ocw_cap > 0 cap K and OCW; d > 0 sets the ring depth (default 3).
+// quad = 1 asks for a quad plan (K = 8, OCW of 3, 5 or 9).
 Plan choose_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 Sched* sched, int k_cap = 0, int ocw_cap = 0, int d = 0);
-int plan_pl(const Geom& g, int K);
+                 Sched* sched, int k_cap = 0, int ocw_cap = 0, int d = 0, int quad = 0);
+int plan_pl(const Geom& g, int K, int quad = 0);
 
 // Header entries at the start of a wavefront's per-chunk block of non-zeros.
 int block_header(int OCW);
