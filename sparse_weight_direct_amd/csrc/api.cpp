@@ -606,10 +606,10 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
 // times a unit's cost, the larger of its input copy (LDS DMA at ~15 B/cycle with 16-byte
 // loads, ~3.7 with 4-byte ones) and its walk (~2.3 cycles per non-zero and 64-position block
 // of LDS reads), plus a fixed cost per chunk step and per launch.  A quad plan's walk costs
-// 0.70 + 0.334 / r of a K = 7 walk per non-zero, r being the mean run of one class of one
-// slot in one chunk (a run boundary breaks its pipeline), and its steps ~3500 cycles more
-// (36 class runs per consumer per step); both fitted to imb80/95/99 on MI355X.  Only used to
-// rank the handle's variants.
+// 0.83 + 0.30 / r of a K = 7 walk per non-zero, r being the mean run of one class of one slot
+// in one chunk (a run boundary breaks its pipeline), and its steps ~1000 cycles more (36 class
+// runs per consumer per step); both fitted to imb80/95/99 on MI355X.  Only used to rank the
+// handle's variants.
 double estimate_cycles(const sc::Geom& g, const Variant& v, int N, long long nnz) {
   const sc::Plan& p = v.p;
   const long long ext = (long long)N * g.HYp * g.Pp;
@@ -620,8 +620,8 @@ double estimate_cycles(const sc::Geom& g, const Variant& v, int N, long long nnz
   double step = 1500.0;
   if (p.quad) {
     const double r = std::max(0.05, (double)nnz / ((double)g.M * p.nch * 4.0));
-    walk = (double)nnz / p.G * 7 * 2.3 * (0.70 + 0.334 / r);
-    step += 3500.0;
+    walk = (double)nnz / p.G * 7 * 2.3 * (0.83 + 0.30 / r);
+    step += 1000.0;
   }
   return 6000.0 + (double)per_cu * (step * p.nch + std::max(stage, walk));
 }

@@ -366,16 +366,18 @@ __device__ __forceinline__ int stage_rows(const KArgs& a, v4i rsrc, int I0, int 
   return a.nsb * ncl;
 }
 
-// Output word offset (without the channel term) of each of the lane's K positions, or -1.
-// Position b of the lane is I0 + lane + 64 b, or in a quad plan I0 + 252 (b / 4) + 4 lane +
-// b % 4 (lane 63 stores nothing).
+// Output word offset (without the channel term) of each of the lane's K store positions, or
+// -1.  Store b of the lane writes position I0 + lane + 64 b, or in a quad plan
+// I0 + 252 (b / 4) + lane + 64 (b % 4) (positions past 251 of a block are lane 63's junk):
+// quad results are transposed through LDS first, so that the stores stay lane-consecutive.
 template <int K, bool Q>
 __device__ __forceinline__ void output_bases(const KArgs& a, int I0, int lane, int (&ob)[K]) {
 #pragma unroll
   for (int b = 0; b < K; b++) {
-    const long long I = Q ? (long long)I0 + kQuadBlock * (b >> 2) + 4 * lane + (b & 3) : (long long)I0 + lane + 64 * b;
+    const int in_block = lane + 64 * (Q ? (b & 3) : b);
+    const long long I = Q ? (long long)I0 + kQuadBlock * (b >> 2) + in_block : (long long)I0 + in_block;
     ob[b] = -1;
-    if ((!Q || lane < 63) && I < a.ext_total) {
+    if ((!Q || in_block < kQuadBlock) && I < a.ext_total) {
       const int Ii = (int)I;
       const int n = Ii / a.img_ext;
       const int rem = Ii - n * a.img_ext;
@@ -811,9 +813,31 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
           }
           // ordinary (write-back) stores: the partial 64-byte segments at output-row and tile
           // boundaries are merged in L2 instead of being written to HBM separately
+          if constexpr (Q) {
+            // a quad lane holds positions 4l..4l+3 of each block: transpose each block through
+            // this consumer's entry ring (1 KB, idle once the unit's last walk is issued; the
+            // wave's LDS accesses complete in order), then store position l + 64k from lane l
+            float* tb = reinterpret_cast<float*>(lds + a.ring_words) + (threadIdx.x >> 6) * 256;
 #pragma unroll
-          for (int q = 0; q < K; q++)
-            if (ob[q] >= 0) y[ob[q] + row * plane] = acc[o][q];
+            for (int b = 0; b < 2; b++) {
+              v4f v;
+              v.x = acc[o][4 * b];
+              v.y = acc[o][4 * b + 1];
+              v.z = acc[o][4 * b + 2];
+              v.w = acc[o][4 * b + 3];
+              *reinterpret_cast<v4f*>(tb + 4 * lane) = v;
+              float t[4];
+#pragma unroll
+              for (int k = 0; k < 4; k++) t[k] = tb[lane + 64 * k];
+#pragma unroll
+              for (int k = 0; k < 4; k++)
+                if (ob[4 * b + k] >= 0) y[ob[4 * b + k] + row * plane] = t[k];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < K; q++)
+              if (ob[q] >= 0) y[ob[q] + row * plane] = acc[o][q];
+          }
         }
 #pragma unroll
         for (int q = 0; q < K; q++) acc[o][q] = 0.0f;
