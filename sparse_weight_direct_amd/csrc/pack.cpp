@@ -24,7 +24,11 @@ bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* 
   g->F = (int)((wp - S) / st + 1);
   g->HYp = (int)((hp + st - 1) / st);
   g->Rr = (R - 1) / st + 1;
-  g->wide = (st == 1 && W % 4 == 0 && pad <= 2) ? 1 : 0;
+  // wide layout: input column x at phase column x + 4 in rows of W + 4 words, output column f
+  // at extended column f + 4 - pad.  The last output column F - 1 = W + 2 pad - S fits in the
+  // row only if pad < S, and the right padding wraps into the next row's 4 zero columns only
+  // if pad <= 2 (pad <= 4 would do; 2 keeps the halo small)
+  g->wide = (st == 1 && W % 4 == 0 && pad <= 2 && pad < S) ? 1 : 0;
   if (const char* e = std::getenv("SPARSECONV_PLAN"))
     if (std::strstr(e, "NARROW")) g->wide = 0;  // tuning only
   g->xoff = g->wide ? 4 : pad;

@@ -6,7 +6,7 @@
 //    position (yp, xp) lands in phase (yp % st, xp % st) at phase coordinates
 //    (yp / st, xp / st).  A phase plane has HYp = ceil((H+2p)/st) rows of Pp = ceil((W+2p)/st)
 //    words.  For stride 1 this is just the zero-padded image.
-//  * Wide layout (stride 1, W % 4 == 0, pad <= 2): input column x sits at phase column x + 4
+//  * Wide layout (stride 1, W % 4 == 0, pad <= 2, pad < S): input column x sits at phase column x + 4
 //    and Pp = W + 4, so every aligned group of 4 words is 4 input words or 4 zeros and can be
 //    copied with 16-byte loads; output column f then sits at extended column f + 4 - pad.
 //    In general input column x sits at phase column (x + xoff) / st (xoff = pad, or 4 in the

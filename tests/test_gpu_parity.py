@@ -136,6 +136,23 @@ def test_persistent_runs_of_many_units(plan, monkeypatch):
     assert_parity(y, r["y64"], r["mag"], plan)
 
 
+@pytest.mark.parametrize("plan", ["", "QUAD=1", "K=8,OCW=5", "NARROW"])
+@pytest.mark.parametrize("N,C,H,W,M,R,S,pad", [(1, 62, 37, 20, 114, 3, 1, 1), (1, 16, 26, 32, 123, 1, 1, 1),
+                                               (4, 20, 6, 12, 87, 1, 2, 2), (2, 8, 9, 16, 20, 2, 2, 2),
+                                               (2, 8, 9, 16, 20, 1, 3, 2)])
+def test_padding_at_least_the_filter_width(N, C, H, W, M, R, S, pad, plan, monkeypatch):
+    """Stride 1, W % 4 == 0 and pad >= S: the output is wider than the input (F = W + 2 pad -
+    S + 1 > W), so the last output columns lie past the input row.  (The 16-byte staging
+    layout cannot hold them and must not be used; these shapes once left the last column
+    unwritten.)  The last case has pad < S for contrast."""
+    if plan:
+        monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    d = workloads.make_custom(N, C, H, W, M, R, S, 1, pad, 0.1, 9100 + W + S)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, pad)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, pad)
+    assert_parity(y, r["y64"], r["mag"], f"pad {pad} S {S} {plan}")
+
+
 @pytest.mark.parametrize("R,S,stride,pad,H,W", [(3, 3, 1, 1, 30, 41), (11, 11, 4, 0, 67, 59), (5, 3, 2, 2, 17, 23),
                                                 (1, 1, 1, 0, 7, 7)])
 def test_single_nonzero_bit_exact(R, S, stride, pad, H, W):
