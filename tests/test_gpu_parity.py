@@ -309,3 +309,58 @@ def test_side_stream():
     with torch.cuda.stream(s):
         y, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, stream=s)
     assert_parity(y, r["y64"], r["mag"], "stream")
+
+
+def _sweep_cases(count, seed):
+    """Seeded shapes over wide ranges: filters 1..11 (R != S), stride 1..4, pad 0..3, 1..300
+    channels, densities 0..1, one dense row in some (split across wavefronts)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        R = int(rng.choice([1, 1, 2, 3, 3, 3, 5, 7, 11]))
+        S = int(rng.choice([1, 1, 2, 3, 3, 3, 5, 7, 11]))
+        st, pad = int(rng.integers(1, 5)), int(rng.integers(0, 4))
+        H = int(rng.integers(max(1, R - 2 * pad), 36))
+        W = int(rng.integers(max(1, S - 2 * pad), 36))
+        N = int(rng.integers(1, 6))
+        C = int(rng.choice([1, 3, 16, 40, 130, 300]))
+        M = int(rng.choice([1, 7, 33, 140, 300]))
+        keep = float(rng.choice([0.0, 0.01, 0.05, 0.2, 0.6, 1.0]))
+        dense_row = int(rng.integers(0, M)) if (rng.random() < 0.3 and M > 2) else -1
+        E, F = (H + 2 * pad - R) // st + 1, (W + 2 * pad - S) // st + 1
+        if C * M * R * S > 400_000 or N * C * H * W > 200_000 or N * M * E * F > 300_000:
+            continue
+        if (keep * C * M * R * S + C * R * S) * N * E * F > 5e7:  # keeps the oracle quick
+            continue
+        out.append((N, C, H, W, M, R, S, st, pad, keep, dense_row, seed * 1000 + len(out)))
+    return out
+
+
+@pytest.mark.parametrize("plan", ["", "QUAD=1"])
+def test_random_sweep_wide_ranges(plan, monkeypatch):
+    """150 seeded shapes per plan kind against the oracle, failures listed together (a sweep
+    like this one found the wide-layout bug with pad >= S).  A forced quad plan may not fit
+    the LDS on large stride-4 phase planes; such shapes are refused at pack (SC_EUNSUPPORTED)
+    and skipped, the default plans must take every shape."""
+    if plan:
+        monkeypatch.setenv("SPARSECONV_PLAN", plan)
+    failures, ran = [], 0
+    for c in _sweep_cases(150, 4711):
+        N, C, H, W, M, R, S, st, pad, keep, dense_row, seed = c
+        d = workloads.make_custom(N, C, H, W, M, R, S, st, pad, keep, seed)
+        mask = d["mask"].copy()
+        if dense_row >= 0:
+            mask[dense_row] = 1
+        try:
+            y, _ = gpu_sparse(d["x"], d["w"], mask, st, pad)
+        except sc.SparseConvError as e:
+            if plan and e.status == sc.SC_EUNSUPPORTED:
+                continue
+            raise
+        ran += 1
+        r = oracle.reference(d["x"], d["w"], mask, st, pad)
+        ok = oracle.within_tolerance(y, r["y64"], r["mag"], 1e-5)
+        if not ok.all():
+            failures.append((c, int((~ok).sum())))
+    assert ran >= 140, ran
+    assert not failures, failures[:5]
