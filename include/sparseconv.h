@@ -87,6 +87,26 @@ typedef enum {
                                 SC_PACK_FP16_WORD (SC_EINVAL).  Limit: C*(H+2pad)*(W+2pad) <
                                 2^30 (SC_EUNSUPPORTED). */
 
+#define SC_PACK_LDS_TILE 16u  /* use the LDS-tile kernel for fp32 weights instead of the default
+                                weights-in-code kernel (below).  Not combinable with
+                                SC_PACK_ESCOIN_MAP (SC_EINVAL). */
+/*
+ * Default mapping for fp32 weights (no SC_PACK_LDS_TILE, SC_PACK_ESCOIN_MAP, SC_PACK_FP16_WORD
+ * or SC_PACK_ALL_TAPS): the weights-in-code kernel.  Pack writes the layer's non-zeros into
+ * the instruction stream of a gfx950 kernel generated for this layer (one FMA with the weight
+ * as a 32-bit literal per non-zero; the output channel's accumulator register and the filter
+ * tap's input register fixed in the instruction), assembles it in-process (amd_comgr) and
+ * loads it on the current device (hipModuleLoadData).  A wavefront holds the accumulators of
+ * all output channels of one group for 64 - (S-1)/stride consecutive output positions and
+ * reads each input row vector once for all of them (Tuteja et al., Sec. 5.1: one input region,
+ * reused by every output channel).  The stretched offsets of "Escoin" (weight stretching)
+ * appear as the channel's scalar offset c*H*W plus the row vector's lane offset r*W + s.
+ * sc_info.mapping is 2 for such handles and bake_* describe the kernel;
+ * sparseconv_export_kernel_source returns its assembly.  If the layer does not fit the
+ * mapping (too many output channels per group for the registers), pack uses the LDS-tile
+ * kernel; a batch whose input or output exceeds 2^31 bytes runs on the LDS-tile kernel too.
+ */
+
 typedef struct {
   int32_t format;          /* sc_weights_format */
   const float* values;     /* host.  DENSE: M*C*R*S values.  CSR: nnz values (row order) */
@@ -135,7 +155,17 @@ typedef struct {
                             weight}), or 4 ({LDS offset, fp16 weight}) with SC_PACK_FP16_WORD */
   int32_t mapping;       /* 0: LDS-tile kernel (the plan fields above); 1: SC_PACK_ESCOIN_MAP
                             (tile_pixels = output positions per workgroup, lds_bytes = its
-                            row buffer, max_wave_nnz = the longest row) */
+                            row buffer, max_wave_nnz = the longest row); 2: weights-in-code
+                            kernel (the bake_* fields; the plan fields above then describe
+                            the handle's LDS-tile plans, used only for batches too large for
+                            the weights-in-code kernel) */
+  int32_t bake_groups;      /* weights-in-code: output-channel groups (one code section each) */
+  int32_t bake_valid_lanes; /* weights-in-code: output positions per wavefront, 64 - (S-1)/stride */
+  int32_t bake_pitch;       /* weights-in-code: extended row pitch F + (S-1)/stride */
+  int32_t bake_wpb;         /* weights-in-code: wavefronts per workgroup */
+  int32_t bake_depth;       /* weights-in-code: filter-row steps of input loads in flight */
+  int32_t bake_vgprs;       /* weights-in-code: VGPRs per lane */
+  int64_t bake_code_bytes;  /* weights-in-code: bytes of generated code */
 } sc_info;
 
 /*
@@ -220,6 +250,15 @@ sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t
  * be NULL.  SC_EINVAL on a NULL handle or one packed without SC_PACK_FP16_WORD.
  */
 sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t* words);
+
+/*
+ * Copy out the assembly of the handle's weights-in-code kernel (for inspection and the CPU
+ * checks of the generated code): *len receives its length plus one; up to cap - 1 bytes and
+ * a terminating NUL are written to buf (host, owned by the caller; may be NULL to query the
+ * length).  SC_EINVAL on a NULL handle or len, or a handle without such a kernel (the message
+ * says why the layer was not baked).
+ */
+sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t cap, int64_t* len);
 
 /* Free the handle and its device buffers.  NULL is a no-op.  Must not race a forward
  * still running on the device that reads this handle (synchronise the stream first). */

@@ -39,12 +39,14 @@ SC_PACK_HOST_ONLY = 1
 SC_PACK_ALL_TAPS = 2
 SC_PACK_FP16_WORD = 4
 SC_PACK_ESCOIN_MAP = 8
+SC_PACK_LDS_TILE = 16
+MAPPING_LDS_TILE, MAPPING_ESCOIN, MAPPING_BAKED = 0, 1, 2
 _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: "SC_EDEVICE",
                  5: "SC_EUNSUPPORTED"}
 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
-            "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words", "sparseconv_destroy",
-            "sparseconv_last_error")
+            "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
+            "sparseconv_export_kernel_source", "sparseconv_destroy", "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -58,7 +60,10 @@ class sc_info(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels",
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
                                                "pipeline_depth", "step_balance_permille",
-                                               "split_pieces", "plan_variants", "entry_bytes", "mapping")]
+                                               "split_pieces", "plan_variants", "entry_bytes", "mapping",
+                                               "bake_groups", "bake_valid_lanes", "bake_pitch", "bake_wpb",
+                                               "bake_depth", "bake_vgprs")] + \
+               [("bake_code_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -79,6 +84,8 @@ _lib.sparseconv_export_packed.restype = _i32
 _lib.sparseconv_export_packed.argtypes = [_vp, _vp, _vp, _vp]
 _lib.sparseconv_export_words.restype = _i32
 _lib.sparseconv_export_words.argtypes = [_vp, _vp, _vp]
+_lib.sparseconv_export_kernel_source.restype = _i32
+_lib.sparseconv_export_kernel_source.argtypes = [_vp, ctypes.c_char_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -198,6 +205,16 @@ def sparseconv_export_words(handle: int):
     return rowptr, words
 
 
+def sparseconv_export_kernel_source(handle: int) -> str:
+    """Assembly of the handle's weights-in-code kernel."""
+    n = ctypes.c_int64()
+    _check(_lib.sparseconv_export_kernel_source(handle, None, 0, ctypes.byref(n)), "sparseconv_export_kernel_source")
+    buf = ctypes.create_string_buffer(n.value)
+    _check(_lib.sparseconv_export_kernel_source(handle, buf, n.value, ctypes.byref(n)),
+           "sparseconv_export_kernel_source")
+    return buf.value.decode()
+
+
 def sparseconv_destroy(handle) -> None:
     _lib.sparseconv_destroy(handle)
 
@@ -229,6 +246,9 @@ class Handle:
 
     def export_words(self):
         return sparseconv_export_words(self.ptr)
+
+    def kernel_source(self) -> str:
+        return sparseconv_export_kernel_source(self.ptr)
 
     def workspace_size(self, N: int) -> int:
         return sparseconv_workspace_size(self.ptr, N)

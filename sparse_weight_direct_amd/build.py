@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparseconv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "escoin.hip", "pack.cpp", "api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "escoin.hip", "pack.cpp", "bake.cpp", "api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 instructions are disabled for all device code: hipcc would otherwise form
@@ -40,7 +40,9 @@ def build(verbose: bool = False) -> str:
         if out.strip():
             msgs.append(out)
     tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp])
+    # amd_comgr assembles the weights-in-code kernels at pack time
+    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
+                   ["-L/opt/rocm/lib", "-lamd_comgr", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{out}")
     if verbose and (msgs or out.strip()):

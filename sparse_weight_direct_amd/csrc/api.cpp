@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "../../include/sparseconv.h"
+#include "bake.h"
 #include "plan.h"
 
 namespace {
@@ -78,6 +79,14 @@ struct sc_handle {
   bool host_only;
   void* dmem;
   size_t dbytes;
+  // weights-in-code mapping (bake.h): the generated kernel, its code object and module
+  bool baked;
+  sc::BakePlan bake;
+  std::string bake_src;
+  std::vector<char> bake_elf;
+  std::string bake_why;           // why the layer was not baked ("" if it was)
+  hipModule_t bake_mod;
+  hipFunction_t bake_fn;
 };
 
 namespace {
@@ -201,8 +210,10 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
   if (!out) return fail(SC_EINVAL, "out is NULL");
   *out = nullptr;
   if (!w) return fail(SC_EINVAL, "weights descriptor is NULL");
-  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS | SC_PACK_FP16_WORD | SC_PACK_ESCOIN_MAP))
+  if (flags & ~(SC_PACK_HOST_ONLY | SC_PACK_ALL_TAPS | SC_PACK_FP16_WORD | SC_PACK_ESCOIN_MAP | SC_PACK_LDS_TILE))
     return fail(SC_EINVAL, "unknown pack flag");
+  if ((flags & SC_PACK_ESCOIN_MAP) && (flags & SC_PACK_LDS_TILE))
+    return fail(SC_EINVAL, "SC_PACK_ESCOIN_MAP and SC_PACK_LDS_TILE select different mappings");
   const bool h16 = (flags & SC_PACK_FP16_WORD) != 0;
   const bool escoin = (flags & SC_PACK_ESCOIN_MAP) != 0;
   if (h16 && escoin) return fail(SC_EINVAL, "SC_PACK_FP16_WORD and SC_PACK_ESCOIN_MAP cannot be combined");
@@ -275,11 +286,39 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
           vars.push_back(std::move(v));
       }
     }
-    if (vars.empty() && !escoin)
+    // weights-in-code kernel (bake.h): the default mapping for fp32 weights, unless the
+    // caller asks for the LDS-tile kernel, forces one of its plans (SPARSECONV_PLAN), or
+    // turns baking off (SPARSECONV_BAKE=off)
+    bool baked = false;
+    sc::BakePlan bake_plan;
+    std::string bake_src, bake_why;
+    std::vector<char> bake_elf;
+    {
+      const char* plan_env = std::getenv("SPARSECONV_PLAN");
+      const char* bake_env = std::getenv("SPARSECONV_BAKE");
+      if (escoin) bake_why = "SC_PACK_ESCOIN_MAP";
+      else if (flags & SC_PACK_LDS_TILE) bake_why = "SC_PACK_LDS_TILE";
+      else if (flags & SC_PACK_ALL_TAPS) bake_why = "SC_PACK_ALL_TAPS (every tap: the code would not fit the caches)";
+      else if (h16) bake_why = "SC_PACK_FP16_WORD (the kernel reads the 32-bit words)";
+      else if (plan_env && plan_env[0]) bake_why = "SPARSECONV_PLAN forces an LDS-tile plan";
+      else if (bake_env && std::strcmp(bake_env, "off") == 0) bake_why = "SPARSECONV_BAKE=off";
+      else if (sc::bake_choose(g, rowptr, col, sc::bake_force_from_env(), &bake_plan, &bake_why) &&
+               sc::bake_generate(g, rowptr, col, val, &bake_plan, &bake_src, &bake_why) &&
+               sc::bake_assemble(bake_src, &bake_elf, &bake_why))
+        baked = true;
+    }
+    if (vars.empty() && !escoin && !baked)
       return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
     h->magic = kMagic;
+    h->baked = baked;
+    h->bake = std::move(bake_plan);
+    h->bake_src = std::move(bake_src);
+    h->bake_elf = std::move(bake_elf);
+    h->bake_why = std::move(bake_why);
+    h->bake_mod = nullptr;
+    h->bake_fn = nullptr;
     h->g = g;
     h->nnz = nnz;
     h->h16 = h16;
@@ -477,6 +516,18 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         base += b_ent + b_seg + b_slot + b_comb;
       }
     }
+    if (h->baked && !h->host_only) {
+      if (hipModuleLoadData(&h->bake_mod, h->bake_elf.data()) != hipSuccess) {
+        h->bake_mod = nullptr;
+        sparseconv_destroy(h);
+        return fail(SC_EDEVICE, "loading the weights-in-code kernel failed (hipModuleLoadData)");
+      }
+      if (hipModuleGetFunction(&h->bake_fn, h->bake_mod, "sc_baked") != hipSuccess) {
+        sparseconv_destroy(h);
+        return fail(SC_EDEVICE, "weights-in-code kernel symbol not found (hipModuleGetFunction)");
+      }
+      std::vector<char>().swap(h->bake_elf);
+    }
     for (Variant& v : h->var) {  // the host copies are not needed any more
       std::vector<uint32_t>().swap(v.ent);
       std::vector<int32_t>().swap(v.bstart);
@@ -504,7 +555,16 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->packed_bytes = ((h->h16 ? 1 : 2) * h->nnz + h->g.M + 1) * 4;
   info->device_bytes = (int64_t)h->dbytes;
   info->entry_bytes = h->h16 ? 4 : 8;
-  info->mapping = h->escoin ? 1 : 0;
+  info->mapping = h->escoin ? 1 : h->baked ? 2 : 0;
+  if (h->baked) {
+    info->bake_groups = h->bake.G;
+    info->bake_valid_lanes = h->bake.V;
+    info->bake_pitch = h->bake.Pb;
+    info->bake_wpb = h->bake.WPB;
+    info->bake_depth = h->bake.D;
+    info->bake_vgprs = h->bake.vgprs;
+    info->bake_code_bytes = h->bake.code_bytes;
+  }
   if (h->escoin) {
     info->tile_pixels = 256 * sc::kEscoinP;
     info->rows_per_wave = 1;
@@ -517,6 +577,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
     info->max_wave_nnz = (int32_t)longest;
     return SC_OK;
   }
+  if (h->var.empty()) return SC_OK;  // baked only: no LDS-tile plan fits this layer
   const Variant& v = h->var[0];  // the default plan
   info->tile_pixels = v.p.tp;
   info->waves_per_group = v.p.NW - 1;
@@ -550,8 +611,23 @@ sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t*
   return SC_OK;
 }
 
+sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t cap, int64_t* len) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!len) return fail(SC_EINVAL, "len is NULL");
+  if (!h->baked) return fail(SC_EINVAL, "handle holds no weights-in-code kernel: " + h->bake_why);
+  *len = (int64_t)h->bake_src.size() + 1;
+  if (buf && cap > 0) {
+    const size_t n = std::min<size_t>((size_t)cap - 1, h->bake_src.size());
+    std::memcpy(buf, h->bake_src.data(), n);
+    buf[n] = '\0';
+  }
+  return SC_OK;
+}
+
 void sparseconv_destroy(sc_handle* h) {
   if (!h || h->magic != kMagic) return;
+  if (h->bake_mod) (void)hipModuleUnload(h->bake_mod);
   if (h->dmem) (void)hipFree(h->dmem);
   h->magic = kDead;
   delete h;
@@ -683,6 +759,38 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
     if (e != (int)hipSuccess)
       return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
     return SC_OK;
+  }
+  if (h->baked) {
+    const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
+    const long long qtot = (long long)N * g.E * h->bake.Pb;
+    if (nin * 4 < (1LL << 31) && nout * 4 < (1LL << 31) && qtot < (1LL << 31) - 128) {
+      if (!input || !output) return fail(SC_EINVAL, "input or output is NULL");
+      if (ranges_overlap(input, nin * 4, output, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
+      if ((reinterpret_cast<uintptr_t>(input) & 3) || (reinterpret_cast<uintptr_t>(output) & 3))
+        return fail(SC_EINVAL, "input or output is not 4-byte aligned");
+      if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+        return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+      const sc::BakePlan& bp = h->bake;
+      sc::BakeArgs a{};
+      a.x = reinterpret_cast<uint64_t>(input);
+      a.y = reinterpret_cast<uint64_t>(output);
+      a.N = (uint32_t)N;
+      a.qtot = (uint32_t)qtot;
+      a.ntiles = (uint32_t)((qtot + bp.V - 1) / bp.V);
+      a.x_bytes = (uint32_t)(nin * 4);
+      a.y_bytes = (uint32_t)(nout * 4);
+      const long long units = (long long)a.ntiles * bp.G;
+      const long long wgs = (units + bp.WPB - 1) / bp.WPB;
+      a.per_xcd = (uint32_t)((wgs + 7) / 8);
+      size_t asz = sizeof(a);
+      void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &asz, HIP_LAUNCH_PARAM_END};
+      const hipError_t e = hipModuleLaunchKernel(h->bake_fn, 8 * a.per_xcd, 1, 1, 64 * bp.WPB, 1, 1, 0,
+                                                 reinterpret_cast<hipStream_t>(hip_stream), nullptr, cfg);
+      if (e != hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e));
+      return SC_OK;
+    }
+    if (h->var.empty())
+      return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel's 32-bit buffer ranges");
   }
   const Variant& v = h->var[pick_variant(h, N)];
   sc_status s = check_io(g, v.p, input, output, N);

@@ -1,0 +1,85 @@
+// Weights-in-code mapping ("baked" kernels): at pack time the filter bank of one layer is
+// written into the instruction stream of a gfx950 kernel, every stored non-zero becoming
+// one v_fmac_f32 whose multiplier is a 32-bit literal, with the output channel's
+// accumulator and the filter tap's input register fixed in the instruction.  The kernel is
+// assembled in-process (amd_comgr) and loaded as a code object (hipModuleLoadData).
+//
+// Why: unstructured sparsity gives every non-zero its own output channel and filter tap.
+// A kernel that reads the weights as data must select both per non-zero at run time,
+// which costs instructions, LDS reads or register-index changes for every FMA.  Fixed in
+// the code, the selection costs nothing: per non-zero the wavefront issues exactly one
+// VALU instruction, which does 64 FMAs (one per output position of its lanes).
+//
+// Work decomposition.  Output positions are numbered in an extended space of N*E*Pb
+// positions, Pb = F + (S-1)/st: position q = (n*E + e)*Pb + f, junk where f >= F.  A
+// wavefront takes V = 64 - (S-1)/st consecutive positions (lanes V..63 are junk) and one
+// group of output channels, whose accumulators it keeps in VGPRs for the whole input.  It
+// walks the input channel by channel and filter row by filter row (a "step" (c, r)); per
+// step it loads, for each stride phase sp of the filter columns, the vector
+// X[n, c, e*st - pad + r, f*st + sp - pad] over its lanes (zero where that lies in the
+// padding: the offset is then out of the buffer's range), and obtains the taps s = sp +
+// st*sq of the same row by shifting that vector sq lanes down (DPP wave_shl:1, repeated).
+// Loads run a fixed number of steps ahead of the FMAs.  At the end every lane stores its
+// valid positions of every output channel of the group (coalesced NCHW rows).
+//
+// The code is straight-line apart from the selection of the group's section at the start:
+// there is no loop, so no wave can run away; the only memory accesses are the kernel
+// argument load and buffer loads/stores whose descriptors bound them to the caller's input
+// and output, so no address computed inside the kernel can reach other memory.
+#pragma once
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+namespace sc {
+
+struct BakePlan {
+  int G = 1;        // output-channel groups, one code section each
+  int D = 4;        // steps whose loads are in flight ahead of the FMAs
+  int dpp = 1;      // 1: shifted taps by lane shifts; 0: one load per tap (V = 64)
+  int WPB = 4;      // wavefronts per workgroup
+  int Pb = 0;       // extended row pitch F + maxsq
+  int V = 64;       // valid positions per wavefront = 64 - maxsq
+  int maxsq = 0;    // largest lane shift (S-1)/st (0 without DPP)
+  int vgprs = 0, sgprs = 0;
+  long long fmas = 0;        // FMA instructions over all sections (= nnz)
+  long long code_bytes = 0;  // size of the generated instruction stream
+  std::vector<std::vector<int>> rows;  // output channels of each group
+};
+
+// Kernel arguments, in the order of the kernel's argument segment (40 bytes).
+struct BakeArgs {
+  uint64_t x, y;      // input and output base addresses
+  uint32_t N;         // images
+  uint32_t ntiles;    // wavefront tiles: ceil(N*E*Pb / V)
+  uint32_t x_bytes;   // N*C*H*W*4: range of the input descriptor (< 2^31)
+  uint32_t y_bytes;   // N*M*E*F*4: range of the output descriptor (< 2^31)
+  uint32_t qtot;      // N*E*Pb
+  uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
+};
+
+// Options from SPARSECONV_BAKE="G=..,D=..,DPP=..,WPB=.." (tuning and tests only); fields
+// left at -1 are chosen by bake_choose.
+struct BakeForce {
+  int G = -1, D = -1, dpp = -1, WPB = -1;
+};
+BakeForce bake_force_from_env();
+
+// Choose the plan (groups, depth, lane shifts) for the layer; false if the layer does not
+// fit the mapping (too many output channels per group for the registers, or too much code).
+bool bake_choose(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
+                 const BakeForce& f, BakePlan* plan, std::string* why);
+
+// Generate the GCN assembly of the layer's kernel (symbol "sc_baked").
+bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
+                   const std::vector<float>& val, BakePlan* plan, std::string* src, std::string* err);
+
+// Assemble and link with amd_comgr into a code object for gfx950.
+bool bake_assemble(const std::string& src, std::vector<char>* elf, std::string* err);
+
+// Magic numbers for q = mulhi(n, m) >> l == n / d for every n < 2^31 (d >= 2).
+void bake_magic(uint32_t d, uint32_t* m, int* l);
+
+}  // namespace sc

@@ -1,0 +1,329 @@
+"""A small CPU interpreter for the gfx950 instructions the weights-in-code generator emits.
+
+Test infrastructure: it runs the generated kernel of a packed layer on the host, wavefront
+by wavefront, so that the CPU suite can compare the generated code with the oracle without
+a GPU.  It executes exactly the instruction forms the generator writes and rejects anything
+else, and it checks the rules the hardware does not check for the code:
+
+  * the wait states gfx950 needs and does not enforce itself (as its compiler's hazard
+    recognizer inserts them): a DPP read of a VGPR two after a VALU write of it or the issue
+    of a load into it, v_readfirstlane of a VGPR one after a VALU write of it, and a VALU
+    read of VCC two after a VALU write of VCC;
+  * a VGPR that an outstanding buffer load will write may not be read or written before an
+    s_waitcnt vmcnt has retired that load (loads retire in order);
+  * only VGPRs below the kernel's declared count are used;
+  * every output element is stored at most once per launch.
+
+Buffer loads and stores follow the raw-buffer rules the kernel relies on: an access whose
+offset (vector offset plus scalar offset) is at or past the descriptor's byte range loads
+zero or is dropped.  Floating-point FMAs are evaluated in double precision and rounded once
+to fp32 (a fused fp32 FMA rounds the exact a*b + c once; the double sum can differ from it
+only by a double rounding, far inside the comparison tolerance).
+"""
+from __future__ import annotations
+
+import re
+import struct
+
+import numpy as np
+
+_REG = re.compile(r"^([sv])(\d+)$")
+_RANGE = re.compile(r"^([sv])\[(\d+):(\d+)\]$")
+
+
+class EmuError(AssertionError):
+    pass
+
+
+def _u32(x):
+    return np.uint32(x & 0xFFFFFFFF)
+
+
+class Kernel:
+    """Parsed code of one generated kernel (the text before its descriptor)."""
+
+    def __init__(self, src: str):
+        code = src.split("\t.section .rodata")[0]
+        self.instrs = []
+        self.labels = {}
+        for raw in code.splitlines():
+            line = raw.strip()
+            if not line or line.startswith("."):
+                if line.endswith(":"):
+                    self.labels[line[:-1]] = len(self.instrs)
+                continue
+            if line.endswith(":"):
+                self.labels[line[:-1]] = len(self.instrs)
+                continue
+            op, _, rest = line.partition(" ")
+            args = [a.strip() for a in re.split(r",(?![^\[]*\])", rest)] if rest else []
+            self.instrs.append((op, args))
+        m = re.search(r"\.amdhsa_next_free_vgpr (\d+)", src)
+        self.nvgpr = int(m.group(1))
+        m = re.search(r"\.amdhsa_next_free_sgpr (\d+)", src)
+        self.nsgpr = int(m.group(1))
+
+
+class Wave:
+    def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs):
+        self.k = kern
+        self.s = np.zeros(110, np.uint64)  # scalar registers (kept as u32 values)
+        self.v = np.zeros((256, 64), np.uint32)
+        self.vcc = np.zeros(64, bool)
+        self.scc = False
+        self.kernarg = kernarg
+        self.bufs = bufs  # list of (base address, numpy uint32 view) for x and y
+        self.s[2] = wg_id
+        self.v[0] = np.arange(64, dtype=np.uint32) + 64 * wave_in_wg
+        self.valu = 0
+        self.wr = np.full(256, -100, np.int64)
+        self.vcc_wr = -100
+        self.pending = []  # VGPRs of outstanding loads, oldest first
+        self.stores = []   # (buffer index, element indices, values)
+
+    # ---- operands ----
+    def sreg(self, a):
+        m = _REG.match(a)
+        if not m or m.group(1) != "s":
+            raise EmuError(f"expected an SGPR, got {a}")
+        i = int(m.group(2))
+        if i >= self.k.nsgpr:
+            raise EmuError(f"s{i} beyond the declared {self.k.nsgpr} SGPRs")
+        return i
+
+    def vreg(self, a, write=False):
+        m = _REG.match(a)
+        if not m or m.group(1) != "v":
+            raise EmuError(f"expected a VGPR, got {a}")
+        i = int(m.group(2))
+        if i >= self.k.nvgpr:
+            raise EmuError(f"v{i} beyond the declared {self.k.nvgpr} VGPRs")
+        if i in self.pending:
+            raise EmuError(f"v{i} {'written' if write else 'read'} while a load into it is outstanding")
+        return i
+
+    def sval(self, a):
+        """A scalar operand value (SGPR, integer constant, or a difference of two labels,
+        taken in instruction slots as the emulated program counter counts them)."""
+        if a.startswith("s"):
+            return int(self.s[self.sreg(a)]) & 0xFFFFFFFF
+        if a.startswith(".L"):
+            x, y = a.split("-")
+            return (self.k.labels[x] - self.k.labels[y]) & 0xFFFFFFFF
+        return int(a, 0) & 0xFFFFFFFF
+
+    def need(self, since, n, what):
+        if self.valu - since - 1 < n:
+            raise EmuError(f"{what}: {self.valu - since - 1} wait states, {n} needed")
+
+    def src_vec(self, a):
+        """A vector-instruction source: VGPR (per lane), SGPR or constant (broadcast)."""
+        if a.startswith("v"):
+            return self.v[self.vreg(a)].copy()
+        return np.full(64, self.sval(a), np.uint32)
+
+    def wv(self, a, vals):
+        i = self.vreg(a, write=True)
+        self.v[i] = vals.astype(np.uint32)
+        self.wr[i] = self.valu
+        self.valu += 1
+
+    def rsrc(self, a):
+        m = _RANGE.match(a)
+        base = int(m.group(2))
+        w = [int(self.s[base + j]) & 0xFFFFFFFF for j in range(4)]
+        addr = w[0] | ((w[1] & 0xFFFF) << 32)
+        if (w[1] >> 16) != 0 or w[3] != 0x20000:
+            raise EmuError(f"unexpected descriptor {w}")
+        return addr, w[2]
+
+    def buffer(self, addr):
+        for i, (base, arr) in enumerate(self.bufs):
+            if base == addr:
+                return i, arr
+        raise EmuError(f"descriptor base {addr:#x} is no known buffer")
+
+    # ---- execution ----
+    def run(self, max_steps=10_000_000):
+        pc = 0
+        steps = 0
+        ins = self.k.instrs
+        while True:
+            steps += 1
+            if steps > max_steps:
+                raise EmuError("too many steps")
+            op, a = ins[pc]
+            pc += 1
+            if op == "s_endpgm":
+                return
+            if op == "s_load_dwordx8" or op == "s_load_dwordx2":
+                m = _RANGE.match(a[0])
+                lo, hi = int(m.group(2)), int(m.group(3))
+                off = int(a[2], 0)
+                n = hi - lo + 1
+                vals = struct.unpack_from(f"<{n}I", self.kernarg, off)
+                for j in range(n):
+                    self.s[lo + j] = vals[j]
+            elif op == "s_waitcnt":
+                m = re.match(r"(vmcnt|lgkmcnt)\((\d+)\)", a[0])
+                if m.group(1) == "vmcnt":
+                    keep = int(m.group(2))
+                    while len(self.pending) > keep:
+                        self.pending.pop(0)
+            elif op == "s_nop":
+                self.valu += int(a[0]) + 1
+            elif op == "s_mov_b32":
+                self.s[self.sreg(a[0])] = self.sval(a[1])
+            elif op in ("s_and_b32", "s_mul_i32", "s_lshr_b32", "s_add_u32", "s_sub_u32"):
+                x, y = self.sval(a[1]), self.sval(a[2])
+                r = {"s_and_b32": x & y, "s_mul_i32": x * y, "s_lshr_b32": x >> (y & 31),
+                     "s_add_u32": x + y, "s_sub_u32": x - y}[op]
+                if op == "s_add_u32":
+                    self.scc = r > 0xFFFFFFFF
+                self.s[self.sreg(a[0])] = r & 0xFFFFFFFF
+            elif op == "s_cmp_lt_u32":
+                self.scc = self.sval(a[0]) < self.sval(a[1])
+            elif op == "s_cmp_eq_u32":
+                self.scc = self.sval(a[0]) == self.sval(a[1])
+            elif op == "s_cbranch_scc1":
+                if self.scc:
+                    pc = self.k.labels[a[0]]
+            elif op == "s_cbranch_scc0":
+                if not self.scc:
+                    pc = self.k.labels[a[0]]
+            elif op == "s_getpc_b64":
+                m = _RANGE.match(a[0])
+                self.s[int(m.group(2))] = pc
+                self.s[int(m.group(3))] = 0
+            elif op == "s_addc_u32":
+                r = self.sval(a[1]) + self.sval(a[2]) + (1 if self.scc else 0)
+                self.s[self.sreg(a[0])] = r & 0xFFFFFFFF
+            elif op == "s_setpc_b64":
+                m = _RANGE.match(a[0])
+                pc = int(self.s[int(m.group(2))])
+            elif op == "v_readfirstlane_b32":
+                src = self.vreg(a[1])
+                self.need(self.wr[src], 1, f"v_readfirstlane of v{src}")
+                self.s[self.sreg(a[0])] = int(self.v[src][0])
+                self.valu += 1
+            elif op in ("v_lshrrev_b32_e32", "v_lshlrev_b32_e32", "v_and_b32_e32", "v_add_u32_e32",
+                        "v_sub_u32_e32"):
+                x = self.src_vec(a[1]).astype(np.uint64)
+                y = self.src_vec(a[2]).astype(np.uint64)
+                if op == "v_lshrrev_b32_e32":
+                    r = y >> (x & 31)
+                elif op == "v_lshlrev_b32_e32":
+                    r = y << (x & 31)
+                elif op == "v_and_b32_e32":
+                    r = x & y
+                elif op == "v_add_u32_e32":
+                    r = x + y
+                else:
+                    r = x - y
+                self.wv(a[0], (r & 0xFFFFFFFF).astype(np.uint32))
+            elif op == "v_mov_b32_e32":
+                self.wv(a[0], self.src_vec(a[1]))
+            elif op == "v_bfrev_b32_e32":
+                x = self.sval(a[1])
+                self.wv(a[0], np.full(64, int(f"{x:032b}"[::-1], 2), np.uint32))
+            elif op in ("v_mul_hi_u32", "v_mul_lo_u32"):
+                x = self.src_vec(a[1]).astype(np.uint64)
+                y = self.src_vec(a[2]).astype(np.uint64)
+                p = x * y
+                self.wv(a[0], ((p >> 32) if op == "v_mul_hi_u32" else p) & 0xFFFFFFFF)
+            elif op == "v_cmp_gt_u32_e32":
+                if a[0] != "vcc":
+                    raise EmuError("v_cmp writes vcc only")
+                self.vcc = self.src_vec(a[1]) > self.src_vec(a[2])
+                self.vcc_wr = self.valu
+                self.valu += 1
+            elif op == "v_cndmask_b32_e32":
+                if a[3] != "vcc":
+                    raise EmuError("v_cndmask reads vcc only")
+                self.need(self.vcc_wr, 2, "v_cndmask read of vcc")
+                self.wv(a[0], np.where(self.vcc, self.src_vec(a[2]), self.src_vec(a[1])))
+            elif op == "v_mov_b32_dpp":
+                srcp, _, mods = a[1].partition(" ")
+                if mods != "wave_shl:1 row_mask:0xf bank_mask:0xf":
+                    raise EmuError(f"DPP control not emulated: {mods}")
+                dst = self.vreg(a[0], write=True)
+                src = self.vreg(srcp)
+                self.need(self.wr[src], 2, f"DPP read of v{src}")
+                out = self.v[dst].copy()
+                out[:63] = self.v[src][1:]
+                self.v[dst] = out
+                self.wr[dst] = self.valu
+                self.valu += 1
+            elif op == "v_fmamk_f32":
+                x = self.src_vec(a[1]).view(np.float32).astype(np.float64)
+                k = np.float64(np.uint32(int(a[2], 0)).view(np.float32))
+                z = self.src_vec(a[3]).view(np.float32).astype(np.float64)
+                self.wv(a[0], (x * k + z).astype(np.float32).view(np.uint32))
+            elif op == "v_fmac_f32_e32":
+                k = self.src_vec(a[1]).view(np.float32).astype(np.float64)
+                x = self.src_vec(a[2]).view(np.float32).astype(np.float64)
+                d = self.v[self.vreg(a[0])].view(np.float32).astype(np.float64)
+                self.wv(a[0], (k * x + d).astype(np.float32).view(np.uint32))
+            elif op == "buffer_load_dword" or op == "buffer_store_dword":
+                so, _, mods = a[3].partition(" ")
+                if mods != "offen":
+                    raise EmuError("buffer access other than offen")
+                addr, nrec = self.rsrc(a[2])
+                bi, arr = self.buffer(addr)
+                voff = self.src_vec(a[1]).astype(np.uint64)
+                soff = self.sval(so)
+                off = voff + np.uint64(soff)
+                inb = off < np.uint64(nrec)
+                if ((voff < np.uint64(nrec)) != inb).any():
+                    raise EmuError("range check would depend on the scalar offset")
+                if (off[inb] % 4).any():
+                    raise EmuError("misaligned access")
+                idx = (off[inb] // 4).astype(np.int64)
+                if (idx >= arr.size).any():
+                    raise EmuError("descriptor range larger than the buffer")
+                if op == "buffer_load_dword":
+                    d = self.vreg(a[0], write=True)
+                    vals = np.zeros(64, np.uint32)
+                    vals[inb] = arr[idx]
+                    self.v[d] = vals
+                    self.wr[d] = self.valu  # the DPP rule counts from the load's issue
+                    self.pending.append(d)
+                    if len(self.pending) > 63:
+                        raise EmuError("more than 63 loads outstanding")
+                else:
+                    d = self.vreg(a[0])
+                    self.stores.append((bi, idx, self.v[d][inb].copy()))
+            else:
+                raise EmuError(f"instruction not emulated: {op} {a}")
+
+
+def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
+    """Run a generated kernel over the batch x (N, C, H, W) and return y (N, M, E, F).
+
+    ``info`` holds the handle's baked-plan fields (sparseconv_query): valid lanes, row
+    pitch, groups and wavefronts per workgroup, from which the launch is set up exactly as
+    the library's forward pass does."""
+    k = Kernel(src)
+    N = x.shape[0]
+    V, Pb, G, WPB = info["bake_valid_lanes"], info["bake_pitch"], info["bake_groups"], info["bake_wpb"]
+    qtot = N * E * Pb
+    ntiles = (qtot + V - 1) // V
+    units = ntiles * G
+    wgs = (units + WPB - 1) // WPB
+    per_xcd = (wgs + 7) // 8
+    xb = np.ascontiguousarray(x, np.float32).reshape(-1).view(np.uint32)
+    y = np.full(N * M * E * F, 0x7FC00000, np.uint32)  # NaN: unwritten
+    xaddr, yaddr = 0x10000000, 0x7F0000000
+    kernarg = struct.pack("<QQIIIIII", xaddr, yaddr, N, ntiles, xb.size * 4, y.size * 4, qtot, per_xcd)
+    written = np.zeros(y.size, np.int32)
+    for b in range(8 * per_xcd):
+        for w in range(WPB):
+            wave = Wave(k, kernarg, b, w, [(xaddr, xb), (yaddr, y)])
+            wave.run()
+            for bi, idx, vals in wave.stores:
+                assert bi == 1, "store into the input"
+                y[idx] = vals
+                written[idx] += 1
+    if (written > 1).any():
+        raise EmuError(f"{int((written > 1).sum())} output elements stored more than once")
+    return y.view(np.float32).reshape(N, M, E, F), written.reshape(N, M, E, F)

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) == 9
+    assert len(names) == len(sc.EXPORTED) >= 10
     lib = ctypes.CDLL(sc.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -135,7 +135,7 @@ def test_shape_and_limit_errors():
     st, msg = _status(lambda: sc.sparseconv_pack(1, 1, 1, 1, 65536, 65536, 1, 0, values=big,
                                                  flags=sc.SC_PACK_HOST_ONLY))
     assert st == sc.SC_EUNSUPPORTED and "2^32" in msg
-    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 1, 1, values=w, flags=16))
+    st, _ = _status(lambda: sc.sparseconv_pack(2, 1, 3, 3, 5, 5, 1, 1, values=w, flags=1 << 10))
     assert st == sc.SC_EINVAL
 
 
@@ -245,7 +245,15 @@ def test_escoin_mapping_handle_on_host():
     for n in (0, 1, 3):
         want = n * L.C * (L.H + 2 * L.pad) * (L.W + 2 * L.pad) * 4
         assert h.workspace_size(n) == (want + 255) // 256 * 256
-    assert _pack_host(d, L).workspace_size(5) == 0 and _pack_host(d, L).info()["mapping"] == 0
+    assert _pack_host(d, L).workspace_size(5) == 0 and _pack_host(d, L).info()["mapping"] == sc.MAPPING_BAKED
+    assert _pack_host(d, L, ).info()["bake_groups"] >= 1
+    lds = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                    flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_LDS_TILE)
+    assert lds.info()["mapping"] == sc.MAPPING_LDS_TILE and lds.info()["bake_groups"] == 0
+    st, msg = _status(lambda: sc.sparseconv_pack(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"],
+                                                 mask=d["mask"], flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ESCOIN_MAP
+                                                 | sc.SC_PACK_LDS_TILE))
+    assert st == sc.SC_EINVAL
     st, msg = _status(lambda: sc.sparseconv_pack(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"],
                                                  mask=d["mask"], flags=sc.SC_PACK_HOST_ONLY | sc.SC_PACK_ESCOIN_MAP
                                                  | sc.SC_PACK_FP16_WORD))

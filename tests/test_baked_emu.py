@@ -1,0 +1,117 @@
+"""The weights-in-code kernels on the CPU: pack a layer on the host (SC_PACK_HOST_ONLY
+generates and assembles the kernel without a device), run its generated gfx950 code in the
+instruction emulator (tests/gcn_emu.py), and compare every output element with the oracle.
+
+The emulator also checks what the hardware leaves to the code: the wait states gfx950 needs
+between dependent instructions, loads retired before their registers are read, VGPRs within
+the declared count, and each output element stored exactly once (junk lanes and padding
+positions never stored, no position stored twice)."""
+import numpy as np
+import pytest
+
+import gcn_emu
+import oracle
+import sparse_weight_direct_amd as sc
+import workloads
+
+
+def _emulate(d, stride, pad, env=None, monkeypatch=None):
+    if env is not None:
+        monkeypatch.setenv("SPARSECONV_BAKE", env)
+    x, w, mask = d["x"], d["w"], d["mask"]
+    M, C, R, S = w.shape
+    N, _, H, W = x.shape
+    h = sc.Handle(M, C, R, S, H, W, stride, pad, values=w, mask=mask, flags=sc.SC_PACK_HOST_ONLY)
+    info = h.info()
+    assert info["mapping"] == sc.MAPPING_BAKED, info
+    y, written = gcn_emu.run_baked(h.kernel_source(), info, x, M, h.E, h.F)
+    return y, written, info
+
+
+def _check(d, stride, pad, what, env=None, monkeypatch=None):
+    y, written, info = _emulate(d, stride, pad, env, monkeypatch)
+    assert (written == 1).all(), f"{what}: {int((written != 1).sum())} outputs not stored exactly once"
+    r = oracle.reference(d["x"], d["w"], d["mask"], stride, pad)
+    ok = oracle.within_tolerance(y, r["y64"], r["mag"], 1e-5)
+    assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance"
+    return y, info
+
+
+def test_tiny_layer():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    _check(d, L.stride, L.pad, "tiny")
+
+
+CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
+    (2, 5, 13, 11, 9, 3, 3, 1, 1, 0.3, 5),
+    (2, 3, 27, 23, 7, 5, 5, 2, 2, 0.4, 6),
+    (3, 4, 9, 9, 6, 1, 1, 1, 0, 0.5, 7),
+    (2, 3, 40, 37, 5, 11, 11, 4, 0, 0.2, 8),
+    (1, 3, 10, 12, 150, 3, 3, 1, 1, 0.2, 9),
+    (1, 2, 6, 70, 9, 3, 7, 1, 3, 0.5, 10),
+    (4, 2, 5, 3, 11, 2, 3, 3, 2, 0.7, 11),   # several images per wavefront, stride 3
+    (1, 6, 1, 90, 5, 1, 4, 1, 1, 0.6, 12),   # one input row
+    (2, 7, 17, 19, 13, 3, 3, 1, 1, 0.0, 13),  # no non-zero at all: exact +0 everywhere
+    (2, 4, 15, 15, 12, 3, 3, 1, 1, 1.0, 14),  # dense filters
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=lambda c: "N{}C{}H{}W{}M{}R{}S{}st{}p{}k{}".format(*c[:10]))
+def test_random_shapes(c):
+    d = workloads.make_custom(*c)
+    y, info = _check(d, c[7], c[8], str(c))
+    if c[9] == 0.0:
+        assert np.all(y == 0) and not np.signbit(y).any()
+
+
+@pytest.mark.parametrize("env", ["G=3", "DPP=0", "G=2,DPP=0,D=3", "WPB=1", "D=1", "G=5,WPB=2,D=2"])
+def test_plan_options(env, monkeypatch):
+    """Groups, lane shifts off, load depth and wavefronts per workgroup change the code but
+    not the per-channel summation order: the outputs must equal the default plan's bit for
+    bit, and the oracle's within tolerance."""
+    c = (2, 3, 27, 23, 17, 5, 5, 2, 2, 0.4, 6)
+    d = workloads.make_custom(*c)
+    base, _ = _check(d, c[7], c[8], "default")
+    y, info = _check(d, c[7], c[8], env, env, monkeypatch)
+    assert np.array_equal(y.view(np.uint32), base.view(np.uint32))
+
+
+def test_single_nonzero_bit_exact():
+    """One non-zero per output channel: the kernel's single rounding fma(w, x, +0) and the
+    oracle's rounded double product are the same fp32 value; +0 where the tap lies in the
+    padding."""
+    rng = np.random.default_rng(3)
+    N, C, M, H, W, R, S, st, pad = 2, 5, 6, 30, 41, 3, 3, 1, 1
+    x = rng.uniform(-1, 1, (N, C, H, W)).astype(np.float32)
+    w = np.zeros((M, C, R, S), np.float32)
+    w[2, 4, R - 1, 0] = np.float32(0.8125)
+    w[5, 0, 0, S - 1] = np.float32(-1.3)
+    d = {"x": x, "w": w, "mask": None}
+    y, written, _ = _emulate(d, st, pad)
+    r = oracle.reference(x, w, None, st, pad)
+    np.testing.assert_array_equal(y.view(np.uint32), r["y"].view(np.uint32))
+
+
+def test_generated_code_shape():
+    """Per non-zero exactly one FMA with the weight as a literal (first use of an accumulator
+    as w*x + 0), every FMA's weight is one of the layer's weights, and nothing else in the
+    hot loop touches memory but the row-vector loads."""
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_HOST_ONLY)
+    src = h.kernel_source()
+    code = src.split("\t.section .rodata")[0]
+    fmas = [ln for ln in code.splitlines() if "v_fmac_f32" in ln or "v_fmamk_f32" in ln]
+    nnz = int(d["mask"].sum())
+    assert len(fmas) == nnz
+    lits = set()
+    for ln in fmas:
+        tok = [t.strip() for t in ln.replace("\t", " ").split(",")]
+        lits.add(int(tok[1] if "fmac" in ln else tok[2], 0))
+    vals = set(int(v) for v in d["w"][d["mask"].astype(bool)].view(np.uint32))
+    assert lits <= vals
+    ops = set(ln.split()[0] for ln in code.splitlines() if ln.startswith("\t") and not ln.startswith("\t."))
+    assert {o for o in ops if o.startswith(("global_", "flat_", "scratch_", "ds_"))} == set()
+    assert {o for o in ops if o.startswith("buffer_")} == {"buffer_load_dword", "buffer_store_dword"}
