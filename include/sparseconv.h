@@ -159,14 +159,42 @@ typedef struct {
                             kernel (the bake_* fields; the plan fields above then describe
                             the handle's LDS-tile plans, used only for batches too large for
                             the weights-in-code kernel) */
-  int32_t bake_groups;      /* weights-in-code: output-channel groups (one code section each) */
-  int32_t bake_valid_lanes; /* weights-in-code: output positions per wavefront, 64 - (S-1)/stride */
-  int32_t bake_pitch;       /* weights-in-code: extended row pitch F + (S-1)/stride */
-  int32_t bake_wpb;         /* weights-in-code: wavefronts per workgroup */
-  int32_t bake_depth;       /* weights-in-code: filter-row steps of input loads in flight */
-  int32_t bake_vgprs;       /* weights-in-code: VGPRs per lane */
-  int64_t bake_code_bytes;  /* weights-in-code: bytes of generated code */
+  /* weights-in-code kernels (mapping 2): the handle holds a base kernel (described here)
+     and variants that give small batches more wavefronts; sparseconv_launch_info tells
+     which one a forward of N images launches */
+  int32_t bake_groups;      /* output-channel groups; a wavefront holds one group's accumulators */
+  int32_t bake_splits;      /* channel splits: wavefronts sharing a unit's input channels, whose
+                               partial sums are added in LDS in split order */
+  int32_t bake_units_per_wg;/* units (wavefront tile x group) per workgroup */
+  int32_t bake_valid_lanes; /* output positions per wavefront, 64 - (S-1)/stride */
+  int32_t bake_pitch;       /* extended row pitch F + (S-1)/stride */
+  int32_t bake_depth;       /* filter-row steps of input loads in flight */
+  int32_t bake_vgprs;       /* VGPRs per lane */
+  int32_t bake_lds_bytes;   /* LDS per workgroup (partial sums of the channel splits) */
+  int32_t bake_variants;    /* weights-in-code kernels the handle holds */
+  int64_t bake_code_bytes;  /* bytes of generated code of the base kernel */
 } sc_info;
+
+/* The kernel a forward of N images launches (filled by sparseconv_launch_info). */
+typedef struct {
+  int32_t mapping;       /* 0 LDS-tile kernel, 1 "Escoin" mapping, 2 weights-in-code kernel */
+  int32_t variant;       /* index of the plan among the handle's plans of that mapping */
+  int64_t grid;          /* workgroups of the (main) launch */
+  int64_t waves;         /* wavefronts of the (main) launch */
+  int64_t pre_grid;      /* "Escoin" mapping: workgroups of its pad_in launch (else 0) */
+  int32_t block;         /* threads per workgroup */
+  int32_t lds_bytes;     /* LDS per workgroup */
+  int32_t vgprs;         /* weights-in-code: VGPRs per lane */
+  int32_t groups;        /* weights-in-code: output-channel groups; LDS-tile: row groups */
+  int32_t splits;        /* weights-in-code: channel splits */
+  int32_t units_per_wg;  /* weights-in-code: units per workgroup */
+  int32_t depth;         /* weights-in-code: load steps in flight */
+  int32_t valid_lanes;   /* weights-in-code: output positions per wavefront */
+  int32_t tile_pixels;   /* LDS-tile: extended positions per work unit */
+  int32_t rows_per_wave; /* LDS-tile: output-channel slots per wavefront */
+  int32_t chunk_channels;/* LDS-tile: input channels per staged chunk */
+  int32_t quad;          /* LDS-tile: 1 for a quad plan (16-byte LDS reads) */
+} sc_launch;
 
 /*
  * Pack a filter bank for one layer geometry (once per layer; weights then stay resident).
@@ -252,7 +280,14 @@ sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t
 sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t* words);
 
 /*
- * Copy out the assembly of the handle's weights-in-code kernel (for inspection and the CPU
+ * Describe the launch a forward of N >= 1 images would make on this handle (the plan the
+ * forward's cost estimate picks for N), without launching anything.  SC_EINVAL on a NULL
+ * handle or out, SC_ESHAPE for N < 1.
+ */
+sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out);
+
+/*
+ * Copy out the assembly of the handle's (base) weights-in-code kernel (for inspection and the CPU
  * checks of the generated code): *len receives its length plus one; up to cap - 1 bytes and
  * a terminating NUL are written to buf (host, owned by the caller; may be NULL to query the
  * length).  SC_EINVAL on a NULL handle or len, or a handle without such a kernel (the message

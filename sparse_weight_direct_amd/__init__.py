@@ -46,7 +46,8 @@ _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: 
 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
             "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
-            "sparseconv_export_kernel_source", "sparseconv_destroy", "sparseconv_last_error")
+            "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_destroy",
+            "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -61,9 +62,21 @@ class sc_info(ctypes.Structure):
                                                "lds_bytes", "max_wave_nnz", "waves_per_group",
                                                "pipeline_depth", "step_balance_permille",
                                                "split_pieces", "plan_variants", "entry_bytes", "mapping",
-                                               "bake_groups", "bake_valid_lanes", "bake_pitch", "bake_wpb",
-                                               "bake_depth", "bake_vgprs")] + \
+                                               "bake_groups", "bake_splits", "bake_units_per_wg",
+                                               "bake_valid_lanes", "bake_pitch", "bake_depth", "bake_vgprs",
+                                               "bake_lds_bytes", "bake_variants")] + \
                [("bake_code_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class sc_launch(ctypes.Structure):
+    _fields_ = [("mapping", ctypes.c_int32), ("variant", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("waves", ctypes.c_int64), ("pre_grid", ctypes.c_int64)] + \
+               [(n, ctypes.c_int32) for n in ("block", "lds_bytes", "vgprs", "groups", "splits", "units_per_wg",
+                                               "depth", "valid_lanes", "tile_pixels", "rows_per_wave",
+                                               "chunk_channels", "quad")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -86,6 +99,8 @@ _lib.sparseconv_export_words.restype = _i32
 _lib.sparseconv_export_words.argtypes = [_vp, _vp, _vp]
 _lib.sparseconv_export_kernel_source.restype = _i32
 _lib.sparseconv_export_kernel_source.argtypes = [_vp, ctypes.c_char_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+_lib.sparseconv_launch_info.restype = _i32
+_lib.sparseconv_launch_info.argtypes = [_vp, _i32, ctypes.POINTER(sc_launch)]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -215,6 +230,13 @@ def sparseconv_export_kernel_source(handle: int) -> str:
     return buf.value.decode()
 
 
+def sparseconv_launch_info(handle: int, N: int) -> dict:
+    """The launch a forward of N images makes (mapping, plan variant, grid, ...)."""
+    out = sc_launch()
+    _check(_lib.sparseconv_launch_info(handle, N, ctypes.byref(out)), "sparseconv_launch_info")
+    return out.as_dict()
+
+
 def sparseconv_destroy(handle) -> None:
     _lib.sparseconv_destroy(handle)
 
@@ -249,6 +271,9 @@ class Handle:
 
     def kernel_source(self) -> str:
         return sparseconv_export_kernel_source(self.ptr)
+
+    def launch_info(self, N: int) -> dict:
+        return sparseconv_launch_info(self.ptr, N)
 
     def workspace_size(self, N: int) -> int:
         return sparseconv_workspace_size(self.ptr, N)

@@ -61,6 +61,14 @@ struct Variant {
   const int32_t* d_comb;
 };
 
+struct BakedKernel {
+  sc::BakePlan p;
+  std::string src;
+  std::vector<char> elf;
+  hipModule_t mod = nullptr;
+  hipFunction_t fn = nullptr;
+};
+
 struct sc_handle {
   uint64_t magic;
   sc::Geom g;
@@ -79,14 +87,12 @@ struct sc_handle {
   bool host_only;
   void* dmem;
   size_t dbytes;
-  // weights-in-code mapping (bake.h): the generated kernel, its code object and module
+  // weights-in-code mapping (bake.h): the generated kernels (the base plan first, then the
+  // variants for small batches), their code objects and modules
   bool baked;
-  sc::BakePlan bake;
-  std::string bake_src;
-  std::vector<char> bake_elf;
+  std::vector<BakedKernel> bk;
   std::string bake_why;           // why the layer was not baked ("" if it was)
-  hipModule_t bake_mod;
-  hipFunction_t bake_fn;
+  int cus;                        // compute units of the device (256 on the host)
 };
 
 namespace {
@@ -289,10 +295,8 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
     // weights-in-code kernel (bake.h): the default mapping for fp32 weights, unless the
     // caller asks for the LDS-tile kernel, forces one of its plans (SPARSECONV_PLAN), or
     // turns baking off (SPARSECONV_BAKE=off)
-    bool baked = false;
-    sc::BakePlan bake_plan;
-    std::string bake_src, bake_why;
-    std::vector<char> bake_elf;
+    std::vector<BakedKernel> bk;
+    std::string bake_why;
     {
       const char* plan_env = std::getenv("SPARSECONV_PLAN");
       const char* bake_env = std::getenv("SPARSECONV_BAKE");
@@ -302,23 +306,29 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       else if (h16) bake_why = "SC_PACK_FP16_WORD (the kernel reads the 32-bit words)";
       else if (plan_env && plan_env[0]) bake_why = "SPARSECONV_PLAN forces an LDS-tile plan";
       else if (bake_env && std::strcmp(bake_env, "off") == 0) bake_why = "SPARSECONV_BAKE=off";
-      else if (sc::bake_choose(g, rowptr, col, sc::bake_force_from_env(), &bake_plan, &bake_why) &&
-               sc::bake_generate(g, rowptr, col, val, &bake_plan, &bake_src, &bake_why) &&
-               sc::bake_assemble(bake_src, &bake_elf, &bake_why))
-        baked = true;
+      else {
+        for (sc::BakePlan& bp : sc::bake_candidates(g, rowptr, col, sc::bake_force_from_env(), &bake_why)) {
+          BakedKernel k;
+          k.p = std::move(bp);
+          std::string why;
+          if (sc::bake_generate(g, rowptr, col, val, &k.p, &k.src, &why) && sc::bake_assemble(k.src, &k.elf, &why))
+            bk.push_back(std::move(k));
+          else if (bk.empty())
+            bake_why = why;
+        }
+      }
     }
+    const bool baked = !bk.empty();
+    if (baked) bake_why.clear();
     if (vars.empty() && !escoin && !baked)
       return fail(SC_EUNSUPPORTED, "no launch plan fits (rows too wide or too dense for the LDS ring)");
 
     h = new sc_handle();
     h->magic = kMagic;
     h->baked = baked;
-    h->bake = std::move(bake_plan);
-    h->bake_src = std::move(bake_src);
-    h->bake_elf = std::move(bake_elf);
+    h->bk = std::move(bk);
     h->bake_why = std::move(bake_why);
-    h->bake_mod = nullptr;
-    h->bake_fn = nullptr;
+    h->cus = 256;
     h->g = g;
     h->nnz = nnz;
     h->h16 = h16;
@@ -517,16 +527,21 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       }
     }
     if (h->baked && !h->host_only) {
-      if (hipModuleLoadData(&h->bake_mod, h->bake_elf.data()) != hipSuccess) {
-        h->bake_mod = nullptr;
-        sparseconv_destroy(h);
-        return fail(SC_EDEVICE, "loading the weights-in-code kernel failed (hipModuleLoadData)");
+      int cus = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
+        h->cus = cus;
+      for (BakedKernel& k : h->bk) {
+        if (hipModuleLoadData(&k.mod, k.elf.data()) != hipSuccess) {
+          k.mod = nullptr;
+          sparseconv_destroy(h);
+          return fail(SC_EDEVICE, "loading the weights-in-code kernel failed (hipModuleLoadData)");
+        }
+        if (hipModuleGetFunction(&k.fn, k.mod, "sc_baked") != hipSuccess) {
+          sparseconv_destroy(h);
+          return fail(SC_EDEVICE, "weights-in-code kernel symbol not found (hipModuleGetFunction)");
+        }
+        std::vector<char>().swap(k.elf);
       }
-      if (hipModuleGetFunction(&h->bake_fn, h->bake_mod, "sc_baked") != hipSuccess) {
-        sparseconv_destroy(h);
-        return fail(SC_EDEVICE, "weights-in-code kernel symbol not found (hipModuleGetFunction)");
-      }
-      std::vector<char>().swap(h->bake_elf);
     }
     for (Variant& v : h->var) {  // the host copies are not needed any more
       std::vector<uint32_t>().swap(v.ent);
@@ -557,13 +572,17 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
   info->entry_bytes = h->h16 ? 4 : 8;
   info->mapping = h->escoin ? 1 : h->baked ? 2 : 0;
   if (h->baked) {
-    info->bake_groups = h->bake.G;
-    info->bake_valid_lanes = h->bake.V;
-    info->bake_pitch = h->bake.Pb;
-    info->bake_wpb = h->bake.WPB;
-    info->bake_depth = h->bake.D;
-    info->bake_vgprs = h->bake.vgprs;
-    info->bake_code_bytes = h->bake.code_bytes;
+    const sc::BakePlan& b = h->bk[0].p;
+    info->bake_groups = b.G;
+    info->bake_splits = b.Q;
+    info->bake_units_per_wg = b.T;
+    info->bake_valid_lanes = b.V;
+    info->bake_pitch = b.Pb;
+    info->bake_depth = b.D;
+    info->bake_vgprs = b.vgprs;
+    info->bake_lds_bytes = b.lds_bytes;
+    info->bake_variants = (int32_t)h->bk.size();
+    info->bake_code_bytes = b.code_bytes;
   }
   if (h->escoin) {
     info->tile_pixels = 256 * sc::kEscoinP;
@@ -616,10 +635,11 @@ sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t
   if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
   if (!len) return fail(SC_EINVAL, "len is NULL");
   if (!h->baked) return fail(SC_EINVAL, "handle holds no weights-in-code kernel: " + h->bake_why);
-  *len = (int64_t)h->bake_src.size() + 1;
+  const std::string& src = h->bk[0].src;
+  *len = (int64_t)src.size() + 1;
   if (buf && cap > 0) {
-    const size_t n = std::min<size_t>((size_t)cap - 1, h->bake_src.size());
-    std::memcpy(buf, h->bake_src.data(), n);
+    const size_t n = std::min<size_t>((size_t)cap - 1, src.size());
+    std::memcpy(buf, src.data(), n);
     buf[n] = '\0';
   }
   return SC_OK;
@@ -627,7 +647,8 @@ sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t
 
 void sparseconv_destroy(sc_handle* h) {
   if (!h || h->magic != kMagic) return;
-  if (h->bake_mod) (void)hipModuleUnload(h->bake_mod);
+  for (BakedKernel& k : h->bk)
+    if (k.mod) (void)hipModuleUnload(k.mod);
   if (h->dmem) (void)hipFree(h->dmem);
   h->magic = kDead;
   delete h;
@@ -715,6 +736,48 @@ size_t pick_variant(const sc_handle* h, int N) {
   return best;
 }
 
+// Whether a batch of N images fits the weights-in-code kernels' 32-bit buffer ranges.
+bool baked_fits(const sc_handle* h, int N) {
+  if (!h->baked) return false;
+  const sc::Geom& g = h->g;
+  const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
+  long long pb = 0;
+  for (const BakedKernel& k : h->bk) pb = std::max<long long>(pb, k.p.Pb);
+  return nin * 4 < (1LL << 31) && nout * 4 < (1LL << 31) && (long long)N * g.E * pb < (1LL << 31) - 128;
+}
+
+// The weights-in-code kernel a forward of N images launches (-1: none, use the LDS-tile
+// plans): the handle's kernel with the lowest estimated cycles for N.
+int pick_baked(const sc_handle* h, int N) {
+  if (!baked_fits(h, N)) return -1;
+  int best = 0;
+  double bc = 0;
+  for (size_t i = 0; i < h->bk.size(); i++) {
+    const double c = sc::bake_estimate(h->g, h->bk[i].p, N, h->cus);
+    if (i == 0 || c < bc) {
+      best = (int)i;
+      bc = c;
+    }
+  }
+  return best;
+}
+
+// Kernel arguments and grid of a weights-in-code kernel for N images (pointers left 0).
+sc::BakeArgs baked_args(const sc_handle* h, const sc::BakePlan& bp, int N) {
+  const sc::Geom& g = h->g;
+  const long long qtot = (long long)N * g.E * bp.Pb;
+  sc::BakeArgs a{};
+  a.N = (uint32_t)N;
+  a.qtot = (uint32_t)qtot;
+  a.ntiles = (uint32_t)((qtot + bp.V - 1) / bp.V);
+  a.x_bytes = (uint32_t)((long long)N * g.C * g.H * g.W * 4);
+  a.y_bytes = (uint32_t)((long long)N * g.M * g.E * g.F * 4);
+  const long long units = (long long)a.ntiles * bp.G;
+  const long long wgs = (units + bp.T - 1) / bp.T;
+  a.per_xcd = (uint32_t)((wgs + 7) / 8);
+  return a;
+}
+
 // Bytes of the padded input the "Escoin" mapping writes for N images (0 for other handles).
 long long workspace_bytes(const sc_handle* h, int N) {
   if (!h->escoin || N <= 0) return 0;
@@ -760,38 +823,28 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
       return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
     return SC_OK;
   }
-  if (h->baked) {
+  const int bi = pick_baked(h, N);
+  if (bi >= 0) {
     const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
-    const long long qtot = (long long)N * g.E * h->bake.Pb;
-    if (nin * 4 < (1LL << 31) && nout * 4 < (1LL << 31) && qtot < (1LL << 31) - 128) {
-      if (!input || !output) return fail(SC_EINVAL, "input or output is NULL");
-      if (ranges_overlap(input, nin * 4, output, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
-      if ((reinterpret_cast<uintptr_t>(input) & 3) || (reinterpret_cast<uintptr_t>(output) & 3))
-        return fail(SC_EINVAL, "input or output is not 4-byte aligned");
-      if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
-        return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
-      const sc::BakePlan& bp = h->bake;
-      sc::BakeArgs a{};
-      a.x = reinterpret_cast<uint64_t>(input);
-      a.y = reinterpret_cast<uint64_t>(output);
-      a.N = (uint32_t)N;
-      a.qtot = (uint32_t)qtot;
-      a.ntiles = (uint32_t)((qtot + bp.V - 1) / bp.V);
-      a.x_bytes = (uint32_t)(nin * 4);
-      a.y_bytes = (uint32_t)(nout * 4);
-      const long long units = (long long)a.ntiles * bp.G;
-      const long long wgs = (units + bp.WPB - 1) / bp.WPB;
-      a.per_xcd = (uint32_t)((wgs + 7) / 8);
-      size_t asz = sizeof(a);
-      void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &asz, HIP_LAUNCH_PARAM_END};
-      const hipError_t e = hipModuleLaunchKernel(h->bake_fn, 8 * a.per_xcd, 1, 1, 64 * bp.WPB, 1, 1, 0,
-                                                 reinterpret_cast<hipStream_t>(hip_stream), nullptr, cfg);
-      if (e != hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e));
-      return SC_OK;
-    }
-    if (h->var.empty())
-      return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel's 32-bit buffer ranges");
+    if (!input || !output) return fail(SC_EINVAL, "input or output is NULL");
+    if (ranges_overlap(input, nin * 4, output, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
+    if ((reinterpret_cast<uintptr_t>(input) & 3) || (reinterpret_cast<uintptr_t>(output) & 3))
+      return fail(SC_EINVAL, "input or output is not 4-byte aligned");
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+      return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+    const BakedKernel& k = h->bk[bi];
+    sc::BakeArgs a = baked_args(h, k.p, N);
+    a.x = reinterpret_cast<uint64_t>(input);
+    a.y = reinterpret_cast<uint64_t>(output);
+    size_t asz = sizeof(a);
+    void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &asz, HIP_LAUNCH_PARAM_END};
+    const hipError_t e = hipModuleLaunchKernel(k.fn, 8 * a.per_xcd, 1, 1, 64 * k.p.wpb(), 1, 1, 0,
+                                               reinterpret_cast<hipStream_t>(hip_stream), nullptr, cfg);
+    if (e != hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return SC_OK;
   }
+  if (h->var.empty())
+    return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel's 32-bit buffer ranges");
   const Variant& v = h->var[pick_variant(h, N)];
   sc_status s = check_io(g, v.p, input, output, N);
   if (s != SC_OK) return s;
@@ -819,6 +872,60 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
                              int32_t pad, void* hip_stream) {
   g_err.clear();
   return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, nullptr, 0, false, hip_stream);
+}
+
+sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!out) return fail(SC_EINVAL, "out is NULL");
+  if (N < 1) return fail(SC_ESHAPE, "N < 1");
+  std::memset(out, 0, sizeof(*out));
+  if (h->escoin) {
+    out->mapping = 1;
+    const long long runs = (h->esc.Hp * (long long)h->esc.Wp + 255) / 256;
+    out->grid = (int64_t)N * h->g.M * h->esc.tiles;
+    out->block = 256;
+    out->pre_grid = (int64_t)N * h->g.C * runs;
+    out->lds_bytes = h->esc.chunk * 8;
+    return SC_OK;
+  }
+  const int bi = pick_baked(h, N);
+  if (bi >= 0) {
+    const sc::BakePlan& p = h->bk[bi].p;
+    const sc::BakeArgs a = baked_args(h, p, N);
+    out->mapping = 2;
+    out->variant = bi;
+    out->grid = 8LL * a.per_xcd;
+    out->block = 64 * p.wpb();
+    out->lds_bytes = p.lds_bytes;
+    out->vgprs = p.vgprs;
+    out->groups = p.G;
+    out->splits = p.Q;
+    out->units_per_wg = p.T;
+    out->depth = p.D;
+    out->valid_lanes = p.V;
+    out->waves = (int64_t)a.ntiles * p.G * p.Q;
+    return SC_OK;
+  }
+  if (h->var.empty()) return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel");
+  const size_t vi = pick_variant(h, N);
+  const Variant& v = h->var[vi];
+  const sc::Geom& g = h->g;
+  const long long ext = (long long)N * g.HYp * g.Pp;
+  const long long units = (ext + v.p.tp - 1) / v.p.tp * v.p.G;
+  const long long slots = (long long)v.cus * v.per_cu;
+  out->mapping = 0;
+  out->variant = (int32_t)vi;
+  out->grid = units < slots ? units : slots;
+  out->block = 64 * v.p.NW;
+  out->lds_bytes = v.p.lds_bytes;
+  out->tile_pixels = v.p.tp;
+  out->rows_per_wave = v.p.OCW;
+  out->groups = v.p.G;
+  out->chunk_channels = v.p.Cc;
+  out->quad = v.p.quad;
+  out->waves = out->grid * v.p.NW;
+  return SC_OK;
 }
 
 sc_status sparseconv_workspace_size(const sc_handle* h, int32_t N, int64_t* bytes) {

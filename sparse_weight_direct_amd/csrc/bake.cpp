@@ -44,9 +44,10 @@ BakeForce bake_force_from_env() {
   const char* e = std::getenv("SPARSECONV_BAKE");
   if (!e || !*e) return f;
   f.G = env_key(e, "G", -1);
+  f.Q = env_key(e, "Q", -1);
+  f.T = env_key(e, "T", -1);
   f.D = env_key(e, "D", -1);
   f.dpp = env_key(e, "DPP", -1);
-  f.WPB = env_key(e, "WPB", -1);
   return f;
 }
 
@@ -56,106 +57,298 @@ constexpr int kMaxVgpr = 256;   // architectural VGPRs a VALU instruction can na
 constexpr int kFixedV = 5;      // v0 id, v1 lane, v2 zero, v3 out-of-range marker, v4 output offset
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 4ll << 20;  // refuse kernels above 4 MB of code
+constexpr long long kGroupCode = 60 * 1024;  // a group's code that the shared instruction cache keeps
+constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
 // the other columns), or every column when lane shifts are off.
 inline int row_vectors(const Geom& g, int dpp) { return dpp ? std::min(g.st, g.S) : g.S; }
+
+// Registers of a plan with Mg accumulators and load depth D.
+inline int plan_vgprs(const Geom& g, int dpp, int maxsq, int Mg, int D) {
+  const int P = row_vectors(g, dpp);
+  const int acc0 = (kFixedV + g.R * P + (D + 1) * P + P * maxsq + 1) & ~1;  // even: 16-byte LDS writes
+  return (std::max(acc0 + Mg, acc0 + kTemps) + 3) & ~3;
+}
 
 struct Step {
   int c, r;
   uint64_t used;    // bit p: row vector p of this step is read by some non-zero
   int sqmax[64];    // per row vector: largest lane shift read (-1 unused)
   std::vector<int> nz;  // indices (into the sorted non-zero list) of the step's non-zeros
+  int loads() const {
+    int n = 0;
+    for (int k = 0; k < 64; k++) n += (int)(used >> k & 1ull);
+    return n;
+  }
+  int shifts() const {
+    int n = 0;
+    for (int k = 0; k < 64; k++) n += std::max(0, sqmax[k]);
+    return n;
+  }
 };
 
-}  // namespace
+// The non-zeros of a group sorted by (c, r, lane shift, phase, row), split into steps.
+struct Nz {
+  int m, c, r, pv, sq;
+  uint32_t bits;
+};
 
-bool bake_choose(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 const BakeForce& f, BakePlan* plan, std::string* why) {
-  const int M = g.M;
-  BakePlan p;
-  p.dpp = f.dpp >= 0 ? f.dpp : 1;
-  if (row_vectors(g, p.dpp) > 32) {
-    *why = "more than 32 row vectors per filter row";
-    return false;
-  }
-  p.maxsq = p.dpp ? (g.S - 1) / g.st : 0;
-  if (p.maxsq >= 32) {
-    *why = "filter reach too wide for lane shifts";
-    return false;
-  }
-  p.V = 64 - p.maxsq;
-  p.Pb = g.F + p.maxsq;
-  p.WPB = f.WPB > 0 ? f.WPB : 4;
-  const int P = row_vectors(g, p.dpp);
-  const int RV = g.R * P;
-  // registers besides the accumulators: fixed, per-row-vector offsets, the shifted copies
-  // of one step; the load ring takes (D+1)*P.  Target at most 168 (three wavefronts per
-  // SIMD) with at least two steps in flight, else up to 256.
-  const int base = kFixedV + RV + P * p.maxsq;
-  const long long nnz = rowptr[M];
-  long long steps_total = 0;
-  {
-    std::vector<char> seen((size_t)g.C * g.R, 0);
-    for (int j = 0; j < (int)nnz; j++) {
-      const int c = col[j] / (g.R * g.S), r = (col[j] / g.S) % g.R;
-      if (!seen[(size_t)c * g.R + r]) {
-        seen[(size_t)c * g.R + r] = 1;
-        steps_total++;
-      }
+std::vector<Step> group_steps(const Geom& g, int dpp, const std::vector<Nz>& L) {
+  std::vector<Step> steps;
+  for (size_t i = 0; i < L.size(); i++) {
+    if (steps.empty() || steps.back().c != L[i].c || steps.back().r != L[i].r) {
+      Step st;
+      st.c = L[i].c;
+      st.r = L[i].r;
+      st.used = 0;
+      for (int k = 0; k < 64; k++) st.sqmax[k] = -1;
+      steps.push_back(st);
     }
+    Step& st = steps.back();
+    st.used |= 1ull << L[i].pv;
+    st.sqmax[L[i].pv] = std::max(st.sqmax[L[i].pv], L[i].sq);
+    st.nz.push_back((int)i);
   }
-  int G = f.G > 0 ? f.G : 0;
-  if (G == 0) {
-    // the fewest groups that keep a group's accumulators in registers and its code within
-    // the 64 KB instruction cache a pair of CUs shares (a group's waves run one section)
-    for (G = 1; G <= M; G++) {
-      const int mg = (M + G - 1) / G;
-      const long long code = nnz / G * 8 + steps_total * (8 + P * 8 + P * p.maxsq * 8) + mg * 16 + 2048;
-      if (base + mg + 2 * P <= 168 && code <= 56 * 1024) break;
-      if (base + mg + 2 * P <= 168 && G >= 8) break;
-    }
-    if (G > M) G = M;
-  }
+  (void)g;
+  (void)dpp;
+  return steps;
+}
+
+// Rows to groups: largest first onto the least-loaded group with room (balance by
+// non-zeros, at most mg rows per group).
+std::vector<std::vector<int>> deal_rows(int M, int G, const std::vector<int32_t>& rowptr) {
   const int mg = (M + G - 1) / G;
-  if (base + mg + 2 * P > kMaxVgpr - 4) {
-    *why = "output channels per group exceed the registers";
-    return false;
-  }
-  int D = f.D > 0 ? f.D : 0;
-  const int budget = (base + mg + 2 * P <= 168) ? 168 : kMaxVgpr - 4;
-  if (D == 0) {
-    D = (budget - base - mg) / P - 1;
-    D = std::min(D, std::max(1, 63 / P));
-    D = std::min(D, 16);
-    D = std::max(D, 1);
-  }
-  if (D * P > 63 || base + mg + (D + 1) * P > kMaxVgpr - 4) {
-    *why = "load ring does not fit";
-    return false;
-  }
-  p.G = G;
-  p.D = D;
-  // rows to groups: largest first onto the least-loaded group with room (balance by
-  // non-zeros, at most mg rows per group)
   std::vector<int> order(M);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return rowptr[a + 1] - rowptr[a] > rowptr[b + 1] - rowptr[b]; });
-  p.rows.assign(G, {});
+  std::vector<std::vector<int>> rows(G);
   std::vector<long long> load(G, 0);
   for (int m : order) {
     int best = -1;
     for (int q = 0; q < G; q++) {
-      if ((int)p.rows[q].size() >= mg) continue;
+      if ((int)rows[q].size() >= mg) continue;
       if (best < 0 || load[q] < load[best]) best = q;
     }
-    p.rows[best].push_back(m);
+    rows[best].push_back(m);
     load[best] += rowptr[m + 1] - rowptr[m];
   }
-  for (auto& r : p.rows) std::sort(r.begin(), r.end());
-  *plan = p;
+  for (auto& r : rows) std::sort(r.begin(), r.end());
+  return rows;
+}
+
+// Sorted non-zeros of each group.
+std::vector<std::vector<Nz>> group_nonzeros(const Geom& g, int dpp, const std::vector<std::vector<int>>& rows,
+                                            const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
+                                            const std::vector<float>* val) {
+  const int RS = g.R * g.S;
+  std::vector<int> group_of(g.M, -1);
+  for (size_t q = 0; q < rows.size(); q++)
+    for (int m : rows[q]) group_of[m] = (int)q;
+  std::vector<std::vector<Nz>> nzs(rows.size());
+  for (int m = 0; m < g.M; m++)
+    for (int j = rowptr[m]; j < rowptr[m + 1]; j++) {
+      const int c = col[j] / RS, r = (col[j] / g.S) % g.R, s = col[j] % g.S;
+      Nz z;
+      z.m = m;
+      z.c = c;
+      z.r = r;
+      z.pv = dpp ? s % g.st : s;
+      z.sq = dpp ? s / g.st : 0;
+      z.bits = 0;
+      if (val) std::memcpy(&z.bits, &(*val)[j], 4);
+      nzs[group_of[m]].push_back(z);
+    }
+  for (auto& L : nzs)
+    std::stable_sort(L.begin(), L.end(), [](const Nz& a, const Nz& b) {
+      if (a.c != b.c) return a.c < b.c;
+      if (a.r != b.r) return a.r < b.r;
+      if (a.sq != b.sq) return a.sq < b.sq;
+      if (a.pv != b.pv) return a.pv < b.pv;
+      return a.m < b.m;
+    });
+  return nzs;
+}
+
+// Cost of a step in VALU instructions (FMAs and lane shifts), with a load weighed like
+// two: the steps of a group are split over the Q channel-split wavefronts by this cost.
+inline long long step_cost(const Step& st) { return (long long)st.nz.size() + st.shifts() + 2 * st.loads(); }
+
+// Split [0, steps) into Q contiguous parts of about equal cost; returns Q + 1 bounds.
+std::vector<int> split_steps(const std::vector<Step>& steps, int Q) {
+  long long total = 0;
+  for (const Step& st : steps) total += step_cost(st);
+  std::vector<int> b(Q + 1, (int)steps.size());
+  b[0] = 0;
+  long long acc = 0;
+  int q = 1;
+  for (int i = 0; i < (int)steps.size() && q < Q; i++) {
+    acc += step_cost(steps[i]);
+    while (q < Q && acc * Q >= total * q) b[q++] = i + 1;
+  }
+  return b;
+}
+
+// Fill the plan's derived fields (registers, LDS, section sizes) for given G, Q, T, D.
+bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col, BakePlan* pp,
+                   int D_forced, std::string* why) {
+  BakePlan& p = *pp;
+  const int P = row_vectors(g, p.dpp);
+  p.rows = deal_rows(g.M, p.G, rowptr);
+  int mg = 0;
+  for (auto& r : p.rows) mg = std::max(mg, (int)r.size());
+  p.Mg = p.Q > 1 ? (mg + 3) & ~3 : mg;
+  int D = D_forced;
+  if (D <= 0) {
+    // deepest ring that keeps the target occupancy (or, past it, fits at all)
+    const int cap = std::max(1, std::min(63 / P, 48));
+    const int target = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, 1) <= kVgprTarget ? kVgprTarget : kMaxVgpr;
+    D = 1;
+    while (D < cap && plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D + 1) <= target) D++;
+  }
+  if (D * P > 63 || plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D) > kMaxVgpr) {
+    *why = "output channels per group and load ring exceed the registers";
+    return false;
+  }
+  if (p.Q > 1 && g.R * P + (D + 1) * P + P * p.maxsq < 6) {
+    // split 0 reads the partial sums into registers of the offset, ring and shift region
+    *why = "channel splits need a load depth of at least 3";
+    return false;
+  }
+  p.D = D;
+  p.vgprs = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D);
+  p.lds_bytes = p.Q > 1 ? p.T * (p.Q - 1) * (p.Mg / 4) * 1024 : 0;
+  if (p.lds_bytes > 160 * 1024) {
+    *why = "channel-split partial sums exceed the LDS";
+    return false;
+  }
+  if (p.Q > 1 && (p.Q - 1) * (p.Mg / 4) * 1024 > 65535 + 1024) {
+    // partial-sum offsets of one unit are 16-bit instruction offsets
+    *why = "channel-split partial sums exceed the 64 KB offset range";
+    return false;
+  }
+  // section sizes
+  auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, nullptr);
+  p.sec_valu = 0;
+  p.sec_steps = 0;
+  long long code = 2048;
+  for (auto& L : nzs) {
+    auto steps = group_steps(g, p.dpp, L);
+    auto b = split_steps(steps, p.Q);
+    for (int q = 0; q < p.Q; q++) {
+      long long v = 0, st = 0;
+      for (int i = b[q]; i < b[q + 1]; i++) {
+        v += (long long)steps[i].nz.size() + steps[i].shifts();
+        st++;
+        code += 8 * (long long)steps[i].nz.size() + 8 * steps[i].shifts() + 8 * steps[i].loads() + 8;
+      }
+      v += p.Q > 1 ? (q == 0 ? (p.Q - 1) * p.Mg + p.Mg : p.Mg / 4) : p.Mg / 4;
+      p.sec_valu = std::max(p.sec_valu, v);
+      p.sec_steps = std::max(p.sec_steps, st);
+    }
+  }
+  p.code_bytes = code;
   return true;
+}
+
+}  // namespace
+
+std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>& rowptr,
+                                      const std::vector<int32_t>& col, const BakeForce& f, std::string* why) {
+  std::vector<BakePlan> out;
+  BakePlan p;
+  p.dpp = f.dpp >= 0 ? f.dpp : 1;
+  if (row_vectors(g, p.dpp) > 32) {
+    *why = "more than 32 row vectors per filter row";
+    return out;
+  }
+  p.maxsq = p.dpp ? (g.S - 1) / g.st : 0;
+  if (p.maxsq >= 32) {
+    *why = "filter reach too wide for lane shifts";
+    return out;
+  }
+  p.V = 64 - p.maxsq;
+  p.Pb = g.F + p.maxsq;
+  const int M = g.M;
+  const long long nnz = rowptr[M];
+  // base groups: the fewest whose accumulators fit the target occupancy and whose code
+  // (about 8 bytes per non-zero, plus per-step loads and shifts) fits the instruction cache
+  long long steps_all = 0;
+  {
+    std::vector<char> seen((size_t)g.C * g.R, 0);
+    for (long long j = 0; j < nnz; j++) {
+      const int c = col[j] / (g.R * g.S), r = (col[j] / g.S) % g.R;
+      if (!seen[(size_t)c * g.R + r]) {
+        seen[(size_t)c * g.R + r] = 1;
+        steps_all++;
+      }
+    }
+  }
+  const int P = row_vectors(g, p.dpp);
+  int G0 = 1;
+  for (; G0 < M; G0++) {
+    const int mg = (M + G0 - 1) / G0;
+    const long long code = nnz / G0 * 8 + steps_all * (8 + 8 * P + 8 * P * p.maxsq);
+    if (plan_vgprs(g, p.dpp, p.maxsq, mg, 8) <= kVgprTarget && code <= kGroupCode) break;
+    if (plan_vgprs(g, p.dpp, p.maxsq, mg, 8) <= kVgprTarget && G0 >= 8) break;
+  }
+  struct Shape {
+    int G, Q, T;
+  };
+  std::vector<Shape> shapes;
+  if (f.any()) {
+    const int G = f.G > 0 ? std::min(f.G, M) : G0;
+    const int Q = f.Q > 0 ? f.Q : 1;
+    shapes.push_back({G, Q, f.T > 0 ? f.T : std::max(1, 4 / Q)});
+  } else {
+    shapes = {{G0, 1, 4}, {G0, 1, 1}, {G0, 2, 1}, {G0, 4, 1}, {std::min(M, 2 * G0), 2, 1},
+              {std::min(M, 4 * G0), 2, 1}, {std::min(M, 4 * G0), 4, 1}};
+  }
+  for (const Shape& sh : shapes) {
+    if (sh.Q != 1 && sh.Q != 2 && sh.Q != 4 && sh.Q != 8) {
+      *why = "channel splits must be 1, 2, 4 or 8";
+      continue;
+    }
+    if (sh.Q * sh.T > 16) {
+      *why = "more than 16 wavefronts per workgroup";
+      continue;
+    }
+    bool dup = false;
+    for (const BakePlan& o : out) dup = dup || (o.G == sh.G && o.Q == sh.Q && o.T == sh.T);
+    if (dup) continue;
+    BakePlan c = p;
+    c.G = sh.G;
+    c.Q = sh.Q;
+    c.T = sh.T;
+    std::string w;
+    if (complete_plan(g, rowptr, col, &c, f.D, &w))
+      out.push_back(std::move(c));
+    else if (out.empty())
+      *why = w;
+  }
+  return out;
+}
+
+double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus) {
+  const long long qtot = (long long)N * g.E * p.Pb;
+  const long long ntiles = (qtot + p.V - 1) / p.V;
+  const long long waves = ntiles * p.G * p.Q;
+  const long long simds = 4LL * cus;
+  // resident wavefronts per SIMD (registers; LDS per workgroup)
+  int per_simd = std::min(8, 512 / std::max(8, p.vgprs));
+  if (p.lds_bytes > 0) {
+    const int wg_per_cu = 160 * 1024 / p.lds_bytes;
+    per_simd = std::min(per_simd, std::max(1, wg_per_cu * p.wpb() / 4));
+  }
+  // VALU time: a SIMD runs ceil(waves / simds) wavefronts' instructions one after the other
+  const double rounds = std::ceil((double)waves / simds);
+  const double valu = rounds * (double)p.sec_valu * 4.0;
+  // load latency: each wavefront's chain of load steps advances D steps per memory latency
+  const double lat = (double)p.sec_steps / p.D * 900.0 * std::ceil((double)waves / (simds * per_simd));
+  // HBM: input read once, output written once, at about 5 TB/s (2.3 KB per cycle at 2.2 GHz)
+  const double hbm = 4.0 * ((double)N * g.C * g.H * g.W + (double)N * g.M * g.E * g.F) / 2300.0;
+  return 5000.0 + std::max(valu, std::max(lat, hbm)) + 0.25 * std::min(valu, std::max(lat, hbm));
 }
 
 namespace {
@@ -176,11 +369,11 @@ struct Emitter {
   std::vector<long long> wr;          // per VGPR: index of its last VALU write
   long long code = 0;                 // bytes
   Emitter() : wr(kMaxVgpr, -100) {}
-  void line(const char* fmt, ...) __attribute__((format(printf, 2, 3))) {
+  void line(const char* f, ...) __attribute__((format(printf, 2, 3))) {
     char buf[256];
     va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_start(ap, f);
+    vsnprintf(buf, sizeof buf, f, ap);
     va_end(ap);
     s += '\t';
     s += buf;
@@ -210,17 +403,19 @@ struct Emitter {
   void dpp_guard(int v) { guard(wr[v], 2); }
   void rfl_guard(int v) { guard(wr[v], 1); }
   void vcc_guard() { guard(vcc_wr, 2); }
-  // a v_cmp writing VCC
-  void cmp(const char* text) {
-    line("%s", text);
+  void cmp(const std::string& text) {
+    line("%s", text.c_str());
     vcc_wr = valu;
     valu_op(-1, 4);
   }
-  // a v_cndmask reading VCC
-  void cnd(int d, const char* text) {
+  void cnd(int d, const std::string& text) {
     vcc_guard();
-    line("%s", text);
+    line("%s", text.c_str());
     valu_op(d, 4);
+  }
+  void v(int d, int bytes, const std::string& text) {
+    line("%s", text.c_str());
+    valu_op(d, bytes);
   }
 };
 
@@ -231,19 +426,17 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   BakePlan& p = *plan;
   const int P = row_vectors(g, p.dpp);
   const int RV = g.R * P;
-  const int RS = g.R * g.S;
-  const int mg = 0 == p.G ? 0 : (int)std::max_element(p.rows.begin(), p.rows.end(),
-                                                       [](const std::vector<int>& a, const std::vector<int>& b) {
-                                                         return a.size() < b.size();
-                                                       })->size();
+  const int Q = p.Q, T = p.T, WPB = p.wpb();
+  int lq = 0;
+  while ((1 << lq) < Q) lq++;
   // register map
   const int vOff = kFixedV;                 // RV per-row-vector input offsets
   const int vRing = vOff + RV;              // (D+1) * P loaded row vectors
   const int vSh = vRing + (p.D + 1) * P;    // P * maxsq shifted copies
-  const int vAcc = vSh + P * p.maxsq;       // mg accumulators
+  const int vAcc = (vSh + P * p.maxsq + 1) & ~1;  // Mg accumulators (even: 16-byte LDS writes)
   const int vTmp = vAcc;                    // prologue temporaries overlap the accumulators
-  const int nv = (std::max(vAcc + mg, vTmp + kTemps) + 3) & ~3;  // granule of the unified register file
-  if (nv > kMaxVgpr) {
+  const int nv = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, p.D);
+  if (nv > kMaxVgpr || vAcc + p.Mg > nv) {
     *err = "baked kernel needs more than 256 VGPRs";
     return false;
   }
@@ -257,27 +450,25 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   E.s += "\t.amdhsa_code_object_version 6\n";
   E.s += "\t.text\n\t.globl sc_baked\n\t.p2align 8\n\t.type sc_baked,@function\n";
   E.label("sc_baked");
-  // ---- prologue: kernel arguments, unit -> (tile, group) ----
+  // ---- prologue: kernel arguments, wavefront -> (unit, split), unit -> (tile, group) ----
   E.line("s_load_dwordx8 s[20:27], s[0:1], 0x0");
   E.line("s_load_dwordx2 s[28:29], s[0:1], 0x20");
-  E.line("v_lshrrev_b32_e32 v%d, 6, v0", vTmp);
-  E.valu_op(vTmp, 4);
-  E.line("v_and_b32_e32 v1, 63, v0");
-  E.valu_op(1, 4);
-  E.line("v_mov_b32_e32 v2, 0");
-  E.valu_op(2, 4);
-  E.line("v_bfrev_b32_e32 v3, 1");  // 0x80000000
-  E.valu_op(3, 4);
+  E.v(vTmp, 4, fmt("v_lshrrev_b32_e32 v%d, 6, v0", vTmp));
+  E.v(1, 4, "v_and_b32_e32 v1, 63, v0");
+  E.v(2, 4, "v_mov_b32_e32 v2, 0");
+  E.v(3, 4, "v_bfrev_b32_e32 v3, 1");  // 0x80000000
   E.rfl_guard(vTmp);
-  E.line("v_readfirstlane_b32 s14, v%d", vTmp);
-  E.valu_op(-1, 8);
+  E.v(-1, 8, fmt("v_readfirstlane_b32 s14, v%d", vTmp));
   E.line("s_waitcnt lgkmcnt(0)");
+  // split q = wave % Q (s3), unit within the workgroup = wave / Q
+  E.line("s_and_b32 s3, s14, %d", Q - 1);
+  E.line("s_lshr_b32 s14, s14, %d", lq);
   // logical workgroup: consecutive logical ids on one XCD (the grid is 8 * per_xcd)
   E.line("s_and_b32 s15, s2, 7");
   E.line("s_mul_i32 s15, s15, s29");
   E.line("s_lshr_b32 s16, s2, 3");
   E.line("s_add_u32 s15, s15, s16");
-  E.line("s_mul_i32 s15, s15, %d", p.WPB);
+  E.line("s_mul_i32 s15, s15, %d", T);
   E.line("s_add_u32 s15, s15, s14");  // unit; units are ordered group-major
   E.line("s_mov_b32 s16, 0");
   for (int q = 0; q < p.G; q++) {
@@ -301,246 +492,223 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   const int tPos = vTmp, tN = vTmp + 1, tRem = vTmp + 2, tE = vTmp + 3, tF = vTmp + 4, tIy = vTmp + 5,
             tIx = vTmp + 6, tRb = vTmp + 7, t0 = vTmp + 8, t1 = vTmp + 9, t2 = vTmp + 10;
   E.line("s_mul_i32 s17, s15, %d", p.V);
-  E.line("v_add_u32_e32 v%d, s17, v1", tPos);
-  E.valu_op(tPos, 4);
+  E.v(tPos, 4, fmt("v_add_u32_e32 v%d, s17, v1", tPos));
   auto divide = [&](int dst, int num, uint32_t d, int sreg) {
     if (d == 1) {
-      E.line("v_mov_b32_e32 v%d, v%d", dst, num);
-      E.valu_op(dst, 4);
+      E.v(dst, 4, fmt("v_mov_b32_e32 v%d, v%d", dst, num));
       return;
     }
     uint32_t m;
     int l;
     bake_magic(d, &m, &l);
     E.line("s_mov_b32 s%d, 0x%x", sreg, m);
-    E.line("v_mul_hi_u32 v%d, v%d, s%d", dst, num, sreg);
-    E.valu_op(dst, 8);
-    if (l > 0) {
-      E.line("v_lshrrev_b32_e32 v%d, %d, v%d", dst, l, dst);
-      E.valu_op(dst, 4);
-    }
+    E.v(dst, 8, fmt("v_mul_hi_u32 v%d, v%d, s%d", dst, num, sreg));
+    if (l > 0) E.v(dst, 4, fmt("v_lshrrev_b32_e32 v%d, %d, v%d", dst, l, dst));
   };
   const uint32_t EPb = (uint32_t)g.E * (uint32_t)p.Pb;
   divide(tN, tPos, EPb, 17);
   E.line("s_mov_b32 s18, 0x%x", EPb);
-  E.line("v_mul_lo_u32 v%d, v%d, s18", t0, tN);
-  E.valu_op(t0, 8);
-  E.line("v_sub_u32_e32 v%d, v%d, v%d", tRem, tPos, t0);
-  E.valu_op(tRem, 4);
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+  E.v(tRem, 4, fmt("v_sub_u32_e32 v%d, v%d, v%d", tRem, tPos, t0));
   divide(tE, tRem, (uint32_t)p.Pb, 17);
   E.line("s_mov_b32 s18, 0x%x", (uint32_t)p.Pb);
-  E.line("v_mul_lo_u32 v%d, v%d, s18", t0, tE);
-  E.valu_op(t0, 8);
-  E.line("v_sub_u32_e32 v%d, v%d, v%d", tF, tRem, t0);
-  E.valu_op(tF, 4);
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tE));
+  E.v(tF, 4, fmt("v_sub_u32_e32 v%d, v%d, v%d", tF, tRem, t0));
   // iy0 = e*st - pad, ix0 = f*st - pad (32-bit two's complement)
   E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.st);
   E.line("s_mov_b32 s19, 0x%x", (uint32_t)(-g.pad));
-  E.line("v_mul_lo_u32 v%d, v%d, s18", tIy, tE);
-  E.valu_op(tIy, 8);
-  E.line("v_add_u32_e32 v%d, s19, v%d", tIy, tIy);
-  E.valu_op(tIy, 4);
-  E.line("v_mul_lo_u32 v%d, v%d, s18", tIx, tF);
-  E.valu_op(tIx, 8);
-  E.line("v_add_u32_e32 v%d, s19, v%d", tIx, tIx);
-  E.valu_op(tIx, 4);
+  E.v(tIy, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", tIy, tE));
+  E.v(tIy, 4, fmt("v_add_u32_e32 v%d, s19, v%d", tIy, tIy));
+  E.v(tIx, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", tIx, tF));
+  E.v(tIx, 4, fmt("v_add_u32_e32 v%d, s19, v%d", tIx, tIx));
   // row base rb = n*C*H + iy0 (input word of (n, c=0, iy0, 0) divided by W)
   E.line("s_mov_b32 s18, 0x%x", (uint32_t)((uint64_t)g.C * g.H));
-  E.line("v_mul_lo_u32 v%d, v%d, s18", t0, tN);
-  E.valu_op(t0, 8);
-  E.line("v_add_u32_e32 v%d, v%d, v%d", tRb, t0, tIy);
-  E.valu_op(tRb, 4);
-  E.line("s_mov_b32 s30, 0x%x", (uint32_t)g.H);   // H
-  E.line("s_mov_b32 s31, 0x%x", (uint32_t)g.W);   // W
-  // s24 = N (kernel argument)
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+  E.v(tRb, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", tRb, t0, tIy));
+  E.line("s_mov_b32 s30, 0x%x", (uint32_t)g.H);
+  E.line("s_mov_b32 s31, 0x%x", (uint32_t)g.W);
   // per row vector (r, p): offset 4*((rb + r)*W + ix0 + cp), or out of range when the input
-  // row or column lies in the padding or the image is past the batch
+  // row or column lies in the padding or the image is past the batch (s24 = N)
   for (int r = 0; r < g.R; r++) {
     for (int pp = 0; pp < P; pp++) {
-      const int cp = pp;  // column offset: stride phase sp (lane shifts) or the column s
       const int dst = vOff + r * P + pp;
-      E.line("v_add_u32_e32 v%d, %d, v%d", t0, r, tIy);  // iy
-      E.valu_op(t0, r <= 64 ? 4 : 8);
-      E.line("v_add_u32_e32 v%d, %d, v%d", t1, cp, tIx);  // ix
-      E.valu_op(t1, cp <= 64 ? 4 : 8);
-      E.line("v_add_u32_e32 v%d, %d, v%d", t2, r, tRb);
-      E.valu_op(t2, r <= 64 ? 4 : 8);
-      E.line("v_mul_lo_u32 v%d, v%d, s31", t2, t2);
-      E.valu_op(t2, 8);
-      E.line("v_add_u32_e32 v%d, v%d, v%d", t2, t2, t1);
-      E.valu_op(t2, 4);
-      E.line("v_lshlrev_b32_e32 v%d, 2, v%d", t2, t2);
-      E.valu_op(t2, 4);
-      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s30, v%d", t0).c_str());
-      E.cnd(t2, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t2, t2).c_str());
-      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s31, v%d", t1).c_str());
-      E.cnd(t2, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t2, t2).c_str());
-      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN).c_str());
-      E.cnd(dst, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", dst, t2).c_str());
+      E.v(t0, 4, fmt("v_add_u32_e32 v%d, %d, v%d", t0, r, tIy));   // iy
+      E.v(t1, 4, fmt("v_add_u32_e32 v%d, %d, v%d", t1, pp, tIx));  // ix
+      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s30, v%d", t0));
+      E.v(t2, 4, fmt("v_add_u32_e32 v%d, %d, v%d", t2, r, tRb));
+      E.v(t2, 8, fmt("v_mul_lo_u32 v%d, v%d, s31", t2, t2));
+      E.v(t2, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t2, t2, t1));
+      E.v(t2, 4, fmt("v_lshlrev_b32_e32 v%d, 2, v%d", t2, t2));
+      E.cnd(t2, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t2, t2));
+      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s31, v%d", t1));
+      E.cnd(t2, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t2, t2));
+      E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN));
+      E.cnd(dst, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", dst, t2));
     }
   }
   // output offset 4*((n*M*E + e)*F + f), out of range for junk lanes (lane >= V, f >= F,
   // image past the batch)
   E.line("s_mov_b32 s18, 0x%x", (uint32_t)((uint64_t)g.M * g.E));
-  E.line("v_mul_lo_u32 v%d, v%d, s18", t0, tN);
-  E.valu_op(t0, 8);
-  E.line("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tE);
-  E.valu_op(t0, 4);
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+  E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tE));
   E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.F);
-  E.line("v_mul_lo_u32 v%d, v%d, s18", t0, t0);
-  E.valu_op(t0, 8);
-  E.line("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tF);
-  E.valu_op(t0, 4);
-  E.line("v_lshlrev_b32_e32 v%d, 2, v%d", t0, t0);
-  E.valu_op(t0, 4);
-  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", tF).c_str());
-  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0).c_str());
-  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN).c_str());
-  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0).c_str());
-  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, %d, v1", p.V).c_str());
-  E.cnd(4, fmt("v_cndmask_b32_e32 v4, v3, v%d, vcc", t0).c_str());
-  // ---- select the group's section ----
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", tF));
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, t0));
+  E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tF));
+  E.v(t0, 4, fmt("v_lshlrev_b32_e32 v%d, 2, v%d", t0, t0));
+  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN));
+  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, %d, v1", p.V));
+  E.cnd(4, fmt("v_cndmask_b32_e32 v4, v3, v%d, vcc", t0));
+  // ---- select the section of (group, split): s16 * Q + s3 ----
   // (sections can lie further than a 16-bit branch offset reaches: jump with s_setpc)
-  for (int q = 1; q < p.G; q++) {
-    E.line("s_cmp_eq_u32 s16, %d", q);
-    E.line("s_cbranch_scc0 .Lnot%d", q);
+  const int nsec = p.G * Q;
+  if (nsec > 1) {
+    E.line("s_mul_i32 s16, s16, %d", Q);
+    E.line("s_add_u32 s16, s16, s3");
+  }
+  for (int k = 1; k < nsec; k++) {
+    E.line("s_cmp_eq_u32 s16, %d", k);
+    E.line("s_cbranch_scc0 .Lnot%d", k);
     E.line("s_getpc_b64 s[34:35]");
-    E.label(".Lpc" + std::to_string(q));
-    E.line("s_add_u32 s34, s34, .Lsec%d-.Lpc%d", q, q);
+    E.label(".Lpc" + std::to_string(k));
+    E.line("s_add_u32 s34, s34, .Lsec%d-.Lpc%d", k, k);
     E.line("s_addc_u32 s35, s35, 0");
     E.line("s_setpc_b64 s[34:35]");
-    E.label(".Lnot" + std::to_string(q));
+    E.label(".Lnot" + std::to_string(k));
   }
 
-  // non-zeros sorted by (c, r, lane shift, phase, row) so a step's FMAs are contiguous and
-  // consecutive FMAs mostly hit different accumulators
-  struct Nz {
-    int m, c, r, pv, sq;
-    uint32_t bits;
-  };
-  std::vector<int> group_of(g.M, -1), slot_of(g.M, -1);
+  std::vector<int> slot_of(g.M, -1);
   for (int q = 0; q < p.G; q++)
-    for (size_t i = 0; i < p.rows[q].size(); i++) {
-      group_of[p.rows[q][i]] = q;
-      slot_of[p.rows[q][i]] = (int)i;
-    }
-  std::vector<std::vector<Nz>> nzs(p.G);
-  for (int m = 0; m < g.M; m++)
-    for (int j = rowptr[m]; j < rowptr[m + 1]; j++) {
-      const int c = col[j] / RS, r = (col[j] / g.S) % g.R, s = col[j] % g.S;
-      Nz z;
-      z.m = m;
-      z.c = c;
-      z.r = r;
-      z.pv = p.dpp ? s % g.st : s;
-      z.sq = p.dpp ? s / g.st : 0;
-      std::memcpy(&z.bits, &val[j], 4);
-      nzs[group_of[m]].push_back(z);
-    }
+    for (size_t i = 0; i < p.rows[q].size(); i++) slot_of[p.rows[q][i]] = (int)i;
+  auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, &val);
   long long fmas = 0;
-  for (int q = 0; q < p.G; q++) {
-    std::vector<Nz>& L = nzs[q];
-    std::stable_sort(L.begin(), L.end(), [](const Nz& a, const Nz& b) {
-      if (a.c != b.c) return a.c < b.c;
-      if (a.r != b.r) return a.r < b.r;
-      if (a.sq != b.sq) return a.sq < b.sq;
-      if (a.pv != b.pv) return a.pv < b.pv;
-      return a.m < b.m;
-    });
-    // steps: runs of equal (c, r)
-    std::vector<Step> steps;
-    for (size_t i = 0; i < L.size(); i++) {
-      if (steps.empty() || steps.back().c != L[i].c || steps.back().r != L[i].r) {
-        Step st;
-        st.c = L[i].c;
-        st.r = L[i].r;
-        st.used = 0;
-        for (int k = 0; k < 64; k++) st.sqmax[k] = -1;
-        steps.push_back(st);
-      }
-      Step& st = steps.back();
-      st.used |= 1ull << L[i].pv;
-      st.sqmax[L[i].pv] = std::max(st.sqmax[L[i].pv], L[i].sq);
-      st.nz.push_back((int)i);
-    }
-    if (q > 0) E.label(".Lsec" + std::to_string(q));
-    std::vector<char> touched(p.rows[q].size(), 0);
-    const int T = (int)steps.size();
-    long long cur_coff = -1;
-    auto issue_loads = [&](int t) {
-      const Step& st = steps[t];
-      const long long coff = (long long)st.c * HW4;
-      if (coff != cur_coff) {
-        E.line("s_mov_b32 s12, 0x%llx", coff);
-        cur_coff = coff;
-      }
-      const int slot = t % (p.D + 1);
-      for (int pv = 0; pv < P; pv++) {
-        if (!(st.used >> pv & 1ull)) continue;
-        E.line("buffer_load_dword v%d, v%d, s[4:7], s12 offen", vRing + slot * P + pv, vOff + st.r * P + pv);
-        E.wr[vRing + slot * P + pv] = E.valu;  // a DPP read needs 2 wait states after the issue
-        E.code += 8;
-      }
-    };
-    auto nloads = [&](int t) {
-      int n = 0;
-      for (int pv = 0; pv < P; pv++) n += (int)(steps[t].used >> pv & 1ull);
-      return n;
-    };
-    for (int t = 0; t < std::min(T, p.D); t++) issue_loads(t);
-    for (int t = 0; t < T; t++) {
-      const Step& st = steps[t];
-      int after = 0;
-      for (int u = t + 1; u < std::min(T, t + p.D); u++) after += nloads(u);
-      E.line("s_waitcnt vmcnt(%d)", after);
-      E.code += 4;
-      if (t + p.D < T) issue_loads(t + p.D);
-      const int slot = t % (p.D + 1);
-      // lane shifts and FMAs, level by level: shift level k reads level k-1 (a VALU
-      // result, hence the wait states), FMAs of level k-1 fill the gap
-      auto src_reg = [&](int pv, int sq) { return sq == 0 ? vRing + slot * P + pv : vSh + pv * p.maxsq + (sq - 1); };
-      size_t i = 0;
-      int maxlvl = 0;
-      for (int pv = 0; pv < P; pv++) maxlvl = std::max(maxlvl, st.sqmax[pv]);
-      for (int lvl = 0; lvl <= maxlvl; lvl++) {
-        if (lvl > 0) {
-          for (int pv = 0; pv < P; pv++) {
-            if (st.sqmax[pv] < lvl) continue;
-            const int s_reg = src_reg(pv, lvl - 1), d_reg = src_reg(pv, lvl);
-            E.dpp_guard(s_reg);
-            E.line("v_mov_b32_dpp v%d, v%d wave_shl:1 row_mask:0xf bank_mask:0xf", d_reg, s_reg);
-            E.valu_op(d_reg, 8);
+  p.sec_valu = 0;
+  p.sec_steps = 0;
+  const long long prologue_valu = E.valu;
+  for (int gq = 0; gq < p.G; gq++) {
+    const std::vector<Nz>& L = nzs[gq];
+    const std::vector<Step> all = group_steps(g, p.dpp, L);
+    const std::vector<int> bnd = split_steps(all, Q);
+    const int nrow = (int)p.rows[gq].size();
+    for (int sq_ = 0; sq_ < Q; sq_++) {
+      const int sec = gq * Q + sq_;
+      if (sec > 0) E.label(".Lsec" + std::to_string(sec));
+      const long long v0 = E.valu;
+      const int t_begin = bnd[sq_], t_end = bnd[sq_ + 1];
+      const int T_ = t_end - t_begin;
+      std::vector<char> touched(p.Mg, 0);
+      long long cur_coff = -1;
+      auto step_at = [&](int t) -> const Step& { return all[t_begin + t]; };
+      auto issue_loads = [&](int t) {
+        const Step& st = step_at(t);
+        const long long coff = (long long)st.c * HW4;
+        if (coff != cur_coff) {
+          E.line("s_mov_b32 s12, 0x%llx", coff);
+          cur_coff = coff;
+        }
+        const int slot = t % (p.D + 1);
+        for (int pv = 0; pv < P; pv++) {
+          if (!(st.used >> pv & 1ull)) continue;
+          E.line("buffer_load_dword v%d, v%d, s[4:7], s12 offen", vRing + slot * P + pv, vOff + st.r * P + pv);
+          E.wr[vRing + slot * P + pv] = E.valu;  // a DPP read needs 2 wait states after the issue
+          E.code += 8;
+        }
+      };
+      for (int t = 0; t < std::min(T_, p.D); t++) issue_loads(t);
+      for (int t = 0; t < T_; t++) {
+        const Step& st = step_at(t);
+        int after = 0;
+        for (int u = t + 1; u < std::min(T_, t + p.D); u++) after += step_at(u).loads();
+        E.line("s_waitcnt vmcnt(%d)", after);
+        E.code += 4;
+        if (t + p.D < T_) issue_loads(t + p.D);
+        const int slot = t % (p.D + 1);
+        // lane shifts and FMAs, level by level: shift level k reads level k-1 (a VALU
+        // result, hence the wait states), FMAs of level k-1 fill the gap
+        auto src_reg = [&](int pv, int sq) { return sq == 0 ? vRing + slot * P + pv : vSh + pv * p.maxsq + (sq - 1); };
+        size_t i = 0;
+        int maxlvl = 0;
+        for (int pv = 0; pv < P; pv++) maxlvl = std::max(maxlvl, st.sqmax[pv]);
+        for (int lvl = 0; lvl <= maxlvl; lvl++) {
+          if (lvl > 0) {
+            for (int pv = 0; pv < P; pv++) {
+              if (st.sqmax[pv] < lvl) continue;
+              const int s_reg = src_reg(pv, lvl - 1), d_reg = src_reg(pv, lvl);
+              E.dpp_guard(s_reg);
+              E.v(d_reg, 8, fmt("v_mov_b32_dpp v%d, v%d wave_shl:1 row_mask:0xf bank_mask:0xf", d_reg, s_reg));
+            }
+          }
+          for (; i < st.nz.size() && L[st.nz[i]].sq == lvl; i++) {
+            const Nz& z = L[st.nz[i]];
+            const int a = vAcc + slot_of[z.m];
+            const int sr = src_reg(z.pv, z.sq);
+            if (!touched[slot_of[z.m]]) {
+              touched[slot_of[z.m]] = 1;
+              E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
+            } else {
+              E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
+            }
+            fmas++;
           }
         }
-        for (; i < st.nz.size() && L[st.nz[i]].sq == lvl; i++) {
-          const Nz& z = L[st.nz[i]];
-          const int a = vAcc + slot_of[z.m];
-          const int sr = src_reg(z.pv, z.sq);
-          if (!touched[slot_of[z.m]]) {
-            touched[slot_of[z.m]] = 1;
-            E.line("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits);
-          } else {
-            E.line("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr);
+      }
+      // accumulators without a non-zero in this section hold +0
+      const int nacc = Q > 1 ? p.Mg : nrow;
+      for (int k = 0; k < nacc; k++)
+        if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
+      if (Q > 1) {
+        // the lane's byte address of its 16-byte column in the unit's partial sums (split q
+        // writes part q - 1; split 0 reads them all), in the first row-vector offset register,
+        // dead once the last load is issued; the rest of the offset, ring and shift registers
+        // hold the partials split 0 reads
+        const int kb = (p.Mg / 4) * 1024;
+        const int va = vOff;
+        E.line("s_mul_i32 s17, s14, %d", (Q - 1) * kb);
+        if (sq_ > 0) E.line("s_add_u32 s17, s17, %d", (sq_ - 1) * kb);
+        E.v(va, 4, fmt("v_lshlrev_b32_e32 v%d, 4, v1", va));
+        E.v(va, 4, fmt("v_add_u32_e32 v%d, s17, v%d", va, va));
+        if (sq_ > 0) {
+          // later splits leave their partial sums in LDS, 16 bytes per lane and 4 channels
+          for (int k4 = 0; k4 < p.Mg / 4; k4++)
+            E.line("ds_write_b128 v%d, v[%d:%d] offset:%d", va, vAcc + 4 * k4, vAcc + 4 * k4 + 3, k4 * 1024);
+          E.line("s_waitcnt lgkmcnt(0)");
+          E.line("s_barrier");
+          E.line("s_endpgm");
+          p.sec_valu = std::max(p.sec_valu, E.valu - v0 + p.Mg / 4);
+          p.sec_steps = std::max<long long>(p.sec_steps, T_);
+          continue;
+        }
+        // split 0 adds them in split order (batches of reads in flight), then stores
+        E.line("s_barrier");
+        const int t0r = (vOff + 2) & ~1;                  // even-aligned temporaries
+        const int nb = std::max(1, std::min(8, (vAcc - t0r) / 4));
+        const int nq = (Q - 1) * (p.Mg / 4);
+        for (int b0 = 0; b0 < nq; b0 += nb) {
+          const int b1 = std::min(nq, b0 + nb);
+          for (int b = b0; b < b1; b++)
+            E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (b - b0), t0r + 4 * (b - b0) + 3, va, b * 1024);
+          E.line("s_waitcnt lgkmcnt(0)");
+          for (int b = b0; b < b1; b++) {
+            const int k4 = b % (p.Mg / 4);
+            for (int j = 0; j < 4; j++)
+              E.v(vAcc + 4 * k4 + j, 4,
+                  fmt("v_add_f32_e32 v%d, v%d, v%d", vAcc + 4 * k4 + j, vAcc + 4 * k4 + j, t0r + 4 * (b - b0) + j));
           }
-          E.valu_op(a, 8);
-          fmas++;
         }
       }
-    }
-    // stores: output channels without a non-zero in this group hold +0
-    for (size_t k = 0; k < p.rows[q].size(); k++) {
-      if (!touched[k]) {
-        E.line("v_mov_b32_e32 v%d, 0", vAcc + (int)k);
-        E.valu_op(vAcc + (int)k, 4);
+      for (int k = 0; k < nrow; k++) {
+        E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[gq][k] * EF4);
+        E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
+        E.code += 16;
       }
+      E.line("s_endpgm");
+      p.sec_valu = std::max(p.sec_valu, E.valu - v0);
+      p.sec_steps = std::max<long long>(p.sec_steps, T_);
     }
-    for (size_t k = 0; k < p.rows[q].size(); k++) {
-      E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[q][k] * EF4);
-      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + (int)k);
-      E.code += 16;
-    }
-    E.line("s_endpgm");
   }
+  (void)prologue_valu;
   E.code += 512;  // prologue (approximate)
   p.fmas = fmas;
   p.code_bytes = E.code;
@@ -554,7 +722,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
            "\t.section .rodata,\"a\",@progbits\n"
            "\t.p2align 6, 0x0\n"
            "\t.amdhsa_kernel sc_baked\n"
-           "\t\t.amdhsa_group_segment_fixed_size 0\n"
+           "\t\t.amdhsa_group_segment_fixed_size %d\n"
            "\t\t.amdhsa_private_segment_fixed_size 0\n"
            "\t\t.amdhsa_kernarg_size 40\n"
            "\t\t.amdhsa_user_sgpr_count 2\n"
@@ -571,7 +739,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
            "\t\t.amdhsa_ieee_mode 1\n"
            "\t.end_amdhsa_kernel\n"
            "\t.text\n",
-           nv, p.sgprs, nv);
+           p.lds_bytes, nv, p.sgprs, nv);
   E.s += kd;
   char md[2048];
   snprintf(md, sizeof md,
@@ -588,7 +756,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
            "      - .offset: 28\n        .size: 4\n        .value_kind: by_value\n"
            "      - .offset: 32\n        .size: 4\n        .value_kind: by_value\n"
            "      - .offset: 36\n        .size: 4\n        .value_kind: by_value\n"
-           "    .group_segment_fixed_size: 0\n"
+           "    .group_segment_fixed_size: %d\n"
            "    .kernarg_segment_align: 8\n"
            "    .kernarg_segment_size: 40\n"
            "    .max_flat_workgroup_size: %d\n"
@@ -602,7 +770,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
            "amdhsa.version:\n  - 1\n  - 2\n"
            "...\n"
            "\t.end_amdgpu_metadata\n",
-           p.WPB * 64, p.sgprs + 6, nv);
+           p.lds_bytes, WPB * 64, p.sgprs + 6, nv);
   E.s += md;
   *src = std::move(E.s);
   return true;

@@ -36,17 +36,24 @@
 namespace sc {
 
 struct BakePlan {
-  int G = 1;        // output-channel groups, one code section each
+  int G = 1;        // output-channel groups
+  int Q = 1;        // channel splits: the input channels of a unit are split over Q wavefronts
+                    // of one workgroup, whose partial sums are added through LDS
+  int T = 4;        // units per workgroup (a workgroup is Q*T wavefronts)
   int D = 4;        // steps whose loads are in flight ahead of the FMAs
   int dpp = 1;      // 1: shifted taps by lane shifts; 0: one load per tap (V = 64)
-  int WPB = 4;      // wavefronts per workgroup
   int Pb = 0;       // extended row pitch F + maxsq
   int V = 64;       // valid positions per wavefront = 64 - maxsq
   int maxsq = 0;    // largest lane shift (S-1)/st (0 without DPP)
+  int Mg = 0;       // accumulators per wavefront (largest group, padded to 4 when Q > 1)
   int vgprs = 0, sgprs = 0;
+  int lds_bytes = 0;         // partial sums of the channel splits
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
+  long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)
+  long long sec_steps = 0;   // load steps of the longest section
   std::vector<std::vector<int>> rows;  // output channels of each group
+  int wpb() const { return Q * T; }
 };
 
 // Kernel arguments, in the order of the kernel's argument segment (40 bytes).
@@ -60,19 +67,26 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,D=..,DPP=..,WPB=.." (tuning and tests only); fields
-// left at -1 are chosen by bake_choose.
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=.." (tuning and tests only); fields
+// left at -1 are chosen by the packer.
 struct BakeForce {
-  int G = -1, D = -1, dpp = -1, WPB = -1;
+  int G = -1, Q = -1, T = -1, D = -1, dpp = -1;
+  bool any() const { return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0; }
 };
 BakeForce bake_force_from_env();
 
-// Choose the plan (groups, depth, lane shifts) for the layer; false if the layer does not
-// fit the mapping (too many output channels per group for the registers, or too much code).
-bool bake_choose(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                 const BakeForce& f, BakePlan* plan, std::string* why);
+// The plans a handle generates kernels for: one when forced, else the base plan (the fewest
+// groups that fit registers and instruction cache) and variants with more wavefronts per
+// unit of work (channel splits, more groups, one unit per workgroup) for small batches.
+// Empty (with *why) if the layer does not fit the mapping.
+std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>& rowptr,
+                                      const std::vector<int32_t>& col, const BakeForce& f, std::string* why);
 
-// Generate the GCN assembly of the layer's kernel (symbol "sc_baked").
+// Estimated cycles of a forward of N images with plan p on `cus` compute units (ranks the
+// handle's kernels; the constants are fitted to MI355X measurements).
+double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus);
+
+// Generate the GCN assembly of a plan's kernel (symbol "sc_baked").
 bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                    const std::vector<float>& val, BakePlan* plan, std::string* src, std::string* err);
 

@@ -62,11 +62,15 @@ class Kernel:
         self.nvgpr = int(m.group(1))
         m = re.search(r"\.amdhsa_next_free_sgpr (\d+)", src)
         self.nsgpr = int(m.group(1))
+        m = re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", src)
+        self.lds_bytes = int(m.group(1))
 
 
 class Wave:
-    def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs):
+    def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs, lds=None):
         self.k = kern
+        self.lds = lds  # the workgroup's LDS (uint32 words), shared by its waves
+        self.lgkm = []  # VGPRs of outstanding LDS reads
         self.s = np.zeros(110, np.uint64)  # scalar registers (kept as u32 values)
         self.v = np.zeros((256, 64), np.uint32)
         self.vcc = np.zeros(64, bool)
@@ -98,9 +102,18 @@ class Wave:
         i = int(m.group(2))
         if i >= self.k.nvgpr:
             raise EmuError(f"v{i} beyond the declared {self.k.nvgpr} VGPRs")
-        if i in self.pending:
+        if i in self.pending or i in self.lgkm:
             raise EmuError(f"v{i} {'written' if write else 'read'} while a load into it is outstanding")
         return i
+
+    def vtuple(self, a, n):
+        m = _RANGE.match(a)
+        if not m or m.group(1) != "v" or int(m.group(3)) - int(m.group(2)) + 1 != n:
+            raise EmuError(f"expected a {n}-register VGPR tuple, got {a}")
+        lo = int(m.group(2))
+        if lo % 2:
+            raise EmuError(f"VGPR tuple {a} not even-aligned")
+        return [self.vreg(f"v{lo + j}") for j in range(n)]
 
     def sval(self, a):
         """A scalar operand value (SGPR, integer constant, or a difference of two labels,
@@ -143,7 +156,7 @@ class Wave:
                 return i, arr
         raise EmuError(f"descriptor base {addr:#x} is no known buffer")
 
-    # ---- execution ----
+    # ---- execution (a generator: yields at s_barrier) ----
     def run(self, max_steps=10_000_000):
         pc = 0
         steps = 0
@@ -155,6 +168,8 @@ class Wave:
             op, a = ins[pc]
             pc += 1
             if op == "s_endpgm":
+                if self.lgkm:
+                    raise EmuError("program ends with LDS reads outstanding")
                 return
             if op == "s_load_dwordx8" or op == "s_load_dwordx2":
                 m = _RANGE.match(a[0])
@@ -166,10 +181,46 @@ class Wave:
                     self.s[lo + j] = vals[j]
             elif op == "s_waitcnt":
                 m = re.match(r"(vmcnt|lgkmcnt)\((\d+)\)", a[0])
-                if m.group(1) == "vmcnt":
-                    keep = int(m.group(2))
-                    while len(self.pending) > keep:
-                        self.pending.pop(0)
+                keep = int(m.group(2))
+                q = self.pending if m.group(1) == "vmcnt" else self.lgkm
+                while len(q) > keep:
+                    q.pop(0)
+            elif op == "s_barrier":
+                if self.lgkm:
+                    raise EmuError("s_barrier with LDS reads outstanding")
+                yield "barrier"
+            elif op in ("ds_write_b128", "ds_read_b128"):
+                if self.lds is None:
+                    raise EmuError("LDS access in a kernel without LDS")
+                last, _, mods = a[1].partition(" ")
+                off = 0
+                if mods:
+                    key, _, num = mods.partition(":")
+                    if key != "offset":
+                        raise EmuError(f"LDS modifier not emulated: {mods}")
+                    off = int(num)
+                if op == "ds_write_b128":
+                    addr = self.src_vec(a[0]).astype(np.int64) + off
+                    regs = self.vtuple(last, 4)
+                else:
+                    addr = self.src_vec(last).astype(np.int64) + off
+                    regs = self.vtuple(a[0], 4)
+                if (addr % 16).any() or (addr < 0).any() or (addr + 16 > self.lds.size * 4).any():
+                    raise EmuError(f"{op} outside the LDS or misaligned")
+                w = addr // 4
+                for j in range(4):
+                    if op == "ds_write_b128":
+                        self.lds[w + j] = self.v[regs[j]]
+                    else:
+                        self.v[regs[j]] = self.lds[w + j]
+                if op == "ds_read_b128":
+                    self.lgkm.extend(regs)
+                    if len(self.lgkm) > 4 * 15:
+                        raise EmuError("too many LDS reads outstanding")
+            elif op == "v_add_f32_e32":
+                x = self.src_vec(a[1]).view(np.float32)
+                y = self.src_vec(a[2]).view(np.float32)
+                self.wv(a[0], (x + y).view(np.uint32))
             elif op == "s_nop":
                 self.valu += int(a[0]) + 1
             elif op == "s_mov_b32":
@@ -305,11 +356,13 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
     the library's forward pass does."""
     k = Kernel(src)
     N = x.shape[0]
-    V, Pb, G, WPB = info["bake_valid_lanes"], info["bake_pitch"], info["bake_groups"], info["bake_wpb"]
+    V, Pb, G = info["bake_valid_lanes"], info["bake_pitch"], info["bake_groups"]
+    Q, T = info["bake_splits"], info["bake_units_per_wg"]
+    WPB = Q * T
     qtot = N * E * Pb
     ntiles = (qtot + V - 1) // V
     units = ntiles * G
-    wgs = (units + WPB - 1) // WPB
+    wgs = (units + T - 1) // T
     per_xcd = (wgs + 7) // 8
     xb = np.ascontiguousarray(x, np.float32).reshape(-1).view(np.uint32)
     y = np.full(N * M * E * F, 0x7FC00000, np.uint32)  # NaN: unwritten
@@ -317,9 +370,22 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
     kernarg = struct.pack("<QQIIIIII", xaddr, yaddr, N, ntiles, xb.size * 4, y.size * 4, qtot, per_xcd)
     written = np.zeros(y.size, np.int32)
     for b in range(8 * per_xcd):
-        for w in range(WPB):
-            wave = Wave(k, kernarg, b, w, [(xaddr, xb), (yaddr, y)])
-            wave.run()
+        lds = np.full(max(k.lds_bytes, 4) // 4, 0x7FC00000, np.uint32) if k.lds_bytes else None
+        waves = [Wave(k, kernarg, b, w, [(xaddr, xb), (yaddr, y)], lds) for w in range(WPB)]
+        # run every wave up to its next barrier (or its end), then release the barrier; a
+        # barrier waits only for the waves that have not ended
+        gens = [w.run() for w in waves]
+        live = list(range(WPB))
+        while live:
+            at_barrier = []
+            for i in live:
+                try:
+                    next(gens[i])
+                    at_barrier.append(i)
+                except StopIteration:
+                    pass
+            live = at_barrier
+        for wave in waves:
             for bi, idx, vals in wave.stores:
                 assert bi == 1, "store into the input"
                 y[idx] = vals

@@ -65,16 +65,24 @@ def test_random_shapes(c):
         assert np.all(y == 0) and not np.signbit(y).any()
 
 
-@pytest.mark.parametrize("env", ["G=3", "DPP=0", "G=2,DPP=0,D=3", "WPB=1", "D=1", "G=5,WPB=2,D=2"])
+@pytest.mark.parametrize("env", ["G=3", "DPP=0", "G=2,DPP=0,D=3", "T=1", "D=1", "G=5,T=2,D=2", "Q=2,T=1",
+                                 "Q=4,T=1", "Q=8,T=2", "G=3,Q=2,T=3,D=3", "Q=2,DPP=0,D=4"])
 def test_plan_options(env, monkeypatch):
-    """Groups, lane shifts off, load depth and wavefronts per workgroup change the code but
-    not the per-channel summation order: the outputs must equal the default plan's bit for
-    bit, and the oracle's within tolerance."""
-    c = (2, 3, 27, 23, 17, 5, 5, 2, 2, 0.4, 6)
+    """Groups, lane shifts off, load depth and units per workgroup change the code but not
+    the per-channel summation order: the outputs must equal the default plan's bit for bit,
+    and the oracle's within tolerance.  Channel splits (Q) add partial sums of channel
+    ranges in LDS: the order changes, the result stays within tolerance, and repeating the
+    launch gives the same bits."""
+    c = (2, 7, 27, 23, 17, 5, 5, 2, 2, 0.4, 6)
     d = workloads.make_custom(*c)
     base, _ = _check(d, c[7], c[8], "default")
     y, info = _check(d, c[7], c[8], env, env, monkeypatch)
-    assert np.array_equal(y.view(np.uint32), base.view(np.uint32))
+    if "Q=" not in env:
+        assert np.array_equal(y.view(np.uint32), base.view(np.uint32))
+    else:
+        assert info["bake_splits"] > 1 and info["bake_lds_bytes"] > 0
+        y2, _, _ = _emulate(d, c[7], c[8])
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
 def test_single_nonzero_bit_exact():
