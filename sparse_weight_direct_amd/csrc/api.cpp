@@ -747,9 +747,16 @@ bool baked_fits(const sc_handle* h, int N) {
 }
 
 // The weights-in-code kernel a forward of N images launches (-1: none, use the LDS-tile
-// plans): the handle's kernel with the lowest estimated cycles for N.
+// plans): the base kernel when it gives every SIMD a wavefront (measured best on the large
+// layers), else the handle's kernel with the lowest estimated cycles for N.
 int pick_baked(const sc_handle* h, int N) {
   if (!baked_fits(h, N)) return -1;
+  {
+    const sc::BakePlan& b = h->bk[0].p;
+    const long long qtot = (long long)N * h->g.E * b.Pb;
+    const long long waves = (qtot + b.V - 1) / b.V * b.G * b.Q;
+    if (waves >= 4LL * h->cus) return 0;
+  }
   int best = 0;
   double bc = 0;
   for (size_t i = 0; i < h->bk.size(); i++) {

@@ -13,6 +13,7 @@
 #include <amd_comgr/amd_comgr.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -57,7 +58,6 @@ constexpr int kMaxVgpr = 256;   // architectural VGPRs a VALU instruction can na
 constexpr int kFixedV = 5;      // v0 id, v1 lane, v2 zero, v3 out-of-range marker, v4 output offset
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 4ll << 20;  // refuse kernels above 4 MB of code
-constexpr long long kGroupCode = 60 * 1024;  // a group's code that the shared instruction cache keeps
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
@@ -202,7 +202,7 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   int D = D_forced;
   if (D <= 0) {
     // deepest ring that keeps the target occupancy (or, past it, fits at all)
-    const int cap = std::max(1, std::min(63 / P, 48));
+    const int cap = std::max(1, 63 / P);
     const int target = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, 1) <= kVgprTarget ? kVgprTarget : kMaxVgpr;
     D = 1;
     while (D < cap && plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D + 1) <= target) D++;
@@ -232,20 +232,23 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, nullptr);
   p.sec_valu = 0;
   p.sec_steps = 0;
+  p.sec_loads = 0;
   long long code = 2048;
   for (auto& L : nzs) {
     auto steps = group_steps(g, p.dpp, L);
     auto b = split_steps(steps, p.Q);
     for (int q = 0; q < p.Q; q++) {
-      long long v = 0, st = 0;
+      long long v = 0, st = 0, ld = 0;
       for (int i = b[q]; i < b[q + 1]; i++) {
         v += (long long)steps[i].nz.size() + steps[i].shifts();
         st++;
+        ld += steps[i].loads();
         code += 8 * (long long)steps[i].nz.size() + 8 * steps[i].shifts() + 8 * steps[i].loads() + 8;
       }
       v += p.Q > 1 ? (q == 0 ? (p.Q - 1) * p.Mg + p.Mg : p.Mg / 4) : p.Mg / 4;
       p.sec_valu = std::max(p.sec_valu, v);
       p.sec_steps = std::max(p.sec_steps, st);
+      p.sec_loads = std::max(p.sec_loads, ld);
     }
   }
   p.code_bytes = code;
@@ -272,27 +275,11 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
   p.Pb = g.F + p.maxsq;
   const int M = g.M;
   const long long nnz = rowptr[M];
-  // base groups: the fewest whose accumulators fit the target occupancy and whose code
-  // (about 8 bytes per non-zero, plus per-step loads and shifts) fits the instruction cache
-  long long steps_all = 0;
-  {
-    std::vector<char> seen((size_t)g.C * g.R, 0);
-    for (long long j = 0; j < nnz; j++) {
-      const int c = col[j] / (g.R * g.S), r = (col[j] / g.S) % g.R;
-      if (!seen[(size_t)c * g.R + r]) {
-        seen[(size_t)c * g.R + r] = 1;
-        steps_all++;
-      }
-    }
-  }
-  const int P = row_vectors(g, p.dpp);
+  // base groups: the fewest whose accumulators fit the register target (measured on the
+  // 112x112 layers, one group per wavefront beats more groups even with several hundred KB of
+  // code: more groups repeat the row loads and lane shifts per group)
   int G0 = 1;
-  for (; G0 < M; G0++) {
-    const int mg = (M + G0 - 1) / G0;
-    const long long code = nnz / G0 * 8 + steps_all * (8 + 8 * P + 8 * P * p.maxsq);
-    if (plan_vgprs(g, p.dpp, p.maxsq, mg, 8) <= kVgprTarget && code <= kGroupCode) break;
-    if (plan_vgprs(g, p.dpp, p.maxsq, mg, 8) <= kVgprTarget && G0 >= 8) break;
-  }
+  while (G0 < M && plan_vgprs(g, p.dpp, p.maxsq, (M + G0 - 1) / G0, 2) > kVgprTarget) G0++;
   struct Shape {
     int G, Q, T;
   };
@@ -302,8 +289,10 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     const int Q = f.Q > 0 ? f.Q : 1;
     shapes.push_back({G, Q, f.T > 0 ? f.T : std::max(1, 4 / Q)});
   } else {
-    shapes = {{G0, 1, 4}, {G0, 1, 1}, {G0, 2, 1}, {G0, 4, 1}, {std::min(M, 2 * G0), 2, 1},
-              {std::min(M, 4 * G0), 2, 1}, {std::min(M, 4 * G0), 4, 1}};
+    // the base plan, then variants that give small batches more wavefronts: channel splits
+    // (no repeated loads, a reduction in LDS) and more groups (repeated loads, no reduction)
+    shapes = {{G0, 1, 4}, {G0, 2, 1}, {std::min(M, 2 * G0), 1, 4}, {std::min(M, 4 * G0), 1, 4},
+              {std::min(M, 2 * G0), 2, 1}};
   }
   for (const Shape& sh : shapes) {
     if (sh.Q != 1 && sh.Q != 2 && sh.Q != 4 && sh.Q != 8) {
@@ -334,21 +323,15 @@ double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus) {
   const long long qtot = (long long)N * g.E * p.Pb;
   const long long ntiles = (qtot + p.V - 1) / p.V;
   const long long waves = ntiles * p.G * p.Q;
-  const long long simds = 4LL * cus;
-  // resident wavefronts per SIMD (registers; LDS per workgroup)
-  int per_simd = std::min(8, 512 / std::max(8, p.vgprs));
-  if (p.lds_bytes > 0) {
-    const int wg_per_cu = 160 * 1024 / p.lds_bytes;
-    per_simd = std::min(per_simd, std::max(1, wg_per_cu * p.wpb() / 4));
-  }
-  // VALU time: a SIMD runs ceil(waves / simds) wavefronts' instructions one after the other
-  const double rounds = std::ceil((double)waves / simds);
-  const double valu = rounds * (double)p.sec_valu * 4.0;
-  // load latency: each wavefront's chain of load steps advances D steps per memory latency
-  const double lat = (double)p.sec_steps / p.D * 900.0 * std::ceil((double)waves / (simds * per_simd));
+  const double simds = 4.0 * cus;
+  // VALU: a SIMD runs about ceil(waves / SIMDs) sections' instructions one after the other
+  const double valu = std::ceil((double)waves / simds) * (double)p.sec_valu * 4.0;
+  // loads: a section's row loads are issued one step after another (~35 cycles each)
+  const double loads = (double)p.sec_loads * 35.0;
   // HBM: input read once, output written once, at about 5 TB/s (2.3 KB per cycle at 2.2 GHz)
   const double hbm = 4.0 * ((double)N * g.C * g.H * g.W + (double)N * g.M * g.E * g.F) / 2300.0;
-  return 5000.0 + std::max(valu, std::max(lat, hbm)) + 0.25 * std::min(valu, std::max(lat, hbm));
+  // launch, first loads and the final stores (~5 us)
+  return 11000.0 + std::max(valu, std::max(loads, hbm));
 }
 
 namespace {

@@ -52,6 +52,7 @@ struct BakePlan {
   long long code_bytes = 0;  // size of the generated instruction stream
   long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)
   long long sec_steps = 0;   // load steps of the longest section
+  long long sec_loads = 0;   // row loads of the section with the most
   std::vector<std::vector<int>> rows;  // output channels of each group
   int wpb() const { return Q * T; }
 };

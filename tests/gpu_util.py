@@ -16,11 +16,11 @@ REL_TOL = 1e-5
 MAX_FORWARD_MS = 100.0
 
 
-def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None):
+def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None, flags=0):
     N, C, H, W = x.shape
     M, _, R, S = w.shape
     if handle is None:
-        handle = sc.Handle(M, C, R, S, H, W, stride, pad, values=w, mask=mask)
+        handle = sc.Handle(M, C, R, S, H, W, stride, pad, values=w, mask=mask, flags=flags)
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     out = torch.full((N, M, handle.E, handle.F), float("nan") if poison else 0.0, dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream() if stream is None else stream

@@ -93,12 +93,12 @@ def test_single_nonzero_bit_exact_fp16_word(R, S, stride, pad, H, W):
 
 
 def test_fp16_and_fp32_handles_agree_on_fp16_exact_weights():
-    """Weights that fp16 holds exactly: the two entry formats compute the same products in
-    the same order, so their outputs are identical bit for bit."""
+    """Weights that fp16 holds exactly: the two entry formats of the LDS-tile kernel compute
+    the same products in the same order, so their outputs are identical bit for bit."""
     d = workloads.make("mid")
     L = d["layer"]
     w16 = d["w"].astype(np.float16).astype(np.float32)
-    y32, _ = gpu_sparse(d["x"], w16, d["mask"], L.stride, L.pad)
+    y32, _ = gpu_sparse(d["x"], w16, d["mask"], L.stride, L.pad, flags=sc.SC_PACK_LDS_TILE)
     y16, _ = gpu_sparse(d["x"], w16, d["mask"], L.stride, L.pad,
                         handle=_handle16(w16, d["mask"], L.H, L.W, L.stride, L.pad))
     np.testing.assert_array_equal(y16.view(np.uint32), y32.view(np.uint32))

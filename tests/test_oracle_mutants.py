@@ -35,6 +35,11 @@ MUTANTS = {
                            "words[j] = oracle_pack_word(value[j], c, r, s);"),
     "word_ic_shift": ("((uint32_t)ic << 8)", "((uint32_t)ic << 9)"),
     "word_decode_col_order": ("colidx[j] = (ic * R + py) * S + px;", "colidx[j] = (ic * S + px) * R + py;"),
+    # the per-plane form that checks full-size layers plane by plane
+    "planes_n_m_swapped": ("conv_plane_csr(planes_sel[q] / M, planes_sel[q] % M,",
+                           "conv_plane_csr(planes_sel[q] % M, planes_sel[q] / M,"),
+    "planes_split_by_images": ("conv_plane_csr(planes_sel[q] / M, planes_sel[q] % M,",
+                               "conv_plane_csr(planes_sel[q] / N, planes_sel[q] % N,"),
 }
 
 
@@ -73,6 +78,15 @@ def _pins_pass():
                                        torch.from_numpy(d["w_masked"]).double(), stride=st, padding=p).numpy()
         if t.shape != r["y64"].shape or not np.all(np.abs(t - r["y64"]) <= 1e-12 * r["mag"] + 1e-300):
             return False
+    # the per-plane form: every (n, m) plane, in a shuffled order, equals the full form
+    d = workloads.make_custom(3, 4, 9, 8, 5, 3, 2, 2, 1, 0.6, 950)
+    rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+    y64, mag = oracle.conv_csr(d["x"], rowptr, colidx, value, 5, 3, 2, 2, 1)
+    planes = np.random.default_rng(1).permutation(15)
+    yp, mp = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, 5, 3, 2, 2, 1, planes)
+    if not (np.array_equal(yp, y64.reshape(15, *y64.shape[2:])[planes]) and
+            np.array_equal(mp, mag.reshape(15, *mag.shape[2:])[planes])):
+        return False
     C, R, S, H, W = 3, 2, 3, 5, 7
     off = oracle.stretch(np.arange(C * R * S, dtype=np.int32), C, R, S, H, W).reshape(C, R, S)
     x = np.arange(C * H * W, dtype=np.float32).reshape(C, H, W)
@@ -104,3 +118,60 @@ def test_mutant_is_rejected(name, tmp_path):
         assert not _pins_pass(), f"mutant {name} survived the pins"
     finally:
         oracle._lib = saved
+
+
+# Planted mistakes in the comparator (oracle.within_tolerance), each a plausible slip.
+def _tol_exact(y_gpu, y_ref64, mag, rel=1e-5):  # the comparator as written
+    return oracle.within_tolerance(y_gpu, y_ref64, mag, rel)
+
+
+def _tol_strict(y_gpu, y_ref64, mag, rel=1e-5):  # "<" where the bar is "<="
+    d = np.abs(y_gpu.astype(np.float64) - y_ref64)
+    ok = d < rel * mag
+    zero = mag == 0
+    ok[zero] = y_gpu[zero] == 0
+    return ok
+
+
+def _tol_absolute(y_gpu, y_ref64, mag, rel=1e-5):  # absolute instead of relative bound
+    d = np.abs(y_gpu.astype(np.float64) - y_ref64)
+    ok = d <= rel
+    zero = mag == 0
+    ok[zero] = y_gpu[zero] == 0
+    return ok
+
+
+def _tol_no_zero_rule(y_gpu, y_ref64, mag, rel=1e-5):  # forgets "mag == 0 => exactly 0"
+    d = np.abs(y_gpu.astype(np.float64) - y_ref64)
+    return d <= rel * mag + 1e-30
+
+
+def _tol_nan_passes(y_gpu, y_ref64, mag, rel=1e-5):  # NaN compares as "not outside"
+    d = np.abs(y_gpu.astype(np.float64) - y_ref64)
+    ok = ~(d > rel * mag)
+    zero = mag == 0
+    ok[zero] = y_gpu[zero] == 0
+    return ok
+
+
+def _tol_fp32_diff(y_gpu, y_ref64, mag, rel=1e-5):  # difference taken in fp32
+    d = np.abs(y_gpu - y_ref64.astype(np.float32)).astype(np.float64)
+    ok = d <= rel * mag
+    zero = mag == 0
+    ok[zero] = y_gpu[zero] == 0
+    return ok
+
+
+TOL_MUTANTS = {"strict": _tol_strict, "absolute": _tol_absolute, "no_zero_rule": _tol_no_zero_rule,
+               "nan_passes": _tol_nan_passes, "fp32_diff": _tol_fp32_diff}
+
+
+def test_comparator_pins_accept_the_comparator():
+    from test_oracle_pins import tolerance_pins_pass
+    assert tolerance_pins_pass(_tol_exact)
+
+
+@pytest.mark.parametrize("name", sorted(TOL_MUTANTS))
+def test_comparator_mutant_is_rejected(name):
+    from test_oracle_pins import tolerance_pins_pass
+    assert not tolerance_pins_pass(TOL_MUTANTS[name]), f"comparator mutant {name} survived the pins"

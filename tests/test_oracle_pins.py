@@ -284,3 +284,60 @@ def test_out_size_matches_torch_shapes_and_first_layer():
         assert oracle.out_size(n_in, pad, k, stride) == t.shape[2]
     assert oracle.out_size(227, 0, 11, 4) == 55
     assert oracle.out_size(2, 0, 3, 1) == 0
+
+
+def test_conv_csr_planes_equals_full_convolution():
+    """The per-plane form used on full-size layers: any selection of (n, m) planes, in any
+    order and with repeats, equals the corresponding planes of the full list form bit for bit
+    ([T] Sec. 3 Eq. (3) summed per output plane; plane id n*M + m)."""
+    rng = np.random.default_rng(17)
+    for i, (N, C, H, W, M, R, S, st, p) in enumerate([(3, 4, 9, 8, 5, 3, 2, 2, 1), (2, 3, 11, 13, 7, 1, 3, 1, 0),
+                                                       (4, 2, 6, 6, 3, 3, 3, 1, 2)]):
+        d = workloads.make_custom(N, C, H, W, M, R, S, st, p, 0.5, 7100 + i)
+        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+        y64, mag = oracle.conv_csr(d["x"], rowptr, colidx, value, M, R, S, st, p)
+        planes = np.concatenate([rng.permutation(N * M), rng.integers(0, N * M, 5)])
+        yp, mp = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, M, R, S, st, p, planes)
+        E, F = y64.shape[2:]
+        np.testing.assert_array_equal(yp, y64.reshape(N * M, E, F)[planes])
+        np.testing.assert_array_equal(mp, mag.reshape(N * M, E, F)[planes])
+
+
+def tolerance_pins_pass(fn) -> bool:
+    """Hand-built cases of the parity bar |y - y_ref| <= rel * MAG (MAG = sum |w*x|), with
+    MAG = 0 requiring y == 0 exactly; the comparison in double precision."""
+    rel = 1e-5
+    mag = np.array([1.0, 1.0, 1.0, 0.0, 0.0, 2.0, 1e6, 1.0, 3.0], np.float64)
+    ref = np.array([0.5, 0.5, 0.5, 0.0, 0.0, -1.0, 1e6 - 3.0, 0.25, 1.0], np.float64)
+    d_at = rel * mag  # the bound, reached exactly by representable differences below
+    y = np.array([0.5,                    # exact
+                  0.5 + 2.0 ** -17,       # |d| = 7.6e-6 < 1e-5: inside
+                  0.5 + 2.0 ** -16,       # |d| = 1.5e-5 > 1e-5: outside
+                  0.0,                    # MAG = 0 and y = 0: passes
+                  1e-35,                  # MAG = 0 and y != 0 (however small): fails
+                  -1.0 + 2.0 ** -17,      # |d| = 7.6e-6 <= 2e-5: inside
+                  1e6 - 3.0 + 8.0,        # |d| = 8 <= 10: inside (relative, not absolute)
+                  np.nan,                 # NaN: fails
+                  1.0 + 2.0 ** -23],      # |d| = 1.2e-7: inside; in fp32 arithmetic also fine
+                 np.float64).astype(np.float32)
+    want = np.array([True, True, False, True, False, True, True, False, True])
+    if not np.array_equal(fn(y, ref, mag, rel), want):
+        return False
+    # a difference exactly at the bound passes (the bar is <=): y_ref = 1, MAG = 2^20 makes
+    # rel*MAG = 10.48576 and y = 1 + 10.4857... is not exact in fp32, so use MAG with an
+    # exact bound: rel * MAG = 0.5 at MAG = 50000 (0.5 = y - y_ref exactly)
+    y2 = np.array([1.5], np.float32)
+    if not fn(y2, np.array([1.0]), np.array([50000.0]), rel).all():
+        return False
+    # the difference must be taken in double: a reference between two fp32 values
+    y3 = np.array([1.0], np.float32)
+    ref3 = np.array([1.0 + 2.0 ** -30])
+    if not fn(y3, ref3, np.array([2.0 ** -13]), rel).all():  # |d| = 2^-30 = 9.3e-10 <= 1.2e-9
+        return False
+    if fn(y3, ref3, np.array([2.0 ** -18]), rel).any():      # bound 3.8e-11 < 2^-30: outside
+        return False
+    return True
+
+
+def test_within_tolerance_rules():
+    assert tolerance_pins_pass(oracle.within_tolerance)
