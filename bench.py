@@ -4,15 +4,17 @@
 A step is one sparseconv_forward over one batch: the 112x112 layer, batch 8, C = M = 128,
 3x3, stride 1, pad 1, whose output channels have Beta(0.5, b) densities with mean
 sparsity 95% (the middle of the 90-99% range the method targets).  Packing happens once,
-before timing, as in deployment (weights stay resident).
+before timing, as in deployment (weights stay resident); the forward launches one kernel.
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
-with a device synchronisation on both sides.  Input/output buffer sets rotate so the
-working set exceeds the 256 MB Infinity Cache and every step reads its input from HBM.
+with a device synchronisation on both sides.  Input/output buffer sets rotate so the working
+set exceeds the 256 MB Infinity Cache and every step reads its input from HBM ("cold").
 
-Printed: one JSON line with effective TFLOP/s (2*nnz*N*E*F per second), the roofline of the
-kernel (algorithmic bytes per launch over its average duration against 8 TB/s), the dense
-direct baseline on the same GPU, and the CPU oracle timed on this host as a baseline.
+Printed: one JSON line with effective TFLOP/s (2*nnz*N*E*F per second) as ``value``, the
+roofline of the kernel (bound from the arithmetic intensity against the ridge of 8 TB/s and
+the fp32 vector FMA peak without packed math), the HBM fraction, the plan the forward
+launched, every other workload layer timed the same way (``per_config``), the dense direct
+baseline and torch's conv2d (MIOpen) on the same GPU, and the CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -34,12 +37,12 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stored_traffic(layer: str):
+def stored_traffic(tag: str, mapping: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when it is
-    missing, for another workload, or taken on different kernel sources.  ``layer`` is the
-    workload tag (the layer name, with "_fp16word" for the packed-word form)."""
+    missing, for another workload, or taken on different kernel sources."""
     from sparse_weight_direct_amd.rocprof_summary import kernel_digest
-    path = os.path.join(PROFILE_DIR, f"sparse_direct_fwd_{layer}_traffic.txt")
+    kernel = {0: "sparse_direct_fwd", 1: "escoin_sconv", 2: "sc_baked"}.get(mapping, "?")
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{tag}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -47,7 +50,7 @@ def stored_traffic(layer: str):
         m = re.match(r"^(\w+):\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    if kv.get("kernel_digest") != kernel_digest() or kv.get("workload") != layer:
+    if kv.get("kernel_digest") != kernel_digest(kernel) or kv.get("workload") != tag:
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -62,16 +65,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layer", default=None, help="layer name from workloads.LAYERS")
     ap.add_argument("--rotate-mb", type=int, default=768, help="total size of the rotated buffer sets")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (and the parity check)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense direct baseline")
-    ap.add_argument("--miopen", action="store_true", help="also time torch conv2d (MIOpen) as context")
+    ap.add_argument("--no-miopen", action="store_true", help="skip torch conv2d (MIOpen) as context")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the other workload layers")
+    ap.add_argument("--lds-tile", action="store_true", help="use the LDS-tile kernel (SC_PACK_LDS_TILE)")
     ap.add_argument("--chain", default=None,
                     help="also time a layer stack from workloads.CHAINS, eager launches vs one graph replay")
     ap.add_argument("--fp16-word", action="store_true",
                     help="pack the weights as 32-bit words with an fp16 value (SC_PACK_FP16_WORD)")
     ap.add_argument("--escoin", action="store_true",
                     help="time the second mapping (SC_PACK_ESCOIN_MAP: pad_in + one output channel per workgroup)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target CPU time of one timed oracle run")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
     args = ap.parse_args()
@@ -88,30 +93,12 @@ def main():
     import workloads
     from sparse_weight_direct_amd import roofline
 
-    layer = args.layer or workloads.BENCH_LAYER
-    d = workloads.make(layer)
-    L = d["layer"]
-    N, C, H, W, M, R, S, st, pad, E, F = L.N, L.C, L.H, L.W, L.M, L.R, L.S, L.stride, L.pad, L.E, L.F
-    log(f"[bench] layer {layer}: N={N} C={C} {H}x{W} M={M} {R}x{S} s{st} p{pad} -> {E}x{F}")
+    flags = ((sc.SC_PACK_FP16_WORD if args.fp16_word else 0) | (sc.SC_PACK_ESCOIN_MAP if args.escoin else 0)
+             | (sc.SC_PACK_LDS_TILE if args.lds_tile else 0))
     dev = torch.device("cuda:0")
-    h = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w"], mask=d["mask"],
-                  flags=(sc.SC_PACK_FP16_WORD if args.fp16_word else 0) | (sc.SC_PACK_ESCOIN_MAP if args.escoin else 0))
-    info = h.info()
-    nnz = info["nnz"]
-    tag = layer + ("_fp16word" if args.fp16_word else "") + ("_escoin" if args.escoin else "")
-    ws_bytes = h.workspace_size(N)
-    ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=dev) if ws_bytes else None
-    flops = roofline.effective_flops(nnz, N, E, F)
-    alg_bytes = roofline.algorithmic_bytes(N, C, H, W, M, E, F, nnz, info["entry_bytes"])
-    set_bytes = 4 * (N * C * H * W + N * M * E * F)
-    nsets = max(1, math.ceil(args.rotate_mb * (1 << 20) / set_bytes))
-    x0 = torch.from_numpy(d["x"]).to(dev)
-    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
-    ys = [torch.empty((N, M, E, F), dtype=torch.float32, device=dev) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
-    log(f"[bench] nnz={nnz} plan={info} sets={nsets} ({nsets * set_bytes / 2**20:.0f} MiB rotated)")
 
-    def run(fn, steps, warmup):
+    def run(fn, steps, warmup, nsets):
         for i in range(warmup):
             fn(i % nsets)
         torch.cuda.synchronize()
@@ -126,73 +113,89 @@ def main():
         torch.cuda.synchronize()
         total = evs[0].elapsed_time(evs[-1])
         per = [evs[g].elapsed_time(evs[g + 1]) / (bounds[g + 1] - bounds[g]) for g in range(groups)]
-        mean = total / steps
         sem = float(np.std(per, ddof=1) / math.sqrt(len(per))) if len(per) > 1 else 0.0
-        return mean, sem
+        return total / steps, sem
 
-    def sparse_step(i):
-        h.forward(xs[i], ys[i], stream=stream, workspace=ws)
+    def setup(name):
+        """Pack a layer and allocate rotated buffer sets (inputs resident in HBM)."""
+        d = workloads.make(name)
+        L = d["layer"]
+        h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"], flags=flags)
+        ws_bytes = h.workspace_size(L.N)
+        ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=dev) if ws_bytes else None
+        set_bytes = 4 * (L.N * L.C * L.H * L.W + L.N * L.M * L.E * L.F)
+        nsets = max(1, math.ceil(args.rotate_mb * (1 << 20) / set_bytes))
+        x0 = torch.from_numpy(d["x"]).to(dev)
+        xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+        ys = [torch.empty((L.N, L.M, L.E, L.F), dtype=torch.float32, device=dev) for _ in range(nsets)]
+        return d, L, h, ws, xs, ys, nsets, set_bytes
+
+    def describe(L, info, ms):
+        nnz = info["nnz"]
+        flops = roofline.effective_flops(nnz, L.N, L.E, L.F)
+        alg = roofline.algorithmic_bytes(L.N, L.C, L.H, L.W, L.M, L.E, L.F, nnz, info["entry_bytes"])
+        ai = flops / alg
+        ridge = roofline.FP32_VECTOR_NONPACKED_TFLOPS * 1e12 / (roofline.HBM_PEAK_GBS * 1e9)
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbs = alg / (ms * 1e-3) / 1e9
+        bound = "alu" if ai > ridge else "hbm"
+        frac = tflops / roofline.FP32_VECTOR_NONPACKED_TFLOPS if bound == "alu" else gbs / roofline.HBM_PEAK_GBS
+        return dict(flops=flops, alg=alg, ai=ai, tflops=tflops, gbs=gbs, bound=bound, frac=frac)
+
+    layer = args.layer or workloads.BENCH_LAYER
+    d, L, h, ws, xs, ys, nsets, set_bytes = setup(layer)
+    N, C, H, W, M, R, S, st, pad, E, F = L.N, L.C, L.H, L.W, L.M, L.R, L.S, L.stride, L.pad, L.E, L.F
+    info = h.info()
+    nnz = info["nnz"]
+    launch = h.launch_info(N)
+    log(f"[bench] layer {layer}: N={N} C={C} {H}x{W} M={M} {R}x{S} s{st} p{pad} -> {E}x{F}, nnz={nnz}, "
+        f"launch {launch}, {nsets} rotated sets ({nsets * set_bytes / 2**20:.0f} MiB)")
 
     log(f"[bench] sparse: warmup {args.warmup}, timed {args.steps}")
-    ms, sem = run(sparse_step, args.steps, args.warmup)
-    tflops = flops / (ms * 1e-3) / 1e12
-    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
-    ai = flops / alg_bytes
-    flop_roof = min(roofline.HBM_PEAK_GBS * 1e9 * ai, roofline.FP32_VECTOR_PEAK_TFLOPS * 1e12) / 1e12
-    log(f"[bench] sparse {ms * 1e3:.2f} us/step (SEM {sem * 1e3:.2f}), {tflops:.2f} TFLOP/s, {achieved_gbs:.0f} GB/s")
-
-    def oracle_csr():
-        """The oracle's CSR of the layer; for the packed-word form, the non-zeros decoded
-        from the oracle's own words (fp16-rounded weights)."""
-        import oracle
-        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
-        if args.fp16_word:
-            colidx, value = oracle.csr_from_words(oracle.words_from_csr(colidx, value, C, R, S), R, S)
-        return rowptr, colidx, value
-
-    # correctness of the timed buffers: sampled planes against the oracle
-    parity = None
-    try:
-        import oracle
-        rowptr, colidx, value = oracle_csr()
-        rng = np.random.default_rng(0)
-        planes = sorted(set(int(p) for p in rng.choice(N * M, min(8, N * M), replace=False)))
-        y64, mag = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, M, R, S, st, pad, planes)
-        got = ys[0].cpu().numpy().reshape(N * M, E, F)[planes]
-        parity = bool(oracle.within_tolerance(got, y64, mag, 1e-5).all())
-    except Exception as e:  # report, never hide
-        parity = f"error: {e}"
-    log(f"[bench] parity on timed buffers: {parity}")
+    ms, sem = run(lambda i: h.forward(xs[i], ys[i], stream=stream, workspace=ws), args.steps, args.warmup, nsets)
+    m = describe(L, info, ms)
+    log(f"[bench] sparse {ms * 1e3:.2f} us/step (SEM {sem * 1e3:.2f}), {m['tflops']:.2f} TFLOP/s, "
+        f"{m['gbs']:.0f} GB/s algorithmic, AI {m['ai']:.1f}")
 
     extra = {}
-    # warm variant: back-to-back forwards on one buffer set, whose input and output stay in
-    # the Infinity Cache when they fit (context only; value above is the rotated, cold form)
-    wsteps = max(10, args.steps // 2)
-    wms, wsem = run(lambda i: h.forward(xs[0], ys[0], stream=stream, workspace=ws), wsteps, 3)
+    # warm variant: back-to-back forwards on one buffer set, whose input and output stay in the
+    # Infinity Cache when they fit (context only; value is the rotated, cold form)
+    wms, wsem = run(lambda i: h.forward(xs[0], ys[0], stream=stream, workspace=ws), max(10, args.steps // 2), 3, 1)
     extra["warm_one_set"] = {"ms_per_step": round(wms, 5), "sem_ms": round(wsem, 5),
-                             "tflops": round(flops / (wms * 1e-3) / 1e12, 3), "set_mb": round(set_bytes / 2**20, 1)}
-    log(f"[bench] warm (one buffer set, {set_bytes / 2**20:.0f} MiB): {wms * 1e3:.2f} us/step")
+                             "tflops": round(m["flops"] / (wms * 1e-3) / 1e12, 3),
+                             "set_mb": round(set_bytes / 2**20, 1)}
+    log(f"[bench] warm (one buffer set): {wms * 1e3:.2f} us/step")
+
     if not args.no_dense:
-        hd = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w_masked"], flags=sc.SC_PACK_ALL_TAPS)
+        wd = torch.from_numpy(d["w_masked"]).to(dev)
+        yd = torch.empty((N, M, E, F), dtype=torch.float32, device=dev)
+        if hasattr(sc, "sparseconv_dense_forward"):
+            def dense_step(i):
+                sc.sparseconv_dense_forward(wd, xs[i], yd, N, C, H, W, M, R, S, st, pad, stream)
+            kind = "sparseconv_dense_forward (dense weights on the device, every tap)"
+        else:
+            hd = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w_masked"], flags=sc.SC_PACK_ALL_TAPS)
 
-        def dense_step(i):
-            hd.forward(xs[i], ys[i], stream=stream)
-
+            def dense_step(i):
+                hd.forward(xs[i], yd, stream=stream)
+            kind = "LDS-tile kernel on a handle storing every tap"
         dsteps = max(10, args.steps // 10)
-        log(f"[bench] dense direct baseline: warmup 2, timed {dsteps}")
-        dms, dsem = run(dense_step, dsteps, 2)
-        extra["dense_direct"] = {"ms_per_step": round(dms, 5), "sem_ms": round(dsem, 5),
-                                 "tflops_dense_work": round(roofline.dense_flops(N, C, M, E, F, R, S) / (dms * 1e-3) / 1e12, 3),
+        dms, dsem = run(dense_step, dsteps, 2, nsets)
+        extra["dense_direct"] = {"kind": kind, "ms_per_step": round(dms, 5), "sem_ms": round(dsem, 5),
+                                 "tflops_dense_work": round(roofline.dense_flops(N, C, M, E, F, R, S) / (dms * 1e-3)
+                                                            / 1e12, 3),
                                  "speedup_sparse_over_dense": round(dms / ms, 3)}
-        log(f"[bench] dense {dms * 1e3:.1f} us/step -> sparse speedup {dms / ms:.2f}x")
-    if args.miopen:
+        log(f"[bench] dense direct {dms * 1e3:.1f} us/step -> sparse speedup {dms / ms:.2f}x")
+    if not args.no_miopen:
         wd = torch.from_numpy(d["w_masked"]).to(dev)
 
         def miopen_step(i):
             torch.nn.functional.conv2d(xs[i], wd, stride=st, padding=pad)
 
-        mms, _ = run(miopen_step, max(10, args.steps // 10), 3)
-        extra["torch_conv2d_miopen_ms"] = round(mms, 5)
+        mms, msem = run(miopen_step, max(10, args.steps // 10), 3, nsets)
+        extra["torch_conv2d_miopen"] = {"ms_per_step": round(mms, 5), "sem_ms": round(msem, 5),
+                                        "speedup_sparse_over_miopen": round(mms / ms, 3)}
+        log(f"[bench] torch conv2d (MIOpen, dense fp32) {mms * 1e3:.1f} us/step")
 
     if args.chain:
         from sparse_weight_direct_amd.chain import LayerChain
@@ -200,9 +203,9 @@ def main():
         chain = LayerChain([sc.Handle(values=cd["w"], mask=cd["mask"], **cd["geom"]) for cd in layers],
                            N=layers[0]["x"].shape[0], device=dev)
         chain.x.copy_(torch.from_numpy(layers[0]["x"]))
-        eager_ms, _ = run(lambda i: chain.run(), args.steps, args.warmup)
+        eager_ms, _ = run(lambda i: chain.run(), args.steps, args.warmup, 1)
         chain.capture()
-        graph_ms, _ = run(lambda i: chain.replay(), args.steps, args.warmup)
+        graph_ms, _ = run(lambda i: chain.replay(), args.steps, args.warmup, 1)
         cflops = sum(roofline.effective_flops(int(cd["mask"].sum()), cd["x"].shape[0] if j == 0 else chain.N,
                                               chain.handles[j].E, chain.handles[j].F)
                      for j, cd in enumerate(layers))
@@ -215,41 +218,85 @@ def main():
         nb = args.copy_mb << 20
         src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-
-        def copy_step(i):
-            dst.copy_(src)
-
-        cms, _ = run(copy_step, 10, 2)
+        cms, _ = run(lambda i: dst.copy_(src), 10, 2, 1)
         extra["copy_reference"] = {"bytes_per_copy": nb, "ms": round(cms, 5),
                                    "gbs_read_plus_write": round(2 * nb / (cms * 1e-3) / 1e9, 1)}
-        log(f"[bench] copy of {args.copy_mb} MiB: {cms * 1e3:.1f} us -> {2 * nb / (cms * 1e-3) / 1e9:.0f} GB/s (read+write)")
+        log(f"[bench] copy of {args.copy_mb} MiB: {2 * nb / (cms * 1e-3) / 1e9:.0f} GB/s (read+write)")
         del src, dst
 
+    # every workload layer, timed the same way (cold, rotated sets), with the launched plan
+    if not args.no_configs and not args.layer:
+        per = {}
+        for name in workloads.LAYERS:
+            if name == layer:
+                continue
+            dd, LL, hh, wws, xxs, yys, nn, _ = setup(name)
+            steps = 40
+            cms_, csem = run(lambda i: hh.forward(xxs[i], yys[i], stream=stream, workspace=wws), steps, 5, nn)
+            mm = describe(LL, hh.info(), cms_)
+            li = hh.launch_info(LL.N)
+            per[name] = {"us": round(cms_ * 1e3, 2), "sem_us": round(csem * 1e3, 2), "tflops": round(mm["tflops"], 3),
+                         "frac_of_8tbs": round(mm["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(mm["ai"], 2),
+                         "bound": mm["bound"], "roofline_frac": round(mm["frac"], 4), "nnz": hh.info()["nnz"],
+                         "launch": {k: li[k] for k in ("mapping", "variant", "groups", "splits", "units_per_wg",
+                                                       "depth", "grid", "waves", "vgprs", "lds_bytes",
+                                                       "tile_pixels", "quad")}}
+            log(f"[bench] config {name}: {cms_ * 1e3:.1f} us, {mm['tflops']:.2f} TFLOP/s, "
+                f"{mm['gbs'] / roofline.HBM_PEAK_GBS:.3f} of 8 TB/s, launch {per[name]['launch']}")
+            del dd, hh, xxs, yys
+            torch.cuda.empty_cache()
+        per[layer] = {"us": round(ms * 1e3, 2), "sem_us": round(sem * 1e3, 2), "tflops": round(m["tflops"], 3),
+                      "frac_of_8tbs": round(m["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(m["ai"], 2),
+                      "bound": m["bound"], "roofline_frac": round(m["frac"], 4), "nnz": nnz,
+                      "launch": {k: launch[k] for k in ("mapping", "variant", "groups", "splits", "units_per_wg",
+                                                        "depth", "grid", "waves", "vgprs", "lds_bytes", "tile_pixels",
+                                                        "quad")}}
+        extra["per_config"] = per
+
+    # CPU oracle: one untimed run over the whole batch (whose result also checks every output
+    # of the first timed buffer set), then three timed runs over a bounded sample of images
+    # (median), and a single-thread run over a few output planes
     cpu = None
+    parity = None
     if not args.no_cpu:
         import oracle
-        rowptr, colidx, value = oracle_csr()
+
+        rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
+        if args.fp16_word:
+            colidx, value = oracle.csr_from_words(oracle.words_from_csr(colidx, value, C, R, S), R, S)
         threads = oracle.max_threads()
         t = time.perf_counter()
-        oracle.conv_csr(d["x"][:1], rowptr, colidx, value, M, R, S, st, pad)
-        t1 = time.perf_counter() - t
-        n_img = max(1, min(N, int(args.cpu_seconds / max(t1, 1e-3))))
-        log(f"[bench] CPU oracle: 1 image {t1:.3f} s; timing {n_img} image(s) per run on {threads} threads")
-        # a batch that finishes quickly is repeated until about cpu_seconds have passed
-        reps = 0
+        y64, mag = oracle.conv_csr(d["x"], rowptr, colidx, value, M, R, S, st, pad)
+        t_full = time.perf_counter() - t
+        got = ys[0].cpu().numpy()
+        ok = oracle.within_tolerance(got, y64, mag, 1e-5)
+        parity = {"checked": int(ok.size), "outside_tolerance": int((~ok).sum()), "all_within": bool(ok.all())}
+        log(f"[bench] CPU oracle: full batch {t_full:.3f} s on {threads} threads; parity on timed buffers {parity}")
+        # a timed run repeats the whole batch until about cpu_seconds have passed
+        reps = max(1, int(math.ceil(args.cpu_seconds / max(t_full, 1e-4))))
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            for _ in range(reps):
+                oracle.conv_csr(d["x"], rowptr, colidx, value, M, R, S, st, pad)
+            times.append(time.perf_counter() - t)
+        tmed = statistics.median(times)
+        n_img = N * reps
+        planes = np.arange(min(64, M))
         t = time.perf_counter()
-        while True:
-            oracle.conv_csr(d["x"][:n_img], rowptr, colidx, value, M, R, S, st, pad)
-            reps += 1
-            tc = time.perf_counter() - t
-            if tc >= args.cpu_seconds or reps >= 10000:
-                break
-        cpu = {"value": roofline.effective_flops(nnz, n_img, E, F) * reps / tc / 1e12, "unit": "TFLOP/s",
+        oracle.conv_csr_planes(d["x"][:1], rowptr, colidx, value, M, R, S, st, pad, planes, nthreads=1)
+        t1 = time.perf_counter() - t
+        nnz_planes = int(sum(rowptr[p + 1] - rowptr[p] for p in planes))
+        cpu = {"value": round(roofline.effective_flops(nnz, n_img, E, F) / tmed / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"list-form oracle (fp64 accumulate), {reps} run(s) over {n_img} of {N} images, "
-                         f"all {M} output channels, {tc:.1f} s"}
+               "sample": f"list-form oracle (fp64 accumulate), median of 3 timed runs, each the whole batch "
+                         f"({N} images, all {M} output channels) {reps} times over ({tmed:.2f} s each), after one "
+                         f"untimed run over the batch ({t_full:.3f} s)",
+               "single_thread_tflops": round(2.0 * nnz_planes * E * F / t1 / 1e12, 6),
+               "single_thread_sample": f"{len(planes)} output planes of one image, 1 thread, {t1:.2f} s"}
 
-    traffic = stored_traffic(tag)
+    traffic = stored_traffic(layer + ("_fp16word" if args.fp16_word else "") + ("_escoin" if args.escoin else ""),
+                             launch["mapping"])
     sp = round(100 * L.sparsity)
     mask_text = {"beta_rows": f"per-channel density Beta(0.5,b) mean sparsity {sp}%",
                  "exact": f"uniform unstructured {sp}% sparsity (exact count)",
@@ -257,9 +304,11 @@ def main():
     mask_text += {"u11": ", inputs U[-1,1]", "relu_n01": ", inputs ReLU(N(0,1))"}.get(L.x_dist, "")
     mask_text += {"u11": ", weights U[-1,1]", "n0.05": ", weights N(0,0.05)", "n0.02": ", weights N(0,0.02)"}.get(
         L.w_dist, "")
+    peak = roofline.FP32_VECTOR_NONPACKED_TFLOPS if m["bound"] == "alu" else roofline.HBM_PEAK_GBS
+    achieved = m["tflops"] if m["bound"] == "alu" else m["gbs"]
     out = {
         "metric": "sparse conv effective TFLOP/s (2*nnz*N*E*F/s) and % of HBM roofline",
-        "value": round(tflops, 4),
+        "value": round(m["tflops"], 4),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -271,20 +320,22 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{layer}: N={N} C={C} H=W={H} M={M} {R}x{S} stride {st} pad {pad}, "
-                               f"{mask_text}, "
-                               f"realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)"
+                               f"{mask_text}, realized nnz={nnz} ({100 * (1 - nnz / (M * C * R * S)):.2f}% sparse)"
                                + (", weights as 32-bit words with fp16 values" if args.fp16_word else "")
-                               + (", Escoin mapping (pad_in + one output channel per workgroup)" if args.escoin else ""),
+                               + (", Escoin mapping (pad_in + one output channel per workgroup)" if args.escoin else "")
+                               + (", LDS-tile kernel" if args.lds_tile else ""),
                    "N": N, "C": C, "H": H, "W": W, "M": M, "R": R, "S": S, "stride": st, "pad": pad, "nnz": nnz},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": roofline.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / roofline.HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {"bound": m["bound"], "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s" if m["bound"] == "alu" else "GB/s", "frac": round(m["frac"], 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "sem_ms": round(sem, 6),
-        "arithmetic_intensity": round(ai, 2),
-        "flop_roofline_frac": round(tflops / flop_roof, 4),
+        "hbm": {"achieved_gbs": round(m["gbs"], 1), "peak_gbs": roofline.HBM_PEAK_GBS,
+                "frac": round(m["gbs"] / roofline.HBM_PEAK_GBS, 4), "algorithmic_bytes": int(m["alg"])},
+        "arithmetic_intensity": round(m["ai"], 2),
+        "ridge_flop_per_byte": round(roofline.FP32_VECTOR_NONPACKED_TFLOPS / roofline.HBM_PEAK_GBS * 1e3, 2),
         "parity_on_timed_buffers": parity,
-        "plan": {k: info[k] for k in ("tile_pixels", "rows_per_wave", "row_groups", "chunk_channels", "lds_bytes",
-                                      "max_wave_nnz", "entry_bytes", "mapping")},
+        "plan": launch,
         "rotated_sets": nsets,
     }
     out.update(extra)

@@ -25,15 +25,22 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = [os.path.join(ROOT, "sparse_weight_direct_amd", "csrc", f)
-                  for f in ("kernels.hip", "xcd.h", "plan.h", "pack.cpp", "api.cpp")]
+_CSRC = os.path.join(ROOT, "sparse_weight_direct_amd", "csrc")
+# the sources each kernel is built from; a weights-in-code kernel is generated at pack time
+# from the generator and the layer's weights, which the seeded workloads fix
+KERNEL_SOURCES = {
+    "sparse_direct_fwd": [os.path.join(_CSRC, f) for f in ("kernels.hip", "xcd.h", "plan.h", "pack.cpp", "api.cpp")],
+    "escoin_sconv": [os.path.join(_CSRC, f) for f in ("escoin.hip", "xcd.h", "plan.h", "api.cpp")],
+    "sc_baked": [os.path.join(_CSRC, f) for f in ("bake.cpp", "bake.h", "plan.h", "pack.cpp", "api.cpp")] +
+                [os.path.join(ROOT, "workloads.py")],
+}
 COPY_KERNELS = ("__amd_rocclr_copyBuffer", "copy", "Copy")
 
 
-def kernel_digest() -> str:
-    """Digest of the sources the forward kernel is built from (ties stored counters to them)."""
+def kernel_digest(kernel: str = "sc_baked") -> str:
+    """Digest of the sources a kernel is built from (ties stored counters to them)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -110,7 +117,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int, worklo
         res[counter] = (kib, ckib, factor, len(kern[0]) if kern else 0)
     fb = res["FETCH_SIZE"][0] * 1024 * res["FETCH_SIZE"][2]
     wb = res["WRITE_SIZE"][0] * 1024 * res["WRITE_SIZE"][2]
-    print(f"kernel_digest: {kernel_digest()}")
+    print(f"kernel_digest: {kernel_digest(kernel) if kernel in KERNEL_SOURCES else '?'}")
     print(f"workload: {workload}")
     print(f"kernel: {kernel}")
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -132,7 +139,7 @@ def main(argv=None):
     tr = sub.add_parser("traffic")
     tr.add_argument("--fetch", required=True)
     tr.add_argument("--write", required=True)
-    tr.add_argument("--kernel", default="sparse_direct_fwd")
+    tr.add_argument("--kernel", default="sc_baked")
     tr.add_argument("--copy-bytes", type=int, required=True)
     tr.add_argument("--workload", required=True)
     a = ap.parse_args(argv)

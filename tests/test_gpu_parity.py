@@ -11,20 +11,25 @@ import torch
 import oracle
 import sparse_weight_direct_amd as sc
 import workloads
-from gpu_util import assert_parity, gpu_dense, gpu_sparse
+from gpu_util import assert_layer_parity, assert_parity, gpu_dense, gpu_sparse
 
 pytestmark = pytest.mark.gpu
 
 FULL_LAYERS = ["tiny", "mid", "late", "first11", "pw1x1"]
+# the two kernels for fp32 weights: the default weights-in-code kernel and the LDS-tile kernel
+MAPPINGS = {"baked": 0, "lds_tile": sc.SC_PACK_LDS_TILE}
+MAPPING_ID = {"baked": sc.MAPPING_BAKED, "lds_tile": sc.MAPPING_LDS_TILE}
 
 
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
 @pytest.mark.parametrize("name", FULL_LAYERS)
-def test_layer_full_parity(name):
+def test_layer_full_parity(name, mapping):
     d = workloads.make(name)
     L = d["layer"]
     r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
-    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
-    assert_parity(y, r["y64"], r["mag"], name)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, flags=MAPPINGS[mapping])
+    assert h.launch_info(L.N)["mapping"] == MAPPING_ID[mapping]
+    assert_parity(y, r["y64"], r["mag"], f"{name} {mapping}")
     # packed offsets exported by the device handle are the canonical ones, bit for bit
     rowptr, off, val = h.export()
     np.testing.assert_array_equal(rowptr, r["rowptr"])
@@ -32,25 +37,17 @@ def test_layer_full_parity(name):
     np.testing.assert_array_equal(val.view(np.uint32), r["values"].view(np.uint32))
 
 
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
 @pytest.mark.parametrize("name", ["imb80", "imb90", "imb95", "imb99"])
-def test_imbalance_sweep_sampled_planes(name):
-    """Full-size 112x112 batch-8 layers in the benchmark's launch configuration; the oracle
-    recomputes a sample of (n, m) planes one by one: the heaviest and lightest channels,
-    empty channels and random ones, in the first and last image."""
+def test_imbalance_sweep_full_size(name, mapping):
+    """The 112x112 batch-8 layers in the benchmark's launch configuration, against the oracle
+    on every output; empty channels exact +0."""
     d = workloads.make(name)
     L = d["layer"]
-    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
-    assert np.isfinite(y).all()
-    rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
-    rows = np.diff(rowptr)
-    rng = np.random.default_rng(L.seed)
-    ms = {int(rows.argmax()), int(rows.argmin())} | set(int(m) for m in rng.choice(L.M, 6, replace=False))
-    ms |= set(int(m) for m in np.flatnonzero(rows == 0)[:2])
-    planes = sorted({n * L.M + m for n in (0, L.N - 1, int(rng.integers(L.N))) for m in ms})
-    y64, mag = oracle.conv_csr_planes(d["x"], rowptr, colidx, value, L.M, L.R, L.S, L.stride, L.pad, planes)
-    got = np.stack([y[p // L.M, p % L.M] for p in planes])
-    assert_parity(got, y64, mag, name)
-    # empty channels are exact +0
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, flags=MAPPINGS[mapping])
+    assert h.launch_info(L.N)["mapping"] == MAPPING_ID[mapping]
+    assert_layer_parity(name, y, f"{name} {mapping}")
+    rows = np.diff(oracle.csr_from_dense(d["w"], d["mask"])[0])
     for m in np.flatnonzero(rows == 0):
         assert np.all(y[:, m] == 0) and not np.signbit(y[:, m]).any()
 
@@ -70,12 +67,13 @@ def _tiny_cases(count, seed0):
     return out
 
 
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
 @pytest.mark.parametrize("c", _tiny_cases(40, 3), ids=lambda c: "N{N}C{C}H{H}W{W}M{M}R{R}S{S}st{stride}p{pad}k{keep}".format(**c))
-def test_random_shapes(c):
+def test_random_shapes(c, mapping):
     d = workloads.make_custom(c["N"], c["C"], c["H"], c["W"], c["M"], c["R"], c["S"], c["stride"], c["pad"],
                               c["keep"], c["seed"])
     r = oracle.reference(d["x"], d["w"], d["mask"], c["stride"], c["pad"])
-    y, _ = gpu_sparse(d["x"], d["w"], d["mask"], c["stride"], c["pad"])
+    y, _ = gpu_sparse(d["x"], d["w"], d["mask"], c["stride"], c["pad"], flags=MAPPINGS[mapping])
     assert_parity(y, r["y64"], r["mag"], str(c))
 
 
@@ -106,14 +104,17 @@ def test_wide_layout_plans(plan, pad, monkeypatch):
     assert_parity(y, r["y64"], r["mag"], f"{plan} pad {pad}")
 
 
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
 @pytest.mark.parametrize("name", ["tiny", "mid"])
-def test_misaligned_input_pointer(name):
-    """An input that is 4-byte but not 16-byte aligned: the wide layout is then staged with
-    4-byte loads (same LDS layout); the output is also written through an offset view."""
+def test_misaligned_input_pointer(name, mapping):
+    """An input that is 4-byte but not 16-byte aligned: the LDS-tile kernel's wide layout is
+    then staged with 4-byte loads (same LDS layout); the output is also written through an
+    offset view."""
     d = workloads.make(name)
     L = d["layer"]
     r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
-    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=MAPPINGS[mapping])
     xs = torch.empty(d["x"].size + 1, dtype=torch.float32, device="cuda")
     x = xs[1:].view(d["x"].shape)
     x.copy_(torch.from_numpy(d["x"]))
@@ -153,9 +154,10 @@ def test_padding_at_least_the_filter_width(N, C, H, W, M, R, S, pad, plan, monke
     assert_parity(y, r["y64"], r["mag"], f"pad {pad} S {S} {plan}")
 
 
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
 @pytest.mark.parametrize("R,S,stride,pad,H,W", [(3, 3, 1, 1, 30, 41), (11, 11, 4, 0, 67, 59), (5, 3, 2, 2, 17, 23),
                                                 (1, 1, 1, 0, 7, 7)])
-def test_single_nonzero_bit_exact(R, S, stride, pad, H, W):
+def test_single_nonzero_bit_exact(R, S, stride, pad, H, W, mapping):
     rng = np.random.default_rng(R * 31 + W)
     N, C, M = 2, 5, 6
     x = rng.uniform(-1, 1, (N, C, H, W)).astype(np.float32)
@@ -163,36 +165,39 @@ def test_single_nonzero_bit_exact(R, S, stride, pad, H, W):
     w[2, 4, R - 1, 0] = np.float32(0.8125)
     w[5, 0, 0, S - 1] = np.float32(-1.3)
     r = oracle.reference(x, w, None, stride, pad)
-    y, _ = gpu_sparse(x, w, None, stride, pad)
+    y, _ = gpu_sparse(x, w, None, stride, pad, flags=MAPPINGS[mapping])
     np.testing.assert_array_equal(y.view(np.uint32), r["y"].view(np.uint32))
 
 
-def test_delta_kernel_identity_bit_exact():
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_delta_kernel_identity_bit_exact(mapping):
     d = workloads.make_custom(2, 24, 31, 29, 24, 3, 3, 1, 1, 0.0, 8)
     w = np.zeros((24, 24, 3, 3), np.float32)
     for m in range(24):
         w[m, m, 1, 1] = 1.0
-    y, _ = gpu_sparse(d["x"], w, None, 1, 1)
+    y, _ = gpu_sparse(d["x"], w, None, 1, 1, flags=MAPPINGS[mapping])
     np.testing.assert_array_equal(y.view(np.uint32), d["x"].view(np.uint32))
 
 
-def test_all_zero_weights_and_empty_rows():
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_all_zero_weights_and_empty_rows(mapping):
     d = workloads.make_custom(2, 8, 12, 12, 40, 3, 3, 1, 1, 0.2, 21)
     mask = d["mask"].copy()
     mask[::3] = 0
-    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1, flags=MAPPINGS[mapping])
     assert np.all(y[:, ::3] == 0) and not np.signbit(y[:, ::3]).any()
-    y0, _ = gpu_sparse(d["x"], d["w"], np.zeros_like(mask), 1, 1)
+    y0, _ = gpu_sparse(d["x"], d["w"], np.zeros_like(mask), 1, 1, flags=MAPPINGS[mapping])
     assert np.all(y0 == 0) and not np.signbit(y0).any()
 
 
-def test_skewed_rows_one_dense_channel():
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_skewed_rows_one_dense_channel(mapping):
     """One fully dense output channel among nearly empty ones (worst case for balance)."""
     d = workloads.make_custom(2, 64, 20, 20, 32, 3, 3, 1, 1, 0.02, 31)
     mask = d["mask"].copy()
     mask[7] = 1
     r = oracle.reference(d["x"], d["w"], mask, 1, 1)
-    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    y, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1, flags=MAPPINGS[mapping])
     assert_parity(y, r["y64"], r["mag"], "skewed")
 
 
@@ -208,7 +213,7 @@ def test_split_rows_many_units(plan, monkeypatch):
     mask[3] = 1
     mask[20] = 1
     r = oracle.reference(d["x"], d["w"], mask, 1, 1)
-    y, h = gpu_sparse(d["x"], d["w"], mask, 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], mask, 1, 1, flags=sc.SC_PACK_LDS_TILE)
     assert h.info()["split_pieces"] > 0
     assert_parity(y, r["y64"], r["mag"], "split " + plan)
     y2, _ = gpu_sparse(d["x"], d["w"], mask, 1, 1, handle=h)
@@ -240,20 +245,24 @@ def test_split_rows_in_some_groups_finish_promptly(name, plan, monkeypatch):
     assert e0.elapsed_time(e1) < 20.0, f"forward took {e0.elapsed_time(e1):.1f} ms"
 
 
-def test_fewer_channels_than_wavefronts():
-    """M = 4 output channels on 15 computing wavefronts: every channel is split."""
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_fewer_channels_than_wavefronts(mapping):
+    """M = 4 output channels: on the LDS-tile kernel's 15 computing wavefronts every channel
+    is split; the weights-in-code kernel holds all four in one wavefront."""
     d = workloads.make_custom(2, 16, 30, 30, 4, 3, 3, 1, 1, 0.5, 42)
     r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
-    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1, flags=MAPPINGS[mapping])
     assert h.info()["split_pieces"] > 0
     assert_parity(y, r["y64"], r["mag"], "M=4")
 
 
-def test_csr_input_path_and_determinism():
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_csr_input_path_and_determinism(mapping):
     d = workloads.make("mid")
     L = d["layer"]
     rowptr, colidx, value = oracle.csr_from_dense(d["w"], d["mask"])
-    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=value, colidx=colidx, rowptr=rowptr)
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=value, colidx=colidx, rowptr=rowptr,
+                  flags=MAPPINGS[mapping])
     y1, _ = gpu_sparse(d["x"], d["w"], None, L.stride, L.pad, handle=h)
     y2, _ = gpu_sparse(d["x"], d["w"], None, L.stride, L.pad, handle=h)
     np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
@@ -261,11 +270,14 @@ def test_csr_input_path_and_determinism():
     assert_parity(y1, r["y64"], r["mag"], "csr")
 
 
-def test_batch_sizes_share_one_handle():
-    """N is a forward-time argument: one handle, several batch sizes, incl. N = 0."""
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_batch_sizes_share_one_handle(mapping):
+    """N is a forward-time argument: one handle, several batch sizes, incl. N = 0 (the
+    weights-in-code handle launches different kernels of its set for different N)."""
     d = workloads.make("late")
     L = d["layer"]
-    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=MAPPINGS[mapping])
     for n in (1, 3, 32):
         x = d["x"][:n]
         r = oracle.reference(x, d["w"], d["mask"], L.stride, L.pad)
@@ -301,13 +313,14 @@ def test_dense_baseline_parity(name):
     assert_parity(y, r["y64"], r["mag"], "dense " + name)
 
 
-def test_side_stream():
+@pytest.mark.parametrize("mapping", sorted(MAPPINGS))
+def test_side_stream(mapping):
     d = workloads.make("mid")
     L = d["layer"]
     r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        y, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, stream=s)
+        y, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, stream=s, flags=MAPPINGS[mapping])
     assert_parity(y, r["y64"], r["mag"], "stream")
 
 
@@ -336,7 +349,7 @@ def _sweep_cases(count, seed):
     return out
 
 
-@pytest.mark.parametrize("plan", ["", "QUAD=1"])
+@pytest.mark.parametrize("plan", ["", "QUAD=1", "NARROW"])
 def test_random_sweep_wide_ranges(plan, monkeypatch):
     """150 seeded shapes per plan kind against the oracle, failures listed together (a sweep
     like this one found the wide-layout bug with pad >= S).  A forced quad plan may not fit
