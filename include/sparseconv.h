@@ -280,6 +280,18 @@ sc_status sparseconv_export_packed(const sc_handle* h, int32_t* rowptr, uint32_t
 sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t* words);
 
 /*
+ * Read the handle's device status word into *status (host), and with clear != 0 reset it to
+ * 0.  Bit 0 set: in some launch of the LDS-tile kernel on this handle since the last clear, a
+ * wavefront's bounded wait on a counter in LDS gave up (after about 2^22 sleeps, far beyond
+ * any real wait): that launch's output may be wrong.  The kernel never hangs on such a
+ * failure; this word is how it is reported.  The weights-in-code and "Escoin" kernels have no
+ * such waits.  Reads device memory with a blocking copy: synchronise the streams that ran
+ * forwards on this handle first.  SC_EINVAL on a NULL handle or status, or a host-only
+ * handle; SC_EDEVICE if the copy fails.
+ */
+sc_status sparseconv_device_status(const sc_handle* h, uint32_t* status, int32_t clear);
+
+/*
  * Describe the launch a forward of N >= 1 images would make on this handle (the plan the
  * forward's cost estimate picks for N), without launching anything.  SC_EINVAL on a NULL
  * handle or out, SC_ESHAPE for N < 1.
@@ -295,8 +307,11 @@ sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out);
  */
 sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t cap, int64_t* len);
 
-/* Free the handle and its device buffers.  NULL is a no-op.  Must not race a forward
- * still running on the device that reads this handle (synchronise the stream first). */
+/* Free the handle and its device buffers.  NULL, or a pointer that is not a live handle
+ * (already destroyed, or never returned by sparseconv_pack), is ignored: the library keeps a
+ * registry of live handles, and every entry point reports SC_EINVAL ("invalid or destroyed
+ * handle") for a pointer not in it.  Must not race a forward still running on the device that
+ * reads this handle (synchronise the stream first). */
 void sparseconv_destroy(sc_handle* h);
 
 /* Message of the calling thread's last failure ("" if none).  Valid until that thread's

@@ -46,8 +46,8 @@ _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: 
 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
             "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
-            "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_destroy",
-            "sparseconv_last_error")
+            "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_device_status",
+            "sparseconv_destroy", "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -101,6 +101,8 @@ _lib.sparseconv_export_kernel_source.restype = _i32
 _lib.sparseconv_export_kernel_source.argtypes = [_vp, ctypes.c_char_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
 _lib.sparseconv_launch_info.restype = _i32
 _lib.sparseconv_launch_info.argtypes = [_vp, _i32, ctypes.POINTER(sc_launch)]
+_lib.sparseconv_device_status.restype = _i32
+_lib.sparseconv_device_status.argtypes = [_vp, ctypes.POINTER(_u32), _i32]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -237,12 +239,15 @@ def sparseconv_launch_info(handle: int, N: int) -> dict:
     return out.as_dict()
 
 
+def sparseconv_device_status(handle: int, clear: bool = False) -> int:
+    """The handle's device status word (bit 0: a bounded wait in the LDS-tile kernel gave up)."""
+    st = _u32()
+    _check(_lib.sparseconv_device_status(handle, ctypes.byref(st), 1 if clear else 0), "sparseconv_device_status")
+    return st.value
+
+
 def sparseconv_destroy(handle) -> None:
     _lib.sparseconv_destroy(handle)
-
-
-def out_size(n_in: int, pad: int, k: int, stride: int) -> int:
-    return (n_in + 2 * pad - k) // stride + 1
 
 
 class Handle:
@@ -251,9 +256,10 @@ class Handle:
     def __init__(self, M, C, R, S, H, W, stride, pad, *, values=None, mask=None, colidx=None,
                  rowptr=None, flags=0):
         self.geom = dict(M=M, C=C, R=R, S=S, H=H, W=W, stride=stride, pad=pad)
-        self.E, self.F = out_size(H, pad, R, stride), out_size(W, pad, S, stride)
         self.ptr = sparseconv_pack(M, C, R, S, H, W, stride, pad, values=values, mask=mask,
                                    colidx=colidx, rowptr=rowptr, flags=flags)
+        info = sparseconv_query(self.ptr)  # output extent as the library computes it
+        self.E, self.F = info["E"], info["F"]
 
     @classmethod
     def from_dense(cls, w: np.ndarray, H: int, W: int, stride: int, pad: int, mask=None, flags=0):
@@ -275,6 +281,9 @@ class Handle:
     def launch_info(self, N: int) -> dict:
         return sparseconv_launch_info(self.ptr, N)
 
+    def device_status(self, clear: bool = False) -> int:
+        return sparseconv_device_status(self.ptr, clear)
+
     def workspace_size(self, N: int) -> int:
         return sparseconv_workspace_size(self.ptr, N)
 
@@ -284,9 +293,16 @@ class Handle:
         used; handles packed with SC_PACK_ESCOIN_MAP need one."""
         import torch
         g = self.geom
+        if x.dim() != 4 or tuple(x.shape[1:]) != (g["C"], g["H"], g["W"]):
+            raise ValueError(f"input shape {tuple(x.shape)} is not (N, {g['C']}, {g['H']}, {g['W']})")
         N = x.shape[0]
         if out is None:
             out = torch.empty((N, g["M"], self.E, self.F), dtype=torch.float32, device=x.device)
+        elif tuple(out.shape) != (N, g["M"], self.E, self.F):
+            raise ValueError(f"output shape {tuple(out.shape)} is not ({N}, {g['M']}, {self.E}, {self.F})")
+        for name, t in (("input", x), ("output", out)):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor")
         if workspace is None:
             sparseconv_forward(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
                                g["stride"], g["pad"], stream)

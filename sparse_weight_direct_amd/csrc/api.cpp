@@ -16,8 +16,11 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <mutex>
 #include <numeric>
 #include <string>
+#include <thread>
+#include <unordered_set>
 #include <vector>
 
 #include "../../include/sparseconv.h"
@@ -27,9 +30,26 @@
 namespace {
 
 constexpr uint64_t kMagic = 0x53434f4e56484e44ull;  // live handle
-constexpr uint64_t kDead = 0x444541444841444eull;   // destroyed handle
 
 thread_local std::string g_err;
+
+// Live handles: every entry point checks its handle against this set before touching it, so
+// a destroyed (or never created) handle is reported as invalid instead of being read.
+std::mutex g_live_mu;
+std::unordered_set<const void*> g_live;
+
+void live_add(const void* h) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  g_live.insert(h);
+}
+bool live_remove(const void* h) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.erase(h) == 1;
+}
+bool live_has(const void* h) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.count(h) == 1;
+}
 
 sc_status fail(sc_status s, const std::string& msg) {
   g_err = msg;
@@ -93,11 +113,12 @@ struct sc_handle {
   std::vector<BakedKernel> bk;
   std::string bake_why;           // why the layer was not baked ("" if it was)
   int cus;                        // compute units of the device (256 on the host)
+  uint32_t* d_status;             // device status word (bit 0: a bounded wait gave up)
 };
 
 namespace {
 
-bool valid_handle(const sc_handle* h) { return h && h->magic == kMagic; }
+bool valid_handle(const sc_handle* h) { return h && live_has(h) && h->magic == kMagic; }
 
 // IEEE 754 binary16 bits of an fp32 value, rounded to nearest with ties to even, by integer
 // operations on the fp32 encoding: rebias the exponent (normal halves) or shift the full
@@ -307,15 +328,25 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
       else if (plan_env && plan_env[0]) bake_why = "SPARSECONV_PLAN forces an LDS-tile plan";
       else if (bake_env && std::strcmp(bake_env, "off") == 0) bake_why = "SPARSECONV_BAKE=off";
       else {
-        for (sc::BakePlan& bp : sc::bake_candidates(g, rowptr, col, sc::bake_force_from_env(), &bake_why)) {
-          BakedKernel k;
-          k.p = std::move(bp);
-          std::string why;
-          if (sc::bake_generate(g, rowptr, col, val, &k.p, &k.src, &why) && sc::bake_assemble(k.src, &k.elf, &why))
-            bk.push_back(std::move(k));
-          else if (bk.empty())
-            bake_why = why;
+        // generate and assemble the candidate kernels in parallel (one thread each)
+        std::vector<sc::BakePlan> cands = sc::bake_candidates(g, rowptr, col, sc::bake_force_from_env(), &bake_why);
+        std::vector<BakedKernel> built(cands.size());
+        std::vector<std::string> whys(cands.size());
+        std::vector<char> good(cands.size(), 0);
+        auto work = [&](size_t i) {
+          built[i].p = cands[i];
+          good[i] = sc::bake_generate(g, rowptr, col, val, &built[i].p, &built[i].src, &whys[i]) &&
+                    sc::bake_assemble(built[i].src, &built[i].elf, &whys[i]);
+        };
+        std::vector<std::thread> th;
+        for (size_t i = 1; i < cands.size(); i++) th.emplace_back(work, i);
+        if (!cands.empty()) work(0);
+        for (auto& t : th) t.join();
+        for (size_t i = 0; i < cands.size(); i++) {
+          if (good[i]) bk.push_back(std::move(built[i]));
+          else if (bk.empty() && i == 0) bake_why = whys[i];
         }
+        if (!bk.empty() && !good[0]) bk.clear();  // the base kernel is required
       }
     }
     const bool baked = !bk.empty();
@@ -325,10 +356,12 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
 
     h = new sc_handle();
     h->magic = kMagic;
+    live_add(h);
     h->baked = baked;
     h->bk = std::move(bk);
     h->bake_why = std::move(bake_why);
     h->cus = 256;
+    h->d_status = nullptr;
     h->g = g;
     h->nnz = nnz;
     h->h16 = h16;
@@ -482,7 +515,7 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_EDEVICE, "no HIP device available");
       }
       auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-      size_t total = al(esc_ent.size() * 4) + (escoin ? al(rowptr.size() * 4) : 0);
+      size_t total = 256 + al(esc_ent.size() * 4) + (escoin ? al(rowptr.size() * 4) : 0);  // status word first
       for (const Variant& v : h->var)
         total += al(v.ent.size() * 4) + al(v.bstart.size() * 4) + al(v.sched.slot_row.size() * 4) +
                  al(v.sched.slot_comb.size() * 4);
@@ -493,6 +526,12 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
         return fail(SC_ENOMEM, "hipMalloc of the packed filter bank failed");
       }
       char* base = static_cast<char*>(h->dmem);
+      h->d_status = reinterpret_cast<uint32_t*>(base);
+      if (hipMemset(base, 0, 256) != hipSuccess) {
+        sparseconv_destroy(h);
+        return fail(SC_EDEVICE, "clearing the device status word failed");
+      }
+      base += 256;
       if (escoin) {
         h->d_esc_ent = reinterpret_cast<const uint32_t*>(base);
         h->d_esc_rowptr = reinterpret_cast<const int32_t*>(base + al(esc_ent.size() * 4));
@@ -646,11 +685,10 @@ sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t
 }
 
 void sparseconv_destroy(sc_handle* h) {
-  if (!h || h->magic != kMagic) return;
+  if (!h || !live_remove(h)) return;
   for (BakedKernel& k : h->bk)
     if (k.mod) (void)hipModuleUnload(k.mod);
   if (h->dmem) (void)hipFree(h->dmem);
-  h->magic = kDead;
   delete h;
 }
 
@@ -696,6 +734,9 @@ sc::KArgs make_args(const sc::Geom& g, const sc::Plan& p, const float* in, float
   a.tp = p.tp;
   a.ring_words = p.ring_words;
   a.ntiles = (int)((a.ext_total + p.tp - 1) / p.tp);
+  a.spin_limit = 1 << 22;
+  if (const char* e = std::getenv("SPARSECONV_SPIN_LIMIT"))  // tests of the failure report only
+    if (std::atoi(e) > 0) a.spin_limit = std::atoi(e);
   return a;
 }
 
@@ -858,6 +899,7 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
   sc::KArgs a = make_args(g, v.p, input, output, N);
+  a.status = h->d_status;
   a.ent = v.d_ent;
   a.seg = v.d_seg;
   a.slot_row = v.d_slot;
@@ -932,6 +974,21 @@ sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out) 
   out->chunk_channels = v.p.Cc;
   out->quad = v.p.quad;
   out->waves = out->grid * v.p.NW;
+  return SC_OK;
+}
+
+sc_status sparseconv_device_status(const sc_handle* h, uint32_t* status, int32_t clear) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!status) return fail(SC_EINVAL, "status is NULL");
+  if (h->host_only || !h->d_status) return fail(SC_EINVAL, "handle was packed with SC_PACK_HOST_ONLY");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+  if (hipMemcpy(status, h->d_status, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(SC_EDEVICE, "reading the device status word failed");
+  if (clear && *status != 0 && hipMemset(h->d_status, 0, 4) != hipSuccess)
+    return fail(SC_EDEVICE, "clearing the device status word failed");
   return SC_OK;
 }
 

@@ -20,6 +20,7 @@
 #include <cstring>
 #include <map>
 #include <numeric>
+#include <string>
 
 namespace sc {
 
@@ -57,7 +58,7 @@ namespace {
 constexpr int kMaxVgpr = 256;   // architectural VGPRs a VALU instruction can name
 constexpr int kFixedV = 5;      // v0 id, v1 lane, v2 zero, v3 out-of-range marker, v4 output offset
 constexpr int kTemps = 12;      // prologue temporaries
-constexpr long long kCodeMax = 4ll << 20;  // refuse kernels above 4 MB of code
+constexpr long long kCodeMax = 2ll << 20;  // refuse kernels above 2 MB of code (~250K non-zeros)
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
@@ -275,6 +276,10 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
   p.Pb = g.F + p.maxsq;
   const int M = g.M;
   const long long nnz = rowptr[M];
+  if (nnz * 8 > kCodeMax) {  // 8 bytes of code per non-zero: refuse before generating
+    *why = "too many non-zeros for a weights-in-code kernel (" + std::to_string(nnz) + ")";
+    return out;
+  }
   // base groups: the fewest whose accumulators fit the register target (measured on the
   // 112x112 layers, one group per wavefront beats more groups even with several hundred KB of
   // code: more groups repeat the row loads and lane shifts per group)

@@ -117,12 +117,18 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef SC_VM4
 
 // Bounded wait until the LDS counter *p reaches target (every lane reads the same word).
-constexpr int kSpinLimit = 1 << 22;  // sleeps of about 64 cycles: far beyond any real wait
-__device__ __forceinline__ void lds_wait_ge(const uint32_t* p, uint32_t target) {
-  for (int i = 0; i < kSpinLimit; i++) {
+// a.spin_limit sleeps of about 64 cycles (2^22 by default: far beyond any real wait).  A
+// wait that gives up sets bit 0 of the handle's device status word (a vector global atomic
+// from lane 0), so a synchronisation failure is reported (sparseconv_device_status) instead
+// of passing as a plausible result; the wavefront then carries on, so every kernel ends.
+__device__ __forceinline__ void lds_wait_ge(const uint32_t* p, uint32_t target, const KArgs& a) {
+  int i = 0;
+  for (; i < a.spin_limit; i++) {
     if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (i == a.spin_limit && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("" ::: "memory");
 }
 
@@ -627,7 +633,7 @@ __device__ __forceinline__ void producer(const KArgs& a, const float* __restrict
                            __HIP_MEMORY_SCOPE_WORKGROUP);
         pending = -1;
       }
-      lds_wait_ge(&done[buf], target);
+      lds_wait_ge(&done[buf], target, a);
     }
     if (it.tile != cur_tile) {
       cur_tile = it.tile;
@@ -704,7 +710,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
   int units_done = 0;  // units finished by this workgroup
   for (int s = 0; s < S; s++) {
     const int buf = s % a.D;
-    lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1));
+    lds_wait_ge(&ready[buf], (uint32_t)(s / a.D + 1), a);
     const float* slot = lds + buf * a.slot_words;
     if constexpr (Q) {
       // the consumer's entry ring: entry i of the step's block sits at i & 127.  Before
@@ -783,7 +789,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
         const int v = rows[o];
         if (v <= -2) {
           const int b = -2 - v;
-          lds_wait_ge(&pcons[b], (uint32_t)gen);
+          lds_wait_ge(&pcons[b], (uint32_t)gen, a);
           float* pb = pbuf + b * (64 * K) + lane;
 #pragma unroll
           for (int q = 0; q < K; q++) pb[64 * q] = acc[o][q];
@@ -804,7 +810,7 @@ __device__ __forceinline__ void consumer(const KArgs& a, float* __restrict__ y, 
           const int cm = comb[o];
           for (int i = 0; i < (cm & 255); i++) {
             const int b = (cm >> 8) + i;
-            lds_wait_ge(&pfull[b], (uint32_t)(gen + 1));
+            lds_wait_ge(&pfull[b], (uint32_t)(gen + 1), a);
             const float* pb = pbuf + b * (64 * K) + lane;
 #pragma unroll
             for (int q = 0; q < K; q++) acc[o][q] += pb[64 * q];

@@ -134,6 +134,8 @@ struct KArgs {
   int ring_words;         // quad plans: LDS word offset of the entry rings (Plan::ring_words)
   long long x_words;      // N * C * H * W
   long long ext_total;    // N * img_ext
+  uint32_t* status;       // the handle's device status word (bit 0: a bounded wait gave up)
+  int spin_limit;         // sleeps before a wait gives up
 };
 
 bool make_geom(int M, int C, int R, int S, int H, int W, int st, int pad, Geom* g);

@@ -32,6 +32,7 @@ def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None, f
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     assert ms < MAX_FORWARD_MS, f"forward took {ms:.1f} ms: a bounded wait in the kernel timed out"
+    assert handle.device_status() == 0, "a bounded wait in the kernel gave up (device status word)"
     return out.cpu().numpy(), handle
 
 

@@ -263,3 +263,47 @@ def test_escoin_mapping_handle_on_host():
     st, msg = _status(lambda: sc.sparseconv_forward_workspace(h.ptr, 1 << 20, 1 << 24, 1, L.C, L.H, L.W, L.M, L.R,
                                                               L.S, L.stride, L.pad, 1 << 28, 1 << 24, stream=0))
     assert st == sc.SC_EINVAL and "HOST_ONLY" in msg
+
+
+def test_destroyed_and_foreign_handles_are_rejected():
+    """The library keeps a registry of live handles: a destroyed handle, a second destroy and
+    a pointer that never was a handle are reported (or ignored by destroy), never read."""
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = _pack_host(d, L)
+    ptr = h.ptr
+    assert sc.sparseconv_query(ptr)["M"] == L.M
+    sc.sparseconv_destroy(ptr)
+    h.ptr = None
+    st, msg = _status(lambda: sc.sparseconv_query(ptr))
+    assert st == sc.SC_EINVAL and "destroyed" in msg
+    sc.sparseconv_destroy(ptr)  # second destroy: ignored
+    buf = np.zeros(64, np.uint8)
+    fake = buf.ctypes.data
+    st, _ = _status(lambda: sc.sparseconv_query(fake))
+    assert st == sc.SC_EINVAL
+    sc.sparseconv_destroy(fake)  # not a handle: ignored
+    st, _ = _status(lambda: sc.sparseconv_export_packed(fake))
+    assert st == sc.SC_EINVAL
+
+
+def test_binding_checks_tensor_shapes_before_launch():
+    """Handle.forward rejects an input or output whose shape differs from the handle's
+    geometry before any pointer reaches the library (so a wrong-sized tensor cannot make the
+    kernel read or write past it); output sizes come from the library's own E and F."""
+    import torch
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = _pack_host(d, L)
+    assert (h.E, h.F) == (L.E, L.F)
+    good_x = torch.zeros((1, L.C, L.H, L.W))
+    with pytest.raises(ValueError, match="input shape"):
+        h.forward(torch.zeros((1, L.C, L.H + 1, L.W)))
+    with pytest.raises(ValueError, match="input shape"):
+        h.forward(torch.zeros((L.C, L.H, L.W)))
+    with pytest.raises(ValueError, match="output shape"):
+        h.forward(good_x, torch.zeros((1, L.M, L.E, L.F + 1)))
+    with pytest.raises(ValueError, match="output shape"):
+        h.forward(good_x, torch.zeros((2, L.M, L.E, L.F)))
+    with pytest.raises(ValueError, match="float32"):
+        h.forward(good_x.double(), torch.zeros((1, L.M, L.E, L.F)))

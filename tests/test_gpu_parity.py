@@ -377,3 +377,26 @@ def test_random_sweep_wide_ranges(plan, monkeypatch):
             failures.append((c, int((~ok).sum())))
     assert ran >= 140, ran
     assert not failures, failures[:5]
+
+
+def test_bounded_wait_give_up_is_reported(monkeypatch):
+    """Every wait of the LDS-tile kernel is bounded; one that gives up sets the handle's
+    device status word.  A spin limit of one sleep, set from the host, makes waits give up
+    in a normal launch (the kernel still ends: its loops have fixed trip counts); the status
+    reports it, and after clearing, a launch with the normal limit is clean and correct."""
+    d = workloads.make("mid")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_LDS_TILE)
+    x = torch.from_numpy(d["x"]).cuda()
+    y = torch.empty((L.N, L.M, L.E, L.F), device="cuda")
+    assert h.device_status() == 0
+    monkeypatch.setenv("SPARSECONV_SPIN_LIMIT", "1")
+    h.forward(x, y)
+    torch.cuda.synchronize()
+    assert h.device_status(clear=True) & 1
+    assert h.device_status() == 0
+    monkeypatch.delenv("SPARSECONV_SPIN_LIMIT")
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    got, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, handle=h)
+    assert_parity(got, r["y64"], r["mag"], "after clearing")
