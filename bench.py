@@ -169,16 +169,9 @@ def main():
     if not args.no_dense:
         wd = torch.from_numpy(d["w_masked"]).to(dev)
         yd = torch.empty((N, M, E, F), dtype=torch.float32, device=dev)
-        if hasattr(sc, "sparseconv_dense_forward"):
-            def dense_step(i):
-                sc.sparseconv_dense_forward(wd, xs[i], yd, N, C, H, W, M, R, S, st, pad, stream)
-            kind = "sparseconv_dense_forward (dense weights on the device, every tap)"
-        else:
-            hd = sc.Handle(M, C, R, S, H, W, st, pad, values=d["w_masked"], flags=sc.SC_PACK_ALL_TAPS)
-
-            def dense_step(i):
-                hd.forward(xs[i], yd, stream=stream)
-            kind = "LDS-tile kernel on a handle storing every tap"
+        def dense_step(i):
+            sc.sparseconv_dense_forward(wd, xs[i], yd, N, C, H, W, M, R, S, st, pad, stream)
+        kind = "sparseconv_dense_forward (dense fp32 weights on the device, every tap, vector FMA)"
         dsteps = max(10, args.steps // 10)
         dms, dsem = run(dense_step, dsteps, 2, nsets)
         extra["dense_direct"] = {"kind": kind, "ms_per_step": round(dms, 5), "sem_ms": round(dsem, 5),
@@ -194,6 +187,8 @@ def main():
 
         mms, msem = run(miopen_step, max(10, args.steps // 10), 3, nsets)
         extra["torch_conv2d_miopen"] = {"ms_per_step": round(mms, 5), "sem_ms": round(msem, 5),
+                                        "tflops_dense_work": round(roofline.dense_flops(N, C, M, E, F, R, S)
+                                                                   / (mms * 1e-3) / 1e12, 3),
                                         "speedup_sparse_over_miopen": round(mms / ms, 3)}
         log(f"[bench] torch conv2d (MIOpen, dense fp32) {mms * 1e3:.1f} us/step")
 

@@ -307,6 +307,28 @@ sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out);
  */
 sc_status sparseconv_export_kernel_source(const sc_handle* h, char* buf, int64_t cap, int64_t* len);
 
+/*
+ * Dense direct convolution baseline: the same output as a handle holding every tap, computed
+ * from a dense weight tensor already on the device, with no packing and no handle.  Every
+ * term of the sum above is evaluated, zero weights included: the dense work and traffic of
+ * Tuteja et al., Sec. 4 Eq. (5)/(6) (2*N*E*F*M*C*R*S flops), the baseline their Sec. 6.1 /
+ * Fig. 5 compare the sparse kernel with, here on the same GPU.
+ *   w_dense_dev  device, M*C*R*S fp32, (m, c, r, s) row-major, 4-byte aligned; read only.
+ *   input        device, N*C*H*W fp32, NCHW contiguous, 4-byte aligned.
+ *   output       device, N*M*E*F fp32, NCHW contiguous, overwritten; must overlap neither
+ *                input nor w_dense_dev.
+ *   N >= 0 (0 is a no-op); M,C,R,S,H,W >= 1, stride >= 1, pad >= 0, E and F >= 1.
+ *   hip_stream   hipStream_t to launch on (NULL: the default stream), on the current device.
+ * Asynchronous, like sparseconv_forward.  Summation order per output: filter rows, then input
+ * channels, then filter columns (it differs from the sparse kernels' order, so results agree
+ * to rounding, not bit for bit).  Limits (SC_EUNSUPPORTED): N*C*H*W*4 and N*M*E*F*4 below
+ * 2^31 bytes, M*C*R*S < 2^31.  Errors: SC_EINVAL (null or misaligned pointers, overlap),
+ * SC_ESHAPE (a dimension out of range, E or F < 1), SC_EDEVICE (launch failure).
+ */
+sc_status sparseconv_dense_forward(const float* w_dense_dev, const float* input, float* output, int32_t N,
+                                   int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                                   int32_t stride, int32_t pad, void* hip_stream);
+
 /* Free the handle and its device buffers.  NULL, or a pointer that is not a live handle
  * (already destroyed, or never returned by sparseconv_pack), is ignored: the library keeps a
  * registry of live handles, and every entry point reports SC_EINVAL ("invalid or destroyed

@@ -47,7 +47,7 @@ _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
             "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
             "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_device_status",
-            "sparseconv_destroy", "sparseconv_last_error")
+            "sparseconv_dense_forward", "sparseconv_destroy", "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -103,6 +103,8 @@ _lib.sparseconv_launch_info.restype = _i32
 _lib.sparseconv_launch_info.argtypes = [_vp, _i32, ctypes.POINTER(sc_launch)]
 _lib.sparseconv_device_status.restype = _i32
 _lib.sparseconv_device_status.argtypes = [_vp, ctypes.POINTER(_u32), _i32]
+_lib.sparseconv_dense_forward.restype = _i32
+_lib.sparseconv_dense_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -244,6 +246,29 @@ def sparseconv_device_status(handle: int, clear: bool = False) -> int:
     st = _u32()
     _check(_lib.sparseconv_device_status(handle, ctypes.byref(st), 1 if clear else 0), "sparseconv_device_status")
     return st.value
+
+
+def sparseconv_dense_forward(w, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
+    """Dense direct baseline: ``w`` a device tensor (or address) of M*C*R*S fp32 weights."""
+    _check(_lib.sparseconv_dense_forward(_dev_ptr(w), _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad,
+                                         _stream_ptr(stream)), "sparseconv_dense_forward")
+
+
+def dense_forward(w, x, out, stride: int, pad: int, stream=None):
+    """Dense direct convolution of x (N, C, H, W) with every tap of w (M, C, R, S), both float32
+    CUDA tensors, into out (N, M, E, F)."""
+    if w.dim() != 4 or x.dim() != 4 or out.dim() != 4:
+        raise ValueError("w, x and out must be 4-d tensors")
+    M, C, R, S = (int(v) for v in w.shape)
+    N, Cx, H, W = (int(v) for v in x.shape)
+    if Cx != C:
+        raise ValueError(f"input has {Cx} channels, the weights {C}")
+    # the library writes N*M*E*F outputs: out must have exactly that shape
+    E, F = (H + 2 * pad - R) // stride + 1, (W + 2 * pad - S) // stride + 1
+    if tuple(out.shape) != (N, M, E, F):
+        raise ValueError(f"output shape {tuple(out.shape)} is not ({N}, {M}, {E}, {F})")
+    sparseconv_dense_forward(w, x, out, N, C, H, W, M, R, S, stride, pad, stream)
+    return out
 
 
 def sparseconv_destroy(handle) -> None:

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparseconv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "escoin.hip", "pack.cpp", "bake.cpp", "api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "escoin.hip", "dense.hip", "pack.cpp", "bake.cpp", "api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 instructions are disabled for all device code: hipcc would otherwise form

@@ -992,6 +992,49 @@ sc_status sparseconv_device_status(const sc_handle* h, uint32_t* status, int32_t
   return SC_OK;
 }
 
+sc_status sparseconv_dense_forward(const float* w_dense_dev, const float* input, float* output, int32_t N,
+                                   int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                                   int32_t stride, int32_t pad, void* hip_stream) {
+  g_err.clear();
+  if (N < 0) return fail(SC_ESHAPE, "N < 0");
+  if (M < 1 || C < 1 || R < 1 || S < 1 || H < 1 || W < 1 || stride < 1 || pad < 0)
+    return fail(SC_ESHAPE, "M, C, R, S, H, W and stride must be >= 1 and pad >= 0");
+  const long long E = ((long long)H + 2LL * pad - R) / stride + 1, F = ((long long)W + 2LL * pad - S) / stride + 1;
+  if (H + 2LL * pad < R || W + 2LL * pad < S || E < 1 || F < 1) return fail(SC_ESHAPE, "E or F < 1");
+  const long long nw = (long long)M * C * R * S;
+  if (nw >= (1LL << 31)) return fail(SC_EUNSUPPORTED, "M*C*R*S >= 2^31");
+  if (N == 0) return SC_OK;
+  const long long nin = (long long)N * C * H * W, nout = (long long)N * M * E * F;
+  if (nin * 4 >= (1LL << 31) || nout * 4 >= (1LL << 31))
+    return fail(SC_EUNSUPPORTED, "N*C*H*W*4 or N*M*E*F*4 >= 2^31 bytes (32-bit buffer offsets)");
+  if (!w_dense_dev || !input || !output) return fail(SC_EINVAL, "weights, input or output is NULL");
+  if ((reinterpret_cast<uintptr_t>(w_dense_dev) | reinterpret_cast<uintptr_t>(input) |
+       reinterpret_cast<uintptr_t>(output)) & 3)
+    return fail(SC_EINVAL, "weights, input or output is not 4-byte aligned");
+  if (ranges_overlap(input, nin * 4, output, nout * 4)) return fail(SC_EINVAL, "input and output overlap");
+  if (ranges_overlap(w_dense_dev, nw * 4, output, nout * 4)) return fail(SC_EINVAL, "weights and output overlap");
+  sc::DenseArgs a{};
+  a.C = C, a.H = H, a.W = W, a.M = M, a.R = R, a.S = S, a.st = stride, a.pad = pad;
+  a.E = (int)E, a.F = (int)F;
+  a.EF = (int)(E * F);
+  a.MEF = (int)(M * E * F);
+  a.CHW = (int)((long long)C * H * W);
+  a.HW4 = (int)((long long)H * W * 4);
+  a.RS = R * S;
+  a.CRS = (int)((long long)C * R * S);
+  a.qtot = (int)(N * E * F);
+  a.x_bytes = (uint32_t)(nin * 4);
+  a.y_bytes = (uint32_t)(nout * 4);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    return fail(SC_EDEVICE, "no current HIP device");
+  const int e = sc::launch_dense(a, w_dense_dev, input, output, 4 * cus, hip_stream);
+  if (e != (int)hipSuccess)
+    return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
+  return SC_OK;
+}
+
 sc_status sparseconv_workspace_size(const sc_handle* h, int32_t N, int64_t* bytes) {
   g_err.clear();
   if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");

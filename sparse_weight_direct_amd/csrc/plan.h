@@ -177,4 +177,20 @@ struct EscoinArgs {
 int launch_escoin(const EscoinArgs& a, const float* x, float* xp, float* y, const uint32_t* ent,
                   const int32_t* rowptr, void* stream);
 
+// Dense direct baseline (dense.hip): every tap of a dense M x C x R x S filter tensor on the
+// device.  The caller fills the geometry; the launcher sets tgroups and groups.  Input and
+// output must each be < 2^31 bytes (32-bit buffer offsets).
+struct DenseArgs {
+  int C, H, W, M, R, S, st, pad, E, F;
+  int EF, MEF, CHW, HW4;   // E*F, M*E*F, C*H*W, H*W*4
+  int RS, CRS;             // R*S, C*R*S
+  int qtot;                // N*E*F output positions per channel (< 2^31)
+  uint32_t x_bytes, y_bytes;
+  int tgroups, groups;     // position-tile groups and output-channel groups
+};
+// Tile shape of a launch: K positions per lane, MG output channels per wavefront, picked for
+// the layer and the device's SIMD count.
+void dense_pick(const DenseArgs& a, int simds, int* K, int* MG);
+int launch_dense(DenseArgs a, const float* w, const float* x, float* y, int simds, void* stream);
+
 }  // namespace sc

@@ -36,8 +36,8 @@ def gpu_sparse(x, w, mask, stride, pad, handle=None, poison=True, stream=None, f
     return out.cpu().numpy(), handle
 
 
-def gpu_dense(x, w_masked, stride, pad):
-    """Dense direct baseline: the same kernel on a handle storing every filter tap."""
+def gpu_all_taps(x, w_masked, stride, pad):
+    """A handle storing every filter tap (SC_PACK_ALL_TAPS), zeros included."""
     N, C, H, W = x.shape
     h = sc.Handle.from_dense(np.ascontiguousarray(w_masked), H, W, stride, pad, flags=sc.SC_PACK_ALL_TAPS)
     y, _ = gpu_sparse(x, w_masked, None, stride, pad, handle=h)

@@ -12,4 +12,5 @@ int launch_sparse(const Plan&, const KArgs&, void*, int) { return 100; }
 int launch_escoin(const EscoinArgs&, const float*, float*, float*, const uint32_t*, const int32_t*, void*) {
   return 100;
 }
+int launch_dense(DenseArgs, const float*, const float*, float*, int, void*) { return 100; }
 }  // namespace sc

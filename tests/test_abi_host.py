@@ -307,3 +307,29 @@ def test_binding_checks_tensor_shapes_before_launch():
         h.forward(good_x, torch.zeros((2, L.M, L.E, L.F)))
     with pytest.raises(ValueError, match="float32"):
         h.forward(good_x.double(), torch.zeros((1, L.M, L.E, L.F)))
+
+
+def test_dense_forward_checks_before_any_device_work():
+    """sparseconv_dense_forward validates shapes, pointers, alignment, overlap and the 32-bit
+    limits on the host and returns before touching a device; N = 0 is a no-op."""
+    base = 1 << 40  # never dereferenced: every call below fails (or returns) before a launch
+    a = dict(N=2, C=3, H=10, W=12, M=4, R=3, S=3, stride=1, pad=1)
+
+    def call(w=base, x=base + (1 << 30), y=base + (2 << 30), **kw):
+        g = dict(a, **kw)
+        return _status(lambda: sc.sparseconv_dense_forward(w, x, y, g["N"], g["C"], g["H"], g["W"], g["M"],
+                                                           g["R"], g["S"], g["stride"], g["pad"], 0))
+
+    assert call(N=0) == (sc.SC_OK, "")
+    assert call(N=0, w=0, x=0, y=0) == (sc.SC_OK, "")
+    assert call(N=-1)[0] == sc.SC_ESHAPE
+    assert call(R=13)[0] == sc.SC_ESHAPE          # filter taller than the padded input
+    assert call(stride=0)[0] == sc.SC_ESHAPE
+    assert call(pad=-1)[0] == sc.SC_ESHAPE
+    assert call(M=0)[0] == sc.SC_ESHAPE
+    assert call(w=0)[0] == sc.SC_EINVAL
+    assert call(x=base + (1 << 30) + 2)[0] == sc.SC_EINVAL          # misaligned
+    assert call(y=base + (1 << 30) + 64)[0] == sc.SC_EINVAL         # output overlaps input
+    assert call(y=base)[0] == sc.SC_EINVAL                          # output overlaps the weights
+    assert call(N=1 << 20, C=64, H=64, W=64)[0] == sc.SC_EUNSUPPORTED  # input >= 2^31 bytes
+    assert call(M=1 << 16, C=1 << 12, R=3, S=3, N=1)[0] == sc.SC_EUNSUPPORTED  # M*C*R*S >= 2^31

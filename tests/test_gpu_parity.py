@@ -11,7 +11,7 @@ import torch
 import oracle
 import sparse_weight_direct_amd as sc
 import workloads
-from gpu_util import assert_layer_parity, assert_parity, gpu_dense, gpu_sparse
+from gpu_util import assert_layer_parity, assert_parity, gpu_all_taps, gpu_sparse
 
 pytestmark = pytest.mark.gpu
 
@@ -305,12 +305,12 @@ def test_forward_rejects_mismatched_dims_and_overlap():
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid", "first11"])
-def test_dense_baseline_parity(name):
+def test_all_taps_handle_parity(name):
     d = workloads.make(name, n_override=2)
     L = d["layer"]
     r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
-    y = gpu_dense(d["x"], d["w_masked"], L.stride, L.pad)
-    assert_parity(y, r["y64"], r["mag"], "dense " + name)
+    y = gpu_all_taps(d["x"], d["w_masked"], L.stride, L.pad)
+    assert_parity(y, r["y64"], r["mag"], "all taps " + name)
 
 
 @pytest.mark.parametrize("mapping", sorted(MAPPINGS))
