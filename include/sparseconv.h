@@ -83,7 +83,8 @@ typedef enum {
                                 LDS and reads the padded input through the caches, one output
                                 position per thread at a time.  Same result bar as the default
                                 mapping.  Such a handle runs only through
-                                sparseconv_forward_workspace.  Not combinable with
+                                sparseconv_forward_workspace (or sparseconv_forward_noalloc,
+                                within its static workspace).  Not combinable with
                                 SC_PACK_FP16_WORD (SC_EINVAL).  Limit: C*(H+2pad)*(W+2pad) <
                                 2^30 (SC_EUNSUPPORTED). */
 
@@ -255,6 +256,29 @@ sc_status sparseconv_forward_workspace(const sc_handle* h, const float* input, f
                                        int32_t N, int32_t C, int32_t H, int32_t W, int32_t M,
                                        int32_t R, int32_t S, int32_t stride, int32_t pad,
                                        void* workspace, int64_t workspace_bytes, void* hip_stream);
+
+/*
+ * Forward pass that allocates nothing, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The contract
+ * of sparseconv_forward_workspace, with the workspace taken from a static device array of the
+ * library instead of the caller (SC_NOALLOC_SCRATCH_BYTES, 256-byte aligned, one copy per GPU,
+ * held from the library's first use of that GPU until the process ends).  Handles packed with
+ * SC_PACK_ESCOIN_MAP keep the padded input there; a batch that needs more than
+ * SC_NOALLOC_SCRATCH_BYTES (sparseconv_workspace_size) is rejected with SC_EUNSUPPORTED before
+ * anything is launched (use sparseconv_forward_workspace for it).  Other handles need no
+ * workspace and behave exactly as with sparseconv_forward.  The array's address on a device is
+ * resolved once (hipGetSymbolAddress) when an SC_PACK_ESCOIN_MAP handle is packed there, or
+ * else at the first call on that device.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (each call rewrites all of the array it reads): two calls
+ * that overlap in time on one GPU (several streams, or host threads without ordering) race
+ * and may give wrong outputs; keep them on one stream.  Errors as sparseconv_forward_workspace,
+ * plus SC_EUNSUPPORTED for a batch beyond the array and SC_EDEVICE if its address cannot be
+ * resolved.
+ */
+#define SC_NOALLOC_SCRATCH_BYTES (32LL * 1024 * 1024)
+sc_status sparseconv_forward_noalloc(const sc_handle* h, const float* input, float* output, int32_t N,
+                                     int32_t C, int32_t H, int32_t W, int32_t M, int32_t R, int32_t S,
+                                     int32_t stride, int32_t pad, void* hip_stream);
 
 /* Fill *info with the handle's geometry, sizes and launch plan.  SC_EINVAL on NULL. */
 sc_status sparseconv_query(const sc_handle* h, sc_info* info);

@@ -47,7 +47,8 @@ _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
             "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
             "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_device_status",
-            "sparseconv_dense_forward", "sparseconv_destroy", "sparseconv_last_error")
+            "sparseconv_dense_forward", "sparseconv_forward_noalloc", "sparseconv_destroy",
+            "sparseconv_last_error")
 
 
 class sc_weights(ctypes.Structure):
@@ -105,6 +106,8 @@ _lib.sparseconv_device_status.restype = _i32
 _lib.sparseconv_device_status.argtypes = [_vp, ctypes.POINTER(_u32), _i32]
 _lib.sparseconv_dense_forward.restype = _i32
 _lib.sparseconv_dense_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
+_lib.sparseconv_forward_noalloc.restype = _i32
+_lib.sparseconv_forward_noalloc.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -189,6 +192,11 @@ def sparseconv_forward_workspace(handle: int, x, y, N, C, H, W, M, R, S, stride,
     _check(_lib.sparseconv_forward_workspace(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad, wp,
                                              int(workspace_bytes), _stream_ptr(stream)),
            "sparseconv_forward_workspace")
+
+
+def sparseconv_forward_noalloc(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
+    _check(_lib.sparseconv_forward_noalloc(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad,
+                                           _stream_ptr(stream)), "sparseconv_forward_noalloc")
 
 
 def sparseconv_workspace_size(handle: int, N: int) -> int:

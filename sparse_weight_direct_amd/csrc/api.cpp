@@ -543,6 +543,10 @@ sc_status sparseconv_pack(const sc_weights* w, int32_t M, int32_t C, int32_t R, 
           return fail(SC_EDEVICE, "upload of the packed filter bank failed");
         }
         base += al(esc_ent.size() * 4) + al(rowptr.size() * 4);
+        // set-up for sparseconv_forward_noalloc: resolve the static workspace's address on this
+        // device now, outside any stream capture (a failure is reported by that call)
+        void* sp = nullptr;
+        (void)sc::scratch_address(&sp);
       }
       for (Variant& v : h->var) {
         const size_t b_ent = al(v.ent.size() * 4), b_seg = al(v.bstart.size() * 4);
@@ -1033,6 +1037,32 @@ sc_status sparseconv_dense_forward(const float* w_dense_dev, const float* input,
   if (e != (int)hipSuccess)
     return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
   return SC_OK;
+}
+
+sc_status sparseconv_forward_noalloc(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C,
+                                     int32_t H, int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride,
+                                     int32_t pad, void* hip_stream) {
+  g_err.clear();
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (!h->escoin) return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, nullptr, 0, false, hip_stream);
+  const sc::Geom& g = h->g;
+  if (N < 0) return fail(SC_ESHAPE, "N < 0");
+  if (C != g.C || H != g.H || W != g.W || M != g.M || R != g.R || S != g.S || stride != g.st || pad != g.pad)
+    return fail(SC_ESHAPE, "forward dims differ from the packed handle");
+  const long long need = workspace_bytes(h, N);
+  if (need > sc::kScratchBytes)
+    return fail(SC_EUNSUPPORTED, "this batch needs a " + std::to_string(need) +
+                                     "-byte workspace, more than the library's static " +
+                                     std::to_string(sc::kScratchBytes) + " bytes (use sparseconv_forward_workspace)");
+  void* scratch = nullptr;
+  if (N > 0) {
+    const int e = sc::scratch_address(&scratch);
+    if (e != (int)hipSuccess)
+      return fail(SC_EDEVICE, std::string("resolving the static workspace failed: ") +
+                                  hipGetErrorString((hipError_t)e));
+  }
+  return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, scratch, sc::kScratchBytes, true,
+                      hip_stream);
 }
 
 sc_status sparseconv_workspace_size(const sc_handle* h, int32_t N, int64_t* bytes) {

@@ -19,12 +19,24 @@
 // choice on this chip.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "plan.h"
 #include "xcd.h"
 
 namespace sc {
 
 namespace {
+
+// Static workspace for callers that cannot allocate (sparseconv_forward_noalloc): device
+// memory of this code object, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): it uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
 
 // One thread per padded word; a workgroup covers a run of one padded plane.
 __global__ __launch_bounds__(256) void pad_in(const float* __restrict__ x, float* __restrict__ xp, int H, int W,
@@ -117,6 +129,24 @@ __global__ __launch_bounds__(256) void sconv(const EscoinArgs a, const float* __
 }
 
 }  // namespace
+
+int scratch_address(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return (int)hipSuccess;
+}
 
 int launch_escoin(const EscoinArgs& a, const float* x, float* xp, float* y, const uint32_t* ent,
                   const int32_t* rowptr, void* stream) {

@@ -177,6 +177,12 @@ struct EscoinArgs {
 int launch_escoin(const EscoinArgs& a, const float* x, float* xp, float* y, const uint32_t* ent,
                   const int32_t* rowptr, void* stream);
 
+// The static workspace of escoin.hip (kScratchBytes, 256-byte aligned): *ptr receives its
+// device address on the current device, resolved once per device (hipGetSymbolAddress) and
+// cached.  Returns a hipError_t.
+constexpr long long kScratchBytes = 32LL << 20;  // SC_NOALLOC_SCRATCH_BYTES
+int scratch_address(void** ptr);
+
 // Dense direct baseline (dense.hip): every tap of a dense M x C x R x S filter tensor on the
 // device.  The caller fills the geometry; the launcher sets tgroups and groups.  Input and
 // output must each be < 2^31 bytes (32-bit buffer offsets).
