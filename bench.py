@@ -4,7 +4,9 @@
 A step is one sparseconv_forward over one batch: the 112x112 layer, batch 8, C = M = 128,
 3x3, stride 1, pad 1, whose output channels have Beta(0.5, b) densities with mean
 sparsity 95% (the middle of the 90-99% range the method targets).  Packing happens once,
-before timing, as in deployment (weights stay resident); the forward launches one kernel.
+before timing, as in deployment (weights stay resident), and so does the choice of kernel for
+the batch size (sparseconv_tune times the handle's kernels and pins the fastest); the forward
+launches one kernel.
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
 with a device synchronisation on both sides.  Input/output buffer sets rotate so the working
@@ -12,8 +14,9 @@ set exceeds the 256 MB Infinity Cache and every step reads its input from HBM ("
 
 Printed: one JSON line with effective TFLOP/s (2*nnz*N*E*F per second) as ``value``, the
 roofline of the kernel (bound from the arithmetic intensity against the ridge of 8 TB/s and
-the fp32 vector FMA peak without packed math), the HBM fraction, the plan the forward
-launched, every other workload layer timed the same way (``per_config``), the dense direct
+the 157.3 TFLOP/s fp32 vector FMA peak, which plain v_fmac_f32 reaches: the FMA probe timed
+here measures it), the HBM fraction, the plan the forward launched, the roof probes (FMA rate
+by wavefronts per SIMD, LDS read bandwidth), every other workload layer timed the same way (``per_config``), the dense direct
 baseline and torch's conv2d (MIOpen) on the same GPU, and the CPU oracle on this host.
 """
 from __future__ import annotations
@@ -77,6 +80,9 @@ def main():
     ap.add_argument("--escoin", action="store_true",
                     help="time the second mapping (SC_PACK_ESCOIN_MAP: pad_in + one output channel per workgroup)")
     ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target CPU time of one timed oracle run")
+    ap.add_argument("--no-probes", action="store_true", help="skip the FMA and LDS roof probes")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="launch the kernels the cost estimate picks instead of tuning each layer first")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
     args = ap.parse_args()
@@ -128,6 +134,10 @@ def main():
         x0 = torch.from_numpy(d["x"]).to(dev)
         xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
         ys = [torch.empty((L.N, L.M, L.E, L.F), dtype=torch.float32, device=dev) for _ in range(nsets)]
+        if not args.no_tune and ws is None:
+            # deployment setup, once per layer and batch size: time the handle's kernels for
+            # this batch and pin the fastest (sparseconv_tune); the timed steps launch it
+            h.tune(xs[0], ys[0], reps=5, stream=stream)
         return d, L, h, ws, xs, ys, nsets, set_bytes
 
     def describe(L, info, ms):
@@ -135,11 +145,11 @@ def main():
         flops = roofline.effective_flops(nnz, L.N, L.E, L.F)
         alg = roofline.algorithmic_bytes(L.N, L.C, L.H, L.W, L.M, L.E, L.F, nnz, info["entry_bytes"])
         ai = flops / alg
-        ridge = roofline.FP32_VECTOR_NONPACKED_TFLOPS * 1e12 / (roofline.HBM_PEAK_GBS * 1e9)
+        ridge = roofline.FP32_VECTOR_PEAK_TFLOPS * 1e12 / (roofline.HBM_PEAK_GBS * 1e9)
         tflops = flops / (ms * 1e-3) / 1e12
         gbs = alg / (ms * 1e-3) / 1e9
         bound = "alu" if ai > ridge else "hbm"
-        frac = tflops / roofline.FP32_VECTOR_NONPACKED_TFLOPS if bound == "alu" else gbs / roofline.HBM_PEAK_GBS
+        frac = tflops / roofline.FP32_VECTOR_PEAK_TFLOPS if bound == "alu" else gbs / roofline.HBM_PEAK_GBS
         return dict(flops=flops, alg=alg, ai=ai, tflops=tflops, gbs=gbs, bound=bound, frac=frac)
 
     layer = args.layer or workloads.BENCH_LAYER
@@ -218,6 +228,22 @@ def main():
                                    "gbs_read_plus_write": round(2 * nb / (cms * 1e-3) / 1e9, 1)}
         log(f"[bench] copy of {args.copy_mb} MiB: {2 * nb / (cms * 1e-3) / 1e9:.0f} GB/s (read+write)")
         del src, dst
+
+    if not args.no_probes:
+        # roofs of the instruction mixes the kernels are made of (csrc/probes.hip): the fp32 FMA
+        # rate of plain v_fmac_f32 (literal weight, as in the weights-in-code kernels; VGPR
+        # weight) by wavefronts per SIMD, and the LDS read bandwidth
+        from sparse_weight_direct_amd import probes
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        fma = {f"literal_{w}_waves_per_simd": round(probes.fma_rate(cus, w, True), 2) for w in (1, 2, 4)}
+        fma["vgpr_4_waves_per_simd"] = round(probes.fma_rate(cus, 4, False), 2)
+        best = max(fma.values())
+        extra["roof_probes"] = {
+            "fma_tflops": fma, "fma_peak_tflops": roofline.FP32_VECTOR_PEAK_TFLOPS,
+            "fma_frac_of_peak": round(best / roofline.FP32_VECTOR_PEAK_TFLOPS, 3),
+            "lds_read_tbs": {"b32": round(probes.lds_read_rate(cus, 1), 2), "b128": round(probes.lds_read_rate(cus, 4), 2)},
+            "headline_kernel_lds_bytes": 0 if launch["mapping"] == sc.MAPPING_BAKED and launch["splits"] <= 1 else None}
+        log(f"[bench] roof probes: FMA {fma} TFLOP/s, LDS {extra['roof_probes']['lds_read_tbs']} TB/s")
 
     # every workload layer, timed the same way (cold, rotated sets), with the launched plan
     if not args.no_configs and not args.layer:
@@ -299,7 +325,7 @@ def main():
     mask_text += {"u11": ", inputs U[-1,1]", "relu_n01": ", inputs ReLU(N(0,1))"}.get(L.x_dist, "")
     mask_text += {"u11": ", weights U[-1,1]", "n0.05": ", weights N(0,0.05)", "n0.02": ", weights N(0,0.02)"}.get(
         L.w_dist, "")
-    peak = roofline.FP32_VECTOR_NONPACKED_TFLOPS if m["bound"] == "alu" else roofline.HBM_PEAK_GBS
+    peak = roofline.FP32_VECTOR_PEAK_TFLOPS if m["bound"] == "alu" else roofline.HBM_PEAK_GBS
     achieved = m["tflops"] if m["bound"] == "alu" else m["gbs"]
     out = {
         "metric": "sparse conv effective TFLOP/s (2*nnz*N*E*F/s) and % of HBM roofline",
@@ -328,7 +354,7 @@ def main():
         "hbm": {"achieved_gbs": round(m["gbs"], 1), "peak_gbs": roofline.HBM_PEAK_GBS,
                 "frac": round(m["gbs"] / roofline.HBM_PEAK_GBS, 4), "algorithmic_bytes": int(m["alg"])},
         "arithmetic_intensity": round(m["ai"], 2),
-        "ridge_flop_per_byte": round(roofline.FP32_VECTOR_NONPACKED_TFLOPS / roofline.HBM_PEAK_GBS * 1e3, 2),
+        "ridge_flop_per_byte": round(roofline.FP32_VECTOR_PEAK_TFLOPS / roofline.HBM_PEAK_GBS * 1e3, 2),
         "parity_on_timed_buffers": parity,
         "plan": launch,
         "rotated_sets": nsets,

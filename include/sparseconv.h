@@ -316,8 +316,26 @@ sc_status sparseconv_export_words(const sc_handle* h, int32_t* rowptr, uint32_t*
 sc_status sparseconv_device_status(const sc_handle* h, uint32_t* status, int32_t clear);
 
 /*
- * Describe the launch a forward of N >= 1 images would make on this handle (the plan the
- * forward's cost estimate picks for N), without launching anything.  SC_EINVAL on a NULL
+ * Choose, by measurement, the kernel later forwards of N >= 1 images launch on this handle (as a
+ * library's "find" step does): every kernel the handle holds for such a batch (the
+ * weights-in-code kernels of its plans, or its LDS-tile plans) runs reps + 1 times on the
+ * caller's input and output on hip_stream, the fastest average over the last reps wins and is
+ * recorded for N, and *chosen (may be NULL) receives its index (sc_launch.variant).  Arguments as
+ * sparseconv_forward, plus 1 <= reps <= 1000.  Blocking: synchronises hip_stream; not for use
+ * under stream capture.  The output holds the chosen kernel's result afterwards.  Handles
+ * packed with SC_PACK_ESCOIN_MAP hold a single kernel: the call only sets *chosen = 0.  A forward running at the same time on another
+ * thread launches the previous or the new choice; either computes the same convolution.
+ * Errors as sparseconv_forward, plus SC_EINVAL for reps out of range and SC_EDEVICE if timing
+ * fails.
+ */
+sc_status sparseconv_tune(sc_handle* h, const float* input, float* output, int32_t N, int32_t C, int32_t H,
+                          int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride, int32_t pad, int32_t reps,
+                          void* hip_stream, int32_t* chosen);
+
+/*
+ * Describe the launch a forward of N >= 1 images would make on this handle (the kernel
+ * sparseconv_tune chose for N, else the one the forward's cost estimate picks), without
+ * launching anything.  SC_EINVAL on a NULL
  * handle or out, SC_ESHAPE for N < 1.
  */
 sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out);

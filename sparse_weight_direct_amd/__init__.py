@@ -47,7 +47,7 @@ _STATUS_NAMES = {0: "SC_OK", 1: "SC_EINVAL", 2: "SC_ESHAPE", 3: "SC_ENOMEM", 4: 
 EXPORTED = ("sparseconv_pack", "sparseconv_forward", "sparseconv_forward_workspace", "sparseconv_workspace_size",
             "sparseconv_query", "sparseconv_export_packed", "sparseconv_export_words",
             "sparseconv_export_kernel_source", "sparseconv_launch_info", "sparseconv_device_status",
-            "sparseconv_dense_forward", "sparseconv_forward_noalloc", "sparseconv_destroy",
+            "sparseconv_dense_forward", "sparseconv_forward_noalloc", "sparseconv_tune", "sparseconv_destroy",
             "sparseconv_last_error")
 
 
@@ -108,6 +108,8 @@ _lib.sparseconv_dense_forward.restype = _i32
 _lib.sparseconv_dense_forward.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
 _lib.sparseconv_forward_noalloc.restype = _i32
 _lib.sparseconv_forward_noalloc.argtypes = [_vp, _vp, _vp] + [_i32] * 9 + [_vp]
+_lib.sparseconv_tune.restype = _i32
+_lib.sparseconv_tune.argtypes = [_vp, _vp, _vp] + [_i32] * 10 + [_vp, ctypes.POINTER(_i32)]
 _lib.sparseconv_destroy.restype = None
 _lib.sparseconv_destroy.argtypes = [_vp]
 _lib.sparseconv_last_error.restype = ctypes.c_char_p
@@ -197,6 +199,15 @@ def sparseconv_forward_workspace(handle: int, x, y, N, C, H, W, M, R, S, stride,
 def sparseconv_forward_noalloc(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, stream=None) -> None:
     _check(_lib.sparseconv_forward_noalloc(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad,
                                            _stream_ptr(stream)), "sparseconv_forward_noalloc")
+
+
+def sparseconv_tune(handle: int, x, y, N, C, H, W, M, R, S, stride, pad, reps=5, stream=None) -> int:
+    """Time the handle's kernels for N images on (x, y); later forwards of N use the fastest,
+    whose index is returned."""
+    chosen = _i32(-1)
+    _check(_lib.sparseconv_tune(handle, _dev_ptr(x), _dev_ptr(y), N, C, H, W, M, R, S, stride, pad, reps,
+                                _stream_ptr(stream), ctypes.byref(chosen)), "sparseconv_tune")
+    return chosen.value
 
 
 def sparseconv_workspace_size(handle: int, N: int) -> int:
@@ -344,6 +355,21 @@ class Handle:
                                          g["stride"], g["pad"], workspace,
                                          workspace.numel() * workspace.element_size(), stream)
         return out
+
+    def tune(self, x, out=None, reps: int = 5, stream=None) -> int:
+        """Choose by measurement the kernel forwards of x.shape[0] images launch (see
+        sparseconv_tune); returns its index.  out receives the convolution."""
+        import torch
+        g = self.geom
+        if x.dim() != 4 or tuple(x.shape[1:]) != (g["C"], g["H"], g["W"]):
+            raise ValueError(f"input shape {tuple(x.shape)} is not (N, {g['C']}, {g['H']}, {g['W']})")
+        N = x.shape[0]
+        if out is None:
+            out = torch.empty((N, g["M"], self.E, self.F), dtype=torch.float32, device=x.device)
+        elif tuple(out.shape) != (N, g["M"], self.E, self.F):
+            raise ValueError(f"output shape {tuple(out.shape)} is not ({N}, {g['M']}, {self.E}, {self.F})")
+        return sparseconv_tune(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"], g["stride"],
+                               g["pad"], reps, stream)
 
     def close(self):
         if getattr(self, "ptr", None):

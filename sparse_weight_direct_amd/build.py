@@ -7,6 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparseconv.so")
+PROBE_LIB = os.path.join(HERE, "libscprobe.so")  # roof probes timed by the benchmark
+PROBE_SOURCE = os.path.join(HERE, "csrc", "probes.hip")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "escoin.hip", "dense.hip", "pack.cpp", "bake.cpp", "api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -48,6 +50,11 @@ def build(verbose: bool = False) -> str:
     if verbose and (msgs or out.strip()):
         print("\n".join(msgs + [out]))
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    rc, out = _run([HIPCC] + FLAGS + ["-shared", PROBE_SOURCE, "-o", tmp])
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed on probes.hip ({rc}):\n{out}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

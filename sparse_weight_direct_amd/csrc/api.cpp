@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -114,6 +115,10 @@ struct sc_handle {
   std::string bake_why;           // why the layer was not baked ("" if it was)
   int cus;                        // compute units of the device (256 on the host)
   uint32_t* d_status;             // device status word (bit 0: a bounded wait gave up)
+  // kernels chosen by measurement (sparseconv_tune): {N, kind (0: weights-in-code kernel bk[i],
+  // 1: LDS-tile plan var[i]), i}; forwards of those batch sizes launch them
+  mutable std::mutex tune_mu;
+  std::vector<std::array<int, 3>> tuned;
 };
 
 namespace {
@@ -768,7 +773,17 @@ double estimate_cycles(const sc::Geom& g, const Variant& v, int N, long long nnz
   return 6000.0 + (double)per_cu * (step * p.nch + std::max(stage, walk));
 }
 
+// The kernel sparseconv_tune chose for N images (-1: none).
+int tuned_choice(const sc_handle* h, int N, int kind) {
+  std::lock_guard<std::mutex> lk(h->tune_mu);
+  for (const auto& t : h->tuned)
+    if (t[0] == N && t[1] == kind) return t[2];
+  return -1;
+}
+
 size_t pick_variant(const sc_handle* h, int N) {
+  const int t = tuned_choice(h, N, 1);
+  if (t >= 0 && (size_t)t < h->var.size()) return (size_t)t;
   size_t best = 0;
   double bc = 0;
   for (size_t i = 0; i < h->var.size(); i++) {
@@ -796,6 +811,8 @@ bool baked_fits(const sc_handle* h, int N) {
 // layers), else the handle's kernel with the lowest estimated cycles for N.
 int pick_baked(const sc_handle* h, int N) {
   if (!baked_fits(h, N)) return -1;
+  const int t = tuned_choice(h, N, 0);
+  if (t >= 0 && (size_t)t < h->bk.size()) return t;
   {
     const sc::BakePlan& b = h->bk[0].p;
     const long long qtot = (long long)N * h->g.E * b.Pb;
@@ -835,6 +852,9 @@ long long workspace_bytes(const sc_handle* h, int N) {
   if (!h->escoin || N <= 0) return 0;
   return ((long long)N * h->esc.img_words * 4 + 255) & ~255LL;
 }
+
+sc_status launch_bk(const sc_handle* h, int bi, const float* input, float* output, int N, void* hip_stream);
+sc_status launch_var(const sc_handle* h, size_t vi, const float* input, float* output, int N, void* hip_stream);
 
 sc_status forward_impl(const sc_handle* h, const float* input, float* output, int32_t N, int32_t C, int32_t H,
                        int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride, int32_t pad, void* workspace,
@@ -884,24 +904,35 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
       return fail(SC_EINVAL, "input or output is not 4-byte aligned");
     if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
       return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
-    const BakedKernel& k = h->bk[bi];
-    sc::BakeArgs a = baked_args(h, k.p, N);
-    a.x = reinterpret_cast<uint64_t>(input);
-    a.y = reinterpret_cast<uint64_t>(output);
-    size_t asz = sizeof(a);
-    void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &asz, HIP_LAUNCH_PARAM_END};
-    const hipError_t e = hipModuleLaunchKernel(k.fn, 8 * a.per_xcd, 1, 1, 64 * k.p.wpb(), 1, 1, 0,
-                                               reinterpret_cast<hipStream_t>(hip_stream), nullptr, cfg);
-    if (e != hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e));
-    return SC_OK;
+    return launch_bk(h, bi, input, output, N, hip_stream);
   }
   if (h->var.empty())
     return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel's 32-bit buffer ranges");
-  const Variant& v = h->var[pick_variant(h, N)];
-  sc_status s = check_io(g, v.p, input, output, N);
+  const size_t vi = pick_variant(h, N);
+  sc_status s = check_io(g, h->var[vi].p, input, output, N);
   if (s != SC_OK) return s;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+  return launch_var(h, vi, input, output, N, hip_stream);
+}
+
+// Launch weights-in-code kernel bi / LDS-tile plan vi (arguments already checked).
+sc_status launch_bk(const sc_handle* h, int bi, const float* input, float* output, int N, void* hip_stream) {
+  const BakedKernel& k = h->bk[bi];
+  sc::BakeArgs a = baked_args(h, k.p, N);
+  a.x = reinterpret_cast<uint64_t>(input);
+  a.y = reinterpret_cast<uint64_t>(output);
+  size_t asz = sizeof(a);
+  void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &asz, HIP_LAUNCH_PARAM_END};
+  const hipError_t e = hipModuleLaunchKernel(k.fn, 8 * a.per_xcd, 1, 1, 64 * k.p.wpb(), 1, 1, 0,
+                                             reinterpret_cast<hipStream_t>(hip_stream), nullptr, cfg);
+  if (e != hipSuccess) return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return SC_OK;
+}
+
+sc_status launch_var(const sc_handle* h, size_t vi, const float* input, float* output, int N, void* hip_stream) {
+  const sc::Geom& g = h->g;
+  const Variant& v = h->var[vi];
   sc::KArgs a = make_args(g, v.p, input, output, N);
   a.status = h->d_status;
   a.ent = v.d_ent;
@@ -925,6 +956,71 @@ sc_status sparseconv_forward(const sc_handle* h, const float* input, float* outp
                              int32_t pad, void* hip_stream) {
   g_err.clear();
   return forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, nullptr, 0, false, hip_stream);
+}
+
+sc_status sparseconv_tune(sc_handle* h, const float* input, float* output, int32_t N, int32_t C, int32_t H,
+                          int32_t W, int32_t M, int32_t R, int32_t S, int32_t stride, int32_t pad, int32_t reps,
+                          void* hip_stream, int32_t* chosen) {
+  g_err.clear();
+  if (chosen) *chosen = -1;
+  if (!valid_handle(h)) return fail(SC_EINVAL, "invalid or destroyed handle");
+  if (reps < 1 || reps > 1000) return fail(SC_EINVAL, "reps must be 1..1000");
+  if (N < 1) return fail(SC_ESHAPE, "N < 1");
+  if (h->escoin) {  // a single kernel: nothing to choose
+    if (chosen) *chosen = 0;
+    return SC_OK;
+  }
+  // one forward with the current choice checks every argument (and warms up)
+  sc_status st = forward_impl(h, input, output, N, C, H, W, M, R, S, stride, pad, nullptr, 0, false, hip_stream);
+  if (st != SC_OK) return st;
+  const bool bk = pick_baked(h, N) >= 0;
+  const int n = bk ? (int)h->bk.size() : (int)h->var.size();
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(SC_EDEVICE, "hipEventCreate failed");
+  }
+  int best = -1;
+  float best_ms = 0.0f;
+  for (int i = 0; i < n && st == SC_OK; i++) {
+    auto launch = [&]() { return bk ? launch_bk(h, i, input, output, N, hip_stream)
+                                    : launch_var(h, (size_t)i, input, output, N, hip_stream); };
+    st = launch();  // first launch of a kernel: not timed
+    if (st != SC_OK) break;
+    if (hipEventRecord(e0, s) != hipSuccess) st = fail(SC_EDEVICE, "hipEventRecord failed");
+    for (int r = 0; r < reps && st == SC_OK; r++) st = launch();
+    if (st != SC_OK) break;
+    float ms = 0.0f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      st = fail(SC_EDEVICE, "timing the kernels failed");
+      break;
+    }
+    if (best < 0 || ms < best_ms) {
+      best = i;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != SC_OK) return st;
+  {
+    std::lock_guard<std::mutex> lk(h->tune_mu);
+    const int kind = bk ? 0 : 1;
+    bool found = false;
+    for (auto& t : h->tuned)
+      if (t[0] == N && t[1] == kind) {
+        t[2] = best;
+        found = true;
+      }
+    if (!found) h->tuned.push_back({N, kind, best});
+  }
+  // leave the chosen kernel's result in the output
+  st = bk ? launch_bk(h, best, input, output, N, hip_stream) : launch_var(h, (size_t)best, input, output, N, hip_stream);
+  if (st != SC_OK) return st;
+  if (chosen) *chosen = best;
+  return SC_OK;
 }
 
 sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out) {

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -50,13 +51,15 @@ BakeForce bake_force_from_env() {
   f.T = env_key(e, "T", -1);
   f.D = env_key(e, "D", -1);
   f.dpp = env_key(e, "DPP", -1);
+  f.perm = env_key(e, "PERM", -1);
   return f;
 }
 
 namespace {
 
 constexpr int kMaxVgpr = 256;   // architectural VGPRs a VALU instruction can name
-constexpr int kFixedV = 5;      // v0 id, v1 lane, v2 zero, v3 out-of-range marker, v4 output offset
+constexpr int kFixedV = 6;      // v0 id, v1 lane, v2 zero, v3 out-of-range marker, v4 output offset,
+                                 // v5 lane * 4 (the lane-shift address)
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 2ll << 20;  // refuse kernels above 2 MB of code (~250K non-zeros)
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
@@ -65,10 +68,13 @@ constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
 // the other columns), or every column when lane shifts are off.
 inline int row_vectors(const Geom& g, int dpp) { return dpp ? std::min(g.st, g.S) : g.S; }
 
-// Registers of a plan with Mg accumulators and load depth D.
-inline int plan_vgprs(const Geom& g, int dpp, int maxsq, int Mg, int D) {
-  const int P = row_vectors(g, dpp);
-  const int acc0 = (kFixedV + g.R * P + (D + 1) * P + P * maxsq + 1) & ~1;  // even: 16-byte LDS writes
+// Registers of a plan with Mg accumulators and load depth D: the fixed registers, the row
+// offsets, the load ring, the shifted copies (two sets when the shifts of the next step are
+// in flight through the LDS crossbar while this step's FMAs run) and the accumulators.
+inline int shift_regs(const Geom& g, const BakePlan& p) { return row_vectors(g, p.dpp) * p.maxsq * (p.perm ? 2 : 1); }
+inline int plan_vgprs(const Geom& g, const BakePlan& p, int Mg, int D) {
+  const int P = row_vectors(g, p.dpp);
+  const int acc0 = (kFixedV + g.R * P + (D + 1) * P + shift_regs(g, p) + 1) & ~1;  // even: 16-byte LDS writes
   return (std::max(acc0 + Mg, acc0 + kTemps) + 3) & ~3;
 }
 
@@ -200,33 +206,33 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   int mg = 0;
   for (auto& r : p.rows) mg = std::max(mg, (int)r.size());
   p.Mg = p.Q > 1 ? (mg + 3) & ~3 : mg;
+  // lane shifts through the LDS crossbar are issued a step ahead, so a step waits for the next
+  // step's row vectors: they need a load depth of at least 2 (else DPP moves)
+  if (D_forced == 1) p.perm = 0;
   int D = D_forced;
-  if (D <= 0) {
+  for (int pass = 0; pass < 2 && D_forced <= 0; pass++) {
     // deepest ring that keeps the target occupancy (or, past it, fits at all)
     const int cap = std::max(1, 63 / P);
-    const int target = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, 1) <= kVgprTarget ? kVgprTarget : kMaxVgpr;
+    const int target = plan_vgprs(g, p, p.Mg, 1) <= kVgprTarget ? kVgprTarget : kMaxVgpr;
     D = 1;
-    while (D < cap && plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D + 1) <= target) D++;
+    while (D < cap && plan_vgprs(g, p, p.Mg, D + 1) <= target) D++;
+    if (!p.perm || D >= 2) break;
+    p.perm = 0;
   }
-  if (D * P > 63 || plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D) > kMaxVgpr) {
+  if (D * P > 63 || plan_vgprs(g, p, p.Mg, D) > kMaxVgpr) {
     *why = "output channels per group and load ring exceed the registers";
     return false;
   }
-  if (p.Q > 1 && g.R * P + (D + 1) * P + P * p.maxsq < 6) {
+  if (p.Q > 1 && g.R * P + (D + 1) * P + shift_regs(g, p) < 6) {
     // split 0 reads the partial sums into registers of the offset, ring and shift region
     *why = "channel splits need a load depth of at least 3";
     return false;
   }
   p.D = D;
-  p.vgprs = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, D);
+  p.vgprs = plan_vgprs(g, p, p.Mg, D);
   p.lds_bytes = p.Q > 1 ? p.T * (p.Q - 1) * (p.Mg / 4) * 1024 : 0;
   if (p.lds_bytes > 160 * 1024) {
     *why = "channel-split partial sums exceed the LDS";
-    return false;
-  }
-  if (p.Q > 1 && (p.Q - 1) * (p.Mg / 4) * 1024 > 65535 + 1024) {
-    // partial-sum offsets of one unit are 16-bit instruction offsets
-    *why = "channel-split partial sums exceed the 64 KB offset range";
     return false;
   }
   // section sizes
@@ -241,7 +247,7 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
     for (int q = 0; q < p.Q; q++) {
       long long v = 0, st = 0, ld = 0;
       for (int i = b[q]; i < b[q + 1]; i++) {
-        v += (long long)steps[i].nz.size() + steps[i].shifts();
+        v += (long long)steps[i].nz.size() + (p.perm ? 0 : steps[i].shifts());
         st++;
         ld += steps[i].loads();
         code += 8 * (long long)steps[i].nz.size() + 8 * steps[i].shifts() + 8 * steps[i].loads() + 8;
@@ -272,6 +278,10 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     *why = "filter reach too wide for lane shifts";
     return out;
   }
+  // lane shifts through the LDS crossbar unless a step's shifts exceed what one
+  // s_waitcnt lgkmcnt can leave outstanding (15), or there are none
+  p.perm = f.perm >= 0 ? f.perm : 1;
+  if (!p.dpp || p.maxsq == 0 || row_vectors(g, p.dpp) * p.maxsq > 15) p.perm = 0;
   p.V = 64 - p.maxsq;
   p.Pb = g.F + p.maxsq;
   const int M = g.M;
@@ -283,8 +293,22 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
   // base groups: the fewest whose accumulators fit the register target (measured on the
   // 112x112 layers, one group per wavefront beats more groups even with several hundred KB of
   // code: more groups repeat the row loads and lane shifts per group)
-  int G0 = 1;
-  while (G0 < M && plan_vgprs(g, p.dpp, p.maxsq, (M + G0 - 1) / G0, 2) > kVgprTarget) G0++;
+  auto fewest_groups = [&](const BakePlan& q) {
+    int n = 1;
+    while (n < M && plan_vgprs(g, q, (M + n - 1) / n, 2) > kVgprTarget) n++;
+    return n;
+  };
+  int G0 = fewest_groups(p);
+  if (p.perm) {
+    // the second set of shift registers must not cost a group: DPP shifts if they need fewer
+    BakePlan q = p;
+    q.perm = 0;
+    const int g_dpp = fewest_groups(q);
+    if (g_dpp < G0 && f.perm < 0) {
+      p.perm = 0;
+      G0 = g_dpp;
+    }
+  }
   struct Shape {
     int G, Q, T;
   };
@@ -300,8 +324,8 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
               {std::min(M, 2 * G0), 2, 1}};
   }
   for (const Shape& sh : shapes) {
-    if (sh.Q != 1 && sh.Q != 2 && sh.Q != 4 && sh.Q != 8) {
-      *why = "channel splits must be 1, 2, 4 or 8";
+    if (sh.Q < 1 || sh.Q > 16) {
+      *why = "channel splits must be 1 to 16";
       continue;
     }
     if (sh.Q * sh.T > 16) {
@@ -420,10 +444,10 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   // register map
   const int vOff = kFixedV;                 // RV per-row-vector input offsets
   const int vRing = vOff + RV;              // (D+1) * P loaded row vectors
-  const int vSh = vRing + (p.D + 1) * P;    // P * maxsq shifted copies
-  const int vAcc = (vSh + P * p.maxsq + 1) & ~1;  // Mg accumulators (even: 16-byte LDS writes)
+  const int vSh = vRing + (p.D + 1) * P;    // P * maxsq shifted copies (two sets with perm)
+  const int vAcc = (vSh + shift_regs(g, p) + 1) & ~1;  // Mg accumulators (even: 16-byte LDS writes)
   const int vTmp = vAcc;                    // prologue temporaries overlap the accumulators
-  const int nv = plan_vgprs(g, p.dpp, p.maxsq, p.Mg, p.D);
+  const int nv = plan_vgprs(g, p, p.Mg, p.D);
   if (nv > kMaxVgpr || vAcc + p.Mg > nv) {
     *err = "baked kernel needs more than 256 VGPRs";
     return false;
@@ -445,12 +469,23 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   E.v(1, 4, "v_and_b32_e32 v1, 63, v0");
   E.v(2, 4, "v_mov_b32_e32 v2, 0");
   E.v(3, 4, "v_bfrev_b32_e32 v3, 1");  // 0x80000000
+  E.v(5, 4, "v_lshlrev_b32_e32 v5, 2, v1");
   E.rfl_guard(vTmp);
   E.v(-1, 8, fmt("v_readfirstlane_b32 s14, v%d", vTmp));
   E.line("s_waitcnt lgkmcnt(0)");
   // split q = wave % Q (s3), unit within the workgroup = wave / Q
-  E.line("s_and_b32 s3, s14, %d", Q - 1);
-  E.line("s_lshr_b32 s14, s14, %d", lq);
+  if ((Q & (Q - 1)) == 0) {
+    E.line("s_and_b32 s3, s14, %d", Q - 1);
+    E.line("s_lshr_b32 s14, s14, %d", lq);
+  } else {
+    // wave / Q = (wave * ceil(2^16 / Q)) >> 16, exact for wave < 16 and Q <= 16
+    E.line("s_mul_i32 s3, s14, %d", (65536 + Q - 1) / Q);
+    E.line("s_lshr_b32 s3, s3, 16");
+    E.line("s_mul_i32 s17, s3, %d", Q);
+    E.line("s_sub_u32 s17, s14, s17");
+    E.line("s_mov_b32 s14, s3");
+    E.line("s_mov_b32 s3, s17");
+  }
   // logical workgroup: consecutive logical ids on one XCD (the grid is 8 * per_xcd)
   E.line("s_and_b32 s15, s2, 7");
   E.line("s_mul_i32 s15, s15, s29");
@@ -605,40 +640,97 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
         }
       };
       for (int t = 0; t < std::min(T_, p.D); t++) issue_loads(t);
-      for (int t = 0; t < T_; t++) {
+      // FMAs of step t at shift level lvl (0: the loaded row vector)
+      size_t nzi = 0;
+      auto emit_fmas = [&](int t, int lvl, const std::function<int(int, int)>& src_reg) {
         const Step& st = step_at(t);
-        int after = 0;
-        for (int u = t + 1; u < std::min(T_, t + p.D); u++) after += step_at(u).loads();
-        E.line("s_waitcnt vmcnt(%d)", after);
-        E.code += 4;
-        if (t + p.D < T_) issue_loads(t + p.D);
-        const int slot = t % (p.D + 1);
-        // lane shifts and FMAs, level by level: shift level k reads level k-1 (a VALU
-        // result, hence the wait states), FMAs of level k-1 fill the gap
-        auto src_reg = [&](int pv, int sq) { return sq == 0 ? vRing + slot * P + pv : vSh + pv * p.maxsq + (sq - 1); };
-        size_t i = 0;
-        int maxlvl = 0;
-        for (int pv = 0; pv < P; pv++) maxlvl = std::max(maxlvl, st.sqmax[pv]);
-        for (int lvl = 0; lvl <= maxlvl; lvl++) {
-          if (lvl > 0) {
-            for (int pv = 0; pv < P; pv++) {
-              if (st.sqmax[pv] < lvl) continue;
-              const int s_reg = src_reg(pv, lvl - 1), d_reg = src_reg(pv, lvl);
-              E.dpp_guard(s_reg);
-              E.v(d_reg, 8, fmt("v_mov_b32_dpp v%d, v%d wave_shl:1 row_mask:0xf bank_mask:0xf", d_reg, s_reg));
-            }
+        for (; nzi < st.nz.size() && L[st.nz[nzi]].sq == lvl; nzi++) {
+          const Nz& z = L[st.nz[nzi]];
+          const int a = vAcc + slot_of[z.m];
+          const int sr = src_reg(z.pv, z.sq);
+          if (!touched[slot_of[z.m]]) {
+            touched[slot_of[z.m]] = 1;
+            E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
+          } else {
+            E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
           }
-          for (; i < st.nz.size() && L[st.nz[i]].sq == lvl; i++) {
-            const Nz& z = L[st.nz[i]];
-            const int a = vAcc + slot_of[z.m];
-            const int sr = src_reg(z.pv, z.sq);
-            if (!touched[slot_of[z.m]]) {
-              touched[slot_of[z.m]] = 1;
-              E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
-            } else {
-              E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
+          fmas++;
+        }
+      };
+      auto loads_between = [&](int u0, int u1) {
+        int n = 0;
+        for (int u = u0; u < std::min(T_, u1); u++) n += step_at(u).loads();
+        return n;
+      };
+      if (p.perm) {
+        // Lane shifts through the LDS crossbar: the copy of row vector pv shifted down by sq
+        // lanes is ds_bpermute_b32 with lane address 4*lane + 4*sq (v5 + offset; lanes past
+        // 63 wrap and are junk).  The shifts of step t + 1 are issued before the FMAs of step
+        // t, into the other set of shift registers, so their latency hides behind step t.
+        auto sh_reg = [&](int t, int pv, int sq) { return vSh + ((t & 1) * P + pv) * p.maxsq + (sq - 1); };
+        auto issue_shifts = [&](int t) {
+          const Step& st = step_at(t);
+          const int slot = t % (p.D + 1);
+          int n = 0;
+          for (int pv = 0; pv < P; pv++)
+            for (int sq = 1; sq <= st.sqmax[pv]; sq++) {
+              E.line("ds_bpermute_b32 v%d, v5, v%d offset:%d", sh_reg(t, pv, sq), vRing + slot * P + pv, 4 * sq);
+              E.code += 8;
+              n++;
             }
-            fmas++;
+          return n;
+        };
+        if (T_ > 0) {
+          E.line("s_waitcnt vmcnt(%d)", loads_between(1, p.D));
+          E.code += 4;
+          issue_shifts(0);
+        }
+        for (int t = 0; t < T_; t++) {
+          const Step& st = step_at(t);
+          const int slot = t % (p.D + 1);
+          int next = 0;
+          if (t + 1 < T_) {
+            E.line("s_waitcnt vmcnt(%d)", loads_between(t + 2, t + p.D));
+            E.code += 4;
+          }
+          if (t + p.D < T_) issue_loads(t + p.D);
+          if (t + 1 < T_) next = issue_shifts(t + 1);
+          auto src_reg = [&](int pv, int sq) { return sq == 0 ? vRing + slot * P + pv : sh_reg(t, pv, sq); };
+          nzi = 0;
+          emit_fmas(t, 0, src_reg);
+          int maxlvl = 0;
+          for (int pv = 0; pv < P; pv++) maxlvl = std::max(maxlvl, st.sqmax[pv]);
+          if (maxlvl > 0) {
+            E.line("s_waitcnt lgkmcnt(%d)", next);  // this step's shifts have arrived
+            E.code += 4;
+          }
+          for (int lvl = 1; lvl <= maxlvl; lvl++) emit_fmas(t, lvl, src_reg);
+        }
+      } else {
+        for (int t = 0; t < T_; t++) {
+          const Step& st = step_at(t);
+          E.line("s_waitcnt vmcnt(%d)", loads_between(t + 1, t + p.D));
+          E.code += 4;
+          if (t + p.D < T_) issue_loads(t + p.D);
+          const int slot = t % (p.D + 1);
+          // DPP lane shifts and FMAs, level by level: shift level k reads level k-1 (a VALU
+          // result, hence the wait states), FMAs of level k-1 fill the gap
+          auto src_reg = [&](int pv, int sq) {
+            return sq == 0 ? vRing + slot * P + pv : vSh + pv * p.maxsq + (sq - 1);
+          };
+          nzi = 0;
+          int maxlvl = 0;
+          for (int pv = 0; pv < P; pv++) maxlvl = std::max(maxlvl, st.sqmax[pv]);
+          for (int lvl = 0; lvl <= maxlvl; lvl++) {
+            if (lvl > 0) {
+              for (int pv = 0; pv < P; pv++) {
+                if (st.sqmax[pv] < lvl) continue;
+                const int s_reg = src_reg(pv, lvl - 1), d_reg = src_reg(pv, lvl);
+                E.dpp_guard(s_reg);
+                E.v(d_reg, 8, fmt("v_mov_b32_dpp v%d, v%d wave_shl:1 row_mask:0xf bank_mask:0xf", d_reg, s_reg));
+              }
+            }
+            emit_fmas(t, lvl, src_reg);
           }
         }
       }
@@ -673,10 +765,15 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
         const int t0r = (vOff + 2) & ~1;                  // even-aligned temporaries
         const int nb = std::max(1, std::min(8, (vAcc - t0r) / 4));
         const int nq = (Q - 1) * (p.Mg / 4);
+        // (a batch's reads are addressed from their own base register, vOff + 1, so the
+        // 16-bit instruction offsets stay below 8 KB however large the unit's partials are)
+        const int vb = vOff + 1;
         for (int b0 = 0; b0 < nq; b0 += nb) {
           const int b1 = std::min(nq, b0 + nb);
+          E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", vb, b0 * 1024, va));
           for (int b = b0; b < b1; b++)
-            E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (b - b0), t0r + 4 * (b - b0) + 3, va, b * 1024);
+            E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (b - b0), t0r + 4 * (b - b0) + 3, vb,
+                   (b - b0) * 1024);
           E.line("s_waitcnt lgkmcnt(0)");
           for (int b = b0; b < b1; b++) {
             const int k4 = b % (p.Mg / 4);

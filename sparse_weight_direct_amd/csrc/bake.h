@@ -42,6 +42,8 @@ struct BakePlan {
   int T = 4;        // units per workgroup (a workgroup is Q*T wavefronts)
   int D = 4;        // steps whose loads are in flight ahead of the FMAs
   int dpp = 1;      // 1: shifted taps by lane shifts; 0: one load per tap (V = 64)
+  int perm = 1;     // lane shifts by ds_bpermute_b32 through the LDS crossbar (1) or by DPP
+                    // moves on the VALU (0)
   int Pb = 0;       // extended row pitch F + maxsq
   int V = 64;       // valid positions per wavefront = 64 - maxsq
   int maxsq = 0;    // largest lane shift (S-1)/st (0 without DPP)
@@ -68,11 +70,11 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=.." (tuning and tests only); fields
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=.." (tuning and tests only); fields
 // left at -1 are chosen by the packer.
 struct BakeForce {
-  int G = -1, Q = -1, T = -1, D = -1, dpp = -1;
-  bool any() const { return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0; }
+  int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1;
+  bool any() const { return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0; }
 };
 BakeForce bake_force_from_env();
 

@@ -12,10 +12,12 @@ bank ({u32 offset, fp32 value} per non-zero plus M+1 row pointers) read once.
 """
 from __future__ import annotations
 
-# MI355X published peaks.
+# MI355X published peaks.  The fp32 vector peak is 256 CUs x 4 SIMDs x 32 FMA lanes x 2 FLOP x
+# 2.4 GHz: a wave64 v_fmac_f32 every 2 cycles per SIMD.  Plain (not packed) v_fmac_f32 reaches
+# it: the FMA probe (csrc/probes.hip) measures about 2.4-2.8 cycles per wave64 FMA and SIMD
+# with two or more wavefronts per SIMD, so it is the roof of the fp32 FMA kernels here.
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3      # counts packed FP32 FMA
-FP32_VECTOR_NONPACKED_TFLOPS = 78.6  # 256 CUs x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def ai_table1(sparsity: float, N=32, IC=32, OC=64, H=256, W=256, K=3, P=4.0, P_idx=0.0,
@@ -47,8 +49,7 @@ DEVICES = {
     "Jetson AGX Orin 64GB": (5.32, 0.2048),
     "Jetson Orin Nano 8GB": (5.0, 0.068),
     "Jetson Nano (Tegra X1)": (0.236, 0.0256),
-    "MI355X (fp32, packed FMA)": (FP32_VECTOR_PEAK_TFLOPS, HBM_PEAK_GBS / 1000.0),
-    "MI355X (fp32, no packed FMA)": (FP32_VECTOR_NONPACKED_TFLOPS, HBM_PEAK_GBS / 1000.0),
+    "MI355X (fp32)": (FP32_VECTOR_PEAK_TFLOPS, HBM_PEAK_GBS / 1000.0),
 }
 
 
@@ -89,7 +90,7 @@ def report(bench_json_paths=()) -> str:
     out.append(_fmt_table([(n, p, bw, round(ridge(p, bw), 2)) for n, (p, bw) in DEVICES.items()],
                           ("device", "TFLOP/s", "TB/s", "ridge")))
     sp = [0.90, 0.91, 0.92, 0.93, 0.94, 0.95, 0.96, 0.97, 0.98]
-    devs = ["A100", "Jetson Nano (Tegra X1)", "MI355X (fp32, no packed FMA)"]
+    devs = ["A100", "Jetson Nano (Tegra X1)", "MI355X (fp32)"]
     rows = []
     for s in sp:
         ai = ai_table1(s)
@@ -98,7 +99,7 @@ def report(bench_json_paths=()) -> str:
     out.append(_fmt_table(rows, ("sparsity", "AI") + tuple(devs)))
     for name, dev, N, H, ocs, ics in [("Table 2", "A100 (Table 2)", 32, 256, (32, 64, 128, 256, 512), (1, 16, 32, 64, 128)),
                                       ("Table 3", "Jetson Nano (Tegra X1)", 8, 128, (16, 24, 32, 40, 48), (1, 8, 16, 24, 32)),
-                                      ("Table 2 shape on MI355X", "MI355X (fp32, no packed FMA)", 32, 256,
+                                      ("Table 2 shape on MI355X", "MI355X (fp32)", 32, 256,
                                        (32, 64, 128, 256, 512), (1, 16, 32, 64, 128))]:
         p, bw = DEVICES[dev]
         rows = [(oc,) + tuple(f"{winograd_speedup(oc, ic, p, bw, N=N, H=H):.1f}x" for ic in ics) for oc in ocs]
@@ -114,7 +115,7 @@ def report(bench_json_paths=()) -> str:
             if "arithmetic_intensity" not in d:
                 continue
             ai = d["arithmetic_intensity"]
-            roof = attainable_tflops(ai, *DEVICES["MI355X (fp32, no packed FMA)"])
+            roof = attainable_tflops(ai, *DEVICES["MI355X (fp32)"])
             pts.append((d["config"]["workload"].split(":")[0], ai, d["value"], round(roof, 1),
                         f"{100 * d['value'] / roof:.1f}%"))
     if pts:

@@ -10,7 +10,8 @@ else, and it checks the rules the hardware does not check for the code:
     of a load into it, v_readfirstlane of a VGPR one after a VALU write of it, and a VALU
     read of VCC two after a VALU write of VCC;
   * a VGPR that an outstanding buffer load will write may not be read or written before an
-    s_waitcnt vmcnt has retired that load (loads retire in order);
+    s_waitcnt vmcnt has retired that load (loads retire in order), and likewise a VGPR an
+    outstanding LDS instruction (ds_read, ds_bpermute) will write before s_waitcnt lgkmcnt;
   * only VGPRs below the kernel's declared count are used;
   * every output element is stored at most once per launch.
 
@@ -70,7 +71,7 @@ class Wave:
     def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs, lds=None):
         self.k = kern
         self.lds = lds  # the workgroup's LDS (uint32 words), shared by its waves
-        self.lgkm = []  # VGPRs of outstanding LDS reads
+        self.lgkm = []  # per outstanding LDS instruction (oldest first): the VGPRs it writes
         self.s = np.zeros(110, np.uint64)  # scalar registers (kept as u32 values)
         self.v = np.zeros((256, 64), np.uint32)
         self.vcc = np.zeros(64, bool)
@@ -102,7 +103,7 @@ class Wave:
         i = int(m.group(2))
         if i >= self.k.nvgpr:
             raise EmuError(f"v{i} beyond the declared {self.k.nvgpr} VGPRs")
-        if i in self.pending or i in self.lgkm:
+        if i in self.pending or any(i in regs for regs in self.lgkm):
             raise EmuError(f"v{i} {'written' if write else 'read'} while a load into it is outstanding")
         return i
 
@@ -214,9 +215,25 @@ class Wave:
                     else:
                         self.v[regs[j]] = self.lds[w + j]
                 if op == "ds_read_b128":
-                    self.lgkm.extend(regs)
-                    if len(self.lgkm) > 4 * 15:
-                        raise EmuError("too many LDS reads outstanding")
+                    self.lgkm.append(regs)
+                    if len(self.lgkm) > 15:
+                        raise EmuError("too many LDS instructions outstanding")
+            elif op == "ds_bpermute_b32":
+                # lane l receives data[((addr[l] + offset) >> 2) & 63] through the LDS crossbar
+                srcp, _, mods = a[2].partition(" ")
+                off = 0
+                if mods:
+                    key, _, num = mods.partition(":")
+                    if key != "offset":
+                        raise EmuError(f"ds_bpermute modifier not emulated: {mods}")
+                    off = int(num)
+                addr = self.src_vec(a[1]).astype(np.int64)
+                data = self.v[self.vreg(srcp)].copy()
+                dst = self.vreg(a[0], write=True)
+                self.v[dst] = data[((addr + off) >> 2) & 63]
+                self.lgkm.append([dst])
+                if len(self.lgkm) > 15:
+                    raise EmuError("too many LDS instructions outstanding")
             elif op == "v_add_f32_e32":
                 x = self.src_vec(a[1]).view(np.float32)
                 y = self.src_vec(a[2]).view(np.float32)

@@ -333,3 +333,19 @@ def test_dense_forward_checks_before_any_device_work():
     assert call(y=base)[0] == sc.SC_EINVAL                          # output overlaps the weights
     assert call(N=1 << 20, C=64, H=64, W=64)[0] == sc.SC_EUNSUPPORTED  # input >= 2^31 bytes
     assert call(M=1 << 16, C=1 << 12, R=3, S=3, N=1)[0] == sc.SC_EUNSUPPORTED  # M*C*R*S >= 2^31
+
+
+def test_tune_checks_arguments_before_any_device_work():
+    """sparseconv_tune rejects a host-only handle, a bad repetition count and N < 1 without
+    launching anything."""
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = _pack_host(d, L)
+    fake = 1 << 40
+    args = (L.C, L.H, L.W, L.M, L.R, L.S, L.stride, L.pad)
+    st, msg = _status(lambda: sc.sparseconv_tune(h.ptr, fake, fake + (1 << 30), 1, *args, reps=5, stream=0))
+    assert st == sc.SC_EINVAL and "HOST_ONLY" in msg
+    st, _ = _status(lambda: sc.sparseconv_tune(h.ptr, fake, fake + (1 << 30), 1, *args, reps=0, stream=0))
+    assert st == sc.SC_EINVAL
+    st, _ = _status(lambda: sc.sparseconv_tune(h.ptr, fake, fake + (1 << 30), 0, *args, reps=3, stream=0))
+    assert st == sc.SC_ESHAPE

@@ -66,7 +66,9 @@ def test_random_shapes(c):
 
 
 @pytest.mark.parametrize("env", ["G=3", "DPP=0", "G=2,DPP=0,D=3", "T=1", "D=1", "G=5,T=2,D=2", "Q=2,T=1",
-                                 "Q=4,T=1", "Q=8,T=2", "G=3,Q=2,T=3,D=3", "Q=2,DPP=0,D=4"])
+                                 "Q=4,T=1", "Q=8,T=2", "G=3,Q=2,T=3,D=3", "Q=2,DPP=0,D=4", "PERM=0",
+                                 "PERM=0,G=2,D=3", "PERM=1,D=2", "PERM=0,Q=2,T=1", "Q=3,T=1", "Q=5,T=2",
+                                 "Q=6,T=1,D=3", "G=2,Q=3,T=2"])
 def test_plan_options(env, monkeypatch):
     """Groups, lane shifts off, load depth and units per workgroup change the code but not
     the per-channel summation order: the outputs must equal the default plan's bit for bit,
@@ -121,5 +123,36 @@ def test_generated_code_shape():
     vals = set(int(v) for v in d["w"][d["mask"].astype(bool)].view(np.uint32))
     assert lits <= vals
     ops = set(ln.split()[0] for ln in code.splitlines() if ln.startswith("\t") and not ln.startswith("\t."))
-    assert {o for o in ops if o.startswith(("global_", "flat_", "scratch_", "ds_"))} == set()
+    assert {o for o in ops if o.startswith(("global_", "flat_", "scratch_"))} == set()
     assert {o for o in ops if o.startswith("buffer_")} == {"buffer_load_dword", "buffer_store_dword"}
+    # lane shifts go through the LDS crossbar (ds_bpermute), which uses no LDS memory
+    assert {o for o in ops if o.startswith("ds_")} == {"ds_bpermute_b32"}
+    assert h.info()["bake_lds_bytes"] == 0 and ".amdhsa_group_segment_fixed_size 0" in src
+
+
+SHIFT_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed: shifts of 1..5 lanes, 1..4 phases
+    (2, 5, 13, 11, 9, 3, 3, 1, 1, 0.3, 21),
+    (2, 3, 27, 23, 7, 5, 5, 2, 2, 0.4, 22),
+    (1, 2, 6, 70, 9, 3, 7, 1, 3, 0.5, 23),
+    (2, 3, 40, 37, 5, 11, 11, 4, 0, 0.2, 24),
+    (2, 4, 19, 30, 6, 2, 6, 1, 2, 0.6, 25),
+    (3, 4, 17, 23, 8, 3, 9, 3, 1, 0.5, 26),
+]
+
+
+@pytest.mark.parametrize("c", SHIFT_CASES, ids=lambda c: "R{}S{}st{}".format(*c[5:8]))
+def test_crossbar_shifts_equal_dpp_shifts(c, monkeypatch):
+    """Lane shifts through the LDS crossbar (ds_bpermute) and by DPP moves feed the same FMAs
+    in the same order: the two kernels' outputs agree bit for bit, and with the oracle."""
+    d = workloads.make_custom(*c)
+    y1, info1 = _check(d, c[7], c[8], "crossbar", "PERM=1", monkeypatch)
+    y0, info0 = _check(d, c[7], c[8], "dpp", "PERM=0", monkeypatch)
+    assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
+
+
+def test_channel_split_partials_beyond_64kb_of_offsets(monkeypatch):
+    """128 accumulators and 4 channel splits: split 0 reads 96 KB of partial sums, more than a
+    16-bit instruction offset reaches (each batch of reads is addressed from its own base)."""
+    d = workloads.make_custom(1, 12, 5, 7, 256, 3, 3, 1, 1, 0.3, 31)
+    y, info = _check(d, 1, 1, "G=2,Q=4", "G=2,Q=4,T=1", monkeypatch)
+    assert info["bake_splits"] == 4 and info["bake_lds_bytes"] >= 96 * 1024

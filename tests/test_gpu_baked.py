@@ -143,3 +143,34 @@ def test_graph_replay_equals_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), eager.view(np.uint32))
         torch.ones(1000, device="cuda").sum()  # other work between replays
+
+
+@pytest.mark.parametrize("name,flags", [("late", 0), ("mid", 0), ("mid", sc.SC_PACK_LDS_TILE)])
+def test_tune_pins_the_fastest_kernel(name, flags):
+    """sparseconv_tune times the handle's kernels for the batch, pins the fastest for that N
+    (launch_info reports it), leaves its result in the output, and later forwards use it; every
+    result matches the oracle."""
+    d = workloads.make(name)
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"], flags=flags)
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    x = torch.from_numpy(d["x"]).cuda()
+    y = torch.full((L.N, L.M, L.E, L.F), float("nan"), device="cuda")
+    chosen = h.tune(x, y, reps=3)
+    torch.cuda.synchronize()
+    assert chosen >= 0 and h.launch_info(L.N)["variant"] == chosen
+    assert_parity(y.cpu().numpy(), r["y64"], r["mag"], f"{name} tuned output")
+    y2, _ = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad, handle=h)
+    assert_parity(y2, r["y64"], r["mag"], f"{name} forward after tuning")
+    if L.N > 1:  # another batch size keeps the estimate's choice
+        assert h.launch_info(1)["variant"] == sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"],
+                                                        mask=d["mask"], flags=flags).launch_info(1)["variant"]
+
+
+def test_tune_on_an_escoin_handle_chooses_its_only_kernel():
+    d = workloads.make("tiny")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_ESCOIN_MAP)
+    x = torch.from_numpy(d["x"]).cuda()
+    assert h.tune(x) == 0
