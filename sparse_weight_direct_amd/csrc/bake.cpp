@@ -63,6 +63,7 @@ constexpr int kFixedV = 6;      // v0 id, v1 lane, v2 zero, v3 out-of-range mark
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 2ll << 20;  // refuse kernels above 2 MB of code (~250K non-zeros)
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
+constexpr int kReduceChannels = 32;  // channels per round of the channel-split reduction
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
 // the other columns), or every column when lane shifts are off.
@@ -182,13 +183,14 @@ std::vector<std::vector<Nz>> group_nonzeros(const Geom& g, int dpp, const std::v
 // two: the steps of a group are split over the Q channel-split wavefronts by this cost.
 inline long long step_cost(const Step& st) { return (long long)st.nz.size() + st.shifts() + 2 * st.loads(); }
 
-// Split [0, steps) into Q contiguous parts of about equal cost; returns Q + 1 bounds.
-std::vector<int> split_steps(const std::vector<Step>& steps, int Q) {
-  long long total = 0;
+// Split [0, steps) into Q contiguous parts of about equal cost, counting extra0 more for part 0
+// (split 0 also adds the other parts' partial sums); returns Q + 1 bounds.
+std::vector<int> split_steps(const std::vector<Step>& steps, int Q, long long extra0 = 0) {
+  long long total = extra0;
   for (const Step& st : steps) total += step_cost(st);
   std::vector<int> b(Q + 1, (int)steps.size());
   b[0] = 0;
-  long long acc = 0;
+  long long acc = extra0;
   int q = 1;
   for (int i = 0; i < (int)steps.size() && q < Q; i++) {
     acc += step_cost(steps[i]);
@@ -196,6 +198,9 @@ std::vector<int> split_steps(const std::vector<Step>& steps, int Q) {
   }
   return b;
 }
+
+// VALU cost of split 0's additions of the other splits' partial sums.
+inline long long reduce_cost(const BakePlan& p) { return p.Q > 1 ? (long long)(p.Q - 1) * p.Mg : 0; }
 
 // Fill the plan's derived fields (registers, LDS, section sizes) for given G, Q, T, D.
 bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col, BakePlan* pp,
@@ -230,7 +235,8 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   }
   p.D = D;
   p.vgprs = plan_vgprs(g, p, p.Mg, D);
-  p.lds_bytes = p.Q > 1 ? p.T * (p.Q - 1) * (p.Mg / 4) * 1024 : 0;
+  p.rc = std::min(p.Mg, kReduceChannels);
+  p.lds_bytes = p.Q > 1 ? p.T * (p.Q - 1) * (p.rc / 4) * 1024 : 0;
   if (p.lds_bytes > 160 * 1024) {
     *why = "channel-split partial sums exceed the LDS";
     return false;
@@ -243,7 +249,7 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   long long code = 2048;
   for (auto& L : nzs) {
     auto steps = group_steps(g, p.dpp, L);
-    auto b = split_steps(steps, p.Q);
+    auto b = split_steps(steps, p.Q, reduce_cost(p));
     for (int q = 0; q < p.Q; q++) {
       long long v = 0, st = 0, ld = 0;
       for (int i = b[q]; i < b[q + 1]; i++) {
@@ -319,9 +325,10 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     shapes.push_back({G, Q, f.T > 0 ? f.T : std::max(1, 4 / Q)});
   } else {
     // the base plan, then variants that give small batches more wavefronts: channel splits
-    // (no repeated loads, a reduction in LDS) and more groups (repeated loads, no reduction)
-    shapes = {{G0, 1, 4}, {G0, 2, 1}, {std::min(M, 2 * G0), 1, 4}, {std::min(M, 4 * G0), 1, 4},
-              {std::min(M, 2 * G0), 2, 1}};
+    // (no repeated loads, a reduction in LDS) and more groups (repeated loads, no reduction);
+    // the forward's estimate or sparseconv_tune chooses among them per batch size
+    shapes = {{G0, 1, 4}, {G0, 2, 1}, {G0, 3, 1}, {G0, 4, 1}, {std::min(M, 2 * G0), 1, 4},
+              {std::min(M, 4 * G0), 1, 4}, {std::min(M, 2 * G0), 2, 1}};
   }
   for (const Shape& sh : shapes) {
     if (sh.Q < 1 || sh.Q > 16) {
@@ -613,7 +620,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   for (int gq = 0; gq < p.G; gq++) {
     const std::vector<Nz>& L = nzs[gq];
     const std::vector<Step> all = group_steps(g, p.dpp, L);
-    const std::vector<int> bnd = split_steps(all, Q);
+    const std::vector<int> bnd = split_steps(all, Q, reduce_cost(p));
     const int nrow = (int)p.rows[gq].size();
     for (int sq_ = 0; sq_ < Q; sq_++) {
       const int sec = gq * Q + sq_;
@@ -739,48 +746,59 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
       for (int k = 0; k < nacc; k++)
         if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
       if (Q > 1) {
-        // the lane's byte address of its 16-byte column in the unit's partial sums (split q
-        // writes part q - 1; split 0 reads them all), in the first row-vector offset register,
-        // dead once the last load is issued; the rest of the offset, ring and shift registers
-        // hold the partials split 0 reads
-        const int kb = (p.Mg / 4) * 1024;
+        // Partial sums go through LDS in rounds of KC channels (one buffer of KC channels per
+        // later split, reused each round): splits q >= 1 write their KC accumulators (16 bytes per
+        // lane and 4 channels), barrier; split 0 adds them in split order, barrier.  The lane's
+        // byte address of its 16-byte column (split q writes part q - 1) lives in the first
+        // row-vector offset register, dead once the last load is issued; the rest of the
+        // offset, ring and shift registers hold the partials split 0 reads.
+        const int KC = p.rc;
+        const int kbr = (KC / 4) * 1024;  // bytes of one split's part per round
+        const int rounds = (p.Mg + KC - 1) / KC;
         const int va = vOff;
-        E.line("s_mul_i32 s17, s14, %d", (Q - 1) * kb);
-        if (sq_ > 0) E.line("s_add_u32 s17, s17, %d", (sq_ - 1) * kb);
+        E.line("s_mul_i32 s17, s14, %d", (Q - 1) * kbr);
+        if (sq_ > 0) E.line("s_add_u32 s17, s17, %d", (sq_ - 1) * kbr);
         E.v(va, 4, fmt("v_lshlrev_b32_e32 v%d, 4, v1", va));
         E.v(va, 4, fmt("v_add_u32_e32 v%d, s17, v%d", va, va));
-        if (sq_ > 0) {
-          // later splits leave their partial sums in LDS, 16 bytes per lane and 4 channels
-          for (int k4 = 0; k4 < p.Mg / 4; k4++)
-            E.line("ds_write_b128 v%d, v[%d:%d] offset:%d", va, vAcc + 4 * k4, vAcc + 4 * k4 + 3, k4 * 1024);
-          E.line("s_waitcnt lgkmcnt(0)");
+        const int t0r = (vOff + 2) & ~1;  // even-aligned temporaries
+        const int nb = std::max(1, std::min(8, (vAcc - t0r) / 4));
+        const int vb = vOff + 1;           // base register of a batch of reads
+        for (int j = 0; j < rounds; j++) {
+          const int k40 = j * KC / 4, k41 = std::min(p.Mg, (j + 1) * KC) / 4, nk = k41 - k40;
+          const bool last = j + 1 == rounds;
+          if (sq_ > 0) {
+            for (int k4 = k40; k4 < k41; k4++)
+              E.line("ds_write_b128 v%d, v[%d:%d] offset:%d", va, vAcc + 4 * k4, vAcc + 4 * k4 + 3, (k4 - k40) * 1024);
+            E.line("s_waitcnt lgkmcnt(0)");
+            E.line("s_barrier");
+            if (!last) E.line("s_barrier");  // split 0 has read this round's parts
+            continue;
+          }
           E.line("s_barrier");
+          // block b of the round: split b / nk + 1, channels 4 * (k40 + b % nk) .. + 3
+          const int nq = (Q - 1) * nk;
+          auto off = [&](int b) { return (b / nk) * kbr + (b % nk) * 1024; };
+          for (int b0 = 0; b0 < nq; b0 += nb) {
+            const int b1 = std::min(nq, b0 + nb);
+            E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", vb, off(b0), va));
+            for (int bb = b0; bb < b1; bb++)
+              E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (bb - b0), t0r + 4 * (bb - b0) + 3, vb,
+                     off(bb) - off(b0));
+            E.line("s_waitcnt lgkmcnt(0)");
+            for (int bb = b0; bb < b1; bb++) {
+              const int k4 = k40 + bb % nk;
+              for (int jj = 0; jj < 4; jj++)
+                E.v(vAcc + 4 * k4 + jj, 4,
+                    fmt("v_add_f32_e32 v%d, v%d, v%d", vAcc + 4 * k4 + jj, vAcc + 4 * k4 + jj, t0r + 4 * (bb - b0) + jj));
+            }
+          }
+          if (!last) E.line("s_barrier");  // the parts may be overwritten
+        }
+        if (sq_ > 0) {
           E.line("s_endpgm");
           p.sec_valu = std::max(p.sec_valu, E.valu - v0 + p.Mg / 4);
           p.sec_steps = std::max<long long>(p.sec_steps, T_);
           continue;
-        }
-        // split 0 adds them in split order (batches of reads in flight), then stores
-        E.line("s_barrier");
-        const int t0r = (vOff + 2) & ~1;                  // even-aligned temporaries
-        const int nb = std::max(1, std::min(8, (vAcc - t0r) / 4));
-        const int nq = (Q - 1) * (p.Mg / 4);
-        // (a batch's reads are addressed from their own base register, vOff + 1, so the
-        // 16-bit instruction offsets stay below 8 KB however large the unit's partials are)
-        const int vb = vOff + 1;
-        for (int b0 = 0; b0 < nq; b0 += nb) {
-          const int b1 = std::min(nq, b0 + nb);
-          E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", vb, b0 * 1024, va));
-          for (int b = b0; b < b1; b++)
-            E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (b - b0), t0r + 4 * (b - b0) + 3, vb,
-                   (b - b0) * 1024);
-          E.line("s_waitcnt lgkmcnt(0)");
-          for (int b = b0; b < b1; b++) {
-            const int k4 = b % (p.Mg / 4);
-            for (int j = 0; j < 4; j++)
-              E.v(vAcc + 4 * k4 + j, 4,
-                  fmt("v_add_f32_e32 v%d, v%d, v%d", vAcc + 4 * k4 + j, vAcc + 4 * k4 + j, t0r + 4 * (b - b0) + j));
-          }
         }
       }
       for (int k = 0; k < nrow; k++) {

@@ -50,6 +50,7 @@ struct BakePlan {
   int Mg = 0;       // accumulators per wavefront (largest group, padded to 4 when Q > 1)
   int vgprs = 0, sgprs = 0;
   int lds_bytes = 0;         // partial sums of the channel splits
+  int rc = 0;                // channels per round of the split reduction (LDS per split: rc/4 KB)
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
   long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)

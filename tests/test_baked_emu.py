@@ -150,9 +150,15 @@ def test_crossbar_shifts_equal_dpp_shifts(c, monkeypatch):
     assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
 
 
-def test_channel_split_partials_beyond_64kb_of_offsets(monkeypatch):
-    """128 accumulators and 4 channel splits: split 0 reads 96 KB of partial sums, more than a
-    16-bit instruction offset reaches (each batch of reads is addressed from its own base)."""
+@pytest.mark.parametrize("env", ["G=2,Q=4,T=1", "G=2,Q=3,T=2"])
+def test_channel_split_reduction_in_rounds(env, monkeypatch):
+    """128 accumulators per wavefront and several channel splits: the partial sums go through one
+    LDS buffer of 32 channels per later split, reused over 4 rounds (two barriers per round), so a
+    unit needs (Q - 1) * 8 KB of LDS however many channels it holds; the sums are added in split
+    order, so the result equals the oracle's within tolerance and repeats bit for bit."""
     d = workloads.make_custom(1, 12, 5, 7, 256, 3, 3, 1, 1, 0.3, 31)
-    y, info = _check(d, 1, 1, "G=2,Q=4", "G=2,Q=4,T=1", monkeypatch)
-    assert info["bake_splits"] == 4 and info["bake_lds_bytes"] >= 96 * 1024
+    y, info = _check(d, 1, 1, env, env, monkeypatch)
+    Q, T = info["bake_splits"], info["bake_units_per_wg"]
+    assert Q > 2 and info["bake_lds_bytes"] == T * (Q - 1) * 8 * 1024
+    y2, _, _ = _emulate(d, 1, 1)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
