@@ -245,7 +245,8 @@ def main():
             "fma_tflops": fma, "fma_peak_tflops": roofline.FP32_VECTOR_PEAK_TFLOPS,
             "fma_frac_of_peak": round(best / roofline.FP32_VECTOR_PEAK_TFLOPS, 3),
             "lds_read_tbs": {"b32": round(probes.lds_read_rate(cus, 1), 2), "b128": round(probes.lds_read_rate(cus, 4), 2)},
-            "headline_kernel_lds_bytes": 0 if launch["mapping"] == sc.MAPPING_BAKED and launch["splits"] <= 1 else None}
+            "headline_kernel_lds_bytes_per_workgroup": launch["lds_bytes"],
+            "headline_kernel_stages_input_in_lds": bool(launch["stage"])}
         log(f"[bench] roof probes: FMA {fma} TFLOP/s, LDS {extra['roof_probes']['lds_read_tbs']} TB/s")
 
     # every workload layer, timed the same way (cold, rotated sets), with the launched plan
@@ -262,9 +263,9 @@ def main():
             per[name] = {"us": round(cms_ * 1e3, 2), "sem_us": round(csem * 1e3, 2), "tflops": round(mm["tflops"], 3),
                          "frac_of_8tbs": round(mm["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(mm["ai"], 2),
                          "bound": mm["bound"], "roofline_frac": round(mm["frac"], 4), "nnz": hh.info()["nnz"],
-                         "launch": {k: li[k] for k in ("mapping", "variant", "groups", "splits", "units_per_wg",
-                                                       "depth", "grid", "waves", "vgprs", "lds_bytes",
-                                                       "tile_pixels", "quad")}}
+                         "launch": {k: li[k] for k in ("mapping", "variant", "stage", "groups", "splits",
+                                                       "units_per_wg", "depth", "grid", "waves", "vgprs",
+                                                       "lds_bytes", "tile_pixels", "chunk_channels", "quad")}}
             log(f"[bench] config {name}: {cms_ * 1e3:.1f} us, {mm['tflops']:.2f} TFLOP/s, "
                 f"{mm['gbs'] / roofline.HBM_PEAK_GBS:.3f} of 8 TB/s, launch {per[name]['launch']}")
             del dd, hh, xxs, yys
@@ -272,9 +273,9 @@ def main():
         per[layer] = {"us": round(ms * 1e3, 2), "sem_us": round(sem * 1e3, 2), "tflops": round(m["tflops"], 3),
                       "frac_of_8tbs": round(m["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(m["ai"], 2),
                       "bound": m["bound"], "roofline_frac": round(m["frac"], 4), "nnz": nnz,
-                      "launch": {k: launch[k] for k in ("mapping", "variant", "groups", "splits", "units_per_wg",
-                                                        "depth", "grid", "waves", "vgprs", "lds_bytes", "tile_pixels",
-                                                        "quad")}}
+                      "launch": {k: launch[k] for k in ("mapping", "variant", "stage", "groups", "splits",
+                                                        "units_per_wg", "depth", "grid", "waves", "vgprs",
+                                                        "lds_bytes", "tile_pixels", "chunk_channels", "quad")}}
         extra["per_config"] = per
 
     # CPU oracle: one untimed run over the whole batch (whose result also checks every output

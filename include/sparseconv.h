@@ -173,6 +173,12 @@ typedef struct {
   int32_t bake_vgprs;       /* VGPRs per lane */
   int32_t bake_lds_bytes;   /* LDS per workgroup (partial sums of the channel splits) */
   int32_t bake_variants;    /* weights-in-code kernels the handle holds */
+  int32_t bake_stage;       /* 1: the base kernel stages input rows in LDS (chunks of
+                               bake_chunk_channels channels, bake_buffers chunk buffers, the
+                               copy running bake_buffers - 1 chunks ahead); 0: it loads them
+                               into registers */
+  int32_t bake_chunk_channels;
+  int32_t bake_buffers;
   int64_t bake_code_bytes;  /* bytes of generated code of the base kernel */
 } sc_info;
 
@@ -191,10 +197,11 @@ typedef struct {
   int32_t units_per_wg;  /* weights-in-code: units per workgroup */
   int32_t depth;         /* weights-in-code: load steps in flight */
   int32_t valid_lanes;   /* weights-in-code: output positions per wavefront */
-  int32_t tile_pixels;   /* LDS-tile: extended positions per work unit */
+  int32_t tile_pixels;   /* LDS-tile and staged weights-in-code: positions per work unit */
   int32_t rows_per_wave; /* LDS-tile: output-channel slots per wavefront */
-  int32_t chunk_channels;/* LDS-tile: input channels per staged chunk */
+  int32_t chunk_channels;/* LDS-tile and staged weights-in-code: input channels per staged chunk */
   int32_t quad;          /* LDS-tile: 1 for a quad plan (16-byte LDS reads) */
+  int32_t stage;         /* weights-in-code: 1 when the kernel stages input windows in LDS */
 } sc_launch;
 
 /*

@@ -65,7 +65,8 @@ class sc_info(ctypes.Structure):
                                                "split_pieces", "plan_variants", "entry_bytes", "mapping",
                                                "bake_groups", "bake_splits", "bake_units_per_wg",
                                                "bake_valid_lanes", "bake_pitch", "bake_depth", "bake_vgprs",
-                                               "bake_lds_bytes", "bake_variants")] + \
+                                               "bake_lds_bytes", "bake_variants", "bake_stage",
+                                               "bake_chunk_channels", "bake_buffers")] + \
                [("bake_code_bytes", ctypes.c_int64)]
 
     def as_dict(self):
@@ -77,7 +78,7 @@ class sc_launch(ctypes.Structure):
                 ("waves", ctypes.c_int64), ("pre_grid", ctypes.c_int64)] + \
                [(n, ctypes.c_int32) for n in ("block", "lds_bytes", "vgprs", "groups", "splits", "units_per_wg",
                                                "depth", "valid_lanes", "tile_pixels", "rows_per_wave",
-                                               "chunk_channels", "quad")]
+                                               "chunk_channels", "quad", "stage")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

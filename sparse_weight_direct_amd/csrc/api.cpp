@@ -630,6 +630,9 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
     info->bake_vgprs = b.vgprs;
     info->bake_lds_bytes = b.lds_bytes;
     info->bake_variants = (int32_t)h->bk.size();
+    info->bake_stage = b.stage;
+    info->bake_chunk_channels = b.Cc;
+    info->bake_buffers = b.stage ? b.nbuf : 0;
     info->bake_code_bytes = b.code_bytes;
   }
   if (h->escoin) {
@@ -802,30 +805,42 @@ bool baked_fits(const sc_handle* h, int N) {
   const sc::Geom& g = h->g;
   const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
   long long pb = 0;
-  for (const BakedKernel& k : h->bk) pb = std::max<long long>(pb, k.p.Pb);
-  return nin * 4 < (1LL << 31) && nout * 4 < (1LL << 31) && (long long)N * g.E * pb < (1LL << 31) - 128;
+  for (const BakedKernel& k : h->bk) pb = std::max<long long>(pb, k.p.stage ? (long long)g.HYp * g.Pp / g.E + 1 : k.p.Pb);
+  return nin * 4 < (1LL << 31) && nout * 4 < (1LL << 31) && (long long)N * g.E * pb < (1LL << 31) - 4096;
 }
 
 // The weights-in-code kernel a forward of N images launches (-1: none, use the LDS-tile
-// plans): the base kernel when it gives every SIMD a wavefront (measured best on the large
-// layers), else the handle's kernel with the lowest estimated cycles for N.
+// plans): the one sparseconv_tune pinned for N; else, when it gives every SIMD a wavefront, the
+// staged kernel (measured best on the 112x112 layers: as fast as the base kernel where the
+// FMAs dominate, up to 1.2x faster where the traffic does) or the base kernel; else the
+// handle's kernel with the lowest estimated cycles for N among the unstaged ones (few
+// wavefronts leave the staged kernel's DMA latency exposed).
+long long baked_waves(const sc_handle* h, const sc::BakePlan& bp, int N);
+
+// Whether weights-in-code kernel i can read this input: staged kernels of the wide layout copy
+// 16 bytes per lane, which needs a 16-byte aligned input.
+bool bk_usable(const sc_handle* h, size_t i, const float* input) {
+  const sc::BakePlan& p = h->bk[i].p;
+  return !(p.stage && p.bw == 256 && (reinterpret_cast<uintptr_t>(input) & 15));
+}
+
 int pick_baked(const sc_handle* h, int N) {
   if (!baked_fits(h, N)) return -1;
   const int t = tuned_choice(h, N, 0);
   if (t >= 0 && (size_t)t < h->bk.size()) return t;
-  {
-    const sc::BakePlan& b = h->bk[0].p;
-    const long long qtot = (long long)N * h->g.E * b.Pb;
-    const long long waves = (qtot + b.V - 1) / b.V * b.G * b.Q;
-    if (waves >= 4LL * h->cus) return 0;
-  }
+  for (size_t i = 0; i < h->bk.size(); i++)
+    if (h->bk[i].p.stage && baked_waves(h, h->bk[i].p, N) >= 4LL * h->cus) return (int)i;
+  if (baked_waves(h, h->bk[0].p, N) >= 4LL * h->cus) return 0;
   int best = 0;
   double bc = 0;
+  bool any = false;
   for (size_t i = 0; i < h->bk.size(); i++) {
+    if (h->bk[i].p.stage && h->bk.size() > 1) continue;
     const double c = sc::bake_estimate(h->g, h->bk[i].p, N, h->cus);
-    if (i == 0 || c < bc) {
+    if (!any || c < bc) {
       best = (int)i;
       bc = c;
+      any = true;
     }
   }
   return best;
@@ -834,17 +849,31 @@ int pick_baked(const sc_handle* h, int N) {
 // Kernel arguments and grid of a weights-in-code kernel for N images (pointers left 0).
 sc::BakeArgs baked_args(const sc_handle* h, const sc::BakePlan& bp, int N) {
   const sc::Geom& g = h->g;
-  const long long qtot = (long long)N * g.E * bp.Pb;
   sc::BakeArgs a{};
   a.N = (uint32_t)N;
-  a.qtot = (uint32_t)qtot;
-  a.ntiles = (uint32_t)((qtot + bp.V - 1) / bp.V);
   a.x_bytes = (uint32_t)((long long)N * g.C * g.H * g.W * 4);
   a.y_bytes = (uint32_t)((long long)N * g.M * g.E * g.F * 4);
+  if (bp.stage) {
+    // positions of the padded layout; ntiles = workgroups (blocks of T tiles of 64) per group
+    const long long qtot = (long long)N * g.HYp * g.Pp;
+    a.qtot = (uint32_t)qtot;
+    a.ntiles = (uint32_t)((qtot + 64LL * bp.T - 1) / (64LL * bp.T));
+    a.per_xcd = (uint32_t)(((long long)a.ntiles * bp.G + 7) / 8);
+    return a;
+  }
+  const long long qtot = (long long)N * g.E * bp.Pb;
+  a.qtot = (uint32_t)qtot;
+  a.ntiles = (uint32_t)((qtot + bp.V - 1) / bp.V);
   const long long units = (long long)a.ntiles * bp.G;
   const long long wgs = (units + bp.T - 1) / bp.T;
   a.per_xcd = (uint32_t)((wgs + 7) / 8);
   return a;
+}
+
+// Wavefronts a weights-in-code kernel runs for N images.
+long long baked_waves(const sc_handle* h, const sc::BakePlan& bp, int N) {
+  const sc::BakeArgs a = baked_args(h, bp, N);
+  return bp.stage ? (long long)a.ntiles * bp.T * bp.G : (long long)a.ntiles * bp.G * bp.Q;
 }
 
 // Bytes of the padded input the "Escoin" mapping writes for N images (0 for other handles).
@@ -895,7 +924,7 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
       return fail(SC_EDEVICE, std::string("kernel launch failed: ") + hipGetErrorString((hipError_t)e));
     return SC_OK;
   }
-  const int bi = pick_baked(h, N);
+  int bi = pick_baked(h, N);
   if (bi >= 0) {
     const long long nin = (long long)N * g.C * g.H * g.W, nout = (long long)N * g.M * g.E * g.F;
     if (!input || !output) return fail(SC_EINVAL, "input or output is NULL");
@@ -904,6 +933,15 @@ sc_status forward_impl(const sc_handle* h, const float* input, float* output, in
       return fail(SC_EINVAL, "input or output is not 4-byte aligned");
     if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
       return fail(SC_EINVAL, "current device differs from the device the handle was packed on");
+    if (!bk_usable(h, (size_t)bi, input)) {
+      // a staged kernel on an input that is not 16-byte aligned: the first kernel that reads
+      // rows directly
+      int alt = -1;
+      for (size_t i = 0; i < h->bk.size() && alt < 0; i++)
+        if (bk_usable(h, i, input)) alt = (int)i;
+      if (alt < 0) return fail(SC_EUNSUPPORTED, "this handle's kernel needs a 16-byte aligned input");
+      bi = alt;
+    }
     return launch_bk(h, bi, input, output, N, hip_stream);
   }
   if (h->var.empty())
@@ -984,6 +1022,7 @@ sc_status sparseconv_tune(sc_handle* h, const float* input, float* output, int32
   int best = -1;
   float best_ms = 0.0f;
   for (int i = 0; i < n && st == SC_OK; i++) {
+    if (bk && !bk_usable(h, (size_t)i, input)) continue;
     auto launch = [&]() { return bk ? launch_bk(h, i, input, output, N, hip_stream)
                                     : launch_var(h, (size_t)i, input, output, N, hip_stream); };
     st = launch();  // first launch of a kernel: not timed
@@ -1053,7 +1092,12 @@ sc_status sparseconv_launch_info(const sc_handle* h, int32_t N, sc_launch* out) 
     out->units_per_wg = p.T;
     out->depth = p.D;
     out->valid_lanes = p.V;
-    out->waves = (int64_t)a.ntiles * p.G * p.Q;
+    out->waves = baked_waves(h, p, N);
+    if (p.stage) {
+      out->chunk_channels = p.Cc;
+      out->tile_pixels = p.T * 64;
+      out->stage = 1;
+    }
     return SC_OK;
   }
   if (h->var.empty()) return fail(SC_EUNSUPPORTED, "batch too large for the weights-in-code kernel");

@@ -52,6 +52,10 @@ BakeForce bake_force_from_env() {
   f.D = env_key(e, "D", -1);
   f.dpp = env_key(e, "DPP", -1);
   f.perm = env_key(e, "PERM", -1);
+  f.stage = env_key(e, "STAGE", -1);
+  f.nb = env_key(e, "NB", -1);
+  f.cc = env_key(e, "CC", -1);
+  f.ra = env_key(e, "RA", -1);
   return f;
 }
 
@@ -268,6 +272,100 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   return true;
 }
 
+// Staged plans: registers of the fixed part, the DMA source offsets and the two sets of tap
+// reads, then the accumulators.
+// Steps of tap reads a staged kernel issues ahead: at most 15 LDS reads may be outstanding
+// (the lgkm counter), and the read sets of the steps in flight and the current step hold
+// (ra + 1) * S registers.
+inline int staged_read_ahead(const Geom& g, int forced) {
+  const int cap = std::max(1, 15 / g.S - 1);
+  return std::min(cap, forced > 0 ? forced : 1);  // more measured no faster
+}
+
+inline int staged_vgprs(const Geom& g, int nvb, int Mg, int ra) {
+  const int acc0 = (kFixedV + nvb + (ra + 1) * g.S + 1) & ~1;
+  return (std::max(acc0 + Mg, acc0 + kTemps) + 3) & ~3;
+}
+
+// Fill a staged plan's derived fields for its G, T and (if > 0) forced buffer count and chunk
+// channels (stride 1, no channel splits).
+bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
+                     int nb, int cc, int ra, BakePlan* pp, std::string* why) {
+  BakePlan& p = *pp;
+  if (g.st != 1) {
+    *why = "staged plans need stride 1";
+    return false;
+  }
+  if (g.S > 7) {  // the reads of two steps (up to 2 S) must fit the 15 LDS reads in flight
+    *why = "staged plans read at most 7 taps per step";
+    return false;
+  }
+  p.Q = 1;
+  p.dpp = 1;  // a tap's column s is its lane shift sq: here an LDS offset
+  p.perm = 0;
+  p.maxsq = g.S - 1;
+  p.ra = staged_read_ahead(g, ra);
+  p.V = 64;
+  p.Pb = g.Pp;
+  p.bw = g.wide ? 256 : 64;  // 16 bytes per lane in the wide layout, else 4
+  p.chs = (p.T * 64 + (g.R - 1) * g.Pp + g.S - 1 + p.bw - 1) / p.bw * p.bw;
+  p.nblk = p.chs / p.bw;
+  p.pairdist = (p.T % p.nblk == 0) ? 1 : 0;
+  const int nvb = p.pairdist ? 1 : (p.nblk + p.T - 1) / p.T;
+  // nbuf chunk buffers (the DMA runs nbuf - 1 chunks ahead); every ds_read offset (buffer +
+  // channel + tap) must fit 16 bits
+  const int reach = 4 * ((g.R - 1) * g.Pp + g.S);
+  p.nbuf = nb > 0 ? std::max(2, std::min(nb, 8)) : 2;  // deeper prefetch measured no faster
+  p.Cc = std::min(g.C, cc > 0 ? cc : 8);
+  for (;;) {
+    while (p.Cc > 1 && p.nbuf * p.Cc * p.chs * 4 + reach > 65535) p.Cc--;
+    if (p.nbuf * p.Cc * p.chs * 4 + reach <= 65535) break;
+    if (p.nbuf == 2 || nb > 0) {
+      *why = "staged window too large for 16-bit LDS offsets";
+      return false;
+    }
+    p.nbuf--;
+    p.Cc = std::min(g.C, cc > 0 ? cc : 8);
+  }
+  // at most 48 DMAs of the chunks ahead outstanding per wavefront (the counter holds 63)
+  auto dmas = [&](int cc) { return p.pairdist ? (cc + p.T / p.nblk - 1) / (p.T / p.nblk) : cc * nvb; };
+  while (p.Cc > 1 && (p.nbuf - 1) * dmas(p.Cc) > 48) p.Cc--;
+  if ((p.nbuf - 1) * dmas(p.Cc) > 48) {
+    *why = "staged window needs too many DMAs per chunk";
+    return false;
+  }
+  p.rows = deal_rows(g.M, p.G, rowptr);
+  int mg = 0;
+  for (auto& r : p.rows) mg = std::max(mg, (int)r.size());
+  p.Mg = mg;
+  p.D = 0;
+  p.vgprs = staged_vgprs(g, nvb, p.Mg, p.ra);
+  if (p.vgprs > kMaxVgpr) {
+    *why = "output channels per group exceed the registers";
+    return false;
+  }
+  p.lds_bytes = p.nbuf * p.Cc * p.chs * 4;
+  p.rc = 0;
+  auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, nullptr);
+  p.sec_valu = p.sec_steps = p.sec_loads = 0;
+  long long code = 4096;
+  for (auto& L : nzs) {
+    auto steps = group_steps(g, p.dpp, L);
+    long long v = 0, ld = 0;
+    for (const Step& st : steps) {
+      v += (long long)st.nz.size();
+      code += 8 * (long long)st.nz.size() + 8 * (st.sqmax[0] + 1) + 4;
+    }
+    ld = (long long)((g.C + p.Cc - 1) / p.Cc) * p.Cc * ((p.nblk + p.T - 1) / p.T);
+    p.sec_valu = std::max(p.sec_valu, v + p.Mg / 4);
+    p.sec_steps = std::max<long long>(p.sec_steps, (long long)steps.size());
+    p.sec_loads = std::max(p.sec_loads, ld);
+    code += ld * 24;
+  }
+  p.code_bytes = code;
+  return true;
+}
+
 }  // namespace
 
 std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>& rowptr,
@@ -330,6 +428,28 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     shapes = {{G0, 1, 4}, {G0, 2, 1}, {G0, 3, 1}, {G0, 4, 1}, {std::min(M, 2 * G0), 1, 4},
               {std::min(M, 4 * G0), 1, 4}, {std::min(M, 2 * G0), 2, 1}};
   }
+  // staged plan: forced (STAGE=1), or appended to the candidates for stride-1 layers
+  auto add_staged = [&](int G, int T) {
+    BakePlan c = p;
+    c.stage = 1;
+    c.G = G;
+    c.T = T;
+    std::string w;
+    if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, &c, &w))
+      out.push_back(std::move(c));
+    else if (out.empty())
+      *why = w;
+  };
+  auto staged_groups = [&](int nvb) {
+    int n = 1;
+    while (n < M && staged_vgprs(g, nvb, (M + n - 1) / n, staged_read_ahead(g, f.ra)) > kVgprTarget) n++;
+    return n;
+  };
+  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0) {
+    const int T = f.T > 0 ? f.T : 4;
+    add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T);
+    return out;
+  }
   for (const Shape& sh : shapes) {
     if (sh.Q < 1 || sh.Q > 16) {
       *why = "channel splits must be 1 to 16";
@@ -352,12 +472,13 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     else if (out.empty())
       *why = w;
   }
+  if (!f.any() && g.st == 1) add_staged(staged_groups(2), 4);
   return out;
 }
 
 double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus) {
-  const long long qtot = (long long)N * g.E * p.Pb;
-  const long long ntiles = (qtot + p.V - 1) / p.V;
+  const long long qtot = p.stage ? (long long)N * g.HYp * g.Pp : (long long)N * g.E * p.Pb;
+  const long long ntiles = p.stage ? (qtot + 64LL * p.T - 1) / (64LL * p.T) * p.T : (qtot + p.V - 1) / p.V;
   const long long waves = ntiles * p.G * p.Q;
   const double simds = 4.0 * cus;
   // VALU: a SIMD runs about ceil(waves / SIMDs) sections' instructions one after the other
@@ -440,9 +561,415 @@ struct Emitter {
 
 }  // namespace
 
+// Kernel descriptor and code-object metadata of a generated kernel (symbol sc_baked, the
+// 40-byte BakeArgs argument segment), appended to its code.
+void finish_kernel(Emitter& E, BakePlan& p, int nv, int WPB, std::string* src) {
+  p.sgprs = 40;
+  char kd[2048];
+  snprintf(kd, sizeof kd,
+           "\t.section .rodata,\"a\",@progbits\n"
+           "\t.p2align 6, 0x0\n"
+           "\t.amdhsa_kernel sc_baked\n"
+           "\t\t.amdhsa_group_segment_fixed_size %d\n"
+           "\t\t.amdhsa_private_segment_fixed_size 0\n"
+           "\t\t.amdhsa_kernarg_size 40\n"
+           "\t\t.amdhsa_user_sgpr_count 2\n"
+           "\t\t.amdhsa_user_sgpr_kernarg_segment_ptr 1\n"
+           "\t\t.amdhsa_system_sgpr_workgroup_id_x 1\n"
+           "\t\t.amdhsa_system_vgpr_workitem_id 0\n"
+           "\t\t.amdhsa_next_free_vgpr %d\n"
+           "\t\t.amdhsa_next_free_sgpr %d\n"
+           "\t\t.amdhsa_accum_offset %d\n"
+           "\t\t.amdhsa_reserve_vcc 1\n"
+           "\t\t.amdhsa_float_denorm_mode_32 3\n"
+           "\t\t.amdhsa_float_denorm_mode_16_64 3\n"
+           "\t\t.amdhsa_dx10_clamp 1\n"
+           "\t\t.amdhsa_ieee_mode 1\n"
+           "\t.end_amdhsa_kernel\n"
+           "\t.text\n",
+           p.lds_bytes, nv, p.sgprs, nv);
+  E.s += kd;
+  char md[2048];
+  snprintf(md, sizeof md,
+           "\t.amdgpu_metadata\n"
+           "---\n"
+           "amdhsa.kernels:\n"
+           "  - .agpr_count: 0\n"
+           "    .args:\n"
+           "      - .address_space: global\n        .offset: 0\n        .size: 8\n        .value_kind: global_buffer\n"
+           "      - .address_space: global\n        .offset: 8\n        .size: 8\n        .value_kind: global_buffer\n"
+           "      - .offset: 16\n        .size: 4\n        .value_kind: by_value\n"
+           "      - .offset: 20\n        .size: 4\n        .value_kind: by_value\n"
+           "      - .offset: 24\n        .size: 4\n        .value_kind: by_value\n"
+           "      - .offset: 28\n        .size: 4\n        .value_kind: by_value\n"
+           "      - .offset: 32\n        .size: 4\n        .value_kind: by_value\n"
+           "      - .offset: 36\n        .size: 4\n        .value_kind: by_value\n"
+           "    .group_segment_fixed_size: %d\n"
+           "    .kernarg_segment_align: 8\n"
+           "    .kernarg_segment_size: 40\n"
+           "    .max_flat_workgroup_size: %d\n"
+           "    .name: sc_baked\n"
+           "    .private_segment_fixed_size: 0\n"
+           "    .sgpr_count: %d\n"
+           "    .symbol: sc_baked.kd\n"
+           "    .vgpr_count: %d\n"
+           "    .wavefront_size: 64\n"
+           "amdhsa.target: amdgcn-amd-amdhsa--gfx950\n"
+           "amdhsa.version:\n  - 1\n  - 2\n"
+           "...\n"
+           "\t.end_amdgpu_metadata\n",
+           p.lds_bytes, WPB * 64, p.sgprs + 6, nv);
+  E.s += md;
+  *src = std::move(E.s);
+}
+
+// LDS DMA instructions of chunk k (channels k*Cc ...) that every wavefront of a staged
+// workgroup issues at least (wavefronts skip the blocks and channels past the chunk's end).
+static int staged_dmas_min(const Geom& g, const BakePlan& p, int k) {
+  const int cn = std::min(p.Cc, g.C - k * p.Cc);
+  int best = 1 << 30;
+  for (int w = 0; w < p.T; w++) {
+    int n = 0;
+    if (p.pairdist) {
+      const int per = p.T / p.nblk;
+      for (int i = 0; i * per < cn; i++) n += (w / p.nblk + i * per < cn) ? 1 : 0;
+    } else {
+      const int nvb = (p.nblk + p.T - 1) / p.T;
+      for (int k2 = 0; k2 < nvb; k2++) n += (k2 * p.T + w < p.nblk) ? cn : 0;
+    }
+    best = std::min(best, n);
+  }
+  return best;
+}
+
+// Staged kernel (stride 1).  Positions I = n*HYp*Pp + yp*Pp + xq of the padded layout (the
+// LDS-tile kernel's: HYp = H + 2 pad rows per image, pitch Pp, input column x at xq = x + xoff;
+// output (yp, xq - cshift) valid for yp < E, 0 <= xq - cshift < F); tap (r, s) of position I
+// is the padded word I + r*Pp + s.  Workgroup b covers positions [I0, I0 + T*64) of one group:
+// wavefront w holds I0 + 64 w + lane.  Per chunk of Cc channels each channel's window
+// [I0, I0 + chs) is copied into LDS once (LDS DMA: lane i writes M0 + 4*i*(bw/64); zero where
+// the source lies in the padding: out-of-range offset) into one of nbuf buffers, nbuf - 1
+// chunks ahead of the FMAs; a step's taps are ds_read_b32 from the lane's base v5 at
+// immediate offsets, issued a step ahead.
+bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
+                     const std::vector<float>& val, BakePlan& p, std::string* src, std::string* err) {
+  const int T = p.T, S = g.S;
+  const int nvb = p.pairdist ? 1 : (p.nblk + T - 1) / T;
+  const int lw = p.bw / 64;  // DMA words per lane
+  const int vB = kFixedV;              // DMA source offsets
+  const int NS = p.ra + 1;             // read sets: the current step's and ra steps ahead
+  const int vRd = vB + nvb;            // NS sets of S tap reads
+  const int vAcc = (vRd + NS * S + 1) & ~1;
+  const int vTmp = vAcc;               // prologue temporaries overlap the accumulators
+  const int nv = staged_vgprs(g, nvb, p.Mg, p.ra);
+  if (nv > kMaxVgpr || vAcc + p.Mg > nv) {
+    *err = "staged kernel needs more than 256 VGPRs";
+    return false;
+  }
+  p.vgprs = nv;
+  const long long HW4 = 4ll * g.H * g.W;
+  const long long EF4 = 4ll * g.E * g.F;
+  const int BUF = p.Cc * p.chs * 4;  // bytes of one chunk buffer
+
+  Emitter E;
+  E.s.reserve((size_t)rowptr[g.M] * 48 + 65536);
+  E.s += "\t.amdgcn_target \"amdgcn-amd-amdhsa--gfx950\"\n";
+  E.s += "\t.amdhsa_code_object_version 6\n";
+  E.s += "\t.text\n\t.globl sc_baked\n\t.p2align 8\n\t.type sc_baked,@function\n";
+  E.label("sc_baked");
+  E.line("s_load_dwordx8 s[20:27], s[0:1], 0x0");
+  E.line("s_load_dwordx2 s[28:29], s[0:1], 0x20");
+  E.v(vTmp, 4, fmt("v_lshrrev_b32_e32 v%d, 6, v0", vTmp));
+  E.v(1, 4, "v_and_b32_e32 v1, 63, v0");
+  E.v(2, 4, "v_mov_b32_e32 v2, 0");
+  E.v(3, 4, "v_bfrev_b32_e32 v3, 1");  // 0x80000000
+  E.rfl_guard(vTmp);
+  E.v(-1, 8, fmt("v_readfirstlane_b32 s14, v%d", vTmp));
+  E.line("s_waitcnt lgkmcnt(0)");
+  // logical workgroup -> (group s16, block of T tiles s15); s25 = blocks per group
+  E.line("s_and_b32 s15, s2, 7");
+  E.line("s_mul_i32 s15, s15, s29");
+  E.line("s_lshr_b32 s16, s2, 3");
+  E.line("s_add_u32 s15, s15, s16");
+  E.line("s_mov_b32 s16, 0");
+  for (int q = 0; q < p.G; q++) {
+    E.line("s_cmp_lt_u32 s15, s25");
+    E.line("s_cbranch_scc1 .Lunit");
+    E.line("s_sub_u32 s15, s15, s25");
+    E.line("s_add_u32 s16, s16, 1");
+  }
+  E.line("s_endpgm");
+  E.label(".Lunit");
+  E.line("s_mov_b32 s4, s20");
+  E.line("s_and_b32 s5, s21, 0xffff");
+  E.line("s_mov_b32 s6, s26");
+  E.line("s_mov_b32 s7, 0x20000");
+  E.line("s_mov_b32 s8, s22");
+  E.line("s_and_b32 s9, s23, 0xffff");
+  E.line("s_mov_b32 s10, s27");
+  E.line("s_mov_b32 s11, 0x20000");
+  const int tPos = vTmp, tN = vTmp + 1, tRem = vTmp + 2, tY = vTmp + 3, tX = vTmp + 4, t0 = vTmp + 5,
+            t1 = vTmp + 6, t2 = vTmp + 7;
+  auto divide = [&](int dst, int num, uint32_t d, int sreg) {
+    if (d == 1) {
+      E.v(dst, 4, fmt("v_mov_b32_e32 v%d, v%d", dst, num));
+      return;
+    }
+    uint32_t m;
+    int l;
+    bake_magic(d, &m, &l);
+    E.line("s_mov_b32 s%d, 0x%x", sreg, m);
+    E.v(dst, 8, fmt("v_mul_hi_u32 v%d, v%d, s%d", dst, num, sreg));
+    if (l > 0) E.v(dst, 4, fmt("v_lshrrev_b32_e32 v%d, %d, v%d", dst, l, dst));
+  };
+  const uint32_t IMG = (uint32_t)g.HYp * (uint32_t)g.Pp;
+  // (n, yp, xq) of the extended index in vector register num
+  auto decompose = [&](int num) {
+    divide(tN, num, IMG, 17);
+    E.line("s_mov_b32 s18, 0x%x", IMG);
+    E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+    E.v(tRem, 4, fmt("v_sub_u32_e32 v%d, v%d, v%d", tRem, num, t0));
+    divide(tY, tRem, (uint32_t)g.Pp, 17);
+    E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.Pp);
+    E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tY));
+    E.v(tX, 4, fmt("v_sub_u32_e32 v%d, v%d, v%d", tX, tRem, t0));
+  };
+  // this wavefront's position and LDS base
+  E.line("s_mul_i32 s17, s15, %d", T);
+  E.line("s_add_u32 s17, s17, s14");
+  E.line("s_mul_i32 s17, s17, 64");
+  E.v(tPos, 4, fmt("v_add_u32_e32 v%d, s17, v1", tPos));
+  E.line("s_mul_i32 s18, s14, 64");
+  E.v(5, 4, "v_add_u32_e32 v5, s18, v1");
+  E.v(5, 4, "v_lshlrev_b32_e32 v5, 2, v5");
+  decompose(tPos);
+  // output offset 4*((n*M*E + yp)*F + f), f = xq - cshift; out of range unless yp < E,
+  // f < F (unsigned) and n < N
+  E.v(t1, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", t1, (uint32_t)(-g.cshift), tX));
+  E.line("s_mov_b32 s18, 0x%x", (uint32_t)((uint64_t)g.M * g.E));
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+  E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tY));
+  E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.F);
+  E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, t0));
+  E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, t1));
+  E.v(t0, 4, fmt("v_lshlrev_b32_e32 v%d, 2, v%d", t0, t0));
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", t1));
+  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+  E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.E);
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", tY));
+  E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+  E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN));
+  E.cnd(4, fmt("v_cndmask_b32_e32 v4, v3, v%d, vcc", t0));
+  // DMA source offsets: word J = I0 + blk*bw + lane*lw of the window; input (yp - pad,
+  // xq - xoff) of image n, out of range in the padding and past the batch
+  if (p.pairdist) {
+    // wave w stages block w % nblk of channels w / nblk + i * (T / nblk): s31 = w / nblk
+    E.line("s_mul_i32 s31, s14, %d", (65536 + p.nblk - 1) / p.nblk);
+    E.line("s_lshr_b32 s31, s31, 16");
+    E.line("s_mul_i32 s30, s31, %d", p.nblk);
+    E.line("s_sub_u32 s30, s14, s30");                    // w % nblk
+    E.line("s_mul_i32 s32, s31, %d", p.chs * 4);
+    E.line("s_mul_i32 s17, s30, %d", p.bw * 4);
+    E.line("s_add_u32 s32, s32, s17");                    // LDS part of M0
+    E.line("s_mov_b32 s17, 0x%llx", HW4);
+    E.line("s_mul_i32 s33, s31, s17");                    // channel part of the scalar offset
+  }
+  E.line("s_mul_i32 s19, s15, %d", T * 64);                // I0
+  for (int k = 0; k < nvb; k++) {
+    if (p.pairdist)
+      E.line("s_mov_b32 s17, s30");
+    else
+      E.line("s_add_u32 s17, s14, %d", k * T);
+    E.line("s_mul_i32 s17, s17, %d", p.bw);
+    E.line("s_add_u32 s17, s17, s19");
+    E.v(t2, 4, fmt("v_lshlrev_b32_e32 v%d, %d, v1", t2, lw == 4 ? 2 : 0));
+    E.v(t2, 4, fmt("v_add_u32_e32 v%d, s17, v%d", t2, t2));
+    decompose(t2);
+    E.v(tY, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", tY, (uint32_t)(-g.pad), tY));   // iy
+    E.v(tX, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", tX, (uint32_t)(-g.xoff), tX));  // ix
+    E.line("s_mov_b32 s18, 0x%x", (uint32_t)((uint64_t)g.C * g.H));
+    E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tN));
+    E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tY));
+    E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.W);
+    E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, t0));
+    E.v(t0, 4, fmt("v_add_u32_e32 v%d, v%d, v%d", t0, t0, tX));
+    E.v(t0, 4, fmt("v_lshlrev_b32_e32 v%d, 2, v%d", t0, t0));
+    E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", tX));
+    E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+    E.line("s_mov_b32 s18, 0x%x", (uint32_t)g.H);
+    E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s18, v%d", tY));
+    E.cnd(t0, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", t0, t0));
+    E.cmp(fmt("v_cmp_gt_u32_e32 vcc, s24, v%d", tN));
+    E.cnd(vB + k, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", vB + k, t0));
+  }
+  // select the group's section
+  for (int k = 1; k < p.G; k++) {
+    E.line("s_cmp_eq_u32 s16, %d", k);
+    E.line("s_cbranch_scc0 .Lnot%d", k);
+    E.line("s_getpc_b64 s[34:35]");
+    E.label(".Lpc" + std::to_string(k));
+    E.line("s_add_u32 s34, s34, .Lsec%d-.Lpc%d", k, k);
+    E.line("s_addc_u32 s35, s35, 0");
+    E.line("s_setpc_b64 s[34:35]");
+    E.label(".Lnot" + std::to_string(k));
+  }
+
+  std::vector<int> slot_of(g.M, -1);
+  for (int q = 0; q < p.G; q++)
+    for (size_t i = 0; i < p.rows[q].size(); i++) slot_of[p.rows[q][i]] = (int)i;
+  auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, &val);
+  const char* dma = p.bw == 256 ? "buffer_load_dwordx4" : "buffer_load_dword";
+  long long fmas = 0;
+  int lbl = 0;
+  p.sec_valu = 0;
+  for (int gq = 0; gq < p.G; gq++) {
+    if (gq > 0) E.label(".Lsec" + std::to_string(gq));
+    const long long v0 = E.valu;
+    const std::vector<Nz>& L = nzs[gq];
+    const std::vector<Step> all = group_steps(g, p.dpp, L);
+    const int nrow = (int)p.rows[gq].size();
+    std::vector<char> touched(p.Mg, 0);
+    // chunks that hold steps, in order, with their steps
+    std::vector<int> chunks;
+    std::vector<std::vector<int>> csteps;
+    for (int t = 0; t < (int)all.size(); t++) {
+      const int k = all[t].c / p.Cc;
+      if (chunks.empty() || chunks.back() != k) {
+        chunks.push_back(k);
+        csteps.emplace_back();
+      }
+      csteps.back().push_back(t);
+    }
+    auto stage = [&](int k, int buf) {
+      const int c0 = k * p.Cc, cn = std::min(p.Cc, g.C - c0), boff = buf * BUF;
+      if (p.pairdist) {
+        const int per = T / p.nblk;
+        const int npw = (cn + per - 1) / per;
+        for (int i = 0; i < npw; i++) {
+          const bool guard = (i + 1) * per > cn;
+          const std::string skip = ".Ls" + std::to_string(lbl++);
+          if (guard) {
+            E.line("s_add_u32 s17, s31, %d", i * per);
+            E.line("s_cmp_lt_u32 s17, %d", cn);
+            E.line("s_cbranch_scc0 %s", skip.c_str());
+          }
+          E.line("s_add_u32 m0, s32, 0x%x", boff + i * per * p.chs * 4);
+          E.line("s_add_u32 s12, s33, 0x%llx", (long long)(c0 + i * per) * HW4);
+          E.line("s_nop 0");
+          E.line("%s v%d, s[4:7], s12 offen lds", dma, vB);
+          E.code += 28;
+          if (guard) E.label(skip);
+        }
+      } else {
+        for (int c = 0; c < cn; c++)
+          for (int k2 = 0; k2 < nvb; k2++) {
+            const bool guard = (k2 + 1) * T > p.nblk;
+            const std::string skip = ".Ls" + std::to_string(lbl++);
+            E.line("s_add_u32 s17, s14, %d", k2 * T);
+            if (guard) {
+              E.line("s_cmp_lt_u32 s17, %d", p.nblk);
+              E.line("s_cbranch_scc0 %s", skip.c_str());
+            }
+            E.line("s_mul_i32 s18, s17, %d", p.bw * 4);
+            E.line("s_add_u32 m0, s18, 0x%x", boff + c * p.chs * 4);
+            E.line("s_mov_b32 s12, 0x%llx", (long long)(c0 + c) * HW4);
+            E.line("s_nop 0");
+            E.line("%s v%d, s[4:7], s12 offen lds", dma, vB + k2);
+            E.code += 32;
+            if (guard) E.label(skip);
+          }
+      }
+    };
+    auto rd = [&](int set, int sidx) { return vRd + set * S + sidx; };
+    // the tap reads of step t into read set `set`; returns their count
+    auto reads = [&](int t, int set, int boff, int c0) {
+      const Step& st = all[t];
+      std::vector<char> used(S, 0);
+      for (int i : st.nz) used[L[i].sq] = 1;
+      int n = 0;
+      for (int sidx = 0; sidx < S; sidx++) {
+        if (!used[sidx]) continue;
+        const int off = boff + (st.c - c0) * p.chs * 4 + (st.r * g.Pp + sidx) * 4;
+        E.line("ds_read_b32 v%d, v5 offset:%d", rd(set, sidx), off);
+        E.code += 8;
+        n++;
+      }
+      return n;
+    };
+    // the DMA runs P = nbuf - 1 chunks ahead: chunk i goes to buffer i % nbuf, which chunk
+    // i - nbuf read before the barrier that precedes its staging
+    const int nch = (int)chunks.size(), P = p.nbuf - 1;
+    int issued = 0;
+    auto wait_for = [&](int k) {
+      // chunk k is in LDS once this wavefront's DMAs of chunk k are done (they retire in
+      // order, so at most the DMAs of the chunks issued after it may still be outstanding;
+      // the fewest any wavefront issues for them) and every wavefront has passed the barrier
+      int later = 0;
+      for (int j = k + 1; j < issued; j++) later += staged_dmas_min(g, p, chunks[j]);
+      E.line("s_waitcnt vmcnt(%d)", std::min(later, 63));
+      E.line("s_barrier");
+    };
+    for (; issued < std::min(P, nch); issued++) stage(chunks[issued], issued % p.nbuf);
+    if (nch > 0) wait_for(0);
+    for (int ci = 0; ci < nch; ci++) {
+      const int boff = (ci % p.nbuf) * BUF, c0 = chunks[ci] * p.Cc;
+      if (ci + P < nch) {
+        stage(chunks[ci + P], (ci + P) % p.nbuf);
+        issued++;
+      }
+      // step j's taps go to read set j % NS, issued ra steps ahead; before step j's FMAs
+      // only the reads of the steps after it may be outstanding
+      const std::vector<int>& ts = csteps[ci];
+      const int nts = (int)ts.size();
+      std::vector<int> nrd(nts, 0);
+      for (int j = 0; j < std::min(p.ra, nts); j++) nrd[j] = reads(ts[j], j % NS, boff, c0);
+      for (int j = 0; j < nts; j++) {
+        if (j + p.ra < nts) nrd[j + p.ra] = reads(ts[j + p.ra], (j + p.ra) % NS, boff, c0);
+        int later = 0;
+        for (int k = j + 1; k < std::min(nts, j + p.ra + 1); k++) later += nrd[k];
+        E.line("s_waitcnt lgkmcnt(%d)", later);
+        E.code += 4;
+        const Step& st = all[ts[j]];
+        for (int i : st.nz) {
+          const Nz& z = L[i];
+          const int a = vAcc + slot_of[z.m];
+          const int sr = rd(j % NS, z.sq);
+          if (!touched[slot_of[z.m]]) {
+            touched[slot_of[z.m]] = 1;
+            E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
+          } else {
+            E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
+          }
+          fmas++;
+        }
+      }
+      if (ci + 1 < nch) wait_for(ci + 1);
+    }
+    for (int k = 0; k < nrow; k++)
+      if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
+    for (int k = 0; k < nrow; k++) {
+      E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[gq][k] * EF4);
+      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
+      E.code += 16;
+    }
+    E.line("s_endpgm");
+    p.sec_valu = std::max(p.sec_valu, E.valu - v0);
+  }
+  E.code += 1024;
+  p.fmas = fmas;
+  p.code_bytes = E.code;
+  if (E.code > kCodeMax) {
+    *err = "baked kernel code too large";
+    return false;
+  }
+  finish_kernel(E, p, nv, T, src);
+  return true;
+}
+
 bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                    const std::vector<float>& val, BakePlan* plan, std::string* src, std::string* err) {
   BakePlan& p = *plan;
+  if (p.stage) return generate_staged(g, rowptr, col, val, p, src, err);
   const int P = row_vectors(g, p.dpp);
   const int RV = g.R * P;
   const int Q = p.Q, T = p.T, WPB = p.wpb();
@@ -819,63 +1346,7 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
     *err = "baked kernel code too large";
     return false;
   }
-  p.sgprs = 40;
-  char kd[2048];
-  snprintf(kd, sizeof kd,
-           "\t.section .rodata,\"a\",@progbits\n"
-           "\t.p2align 6, 0x0\n"
-           "\t.amdhsa_kernel sc_baked\n"
-           "\t\t.amdhsa_group_segment_fixed_size %d\n"
-           "\t\t.amdhsa_private_segment_fixed_size 0\n"
-           "\t\t.amdhsa_kernarg_size 40\n"
-           "\t\t.amdhsa_user_sgpr_count 2\n"
-           "\t\t.amdhsa_user_sgpr_kernarg_segment_ptr 1\n"
-           "\t\t.amdhsa_system_sgpr_workgroup_id_x 1\n"
-           "\t\t.amdhsa_system_vgpr_workitem_id 0\n"
-           "\t\t.amdhsa_next_free_vgpr %d\n"
-           "\t\t.amdhsa_next_free_sgpr %d\n"
-           "\t\t.amdhsa_accum_offset %d\n"
-           "\t\t.amdhsa_reserve_vcc 1\n"
-           "\t\t.amdhsa_float_denorm_mode_32 3\n"
-           "\t\t.amdhsa_float_denorm_mode_16_64 3\n"
-           "\t\t.amdhsa_dx10_clamp 1\n"
-           "\t\t.amdhsa_ieee_mode 1\n"
-           "\t.end_amdhsa_kernel\n"
-           "\t.text\n",
-           p.lds_bytes, nv, p.sgprs, nv);
-  E.s += kd;
-  char md[2048];
-  snprintf(md, sizeof md,
-           "\t.amdgpu_metadata\n"
-           "---\n"
-           "amdhsa.kernels:\n"
-           "  - .agpr_count: 0\n"
-           "    .args:\n"
-           "      - .address_space: global\n        .offset: 0\n        .size: 8\n        .value_kind: global_buffer\n"
-           "      - .address_space: global\n        .offset: 8\n        .size: 8\n        .value_kind: global_buffer\n"
-           "      - .offset: 16\n        .size: 4\n        .value_kind: by_value\n"
-           "      - .offset: 20\n        .size: 4\n        .value_kind: by_value\n"
-           "      - .offset: 24\n        .size: 4\n        .value_kind: by_value\n"
-           "      - .offset: 28\n        .size: 4\n        .value_kind: by_value\n"
-           "      - .offset: 32\n        .size: 4\n        .value_kind: by_value\n"
-           "      - .offset: 36\n        .size: 4\n        .value_kind: by_value\n"
-           "    .group_segment_fixed_size: %d\n"
-           "    .kernarg_segment_align: 8\n"
-           "    .kernarg_segment_size: 40\n"
-           "    .max_flat_workgroup_size: %d\n"
-           "    .name: sc_baked\n"
-           "    .private_segment_fixed_size: 0\n"
-           "    .sgpr_count: %d\n"
-           "    .symbol: sc_baked.kd\n"
-           "    .vgpr_count: %d\n"
-           "    .wavefront_size: 64\n"
-           "amdhsa.target: amdgcn-amd-amdhsa--gfx950\n"
-           "amdhsa.version:\n  - 1\n  - 2\n"
-           "...\n"
-           "\t.end_amdgpu_metadata\n",
-           p.lds_bytes, WPB * 64, p.sgprs + 6, nv);
-  E.s += md;
-  *src = std::move(E.s);
+  finish_kernel(E, p, nv, WPB, src);
   return true;
 }
 

@@ -51,6 +51,15 @@ struct BakePlan {
   int vgprs = 0, sgprs = 0;
   int lds_bytes = 0;         // partial sums of the channel splits
   int rc = 0;                // channels per round of the split reduction (LDS per split: rc/4 KB)
+  // staged plans (stride 1): the workgroup's T wavefronts cover T*64 consecutive positions of
+  // the padded layout (V = 64, pitch Pb = the layout's row pitch); per chunk of Cc channels each
+  // channel's window (chs words) is copied into LDS once by LDS DMA (bw words per instruction)
+  // into one of nbuf chunk buffers, nbuf - 1 chunks ahead of the FMAs, and every tap is a
+  // ds_read_b32 at an immediate offset
+  int stage = 0;
+  int Cc = 0, chs = 0, bw = 0, nblk = 0, nbuf = 2;
+  int ra = 1;                // steps whose tap reads are issued ahead of the FMAs
+  int pairdist = 0;          // 1: wave w stages block w % nblk of every (T / nblk)-th channel
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
   long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)
@@ -71,11 +80,13 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=.." (tuning and tests only); fields
-// left at -1 are chosen by the packer.
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=.." (tuning and
+// tests only); fields left at -1 are chosen by the packer.
 struct BakeForce {
-  int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1;
-  bool any() const { return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0; }
+  int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1;
+  bool any() const {
+    return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0;
+  }
 };
 BakeForce bake_force_from_env();
 

@@ -68,9 +68,12 @@ class Kernel:
 
 
 class Wave:
-    def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs, lds=None):
+    def __init__(self, kern: Kernel, kernarg: bytes, wg_id: int, wave_in_wg: int, bufs, lds=None, lds_pend=None):
         self.k = kern
         self.lds = lds  # the workgroup's LDS (uint32 words), shared by its waves
+        self.lds_pend = lds_pend  # per LDS word: an LDS DMA into it is not yet retired (vmcnt)
+        self.m0 = None
+        self.m0_wr = -100  # instruction count at the last write of m0
         self.lgkm = []  # per outstanding LDS instruction (oldest first): the VGPRs it writes
         self.s = np.zeros(110, np.uint64)  # scalar registers (kept as u32 values)
         self.v = np.zeros((256, 64), np.uint32)
@@ -103,7 +106,7 @@ class Wave:
         i = int(m.group(2))
         if i >= self.k.nvgpr:
             raise EmuError(f"v{i} beyond the declared {self.k.nvgpr} VGPRs")
-        if i in self.pending or any(i in regs for regs in self.lgkm):
+        if any(e == i for e in self.pending if not isinstance(e, tuple)) or any(i in regs for regs in self.lgkm):
             raise EmuError(f"v{i} {'written' if write else 'read'} while a load into it is outstanding")
         return i
 
@@ -164,6 +167,7 @@ class Wave:
         ins = self.k.instrs
         while True:
             steps += 1
+            self.steps = steps
             if steps > max_steps:
                 raise EmuError("too many steps")
             op, a = ins[pc]
@@ -185,7 +189,9 @@ class Wave:
                 keep = int(m.group(2))
                 q = self.pending if m.group(1) == "vmcnt" else self.lgkm
                 while len(q) > keep:
-                    q.pop(0)
+                    e = q.pop(0)
+                    if isinstance(e, tuple):  # an LDS DMA: its words are now written
+                        self.lds_pend[e[1]] = False
             elif op == "s_barrier":
                 if self.lgkm:
                     raise EmuError("s_barrier with LDS reads outstanding")
@@ -218,6 +224,27 @@ class Wave:
                     self.lgkm.append(regs)
                     if len(self.lgkm) > 15:
                         raise EmuError("too many LDS instructions outstanding")
+            elif op == "ds_read_b32":
+                if self.lds is None:
+                    raise EmuError("LDS access in a kernel without LDS")
+                srcp, _, mods = a[1].partition(" ")
+                off = 0
+                if mods:
+                    key, _, num = mods.partition(":")
+                    if key != "offset":
+                        raise EmuError(f"LDS modifier not emulated: {mods}")
+                    off = int(num)
+                addr = self.src_vec(srcp).astype(np.int64) + off
+                if (addr % 4).any() or (addr < 0).any() or (addr + 4 > self.lds.size * 4).any():
+                    raise EmuError("ds_read_b32 outside the LDS or misaligned")
+                w = addr // 4
+                if self.lds_pend is not None and self.lds_pend[w].any():
+                    raise EmuError("LDS read of words an LDS DMA has not finished writing")
+                dst = self.vreg(a[0], write=True)
+                self.v[dst] = self.lds[w]
+                self.lgkm.append([dst])
+                if len(self.lgkm) > 15:
+                    raise EmuError("too many LDS instructions outstanding")
             elif op == "ds_bpermute_b32":
                 # lane l receives data[((addr[l] + offset) >> 2) & 63] through the LDS crossbar
                 srcp, _, mods = a[2].partition(" ")
@@ -240,6 +267,10 @@ class Wave:
                 self.wv(a[0], (x + y).view(np.uint32))
             elif op == "s_nop":
                 self.valu += int(a[0]) + 1
+            elif op == "s_mov_b32" and a[0] == "m0":
+                self.m0, self.m0_wr = self.sval(a[1]), steps
+            elif op == "s_add_u32" and a[0] == "m0":
+                self.m0, self.m0_wr = (self.sval(a[1]) + self.sval(a[2])) & 0xFFFFFFFF, steps
             elif op == "s_mov_b32":
                 self.s[self.sreg(a[0])] = self.sval(a[1])
             elif op in ("s_and_b32", "s_mul_i32", "s_lshr_b32", "s_add_u32", "s_sub_u32"):
@@ -332,6 +363,43 @@ class Wave:
                 x = self.src_vec(a[2]).view(np.float32).astype(np.float64)
                 d = self.v[self.vreg(a[0])].view(np.float32).astype(np.float64)
                 self.wv(a[0], (k * x + d).astype(np.float32).view(np.uint32))
+            elif op in ("buffer_load_dword", "buffer_load_dwordx4") and len(a) == 3:
+                # LDS DMA: lane i writes its 1 (4) dwords at LDS byte m0 + 4*i (16*i); zero where
+                # the offset is out of range
+                so, _, mods = a[2].partition(" ")
+                if mods != "offen lds":
+                    raise EmuError(f"LDS DMA form not emulated: {mods}")
+                if self.lds is None:
+                    raise EmuError("LDS DMA in a kernel without LDS")
+                if self.m0 is None or steps - self.m0_wr < 2:
+                    raise EmuError("LDS DMA without a wait state after writing m0")
+                lw = 4 if op == "buffer_load_dwordx4" else 1
+                addr, nrec = self.rsrc(a[1])
+                bi, arr = self.buffer(addr)
+                voff = self.src_vec(a[0]).astype(np.uint64)
+                soff = self.sval(so)
+                off = voff + np.uint64(soff)
+                inb = off < np.uint64(nrec)
+                if ((voff < np.uint64(nrec)) != inb).any():
+                    raise EmuError("range check would depend on the scalar offset")
+                if (off[inb] % (4 * lw)).any():
+                    raise EmuError("misaligned LDS DMA source")
+                base = int(self.m0)
+                if base % 4 or base < 0 or base + 64 * 4 * lw > self.lds.size * 4:
+                    raise EmuError("LDS DMA outside the LDS")
+                words = np.zeros(64 * lw, np.uint32)
+                src_idx = (off[inb] // 4).astype(np.int64)
+                if (src_idx + lw > arr.size).any():
+                    raise EmuError("descriptor range larger than the buffer")
+                lanes = np.nonzero(inb)[0]
+                for j in range(lw):
+                    words[lanes * lw + j] = arr[src_idx + j]
+                dst = base // 4 + np.arange(64 * lw)
+                self.lds[dst] = words
+                self.lds_pend[dst] = True
+                self.pending.append(("lds", dst))
+                if len(self.pending) > 63:
+                    raise EmuError("more than 63 loads outstanding")
             elif op == "buffer_load_dword" or op == "buffer_store_dword":
                 so, _, mods = a[3].partition(" ")
                 if mods != "offen":
@@ -376,11 +444,18 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
     V, Pb, G = info["bake_valid_lanes"], info["bake_pitch"], info["bake_groups"]
     Q, T = info["bake_splits"], info["bake_units_per_wg"]
     WPB = Q * T
-    qtot = N * E * Pb
-    ntiles = (qtot + V - 1) // V
-    units = ntiles * G
-    wgs = (units + T - 1) // T
-    per_xcd = (wgs + 7) // 8
+    if info.get("bake_stage"):
+        # staged kernels: positions of the padded layout (H + 2 pad rows of Pb words per image),
+        # ntiles = workgroups of T tiles of 64 per group
+        qtot = N * (info["H"] + 2 * info["pad"]) * Pb
+        ntiles = (qtot + 64 * T - 1) // (64 * T)
+        per_xcd = (ntiles * G + 7) // 8
+    else:
+        qtot = N * E * Pb
+        ntiles = (qtot + V - 1) // V
+        units = ntiles * G
+        wgs = (units + T - 1) // T
+        per_xcd = (wgs + 7) // 8
     xb = np.ascontiguousarray(x, np.float32).reshape(-1).view(np.uint32)
     y = np.full(N * M * E * F, 0x7FC00000, np.uint32)  # NaN: unwritten
     xaddr, yaddr = 0x10000000, 0x7F0000000
@@ -388,7 +463,8 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
     written = np.zeros(y.size, np.int32)
     for b in range(8 * per_xcd):
         lds = np.full(max(k.lds_bytes, 4) // 4, 0x7FC00000, np.uint32) if k.lds_bytes else None
-        waves = [Wave(k, kernarg, b, w, [(xaddr, xb), (yaddr, y)], lds) for w in range(WPB)]
+        pend = np.zeros(lds.size, bool) if lds is not None else None
+        waves = [Wave(k, kernarg, b, w, [(xaddr, xb), (yaddr, y)], lds, pend) for w in range(WPB)]
         # run every wave up to its next barrier (or its end), then release the barrier; a
         # barrier waits only for the waves that have not ended
         gens = [w.run() for w in waves]

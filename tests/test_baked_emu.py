@@ -162,3 +162,98 @@ def test_channel_split_reduction_in_rounds(env, monkeypatch):
     assert Q > 2 and info["bake_lds_bytes"] == T * (Q - 1) * 8 * 1024
     y2, _, _ = _emulate(d, 1, 1)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+STAGED_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
+    (2, 20, 13, 16, 9, 3, 3, 1, 1, 0.3, 41),   # wide layout (16-byte DMA), 3 chunks, the last partial
+    (3, 19, 9, 12, 30, 3, 3, 1, 1, 0.4, 42),   # wide, several images per workgroup
+    (2, 5, 13, 11, 9, 3, 3, 1, 1, 0.3, 43),    # narrow layout (4-byte DMA), one partial chunk
+    (1, 9, 6, 70, 9, 3, 7, 1, 3, 0.5, 44),     # pad 3: narrow, 7 taps per step
+    (2, 11, 8, 8, 7, 5, 5, 1, 2, 0.4, 45),     # 5x5, pad 2, wide
+    (2, 17, 9, 9, 6, 1, 1, 1, 0, 0.5, 46),     # 1x1
+    (2, 7, 17, 19, 13, 3, 3, 1, 1, 0.0, 47),   # no non-zero at all: +0 everywhere
+]
+STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2"]
+
+
+@pytest.mark.parametrize("env", STAGED_ENVS)
+@pytest.mark.parametrize("c", STAGED_CASES, ids=lambda c: "N{}C{}H{}W{}M{}R{}S{}p{}k{}".format(*c[:7], c[8], c[9]))
+def test_staged_kernels(c, env, monkeypatch):
+    """Staged kernels: per chunk of channels every wavefront of a workgroup copies part of the
+    workgroup's input window into LDS (LDS DMA, double-buffered, a barrier per chunk) and reads
+    its taps from there.  The emulator checks that no LDS word is read before the DMA that
+    writes it has been waited for, and the wait state after writing m0.  The FMAs are the same
+    as the default plan's in the same order, so the outputs equal its outputs bit for bit.
+    Options: T wavefronts per workgroup, G groups, NB chunk buffers (the DMA runs NB - 1
+    chunks ahead), CC channels per chunk, RA steps of tap reads in flight."""
+    d = workloads.make_custom(*c)
+    y, info = _check(d, c[7], c[8], env, env, monkeypatch)
+    assert info["bake_stage"] == 1 and info["bake_valid_lanes"] == 64
+    T = info["bake_units_per_wg"]
+    assert info["bake_lds_bytes"] >= 2 * info["bake_chunk_channels"] * (64 * T) * 4
+    monkeypatch.delenv("SPARSECONV_BAKE")
+    y0, _, info0 = _emulate(d, c[7], c[8])
+    assert info0["bake_stage"] == 0
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
+    if c[9] == 0.0:
+        assert np.all(y == 0) and not np.signbit(y).any()
+
+
+def _m0_next_to_dma(lines):
+    """The kernel with each m0 write moved to just before its DMA (no wait state between)."""
+    out, held = [], None
+    for ln in lines:
+        t = ln.strip()
+        if t.startswith("s_add_u32 m0"):
+            held = ln
+        elif t == "s_nop 0" and held is not None:
+            continue
+        elif t.startswith("buffer_load") and t.endswith(" lds") and held is not None:
+            out += [held, ln]
+            held = None
+        else:
+            out.append(ln)
+    return out
+
+
+def _loosen_vmcnt(lines):
+    """The kernel with every vmcnt wait one DMA looser."""
+    out = []
+    for ln in lines:
+        t = ln.strip()
+        if t.startswith("s_waitcnt vmcnt("):
+            n = int(t[len("s_waitcnt vmcnt("):-1])
+            ln = ln.replace(t, f"s_waitcnt vmcnt({n + 1})")
+        out.append(ln)
+    return out
+
+
+@pytest.mark.parametrize("drop", ["m0 wait state", "s_waitcnt vmcnt", "vmcnt + 1", "s_barrier"])
+def test_staged_synchronisation_is_checked(drop, monkeypatch):
+    """The emulator rejects a staged kernel with its synchronisation taken out: with no wait
+    state between the m0 write and the DMA that reads m0, without the vmcnt waits before the
+    barriers or with each of them one DMA too loose (a wavefront would read words another
+    wavefront's DMA has not finished writing), or without the barriers (a wavefront reads
+    words nobody has staged yet, or overwrites a buffer others still read)."""
+    d = workloads.make_custom(*STAGED_CASES[0])
+    c = STAGED_CASES[0]
+    monkeypatch.setenv("SPARSECONV_BAKE", "STAGE=1")
+    x, w, mask = d["x"], d["w"], d["mask"]
+    M, C, R, S = w.shape
+    h = sc.Handle(M, C, R, S, x.shape[2], x.shape[3], c[7], c[8], values=w, mask=mask,
+                  flags=sc.SC_PACK_HOST_ONLY)
+    src = h.kernel_source()
+    lines = src.split("\n")
+    if drop == "m0 wait state":
+        bad = "\n".join(_m0_next_to_dma(lines))
+    elif drop == "vmcnt + 1":
+        bad = "\n".join(_loosen_vmcnt(lines))
+    else:
+        bad = "\n".join(ln for ln in lines if not ln.strip().startswith(drop))
+    assert bad != src
+    r = oracle.reference(x, w, mask, c[7], c[8])
+    try:
+        y, _ = gcn_emu.run_baked(bad, h.info(), x, M, h.E, h.F)
+    except gcn_emu.EmuError:
+        return
+    assert not oracle.within_tolerance(y, r["y64"], r["mag"], 1e-5).all()

@@ -14,7 +14,7 @@ import torch
 import oracle
 import sparse_weight_direct_amd as sc
 import workloads
-from gpu_util import assert_parity, gpu_sparse
+from gpu_util import assert_layer_parity, assert_parity, gpu_sparse
 
 pytestmark = pytest.mark.gpu
 
@@ -55,16 +55,17 @@ def test_channel_splits(env, monkeypatch):
 
 def test_batch_size_picks_among_the_handles_kernels():
     """One handle, several batch sizes: the forward launches the kernel its estimate picks
-    for N (the base kernel once every SIMD has a wavefront), and every launch matches the
-    oracle."""
+    for N (the staged kernel once it gives every SIMD a wavefront), and every launch matches
+    the oracle."""
     d = workloads.make("imb95")
     L = d["layer"]
     h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
     assert h.info()["bake_variants"] >= 2
     big = h.launch_info(L.N)
-    assert big["mapping"] == sc.MAPPING_BAKED and big["variant"] == 0
+    assert big["mapping"] == sc.MAPPING_BAKED and big["variant"] == h.info()["bake_variants"] - 1
+    assert big["waves"] >= 4 * torch.cuda.get_device_properties(0).multi_processor_count
     seen = set()
-    for n in (1, 2, 5):
+    for n in (1, 2, 5, 8):
         li = h.launch_info(n)
         seen.add(li["variant"])
         x = d["x"][:n]
@@ -174,3 +175,36 @@ def test_tune_on_an_escoin_handle_chooses_its_only_kernel():
                   flags=sc.SC_PACK_ESCOIN_MAP)
     x = torch.from_numpy(d["x"]).cuda()
     assert h.tune(x) == 0
+
+
+WIDE_LAYER = (3, 21, 23, 36, 50, 3, 3, 1, 1, 0.15, 78)  # W % 4 == 0: 16-byte DMA
+
+
+@pytest.mark.parametrize("layer", [LAYER, WIDE_LAYER], ids=["narrow", "wide"])
+@pytest.mark.parametrize("env", ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "STAGE=1,G=50,T=4",
+                                 "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2"])
+def test_staged_plans(layer, env, monkeypatch):
+    """Staged kernels (input windows copied into LDS by LDS DMA per chunk of channels, taps read
+    from LDS): the same FMAs in the same order as the default plan, so the outputs agree with it
+    bit for bit, and with the oracle."""
+    d = workloads.make_custom(*layer)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
+    monkeypatch.setenv("SPARSECONV_BAKE", "G=1,Q=1,T=4")
+    base, _ = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    monkeypatch.setenv("SPARSECONV_BAKE", env)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    info = h.info()
+    assert info["bake_stage"] == 1 and info["bake_lds_bytes"] > 0
+    assert_parity(y, r["y64"], r["mag"], env)
+    np.testing.assert_array_equal(y.view(np.uint32), base.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["imb95", "imb99", "late", "pw1x1"])
+def test_staged_full_size(name, monkeypatch):
+    """A staged kernel on the full-size layers, every output against the oracle."""
+    d = workloads.make(name)
+    L = d["layer"]
+    monkeypatch.setenv("SPARSECONV_BAKE", "STAGE=1")
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert h.info()["bake_stage"] == 1 and h.launch_info(L.N)["mapping"] == sc.MAPPING_BAKED
+    assert_layer_parity(name, y, f"{name} staged")
