@@ -179,6 +179,8 @@ typedef struct {
                                into registers */
   int32_t bake_chunk_channels;
   int32_t bake_buffers;
+  int32_t bake_sequential;  /* 1: each workgroup runs every group in turn (the stores of one
+                               group overlap the next group's work); 0: one group per workgroup */
   int64_t bake_code_bytes;  /* bytes of generated code of the base kernel */
 } sc_info;
 

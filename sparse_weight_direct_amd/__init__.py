@@ -66,7 +66,7 @@ class sc_info(ctypes.Structure):
                                                "bake_groups", "bake_splits", "bake_units_per_wg",
                                                "bake_valid_lanes", "bake_pitch", "bake_depth", "bake_vgprs",
                                                "bake_lds_bytes", "bake_variants", "bake_stage",
-                                               "bake_chunk_channels", "bake_buffers")] + \
+                                               "bake_chunk_channels", "bake_buffers", "bake_sequential")] + \
                [("bake_code_bytes", ctypes.c_int64)]
 
     def as_dict(self):
@@ -145,10 +145,20 @@ def _dev_ptr(t):
     return t.data_ptr()
 
 
-def _stream_ptr(stream):
+_raw_stream = None  # torch's accessor of the current stream's raw handle (by device index)
+
+
+def _stream_ptr(stream, device=None):
+    """The HIP stream handle for ``stream``: a torch stream, a raw handle, or None for the
+    current stream of ``device`` (a device index; the current device when None)."""
+    global _raw_stream
     if stream is None:
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is None:
+            _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+        if _raw_stream:
+            return _raw_stream(torch.cuda.current_device() if device is None else device)
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -305,6 +315,9 @@ class Handle:
                                    colidx=colidx, rowptr=rowptr, flags=flags)
         info = sparseconv_query(self.ptr)  # output extent as the library computes it
         self.E, self.F = info["E"], info["F"]
+        # what forward compares and passes on every call
+        self._chw, self._mef = (C, H, W), (M, self.E, self.F)
+        self._dims = (C, H, W, M, R, S, stride, pad)
 
     @classmethod
     def from_dense(cls, w: np.ndarray, H: int, W: int, stride: int, pad: int, mask=None, flags=0):
@@ -338,19 +351,21 @@ class Handle:
         used; handles packed with SC_PACK_ESCOIN_MAP need one."""
         import torch
         g = self.geom
-        if x.dim() != 4 or tuple(x.shape[1:]) != (g["C"], g["H"], g["W"]):
-            raise ValueError(f"input shape {tuple(x.shape)} is not (N, {g['C']}, {g['H']}, {g['W']})")
-        N = x.shape[0]
+        shp = x.shape
+        if len(shp) != 4 or shp[1:] != self._chw:
+            raise ValueError(f"input shape {tuple(shp)} is not (N, {g['C']}, {g['H']}, {g['W']})")
+        N = shp[0]
         if out is None:
-            out = torch.empty((N, g["M"], self.E, self.F), dtype=torch.float32, device=x.device)
-        elif tuple(out.shape) != (N, g["M"], self.E, self.F):
+            out = torch.empty((N,) + self._mef, dtype=torch.float32, device=x.device)
+        elif out.shape[1:] != self._mef or out.shape[0] != N:
             raise ValueError(f"output shape {tuple(out.shape)} is not ({N}, {g['M']}, {self.E}, {self.F})")
         for name, t in (("input", x), ("output", out)):
-            if t.dtype != torch.float32 or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous float32 tensor")
+            if t.dtype is not torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor on the GPU")
         if workspace is None:
-            sparseconv_forward(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
-                               g["stride"], g["pad"], stream)
+            # arguments checked above: straight to the library
+            _check(_lib.sparseconv_forward(self.ptr, x.data_ptr(), out.data_ptr(), N, *self._dims,
+                                           _stream_ptr(stream, x.get_device())), "sparseconv_forward")
         else:
             sparseconv_forward_workspace(self.ptr, x, out, N, g["C"], g["H"], g["W"], g["M"], g["R"], g["S"],
                                          g["stride"], g["pad"], workspace,

@@ -633,6 +633,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
     info->bake_stage = b.stage;
     info->bake_chunk_channels = b.Cc;
     info->bake_buffers = b.stage ? b.nbuf : 0;
+    info->bake_sequential = b.seq;
     info->bake_code_bytes = b.code_bytes;
   }
   if (h->escoin) {
@@ -858,7 +859,7 @@ sc::BakeArgs baked_args(const sc_handle* h, const sc::BakePlan& bp, int N) {
     const long long qtot = (long long)N * g.HYp * g.Pp;
     a.qtot = (uint32_t)qtot;
     a.ntiles = (uint32_t)((qtot + 64LL * bp.T - 1) / (64LL * bp.T));
-    a.per_xcd = (uint32_t)(((long long)a.ntiles * bp.G + 7) / 8);
+    a.per_xcd = (uint32_t)(((long long)a.ntiles * (bp.seq ? 1 : bp.G) + 7) / 8);
     return a;
   }
   const long long qtot = (long long)N * g.E * bp.Pb;
@@ -873,7 +874,7 @@ sc::BakeArgs baked_args(const sc_handle* h, const sc::BakePlan& bp, int N) {
 // Wavefronts a weights-in-code kernel runs for N images.
 long long baked_waves(const sc_handle* h, const sc::BakePlan& bp, int N) {
   const sc::BakeArgs a = baked_args(h, bp, N);
-  return bp.stage ? (long long)a.ntiles * bp.T * bp.G : (long long)a.ntiles * bp.G * bp.Q;
+  return bp.stage ? (long long)a.ntiles * bp.T * (bp.seq ? 1 : bp.G) : (long long)a.ntiles * bp.G * bp.Q;
 }
 
 // Bytes of the padded input the "Escoin" mapping writes for N images (0 for other handles).

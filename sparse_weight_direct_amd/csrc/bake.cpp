@@ -56,6 +56,8 @@ BakeForce bake_force_from_env() {
   f.nb = env_key(e, "NB", -1);
   f.cc = env_key(e, "CC", -1);
   f.ra = env_key(e, "RA", -1);
+  f.cb = env_key(e, "CB", -1);
+  f.seq = env_key(e, "SEQ", -1);
   return f;
 }
 
@@ -204,7 +206,8 @@ std::vector<int> split_steps(const std::vector<Step>& steps, int Q, long long ex
 }
 
 // VALU cost of split 0's additions of the other splits' partial sums.
-inline long long reduce_cost(const BakePlan& p) { return p.Q > 1 ? (long long)(p.Q - 1) * p.Mg : 0; }
+// Extra cost of split 0 over the others (none: every split reduces and stores its share).
+inline long long reduce_cost(const BakePlan&) { return 0; }
 
 // Fill the plan's derived fields (registers, LDS, section sizes) for given G, Q, T, D.
 bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col, BakePlan* pp,
@@ -239,10 +242,18 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   }
   p.D = D;
   p.vgprs = plan_vgprs(g, p, p.Mg, D);
-  p.rc = std::min(p.Mg, kReduceChannels);
-  p.lds_bytes = p.Q > 1 ? p.T * (p.Q - 1) * (p.rc / 4) * 1024 : 0;
+  // rounds of rc channels: every split's part of a round (rc/4 KB) for all Q splits within the
+  // 16-bit LDS offsets of one unit's region
+  p.rc = std::min({p.Mg, kReduceChannels, std::max(4, (256 / p.Q) & ~3)});
+  p.lds_bytes = p.Q > 1 ? p.T * p.Q * (p.rc / 4) * 1024 : 0;
   if (p.lds_bytes > 160 * 1024) {
     *why = "channel-split partial sums exceed the LDS";
+    return false;
+  }
+  if (p.Q > 1 && std::min(16, (g.R * P + (D + 1) * P + shift_regs(g, p) - 2) / 4) < p.Q - 1) {
+    // a split reads the other Q - 1 parts of a block into registers of the offset, ring and
+    // shift region
+    *why = "channel splits need 4 (Q - 1) free registers for the reduction";
     return false;
   }
   // section sizes
@@ -262,7 +273,7 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
         ld += steps[i].loads();
         code += 8 * (long long)steps[i].nz.size() + 8 * steps[i].shifts() + 8 * steps[i].loads() + 8;
       }
-      v += p.Q > 1 ? (q == 0 ? (p.Q - 1) * p.Mg + p.Mg : p.Mg / 4) : p.Mg / 4;
+      v += p.Q > 1 ? (p.Q - 1) * p.Mg / p.Q + p.Mg / 4 : p.Mg / 4;
       p.sec_valu = std::max(p.sec_valu, v);
       p.sec_steps = std::max(p.sec_steps, st);
       p.sec_loads = std::max(p.sec_loads, ld);
@@ -274,23 +285,46 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
 
 // Staged plans: registers of the fixed part, the DMA source offsets and the two sets of tap
 // reads, then the accumulators.
-// Steps of tap reads a staged kernel issues ahead: at most 15 LDS reads may be outstanding
-// (the lgkm counter), and the read sets of the steps in flight and the current step hold
-// (ra + 1) * S registers.
-inline int staged_read_ahead(const Geom& g, int forced) {
-  const int cap = std::max(1, 15 / g.S - 1);
+// Batches of tap reads a staged kernel issues ahead (a batch is a step, or with channel
+// batches a channel's steps): at most 15 LDS instructions may be outstanding (the lgkm
+// counter), the current batch's and the ra batches ahead.
+inline int staged_batch_reads(const Geom& g, int cb) { return cb ? (g.R * g.S + 1) / 2 : g.S; }
+inline int staged_read_ahead(const Geom& g, int forced, int cb) {
+  const int cap = std::max(1, 15 / staged_batch_reads(g, cb) - 1);
   return std::min(cap, forced > 0 ? forced : 1);  // more measured no faster
 }
 
-inline int staged_vgprs(const Geom& g, int nvb, int Mg, int ra) {
-  const int acc0 = (kFixedV + nvb + (ra + 1) * g.S + 1) & ~1;
+// Channel batches need every tap of a channel within reach of one base register's 8-bit
+// dword offsets (ds_read2_b32), and two batches of reads within the lgkm counter.
+inline bool staged_cb_ok(const Geom& g) {
+  return (g.R - 1) * g.Pp + g.S - 1 <= 255 && 2 * staged_batch_reads(g, 1) <= 15;
+}
+
+// VGPR layout of a staged kernel: v0..v5 fixed, the DMA source offsets, the read sets
+// (even-aligned pairs with channel batches), one base register per set (channel batches),
+// then the accumulators.
+struct StagedRegs {
+  int setw, rd, base, acc;
+};
+inline StagedRegs staged_regs(const Geom& g, int nvb, int ra, int cb) {
+  StagedRegs r;
+  const int NS = ra + 1;
+  r.setw = cb ? (g.R * g.S + 1) & ~1 : g.S;
+  r.rd = cb ? (kFixedV + nvb + 1) & ~1 : kFixedV + nvb;
+  r.base = r.rd + NS * r.setw;
+  r.acc = (r.base + (cb ? NS : 0) + 1) & ~1;
+  return r;
+}
+
+inline int staged_vgprs(const Geom& g, int nvb, int Mg, int ra, int cb) {
+  const int acc0 = staged_regs(g, nvb, ra, cb).acc;
   return (std::max(acc0 + Mg, acc0 + kTemps) + 3) & ~3;
 }
 
 // Fill a staged plan's derived fields for its G, T and (if > 0) forced buffer count and chunk
 // channels (stride 1, no channel splits).
 bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
-                     int nb, int cc, int ra, BakePlan* pp, std::string* why) {
+                     int nb, int cc, int ra, int cb, BakePlan* pp, std::string* why) {
   BakePlan& p = *pp;
   if (g.st != 1) {
     *why = "staged plans need stride 1";
@@ -304,7 +338,8 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   p.dpp = 1;  // a tap's column s is its lane shift sq: here an LDS offset
   p.perm = 0;
   p.maxsq = g.S - 1;
-  p.ra = staged_read_ahead(g, ra);
+  p.cb = cb >= 0 ? (cb > 0 && staged_cb_ok(g)) : staged_cb_ok(g);
+  p.ra = staged_read_ahead(g, ra, p.cb);
   p.V = 64;
   p.Pb = g.Pp;
   p.bw = g.wide ? 256 : 64;  // 16 bytes per lane in the wide layout, else 4
@@ -339,7 +374,7 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   for (auto& r : p.rows) mg = std::max(mg, (int)r.size());
   p.Mg = mg;
   p.D = 0;
-  p.vgprs = staged_vgprs(g, nvb, p.Mg, p.ra);
+  p.vgprs = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb);
   if (p.vgprs > kMaxVgpr) {
     *why = "output channels per group exceed the registers";
     return false;
@@ -429,25 +464,27 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
               {std::min(M, 4 * G0), 1, 4}, {std::min(M, 2 * G0), 2, 1}};
   }
   // staged plan: forced (STAGE=1), or appended to the candidates for stride-1 layers
-  auto add_staged = [&](int G, int T) {
+  auto add_staged = [&](int G, int T, int seq) {
     BakePlan c = p;
     c.stage = 1;
     c.G = G;
     c.T = T;
+    c.seq = G > 1 ? seq : 0;
     std::string w;
-    if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, &c, &w))
+    if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, f.cb, &c, &w))
       out.push_back(std::move(c));
     else if (out.empty())
       *why = w;
   };
   auto staged_groups = [&](int nvb) {
     int n = 1;
-    while (n < M && staged_vgprs(g, nvb, (M + n - 1) / n, staged_read_ahead(g, f.ra)) > kVgprTarget) n++;
+    const int cb = f.cb >= 0 ? (f.cb > 0 && staged_cb_ok(g)) : staged_cb_ok(g);
+    while (n < M && staged_vgprs(g, nvb, (M + n - 1) / n, staged_read_ahead(g, f.ra, cb), cb) > kVgprTarget) n++;
     return n;
   };
-  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0) {
+  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0) {
     const int T = f.T > 0 ? f.T : 4;
-    add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T);
+    add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T, f.seq > 0 ? 1 : 0);
     return out;
   }
   for (const Shape& sh : shapes) {
@@ -472,14 +509,14 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     else if (out.empty())
       *why = w;
   }
-  if (!f.any() && g.st == 1) add_staged(staged_groups(2), 4);
+  if (!f.any() && g.st == 1) add_staged(staged_groups(2), 4, 0);
   return out;
 }
 
 double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus) {
   const long long qtot = p.stage ? (long long)N * g.HYp * g.Pp : (long long)N * g.E * p.Pb;
   const long long ntiles = p.stage ? (qtot + 64LL * p.T - 1) / (64LL * p.T) * p.T : (qtot + p.V - 1) / p.V;
-  const long long waves = ntiles * p.G * p.Q;
+  const long long waves = ntiles * (p.seq ? 1 : p.G) * p.Q;
   const double simds = 4.0 * cus;
   // VALU: a SIMD runs about ceil(waves / SIMDs) sections' instructions one after the other
   const double valu = std::ceil((double)waves / simds) * (double)p.sec_valu * 4.0;
@@ -657,11 +694,11 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   const int nvb = p.pairdist ? 1 : (p.nblk + T - 1) / T;
   const int lw = p.bw / 64;  // DMA words per lane
   const int vB = kFixedV;              // DMA source offsets
-  const int NS = p.ra + 1;             // read sets: the current step's and ra steps ahead
-  const int vRd = vB + nvb;            // NS sets of S tap reads
-  const int vAcc = (vRd + NS * S + 1) & ~1;
+  const int NS = p.ra + 1;             // read sets: the current batch's and ra batches ahead
+  const StagedRegs sr = staged_regs(g, nvb, p.ra, p.cb);
+  const int SETW = sr.setw, vRd = sr.rd, vBase = sr.base, vAcc = sr.acc;
   const int vTmp = vAcc;               // prologue temporaries overlap the accumulators
-  const int nv = staged_vgprs(g, nvb, p.Mg, p.ra);
+  const int nv = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb);
   if (nv > kMaxVgpr || vAcc + p.Mg > nv) {
     *err = "staged kernel needs more than 256 VGPRs";
     return false;
@@ -692,7 +729,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   E.line("s_lshr_b32 s16, s2, 3");
   E.line("s_add_u32 s15, s15, s16");
   E.line("s_mov_b32 s16, 0");
-  for (int q = 0; q < p.G; q++) {
+  // sections: one per group, or one that runs every group in turn (sequential groups)
+  const int nsec = p.seq ? 1 : p.G;
+  for (int q = 0; q < nsec; q++) {
     E.line("s_cmp_lt_u32 s15, s25");
     E.line("s_cbranch_scc1 .Lunit");
     E.line("s_sub_u32 s15, s15, s25");
@@ -803,7 +842,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     E.cnd(vB + k, fmt("v_cndmask_b32_e32 v%d, v3, v%d, vcc", vB + k, t0));
   }
   // select the group's section
-  for (int k = 1; k < p.G; k++) {
+  for (int k = 1; k < nsec; k++) {
     E.line("s_cmp_eq_u32 s16, %d", k);
     E.line("s_cbranch_scc0 .Lnot%d", k);
     E.line("s_getpc_b64 s[34:35]");
@@ -822,24 +861,41 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   long long fmas = 0;
   int lbl = 0;
   p.sec_valu = 0;
-  for (int gq = 0; gq < p.G; gq++) {
-    if (gq > 0) E.label(".Lsec" + std::to_string(gq));
-    const long long v0 = E.valu;
-    const std::vector<Nz>& L = nzs[gq];
-    const std::vector<Step> all = group_steps(g, p.dpp, L);
-    const int nrow = (int)p.rows[gq].size();
-    std::vector<char> touched(p.Mg, 0);
-    // chunks that hold steps, in order, with their steps
-    std::vector<int> chunks;
-    std::vector<std::vector<int>> csteps;
-    for (int t = 0; t < (int)all.size(); t++) {
-      const int k = all[t].c / p.Cc;
-      if (chunks.empty() || chunks.back() != k) {
-        chunks.push_back(k);
-        csteps.emplace_back();
-      }
-      csteps.back().push_back(t);
+  // the outputs of group q: +0 for accumulators no FMA touched, one store per output channel
+  // (the accumulators are free again once the stores have read them)
+  auto store_group = [&](int q, std::vector<char>& touched) {
+    const int nrow = (int)p.rows[q].size();
+    for (int k = 0; k < nrow; k++)
+      if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
+    for (int k = 0; k < nrow; k++) {
+      E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[q][k] * EF4);
+      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
+      E.code += 16;
     }
+    std::fill(touched.begin(), touched.end(), 0);
+  };
+  for (int sec = 0; sec < nsec; sec++) {
+    if (sec > 0) E.label(".Lsec" + std::to_string(sec));
+    const long long v0 = E.valu;
+    // the section's groups, in order, and its units of work: (group, chunk that holds steps
+    // of that group, those steps); the DMA pipeline runs over the units, across groups
+    std::vector<int> gl;
+    for (int q = 0; q < p.G; q++)
+      if (p.seq || q == sec) gl.push_back(q);
+    std::vector<std::vector<Step>> alls;
+    for (int q : gl) alls.push_back(group_steps(g, p.dpp, nzs[q]));
+    struct Unit {
+      int gi, k;
+      std::vector<int> ts;
+    };
+    std::vector<Unit> units;
+    for (int gi = 0; gi < (int)gl.size(); gi++)
+      for (int t = 0; t < (int)alls[gi].size(); t++) {
+        const int k = alls[gi][t].c / p.Cc;
+        if (units.empty() || units.back().gi != gi || units.back().k != k) units.push_back({gi, k, {}});
+        units.back().ts.push_back(t);
+      }
+    std::vector<char> touched(p.Mg, 0);
     auto stage = [&](int k, int buf) {
       const int c0 = k * p.Cc, cn = std::min(p.Cc, g.C - c0), boff = buf * BUF;
       if (p.pairdist) {
@@ -854,8 +910,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
             E.line("s_cbranch_scc0 %s", skip.c_str());
           }
           E.line("s_add_u32 m0, s32, 0x%x", boff + i * per * p.chs * 4);
-          E.line("s_add_u32 s12, s33, 0x%llx", (long long)(c0 + i * per) * HW4);
-          E.line("s_nop 0");
+          E.line("s_add_u32 s12, s33, 0x%llx", (long long)(c0 + i * per) * HW4);  // m0's wait state
           E.line("%s v%d, s[4:7], s12 offen lds", dma, vB);
           E.code += 28;
           if (guard) E.label(skip);
@@ -872,25 +927,57 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
             }
             E.line("s_mul_i32 s18, s17, %d", p.bw * 4);
             E.line("s_add_u32 m0, s18, 0x%x", boff + c * p.chs * 4);
-            E.line("s_mov_b32 s12, 0x%llx", (long long)(c0 + c) * HW4);
-            E.line("s_nop 0");
+            E.line("s_mov_b32 s12, 0x%llx", (long long)(c0 + c) * HW4);  // m0's wait state
             E.line("%s v%d, s[4:7], s12 offen lds", dma, vB + k2);
             E.code += 32;
             if (guard) E.label(skip);
           }
       }
     };
-    auto rd = [&](int set, int sidx) { return vRd + set * S + sidx; };
-    // the tap reads of step t into read set `set`; returns their count
-    auto reads = [&](int t, int set, int boff, int c0) {
-      const Step& st = all[t];
+    // tap reads go out in batches, ra batches ahead of the FMAs, into read sets of SETW
+    // registers: a batch is one step (reads from the lane's base v5 at full offsets, tap
+    // column s in register s of the set), or with channel batches all steps of one channel
+    // (a base register per set points at the channel's window, and pairs of taps come in
+    // one ds_read2_b32, into consecutive registers in the order of the channel's taps)
+    struct Batch {
+      std::vector<int> steps;   // indices into all
+      std::vector<int> taps;    // channel batches: used taps r*S + s, in order
+      std::vector<int> reg_of;  // channel batches: register slot of tap r*S + s (-1 unused)
+    };
+    auto tapreg = [&](const Batch& bt, int set, int r, int sq) {
+      return p.cb ? vRd + set * SETW + bt.reg_of[r * S + sq] : vRd + set * SETW + sq;
+    };
+    // issue batch bt's reads into read set `set`; returns the LDS instructions issued
+    auto reads = [&](const Batch& bt, int gi, int set, int boff, int c0) {
+      const std::vector<Step>& all = alls[gi];
+      const std::vector<Nz>& L = nzs[gl[gi]];
+      int n = 0;
+      if (p.cb) {
+        const int c = all[bt.steps[0]].c;
+        E.v(vBase + set, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + set, boff + (c - c0) * p.chs * 4));
+        const int base = vRd + set * SETW;
+        const size_t nt = bt.taps.size();
+        for (size_t i = 0; i < nt; i += 2) {
+          const int t0 = bt.taps[i], o0 = (t0 / S) * g.Pp + t0 % S;
+          if (i + 1 < nt) {
+            const int t1 = bt.taps[i + 1], o1 = (t1 / S) * g.Pp + t1 % S;
+            E.line("ds_read2_b32 v[%d:%d], v%d offset0:%d offset1:%d", base + (int)i, base + (int)i + 1,
+                   vBase + set, o0, o1);
+          } else {
+            E.line("ds_read_b32 v%d, v%d offset:%d", base + (int)i, vBase + set, o0 * 4);
+          }
+          E.code += 8;
+          n++;
+        }
+        return n;
+      }
+      const Step& st = all[bt.steps[0]];
       std::vector<char> used(S, 0);
       for (int i : st.nz) used[L[i].sq] = 1;
-      int n = 0;
       for (int sidx = 0; sidx < S; sidx++) {
         if (!used[sidx]) continue;
         const int off = boff + (st.c - c0) * p.chs * 4 + (st.r * g.Pp + sidx) * 4;
-        E.line("ds_read_b32 v%d, v5 offset:%d", rd(set, sidx), off);
+        E.line("ds_read_b32 v%d, v5 offset:%d", vRd + set * SETW + sidx, off);
         E.code += 8;
         n++;
       }
@@ -898,60 +985,83 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     };
     // the DMA runs P = nbuf - 1 chunks ahead: chunk i goes to buffer i % nbuf, which chunk
     // i - nbuf read before the barrier that precedes its staging
-    const int nch = (int)chunks.size(), P = p.nbuf - 1;
+    const int nch = (int)units.size(), P = p.nbuf - 1;
     int issued = 0;
     auto wait_for = [&](int k) {
-      // chunk k is in LDS once this wavefront's DMAs of chunk k are done (they retire in
-      // order, so at most the DMAs of the chunks issued after it may still be outstanding;
-      // the fewest any wavefront issues for them) and every wavefront has passed the barrier
+      // unit k's chunk is in LDS once this wavefront's DMAs of it are done (loads retire in
+      // order, so at most the DMAs issued after them may still be outstanding: the fewest
+      // any wavefront issues for the later units; stores in between are not counted, which
+      // only makes the wait safe whatever their order) and every wavefront has passed the
+      // barrier
       int later = 0;
-      for (int j = k + 1; j < issued; j++) later += staged_dmas_min(g, p, chunks[j]);
+      for (int j = k + 1; j < issued; j++) later += staged_dmas_min(g, p, units[j].k);
       E.line("s_waitcnt vmcnt(%d)", std::min(later, 63));
       E.line("s_barrier");
     };
-    for (; issued < std::min(P, nch); issued++) stage(chunks[issued], issued % p.nbuf);
+    for (; issued < std::min(P, nch); issued++) stage(units[issued].k, issued % p.nbuf);
     if (nch > 0) wait_for(0);
     for (int ci = 0; ci < nch; ci++) {
-      const int boff = (ci % p.nbuf) * BUF, c0 = chunks[ci] * p.Cc;
+      const int gi = units[ci].gi;
+      const std::vector<Step>& all = alls[gi];
+      const std::vector<Nz>& L = nzs[gl[gi]];
+      const int boff = (ci % p.nbuf) * BUF, c0 = units[ci].k * p.Cc;
       if (ci + P < nch) {
-        stage(chunks[ci + P], (ci + P) % p.nbuf);
+        stage(units[ci + P].k, (ci + P) % p.nbuf);
         issued++;
       }
-      // step j's taps go to read set j % NS, issued ra steps ahead; before step j's FMAs
-      // only the reads of the steps after it may be outstanding
-      const std::vector<int>& ts = csteps[ci];
-      const int nts = (int)ts.size();
-      std::vector<int> nrd(nts, 0);
-      for (int j = 0; j < std::min(p.ra, nts); j++) nrd[j] = reads(ts[j], j % NS, boff, c0);
-      for (int j = 0; j < nts; j++) {
-        if (j + p.ra < nts) nrd[j + p.ra] = reads(ts[j + p.ra], (j + p.ra) % NS, boff, c0);
-        int later = 0;
-        for (int k = j + 1; k < std::min(nts, j + p.ra + 1); k++) later += nrd[k];
-        E.line("s_waitcnt lgkmcnt(%d)", later);
-        E.code += 4;
-        const Step& st = all[ts[j]];
-        for (int i : st.nz) {
-          const Nz& z = L[i];
-          const int a = vAcc + slot_of[z.m];
-          const int sr = rd(j % NS, z.sq);
-          if (!touched[slot_of[z.m]]) {
-            touched[slot_of[z.m]] = 1;
-            E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
-          } else {
-            E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
-          }
-          fmas++;
+      // the unit's batches
+      std::vector<Batch> bts;
+      for (int t : units[ci].ts) {
+        if (!p.cb || bts.empty() || all[bts.back().steps[0]].c != all[t].c) {
+          bts.emplace_back();
+          if (p.cb) bts.back().reg_of.assign(g.R * S, -1);
+        }
+        Batch& bt = bts.back();
+        bt.steps.push_back(t);
+        if (p.cb) {
+          std::vector<char> used(S, 0);
+          for (int i : all[t].nz) used[L[i].sq] = 1;
+          for (int sq = 0; sq < S; sq++)
+            if (used[sq]) {
+              bt.reg_of[all[t].r * S + sq] = (int)bt.taps.size();
+              bt.taps.push_back(all[t].r * S + sq);
+            }
         }
       }
+      // batch j's taps go to read set j % NS, issued ra batches ahead; before batch j's FMAs
+      // only the reads of the batches after it may be outstanding
+      const int nbt = (int)bts.size();
+      std::vector<int> nrd(nbt, 0);
+      for (int j = 0; j < std::min(p.ra, nbt); j++) nrd[j] = reads(bts[j], gi, j % NS, boff, c0);
+      for (int j = 0; j < nbt; j++) {
+        if (j + p.ra < nbt) nrd[j + p.ra] = reads(bts[j + p.ra], gi, (j + p.ra) % NS, boff, c0);
+        int later = 0;
+        for (int k = j + 1; k < std::min(nbt, j + p.ra + 1); k++) later += nrd[k];
+        E.line("s_waitcnt lgkmcnt(%d)", later);
+        E.code += 4;
+        for (int t : bts[j].steps) {
+          const Step& st = all[t];
+          for (int i : st.nz) {
+            const Nz& z = L[i];
+            const int a = vAcc + slot_of[z.m];
+            const int sr = tapreg(bts[j], j % NS, st.r, z.sq);
+            if (!touched[slot_of[z.m]]) {
+              touched[slot_of[z.m]] = 1;
+              E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));
+            } else {
+              E.v(a, 8, fmt("v_fmac_f32_e32 v%d, 0x%08x, v%d", a, z.bits, sr));
+            }
+            fmas++;
+          }
+        }
+      }
+      const bool last = ci + 1 == nch || units[ci + 1].gi != gi;
+      if (last) store_group(gl[gi], touched);
       if (ci + 1 < nch) wait_for(ci + 1);
     }
-    for (int k = 0; k < nrow; k++)
-      if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
-    for (int k = 0; k < nrow; k++) {
-      E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[gq][k] * EF4);
-      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
-      E.code += 16;
-    }
+    // groups without any step (all their channels empty) store +0
+    for (int gi = 0; gi < (int)gl.size(); gi++)
+      if (alls[gi].empty()) store_group(gl[gi], touched);
     E.line("s_endpgm");
     p.sec_valu = std::max(p.sec_valu, E.valu - v0);
   }
@@ -1273,62 +1383,84 @@ bool bake_generate(const Geom& g, const std::vector<int32_t>& rowptr, const std:
       for (int k = 0; k < nacc; k++)
         if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
       if (Q > 1) {
-        // Partial sums go through LDS in rounds of KC channels (one buffer of KC channels per
-        // later split, reused each round): splits q >= 1 write their KC accumulators (16 bytes per
-        // lane and 4 channels), barrier; split 0 adds them in split order, barrier.  The lane's
-        // byte address of its 16-byte column (split q writes part q - 1) lives in the first
-        // row-vector offset register, dead once the last load is issued; the rest of the
-        // offset, ring and shift registers hold the partials split 0 reads.
+        // Reduce-scatter of the partial sums through LDS, in rounds of KC channels: block k4
+        // (channels 4 k4 .. 4 k4 + 3) belongs to split k4 % Q.  Each round every split writes
+        // the blocks the others own (16 bytes per lane and block, its own part of the unit's
+        // LDS), barrier; each split adds the Q partial sums of its own blocks in split order,
+        // ((p0 + p1) + ...) + p(Q-1), barrier.  Every split then stores its own blocks.  The
+        // lane's byte address in the unit's LDS lives in the first row-vector offset register,
+        // dead once the last load is issued; the rest of the offset, ring and shift registers
+        // hold the partial sums read.
         const int KC = p.rc;
         const int kbr = (KC / 4) * 1024;  // bytes of one split's part per round
         const int rounds = (p.Mg + KC - 1) / KC;
         const int va = vOff;
-        E.line("s_mul_i32 s17, s14, %d", (Q - 1) * kbr);
-        if (sq_ > 0) E.line("s_add_u32 s17, s17, %d", (sq_ - 1) * kbr);
+        E.line("s_mul_i32 s17, s14, %d", Q * kbr);
         E.v(va, 4, fmt("v_lshlrev_b32_e32 v%d, 4, v1", va));
         E.v(va, 4, fmt("v_add_u32_e32 v%d, s17, v%d", va, va));
         const int t0r = (vOff + 2) & ~1;  // even-aligned temporaries
-        const int nb = std::max(1, std::min(8, (vAcc - t0r) / 4));
-        const int vb = vOff + 1;           // base register of a batch of reads
+        const int ntmp = std::min(16, (vAcc - t0r) / 4);
+        if (ntmp < Q - 1) {
+          *err = "too few free registers for the channel-split reduction";
+          return false;
+        }
+        const int bpb = ntmp / (Q - 1);  // own blocks per batch of reads
+        const int vb = vOff + 1;                       // base register of a batch of reads
         for (int j = 0; j < rounds; j++) {
-          const int k40 = j * KC / 4, k41 = std::min(p.Mg, (j + 1) * KC) / 4, nk = k41 - k40;
+          const int k40 = j * KC / 4, k41 = std::min(p.Mg, (j + 1) * KC) / 4;
           const bool last = j + 1 == rounds;
-          if (sq_ > 0) {
-            for (int k4 = k40; k4 < k41; k4++)
-              E.line("ds_write_b128 v%d, v[%d:%d] offset:%d", va, vAcc + 4 * k4, vAcc + 4 * k4 + 3, (k4 - k40) * 1024);
-            E.line("s_waitcnt lgkmcnt(0)");
-            E.line("s_barrier");
-            if (!last) E.line("s_barrier");  // split 0 has read this round's parts
-            continue;
-          }
+          for (int k4 = k40; k4 < k41; k4++)
+            if (k4 % Q != sq_)
+              E.line("ds_write_b128 v%d, v[%d:%d] offset:%d", va, vAcc + 4 * k4, vAcc + 4 * k4 + 3,
+                     sq_ * kbr + (k4 - k40) * 1024);
+          E.line("s_waitcnt lgkmcnt(0)");
           E.line("s_barrier");
-          // block b of the round: split b / nk + 1, channels 4 * (k40 + b % nk) .. + 3
-          const int nq = (Q - 1) * nk;
-          auto off = [&](int b) { return (b / nk) * kbr + (b % nk) * 1024; };
-          for (int b0 = 0; b0 < nq; b0 += nb) {
-            const int b1 = std::min(nq, b0 + nb);
-            E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", vb, off(b0), va));
-            for (int bb = b0; bb < b1; bb++)
-              E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * (bb - b0), t0r + 4 * (bb - b0) + 3, vb,
-                     off(bb) - off(b0));
+          std::vector<int> mine;
+          for (int k4 = k40; k4 < k41; k4++)
+            if (k4 % Q == sq_) mine.push_back(k4);
+          for (size_t m0 = 0; m0 < mine.size(); m0 += bpb) {
+            const size_t m1 = std::min(mine.size(), m0 + bpb);
+            // the other splits' parts of these blocks: temporary block i holds part q of own
+            // block m, in (block, split) order
+            auto off = [&](int k4, int q) { return q * kbr + (k4 - k40) * 1024; };
+            const int first = off(mine[m0], sq_ == 0 ? 1 : 0);
+            E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v%d", vb, first, va));
+            std::vector<int> tmp_of;  // per (block, q): temporary block index, -1 for the own part
+            int nt = 0;
+            for (size_t m = m0; m < m1; m++)
+              for (int q = 0; q < Q; q++) {
+                if (q == sq_) {
+                  tmp_of.push_back(-1);
+                  continue;
+                }
+                E.line("ds_read_b128 v[%d:%d], v%d offset:%d", t0r + 4 * nt, t0r + 4 * nt + 3, vb,
+                       off(mine[m], q) - first);
+                tmp_of.push_back(nt++);
+              }
             E.line("s_waitcnt lgkmcnt(0)");
-            for (int bb = b0; bb < b1; bb++) {
-              const int k4 = k40 + bb % nk;
-              for (int jj = 0; jj < 4; jj++)
-                E.v(vAcc + 4 * k4 + jj, 4,
-                    fmt("v_add_f32_e32 v%d, v%d, v%d", vAcc + 4 * k4 + jj, vAcc + 4 * k4 + jj, t0r + 4 * (bb - b0) + jj));
+            for (size_t m = m0; m < m1; m++) {
+              const int k4 = mine[m];
+              const int* to = &tmp_of[(m - m0) * Q];
+              for (int jj = 0; jj < 4; jj++) {
+                const int acc = vAcc + 4 * k4 + jj;
+                auto part = [&](int q) { return to[q] < 0 ? acc : t0r + 4 * to[q] + jj; };
+                if (sq_ == 0) {
+                  for (int q = 1; q < Q; q++) E.v(acc, 4, fmt("v_add_f32_e32 v%d, v%d, v%d", acc, acc, part(q)));
+                } else {
+                  // prefix p0 + ... + p(sq-1) in part 0's temporary, then the own part, then the rest
+                  const int pre = part(0);
+                  for (int q = 1; q < sq_; q++) E.v(pre, 4, fmt("v_add_f32_e32 v%d, v%d, v%d", pre, pre, part(q)));
+                  E.v(acc, 4, fmt("v_add_f32_e32 v%d, v%d, v%d", acc, pre, acc));
+                  for (int q = sq_ + 1; q < Q; q++) E.v(acc, 4, fmt("v_add_f32_e32 v%d, v%d, v%d", acc, acc, part(q)));
+                }
+              }
             }
           }
-          if (!last) E.line("s_barrier");  // the parts may be overwritten
-        }
-        if (sq_ > 0) {
-          E.line("s_endpgm");
-          p.sec_valu = std::max(p.sec_valu, E.valu - v0 + p.Mg / 4);
-          p.sec_steps = std::max<long long>(p.sec_steps, T_);
-          continue;
+          if (!last) E.line("s_barrier");  // every split has read this round's parts
         }
       }
       for (int k = 0; k < nrow; k++) {
+        if (Q > 1 && (k / 4) % Q != sq_) continue;
         E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[gq][k] * EF4);
         E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
         E.code += 16;

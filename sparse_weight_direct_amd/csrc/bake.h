@@ -58,7 +58,12 @@ struct BakePlan {
   // ds_read_b32 at an immediate offset
   int stage = 0;
   int Cc = 0, chs = 0, bw = 0, nblk = 0, nbuf = 2;
-  int ra = 1;                // steps whose tap reads are issued ahead of the FMAs
+  int ra = 1;                // batches of tap reads issued ahead of the FMAs
+  int cb = 0;                // 1: a read batch is a channel's steps (ds_read2_b32 pairs from a
+                             // per-channel base register); 0: one step (ds_read_b32)
+  int seq = 0;               // 1: each workgroup runs every group in turn (the stores of one
+                             // group overlap the next group's copies and FMAs); 0: one group
+                             // per workgroup
   int pairdist = 0;          // 1: wave w stages block w % nblk of every (T / nblk)-th channel
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
@@ -80,12 +85,14 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=.." (tuning and
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=.." (tuning and
 // tests only); fields left at -1 are chosen by the packer.
 struct BakeForce {
-  int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1;
+  int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1, cb = -1,
+      seq = -1;
   bool any() const {
-    return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0;
+    return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0 ||
+           cb >= 0 || seq >= 0;
   }
 };
 BakeForce bake_force_from_env();

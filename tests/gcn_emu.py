@@ -245,6 +245,31 @@ class Wave:
                 self.lgkm.append([dst])
                 if len(self.lgkm) > 15:
                     raise EmuError("too many LDS instructions outstanding")
+            elif op == "ds_read2_b32":
+                # two dwords per lane at base + 4*offset0 and base + 4*offset1 (8-bit offsets)
+                # into an even-aligned register pair
+                if self.lds is None:
+                    raise EmuError("LDS access in a kernel without LDS")
+                srcp, _, mods = a[1].partition(" ")
+                offs = {}
+                for mod in mods.split():
+                    key, _, num = mod.partition(":")
+                    if key not in ("offset0", "offset1") or not 0 <= int(num) <= 255:
+                        raise EmuError(f"LDS modifier not emulated: {mod}")
+                    offs[key] = int(num)
+                base = self.src_vec(srcp).astype(np.int64)
+                dst = self.vtuple(a[0], 2)
+                for j, key in enumerate(("offset0", "offset1")):
+                    addr = base + 4 * offs.get(key, 0)
+                    if (addr % 4).any() or (addr < 0).any() or (addr + 4 > self.lds.size * 4).any():
+                        raise EmuError("ds_read2_b32 outside the LDS or misaligned")
+                    w = addr // 4
+                    if self.lds_pend is not None and self.lds_pend[w].any():
+                        raise EmuError("LDS read of words an LDS DMA has not finished writing")
+                    self.v[dst[j]] = self.lds[w]
+                self.lgkm.append(list(dst))
+                if len(self.lgkm) > 15:
+                    raise EmuError("too many LDS instructions outstanding")
             elif op == "ds_bpermute_b32":
                 # lane l receives data[((addr[l] + offset) >> 2) & 63] through the LDS crossbar
                 srcp, _, mods = a[2].partition(" ")
@@ -449,7 +474,7 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
         # ntiles = workgroups of T tiles of 64 per group
         qtot = N * (info["H"] + 2 * info["pad"]) * Pb
         ntiles = (qtot + 64 * T - 1) // (64 * T)
-        per_xcd = (ntiles * G + 7) // 8
+        per_xcd = (ntiles * (1 if info.get("bake_sequential") else G) + 7) // 8
     else:
         qtot = N * E * Pb
         ntiles = (qtot + V - 1) // V

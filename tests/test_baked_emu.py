@@ -153,13 +153,14 @@ def test_crossbar_shifts_equal_dpp_shifts(c, monkeypatch):
 @pytest.mark.parametrize("env", ["G=2,Q=4,T=1", "G=2,Q=3,T=2"])
 def test_channel_split_reduction_in_rounds(env, monkeypatch):
     """128 accumulators per wavefront and several channel splits: the partial sums go through one
-    LDS buffer of 32 channels per later split, reused over 4 rounds (two barriers per round), so a
-    unit needs (Q - 1) * 8 KB of LDS however many channels it holds; the sums are added in split
-    order, so the result equals the oracle's within tolerance and repeats bit for bit."""
+    LDS buffer of 32 channels per split, reused over 4 rounds (two barriers per round), so a unit
+    needs Q * 8 KB of LDS however many channels it holds; each split adds the partial sums of its
+    own blocks of 4 channels in split order and stores them, so the result equals the oracle's
+    within tolerance and repeats bit for bit."""
     d = workloads.make_custom(1, 12, 5, 7, 256, 3, 3, 1, 1, 0.3, 31)
     y, info = _check(d, 1, 1, env, env, monkeypatch)
     Q, T = info["bake_splits"], info["bake_units_per_wg"]
-    assert Q > 2 and info["bake_lds_bytes"] == T * (Q - 1) * 8 * 1024
+    assert Q > 2 and info["bake_lds_bytes"] == T * Q * 8 * 1024
     y2, _, _ = _emulate(d, 1, 1)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
@@ -173,7 +174,8 @@ STAGED_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
     (2, 17, 9, 9, 6, 1, 1, 1, 0, 0.5, 46),     # 1x1
     (2, 7, 17, 19, 13, 3, 3, 1, 1, 0.0, 47),   # no non-zero at all: +0 everywhere
 ]
-STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2"]
+STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2,CB=0",
+               "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2", "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0"]
 
 
 @pytest.mark.parametrize("env", STAGED_ENVS)
@@ -185,7 +187,11 @@ def test_staged_kernels(c, env, monkeypatch):
     writes it has been waited for, and the wait state after writing m0.  The FMAs are the same
     as the default plan's in the same order, so the outputs equal its outputs bit for bit.
     Options: T wavefronts per workgroup, G groups, NB chunk buffers (the DMA runs NB - 1
-    chunks ahead), CC channels per chunk, RA steps of tap reads in flight."""
+    chunks ahead), CC channels per chunk, RA batches of tap reads in flight, CB=1 a channel's
+    taps read as one batch (pairs by ds_read2_b32 from a per-channel base register; the
+    default where the filter's reach allows), CB=0 one step's taps per batch, SEQ=1 every
+    workgroup runs all G groups in turn (the DMA pipeline continues across groups, each
+    group's stores follow its last chunk)."""
     d = workloads.make_custom(*c)
     y, info = _check(d, c[7], c[8], env, env, monkeypatch)
     assert info["bake_stage"] == 1 and info["bake_valid_lanes"] == 64

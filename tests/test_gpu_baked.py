@@ -182,7 +182,8 @@ WIDE_LAYER = (3, 21, 23, 36, 50, 3, 3, 1, 1, 0.15, 78)  # W % 4 == 0: 16-byte DM
 
 @pytest.mark.parametrize("layer", [LAYER, WIDE_LAYER], ids=["narrow", "wide"])
 @pytest.mark.parametrize("env", ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "STAGE=1,G=50,T=4",
-                                 "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2"])
+                                 "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2,CB=0", "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2",
+                                 "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0"])
 def test_staged_plans(layer, env, monkeypatch):
     """Staged kernels (input windows copied into LDS by LDS DMA per chunk of channels, taps read
     from LDS): the same FMAs in the same order as the default plan, so the outputs agree with it
