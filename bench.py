@@ -6,7 +6,8 @@ A step is one sparseconv_forward over one batch: the 112x112 layer, batch 8, C =
 sparsity 95% (the middle of the 90-99% range the method targets).  Packing happens once,
 before timing, as in deployment (weights stay resident), and so does the choice of kernel for
 the batch size where the grid leaves SIMDs idle (sparseconv_tune times the handle's kernels and
-pins the fastest); the forward launches one kernel.
+pins the fastest); the forward launches one kernel (on this layer the staged weights-in-code
+kernel).
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
 with a device synchronisation on both sides.  Input/output buffer sets rotate so the working
@@ -16,8 +17,10 @@ Printed: one JSON line with effective TFLOP/s (2*nnz*N*E*F per second) as ``valu
 roofline of the kernel (bound from the arithmetic intensity against the ridge of 8 TB/s and
 the 157.3 TFLOP/s fp32 vector FMA peak, which plain v_fmac_f32 reaches: the FMA probe timed
 here measures it), the HBM fraction, the plan the forward launched, the roof probes (FMA rate
-by wavefronts per SIMD, LDS read bandwidth), every other workload layer timed the same way (``per_config``), the dense direct
-baseline and torch's conv2d (MIOpen) on the same GPU, and the CPU oracle on this host.
+by wavefronts per SIMD, LDS read bandwidth), every other workload layer timed the same way
+(``per_config``; with ``graph_us``, the same forwards replayed from one HIP graph, which leaves
+out the host's launch cost of about 5 us per call that bounds the smallest layers), the dense
+direct baseline and torch's conv2d (MIOpen) on the same GPU, and the CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -143,6 +146,27 @@ def main():
             h.tune(xs[0], ys[0], reps=5, stream=stream)
         return d, L, h, ws, xs, ys, nsets, set_bytes
 
+    def graph_us(hh, xxs, yys, nn, wws, k=20, reps=3):
+        """GPU time per forward with no host launch cost between forwards: k forwards over
+        rotated (cold) buffer sets captured in one HIP graph, replayed reps times."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(k):
+                hh.forward(xxs[i % nn], yys[i % nn], workspace=wws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (k * reps)
+
     def describe(L, info, ms):
         nnz = info["nnz"]
         flops = roofline.effective_flops(nnz, L.N, L.E, L.F)
@@ -260,17 +284,20 @@ def main():
             cms_, csem = run(lambda i: hh.forward(xxs[i], yys[i], stream=stream, workspace=wws), steps, 5, nn)
             mm = describe(LL, hh.info(), cms_)
             li = hh.launch_info(LL.N)
-            per[name] = {"us": round(cms_ * 1e3, 2), "sem_us": round(csem * 1e3, 2), "tflops": round(mm["tflops"], 3),
+            gus = graph_us(hh, xxs, yys, nn, wws)
+            per[name] = {"us": round(cms_ * 1e3, 2), "sem_us": round(csem * 1e3, 2), "graph_us": round(gus, 2),
+                         "tflops": round(mm["tflops"], 3),
                          "frac_of_8tbs": round(mm["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(mm["ai"], 2),
                          "bound": mm["bound"], "roofline_frac": round(mm["frac"], 4), "nnz": hh.info()["nnz"],
                          "launch": {k: li[k] for k in ("mapping", "variant", "stage", "groups", "splits",
                                                        "units_per_wg", "depth", "grid", "waves", "vgprs",
                                                        "lds_bytes", "tile_pixels", "chunk_channels", "quad")}}
-            log(f"[bench] config {name}: {cms_ * 1e3:.1f} us, {mm['tflops']:.2f} TFLOP/s, "
+            log(f"[bench] config {name}: {cms_ * 1e3:.1f} us ({gus:.1f} us replayed from a graph), {mm['tflops']:.2f} TFLOP/s, "
                 f"{mm['gbs'] / roofline.HBM_PEAK_GBS:.3f} of 8 TB/s, launch {per[name]['launch']}")
             del dd, hh, xxs, yys
             torch.cuda.empty_cache()
-        per[layer] = {"us": round(ms * 1e3, 2), "sem_us": round(sem * 1e3, 2), "tflops": round(m["tflops"], 3),
+        per[layer] = {"us": round(ms * 1e3, 2), "sem_us": round(sem * 1e3, 2),
+                      "graph_us": round(graph_us(h, xs, ys, nsets, ws), 2), "tflops": round(m["tflops"], 3),
                       "frac_of_8tbs": round(m["gbs"] / roofline.HBM_PEAK_GBS, 4), "ai": round(m["ai"], 2),
                       "bound": m["bound"], "roofline_frac": round(m["frac"], 4), "nnz": nnz,
                       "launch": {k: launch[k] for k in ("mapping", "variant", "stage", "groups", "splits",
