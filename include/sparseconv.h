@@ -181,6 +181,8 @@ typedef struct {
   int32_t bake_buffers;
   int32_t bake_sequential;  /* 1: each workgroup runs every group in turn (the stores of one
                                group overlap the next group's work); 0: one group per workgroup */
+  int32_t bake_shared_window; /* 1: a workgroup holds every group's wavefronts for its tiles,
+                                 which stage one input window together */
   int64_t bake_code_bytes;  /* bytes of generated code of the base kernel */
 } sc_info;
 

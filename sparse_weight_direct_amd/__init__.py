@@ -66,7 +66,8 @@ class sc_info(ctypes.Structure):
                                                "bake_groups", "bake_splits", "bake_units_per_wg",
                                                "bake_valid_lanes", "bake_pitch", "bake_depth", "bake_vgprs",
                                                "bake_lds_bytes", "bake_variants", "bake_stage",
-                                               "bake_chunk_channels", "bake_buffers", "bake_sequential")] + \
+                                               "bake_chunk_channels", "bake_buffers", "bake_sequential",
+                                               "bake_shared_window")] + \
                [("bake_code_bytes", ctypes.c_int64)]
 
     def as_dict(self):

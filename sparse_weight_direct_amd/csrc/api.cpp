@@ -634,6 +634,7 @@ sc_status sparseconv_query(const sc_handle* h, sc_info* info) {
     info->bake_chunk_channels = b.Cc;
     info->bake_buffers = b.stage ? b.nbuf : 0;
     info->bake_sequential = b.seq;
+    info->bake_shared_window = b.gw;
     info->bake_code_bytes = b.code_bytes;
   }
   if (h->escoin) {
@@ -811,11 +812,14 @@ bool baked_fits(const sc_handle* h, int N) {
 }
 
 // The weights-in-code kernel a forward of N images launches (-1: none, use the LDS-tile
-// plans): the one sparseconv_tune pinned for N; else, when it gives every SIMD a wavefront, the
-// staged kernel (measured best on the 112x112 layers: as fast as the base kernel where the
-// FMAs dominate, up to 1.2x faster where the traffic does) or the base kernel; else the
+// plans): the one sparseconv_tune pinned for N; else, when it gives every SIMD a wavefront, a
+// staged kernel (measured best on the 112x112 layers: up to 1.2x faster than the base kernel
+// where the traffic dominates) -- the one whose workgroups share their window between twice
+// the groups when the layer has at least kSharedNnzPerChannel non-zeros per output channel
+// (1.07-1.1x faster at 80-90% sparsity, slower at 95-99%) -- or the base kernel; else the
 // handle's kernel with the lowest estimated cycles for N among the unstaged ones (few
 // wavefronts leave the staged kernel's DMA latency exposed).
+constexpr long long kSharedNnzPerChannel = 64;
 long long baked_waves(const sc_handle* h, const sc::BakePlan& bp, int N);
 
 // Whether weights-in-code kernel i can read this input: staged kernels of the wide layout copy
@@ -829,8 +833,14 @@ int pick_baked(const sc_handle* h, int N) {
   if (!baked_fits(h, N)) return -1;
   const int t = tuned_choice(h, N, 0);
   if (t >= 0 && (size_t)t < h->bk.size()) return t;
-  for (size_t i = 0; i < h->bk.size(); i++)
-    if (h->bk[i].p.stage && baked_waves(h, h->bk[i].p, N) >= 4LL * h->cus) return (int)i;
+  const bool shared = h->nnz >= kSharedNnzPerChannel * h->g.M;
+  int staged = -1;
+  for (size_t i = 0; i < h->bk.size(); i++) {
+    const sc::BakePlan& bp = h->bk[i].p;
+    if (!bp.stage || baked_waves(h, bp, N) < 4LL * h->cus) continue;
+    if (staged < 0 || (bool)bp.gw == shared) staged = (int)i;
+  }
+  if (staged >= 0) return staged;
   if (baked_waves(h, h->bk[0].p, N) >= 4LL * h->cus) return 0;
   int best = 0;
   double bc = 0;
@@ -859,7 +869,7 @@ sc::BakeArgs baked_args(const sc_handle* h, const sc::BakePlan& bp, int N) {
     const long long qtot = (long long)N * g.HYp * g.Pp;
     a.qtot = (uint32_t)qtot;
     a.ntiles = (uint32_t)((qtot + 64LL * bp.T - 1) / (64LL * bp.T));
-    a.per_xcd = (uint32_t)(((long long)a.ntiles * (bp.seq ? 1 : bp.G) + 7) / 8);
+    a.per_xcd = (uint32_t)(((long long)a.ntiles * (bp.seq || bp.gw ? 1 : bp.G) + 7) / 8);
     return a;
   }
   const long long qtot = (long long)N * g.E * bp.Pb;

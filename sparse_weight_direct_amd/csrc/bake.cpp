@@ -58,6 +58,7 @@ BakeForce bake_force_from_env() {
   f.ra = env_key(e, "RA", -1);
   f.cb = env_key(e, "CB", -1);
   f.seq = env_key(e, "SEQ", -1);
+  f.gw = env_key(e, "GW", -1);
   return f;
 }
 
@@ -347,8 +348,13 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   p.bw = g.wide ? 256 : 64;  // 16 bytes per lane in the wide layout, else 4
   p.chs = (p.T * 64 + (g.R - 1) * g.Pp + g.S - 1 + p.bw - 1) / p.bw * p.bw;
   p.nblk = p.chs / p.bw;
-  p.pairdist = (p.T % p.nblk == 0) ? 1 : 0;
-  const int nvb = p.pairdist ? 1 : (p.nblk + p.T - 1) / p.T;
+  const int W = p.wpb();  // the wavefronts that share the window's DMA
+  if (W > 16) {
+    *why = "more than 16 wavefronts per workgroup";
+    return false;
+  }
+  p.pairdist = (W % p.nblk == 0) ? 1 : 0;
+  const int nvb = p.pairdist ? 1 : (p.nblk + W - 1) / W;
   // nbuf chunk buffers (the DMA runs nbuf - 1 chunks ahead); every ds_read offset (buffer +
   // channel + tap) must fit 16 bits
   const int reach = 4 * ((g.R - 1) * g.Pp + g.S);
@@ -365,7 +371,7 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     p.Cc = std::min(g.C, cc > 0 ? cc : kStagedChunk);
   }
   // at most 48 DMAs of the chunks ahead outstanding per wavefront (the counter holds 63)
-  auto dmas = [&](int cc) { return p.pairdist ? (cc + p.T / p.nblk - 1) / (p.T / p.nblk) : cc * nvb; };
+  auto dmas = [&](int cc) { return p.pairdist ? (cc + W / p.nblk - 1) / (W / p.nblk) : cc * nvb; };
   while (p.Cc > 1 && (p.nbuf - 1) * dmas(p.Cc) > 48) p.Cc--;
   if ((p.nbuf - 1) * dmas(p.Cc) > 48) {
     *why = "staged window needs too many DMAs per chunk";
@@ -466,12 +472,13 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
               {std::min(M, 4 * G0), 1, 4}, {std::min(M, 2 * G0), 2, 1}};
   }
   // staged plan: forced (STAGE=1), or appended to the candidates for stride-1 layers
-  auto add_staged = [&](int G, int T, int seq) {
+  auto add_staged = [&](int G, int T, int seq, int gw) {
     BakePlan c = p;
     c.stage = 1;
     c.G = G;
     c.T = T;
     c.seq = G > 1 ? seq : 0;
+    c.gw = G > 1 && !c.seq ? gw : 0;
     std::string w;
     if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, f.cb, &c, &w))
       out.push_back(std::move(c));
@@ -484,9 +491,9 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     while (n < M && staged_vgprs(g, nvb, (M + n - 1) / n, staged_read_ahead(g, f.ra, cb), cb) > kVgprTarget) n++;
     return n;
   };
-  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0) {
+  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0 || f.gw >= 0) {
     const int T = f.T > 0 ? f.T : 4;
-    add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T, f.seq > 0 ? 1 : 0);
+    add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T, f.seq > 0 ? 1 : 0, f.gw > 0 ? 1 : 0);
     return out;
   }
   for (const Shape& sh : shapes) {
@@ -511,14 +518,21 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     else if (out.empty())
       *why = w;
   }
-  if (!f.any() && g.st == 1) add_staged(staged_groups(2), 4, 0);
+  if (!f.any() && g.st == 1) {
+    // staged kernels: one group per workgroup, and twice the groups sharing each workgroup's
+    // window (more, lighter wavefronts that repeat the tap reads; faster where the FMAs
+    // dominate)
+    const int G1 = staged_groups(2);
+    add_staged(G1, 4, 0, 0);
+    if (2 * G1 <= M && 4 * 2 * G1 <= 16) add_staged(2 * G1, 4, 0, 1);
+  }
   return out;
 }
 
 double bake_estimate(const Geom& g, const BakePlan& p, int N, int cus) {
   const long long qtot = p.stage ? (long long)N * g.HYp * g.Pp : (long long)N * g.E * p.Pb;
   const long long ntiles = p.stage ? (qtot + 64LL * p.T - 1) / (64LL * p.T) * p.T : (qtot + p.V - 1) / p.V;
-  const long long waves = ntiles * (p.seq ? 1 : p.G) * p.Q;
+  const long long waves = ntiles * (p.seq ? 1 : p.G) * p.Q;  // gw: the same waves, fewer workgroups
   const double simds = 4.0 * cus;
   // VALU: a SIMD runs about ceil(waves / SIMDs) sections' instructions one after the other
   const double valu = std::ceil((double)waves / simds) * (double)p.sec_valu * 4.0;
@@ -667,14 +681,15 @@ void finish_kernel(Emitter& E, BakePlan& p, int nv, int WPB, std::string* src) {
 static int staged_dmas_min(const Geom& g, const BakePlan& p, int k) {
   const int cn = std::min(p.Cc, g.C - k * p.Cc);
   int best = 1 << 30;
-  for (int w = 0; w < p.T; w++) {
+  const int W = p.wpb();  // the wavefronts sharing the window
+  for (int w = 0; w < W; w++) {
     int n = 0;
     if (p.pairdist) {
-      const int per = p.T / p.nblk;
+      const int per = W / p.nblk;
       for (int i = 0; i * per < cn; i++) n += (w / p.nblk + i * per < cn) ? 1 : 0;
     } else {
-      const int nvb = (p.nblk + p.T - 1) / p.T;
-      for (int k2 = 0; k2 < nvb; k2++) n += (k2 * p.T + w < p.nblk) ? cn : 0;
+      const int nvb = (p.nblk + W - 1) / W;
+      for (int k2 = 0; k2 < nvb; k2++) n += (k2 * W + w < p.nblk) ? cn : 0;
     }
     best = std::min(best, n);
   }
@@ -693,7 +708,8 @@ static int staged_dmas_min(const Geom& g, const BakePlan& p, int k) {
 bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                      const std::vector<float>& val, BakePlan& p, std::string* src, std::string* err) {
   const int T = p.T, S = g.S;
-  const int nvb = p.pairdist ? 1 : (p.nblk + T - 1) / T;
+  const int W = p.wpb();  // wavefronts per workgroup: T tiles (x G groups with a shared window)
+  const int nvb = p.pairdist ? 1 : (p.nblk + W - 1) / W;
   const int lw = p.bw / 64;  // DMA words per lane
   const int vB = kFixedV;              // DMA source offsets
   const int NS = p.ra + 1;             // read sets: the current batch's and ra batches ahead
@@ -731,9 +747,11 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   E.line("s_lshr_b32 s16, s2, 3");
   E.line("s_add_u32 s15, s15, s16");
   E.line("s_mov_b32 s16, 0");
-  // sections: one per group, or one that runs every group in turn (sequential groups)
+  // sections: one per group, or one that runs every group in turn (sequential groups); the
+  // workgroups cover every group, or (sequential groups, shared window) all of them at once
   const int nsec = p.seq ? 1 : p.G;
-  for (int q = 0; q < nsec; q++) {
+  const int wg_groups = (p.seq || p.gw) ? 1 : p.G;
+  for (int q = 0; q < wg_groups; q++) {
     E.line("s_cmp_lt_u32 s15, s25");
     E.line("s_cbranch_scc1 .Lunit");
     E.line("s_sub_u32 s15, s15, s25");
@@ -775,12 +793,21 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     E.v(t0, 8, fmt("v_mul_lo_u32 v%d, v%d, s18", t0, tY));
     E.v(tX, 4, fmt("v_sub_u32_e32 v%d, v%d, v%d", tX, tRem, t0));
   };
+  // the wavefront's tile s37 (and with a shared window its group: s16 = w / T, s37 = w % T)
+  if (p.gw) {
+    E.line("s_mul_i32 s16, s14, %d", (65536 + T - 1) / T);
+    E.line("s_lshr_b32 s16, s16, 16");
+    E.line("s_mul_i32 s37, s16, %d", T);
+    E.line("s_sub_u32 s37, s14, s37");
+  } else {
+    E.line("s_mov_b32 s37, s14");
+  }
   // this wavefront's position and LDS base
   E.line("s_mul_i32 s17, s15, %d", T);
-  E.line("s_add_u32 s17, s17, s14");
+  E.line("s_add_u32 s17, s17, s37");
   E.line("s_mul_i32 s17, s17, 64");
   E.v(tPos, 4, fmt("v_add_u32_e32 v%d, s17, v1", tPos));
-  E.line("s_mul_i32 s18, s14, 64");
+  E.line("s_mul_i32 s18, s37, 64");
   E.v(5, 4, "v_add_u32_e32 v5, s18, v1");
   E.v(5, 4, "v_lshlrev_b32_e32 v5, 2, v5");
   decompose(tPos);
@@ -804,7 +831,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   // DMA source offsets: word J = I0 + blk*bw + lane*lw of the window; input (yp - pad,
   // xq - xoff) of image n, out of range in the padding and past the batch
   if (p.pairdist) {
-    // wave w stages block w % nblk of channels w / nblk + i * (T / nblk): s31 = w / nblk
+    // wave w stages block w % nblk of channels w / nblk + i * (W / nblk): s31 = w / nblk
     E.line("s_mul_i32 s31, s14, %d", (65536 + p.nblk - 1) / p.nblk);
     E.line("s_lshr_b32 s31, s31, 16");
     E.line("s_mul_i32 s30, s31, %d", p.nblk);
@@ -820,7 +847,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     if (p.pairdist)
       E.line("s_mov_b32 s17, s30");
     else
-      E.line("s_add_u32 s17, s14, %d", k * T);
+      E.line("s_add_u32 s17, s14, %d", k * W);
     E.line("s_mul_i32 s17, s17, %d", p.bw);
     E.line("s_add_u32 s17, s17, s19");
     E.v(t2, 4, fmt("v_lshlrev_b32_e32 v%d, %d, v1", t2, lw == 4 ? 2 : 0));
@@ -891,17 +918,25 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       std::vector<int> ts;
     };
     std::vector<Unit> units;
-    for (int gi = 0; gi < (int)gl.size(); gi++)
+    for (int gi = 0; gi < (int)gl.size(); gi++) {
+      if (p.gw) {
+        // the waves of every group stage the shared window together: every section runs every
+        // chunk (empty ones too), so all pass the same copies and barriers
+        for (int k = 0; k * p.Cc < g.C; k++) units.push_back({gi, k, {}});
+        for (int t = 0; t < (int)alls[gi].size(); t++) units[alls[gi][t].c / p.Cc].ts.push_back(t);
+        continue;
+      }
       for (int t = 0; t < (int)alls[gi].size(); t++) {
         const int k = alls[gi][t].c / p.Cc;
         if (units.empty() || units.back().gi != gi || units.back().k != k) units.push_back({gi, k, {}});
         units.back().ts.push_back(t);
       }
-    std::vector<char> touched(p.Mg, 0);
+    }
+    std::vector<char> touched(p.Mg, 0), stored(gl.size(), 0);
     auto stage = [&](int k, int buf) {
       const int c0 = k * p.Cc, cn = std::min(p.Cc, g.C - c0), boff = buf * BUF;
       if (p.pairdist) {
-        const int per = T / p.nblk;
+        const int per = W / p.nblk;
         const int npw = (cn + per - 1) / per;
         for (int i = 0; i < npw; i++) {
           const bool guard = (i + 1) * per > cn;
@@ -920,9 +955,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       } else {
         for (int c = 0; c < cn; c++)
           for (int k2 = 0; k2 < nvb; k2++) {
-            const bool guard = (k2 + 1) * T > p.nblk;
+            const bool guard = (k2 + 1) * W > p.nblk;
             const std::string skip = ".Ls" + std::to_string(lbl++);
-            E.line("s_add_u32 s17, s14, %d", k2 * T);
+            E.line("s_add_u32 s17, s14, %d", k2 * W);
             if (guard) {
               E.line("s_cmp_lt_u32 s17, %d", p.nblk);
               E.line("s_cbranch_scc0 %s", skip.c_str());
@@ -1058,12 +1093,15 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
         }
       }
       const bool last = ci + 1 == nch || units[ci + 1].gi != gi;
-      if (last) store_group(gl[gi], touched);
+      if (last) {
+        store_group(gl[gi], touched);
+        stored[gi] = 1;
+      }
       if (ci + 1 < nch) wait_for(ci + 1);
     }
-    // groups without any step (all their channels empty) store +0
+    // groups without any unit (all their channels empty) store +0
     for (int gi = 0; gi < (int)gl.size(); gi++)
-      if (alls[gi].empty()) store_group(gl[gi], touched);
+      if (!stored[gi]) store_group(gl[gi], touched);
     E.line("s_endpgm");
     p.sec_valu = std::max(p.sec_valu, E.valu - v0);
   }
@@ -1074,7 +1112,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     *err = "baked kernel code too large";
     return false;
   }
-  finish_kernel(E, p, nv, T, src);
+  finish_kernel(E, p, nv, W, src);
   return true;
 }
 

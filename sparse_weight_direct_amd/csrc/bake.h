@@ -64,6 +64,8 @@ struct BakePlan {
   int seq = 0;               // 1: each workgroup runs every group in turn (the stores of one
                              // group overlap the next group's copies and FMAs); 0: one group
                              // per workgroup
+  int gw = 0;                // 1: the workgroup holds every group's wavefronts (T tiles x G
+                             // groups), which share the staged window
   int pairdist = 0;          // 1: wave w stages block w % nblk of every (T / nblk)-th channel
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
@@ -71,7 +73,7 @@ struct BakePlan {
   long long sec_steps = 0;   // load steps of the longest section
   long long sec_loads = 0;   // row loads of the section with the most
   std::vector<std::vector<int>> rows;  // output channels of each group
-  int wpb() const { return Q * T; }
+  int wpb() const { return stage && gw ? T * G : Q * T; }
 };
 
 // Kernel arguments, in the order of the kernel's argument segment (40 bytes).
@@ -85,14 +87,14 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=.." (tuning and
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=..,GW=.." (tuning and
 // tests only); fields left at -1 are chosen by the packer.
 struct BakeForce {
   int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1, cb = -1,
-      seq = -1;
+      seq = -1, gw = -1;
   bool any() const {
     return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0 ||
-           cb >= 0 || seq >= 0;
+           cb >= 0 || seq >= 0 || gw >= 0;
   }
 };
 BakeForce bake_force_from_env();

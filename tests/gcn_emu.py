@@ -74,6 +74,7 @@ class Wave:
         self.lds_pend = lds_pend  # per LDS word: an LDS DMA into it is not yet retired (vmcnt)
         self.m0 = None
         self.m0_wr = -100  # instruction count at the last write of m0
+        self.barriers = 0  # s_barrier instructions executed
         self.lgkm = []  # per outstanding LDS instruction (oldest first): the VGPRs it writes
         self.s = np.zeros(110, np.uint64)  # scalar registers (kept as u32 values)
         self.v = np.zeros((256, 64), np.uint32)
@@ -195,6 +196,7 @@ class Wave:
             elif op == "s_barrier":
                 if self.lgkm:
                     raise EmuError("s_barrier with LDS reads outstanding")
+                self.barriers += 1
                 yield "barrier"
             elif op in ("ds_write_b128", "ds_read_b128"):
                 if self.lds is None:
@@ -468,13 +470,13 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
     N = x.shape[0]
     V, Pb, G = info["bake_valid_lanes"], info["bake_pitch"], info["bake_groups"]
     Q, T = info["bake_splits"], info["bake_units_per_wg"]
-    WPB = Q * T
+    WPB = Q * T * (G if info.get("bake_shared_window") else 1)
     if info.get("bake_stage"):
         # staged kernels: positions of the padded layout (H + 2 pad rows of Pb words per image),
         # ntiles = workgroups of T tiles of 64 per group
         qtot = N * (info["H"] + 2 * info["pad"]) * Pb
         ntiles = (qtot + 64 * T - 1) // (64 * T)
-        per_xcd = (ntiles * (1 if info.get("bake_sequential") else G) + 7) // 8
+        per_xcd = (ntiles * (1 if info.get("bake_sequential") or info.get("bake_shared_window") else G) + 7) // 8
     else:
         qtot = N * E * Pb
         ntiles = (qtot + V - 1) // V
@@ -503,6 +505,12 @@ def run_baked(src: str, info: dict, x: np.ndarray, M: int, E: int, F: int):
                 except StopIteration:
                     pass
             live = at_barrier
+        if len(set(w.barriers for w in waves if w.barriers)) > 1:
+            # a workgroup barrier counts arrivals, not code positions: waves that pass a
+            # different number of them would synchronise with the wrong partner barrier (waves
+            # that end before any barrier, e.g. units past the last tile, take no part)
+            raise EmuError(f"workgroup {b}: waves passed different numbers of barriers "
+                           f"{[w.barriers for w in waves]}")
         for wave in waves:
             for bi, idx, vals in wave.stores:
                 assert bi == 1, "store into the input"

@@ -175,7 +175,8 @@ STAGED_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
     (2, 7, 17, 19, 13, 3, 3, 1, 1, 0.0, 47),   # no non-zero at all: +0 everywhere
 ]
 STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2,CB=0",
-               "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2", "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0"]
+               "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2", "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0", "GW=1,G=2",
+               "GW=1,G=5,T=3,CC=3", "GW=1,G=4,CB=0,NB=3"]
 
 
 @pytest.mark.parametrize("env", STAGED_ENVS)
@@ -191,7 +192,9 @@ def test_staged_kernels(c, env, monkeypatch):
     taps read as one batch (pairs by ds_read2_b32 from a per-channel base register; the
     default where the filter's reach allows), CB=0 one step's taps per batch, SEQ=1 every
     workgroup runs all G groups in turn (the DMA pipeline continues across groups, each
-    group's stores follow its last chunk)."""
+    group's stores follow its last chunk), GW=1 a workgroup holds the wavefronts of all G groups
+    for its T tiles, which stage one window together (every section passes every chunk, so all
+    wavefronts pass the same barriers, which the emulator checks)."""
     d = workloads.make_custom(*c)
     y, info = _check(d, c[7], c[8], env, env, monkeypatch)
     assert info["bake_stage"] == 1 and info["bake_valid_lanes"] == 64
