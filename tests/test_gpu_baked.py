@@ -210,3 +210,23 @@ def test_staged_full_size(name, monkeypatch):
     y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
     assert h.info()["bake_stage"] == 1 and h.launch_info(L.N)["mapping"] == sc.MAPPING_BAKED
     assert_layer_parity(name, y, f"{name} staged")
+
+
+def test_staged_kernel_input_not_16_byte_aligned():
+    """The staged kernel copies 16 bytes a lane and needs a 16-byte aligned input; an input 4 bytes
+    off falls back to the first kernel that reads rows directly, with the same result."""
+    d = workloads.make("imb99")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"])
+    assert h.launch_info(L.N)["stage"] == 1
+    x = torch.from_numpy(d["x"]).cuda()
+    xa = torch.empty(x.numel() + 4, device="cuda")[1:1 + x.numel()].view(x.shape)
+    xa.copy_(x)
+    assert xa.data_ptr() % 16 == 4
+    ya = torch.full((L.N, L.M, L.E, L.F), float("nan"), device="cuda")
+    y = torch.full_like(ya, float("nan"))
+    h.forward(x, y)
+    h.forward(xa, ya)
+    torch.cuda.synchronize()
+    assert_layer_parity("imb99", ya.cpu().numpy(), "imb99 unaligned input")
+    assert_layer_parity("imb99", y.cpu().numpy(), "imb99 aligned input")
