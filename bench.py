@@ -238,13 +238,21 @@ def main():
         eager_ms, _ = run(lambda i: chain.run(), args.steps, args.warmup, 1)
         chain.capture()
         graph_ms, _ = run(lambda i: chain.replay(), args.steps, args.warmup, 1)
+        # the same stack 20 times per graph launch: its time on the GPU, without the host's cost
+        # of launching a graph (which bounds one small stack per launch)
+        rep = 20
+        chain.capture(repeat=rep)
+        gpu_ms, _ = run(lambda i: chain.replay(), max(10, args.steps // rep), 2, 1)
+        gpu_ms /= rep
         cflops = sum(roofline.effective_flops(int(cd["mask"].sum()), cd["x"].shape[0] if j == 0 else chain.N,
                                               chain.handles[j].E, chain.handles[j].F)
                      for j, cd in enumerate(layers))
         extra["chain"] = {"name": args.chain, "layers": len(layers), "eager_us": round(eager_ms * 1e3, 2),
                           "graph_us": round(graph_ms * 1e3, 2),
-                          "graph_tflops": round(cflops / (graph_ms * 1e-3) / 1e12, 3)}
-        log(f"[bench] chain {args.chain}: eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3:.1f} us per stack")
+                          "graph_tflops": round(cflops / (graph_ms * 1e-3) / 1e12, 3),
+                          "gpu_us_20_stacks_per_graph": round(gpu_ms * 1e3, 2)}
+        log(f"[bench] chain {args.chain}: eager {eager_ms * 1e3:.1f} us, graph {graph_ms * 1e3:.1f} us per stack, "
+            f"{gpu_ms * 1e3:.1f} us per stack with 20 stacks per graph launch")
 
     if args.copy_mb > 0:
         nb = args.copy_mb << 20

@@ -40,8 +40,13 @@ class LayerChain:
             src = out
         return self.outs[-1]
 
-    def capture(self):
-        """Capture run() into a graph (on a side stream, as torch requires)."""
+    def capture(self, repeat: int = 1):
+        """Capture run() into a graph (on a side stream, as torch requires).  With repeat > 1
+        the graph runs the stack that many times in a row (the same input each time): one
+        graph launch per `repeat` stacks, for measuring the stack's time on the GPU apart from
+        the host's cost of launching the graph."""
+        if repeat < 1:
+            raise ValueError("repeat must be >= 1")
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -50,7 +55,8 @@ class LayerChain:
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            self.run()
+            for _ in range(repeat):
+                self.run()
         return self.graph
 
     def replay(self):

@@ -43,12 +43,15 @@ def test_chain_each_layer_matches_oracle(name):
         src = y  # the next layer's oracle input is this layer's GPU output
 
 
+@pytest.mark.parametrize("repeat", [1, 3])
 @pytest.mark.parametrize("name", list(workloads.CHAINS))
-def test_chain_graph_replays_equal_eager(name):
+def test_chain_graph_replays_equal_eager(name, repeat):
+    """repeat > 1: the graph runs the stack several times on the same input; the last output
+    is still the eager one."""
     _, ch = _chain(name)
     eager = ch.run().clone()
     torch.cuda.synchronize()
-    ch.capture()
+    ch.capture(repeat=repeat)
     other = torch.randn(1 << 20, device="cuda")
     for rep in range(4):
         for o in ch.outs:
