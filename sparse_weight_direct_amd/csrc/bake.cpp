@@ -741,7 +741,8 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   E.rfl_guard(vTmp);
   E.v(-1, 8, fmt("v_readfirstlane_b32 s14, v%d", vTmp));
   E.line("s_waitcnt lgkmcnt(0)");
-  // logical workgroup -> (group s16, block of T tiles s15); s25 = blocks per group
+  // logical workgroup -> (group s16, block of T tiles s15); s25 = blocks per group (with
+  // sequential groups or a shared window every workgroup covers all groups)
   E.line("s_and_b32 s15, s2, 7");
   E.line("s_mul_i32 s15, s15, s29");
   E.line("s_lshr_b32 s16, s2, 3");

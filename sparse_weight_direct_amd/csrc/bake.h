@@ -49,13 +49,14 @@ struct BakePlan {
   int maxsq = 0;    // largest lane shift (S-1)/st (0 without DPP)
   int Mg = 0;       // accumulators per wavefront (largest group, padded to 4 when Q > 1)
   int vgprs = 0, sgprs = 0;
-  int lds_bytes = 0;         // partial sums of the channel splits
+  int lds_bytes = 0;         // LDS per workgroup: partial sums of the channel splits, or the
+                             // staged chunk buffers
   int rc = 0;                // channels per round of the split reduction (LDS per split: rc/4 KB)
-  // staged plans (stride 1): the workgroup's T wavefronts cover T*64 consecutive positions of
-  // the padded layout (V = 64, pitch Pb = the layout's row pitch); per chunk of Cc channels each
-  // channel's window (chs words) is copied into LDS once by LDS DMA (bw words per instruction)
-  // into one of nbuf chunk buffers, nbuf - 1 chunks ahead of the FMAs, and every tap is a
-  // ds_read_b32 at an immediate offset
+  // staged plans (stride 1): a workgroup's T tiles of 64 lanes cover T*64 consecutive positions
+  // of the padded layout (V = 64, pitch Pb = the layout's row pitch); per chunk of Cc channels
+  // each channel's window (chs words) is copied into LDS once by LDS DMA (bw words per
+  // instruction) into one of nbuf chunk buffers, nbuf - 1 chunks ahead of the FMAs, and every
+  // tap is read from LDS at an immediate offset
   int stage = 0;
   int Cc = 0, chs = 0, bw = 0, nblk = 0, nbuf = 2;
   int ra = 1;                // batches of tap reads issued ahead of the FMAs
@@ -66,7 +67,8 @@ struct BakePlan {
                              // per workgroup
   int gw = 0;                // 1: the workgroup holds every group's wavefronts (T tiles x G
                              // groups), which share the staged window
-  int pairdist = 0;          // 1: wave w stages block w % nblk of every (T / nblk)-th channel
+  int pairdist = 0;          // 1: of the W = wpb() wavefronts that share a window, wave w
+                             // stages block w % nblk of every (W / nblk)-th channel
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
   long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)

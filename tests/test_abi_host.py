@@ -349,3 +349,25 @@ def test_tune_checks_arguments_before_any_device_work():
     assert st == sc.SC_EINVAL
     st, _ = _status(lambda: sc.sparseconv_tune(h.ptr, fake, fake + (1 << 30), 0, *args, reps=3, stream=0))
     assert st == sc.SC_ESHAPE
+
+
+def test_launch_rule_for_the_large_layers():
+    """Which weights-in-code kernel a forward launches (host-only handles assume 256 compute
+    units): where the staged kernels give every SIMD a wavefront they are launched, the one
+    whose workgroups share their window between two groups on layers with at least 64
+    non-zeros per output channel, the one-group one below; a batch of one image leaves SIMDs
+    idle and launches an unstaged kernel."""
+    seen = {}
+    for name in ("imb95", "imb90"):
+        d = workloads.make(name)
+        L = d["layer"]
+        h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                      flags=sc.SC_PACK_HOST_ONLY)
+        nnz_per_channel = h.info()["nnz"] / L.M
+        big = h.launch_info(L.N)
+        assert big["stage"] == 1 and big["waves"] >= 4 * 256
+        assert (big["groups"] == 2 and big["block"] == 512) == (nnz_per_channel >= 64), (name, big)
+        small = h.launch_info(1)
+        assert small["stage"] == 0, (name, small)
+        seen[name] = big["groups"]
+    assert seen == {"imb95": 1, "imb90": 2}
