@@ -59,6 +59,9 @@ BakeForce bake_force_from_env() {
   f.cb = env_key(e, "CB", -1);
   f.seq = env_key(e, "SEQ", -1);
   f.gw = env_key(e, "GW", -1);
+  f.c0 = env_key(e, "C0", -1);
+  f.es = env_key(e, "ES", -2);
+  f.esnt = env_key(e, "ESNT", -1);
   return f;
 }
 
@@ -73,6 +76,13 @@ constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
 constexpr int kReduceChannels = 32;  // channels per round of the channel-split reduction
 constexpr int kStagedChunk = 12;     // channels per staged chunk (fewer barriers than 8: ~1 us
                                      // faster on the 112x112 layers; 16 no faster)
+constexpr int kStagedFirst = 0;      // channels of the first staged chunk (0: a full chunk)
+constexpr int kStagedEarly = 0;      // units from the end at which the stores of output channels
+                                     // that are already final start (0: all stores after the walk;
+                                     // -1: at once).  Measured on the 112x112 layers: early stores
+                                     // (with ORD=1) save 1.5-2 us when the input comes from the
+                                     // Infinity Cache, but cost 1-2.5 us on inputs read from HBM,
+                                     // where the writes slow the concurrent input copies
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
 // the other columns), or every column when lane shifts are off.
@@ -155,11 +165,55 @@ std::vector<std::vector<int>> deal_rows(int M, int G, const std::vector<int32_t>
   return rows;
 }
 
-// Sorted non-zeros of each group.
+// The order in which every weights-in-code kernel of a layer walks the input channels
+// (rank[c] = position of channel c in the walk); all plans of a layer share it, so every plan
+// adds each output's products in the same order.  Ascending by default.  With ORD=1 (tuning
+// option, for early stores): an output channel's result is final after the last input channel
+// it has a non-zero in, and from then on its store can overlap the rest of the walk, so the
+// walk greedily completes the output channel with the fewest input channels still to walk,
+// taking that channel's remaining input channels in ascending order; input channels without
+// any non-zero come last.  Measured on the 112x112 layers: on inputs read from HBM the
+// ascending order is ~0.6 us faster (the copies then read neighbouring channel planes).
+std::vector<int> channel_rank(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col) {
+  const int RS = g.R * g.S;
+  if (env_key(std::getenv("SPARSECONV_BAKE"), "ORD", 0) != 1) {
+    std::vector<int> id(g.C);
+    std::iota(id.begin(), id.end(), 0);
+    return id;
+  }
+  std::vector<std::vector<int>> sup(g.M), users(g.C);
+  for (int m = 0; m < g.M; m++) {
+    for (int j = rowptr[m]; j < rowptr[m + 1]; j++) sup[m].push_back(col[j] / RS);
+    std::sort(sup[m].begin(), sup[m].end());
+    sup[m].erase(std::unique(sup[m].begin(), sup[m].end()), sup[m].end());
+    for (int c : sup[m]) users[c].push_back(m);
+  }
+  std::vector<int> remaining(g.M), rank(g.C, -1);
+  for (int m = 0; m < g.M; m++) remaining[m] = (int)sup[m].size();
+  int next = 0;
+  for (;;) {
+    int best = -1;
+    for (int m = 0; m < g.M; m++)
+      if (remaining[m] > 0 && (best < 0 || remaining[m] < remaining[best])) best = m;
+    if (best < 0) break;
+    for (int c : sup[best]) {
+      if (rank[c] >= 0) continue;
+      rank[c] = next++;
+      for (int m : users[c]) remaining[m]--;
+    }
+  }
+  for (int c = 0; c < g.C; c++)
+    if (rank[c] < 0) rank[c] = next++;
+  return rank;
+}
+
+// Sorted non-zeros of each group: by input channel in the walk's order (channel_rank), then
+// filter row, lane shift, phase and output channel.
 std::vector<std::vector<Nz>> group_nonzeros(const Geom& g, int dpp, const std::vector<std::vector<int>>& rows,
                                             const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                                             const std::vector<float>* val) {
   const int RS = g.R * g.S;
+  const std::vector<int> rank = channel_rank(g, rowptr, col);
   std::vector<int> group_of(g.M, -1);
   for (size_t q = 0; q < rows.size(); q++)
     for (int m : rows[q]) group_of[m] = (int)q;
@@ -178,8 +232,8 @@ std::vector<std::vector<Nz>> group_nonzeros(const Geom& g, int dpp, const std::v
       nzs[group_of[m]].push_back(z);
     }
   for (auto& L : nzs)
-    std::stable_sort(L.begin(), L.end(), [](const Nz& a, const Nz& b) {
-      if (a.c != b.c) return a.c < b.c;
+    std::stable_sort(L.begin(), L.end(), [&](const Nz& a, const Nz& b) {
+      if (a.c != b.c) return rank[a.c] < rank[b.c];
       if (a.r != b.r) return a.r < b.r;
       if (a.sq != b.sq) return a.sq < b.sq;
       if (a.pv != b.pv) return a.pv < b.pv;
@@ -480,6 +534,9 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     c.seq = G > 1 ? seq : 0;
     c.gw = G > 1 && !c.seq ? gw : 0;
     std::string w;
+    c.c0 = f.c0 >= 0 ? f.c0 : kStagedFirst;
+    c.es = f.es >= -1 ? f.es : kStagedEarly;
+    c.esnt = f.esnt >= 0 ? f.esnt : 0;
     if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, f.cb, &c, &w))
       out.push_back(std::move(c));
     else if (out.empty())
@@ -491,7 +548,8 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     while (n < M && staged_vgprs(g, nvb, (M + n - 1) / n, staged_read_ahead(g, f.ra, cb), cb) > kVgprTarget) n++;
     return n;
   };
-  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0 || f.gw >= 0) {
+  if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0 || f.gw >= 0 || f.c0 >= 0 ||
+      f.es >= -1 || f.esnt >= 0) {
     const int T = f.T > 0 ? f.T : 4;
     add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T, f.seq > 0 ? 1 : 0, f.gw > 0 ? 1 : 0);
     return out;
@@ -676,10 +734,9 @@ void finish_kernel(Emitter& E, BakePlan& p, int nv, int WPB, std::string* src) {
   *src = std::move(E.s);
 }
 
-// LDS DMA instructions of chunk k (channels k*Cc ...) that every wavefront of a staged
-// workgroup issues at least (wavefronts skip the blocks and channels past the chunk's end).
-static int staged_dmas_min(const Geom& g, const BakePlan& p, int k) {
-  const int cn = std::min(p.Cc, g.C - k * p.Cc);
+// LDS DMA instructions of a chunk of cn channels that every wavefront of a staged workgroup
+// issues at least (wavefronts skip the blocks and channels past the chunk's end).
+static int staged_dmas_min(const BakePlan& p, int cn) {
   int best = 1 << 30;
   const int W = p.wpb();  // the wavefronts sharing the window
   for (int w = 0; w < W; w++) {
@@ -725,6 +782,20 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   const long long HW4 = 4ll * g.H * g.W;
   const long long EF4 = 4ll * g.E * g.F;
   const int BUF = p.Cc * p.chs * 4;  // bytes of one chunk buffer
+  // the walk takes the input channels in the layer's order (channel_rank); chunk k holds the
+  // channels of ranks [cstart[k], cstart[k] + csize[k]).  The first chunks are smaller (c0
+  // channels, doubling up to Cc), so the FMAs start once a few channels have arrived.
+  const std::vector<int> rank = channel_rank(g, rowptr, col);
+  std::vector<int> corder(g.C), cstart, csize, chunk_of(g.C);
+  for (int c = 0; c < g.C; c++) corder[rank[c]] = c;
+  for (int c0 = 0, sz = p.c0 > 0 ? std::min(p.c0, p.Cc) : p.Cc; c0 < g.C; c0 += csize.back(), sz = std::min(p.Cc, 2 * sz)) {
+    cstart.push_back(c0);
+    csize.push_back(std::min(sz, g.C - c0));
+    for (int j = c0; j < c0 + csize.back(); j++) chunk_of[j] = (int)cstart.size() - 1;
+  }
+  const int nchunks = (int)cstart.size();
+  bool ascending = true;
+  for (int c = 0; c < g.C; c++) ascending = ascending && rank[c] == c;
 
   Emitter E;
   E.s.reserve((size_t)rowptr[g.M] * 48 + 65536);
@@ -832,7 +903,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   // DMA source offsets: word J = I0 + blk*bw + lane*lw of the window; input (yp - pad,
   // xq - xoff) of image n, out of range in the padding and past the batch
   if (p.pairdist) {
-    // wave w stages block w % nblk of channels w / nblk + i * (W / nblk): s31 = w / nblk
+    // wave w stages block w % nblk of the chunk's slots w / nblk + i * (W / nblk): s31 = w / nblk
     E.line("s_mul_i32 s31, s14, %d", (65536 + p.nblk - 1) / p.nblk);
     E.line("s_lshr_b32 s31, s31, 16");
     E.line("s_mul_i32 s30, s31, %d", p.nblk);
@@ -891,18 +962,19 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   long long fmas = 0;
   int lbl = 0;
   p.sec_valu = 0;
-  // the outputs of group q: +0 for accumulators no FMA touched, one store per output channel
-  // (the accumulators are free again once the stores have read them)
-  auto store_group = [&](int q, std::vector<char>& touched) {
-    const int nrow = (int)p.rows[q].size();
-    for (int k = 0; k < nrow; k++)
+  int nstores = 0;  // stores issued so far in the current section
+  // outputs of group q, slots ks: +0 for accumulators no FMA touched, one store per output
+  // channel (an accumulator is never written again once its store has been issued)
+  auto store_slots = [&](int q, const std::vector<int>& ks, const std::vector<char>& touched, bool early) {
+    for (int k : ks)
       if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
-    for (int k = 0; k < nrow; k++) {
+    const char* pol = early && p.esnt == 1 ? " nt" : early && p.esnt == 2 ? " sc0 sc1" : early && p.esnt == 3 ? " sc1" : "";
+    for (int k : ks) {
       E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[q][k] * EF4);
-      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen", vAcc + k);
+      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen%s", vAcc + k, pol);
       E.code += 16;
     }
-    std::fill(touched.begin(), touched.end(), 0);
+    nstores += (int)ks.size();
   };
   for (int sec = 0; sec < nsec; sec++) {
     if (sec > 0) E.label(".Lsec" + std::to_string(sec));
@@ -923,20 +995,51 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       if (p.gw) {
         // the waves of every group stage the shared window together: every section runs every
         // chunk (empty ones too), so all pass the same copies and barriers
-        for (int k = 0; k * p.Cc < g.C; k++) units.push_back({gi, k, {}});
-        for (int t = 0; t < (int)alls[gi].size(); t++) units[alls[gi][t].c / p.Cc].ts.push_back(t);
+        for (int k = 0; k < nchunks; k++) units.push_back({gi, k, {}});
+        for (int t = 0; t < (int)alls[gi].size(); t++) units[chunk_of[rank[alls[gi][t].c]]].ts.push_back(t);
         continue;
       }
       for (int t = 0; t < (int)alls[gi].size(); t++) {
-        const int k = alls[gi][t].c / p.Cc;
+        const int k = chunk_of[rank[alls[gi][t].c]];
         if (units.empty() || units.back().gi != gi || units.back().k != k) units.push_back({gi, k, {}});
         units.back().ts.push_back(t);
       }
     }
     std::vector<char> touched(p.Mg, 0), stored(gl.size(), 0);
+    nstores = 0;
+    // the unit holding each slot's last FMA (-1: none): an output channel's store is issued at
+    // the start of the group's next unit, so it overlaps the rest of the walk (the channel
+    // order puts many channels' last FMAs early), or after the group's last unit
+    std::vector<std::vector<int>> last_unit(gl.size());
+    for (int gi = 0; gi < (int)gl.size(); gi++) last_unit[gi].assign(p.rows[gl[gi]].size(), -1);
+    for (int ci = 0; ci < (int)units.size(); ci++) {
+      const int gi = units[ci].gi;
+      for (int t : units[ci].ts)
+        for (int i : alls[gi][t].nz) last_unit[gi][slot_of[nzs[gl[gi]][i].m]] = ci;
+    }
+    // with es >= 0 early stores start only at the group's es-th unit from the end (es = 0: all
+    // stores after the group's last unit)
+    std::vector<int> gfirst(gl.size(), -1), glast(gl.size(), -1);
+    for (int ci = 0; ci < (int)units.size(); ci++) {
+      if (gfirst[units[ci].gi] < 0) gfirst[units[ci].gi] = ci;
+      glast[units[ci].gi] = ci;
+    }
+    // the slots of group gi whose stores are issued at the start of unit ci (ci = glast + 1:
+    // after the group's last unit)
+    auto slots_at = [&](int gi, int ci) {
+      const int from = p.es < 0 ? gfirst[gi] : std::max(gfirst[gi], glast[gi] + 1 - p.es);
+      std::vector<int> ks;
+      for (int k = 0; k < (int)last_unit[gi].size(); k++) {
+        const int u = std::max(from, last_unit[gi][k] + 1);  // -1: at the first unit
+        if (u == ci || (ci == glast[gi] + 1 && u > ci)) ks.push_back(k);
+      }
+      return ks;
+    };
     auto stage = [&](int k, int buf) {
-      const int c0 = k * p.Cc, cn = std::min(p.Cc, g.C - c0), boff = buf * BUF;
-      if (p.pairdist) {
+      const int c0 = cstart[k], cn = csize[k], boff = buf * BUF;
+      if (p.pairdist && ascending) {
+        // the wavefronts of part s31 copy slots s31, s31 + per, ... of the chunk: channel
+        // c0 + s31 + i * per, whose scalar offset is s33 = s31 * H*W*4 plus a constant
         const int per = W / p.nblk;
         const int npw = (cn + per - 1) / per;
         for (int i = 0; i < npw; i++) {
@@ -953,6 +1056,24 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
           E.code += 28;
           if (guard) E.label(skip);
         }
+      } else if (p.pairdist) {
+        // the same slots when the walk's order is not ascending: the slots' channels are not
+        // affine in s31, so each part has its own code (a branch per part)
+        const int per = W / p.nblk;
+        for (int part = 0; part < per && part < cn; part++) {
+          const std::string skip = ".Ls" + std::to_string(lbl++);
+          if (per > 1) {
+            E.line("s_cmp_eq_u32 s31, %d", part);
+            E.line("s_cbranch_scc0 %s", skip.c_str());
+          }
+          for (int j = part; j < cn; j += per) {
+            E.line("s_add_u32 m0, s32, 0x%x", boff + (j - part) * p.chs * 4);
+            E.line("s_mov_b32 s12, 0x%llx", (long long)corder[c0 + j] * HW4);  // m0's wait state
+            E.line("%s v%d, s[4:7], s12 offen lds", dma, vB);
+            E.code += 28;
+          }
+          if (per > 1) E.label(skip);
+        }
       } else {
         for (int c = 0; c < cn; c++)
           for (int k2 = 0; k2 < nvb; k2++) {
@@ -965,7 +1086,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
             }
             E.line("s_mul_i32 s18, s17, %d", p.bw * 4);
             E.line("s_add_u32 m0, s18, 0x%x", boff + c * p.chs * 4);
-            E.line("s_mov_b32 s12, 0x%llx", (long long)(c0 + c) * HW4);  // m0's wait state
+            E.line("s_mov_b32 s12, 0x%llx", (long long)corder[c0 + c] * HW4);  // m0's wait state
             E.line("%s v%d, s[4:7], s12 offen lds", dma, vB + k2);
             E.code += 32;
             if (guard) E.label(skip);
@@ -992,7 +1113,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       int n = 0;
       if (p.cb) {
         const int c = all[bt.steps[0]].c;
-        E.v(vBase + set, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + set, boff + (c - c0) * p.chs * 4));
+        E.v(vBase + set, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + set, boff + (rank[c] - c0) * p.chs * 4));
         const int base = vRd + set * SETW;
         const size_t nt = bt.taps.size();
         for (size_t i = 0; i < nt; i += 2) {
@@ -1014,7 +1135,7 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       for (int i : st.nz) used[L[i].sq] = 1;
       for (int sidx = 0; sidx < S; sidx++) {
         if (!used[sidx]) continue;
-        const int off = boff + (st.c - c0) * p.chs * 4 + (st.r * g.Pp + sidx) * 4;
+        const int off = boff + (rank[st.c] - c0) * p.chs * 4 + (st.r * g.Pp + sidx) * 4;
         E.line("ds_read_b32 v%d, v5 offset:%d", vRd + set * SETW + sidx, off);
         E.code += 8;
         n++;
@@ -1025,28 +1146,37 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     // i - nbuf read before the barrier that precedes its staging
     const int nch = (int)units.size(), P = p.nbuf - 1;
     int issued = 0;
+    std::vector<int> stores_at(nch, 0);  // stores issued before unit j's chunk was staged
     auto wait_for = [&](int k) {
-      // unit k's chunk is in LDS once this wavefront's DMAs of it are done (loads retire in
-      // order, so at most the DMAs issued after them may still be outstanding: the fewest
-      // any wavefront issues for the later units; stores in between are not counted, which
-      // only makes the wait safe whatever their order) and every wavefront has passed the
-      // barrier
-      int later = 0;
-      for (int j = k + 1; j < issued; j++) later += staged_dmas_min(g, p, units[j].k);
+      // unit k's chunk is in LDS once this wavefront's DMAs of it are done and every wavefront
+      // has passed the barrier.  Buffer loads (LDS DMA included) and stores report completion
+      // in the order they were issued, so at most the operations issued after them may still
+      // be outstanding: the DMAs of later units (the fewest any wavefront issues) and the
+      // stores issued since (every wavefront of a section issues the same stores)
+      int later = nstores - stores_at[k];
+      for (int j = k + 1; j < issued; j++) later += staged_dmas_min(p, csize[units[j].k]);
       E.line("s_waitcnt vmcnt(%d)", std::min(later, 63));
       E.line("s_barrier");
     };
-    for (; issued < std::min(P, nch); issued++) stage(units[issued].k, issued % p.nbuf);
+    auto stage_unit = [&](int j) {
+      stores_at[j] = nstores;
+      stage(units[j].k, j % p.nbuf);
+    };
+    for (; issued < std::min(P, nch); issued++) stage_unit(issued);
     if (nch > 0) wait_for(0);
     for (int ci = 0; ci < nch; ci++) {
       const int gi = units[ci].gi;
       const std::vector<Step>& all = alls[gi];
       const std::vector<Nz>& L = nzs[gl[gi]];
-      const int boff = (ci % p.nbuf) * BUF, c0 = units[ci].k * p.Cc;
+      const int boff = (ci % p.nbuf) * BUF, c0 = cstart[units[ci].k];
       if (ci + P < nch) {
-        stage(units[ci + P].k, (ci + P) % p.nbuf);
+        stage_unit(ci + P);
         issued++;
       }
+      // stores of the outputs that are already final: channels without a non-zero in the
+      // group (first unit), channels whose last FMA was in the group's previous unit
+      if (ci == gfirst[gi]) std::fill(touched.begin(), touched.end(), 0);
+      store_slots(gl[gi], slots_at(gi, ci), touched, true);
       // the unit's batches
       std::vector<Batch> bts;
       for (int t : units[ci].ts) {
@@ -1095,14 +1225,19 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       }
       const bool last = ci + 1 == nch || units[ci + 1].gi != gi;
       if (last) {
-        store_group(gl[gi], touched);
+        store_slots(gl[gi], slots_at(gi, ci + 1), touched, false);
         stored[gi] = 1;
       }
       if (ci + 1 < nch) wait_for(ci + 1);
     }
     // groups without any unit (all their channels empty) store +0
     for (int gi = 0; gi < (int)gl.size(); gi++)
-      if (!stored[gi]) store_group(gl[gi], touched);
+      if (!stored[gi]) {
+        std::fill(touched.begin(), touched.end(), 0);
+        std::vector<int> ks(p.rows[gl[gi]].size());
+        std::iota(ks.begin(), ks.end(), 0);
+        store_slots(gl[gi], ks, touched, false);
+      }
     E.line("s_endpgm");
     p.sec_valu = std::max(p.sec_valu, E.valu - v0);
   }

@@ -69,6 +69,11 @@ struct BakePlan {
                              // groups), which share the staged window
   int pairdist = 0;          // 1: of the W = wpb() wavefronts that share a window, wave w
                              // stages block w % nblk of every (W / nblk)-th channel
+  int c0 = 0;                // channels of the first chunk (0: Cc); later chunks double up to Cc
+  int es = 0;                // early stores: an output channel whose last FMA is in unit u is
+                             // stored at the start of unit u + 1 (-1), or not before the group's
+                             // es-th unit from the end (es >= 0; 0: after the last unit)
+  int esnt = 0;              // cache policy of the early stores: 0 default, 1 nt, 2 sc0 sc1, 3 sc1
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
   long long code_bytes = 0;  // size of the generated instruction stream
   long long sec_valu = 0;    // VALU instructions of the longest section (FMAs, shifts, reduction)
@@ -89,14 +94,14 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=..,GW=.." (tuning and
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=..,GW=..,C0=..,ES=..,ESNT=..,ORD=.." (tuning and
 // tests only); fields left at -1 are chosen by the packer.
 struct BakeForce {
   int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1, cb = -1,
-      seq = -1, gw = -1;
+      seq = -1, gw = -1, c0 = -1, es = -2, esnt = -1;
   bool any() const {
     return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0 ||
-           cb >= 0 || seq >= 0 || gw >= 0;
+           cb >= 0 || seq >= 0 || gw >= 0 || c0 >= 0 || es >= -1 || esnt >= 0;
   }
 };
 BakeForce bake_force_from_env();

@@ -10,8 +10,11 @@ else, and it checks the rules the hardware does not check for the code:
     of a load into it, v_readfirstlane of a VGPR one after a VALU write of it, and a VALU
     read of VCC two after a VALU write of VCC;
   * a VGPR that an outstanding buffer load will write may not be read or written before an
-    s_waitcnt vmcnt has retired that load (loads retire in order), and likewise a VGPR an
-    outstanding LDS instruction (ds_read, ds_bpermute) will write before s_waitcnt lgkmcnt;
+    s_waitcnt vmcnt has retired that load (buffer loads and stores, LDS DMA included, report
+    completion in the order they were issued, so vmcnt(n) retires the oldest until n remain;
+    issuing a 64th outstanding operation waits for the oldest, as the hardware stalls the
+    issue at the counter's limit), and likewise a VGPR an outstanding LDS instruction
+    (ds_read, ds_bpermute) will write before s_waitcnt lgkmcnt;
   * only VGPRs below the kernel's declared count are used;
   * every output element is stored at most once per launch.
 
@@ -87,7 +90,8 @@ class Wave:
         self.valu = 0
         self.wr = np.full(256, -100, np.int64)
         self.vcc_wr = -100
-        self.pending = []  # VGPRs of outstanding loads, oldest first
+        self.pending = []  # outstanding vector memory operations, oldest first: a load's VGPR,
+                           # ("lds", words) for an LDS DMA, ("store", None) for a store
         self.stores = []   # (buffer index, element indices, values)
 
     # ---- operands ----
@@ -161,6 +165,16 @@ class Wave:
                 return i, arr
         raise EmuError(f"descriptor base {addr:#x} is no known buffer")
 
+    def _retire(self, q):
+        e = q.pop(0)
+        if isinstance(e, tuple) and e[0] == "lds":  # an LDS DMA: its words are now written
+            self.lds_pend[e[1]] = False
+
+    def _issue_vmem(self, e):
+        if len(self.pending) >= 63:  # the counter is full: the issue waits for the oldest
+            self._retire(self.pending)
+        self.pending.append(e)
+
     # ---- execution (a generator: yields at s_barrier) ----
     def run(self, max_steps=10_000_000):
         pc = 0
@@ -190,9 +204,7 @@ class Wave:
                 keep = int(m.group(2))
                 q = self.pending if m.group(1) == "vmcnt" else self.lgkm
                 while len(q) > keep:
-                    e = q.pop(0)
-                    if isinstance(e, tuple):  # an LDS DMA: its words are now written
-                        self.lds_pend[e[1]] = False
+                    self._retire(q)
             elif op == "s_barrier":
                 if self.lgkm:
                     raise EmuError("s_barrier with LDS reads outstanding")
@@ -424,12 +436,13 @@ class Wave:
                 dst = base // 4 + np.arange(64 * lw)
                 self.lds[dst] = words
                 self.lds_pend[dst] = True
-                self.pending.append(("lds", dst))
-                if len(self.pending) > 63:
-                    raise EmuError("more than 63 loads outstanding")
+                self._issue_vmem(("lds", dst))
             elif op == "buffer_load_dword" or op == "buffer_store_dword":
                 so, _, mods = a[3].partition(" ")
-                if mods != "offen":
+                mods = mods.split()
+                # stores may carry a cache policy (nt, sc0, sc1): it does not change the result
+                if mods[:1] != ["offen"] or (op == "buffer_load_dword" and len(mods) > 1) or \
+                        any(m not in ("nt", "sc0", "sc1") for m in mods[1:]):
                     raise EmuError("buffer access other than offen")
                 addr, nrec = self.rsrc(a[2])
                 bi, arr = self.buffer(addr)
@@ -450,12 +463,11 @@ class Wave:
                     vals[inb] = arr[idx]
                     self.v[d] = vals
                     self.wr[d] = self.valu  # the DPP rule counts from the load's issue
-                    self.pending.append(d)
-                    if len(self.pending) > 63:
-                        raise EmuError("more than 63 loads outstanding")
+                    self._issue_vmem(d)
                 else:
                     d = self.vreg(a[0])
                     self.stores.append((bi, idx, self.v[d][inb].copy()))
+                    self._issue_vmem(("store", None))
             else:
                 raise EmuError(f"instruction not emulated: {op} {a}")
 

@@ -176,7 +176,8 @@ STAGED_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
 ]
 STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2,CB=0",
                "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2", "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0", "GW=1,G=2",
-               "GW=1,G=5,T=3,CC=3", "GW=1,G=4,CB=0,NB=3"]
+               "GW=1,G=5,T=3,CC=3", "GW=1,G=4,CB=0,NB=3", "C0=1", "C0=2,CC=5,NB=3", "GW=1,G=2,C0=1,CC=4", "ES=-1,ORD=1", "ES=2,ESNT=1,CC=3,ORD=1",
+               "SEQ=1,G=2,ES=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3"]
 
 
 @pytest.mark.parametrize("env", STAGED_ENVS)
@@ -194,13 +195,23 @@ def test_staged_kernels(c, env, monkeypatch):
     workgroup runs all G groups in turn (the DMA pipeline continues across groups, each
     group's stores follow its last chunk), GW=1 a workgroup holds the wavefronts of all G groups
     for its T tiles, which stage one window together (every section passes every chunk, so all
-    wavefronts pass the same barriers, which the emulator checks)."""
+    wavefronts pass the same barriers, which the emulator checks), C0 channels in the first
+    chunk (later chunks double up to CC), ES the unit from the end at which the stores of
+    output channels that are already final start (-1: at once; 0, the default: all stores
+    after the walk), ESNT their cache policy, ORD=1 the walk's channel order that completes
+    output channels early (every plan of the handle, the default plan too, takes it).  Early
+    stores go out before the walk ends: the emulator checks each output is stored once, and the
+    comparison with the oracle and the default plan shows it was stored after its last FMA; it
+    models vector memory operations completing in issue order, which the waits rely on."""
     d = workloads.make_custom(*c)
     y, info = _check(d, c[7], c[8], env, env, monkeypatch)
     assert info["bake_stage"] == 1 and info["bake_valid_lanes"] == 64
     T = info["bake_units_per_wg"]
     assert info["bake_lds_bytes"] >= 2 * info["bake_chunk_channels"] * (64 * T) * 4
-    monkeypatch.delenv("SPARSECONV_BAKE")
+    if "ORD=1" in env:  # the default plans with the same channel order
+        monkeypatch.setenv("SPARSECONV_BAKE", "ORD=1")
+    else:
+        monkeypatch.delenv("SPARSECONV_BAKE")
     y0, _, info0 = _emulate(d, c[7], c[8])
     assert info0["bake_stage"] == 0
     assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
