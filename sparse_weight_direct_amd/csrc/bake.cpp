@@ -73,6 +73,23 @@ constexpr int kFixedV = 6;      // v0 id, v1 lane, v2 zero, v3 out-of-range mark
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 2ll << 20;  // refuse kernels above 2 MB of code (~250K non-zeros)
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
+constexpr int kSimdVgprs = 512;   // VGPRs per lane of a SIMD (wave64), allocated in blocks of 8
+constexpr int kLdsBytes = 160 * 1024;  // LDS of a CU
+
+// A workgroup runs on one CU: its wavefronts are spread over the 4 SIMDs, so ceil(W / 4) of
+// them share one SIMD's registers, and its LDS must fit the CU's.  A plan that does not fit
+// cannot be dispatched at all.
+bool fits_cu(int waves, int vgprs, int lds, std::string* why) {
+  if ((waves + 3) / 4 * ((vgprs + 7) & ~7) > kSimdVgprs) {
+    *why = "the workgroup's wavefronts need more registers than a CU has";
+    return false;
+  }
+  if (lds > kLdsBytes) {
+    *why = "the workgroup needs more LDS than a CU has";
+    return false;
+  }
+  return true;
+}
 constexpr int kReduceChannels = 32;  // channels per round of the channel-split reduction
 constexpr int kStagedChunk = 12;     // channels per staged chunk (fewer barriers than 8: ~1 us
                                      // faster on the 112x112 layers; 16 no faster)
@@ -82,7 +99,8 @@ constexpr int kStagedEarly = 0;      // units from the end at which the stores o
                                      // -1: at once).  Measured on the 112x112 layers: early stores
                                      // (with ORD=1) save 1.5-2 us when the input comes from the
                                      // Infinity Cache, but cost 1-2.5 us on inputs read from HBM,
-                                     // where the writes slow the concurrent input copies
+                                     // where the writes slow the input copies of the slowest
+                                     // workgroups (even when issued only in the last chunk, ES=1)
 
 // Row vectors of one filter row: the stride phases of the filter columns (lane shifts give
 // the other columns), or every column when lane shifts are off.
@@ -303,10 +321,11 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   // 16-bit LDS offsets of one unit's region
   p.rc = std::min({p.Mg, kReduceChannels, std::max(4, (256 / p.Q) & ~3)});
   p.lds_bytes = p.Q > 1 ? p.T * p.Q * (p.rc / 4) * 1024 : 0;
-  if (p.lds_bytes > 160 * 1024) {
+  if (p.lds_bytes > kLdsBytes) {
     *why = "channel-split partial sums exceed the LDS";
     return false;
   }
+  if (!fits_cu(p.Q * p.T, p.vgprs, p.lds_bytes, why)) return false;
   if (p.Q > 1 && std::min(16, (g.R * P + (D + 1) * P + shift_regs(g, p) - 2) / 4) < p.Q - 1) {
     // a split reads the other Q - 1 parts of a block into registers of the offset, ring and
     // shift region
@@ -345,8 +364,11 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
 // Batches of tap reads a staged kernel issues ahead (a batch is a step, or with channel
 // batches a channel's steps): at most 15 LDS instructions may be outstanding (the lgkm
 // counter), the current batch's and the ra batches ahead.
-inline int staged_batch_reads(const Geom& g, int cb) { return cb ? (g.R * g.S + 1) / 2 : g.S; }
+inline int staged_batch_reads(const Geom& g, int cb) {
+  return cb == 2 ? g.R * g.S : cb ? (g.R * g.S + 1) / 2 : g.S;
+}
 inline int staged_read_ahead(const Geom& g, int forced, int cb) {
+  if (cb == 2) return 1;  // a batch's reads go out once the previous batch's have landed
   const int cap = std::max(1, 15 / staged_batch_reads(g, cb) - 1);
   return std::min(cap, forced > 0 ? forced : 1);  // more measured no faster
 }
@@ -357,6 +379,16 @@ inline bool staged_cb_ok(const Geom& g) {
   return (g.R - 1) * g.Pp + g.S - 1 <= 255 && 2 * staged_batch_reads(g, 1) <= 15;
 }
 
+// Channel-pair batches (cb = 2, a tuning option): one base register per filter tap (r, s)
+// points at that tap in the first channel window of the LDS region; ds_read2st64_b32 reads the
+// tap of two channels of a chunk at once, its 8-bit offsets counting 256 bytes (a channel
+// window is a multiple of 64 words), so the whole region of chunk buffers must lie within
+// 255 * 256 bytes of the bases, and one batch's reads (one per tap) within the lgkm counter.
+// It saves the per-channel base register and half the waits (imb95: 7073 instead of 7313
+// instructions per wavefront) but measured 1 us slower on the 112x112 layers (likely because
+// the two words a lane reads lie a multiple of 64 words apart, in the same LDS bank).
+inline bool staged_cb2_ok(const Geom& g) { return g.R * g.S <= 15; }
+
 // VGPR layout of a staged kernel: v0..v5 fixed, the DMA source offsets, the read sets
 // (even-aligned pairs with channel batches), one base register per set (channel batches),
 // then the accumulators.
@@ -366,10 +398,10 @@ struct StagedRegs {
 inline StagedRegs staged_regs(const Geom& g, int nvb, int ra, int cb) {
   StagedRegs r;
   const int NS = ra + 1;
-  r.setw = cb ? (g.R * g.S + 1) & ~1 : g.S;
+  r.setw = cb == 2 ? 2 * g.R * g.S : cb ? (g.R * g.S + 1) & ~1 : g.S;
   r.rd = cb ? (kFixedV + nvb + 1) & ~1 : kFixedV + nvb;
   r.base = r.rd + NS * r.setw;
-  r.acc = (r.base + (cb ? NS : 0) + 1) & ~1;
+  r.acc = (r.base + (cb == 2 ? g.R * g.S : cb ? NS : 0) + 1) & ~1;
   return r;
 }
 
@@ -395,7 +427,8 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   p.dpp = 1;  // a tap's column s is its lane shift sq: here an LDS offset
   p.perm = 0;
   p.maxsq = g.S - 1;
-  p.cb = cb >= 0 ? (cb > 0 && staged_cb_ok(g)) : staged_cb_ok(g);
+  p.cb = cb == 2 ? (staged_cb2_ok(g) ? 2 : staged_cb_ok(g) ? 1 : 0)
+                 : cb >= 0 ? (cb > 0 && staged_cb_ok(g)) : staged_cb_ok(g);
   p.ra = staged_read_ahead(g, ra, p.cb);
   p.V = 64;
   p.Pb = g.Pp;
@@ -427,6 +460,7 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   // at most 48 DMAs of the chunks ahead outstanding per wavefront (the counter holds 63)
   auto dmas = [&](int cc) { return p.pairdist ? (cc + W / p.nblk - 1) / (W / p.nblk) : cc * nvb; };
   while (p.Cc > 1 && (p.nbuf - 1) * dmas(p.Cc) > 48) p.Cc--;
+  if (p.cb == 2 && p.nbuf * p.Cc * p.chs * 4 > 255 * 256) p.cb = staged_cb_ok(g) ? 1 : 0;
   if ((p.nbuf - 1) * dmas(p.Cc) > 48) {
     *why = "staged window needs too many DMAs per chunk";
     return false;
@@ -443,6 +477,7 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   }
   p.lds_bytes = p.nbuf * p.Cc * p.chs * 4;
   p.rc = 0;
+  if (!fits_cu(W, p.vgprs, p.lds_bytes, why)) return false;
   auto nzs = group_nonzeros(g, p.dpp, p.rows, rowptr, col, nullptr);
   p.sec_valu = p.sec_steps = p.sec_loads = 0;
   long long code = 4096;
@@ -882,6 +917,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   E.line("s_mul_i32 s18, s37, 64");
   E.v(5, 4, "v_add_u32_e32 v5, s18, v1");
   E.v(5, 4, "v_lshlrev_b32_e32 v5, 2, v5");
+  if (p.cb == 2)  // channel-pair batches: the base of tap (r, s) in the region's first window
+    for (int t = 0; t < g.R * S; t++)
+      E.v(vBase + t, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + t, ((t / S) * g.Pp + t % S) * 4));
   decompose(tPos);
   // output offset 4*((n*M*E + yp)*F + f), f = xq - cshift; out of range unless yp < E,
   // f < F (unsigned) and n < N
@@ -965,14 +1003,39 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   int nstores = 0;  // stores issued so far in the current section
   // outputs of group q, slots ks: +0 for accumulators no FMA touched, one store per output
   // channel (an accumulator is never written again once its store has been issued)
+  // After the walk (free: the read sets, no read in flight) the stores address output channel
+  // m = NB*a + j through the VGPR base v4 + j*E*F*4 (vS_j, made in the read-set registers; vS_0
+  // is v4) and the scalar offset NB*a*E*F*4, which changes only with a (channels stored in
+  // ascending order): one instruction per store instead of two.  Lanes off the output keep an
+  // offset past the buffer's range (v4 = 0x80000000 there, and the offsets added stay below
+  // 2^32 because the output is smaller than 2^31 bytes).
+  const int NBASE = std::min(16, NS * SETW + 1);
   auto store_slots = [&](int q, const std::vector<int>& ks, const std::vector<char>& touched, bool early) {
     for (int k : ks)
       if (!touched[k]) E.v(vAcc + k, 4, fmt("v_mov_b32_e32 v%d, 0", vAcc + k));
     const char* pol = early && p.esnt == 1 ? " nt" : early && p.esnt == 2 ? " sc0 sc1" : early && p.esnt == 3 ? " sc1" : "";
-    for (int k : ks) {
-      E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[q][k] * EF4);
-      E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen%s", vAcc + k, pol);
-      E.code += 16;
+    if (early || NBASE < 2 || ks.size() < 8) {
+      for (int k : ks) {
+        E.line("s_mov_b32 s13, 0x%llx", (long long)p.rows[q][k] * EF4);
+        E.line("buffer_store_dword v%d, v4, s[8:11], s13 offen%s", vAcc + k, pol);
+        E.code += 16;
+      }
+    } else {
+      auto vS = [&](int j) { return j == 0 ? 4 : vRd + j - 1; };
+      E.line("s_mov_b32 s13, 0x%llx", (long long)EF4);
+      for (int j = 1; j < NBASE; j++) E.v(vS(j), 4, fmt("v_add_u32_e32 v%d, s13, v%d", vS(j), vS(j - 1)));
+      std::vector<int> order(ks);
+      std::sort(order.begin(), order.end(), [&](int x, int y) { return p.rows[q][x] < p.rows[q][y]; });
+      int cur = -1;
+      for (int k : order) {
+        const int m = p.rows[q][k], a = m / NBASE;
+        if (a != cur) {
+          E.line("s_mov_b32 s13, 0x%llx", (long long)a * NBASE * EF4);
+          cur = a;
+        }
+        E.line("buffer_store_dword v%d, v%d, s[8:11], s13 offen", vAcc + k, vS(m % NBASE));
+        E.code += 8;
+      }
     }
     nstores += (int)ks.size();
   };
@@ -1098,12 +1161,17 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     // column s in register s of the set), or with channel batches all steps of one channel
     // (a base register per set points at the channel's window, and pairs of taps come in
     // one ds_read2_b32, into consecutive registers in the order of the channel's taps)
+    // Channel-pair batches (cb = 2): the steps of two channels a, b of the chunk; per tap used
+    // by either, one ds_read2st64_b32 from the tap's base register reads it for both channels
+    // (offsets: the two windows, in units of 256 bytes) into registers 2i (a) and 2i + 1 (b).
     struct Batch {
       std::vector<int> steps;   // indices into all
       std::vector<int> taps;    // channel batches: used taps r*S + s, in order
       std::vector<int> reg_of;  // channel batches: register slot of tap r*S + s (-1 unused)
+      int ca = -1, cbch = -1;   // channel-pair batches: the two channels (cbch -1: one)
     };
-    auto tapreg = [&](const Batch& bt, int set, int r, int sq) {
+    auto tapreg = [&](const Batch& bt, int set, int r, int sq, int c) {
+      if (p.cb == 2) return vRd + set * SETW + 2 * bt.reg_of[r * S + sq] + (c == bt.ca ? 0 : 1);
       return p.cb ? vRd + set * SETW + bt.reg_of[r * S + sq] : vRd + set * SETW + sq;
     };
     // issue batch bt's reads into read set `set`; returns the LDS instructions issued
@@ -1111,6 +1179,23 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       const std::vector<Step>& all = alls[gi];
       const std::vector<Nz>& L = nzs[gl[gi]];
       int n = 0;
+      if (p.cb == 2) {
+        const int base = vRd + set * SETW;
+        const int wa = boff + (rank[bt.ca] - c0) * p.chs * 4;
+        for (size_t i = 0; i < bt.taps.size(); i++) {
+          const int t = bt.taps[i];
+          if (bt.cbch >= 0) {
+            const int wb = boff + (rank[bt.cbch] - c0) * p.chs * 4;
+            E.line("ds_read2st64_b32 v[%d:%d], v%d offset0:%d offset1:%d", base + 2 * (int)i, base + 2 * (int)i + 1,
+                   vBase + t, wa / 256, wb / 256);
+          } else {
+            E.line("ds_read_b32 v%d, v%d offset:%d", base + 2 * (int)i, vBase + t, wa);
+          }
+          E.code += 8;
+          n++;
+        }
+        return n;
+      }
       if (p.cb) {
         const int c = all[bt.steps[0]].c;
         E.v(vBase + set, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + set, boff + (rank[c] - c0) * p.chs * 4));
@@ -1180,6 +1265,28 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       // the unit's batches
       std::vector<Batch> bts;
       for (int t : units[ci].ts) {
+        const int c = all[t].c;
+        if (p.cb == 2) {
+          // a new batch unless c is one of the current pair's channels or the pair has room
+          const bool fits = !bts.empty() && (bts.back().ca == c || bts.back().cbch == c ||
+                                             bts.back().cbch < 0);
+          if (!fits) {
+            bts.emplace_back();
+            bts.back().reg_of.assign(g.R * S, -1);
+          }
+          Batch& bt = bts.back();
+          if (bt.ca < 0) bt.ca = c;
+          else if (bt.ca != c) bt.cbch = c;
+          bt.steps.push_back(t);
+          std::vector<char> used(S, 0);
+          for (int i : all[t].nz) used[L[i].sq] = 1;
+          for (int sq = 0; sq < S; sq++)
+            if (used[sq] && bt.reg_of[all[t].r * S + sq] < 0) {
+              bt.reg_of[all[t].r * S + sq] = (int)bt.taps.size();
+              bt.taps.push_back(all[t].r * S + sq);
+            }
+          continue;
+        }
         if (!p.cb || bts.empty() || all[bts.back().steps[0]].c != all[t].c) {
           bts.emplace_back();
           if (p.cb) bts.back().reg_of.assign(g.R * S, -1);
@@ -1202,17 +1309,24 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       std::vector<int> nrd(nbt, 0);
       for (int j = 0; j < std::min(p.ra, nbt); j++) nrd[j] = reads(bts[j], gi, j % NS, boff, c0);
       for (int j = 0; j < nbt; j++) {
-        if (j + p.ra < nbt) nrd[j + p.ra] = reads(bts[j + p.ra], gi, (j + p.ra) % NS, boff, c0);
-        int later = 0;
-        for (int k = j + 1; k < std::min(nbt, j + p.ra + 1); k++) later += nrd[k];
-        E.line("s_waitcnt lgkmcnt(%d)", later);
+        if (p.cb == 2) {
+          // batch j's reads have landed before batch j + 1's go out (at most one batch's
+          // reads, one per tap, in flight), which then overlap batch j's FMAs
+          E.line("s_waitcnt lgkmcnt(0)");
+          if (j + 1 < nbt) nrd[j + 1] = reads(bts[j + 1], gi, (j + 1) % NS, boff, c0);
+        } else {
+          if (j + p.ra < nbt) nrd[j + p.ra] = reads(bts[j + p.ra], gi, (j + p.ra) % NS, boff, c0);
+          int later = 0;
+          for (int k = j + 1; k < std::min(nbt, j + p.ra + 1); k++) later += nrd[k];
+          E.line("s_waitcnt lgkmcnt(%d)", later);
+        }
         E.code += 4;
         for (int t : bts[j].steps) {
           const Step& st = all[t];
           for (int i : st.nz) {
             const Nz& z = L[i];
             const int a = vAcc + slot_of[z.m];
-            const int sr = tapreg(bts[j], j % NS, st.r, z.sq);
+            const int sr = tapreg(bts[j], j % NS, st.r, z.sq, st.c);
             if (!touched[slot_of[z.m]]) {
               touched[slot_of[z.m]] = 1;
               E.v(a, 8, fmt("v_fmamk_f32 v%d, v%d, 0x%08x, v2", a, sr, z.bits));

@@ -259,9 +259,10 @@ class Wave:
                 self.lgkm.append([dst])
                 if len(self.lgkm) > 15:
                     raise EmuError("too many LDS instructions outstanding")
-            elif op == "ds_read2_b32":
-                # two dwords per lane at base + 4*offset0 and base + 4*offset1 (8-bit offsets)
-                # into an even-aligned register pair
+            elif op in ("ds_read2_b32", "ds_read2st64_b32"):
+                # two dwords per lane at base + u*offset0 and base + u*offset1 (8-bit offsets;
+                # u = 4 bytes, or 256 bytes for st64) into an even-aligned register pair
+                unit = 4 if op == "ds_read2_b32" else 256
                 if self.lds is None:
                     raise EmuError("LDS access in a kernel without LDS")
                 srcp, _, mods = a[1].partition(" ")
@@ -274,9 +275,9 @@ class Wave:
                 base = self.src_vec(srcp).astype(np.int64)
                 dst = self.vtuple(a[0], 2)
                 for j, key in enumerate(("offset0", "offset1")):
-                    addr = base + 4 * offs.get(key, 0)
+                    addr = base + unit * offs.get(key, 0)
                     if (addr % 4).any() or (addr < 0).any() or (addr + 4 > self.lds.size * 4).any():
-                        raise EmuError("ds_read2_b32 outside the LDS or misaligned")
+                        raise EmuError(f"{op} outside the LDS or misaligned")
                     w = addr // 4
                     if self.lds_pend is not None and self.lds_pend[w].any():
                         raise EmuError("LDS read of words an LDS DMA has not finished writing")

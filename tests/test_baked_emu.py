@@ -177,7 +177,8 @@ STAGED_CASES = [  # N, C, H, W, M, R, S, stride, pad, keep, seed
 STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3,RA=2", "NB=4,CC=3,RA=4,T=2,CB=0",
                "CB=0", "CB=1,RA=2,T=2", "SEQ=1,G=2", "SEQ=1,G=3,T=2,NB=3", "SEQ=1,G=4,CB=0", "GW=1,G=2",
                "GW=1,G=5,T=3,CC=3", "GW=1,G=4,CB=0,NB=3", "C0=1", "C0=2,CC=5,NB=3", "GW=1,G=2,C0=1,CC=4", "ES=-1,ORD=1", "ES=2,ESNT=1,CC=3,ORD=1",
-               "SEQ=1,G=2,ES=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3"]
+               "SEQ=1,G=2,ES=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3", "CB=2", "CB=2,T=2,CC=5",
+               "GW=1,G=2,CB=2", "SEQ=1,G=2,CB=2,CC=3", "CB=2,ES=-1,ORD=1,C0=1"]
 
 
 @pytest.mark.parametrize("env", STAGED_ENVS)
@@ -191,7 +192,9 @@ def test_staged_kernels(c, env, monkeypatch):
     Options: T wavefronts per workgroup, G groups, NB chunk buffers (the DMA runs NB - 1
     chunks ahead), CC channels per chunk, RA batches of tap reads in flight, CB=1 a channel's
     taps read as one batch (pairs by ds_read2_b32 from a per-channel base register; the
-    default where the filter's reach allows), CB=0 one step's taps per batch, SEQ=1 every
+    default where the filter's reach allows), CB=2 two channels' taps per batch (a tap of both
+    channels in one ds_read2st64_b32 from a base register per tap), CB=0 one step's taps per
+    batch, SEQ=1 every
     workgroup runs all G groups in turn (the DMA pipeline continues across groups, each
     group's stores follow its last chunk), GW=1 a workgroup holds the wavefronts of all G groups
     for its T tiles, which stage one window together (every section passes every chunk, so all
@@ -277,3 +280,19 @@ def test_staged_synchronisation_is_checked(drop, monkeypatch):
     except gcn_emu.EmuError:
         return
     assert not oracle.within_tolerance(y, r["y64"], r["mag"], 1e-5).all()
+
+
+@pytest.mark.parametrize("env", ["G=2,Q=8,T=2", "STAGE=1,T=16"])
+def test_plan_that_does_not_fit_a_cu_is_refused(env, monkeypatch):
+    """A workgroup runs on one CU: 16 wavefronts of 168 VGPRs (4 per SIMD) need more than the
+    512 registers a SIMD's lanes have, and 16 staged tiles more LDS than the CU's 160 KB.  The
+    packer refuses such a forced plan (no weights-in-code kernel; the reason is reported)
+    instead of generating a kernel that cannot be dispatched."""
+    monkeypatch.setenv("SPARSECONV_BAKE", env)
+    d = workloads.make("late")
+    L = d["layer"]
+    h = sc.Handle(L.M, L.C, L.R, L.S, L.H, L.W, L.stride, L.pad, values=d["w"], mask=d["mask"],
+                  flags=sc.SC_PACK_HOST_ONLY)
+    assert h.info()["mapping"] != 2
+    with pytest.raises(sc.SparseConvError, match="than a CU has"):
+        h.kernel_source()
