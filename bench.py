@@ -10,8 +10,12 @@ pins the fastest); the forward launches one kernel (on this layer the staged wei
 kernel).
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
-with a device synchronisation on both sides.  Input/output buffer sets rotate so the working
-set exceeds the 256 MB Infinity Cache and every step reads its input from HBM ("cold").
+with a device synchronisation on both sides, one library call per step.  The same K steps
+launched from HIP graphs (24 forwards captured once and replayed, and a graph of the remaining
+steps) are timed too and reported beside them, a check that the host's launch cost does not
+bound the step (--launch graph makes those the timed steps).
+Input/output buffer sets rotate so the working set exceeds the 256 MB Infinity Cache and every
+step reads its input from HBM ("cold").
 
 Printed: one JSON line with effective TFLOP/s (2*nnz*N*E*F per second) as ``value``, the
 roofline of the kernel (bound from the arithmetic intensity against the ridge of 8 TB/s and
@@ -86,6 +90,9 @@ def main():
     ap.add_argument("--no-probes", action="store_true", help="skip the FMA and LDS roof probes")
     ap.add_argument("--no-tune", action="store_true",
                     help="launch the kernels the cost estimate picks instead of tuning each layer first")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="how the timed steps are launched: one library call per step (default) or from HIP "
+                         "graphs of 24 forwards each; the other form is reported beside it")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
     args = ap.parse_args()
@@ -123,6 +130,44 @@ def main():
         total = evs[0].elapsed_time(evs[-1])
         per = [evs[g].elapsed_time(evs[g + 1]) / (bounds[g + 1] - bounds[g]) for g in range(groups)]
         sem = float(np.std(per, ddof=1) / math.sqrt(len(per))) if len(per) > 1 else 0.0
+        return total / steps, sem
+
+    def run_graph(fwd, steps, warmup, nsets, per_graph=24):
+        """ms per step and its SEM when the steps are launched from HIP graphs: per_graph forwards
+        over the rotated buffer sets (forward j on set j % nsets) captured once and replayed, plus a
+        graph of the remaining steps, so exactly ``steps`` forwards run in the timed region."""
+        for i in range(warmup):
+            fwd(i % nsets)
+        torch.cuda.synchronize()
+        per_graph = max(1, min(per_graph, steps))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for j in range(n):
+                    fwd(j % nsets, None)
+            return g
+
+        full, rest = capture(per_graph), (capture(steps % per_graph) if steps % per_graph else None)
+        torch.cuda.synchronize()
+        full.replay()  # untimed: the graph's first launch
+        torch.cuda.synchronize()
+        nrep = steps // per_graph
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 2)]
+        evs[0].record(stream)
+        for r in range(nrep):
+            full.replay()
+            evs[r + 1].record(stream)
+        if rest is not None:
+            rest.replay()
+        evs[-1].record(stream)
+        torch.cuda.synchronize()
+        total = evs[0].elapsed_time(evs[-1])
+        per = [evs[r].elapsed_time(evs[r + 1]) / per_graph for r in range(nrep)]
+        sem = float(np.std(per, ddof=1) / math.sqrt(len(per))) if len(per) > 1 else 0.0
+        del full, rest
         return total / steps, sem
 
     def setup(name):
@@ -189,9 +234,15 @@ def main():
         f"launch {launch}, {nsets} rotated sets ({nsets * set_bytes / 2**20:.0f} MiB)")
 
     log(f"[bench] sparse: warmup {args.warmup}, timed {args.steps}")
-    ms, sem = run(lambda i: h.forward(xs[i], ys[i], stream=stream, workspace=ws), args.steps, args.warmup, nsets)
+    def fwd(i, st=stream):
+        h.forward(xs[i], ys[i], stream=st, workspace=ws)
+
+    ms_eager, sem_eager = run(fwd, args.steps, args.warmup, nsets)
+    ms_graph, sem_graph = run_graph(fwd, args.steps, args.warmup, nsets)
+    ms, sem = (ms_graph, sem_graph) if args.launch == "graph" else (ms_eager, sem_eager)
     m = describe(L, info, ms)
-    log(f"[bench] sparse {ms * 1e3:.2f} us/step (SEM {sem * 1e3:.2f}), {m['tflops']:.2f} TFLOP/s, "
+    log(f"[bench] sparse {ms * 1e3:.2f} us/step (SEM {sem * 1e3:.2f}, launched {args.launch}; eager "
+        f"{ms_eager * 1e3:.2f}, from graphs {ms_graph * 1e3:.2f}), {m['tflops']:.2f} TFLOP/s, "
         f"{m['gbs']:.0f} GB/s algorithmic, AI {m['ai']:.1f}")
 
     extra = {}
@@ -263,6 +314,22 @@ def main():
                                    "gbs_read_plus_write": round(2 * nb / (cms * 1e-3) / 1e9, 1)}
         log(f"[bench] copy of {args.copy_mb} MiB: {2 * nb / (cms * 1e-3) / 1e9:.0f} GB/s (read+write)")
         del src, dst
+        # the same traffic as one forward of the headline layer, in the same form: a device copy
+        # of one input buffer set (read) into an output-sized buffer (written), rotated over the
+        # same sets, launched back to back -- what plain streaming reaches at this size
+        if xs[0].numel() == ys[0].numel():
+            zs = [torch.empty_like(y) for y in ys]  # the forward's outputs stay for the parity check
+            ms_copy, _ = run(lambda i: zs[i].view(-1).copy_(xs[i].view(-1)), args.steps, args.warmup, nsets)
+            del zs
+            same_bytes = xs[0].numel() * 4 + ys[0].numel() * 4
+            extra["copy_same_size"] = {
+                "bytes_read_plus_written": same_bytes, "us": round(ms_copy * 1e3, 2),
+                "gbs": round(same_bytes / (ms_copy * 1e-3) / 1e9, 1),
+                "frac_of_8tbs": round(same_bytes / (ms_copy * 1e-3) / 1e9 / roofline.HBM_PEAK_GBS, 4),
+                "forward_over_copy": round(ms / ms_copy, 3)}
+            log(f"[bench] copy of one input set into an output buffer ({same_bytes / 2**20:.0f} MiB moved): "
+                f"{ms_copy * 1e3:.2f} us, {extra['copy_same_size']['gbs']:.0f} GB/s; the forward takes "
+                f"{ms / ms_copy:.2f}x as long")
 
     if not args.no_probes:
         # roofs of the instruction mixes the kernels are made of (csrc/probes.hip): the fp32 FMA
@@ -277,9 +344,13 @@ def main():
             "fma_tflops": fma, "fma_peak_tflops": roofline.FP32_VECTOR_PEAK_TFLOPS,
             "fma_frac_of_peak": round(best / roofline.FP32_VECTOR_PEAK_TFLOPS, 3),
             "lds_read_tbs": {"b32": round(probes.lds_read_rate(cus, 1), 2), "b128": round(probes.lds_read_rate(cus, 4), 2)},
+            # a pure read stream over the headline layer's input buffer sets (one per launch,
+            # rotated as the forward reads them): the HBM read rate at this size
+            "hbm_read_gbs_input_sets": round(max(probes.read_rate(xs, cus * k) for k in (4, 8, 16)), 1),
             "headline_kernel_lds_bytes_per_workgroup": launch["lds_bytes"],
             "headline_kernel_stages_input_in_lds": bool(launch["stage"])}
-        log(f"[bench] roof probes: FMA {fma} TFLOP/s, LDS {extra['roof_probes']['lds_read_tbs']} TB/s")
+        log(f"[bench] roof probes: FMA {fma} TFLOP/s, LDS {extra['roof_probes']['lds_read_tbs']} TB/s, "
+            f"HBM read {extra['roof_probes']['hbm_read_gbs_input_sets']} GB/s")
 
     # every workload layer, timed the same way (cold, rotated sets), with the launched plan
     if not args.no_configs and not args.layer:
@@ -374,6 +445,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "launch": {"timed_with": args.launch,
+                   "graph": "HIP graphs of 24 forwards each over the rotated buffer sets (one step = one forward)",
+                   "ms_per_step_graph": round(ms_graph, 6), "sem_ms_graph": round(sem_graph, 6),
+                   "ms_per_step_eager": round(ms_eager, 6), "sem_ms_eager": round(sem_eager, 6)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

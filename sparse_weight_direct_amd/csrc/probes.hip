@@ -6,7 +6,8 @@
 //                   only: the fp32 FMA rate of the vector ALUs for a given number of wavefronts
 //                   per SIMD;
 //   scprobe_lds   - wavefronts issuing ds_read_b32 or ds_read_b128 from LDS into registers:
-//                   the LDS read bandwidth.
+//                   the LDS read bandwidth;
+//   scprobe_read  - a grid-stride stream of 16-byte loads: the HBM read rate of pure reads.
 //
 // Each lane writes one float at the end (so nothing is optimised away) to out[global id]; the
 // caller sizes out for blocks * 256 floats.
@@ -86,9 +87,33 @@ __global__ __launch_bounds__(256) void lds_probe(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Streams n4 16-byte vectors through the vector memory path (each thread 4 loads in flight per
+// step of a grid-stride loop) and writes one value per thread: the HBM read rate of a pure
+// read stream.
+__global__ __launch_bounds__(256) void read_probe(const f4* __restrict__ x, long long n4, float* out) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const f4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    acc += a + b + c + d;
+  }
+  for (; i < n4; i += stride) acc += x[i];
+  out[(long long)blockIdx.x * blockDim.x + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads n4 16-byte vectors at x with blocks workgroups of 256 threads; out holds blocks * 256
+// floats.  Returns a hipError_t.
+int scprobe_read(const void* x, long long n4, float* out, int blocks, void* stream) {
+  if (!x || !out || n4 < 1 || blocks < 1) return (int)hipErrorInvalidValue;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(read_probe, dim3(blocks), dim3(256), 0, s, static_cast<const f4*>(x), n4, out);
+  return (int)hipGetLastError();
+}
 
 // kind 0: literal-weight FMAs, 1: VGPR-weight FMAs.  blocks workgroups of 256 threads (4
 // wavefronts; one per SIMD of a CU), iters * 512 FMAs per wavefront.  Returns a hipError_t.

@@ -11,8 +11,9 @@ _LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libscprobe.so")
 
 def _lib():
     lib = ctypes.CDLL(_LIB)
-    for f in (lib.scprobe_fma, lib.scprobe_lds):
+    for f in (lib.scprobe_fma, lib.scprobe_lds, lib.scprobe_read):
         f.restype = ctypes.c_int
+    lib.scprobe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.scprobe_fma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.scprobe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -66,3 +67,24 @@ def lds_read_rate(cus: int, words: int = 4, blocks_per_cu: int = 4, iters: int =
     ms = _time(launch, 5)
     nbytes = 64.0 * iters * blocks * 256 * 4 * words  # 64 reads per iteration per lane
     return nbytes / (ms * 1e-3) / 1e12
+
+
+def read_rate(bufs, blocks: int, reps: int = 20) -> float:
+    """HBM read rate in GB/s of a pure read stream over the device tensors ``bufs`` (one per
+    launch, rotated: each launch reads one whole buffer), blocks workgroups of 256 threads."""
+    import torch
+    lib = _lib()
+    out = torch.empty(blocks * 256, device=bufs[0].device)
+    s = torch.cuda.current_stream().cuda_stream
+    n4 = bufs[0].numel() * bufs[0].element_size() // 16
+    k = [0]
+
+    def launch():
+        b = bufs[k[0] % len(bufs)]
+        k[0] += 1
+        rc = lib.scprobe_read(b.data_ptr(), n4, out.data_ptr(), blocks, s)
+        if rc != 0:
+            raise RuntimeError(f"scprobe_read failed ({rc})")
+
+    ms = _time(launch, reps)
+    return n4 * 16 / (ms * 1e-3) / 1e9
