@@ -62,6 +62,7 @@ BakeForce bake_force_from_env() {
   f.c0 = env_key(e, "C0", -1);
   f.es = env_key(e, "ES", -2);
   f.esnt = env_key(e, "ESNT", -1);
+  f.vt = env_key(e, "VT", -1);
   return f;
 }
 
@@ -300,7 +301,8 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
   for (int pass = 0; pass < 2 && D_forced <= 0; pass++) {
     // deepest ring that keeps the target occupancy (or, past it, fits at all)
     const int cap = std::max(1, 63 / P);
-    const int target = plan_vgprs(g, p, p.Mg, 1) <= kVgprTarget ? kVgprTarget : kMaxVgpr;
+    const int vt = p.vt > 0 ? p.vt : kVgprTarget;
+    const int target = plan_vgprs(g, p, p.Mg, 1) <= vt ? vt : kMaxVgpr;
     D = 1;
     while (D < cap && plan_vgprs(g, p, p.Mg, D + 1) <= target) D++;
     if (!p.perm || D >= 2) break;
@@ -529,9 +531,11 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
   // base groups: the fewest whose accumulators fit the register target (measured on the
   // 112x112 layers, one group per wavefront beats more groups even with several hundred KB of
   // code: more groups repeat the row loads and lane shifts per group)
+  const int vtarget = f.vt > 0 ? std::min(f.vt, kMaxVgpr) : kVgprTarget;
+  p.vt = vtarget;
   auto fewest_groups = [&](const BakePlan& q) {
     int n = 1;
-    while (n < M && plan_vgprs(g, q, (M + n - 1) / n, 2) > kVgprTarget) n++;
+    while (n < M && plan_vgprs(g, q, (M + n - 1) / n, 2) > vtarget) n++;
     return n;
   };
   int G0 = fewest_groups(p);

@@ -201,6 +201,41 @@ def test_staged_plans(layer, env, monkeypatch):
     np.testing.assert_array_equal(y.view(np.uint32), base.view(np.uint32))
 
 
+@pytest.mark.parametrize("layer", [LAYER, WIDE_LAYER], ids=["narrow", "wide"])
+@pytest.mark.parametrize("env", ["C0=1", "C0=2,CC=5,NB=3", "ES=-1,ORD=1", "ES=2,ESNT=1,CC=3,ORD=1",
+                                 "ES=-1,ORD=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3", "SEQ=1,G=2,ES=1,CC=4",
+                                 "CB=2", "GW=1,G=2,CB=2", "CB=2,ES=-1,ORD=1,C0=1"])
+def test_staged_options(layer, env, monkeypatch):
+    """Staged-kernel options: a smaller first chunk (C0), the walk's channel order that completes
+    output channels early (ORD=1, which every plan of the handle takes) with stores issued during
+    the walk (ES, with a cache policy ESNT; the chunk waits then count those stores, relying on
+    vector memory operations completing in issue order), and channel-pair tap batches (CB=2).
+    The same FMAs in the same order as the default plan of the same channel order: bit for bit
+    equal to it, and within tolerance of the oracle."""
+    d = workloads.make_custom(*layer)
+    r = oracle.reference(d["x"], d["w"], d["mask"], 1, 1)
+    monkeypatch.setenv("SPARSECONV_BAKE", "G=1,Q=1,T=4" + (",ORD=1" if "ORD=1" in env else ""))
+    base, _ = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    monkeypatch.setenv("SPARSECONV_BAKE", env)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], 1, 1)
+    assert h.info()["bake_stage"] == 1
+    assert_parity(y, r["y64"], r["mag"], env)
+    np.testing.assert_array_equal(y.view(np.uint32), base.view(np.uint32))
+
+
+@pytest.mark.parametrize("env", ["STAGE=1,ES=-1,ORD=1", "STAGE=1,ES=1,ESNT=1", "STAGE=1,CB=2,C0=4",
+                                 "GW=1,G=2,ES=-1,ORD=1"])
+def test_staged_options_full_size(env, monkeypatch):
+    """Early stores (their waits count the stores in flight), pair batches and a small first
+    chunk on the full-size 112x112 layer at 95% sparsity: every output against the oracle."""
+    d = workloads.make("imb95")
+    L = d["layer"]
+    monkeypatch.setenv("SPARSECONV_BAKE", env)
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert h.info()["bake_stage"] == 1 and h.launch_info(L.N)["mapping"] == sc.MAPPING_BAKED
+    assert_layer_parity("imb95", y, f"imb95 {env}")
+
+
 @pytest.mark.parametrize("name", ["imb95", "imb99", "late", "pw1x1"])
 def test_staged_full_size(name, monkeypatch):
     """A staged kernel on the full-size layers, every output against the oracle."""
