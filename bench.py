@@ -359,8 +359,8 @@ def main():
             if name == layer:
                 continue
             dd, LL, hh, wws, xxs, yys, nn, _ = setup(name)
-            steps = 40
-            cms_, csem = run(lambda i: hh.forward(xxs[i], yys[i], stream=stream, workspace=wws), steps, 5, nn)
+            steps = 400  # enough launches that the first ones after the synchronisation do not weigh
+            cms_, csem = run(lambda i: hh.forward(xxs[i], yys[i], stream=stream, workspace=wws), steps, 20, nn)
             mm = describe(LL, hh.info(), cms_)
             li = hh.launch_info(LL.N)
             gus = graph_us(hh, xxs, yys, nn, wws)
