@@ -653,11 +653,20 @@ std::string fmt(const char* f, ...) {
   return buf;
 }
 
+// The 8-byte instructions of the hot loops (FMAs with a literal weight, LDS and buffer
+// accesses) are placed at 8-byte aligned addresses: a wavefront issues such an instruction
+// markedly slower when it straddles an 8-byte boundary (measured on a stream of literal FMAs:
+// 5.9 against 4.5 cycles with one wavefront per SIMD, 2.9 against 2.3 with two).  The
+// assembler pads with s_nop 0 where a 4-byte instruction (a wait, a barrier) left the
+// stream misaligned.  AL=0 in SPARSECONV_BAKE turns this off (measurement only).
+static bool hot_align() { return env_key(std::getenv("SPARSECONV_BAKE"), "AL", 1) != 0; }
+
 struct Emitter {
   std::string s;
   long long valu = 0;                 // VALU instructions (and nop wait states) issued
   std::vector<long long> wr;          // per VGPR: index of its last VALU write
   long long code = 0;                 // bytes
+  const bool align = hot_align();
   Emitter() : wr(kMaxVgpr, -100) {}
   void line(const char* f, ...) __attribute__((format(printf, 2, 3))) {
     char buf[256];
@@ -665,6 +674,9 @@ struct Emitter {
     va_start(ap, f);
     vsnprintf(buf, sizeof buf, f, ap);
     va_end(ap);
+    if (align && (!std::strncmp(buf, "v_fmac_f32_e32", 14) || !std::strncmp(buf, "v_fmamk_f32", 11) ||
+                  !std::strncmp(buf, "ds_", 3) || !std::strncmp(buf, "buffer_", 7)))
+      s += "\t.p2align 3\n";
     s += '\t';
     s += buf;
     s += '\n';
