@@ -10,12 +10,11 @@ pins the fastest); the forward launches one kernel (on this layer the staged wei
 kernel).
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
-with a device synchronisation on both sides.  The K steps are launched from HIP graphs (up to
-24 forwards captured once, replayed, and a graph of the remaining steps), as a deployment
-launches a fixed layer: after the synchronisation a single graph launch starts the whole
-window, where K separate library calls would leave the GPU waiting on the host for the first
-of them (about 1.5 us per step over 20 steps).  The same K steps launched one call at a time
-are timed too and reported beside them (--launch eager makes those the value).  Both run after
+with a device synchronisation on both sides, one library call per step.  The same K steps
+launched from HIP graphs (up to 24 forwards captured once and replayed, and a graph of the
+remaining steps) are timed too and reported beside them (--launch graph makes those the value);
+the two agree within the run-to-run spread (±1-2 us), so the host's cost per call does not
+bound the step.  Both run after
 the bench's other measurements of the same layer (references, dense baselines, roof probes,
 1000 warm forwards), so the GPU's clock has left its idle state: from idle it rises over the
 first ~30 ms of sustained work, and a window of a few dozen steps right after start-up would
@@ -99,9 +98,9 @@ def main():
     ap.add_argument("--no-probes", action="store_true", help="skip the FMA and LDS roof probes")
     ap.add_argument("--no-tune", action="store_true",
                     help="launch the kernels the cost estimate picks instead of tuning each layer first")
-    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
-                    help="how the timed steps are launched: from HIP graphs of up to 24 forwards each "
-                         "(default) or one library call per step; the other form is reported beside it")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="how the timed steps are launched: one library call per step (default) or from HIP "
+                         "graphs of up to 24 forwards each; the other form is reported beside it")
     ap.add_argument("--copy-mb", type=int, default=1024,
                     help="size of the device-to-device copy timed as the achievable-HBM reference (0: skip)")
     args = ap.parse_args()
