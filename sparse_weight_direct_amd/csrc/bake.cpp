@@ -811,8 +811,10 @@ static int staged_dmas_min(const BakePlan& p, int cn) {
 // wavefront w holds I0 + 64 w + lane.  Per chunk of Cc channels each channel's window
 // [I0, I0 + chs) is copied into LDS once (LDS DMA: lane i writes M0 + 4*i*(bw/64); zero where
 // the source lies in the padding: out-of-range offset) into one of nbuf buffers, nbuf - 1
-// chunks ahead of the FMAs; a step's taps are ds_read_b32 from the lane's base v5 at
-// immediate offsets, issued a step ahead.
+// chunks ahead of the FMAs; a channel's taps are read as one batch (ds_read2_b32 pairs from a
+// per-channel base register), a batch ahead, or a step's by ds_read_b32 from the lane's base
+// v5 at immediate offsets (cb = 0), or two channels' (cb = 2).  After the walk the outputs
+// are stored through VGPR bases (store_slots).
 bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                      const std::vector<float>& val, BakePlan& p, std::string* src, std::string* err) {
   const int T = p.T, S = g.S;
@@ -1274,8 +1276,8 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
         stage_unit(ci + P);
         issued++;
       }
-      // stores of the outputs that are already final: channels without a non-zero in the
-      // group (first unit), channels whose last FMA was in the group's previous unit
+      // with early stores (ES), the stores of outputs already final: channels without a
+      // non-zero in the group, channels whose last FMA was in an earlier unit (slots_at)
       if (ci == gfirst[gi]) std::fill(touched.begin(), touched.end(), 0);
       store_slots(gl[gi], slots_at(gi, ci), touched, true);
       // the unit's batches
