@@ -63,6 +63,7 @@ BakeForce bake_force_from_env() {
   f.es = env_key(e, "ES", -2);
   f.esnt = env_key(e, "ESNT", -1);
   f.vt = env_key(e, "VT", -1);
+  f.pb = env_key(e, "PB", -1);
   return f;
 }
 
@@ -94,6 +95,7 @@ bool fits_cu(int waves, int vgprs, int lds, std::string* why) {
 constexpr int kReduceChannels = 32;  // channels per round of the channel-split reduction
 constexpr int kStagedChunk = 12;     // channels per staged chunk (fewer barriers than 8: ~1 us
                                      // faster on the 112x112 layers; 16 no faster)
+constexpr int kStagedBases = 1;     // fixed per-slot LDS bases (pb): imb95 0.15-0.35 us faster
 constexpr int kStagedFirst = 0;      // channels of the first staged chunk (0: a full chunk)
 constexpr int kStagedEarly = 0;      // units from the end at which the stores of output channels
                                      // that are already final start (0: all stores after the walk;
@@ -392,23 +394,23 @@ inline bool staged_cb_ok(const Geom& g) {
 inline bool staged_cb2_ok(const Geom& g) { return g.R * g.S <= 15; }
 
 // VGPR layout of a staged kernel: v0..v5 fixed, the DMA source offsets, the read sets
-// (even-aligned pairs with channel batches), one base register per set (channel batches),
-// then the accumulators.
+// (even-aligned pairs with channel batches), the base registers (channel batches: one per
+// read set, or npb > 0 fixed ones, one per chunk slot and buffer), then the accumulators.
 struct StagedRegs {
   int setw, rd, base, acc;
 };
-inline StagedRegs staged_regs(const Geom& g, int nvb, int ra, int cb) {
+inline StagedRegs staged_regs(const Geom& g, int nvb, int ra, int cb, int npb = 0) {
   StagedRegs r;
   const int NS = ra + 1;
   r.setw = cb == 2 ? 2 * g.R * g.S : cb ? (g.R * g.S + 1) & ~1 : g.S;
   r.rd = cb ? (kFixedV + nvb + 1) & ~1 : kFixedV + nvb;
   r.base = r.rd + NS * r.setw;
-  r.acc = (r.base + (cb == 2 ? g.R * g.S : cb ? NS : 0) + 1) & ~1;
+  r.acc = (r.base + (cb == 2 ? g.R * g.S : cb ? (npb > 0 ? npb : NS) : 0) + 1) & ~1;
   return r;
 }
 
-inline int staged_vgprs(const Geom& g, int nvb, int Mg, int ra, int cb) {
-  const int acc0 = staged_regs(g, nvb, ra, cb).acc;
+inline int staged_vgprs(const Geom& g, int nvb, int Mg, int ra, int cb, int npb = 0) {
+  const int acc0 = staged_regs(g, nvb, ra, cb, npb).acc;
   return (std::max(acc0 + Mg, acc0 + kTemps) + 3) & ~3;
 }
 
@@ -472,7 +474,8 @@ bool complete_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   for (auto& r : p.rows) mg = std::max(mg, (int)r.size());
   p.Mg = mg;
   p.D = 0;
-  p.vgprs = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb);
+  if (p.cb != 1) p.pb = 0;
+  p.vgprs = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb, p.pb ? p.nbuf * p.Cc : 0);
   if (p.vgprs > kMaxVgpr) {
     *why = "output channels per group exceed the registers";
     return false;
@@ -576,6 +579,7 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     c.c0 = f.c0 >= 0 ? f.c0 : kStagedFirst;
     c.es = f.es >= -1 ? f.es : kStagedEarly;
     c.esnt = f.esnt >= 0 ? f.esnt : 0;
+    c.pb = f.pb >= 0 ? f.pb : kStagedBases;
     if (complete_staged(g, rowptr, col, f.nb, f.cc, f.ra, f.cb, &c, &w))
       out.push_back(std::move(c));
     else if (out.empty())
@@ -588,7 +592,7 @@ std::vector<BakePlan> bake_candidates(const Geom& g, const std::vector<int32_t>&
     return n;
   };
   if (f.stage == 1 || f.nb > 0 || f.cc > 0 || f.ra > 0 || f.cb >= 0 || f.seq >= 0 || f.gw >= 0 || f.c0 >= 0 ||
-      f.es >= -1 || f.esnt >= 0) {
+      f.es >= -1 || f.esnt >= 0 || f.pb >= 0) {
     const int T = f.T > 0 ? f.T : 4;
     add_staged(f.G > 0 ? std::min(f.G, M) : staged_groups(2), T, f.seq > 0 ? 1 : 0, f.gw > 0 ? 1 : 0);
     return out;
@@ -823,10 +827,11 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   const int lw = p.bw / 64;  // DMA words per lane
   const int vB = kFixedV;              // DMA source offsets
   const int NS = p.ra + 1;             // read sets: the current batch's and ra batches ahead
-  const StagedRegs sr = staged_regs(g, nvb, p.ra, p.cb);
+  const int npb = p.pb ? p.nbuf * p.Cc : 0;
+  const StagedRegs sr = staged_regs(g, nvb, p.ra, p.cb, npb);
   const int SETW = sr.setw, vRd = sr.rd, vBase = sr.base, vAcc = sr.acc;
   const int vTmp = vAcc;               // prologue temporaries overlap the accumulators
-  const int nv = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb);
+  const int nv = staged_vgprs(g, nvb, p.Mg, p.ra, p.cb, npb);
   if (nv > kMaxVgpr || vAcc + p.Mg > nv) {
     *err = "staged kernel needs more than 256 VGPRs";
     return false;
@@ -938,6 +943,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
   if (p.cb == 2)  // channel-pair batches: the base of tap (r, s) in the region's first window
     for (int t = 0; t < g.R * S; t++)
       E.v(vBase + t, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + t, ((t / S) * g.Pp + t % S) * 4));
+  for (int b = 0; b < (npb ? p.nbuf : 0); b++)  // fixed bases: slot j of buffer b
+    for (int j = 0; j < p.Cc; j++)
+      E.v(vBase + b * p.Cc + j, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + b * p.Cc + j, b * BUF + j * p.chs * 4));
   decompose(tPos);
   // output offset 4*((n*M*E + yp)*F + f), f = xq - cshift; out of range unless yp < E,
   // f < F (unsigned) and n < N
@@ -1216,7 +1224,8 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
       }
       if (p.cb) {
         const int c = all[bt.steps[0]].c;
-        E.v(vBase + set, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vBase + set, boff + (rank[c] - c0) * p.chs * 4));
+        const int vb = npb ? vBase + boff / BUF * p.Cc + (rank[c] - c0) : vBase + set;
+        if (!npb) E.v(vb, 8, fmt("v_add_u32_e32 v%d, 0x%x, v5", vb, boff + (rank[c] - c0) * p.chs * 4));
         const int base = vRd + set * SETW;
         const size_t nt = bt.taps.size();
         for (size_t i = 0; i < nt; i += 2) {
@@ -1224,9 +1233,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
           if (i + 1 < nt) {
             const int t1 = bt.taps[i + 1], o1 = (t1 / S) * g.Pp + t1 % S;
             E.line("ds_read2_b32 v[%d:%d], v%d offset0:%d offset1:%d", base + (int)i, base + (int)i + 1,
-                   vBase + set, o0, o1);
+                   vb, o0, o1);
           } else {
-            E.line("ds_read_b32 v%d, v%d offset:%d", base + (int)i, vBase + set, o0 * 4);
+            E.line("ds_read_b32 v%d, v%d offset:%d", base + (int)i, vb, o0 * 4);
           }
           E.code += 8;
           n++;

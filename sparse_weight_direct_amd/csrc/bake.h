@@ -74,6 +74,8 @@ struct BakePlan {
                              // stored at the start of unit u + 1 (-1), or not before the group's
                              // es-th unit from the end (es >= 0; 0: after the last unit)
   int esnt = 0;              // cache policy of the early stores: 0 default, 1 nt, 2 sc0 sc1, 3 sc1
+  int pb = 0;                // channel batches: one LDS base register per chunk slot and buffer,
+                             // set once (else a base is made per channel)
   int vt = 0;                // VGPR target of the unstaged plans' groups and load depth (0: 168,
                              // three wavefronts per SIMD)
   long long fmas = 0;        // FMA instructions over all sections (= nnz)
@@ -96,14 +98,14 @@ struct BakeArgs {
   uint32_t per_xcd;   // workgroups per XCD (the grid is 8*per_xcd workgroups)
 };
 
-// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=..,GW=..,C0=..,ES=..,ESNT=..,ORD=..,VT=.." (tuning and
+// Options from SPARSECONV_BAKE="G=..,Q=..,T=..,D=..,DPP=..,PERM=..,STAGE=..,NB=..,CC=..,RA=..,CB=..,SEQ=..,GW=..,C0=..,ES=..,ESNT=..,ORD=..,VT=..,PB=.." (tuning and
 // tests only); fields left at -1 are chosen by the packer.
 struct BakeForce {
   int G = -1, Q = -1, T = -1, D = -1, dpp = -1, perm = -1, stage = -1, nb = -1, cc = -1, ra = -1, cb = -1,
-      seq = -1, gw = -1, c0 = -1, es = -2, esnt = -1, vt = -1;
+      seq = -1, gw = -1, c0 = -1, es = -2, esnt = -1, vt = -1, pb = -1;
   bool any() const {
     return G > 0 || Q > 0 || T > 0 || D > 0 || dpp >= 0 || perm >= 0 || stage >= 0 || nb > 0 || cc > 0 || ra > 0 ||
-           cb >= 0 || seq >= 0 || gw >= 0 || c0 >= 0 || es >= -1 || esnt >= 0 || vt > 0;
+           cb >= 0 || seq >= 0 || gw >= 0 || c0 >= 0 || es >= -1 || esnt >= 0 || vt > 0 || pb >= 0;
   }
 };
 BakeForce bake_force_from_env();

@@ -204,7 +204,7 @@ def test_staged_plans(layer, env, monkeypatch):
 @pytest.mark.parametrize("layer", [LAYER, WIDE_LAYER], ids=["narrow", "wide"])
 @pytest.mark.parametrize("env", ["C0=1", "C0=2,CC=5,NB=3", "ES=-1,ORD=1", "ES=2,ESNT=1,CC=3,ORD=1",
                                  "ES=-1,ORD=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3", "SEQ=1,G=2,ES=1,CC=4",
-                                 "CB=2", "GW=1,G=2,CB=2", "CB=2,ES=-1,ORD=1,C0=1"])
+                                 "CB=2", "GW=1,G=2,CB=2", "CB=2,ES=-1,ORD=1,C0=1", "PB=1", "PB=1,GW=1,G=2,NB=3"])
 def test_staged_options(layer, env, monkeypatch):
     """Staged-kernel options: a smaller first chunk (C0), the walk's channel order that completes
     output channels early (ORD=1, which every plan of the handle takes) with stores issued during
@@ -224,7 +224,7 @@ def test_staged_options(layer, env, monkeypatch):
 
 
 @pytest.mark.parametrize("env", ["STAGE=1,ES=-1,ORD=1", "STAGE=1,ES=1,ESNT=1", "STAGE=1,CB=2,C0=4",
-                                 "GW=1,G=2,ES=-1,ORD=1"])
+                                 "GW=1,G=2,ES=-1,ORD=1", "STAGE=1,PB=1"])
 def test_staged_options_full_size(env, monkeypatch):
     """Early stores (their waits count the stores in flight), pair batches and a small first
     chunk on the full-size 112x112 layer at 95% sparsity: every output against the oracle."""
