@@ -10,18 +10,16 @@ pins the fastest); the forward launches one kernel (on this layer the staged wei
 kernel).
 
 Timing: W warm-up steps, then exactly K steps between two HIP events on the launch stream,
-with a device synchronisation on both sides, one library call per step.  The same K steps
-launched from HIP graphs (up to 24 forwards captured once and replayed, and a graph of the
-remaining steps) are timed too and reported beside them (--launch graph makes those the value);
-the two agree within the run-to-run spread (±1-2 us), so the host's cost per call does not
-bound the step.  Both run after
+with a device synchronisation on both sides, one library call per step; no event is recorded
+inside a window shorter than 200 steps (an event between two forwards holds the stream for
+~1.5-3 us: with one every 2 steps, a 20-step window ran 1.5 us per step slower), and the SEM
+comes from 5 further windows of K steps timed after it.  The same K steps launched from HIP
+graphs (up to 24 forwards captured once and replayed, and a graph of the remaining steps) are
+timed too and reported beside them (--launch graph makes those the value).  Both run after
 the bench's other measurements of the same layer (references, dense baselines, roof probes,
 1000 warm forwards), so the GPU's clock has left its idle state: from idle it rises over the
 first ~30 ms of sustained work, and a window of a few dozen steps right after start-up would
-time that ramp.  The same K steps
-launched from HIP graphs (24 forwards captured once and replayed, and a graph of the remaining
-steps) are timed too and reported beside them, a check that the host's launch cost does not
-bound the step (--launch graph makes those the timed steps).
+time that ramp.
 Input/output buffer sets rotate so the working set exceeds the 256 MB Infinity Cache and every
 step reads its input from HBM ("cold").
 
@@ -123,10 +121,15 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run(fn, steps, warmup, nsets):
+        """ms per step over exactly ``steps`` launches between two HIP events (after ``warmup``
+        untimed ones and a synchronisation) and its SEM.  An event recorded between launches
+        holds the stream for ~1.5-3 us, so the timed window gets inner events (groups for the
+        SEM) only every 100 steps or more; a shorter window takes its SEM from 5 further
+        windows of the same length, timed after it."""
         for i in range(warmup):
             fn(i % nsets)
         torch.cuda.synchronize()
-        groups = 10 if steps >= 10 else 1
+        groups = max(1, min(10, steps // 100))
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
         bounds = [round(g * steps / groups) for g in range(groups + 1)]
         evs[0].record(stream)
@@ -137,7 +140,16 @@ def main():
         torch.cuda.synchronize()
         total = evs[0].elapsed_time(evs[-1])
         per = [evs[g].elapsed_time(evs[g + 1]) / (bounds[g + 1] - bounds[g]) for g in range(groups)]
-        sem = float(np.std(per, ddof=1) / math.sqrt(len(per))) if len(per) > 1 else 0.0
+        if groups == 1:
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(steps):
+                    fn(i % nsets)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) / steps)
+        sem = float(np.std(per, ddof=1) / math.sqrt(len(per)))
         return total / steps, sem
 
     def run_graph(fwd, steps, warmup, nsets, per_graph=24):
@@ -162,18 +174,21 @@ def main():
         full, rest = capture(per_graph), (capture(steps % per_graph) if steps % per_graph else None)
         torch.cuda.synchronize()
         # no untimed replay: a graph's first launch measured no slower than its later ones
-        nrep = steps // per_graph
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 2)]
+        # an inner event (for the SEM) after every `every` replays: at least 100 forwards apart
+        nrep, every = steps // per_graph, -(-100 // per_graph)
+        marks = [r for r in range(every, nrep + 1, every)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(marks) + 2)]
         evs[0].record(stream)
-        for r in range(nrep):
+        for r in range(1, nrep + 1):
             full.replay()
-            evs[r + 1].record(stream)
+            if r in marks:
+                evs[marks.index(r) + 1].record(stream)
         if rest is not None:
             rest.replay()
         evs[-1].record(stream)
         torch.cuda.synchronize()
         total = evs[0].elapsed_time(evs[-1])
-        per = [evs[r].elapsed_time(evs[r + 1]) / per_graph for r in range(nrep)]
+        per = [evs[i].elapsed_time(evs[i + 1]) / (every * per_graph) for i in range(len(marks))]
         sem = float(np.std(per, ddof=1) / math.sqrt(len(per))) if len(per) > 1 else 0.0
         del full, rest
         return total / steps, sem
