@@ -179,7 +179,8 @@ STAGED_ENVS = ["STAGE=1", "STAGE=1,T=1", "STAGE=1,T=2", "STAGE=1,G=3,T=3", "NB=3
                "GW=1,G=5,T=3,CC=3", "GW=1,G=4,CB=0,NB=3", "C0=1", "C0=2,CC=5,NB=3", "GW=1,G=2,C0=1,CC=4", "ES=-1,ORD=1", "ES=2,ESNT=1,CC=3,ORD=1",
                "SEQ=1,G=2,ES=1,ESNT=2,CC=4", "GW=1,G=2,ES=-1,ORD=1,CC=3", "CB=2", "CB=2,T=2,CC=5",
                "GW=1,G=2,CB=2", "SEQ=1,G=2,CB=2,CC=3", "CB=2,ES=-1,ORD=1,C0=1", "PB=1", "PB=1,NB=3,CC=5,C0=2",
-               "PB=1,GW=1,G=2,RA=2", "PB=1,SEQ=1,G=2,ES=-1,ORD=1", "PB=1,CB=2"]
+               "PB=1,GW=1,G=2,RA=2", "PB=1,SEQ=1,G=2,ES=-1,ORD=1", "PB=1,CB=2", "PB=0", "PB=0,RA=2,CC=5",
+               "PB=0,GW=1,G=2"]
 
 
 @pytest.mark.parametrize("env", STAGED_ENVS)
@@ -193,8 +194,9 @@ def test_staged_kernels(c, env, monkeypatch):
     Options: T wavefronts per workgroup, G groups, NB chunk buffers (the DMA runs NB - 1
     chunks ahead), CC channels per chunk, RA batches of tap reads in flight, CB=1 a channel's
     taps read as one batch (pairs by ds_read2_b32 from a per-channel base register; the
-    default where the filter's reach allows; PB=1 from fixed base registers, one per chunk slot
-    and buffer, set in the prologue), CB=2 two channels' taps per batch (a tap of both
+    default where the filter's reach allows; from fixed base registers, one per chunk slot and
+    buffer, set in the prologue, or with PB=0 from a base made per channel), CB=2 two channels'
+    taps per batch (a tap of both
     channels in one ds_read2st64_b32 from a base register per tap), CB=0 one step's taps per
     batch, SEQ=1 every
     workgroup runs all G groups in turn (the DMA pipeline continues across groups, each
