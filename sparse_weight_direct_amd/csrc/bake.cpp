@@ -95,7 +95,8 @@ bool fits_cu(int waves, int vgprs, int lds, std::string* why) {
 constexpr int kReduceChannels = 32;  // channels per round of the channel-split reduction
 constexpr int kStagedChunk = 12;     // channels per staged chunk (fewer barriers than 8: ~1 us
                                      // faster on the 112x112 layers; 16 no faster)
-constexpr int kStagedBases = 1;     // fixed per-slot LDS bases (pb): imb95 0.15-0.35 us faster
+constexpr int kStagedBases = 1;     // fixed per-slot LDS bases (pb): imb95 0.15-0.35 us, imb90
+                                     // ~4 us faster than a base made per channel
 constexpr int kStagedFirst = 0;      // channels of the first staged chunk (0: a full chunk)
 constexpr int kStagedEarly = 0;      // units from the end at which the stores of output channels
                                      // that are already final start (0: all stores after the walk;
@@ -815,8 +816,9 @@ static int staged_dmas_min(const BakePlan& p, int cn) {
 // wavefront w holds I0 + 64 w + lane.  Per chunk of Cc channels each channel's window
 // [I0, I0 + chs) is copied into LDS once (LDS DMA: lane i writes M0 + 4*i*(bw/64); zero where
 // the source lies in the padding: out-of-range offset) into one of nbuf buffers, nbuf - 1
-// chunks ahead of the FMAs; a channel's taps are read as one batch (ds_read2_b32 pairs from a
-// per-channel base register), a batch ahead, or a step's by ds_read_b32 from the lane's base
+// chunks ahead of the FMAs; a channel's taps are read as one batch (ds_read2_b32 pairs from the
+// base register of its chunk slot and buffer, set in the prologue, or made per channel), a
+// batch ahead, or a step's by ds_read_b32 from the lane's base
 // v5 at immediate offsets (cb = 0), or two channels' (cb = 2).  After the walk the outputs
 // are stored through VGPR bases (store_slots).
 bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
@@ -1185,8 +1187,9 @@ bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const st
     // tap reads go out in batches, ra batches ahead of the FMAs, into read sets of SETW
     // registers: a batch is one step (reads from the lane's base v5 at full offsets, tap
     // column s in register s of the set), or with channel batches all steps of one channel
-    // (a base register per set points at the channel's window, and pairs of taps come in
-    // one ds_read2_b32, into consecutive registers in the order of the channel's taps)
+    // (a base register points at the channel's window: the fixed one of its chunk slot and
+    // buffer, or with pb = 0 one per read set made here; pairs of taps come in one
+    // ds_read2_b32, into consecutive registers in the order of the channel's taps)
     // Channel-pair batches (cb = 2): the steps of two channels a, b of the chunk; per tap used
     // by either, one ds_read2st64_b32 from the tap's base register reads it for both channels
     // (offsets: the two windows, in units of 256 bytes) into registers 2i (a) and 2i + 1 (b).

@@ -21,6 +21,7 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import statistics
 import sys
 
@@ -37,12 +38,24 @@ KERNEL_SOURCES = {
 COPY_KERNELS = ("__amd_rocclr_copyBuffer", "copy", "Copy")
 
 
+def _code_only(path: str) -> bytes:
+    """A source file's code: comments (C++ ``//`` and ``/* */``, Python ``#``), trailing blanks
+    and empty lines removed, so that editing a comment keeps the digest."""
+    text = open(path, encoding="utf-8").read()
+    if path.endswith(".py"):
+        lines = [ln.split("#", 1)[0] if ln.lstrip().startswith("#") else ln for ln in text.splitlines()]
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"(^|\s)//.*$", "", ln) for ln in text.splitlines()]
+    return "\n".join(ln.rstrip() for ln in lines if ln.strip()).encode()
+
+
 def kernel_digest(kernel: str = "sc_baked") -> str:
-    """Digest of the sources a kernel is built from (ties stored counters to them)."""
+    """Digest of the code a kernel is built from, comments left out (ties stored counters to
+    the code they were taken with)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kernel]:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        h.update(_code_only(p))
     return h.hexdigest()[:16]
 
 
