@@ -818,9 +818,9 @@ static int staged_dmas_min(const BakePlan& p, int cn) {
 // the source lies in the padding: out-of-range offset) into one of nbuf buffers, nbuf - 1
 // chunks ahead of the FMAs; a channel's taps are read as one batch (ds_read2_b32 pairs from the
 // base register of its chunk slot and buffer, set in the prologue, or made per channel), a
-// batch ahead, or a step's by ds_read_b32 from the lane's base
-// v5 at immediate offsets (cb = 0), or two channels' (cb = 2).  After the walk the outputs
-// are stored through VGPR bases (store_slots).
+// batch ahead, or a step's by ds_read_b32 from the lane's base v5 at immediate offsets
+// (cb = 0), or two channels' (cb = 2).  After the walk the outputs are stored through VGPR
+// bases (store_slots).
 bool generate_staged(const Geom& g, const std::vector<int32_t>& rowptr, const std::vector<int32_t>& col,
                      const std::vector<float>& val, BakePlan& p, std::string* src, std::string* err) {
   const int T = p.T, S = g.S;
