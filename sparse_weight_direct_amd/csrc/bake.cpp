@@ -75,6 +75,7 @@ constexpr int kFixedV = 6;      // v0 id, v1 lane, v2 zero, v3 out-of-range mark
 constexpr int kTemps = 12;      // prologue temporaries
 constexpr long long kCodeMax = 2ll << 20;  // refuse kernels above 2 MB of code (~250K non-zeros)
 constexpr int kVgprTarget = 168;  // three wavefronts per SIMD
+constexpr int kMinDepth = 4;      // row loads in flight a plan keeps if the registers allow
 constexpr int kSimdVgprs = 512;   // VGPRs per lane of a SIMD (wave64), allocated in blocks of 8
 constexpr int kLdsBytes = 160 * 1024;  // LDS of a CU
 
@@ -308,6 +309,10 @@ bool complete_plan(const Geom& g, const std::vector<int32_t>& rowptr, const std:
     const int target = plan_vgprs(g, p, p.Mg, 1) <= vt ? vt : kMaxVgpr;
     D = 1;
     while (D < cap && plan_vgprs(g, p, p.Mg, D + 1) <= target) D++;
+    // a shallower ring leaves the loads' latency exposed: deepen it to kMinDepth where the
+    // registers allow, at the cost of occupancy (11x11 stride-4 layer, 810 wavefronts, one per
+    // SIMD at most: D = 4 15.1 us against 16.6 with D = 2; D = 6, 8, 15 15.4, 15.9, 17.6)
+    while (D < std::min(cap, kMinDepth) && plan_vgprs(g, p, p.Mg, D + 1) <= kMaxVgpr) D++;
     if (!p.perm || D >= 2) break;
     p.perm = 0;
   }
