@@ -247,6 +247,20 @@ def test_staged_full_size(name, monkeypatch):
     assert_layer_parity(name, y, f"{name} staged")
 
 
+@pytest.mark.parametrize("n", [1, 3, 7])
+def test_staged_kernel_smaller_batches(n, monkeypatch):
+    """One staged handle of the 112x112 layer at 95% sparsity launched on batches of 1, 3 and 7
+    images (52, 155 and 362 workgroups, the last one partly past the batch's positions; the grid
+    rounded up to a multiple of the 8 XCDs): every output against the oracle."""
+    d = workloads.make("imb95", n_override=n)
+    L = d["layer"]
+    monkeypatch.setenv("SPARSECONV_BAKE", "STAGE=1")
+    y, h = gpu_sparse(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert h.launch_info(n)["stage"] == 1
+    r = oracle.reference(d["x"], d["w"], d["mask"], L.stride, L.pad)
+    assert_parity(y, r["y64"], r["mag"], f"imb95 staged N={n}")
+
+
 def test_staged_kernel_input_not_16_byte_aligned():
     """The staged kernel copies 16 bytes a lane and needs a 16-byte aligned input; an input 4 bytes
     off falls back to the first kernel that reads rows directly, with the same result."""
